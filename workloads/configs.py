@@ -1,0 +1,111 @@
+"""Workload shapes for the EAGLE-3 draft-and-verify path.
+
+Pure data: drafter shapes, tree/verify parameters and synthetic-input
+recipes.  Nothing here computes any step of the method.
+
+Shapes follow the drafters the EAGLE-3 pages name (a Llama-3.1-8B-shaped and
+a Llama-3.3-70B-shaped one-layer drafter, "EAGLE-3 精读" §4 结果与消融) plus a
+tiny fp32 drafter small enough for exhaustive CPU checks.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclass(frozen=True)
+class DrafterShape:
+    """One-layer drafter dimensions ("EAGLE-3 精读" §1: fusion 3d -> d, one decoder layer)."""
+    name: str
+    d: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    dtype: str
+    rms_eps: float = 1e-5
+    rope_theta: float = 500000.0
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A full synthetic workload: drafter shape + tree + verify + input recipe."""
+    name: str
+    shape: DrafterShape
+    batch: int = 1
+    depth: int = 3            # D: drafter rounds incl. the root round = max node depth
+    topk: int = 2             # k: children per frontier node and beam width
+    keep: int = 8             # m: drafted nodes sent to verification (plus the root)
+    prefix: int = 64          # committed prefix length before the root
+    commit_rows: int = 1      # rows the COMMIT step appends (root is the last)
+    synthetic_prefix_kv: bool = True   # prefix K/V drawn N(0,1) instead of computed
+    target_sigma: float = 2.0 # target logits N(0, sigma)
+    planted_accept: Optional[float] = None  # planted per-node argmax agreement
+    planted_accept_range: Optional[tuple] = None  # per-request U[lo,hi] (serving)
+    paged: bool = False
+    block_size: int = 16
+    prefix_range: Optional[tuple] = None  # per-request prefix length U[lo,hi]
+    verify_modes: tuple = ("greedy",)
+    temperature: float = 1.0
+    feat_scale: float = 1.0   # target features N(0,1) * feat_scale
+    # TTT
+    ttt_seq: int = 0
+    ttt_steps: int = 5
+
+
+TINY_SHAPE = DrafterShape("tiny-d256", d=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                          ffn=1024, vocab=4096, dtype=F32, rope_theta=10000.0)
+L8B_SHAPE = DrafterShape("llama3.1-8b-drafter", d=4096, n_q_heads=32, n_kv_heads=8,
+                         head_dim=128, ffn=14336, vocab=128256, dtype=BF16)
+L70B_SHAPE = DrafterShape("llama3.3-70b-drafter", d=8192, n_q_heads=64, n_kv_heads=8,
+                          head_dim=128, ffn=28672, vocab=128256, dtype=BF16)
+
+# Tiny fp32 drafter: 64 committed prefix rows, the root is row 63.
+C1_TINY = Workload(
+    "tiny-fp32-b1-tree3x2-keep8", TINY_SHAPE, batch=1, depth=3, topk=2, keep=8,
+    prefix=0, commit_rows=64, synthetic_prefix_kv=False, target_sigma=2.0,
+    verify_modes=("greedy", "sample"), temperature=1.0, feat_scale=1.0 / 16.0)
+
+# 8B-shaped drafter, batch 1, dynamic tree depth 6 / top-10 / 60 kept.
+C2_8B_TREE = Workload(
+    "llama3.1-8b-drafter-b1-tree6x10-keep60", L8B_SHAPE, batch=1, depth=6, topk=10,
+    keep=60, prefix=2048, commit_rows=1, target_sigma=3.0, planted_accept=0.8,
+    verify_modes=("greedy", "sample"))
+
+# Serving: same drafter, batch 64, chain of 3 (k=1), paged 16-token KV.
+C3_8B_CHAIN = Workload(
+    "llama3.1-8b-drafter-b64-chain3-paged16", L8B_SHAPE, batch=64, depth=3, topk=1,
+    keep=3, prefix=2048, commit_rows=1, target_sigma=3.0,
+    planted_accept_range=(0.5, 0.9), paged=True, block_size=16,
+    prefix_range=(256, 2048), verify_modes=("greedy",))
+
+# 70B-shaped drafter, batch 1, tree 6/10/60, temperature-1 sampling verify.
+C4_70B_TREE = Workload(
+    "llama3.3-70b-drafter-b1-tree6x10-keep60", L70B_SHAPE, batch=1, depth=6, topk=10,
+    keep=60, prefix=4096, commit_rows=1, target_sigma=3.0,
+    verify_modes=("sample", "greedy"), temperature=1.0)
+
+# Training-time-test forward, 8B-shaped drafter, 8 x 2048, 5 rollout steps.
+C5_8B_TTT = Workload(
+    "llama3.1-8b-drafter-ttt-b8x2048-r5", L8B_SHAPE, batch=8, ttt_seq=2048, ttt_steps=5)
+
+CONFIGS = [C1_TINY, C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT]
+
+
+def tiny_shape(d=16, hq=2, hkv=1, hd=8, ffn=32, vocab=8, dtype=F32, theta=10000.0, name=None):
+    """Very small drafters for exhaustive oracle checks."""
+    return DrafterShape(name or f"micro-d{d}-v{vocab}-{dtype}", d=d, n_q_heads=hq,
+                        n_kv_heads=hkv, head_dim=hd, ffn=ffn, vocab=vocab, dtype=dtype,
+                        rope_theta=theta)
+
+
+def scaled(w: Workload, **kw) -> Workload:
+    return replace(w, **kw)
