@@ -1,0 +1,301 @@
+// Weight-streaming GEMM for few rows: Y[r, n] = sum_k X[r, k] * W[n, k],
+// r < R <= 64, with a fused epilogue.
+//
+// Batch-1 / batch-64 drafting is bound by HBM: every weight byte is read
+// once per round and used for R <= 64 rows.  One workgroup owns 16*T
+// weight rows ("a tile") and the whole K range; its waves split K into
+// 32*U-wide groups (wave w takes groups w, w+WAVES, ...).  Each lane reads
+// 16-byte runs of one weight row straight into MFMA A registers
+// (v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)..+8]); the X rows
+// are the B operand (column = X row).  Per-wave partial tiles are summed in
+// LDS in a fixed order (deterministic), then the epilogue runs on the
+// [16T x R] fp32 tile.
+//
+// Row maps let a tile hold the two halves of a pair in rows m and m+8:
+// RoPE partners (i, i+hd/2) of one head, or the gate/up rows of one FFN
+// column.  The epilogue then sees both halves in the same workgroup.
+#pragma once
+#include "common.hpp"
+
+namespace e3 {
+
+enum { MAP_PLAIN = 0, MAP_PAIR_HEAD = 1, MAP_PAIR_FFN = 2 };
+
+struct RowMap {
+  int kind, hd, ffn;
+  // Weight row of tile-local row m (0..15) of 16-row tile `tile`.
+  __device__ __forceinline__ int operator()(int tile, int m) const {
+    if (kind == MAP_PLAIN) return tile * 16 + m;
+    if (kind == MAP_PAIR_HEAD) {
+      const int tph = hd >> 4, h = tile / tph, t = tile - h * tph, half = hd >> 1;
+      return h * hd + (m < 8 ? t * 8 + m : half + t * 8 + (m - 8));
+    }
+    return m < 8 ? tile * 8 + m : ffn + tile * 8 + (m - 8);
+  }
+};
+
+// Number of 16-row tiles for N outputs under a map.
+static inline int rowmap_tiles(int kind, int N) { return kind == MAP_PLAIN ? N / 16 : N / 16; }
+
+union U4 {
+  uint4 u;
+  bf16x8 v;
+};
+
+// ---------------------------------------------------------------------------
+// Compute a [16*T x R] tile into LDS `tile_out` (layout [16*T][RP], RP =
+// 16*NT), bf16 operands on MFMA.
+template <int T, int NT, int U, int WAVES>
+__device__ __forceinline__ void rows_tile_bf16(const bf16* __restrict__ X, int ldx, int R,
+                                               const bf16* __restrict__ W, int ldw, int K,
+                                               const int* wrows /*[16*T] in LDS*/,
+                                               float* red /*[WAVES][T][NT][256]*/,
+                                               float* tile_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, q4 = lane >> 4;
+  constexpr int KG = 32 * U;
+  const bf16* wp[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wp[t] = W + (size_t)wrows[t * 16 + m] * ldw;
+  const bf16* xp[NT];
+  bool xv[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const int r = c * 16 + m;
+    xv[c] = r < R;
+    xp[c] = X + (size_t)(xv[c] ? r : 0) * ldx;
+  }
+  f32x4 acc[T][NT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ngroups = K / KG;
+  for (int g = wave; g < ngroups; g += WAVES) {
+    const int kb = g * KG + q4 * (8 * U);
+    U4 a[T][U], b[NT][U];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < U; ++j) a[t][j].u = *(const uint4*)(wp[t] + kb + j * 8);
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (xv[c]) b[c][j].u = *(const uint4*)(xp[c] + kb + j * 8);
+        else b[c][j].u = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+          acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][j].v, b[c][j].v, acc[t][c], 0, 0, 0);
+  }
+  // K tail in 32-wide chunks (one MFMA each), spread over the waves.
+  const int kdone = ngroups * KG;
+  const int ntail = (K - kdone) / 32;
+  for (int c32 = wave; c32 < ntail; c32 += WAVES) {
+    const int kb = kdone + c32 * 32 + q4 * 8;
+    U4 a[T], b[NT];
+#pragma unroll
+    for (int t = 0; t < T; ++t) a[t].u = *(const uint4*)(wp[t] + kb);
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      if (xv[c]) b[c].u = *(const uint4*)(xp[c] + kb);
+      else b[c].u = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+        acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t].v, b[c].v, acc[t][c], 0, 0, 0);
+  }
+  // Output layout of the 16x16 MFMA: lane l holds D[4(l/16)+i][l%16].
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(((wave * T + t) * NT + c) << 8) + ((q4 * 4 + i) << 4) + m] = acc[t][c][i];
+  __syncthreads();
+  constexpr int RP = 16 * NT;
+  for (int e = threadIdx.x; e < T * NT * 256; e += WAVES * 64) {
+    const int t = e / (NT * 256), rem = e - t * NT * 256, c = rem >> 8, mm = (rem >> 4) & 15,
+              n = rem & 15;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += red[(((w * T + t) * NT + c) << 8) + (mm << 4) + n];
+    tile_out[(t * 16 + mm) * RP + c * 16 + n] = s;
+  }
+  __syncthreads();
+}
+
+// fp32 operands (small fp32 drafters): plain FMA, one output per thread at a
+// time, K in order.
+template <int T, int NT, int WAVES>
+__device__ __forceinline__ void rows_tile_f32(const float* __restrict__ X, int ldx, int R,
+                                              const float* __restrict__ W, int ldw, int K,
+                                              const int* wrows, float* tile_out) {
+  constexpr int RP = 16 * NT;
+  for (int e = threadIdx.x; e < 16 * T * R; e += WAVES * 64) {
+    const int mm = e / R, r = e - mm * R;
+    const float* wp = W + (size_t)wrows[mm] * ldw;
+    const float* xp = X + (size_t)r * ldx;
+    float s = 0.f;
+    for (int k = 0; k < K; ++k) s = fmaf(xp[k], wp[k], s);
+    tile_out[mm * RP + r] = s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: grid.x = number of workgroup tiles (16*T weight rows each).
+template <typename TW, int T, int NT, int U, int WAVES, class Epi>
+__global__ __launch_bounds__(WAVES * 64) void rows_gemm_kernel(const TW* __restrict__ X, int ldx,
+                                                               int R, const TW* __restrict__ W,
+                                                               int ldw, int K, int ntiles16,
+                                                               RowMap map, Epi epi) {
+  constexpr int RP = 16 * NT;
+  __shared__ int wrows[16 * T];
+  __shared__ float tile[16 * T * RP];
+  extern __shared__ float red[];
+  const int wg_tile = blockIdx.x;
+  for (int i = threadIdx.x; i < 16 * T; i += WAVES * 64) {
+    const int t16 = wg_tile * T + i / 16;
+    wrows[i] = t16 < ntiles16 ? map(t16, i & 15) : map(0, i & 15);
+  }
+  __syncthreads();
+  if constexpr (sizeof(TW) == 2)
+    rows_tile_bf16<T, NT, U, WAVES>((const bf16*)X, ldx, R, (const bf16*)W, ldw, K, wrows, red, tile);
+  else
+    rows_tile_f32<T, NT, WAVES>((const float*)X, ldx, R, (const float*)W, ldw, K, wrows, tile);
+  for (int t = 0; t < T; ++t) {
+    const int t16 = wg_tile * T + t;
+    if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues.  `tile` is [16][RP] fp32 (row m = tile-local weight row, column
+// r = X row).  They run with all threads of the block.
+
+// out[r, n] = v  (float or bf16-rounded), n = map(tile, m).
+template <typename TO>
+struct EpiStore {
+  TO* out;
+  int ldo;
+  RowMap map;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+    for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
+      const int m = e / R, r = e - m * R;
+      Elem<TO>::st(out, (size_t)r * ldo + map(tile16, m), tile[m * RP + r]);
+    }
+  }
+};
+
+// out[r, n] = res[r, n] + v  (fp32 residual stream).
+struct EpiResidual {
+  float* out;
+  const float* res;
+  int ld;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+    for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
+      const int m = e / R, r = e - m * R;
+      const size_t i = (size_t)r * ld + tile16 * 16 + m;
+      out[i] = res[i] + tile[m * RP + r];
+    }
+  }
+};
+
+// z[r, c] = silu(gate) * up for the 8 FFN columns c of a MAP_PAIR_FFN tile
+// (rows m < 8 gate, m + 8 the matching up row), rounded to TO.
+template <typename TO>
+struct EpiSwiGLU {
+  TO* z;
+  int ffn;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+    for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
+      const int m = e / R, r = e - m * R;
+      const float g = tile[m * RP + r], u = tile[(m + 8) * RP + r];
+      const float s = g / (1.f + expf(-g));
+      Elem<TO>::st(z, (size_t)r * ffn + tile16 * 8 + m, s * u);
+    }
+  }
+};
+
+// Where the k/v of query row r go (draft step): committed cache row
+// ctx_len[b] + rr (COMMIT, contiguous or paged) or tree slot slot_base + rr.
+struct KVDest {
+  void* k;
+  void* v;
+  void* tk;
+  void* tv;
+  const int32_t* ctx_len;
+  const int32_t* block_table;
+  int cap, max_blocks, block_size, rows, mode, slot_base, hkv, hd;
+  int row0;  // global index of the launch's first row
+  // Element offset of (row r, kv head g, dim 0); `tree` tells which buffer.
+  __device__ __forceinline__ size_t off(int r_local, int g, bool& tree) const {
+    const int r = r_local + row0;
+    const int b = r / rows, rr = r - b * rows;
+    if (mode == EAGLE3_TREE) {
+      tree = true;
+      return ((size_t)(b * EAGLE3_MAX_TREE_SLOTS + slot_base + rr) * hkv + g) * hd;
+    }
+    tree = false;
+    const int crow = ctx_len[b] + rr;
+    if (block_table) {
+      const int blk = block_table[(size_t)b * max_blocks + crow / block_size];
+      return ((size_t)blk * block_size + crow % block_size) * hkv * hd + (size_t)g * hd;
+    }
+    return (((size_t)b * cap + crow) * hkv + g) * hd;
+  }
+};
+
+// QKV epilogue for a MAP_PAIR_HEAD tile: rows m and m+8 are the RoPE pair
+// (i, i + hd/2) of one head, i = t*8 + m.  q goes to q_out [R][Hq*hd];
+// k/v go to the KV destination.  Values are rounded to TO after RoPE.
+template <typename TO>
+struct EpiQKV {
+  TO* q_out;
+  const int32_t* pos;  // [R]
+  KVDest dst;
+  int hq;
+  float theta;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+    const int hd = dst.hd, tph = hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
+    const int half = hd >> 1;
+    for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
+      const int m = e / R, r = e - m * R;
+      const int i = t * 8 + m;  // pair index within the head
+      float a = tile[m * RP + r], b = tile[(m + 8) * RP + r];
+      if (head < hq + dst.hkv) {  // q or k: rotate
+        const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
+        const double ang = (double)pos[r] * inv;
+        const float c = (float)cos(ang), s = (float)sin(ang);
+        const float a2 = a * c - b * s, b2 = b * c + a * s;
+        a = a2;
+        b = b2;
+      }
+      if (head < hq) {
+        const size_t o = (size_t)r * hq * hd + (size_t)head * hd;
+        Elem<TO>::st(q_out, o + i, a);
+        Elem<TO>::st(q_out, o + i + half, b);
+      } else {
+        const bool isk = head < hq + dst.hkv;
+        const int g = isk ? head - hq : head - hq - dst.hkv;
+        bool tree;
+        const size_t o = dst.off(r, g, tree);
+        TO* base = (TO*)(isk ? (tree ? dst.tk : dst.k) : (tree ? dst.tv : dst.v));
+        Elem<TO>::st(base, o + i, a);
+        Elem<TO>::st(base, o + i + half, b);
+      }
+    }
+  }
+};
+
+}  // namespace e3

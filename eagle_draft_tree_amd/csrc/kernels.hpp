@@ -1,0 +1,47 @@
+// Host-side launchers of the library's kernels (internal interface between
+// the C ABI layer and the kernel translation units).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace e3 {
+
+// ---- decode attention (attention.hip)
+struct AttnLaunch {
+  const void* q;
+  const void *kc, *vc, *tk, *tv;
+  const int32_t* ctx_len;
+  const int32_t* block_table;
+  const uint64_t* anc;
+  int cap, max_blocks, block_size, cap_rows;
+  int B, rows, hq, hkv, hd, mode;
+  bool bf16;
+  float* part_o;
+  float* part_ml;
+  void* out;  // [B*rows][hq*hd] dtype
+};
+int attn_num_chunks(int cap_rows);
+hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
+
+// ---- top-k + log-probs over vocab rows (topk.hip)
+size_t topk_ws_bytes(int rows, int V);
+hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp,
+                       float* lse, void* ws, hipStream_t st);
+
+// ---- dynamic tree (tree.hip)
+size_t tree_state_bytes_per_req(int k, int D);
+hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32_t* root_tok,
+                              const int32_t* root_pos, void* state, const int32_t* topk_id,
+                              const float* topk_lp, int32_t* next_tok, int32_t* next_parent_slot,
+                              int32_t* next_pos, uint64_t* next_anc, int32_t* v_tok,
+                              int32_t* v_parent, int32_t* v_depth, int32_t* v_pos, uint64_t* v_anc,
+                              hipStream_t st);
+
+// ---- verification (verify.hip)
+hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
+                         const int32_t* v_parent, const float* logits, int mode, float temperature,
+                         const double* u_try, const double* u_res, int32_t* accept_len,
+                         int32_t* accepted, int32_t* bonus, int32_t* status, hipStream_t st);
+
+}  // namespace e3

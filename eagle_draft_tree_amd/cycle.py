@@ -1,0 +1,135 @@
+"""Host-side driver of one EAGLE-3 draft-tree cycle through the C ABI.
+
+fuse -> draft_step(COMMIT) -> tree_expand(INIT) -> [draft_step(TREE) ->
+tree_expand(STEP)] x (D-1) -> tree_expand(FINAL) -> verify.  Only ABI calls
+are enqueued (on torch's current stream); every step runs in the library's
+kernels.  Device buffers come from torch.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class Drafter:
+    """Device-resident drafter weights plus their eagle3_dims/eagle3_weights."""
+
+    def __init__(self, shape, weights: dict, device="cuda"):
+        self.shape = shape
+        self.tensors = {}
+        for name, w in weights.items():
+            if hasattr(w, "torch"):
+                self.tensors[name] = w.torch(device)
+            else:
+                self.tensors[name] = torch.as_tensor(np.asarray(w, dtype=np.float32)).to(device)
+        self.dims = B.dims_of(shape)
+        self.weights = B.weights_of(self.tensors)
+        self.torch_dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+
+@dataclass
+class CycleSpec:
+    batch: int
+    commit_rows: int
+    k: int
+    depth: int
+    keep: int
+    cap_rows: int      # KV rows per request (contiguous cap, or max_blocks*block_size)
+
+
+class CycleBuffers:
+    """Every device buffer one cycle needs (allocated once, reused)."""
+
+    def __init__(self, drafter: Drafter, spec: CycleSpec, device="cuda"):
+        s, dv = drafter.shape, device
+        Bn, n, k, D, m = spec.batch, spec.commit_rows, spec.k, spec.depth, spec.keep
+        i32 = dict(dtype=torch.int32, device=dv)
+        self.spec = spec
+        self.g = torch.empty(Bn * n, s.d, dtype=drafter.torch_dtype, device=dv)
+        self.h_tree = torch.zeros(Bn, B.MAX_TREE_SLOTS + 1, s.d, dtype=torch.float32, device=dv)
+        max_rows = max(n, k)
+        self.ws = torch.empty(B.workspace_size(drafter.dims, Bn, max_rows, spec.cap_rows), dtype=torch.uint8,
+                              device=dv)
+        self.root_ids = torch.empty(Bn, 1, k, **i32)
+        self.root_lp = torch.empty(Bn, 1, k, dtype=torch.float32, device=dv)
+        self.round_ids = [torch.empty(Bn, k, k, **i32) for _ in range(max(D - 1, 0))]
+        self.round_lp = [torch.empty(Bn, k, k, dtype=torch.float32, device=dv) for _ in range(max(D - 1, 0))]
+        self.next_tok = [torch.empty(Bn, k, **i32) for _ in range(max(D - 1, 0))]
+        self.next_par = [torch.empty(Bn, k, **i32) for _ in range(max(D - 1, 0))]
+        self.next_pos = [torch.empty(Bn, k, **i32) for _ in range(max(D - 1, 0))]
+        self.next_anc = [torch.empty(Bn, k, dtype=torch.int64, device=dv) for _ in range(max(D - 1, 0))]
+        self.tree_state = torch.empty(B.tree_state_size(Bn, k, D), dtype=torch.uint8, device=dv)
+        self.v_tok = torch.empty(Bn, m + 1, **i32)
+        self.v_parent = torch.empty(Bn, m + 1, **i32)
+        self.v_depth = torch.empty(Bn, m + 1, **i32)
+        self.v_pos = torch.empty(Bn, m + 1, **i32)
+        self.v_anc = torch.empty(Bn, m + 1, dtype=torch.int64, device=dv)
+        self.accept_len = torch.empty(Bn, **i32)
+        self.accepted = torch.empty(Bn, D, **i32)
+        self.bonus = torch.empty(Bn, **i32)
+        self.status = torch.empty(Bn, **i32)
+        self.commit_logits = None
+        self.round_logits = None
+
+    def keep_logits(self, vocab, device="cuda"):
+        """Also write LM-head logits (for parity checks; not on the hot path)."""
+        Bn, k, D = self.spec.batch, self.spec.k, self.spec.depth
+        self.commit_logits = torch.empty(Bn, 1, vocab, dtype=torch.float32, device=device)
+        self.round_logits = [torch.empty(Bn, k, vocab, dtype=torch.float32, device=device)
+                             for _ in range(max(D - 1, 0))]
+
+
+class KVCache:
+    """Committed KV (contiguous or paged) + tree slots, as an eagle3_kv."""
+
+    def __init__(self, k, v, tk, tv, ctx_len, cap=0, block_table=None, block_size=16):
+        self.k, self.v, self.tk, self.tv = k, v, tk, tv
+        self.ctx_len = ctx_len
+        self.block_table = block_table
+        self.cap = cap
+        self.block_size = block_size
+
+    def struct(self, ctx_len=None):
+        cl = self.ctx_len if ctx_len is None else ctx_len
+        bt = self.block_table
+        return B.KV(self.k.data_ptr(), self.v.data_ptr(), self.cap,
+                    bt.data_ptr() if bt is not None else None,
+                    bt.shape[1] if bt is not None else 0, self.block_size if bt is not None else 0,
+                    cl.data_ptr(), self.tk.data_ptr(), self.tv.data_ptr())
+
+
+def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit_pos, ctx_after,
+              root_tok, root_pos, target_logits=None, mode=B.GREEDY, temperature=1.0, u_try=None,
+              u_res=None, verify=True):
+    """Enqueue one cycle.  feats [B*n,3,d], tokens/commit_pos [B,n] int32,
+    ctx_after [B] (committed rows incl. the new ones), root_tok/root_pos [B]."""
+    sp = buf.spec
+    Bn, n, k, D, m = sp.batch, sp.commit_rows, sp.k, sp.depth, sp.keep
+    B.eagle3_fuse(dr.dims, dr.weights, feats, Bn * n, buf.g)
+    kv_commit = kv.struct()
+    kv_tree = kv.struct(ctx_after)
+    B.eagle3_draft_step(dr.dims, dr.weights, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos,
+                        None, 0, k, B.TOPK_LAST, buf.h_tree, buf.root_ids, buf.root_lp,
+                        buf.commit_logits, buf.ws)
+    B.eagle3_tree_expand(B.INIT, Bn, k, D, m, root_tok, root_pos, buf.tree_state, buf.root_ids, buf.root_lp,
+                         buf.next_tok[0] if D > 1 else buf.v_tok, buf.next_par[0] if D > 1 else buf.v_tok,
+                         buf.next_pos[0] if D > 1 else buf.v_tok, buf.next_anc[0] if D > 1 else buf.v_anc)
+    for j in range(2, D + 1):
+        r = j - 2
+        B.eagle3_draft_step(dr.dims, dr.weights, kv_tree, B.TREE, Bn, k, None, buf.next_par[r],
+                            buf.next_tok[r], buf.next_pos[r], buf.next_anc[r], r * k, k, B.TOPK_ALL,
+                            buf.h_tree, buf.round_ids[r], buf.round_lp[r],
+                            buf.round_logits[r] if buf.round_logits is not None else None, buf.ws)
+        nr = r + 1 if j < D else r  # the last STEP emits no rows (buffers unused)
+        B.eagle3_tree_expand(B.STEP, Bn, k, D, m, None, None, buf.tree_state, buf.round_ids[r],
+                             buf.round_lp[r], buf.next_tok[nr], buf.next_par[nr], buf.next_pos[nr],
+                             buf.next_anc[nr])
+    B.eagle3_tree_expand(B.FINAL, Bn, k, D, m, None, None, buf.tree_state, None, None, None, None, None, None,
+                         buf.v_tok, buf.v_parent, buf.v_depth, buf.v_pos, buf.v_anc)
+    if verify and target_logits is not None:
+        B.eagle3_verify(Bn, m, dr.shape.vocab, D, buf.v_tok, buf.v_parent, target_logits, mode, temperature,
+                        u_try, u_res, buf.accept_len, buf.accepted, buf.bonus, buf.status)

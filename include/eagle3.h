@@ -1,0 +1,262 @@
+/*
+ * eagle3.h -- C ABI of the MI355X (gfx950) EAGLE-3 draft-and-verify library.
+ *
+ * The method: "EAGLE-3 精读" (edgeai1 speculative-decoding knowledge base)
+ *   §1 为什么推翻 feature regression -- low/mid/high target features are
+ *      concatenated to 3d and projected to d (g); a one-layer draft decoder
+ *      combines g, its own state and the token embedding; the target model
+ *      and its LM head are frozen.
+ *   §2 Training-Time Test -- ~5 self-fed rollout steps trained in one graph
+ *      under a special attention mask; inference uses EAGLE-2's
+ *      confidence-value dynamic tree and strict target verification.
+ *   §5 正确性、复现与风险 -- the standard verifier keeps the greedy sequence
+ *      or the sampling distribution if the residual correction is kept.
+ * EAGLE-4 blog (10100.com), 几条技术路线正在收敛 -- tree confidence is the
+ *   product of draft probabilities.  "EAGLE-3" quote page (scholarfeed) --
+ *   every added tree depth is one more sequential drafter round.
+ *
+ * Conventions (all entry points)
+ *  - Every pointer argument that names a tensor is DEVICE memory owned by
+ *    the caller, row-major and contiguous, unless stated otherwise.  Struct
+ *    arguments (eagle3_dims, eagle3_weights, eagle3_kv) are HOST memory read
+ *    during the call only.  The library never allocates and keeps no state
+ *    between calls: scratch memory comes from a caller workspace sized by
+ *    the *_size queries, tree state lives in a caller buffer.
+ *  - Each call validates its arguments on the host, then only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream).  No
+ *    call synchronises or copies to the host.  Enqueued work never uses
+ *    hipMemset*, so every call may be captured into a HIP graph.
+ *  - Types: activations, weights and KV are float32 (EAGLE3_F32) or
+ *    bfloat16 (EAGLE3_BF16, raw 16-bit patterns) as `dims->dtype` says;
+ *    residual stream, logits, log-probs, scores and CE are float32;
+ *    verification uniforms are float64; ids and indices are int32; tree
+ *    masks are uint64 bitsets.  Matrices are [out, in] row-major.
+ *  - Errors: every call returns 0 (EAGLE3_OK) or a negative code.  Argument
+ *    errors are detected before anything is launched; eagle3_last_error()
+ *    gives a thread-local message for the most recent failure.
+ *  - Calls that share a workspace or tree-state buffer must be ordered on
+ *    one stream; concurrent calls on one buffer race.
+ */
+#ifndef EAGLE3_H
+#define EAGLE3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define EAGLE3_OK 0
+#define EAGLE3_EINVAL (-1)       /* NULL pointer, bad size, dtype mismatch          */
+#define EAGLE3_ECAPACITY (-2)    /* (D-1)k > 64 tree slots, m+1 > 64, k > 16, ...   */
+#define EAGLE3_EUNSUPPORTED (-3) /* a shape the kernels do not handle (see each call)*/
+#define EAGLE3_EWORKSPACE (-4)   /* workspace smaller than the size query returned  */
+#define EAGLE3_EHIP (-5)         /* a HIP launch failed                             */
+#define EAGLE3_ENUMERIC (-6)     /* NaN in target logits (written per request)      */
+
+/* ---- enums ------------------------------------------------------------- */
+#define EAGLE3_F32 0
+#define EAGLE3_BF16 1
+
+#define EAGLE3_COMMIT 0 /* draft_step: append committed rows (causal)        */
+#define EAGLE3_TREE 1   /* draft_step: one row per frontier node (tree mask) */
+
+#define EAGLE3_TOPK_ALL 0  /* top-k of every row                           */
+#define EAGLE3_TOPK_LAST 1 /* top-k of the last row of each request only   */
+
+#define EAGLE3_INIT 0  /* tree_expand: root's top-k -> depth-1 nodes  */
+#define EAGLE3_STEP 1  /* tree_expand: one expansion round            */
+#define EAGLE3_FINAL 2 /* tree_expand: top-m rerank -> verify tree    */
+
+#define EAGLE3_GREEDY 0
+#define EAGLE3_SAMPLE 1
+
+#define EAGLE3_MAX_TREE_SLOTS 64 /* drafted tree rows per request per cycle */
+#define EAGLE3_MAX_TOPK 16
+#define EAGLE3_MAX_ROWS 64 /* query rows per request per draft_step */
+
+typedef void *eagle3_stream_t; /* hipStream_t */
+
+/* Drafter dimensions.  head_dim must be 64 or 128; n_q_heads a multiple of
+ * n_kv_heads (q-head h reads KV head floor(h*n_kv_heads/n_q_heads)).  With
+ * dtype BF16 every GEMM K (3d, 2d, n_q_heads*head_dim, ffn) must be a
+ * multiple of 32 and d a multiple of 16; ffn a multiple of 8.  rms_eps is
+ * the RMSNorm epsilon; rope_theta the rotary base (rotate-half form). */
+typedef struct eagle3_dims {
+  int32_t d, n_q_heads, n_kv_heads, head_dim, ffn, vocab, dtype;
+  float rms_eps, rope_theta;
+} eagle3_dims;
+
+/* Drafter weights (device, dtype of dims, [out, in] row-major):
+ *  fc      [d, 3d]           fusion projection (rows: output features; the
+ *                            3d inputs are [f_low | f_mid | f_high])
+ *  emb     [vocab, d]        frozen target token embedding
+ *  qkv     [(Hq+2Hkv)hd, 2d] rows: Hq*hd query, Hkv*hd key, Hkv*hd value;
+ *                            the 2d inputs are [rms(emb[t]) | rms(s)]
+ *  o       [d, Hq*hd]
+ *  gate_up [2*ffn, d]        rows 0..ffn-1 gate, ffn..2ffn-1 up
+ *  down    [d, ffn]
+ *  lm      [vocab, d]        frozen target LM head
+ *  norm_*  [d] float32       RMSNorm gains (embedding, state, FFN, output) */
+typedef struct eagle3_weights {
+  const void *fc, *emb, *qkv, *o, *gate_up, *down, *lm;
+  const float *norm_e, *norm_s, *norm_ffn, *norm_out;
+} eagle3_weights;
+
+/* Draft KV cache of a batch of requests (device, dtype of dims).
+ *  k, v        committed keys/values (after RoPE).  Contiguous when
+ *              block_table == NULL: [B][cap][Hkv][hd], row p = position p.
+ *              Paged otherwise: a pool [n_blocks][block_size][Hkv][hd];
+ *              logical row p of request b lives in block
+ *              block_table[b*max_blocks + p/block_size], offset p%block_size.
+ *  ctx_len     [B] int32: committed rows of each request before this call.
+ *  tk, tv      tree slots [B][64][Hkv][hd] (one slot per drafted tree row). */
+typedef struct eagle3_kv {
+  void *k, *v;
+  int32_t cap;
+  const int32_t *block_table;
+  int32_t max_blocks, block_size;
+  const int32_t *ctx_len;
+  void *tk, *tv;
+} eagle3_kv;
+
+/* Message for a return code (static string). */
+const char *eagle3_strerror(int code);
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char *eagle3_last_error(void);
+/* Library version string. */
+const char *eagle3_version(void);
+
+/* Workspace bytes needed by eagle3_fuse / eagle3_draft_step / eagle3_topk for
+ * batch B with at most max_rows query rows per request (fuse: n = B*max_rows
+ * feature rows).  Contiguous KV prefixes up to max_ctx rows (paged: the
+ * largest logical length) are covered. */
+int eagle3_workspace_size(const eagle3_dims *dims, int B, int max_rows, int max_ctx,
+                          size_t *bytes);
+
+/* Bytes of tree state for B requests, top-k k and depth D. */
+int eagle3_tree_state_size(int B, int k, int D, size_t *bytes);
+
+/* Workspace bytes needed by eagle3_ttt_forward for B sequences of S tokens
+ * and R rollout steps. */
+int eagle3_ttt_workspace_size(const eagle3_dims *dims, int B, int S, int R, size_t *bytes);
+
+/* Step 1 -- multi-layer feature fusion ("EAGLE-3 精读" §1):
+ *   g[i] = [f_low(i) ; f_mid(i) ; f_high(i)] . fc^T       (no bias, no norm)
+ * feats [n][3][d] (dtype), g [n][d] (dtype; bf16 rounds once, RNE).
+ * fp32 accumulation.  n >= 1; up to 64 rows use the weight-streaming kernel,
+ * more rows the tiled MFMA GEMM (bf16 only). */
+int eagle3_fuse(const eagle3_dims *dims, const eagle3_weights *w, const void *feats, int n,
+                void *g, void *ws, size_t ws_bytes, eagle3_stream_t stream);
+
+/* Step 2+3 -- one drafter round ("EAGLE-3 精读" §1; the quote page: one
+ * sequential drafter round per tree depth), then the LM head and per-row
+ * top-k with log-probabilities.
+ *
+ * Per query row (b, r) with state s, token t, position p:
+ *   x = [rms(emb[t])*norm_e ; rms(s)*norm_s]; q,k,v = qkv.x; RoPE(q,k,p)
+ *   a = softmax(q k^T / sqrt(hd)) v over the visible keys (GQA)
+ *   h1 = s + o.a ; h2 = h1 + down.(silu(gate.u) * up.u), u = rms(h1)*norm_ffn
+ *   logits = lm.(rms(h2)*norm_out)
+ * bf16 workloads round x, q/k/v (after RoPE), a, u, silu(gate)*up and
+ * rms(h2) to bf16; s, h1, h2 stay float32.
+ *
+ * mode COMMIT: rows r = 0..rows-1 of request b are new committed rows; row r
+ *   writes its k/v at cache row ctx_len[b]+r and sees cache rows
+ *   0..ctx_len[b]+r.  state = [B][rows][d] (dtype; normally g).  The last
+ *   row's h2 is written to h_tree[b][0] (the root state).  parent_slot, anc
+ *   unused (may be NULL).
+ * mode TREE: row r of request b is a drafted tree node; state = NULL and s =
+ *   h_tree[b][parent_slot[b][r]] (0 = root, 1+j = tree slot j).  It writes
+ *   its k/v to tree slot slot_base+r, sees cache rows 0..ctx_len[b]-1 and
+ *   every tree slot j with bit j of anc[b][r] set (its ancestors and itself),
+ *   and writes h2 to h_tree[b][1+slot_base+r].  slot_base+rows <= 64.
+ * tokens, pos [B][rows] int32.  h_tree [B][65][d] float32.
+ * k in 1..16; topk_rows ALL -> topk_id/topk_lp [B][rows][k], LAST ->
+ *   [B][1][k].  Order: logit desc, token id asc; lp = logit - logsumexp in
+ *   float32.
+ * logits_out: optional (NULL) float32 [B][rows or 1][vocab] copy of the
+ *   logits of the rows whose top-k is taken.
+ * Requires rows <= 64, head_dim in {64,128}; paged KV requires bf16. */
+int eagle3_draft_step(const eagle3_dims *dims, const eagle3_weights *w, const eagle3_kv *kv,
+                      int mode, int B, int rows, const void *state, const int32_t *parent_slot,
+                      const int32_t *tokens, const int32_t *pos, const uint64_t *anc,
+                      int slot_base, int k, int topk_rows, float *h_tree, int32_t *topk_id,
+                      float *topk_lp, float *logits_out, void *ws, size_t ws_bytes,
+                      eagle3_stream_t stream);
+
+/* Step 3b -- EAGLE-2 confidence-value dynamic tree and rerank ("EAGLE-3 精读"
+ * §2; EAGLE-4 blog, 几条技术路线正在收敛: confidence = product of draft
+ * probabilities, kept here as a float32 sum of log-probs).
+ *
+ * INIT: topk_id/topk_lp [B][1][k] are the root's top-k; they become the
+ *   depth-1 nodes (score = lp) and the frontier.  root_tok/root_pos [B] are
+ *   stored.  Emits the frontier rows for the next TREE draft step.
+ * STEP: topk_id/topk_lp [B][k][k] are the top-k of the k frontier rows (row
+ *   rho = frontier rank rho).  Every child gets score = score(parent) + lp
+ *   (one float32 add) and flat index rho*k+i; all k*k join the pool; the new
+ *   frontier is the first k by (score desc, flat asc).  Unless the new depth
+ *   equals D, emits the frontier rows.
+ *   Frontier rows (INIT/STEP) -> next_tok, next_parent_slot (h_tree index of
+ *   the parent), next_pos (root_pos + depth), next_anc (parent's bitset plus
+ *   the node's own tree slot (depth-1)*k + rank), each [B][k].
+ * FINAL: keeps the first m pool nodes by (score desc, depth asc, flat asc) --
+ *   a set closed under ancestors -- and writes the verify tree in canonical
+ *   order (root 0, then by depth, parent's index, child rank): v_tok,
+ *   v_parent (-1 for the root), v_depth, v_pos [B][m+1] int32 and v_anc
+ *   [B][m+1] (bit i set iff verify node i is an ancestor-or-self).
+ * Limits: k <= 16, (D-1)*k <= 64, m+1 <= 64, m <= k + (D-1)k^2. */
+int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t *root_tok,
+                       const int32_t *root_pos, void *tree_state, const int32_t *topk_id,
+                       const float *topk_lp, int32_t *next_tok, int32_t *next_parent_slot,
+                       int32_t *next_pos, uint64_t *next_anc, int32_t *v_tok, int32_t *v_parent,
+                       int32_t *v_depth, int32_t *v_pos, uint64_t *v_anc,
+                       eagle3_stream_t stream);
+
+/* Step 4 -- strict target verification ("EAGLE-3 精读" §5), one kernel that
+ * walks each request's tree.
+ * v_tok, v_parent [B][m+1] (canonical order as emitted by FINAL);
+ * target_logits [B][m+1][V] float32 (row i = target logits after node i).
+ * GREEDY: at each node t* = argmax (lowest id on ties); follow the child
+ *   whose token is t*, else stop: bonus = t*.
+ * SAMPLE (temperature T > 0): float64 weights w(y) = exp((L-max)/T) and
+ *   remaining mass Rm; child c (sibling order) is accepted iff u_try[c]*Rm <
+ *   w(tok c), otherwise its token leaves the support (Rm -= w).  With no
+ *   child accepted the bonus is the smallest token y outside the rejected set
+ *   whose cumulative weight in id order exceeds u_res[node]*Rm (if rounding
+ *   leaves none: the last y with w > 0).  u_try, u_res [B][m+1] float64.
+ * Outputs: accept_len [B], accepted [B][Dmax] (verify-node indices, -1
+ * padded), bonus [B], status [B] (0, or EAGLE3_ENUMERIC when a visited row
+ * holds a NaN; -inf logits mean probability 0). */
+int eagle3_verify(int B, int m, int V, int Dmax, const int32_t *v_tok, const int32_t *v_parent,
+                  const float *target_logits, int mode, float temperature, const double *u_try,
+                  const double *u_res, int32_t *accept_len, int32_t *accepted, int32_t *bonus,
+                  int32_t *status, eagle3_stream_t stream);
+
+/* Step 5 -- training-time-test forward ("EAGLE-3 精读" §2 and §5).
+ * feats [B][S][3][d] (dtype), tokens [B][S].  Rows (j,i), j = 1..R: step 1
+ * feeds (g_i, x_i) at position i; step j >= 2 feeds h2(j-1,i) and the
+ * argmax token of (j-1,i) (or forced_tokens[b][j-2][i] when forced_tokens
+ * != NULL, [B][R-1][S]) at position i+j-1.  Query (j,i) sees step-1 keys
+ * i' <= i and its own chain keys (j',i), 2 <= j' <= j.
+ * Outputs: pred [B][R][S] (argmax of logits(j,i)), ce [B][R][S] = logsumexp
+ * - logit[x_{i+j}] where i+j <= S-1 (0 elsewhere), loss[0] = mean of the
+ * valid ce.  Logits are never materialised.  Requires dtype BF16, head_dim
+ * 128 or 64, S a multiple of 64. */
+int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const void *feats,
+                       const int32_t *tokens, int B, int S, int R, const int32_t *forced_tokens,
+                       int32_t *pred, float *ce, float *loss, void *ws, size_t ws_bytes,
+                       eagle3_stream_t stream);
+
+/* The top-k/log-prob reduction of eagle3_draft_step on caller logits:
+ * logits [rows][V] float32 -> ids [rows][k], lp [rows][k], lse [rows] (lse
+ * may be NULL).  Same order and tie rule.  k in 1..16. */
+int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float *lp, float *lse,
+                void *ws, size_t ws_bytes, eagle3_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE3_H */

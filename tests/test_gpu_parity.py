@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Discrete outputs (ids, tree, accepted nodes, bonus) are
+bit-exact; floats within the stated tolerances."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import eagle3_oracle as O
+from workloads import gen
+from workloads.configs import BF16, C1_TINY, F32, scaled, tiny_shape
+
+from gpu_cases import GpuCycle, dev_i32, host_weights, oracle_cycle, say, topk_agrees
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4          # fp32 drafter vs fp64 oracle
+TOL_BF16 = (2e-2, 1e-2)  # bf16 logits / fusion: atol, rtol
+
+
+# ---------------------------------------------------------------- fusion
+@pytest.mark.parametrize("n", [1, 10, 64, 130])
+def test_fuse_bf16(lib, n):
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.cycle import Drafter
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=1024, dtype=BF16)
+    Wt = gen.gen_weights(shape, seed=0)
+    say("fuse bf16 n", n)
+    dr = Drafter(shape, Wt)
+    feats = gen.draw(5, 1, (n, 3, 256), 1.0, BF16)
+    g = torch.empty(n, 256, dtype=torch.bfloat16, device="cuda")
+    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), n, g)
+    torch.cuda.synchronize()
+    ref = O.fuse(shape, feats.f32(), Wt["fc"].f32())
+    np.testing.assert_allclose(g.float().cpu().numpy(), ref, atol=TOL_BF16[0], rtol=TOL_BF16[1])
+
+
+def test_fuse_fp32_tiny(lib):
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.cycle import Drafter
+    shape = C1_TINY.shape
+    Wt = gen.gen_weights(shape, seed=0)
+    dr = Drafter(shape, Wt)
+    feats = gen.draw(1, 11, (64, 3, 256), 1 / 16, F32)
+    g = torch.empty(64, 256, dtype=torch.float32, device="cuda")
+    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), 64, g)
+    torch.cuda.synchronize()
+    ref = O.fuse(shape, feats.f32(), Wt["fc"].f32())
+    np.testing.assert_allclose(g.cpu().numpy(), ref, atol=TOL_F32, rtol=TOL_F32)
+
+
+# ---------------------------------------------------------------- top-k
+@pytest.mark.parametrize("V,k,rows", [(128256, 10, 10), (128256, 1, 3), (4096, 2, 5), (1000, 16, 4), (128256, 16, 2)])
+def test_topk(lib, V, k, rows):
+    from eagle_draft_tree_amd import binding as Bd
+    say("topk", V, k, rows)
+    g = np.random.default_rng(V + k)
+    L = (g.standard_normal((rows, V)) * 2).astype(np.float32)
+    L[:, 5] = L[:, 7] = L.max(axis=1) + 0.5        # exact tie at the top: lower id first
+    L[0, V - 1] = L[0, 5]                          # three-way tie across partitions
+    if rows > 1:
+        L[1, :] = np.round(L[1, :], 1)             # many ties everywhere
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    ids = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+    lp = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    Bd.eagle3_topk(torch.as_tensor(L).cuda(), rows, V, k, ids, lp, lse, ws)
+    torch.cuda.synchronize()
+    for r in range(rows):
+        o_ids, o_lp, o_lse = O.topk_logprobs(L[r], k)
+        np.testing.assert_array_equal(ids[r].cpu().numpy(), o_ids)
+        np.testing.assert_allclose(lp[r].cpu().numpy(), o_lp, atol=1e-4, rtol=0)
+        assert abs(lse[r].item() - float(o_lse)) < 1e-4
+
+
+# ---------------------------------------------------------------- tree expansion
+@pytest.mark.parametrize("k,D,m,Bn,ties", [(10, 6, 60, 1, 0), (2, 3, 8, 3, 2), (4, 5, 30, 2, 2), (1, 3, 3, 4, 0),
+                                           (16, 5, 63, 1, 3), (3, 4, 20, 2, 1)])
+def test_tree_expand(lib, k, D, m, Bn, ties):
+    from eagle_draft_tree_amd import binding as Bd
+    say("tree", k, D, m, Bn, ties)
+    V = 5000
+    i32 = dict(dtype=torch.int32, device="cuda")
+    state = torch.empty(Bd.tree_state_size(Bn, k, D), dtype=torch.uint8, device="cuda")
+    root_tok = np.arange(Bn, dtype=np.int32) + 7
+    root_pos = np.arange(Bn, dtype=np.int32) * 100 + 50
+    trees = [O.DynamicTree(k, D, root_tok[b], root_pos[b]) for b in range(Bn)]
+    ids0, lp0 = gen.random_topk_rows(k * 1000 + D, Bn, k, V, tie_every=ties)
+    nt = torch.empty(Bn, k, **i32); npar = torch.empty(Bn, k, **i32)
+    npos = torch.empty(Bn, k, **i32); nanc = torch.empty(Bn, k, dtype=torch.int64, device="cuda")
+    Bd.eagle3_tree_expand(Bd.INIT, Bn, k, D, m, dev_i32(root_tok), dev_i32(root_pos), state,
+                          dev_i32(ids0), torch.as_tensor(lp0).cuda(), nt, npar, npos, nanc)
+    for b in range(Bn):
+        trees[b].init(ids0[b], lp0[b])
+
+    def check_rows():
+        torch.cuda.synchronize()
+        for b in range(Bn):
+            rows = trees[b].next_rows()
+            np.testing.assert_array_equal(nt[b].cpu().numpy(), [r[0] for r in rows])
+            np.testing.assert_array_equal(npar[b].cpu().numpy(), [r[1] for r in rows])
+            np.testing.assert_array_equal(npos[b].cpu().numpy(), [r[2] for r in rows])
+            np.testing.assert_array_equal(nanc[b].cpu().numpy().view(np.uint64),
+                                          np.array([r[3] for r in rows], dtype=np.uint64))
+    if D > 1:
+        check_rows()
+    for j in range(2, D + 1):
+        ids, lp = gen.random_topk_rows(k * 1000 + D * 10 + j, Bn * k, k, V, tie_every=ties)
+        if ties:  # ties across rows as well: equal log-probs in different rows
+            lp[1::2] = lp[0::2][: len(lp[1::2])]
+        Bd.eagle3_tree_expand(Bd.STEP, Bn, k, D, m, None, None, state, dev_i32(ids),
+                              torch.as_tensor(lp).cuda(), nt, npar, npos, nanc)
+        for b in range(Bn):
+            trees[b].step(ids[b * k:(b + 1) * k], lp[b * k:(b + 1) * k])
+        if j < D:
+            check_rows()
+    vt = {n: torch.empty(Bn, m + 1, **i32) for n in ("tok", "parent", "depth", "pos")}
+    vanc = torch.empty(Bn, m + 1, dtype=torch.int64, device="cuda")
+    Bd.eagle3_tree_expand(Bd.FINAL, Bn, k, D, m, None, None, state, None, None, None, None, None, None,
+                          vt["tok"], vt["parent"], vt["depth"], vt["pos"], vanc)
+    torch.cuda.synchronize()
+    for b in range(Bn):
+        ref = trees[b].final(m)
+        for n in ("tok", "parent", "depth", "pos"):
+            np.testing.assert_array_equal(vt[n][b].cpu().numpy(), ref[n], err_msg=n)
+        np.testing.assert_array_equal(vanc[b].cpu().numpy().view(np.uint64), ref["anc"])
+
+
+# ---------------------------------------------------------------- verification
+def _run_verify(Bn, m, V, tok, par, L, mode, T=1.0, ut=None, ur=None, Dmax=None):
+    from eagle_draft_tree_amd import binding as Bd
+    Dmax = Dmax or m + 1
+    i32 = dict(dtype=torch.int32, device="cuda")
+    al = torch.empty(Bn, **i32); acc = torch.empty(Bn, Dmax, **i32)
+    bo = torch.empty(Bn, **i32); st = torch.empty(Bn, **i32)
+    Bd.eagle3_verify(Bn, m, V, Dmax, dev_i32(tok), dev_i32(par), torch.as_tensor(L).cuda(), mode, T,
+                     torch.as_tensor(ut).cuda() if ut is not None else None,
+                     torch.as_tensor(ur).cuda() if ur is not None else None, al, acc, bo, st)
+    torch.cuda.synchronize()
+    return al.cpu().numpy(), acc.cpu().numpy(), bo.cpu().numpy(), st.cpu().numpy()
+
+
+@pytest.mark.parametrize("V,m,depth,Bn,mode,T", [
+    (128256, 60, 6, 2, "greedy", 1.0), (4096, 8, 3, 4, "greedy", 1.0), (4096, 8, 3, 4, "sample", 1.0),
+    (128256, 60, 6, 2, "sample", 1.0), (50, 20, 4, 8, "sample", 0.7), (7, 5, 3, 16, "sample", 1.3),
+    (128256, 3, 3, 64, "greedy", 1.0)])
+def test_verify(lib, V, m, depth, Bn, mode, T):
+    from eagle_draft_tree_amd import binding as Bd
+    say("verify", V, m, depth, Bn, mode, T)
+    toks, pars = [], []
+    for b in range(Bn):
+        t, p = gen.random_verify_tree(V * 7 + b, m, V, depth)
+        toks.append(t); pars.append(p)
+    toks, pars = np.array(toks), np.array(pars)
+    L = gen.target_logits(V + m, Bn, m + 1, V, 3.0)
+    gen.plant_agreement(L, toks, pars, np.full(Bn, 0.8), seed=V + m)
+    ut, ur = gen.uniforms(V + m, Bn, m + 1)
+    md = Bd.GREEDY if mode == "greedy" else Bd.SAMPLE
+    al, acc, bo, st = _run_verify(Bn, m, V, toks, pars, L, md, T, ut, ur)
+    for b in range(Bn):
+        if mode == "greedy":
+            ra, rb = O.verify_greedy(toks[b], pars[b], L[b])
+        else:
+            ra, rb = O.verify_sample(toks[b], pars[b], L[b], ut[b], ur[b], T)
+        assert st[b] == 0
+        assert al[b] == len(ra), (b, al[b], ra)
+        assert list(acc[b][: al[b]]) == ra
+        assert bo[b] == rb
+
+
+def test_verify_golden(lib):
+    import json, os
+    from eagle_draft_tree_amd import binding as Bd
+    with open(os.path.join(os.path.dirname(__file__), "golden", "verify_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        L = np.array(c["logits"], np.float32)[None]
+        tok = np.array(c["tok"])[None]; par = np.array(c["parent"])[None]
+        m = len(c["tok"]) - 1
+        if c["mode"] == "greedy":
+            al, acc, bo, st = _run_verify(1, m, L.shape[2], tok, par, L, Bd.GREEDY)
+        else:
+            al, acc, bo, st = _run_verify(1, m, L.shape[2], tok, par, L, Bd.SAMPLE, c.get("T", 1.0),
+                                          np.array(c["u_try"])[None], np.array(c["u_res"])[None])
+        assert list(acc[0][: al[0]]) == c["expect_accepted"], c["name"]
+        assert bo[0] == c["expect_bonus"], c["name"]
+
+
+def test_verify_nan_and_neg_inf(lib):
+    from eagle_draft_tree_amd import binding as Bd
+    V = 300
+    tok, par = gen.random_verify_tree(1, 6, V, 3)
+    L = gen.target_logits(9, 2, 7, V, 2.0)
+    L[0, 0, 17] = np.nan                 # request 0: NaN in the root row
+    L[1, 0, :] = -np.inf                 # request 1: only token 3 possible at the root
+    L[1, 0, 3] = 0.0
+    toks = np.stack([tok, tok]); pars = np.stack([par, par])
+    ut, ur = gen.uniforms(9, 2, 7)
+    al, acc, bo, st = _run_verify(2, 6, V, toks, pars, L, Bd.SAMPLE, 1.0, ut, ur)
+    assert st[0] == Bd.ENUMERIC and st[1] == 0
+    ra, rb = O.verify_sample(tok, par, L[1], ut[1], ur[1])
+    assert al[1] == len(ra) and bo[1] == rb
+
+
+# ---------------------------------------------------------------- whole cycles
+def _cycle_and_oracle(w, seed=1):
+    Wt = gen.gen_weights(w.shape, seed=0)
+    W = host_weights(Wt)
+    ci = gen.gen_cycle_inputs(w, seed=seed)
+    return Wt, W, ci
+
+
+def _compare_cycle(gc, w, W, ci, tol, logit_check=True):
+    """Compare every stage of request 0..B-1; returns number of excused near-ties."""
+    excused = 0
+    buf = gc.buf
+    for b in range(w.batch):
+        vt, rec = oracle_cycle(w, W, ci, b)
+        atol, rtol = tol
+        g_gpu = buf.g.float().cpu().numpy()[b * w.commit_rows:(b + 1) * w.commit_rows]
+        np.testing.assert_allclose(g_gpu, rec["g"], atol=atol, rtol=rtol)
+        cl = buf.commit_logits[b, 0].cpu().numpy()
+        np.testing.assert_allclose(cl, rec["commit_logits"][-1], atol=atol, rtol=rtol)
+        np.testing.assert_allclose(buf.h_tree[b, 0].cpu().numpy(), rec["commit_h2"][-1], atol=atol, rtol=rtol)
+        exact, exc = topk_agrees(buf.root_ids[b, 0].cpu().numpy(), rec["commit_logits"][-1], w.topk, 2 * atol)
+        if not exact:
+            assert exc, "root top-k differs without a near-tie"
+            excused += 1
+            continue
+        diverged = False
+        for r, rd in enumerate(rec["rounds"]):
+            gl = buf.round_logits[r][b].cpu().numpy()
+            np.testing.assert_allclose(gl, rd["logits"], atol=atol, rtol=rtol)
+            for row in range(w.topk):
+                exact, exc = topk_agrees(buf.round_ids[r][b, row].cpu().numpy(), rd["logits"][row], w.topk,
+                                         2 * atol)
+                if not exact:
+                    assert exc, f"round {r} row {row} top-k differs without a near-tie"
+                    diverged = True
+            if diverged:
+                break
+        if diverged:
+            excused += 1
+            continue
+        t = gc.tree()
+        for n in ("tok", "parent", "depth", "pos"):
+            np.testing.assert_array_equal(t[n][b], vt[n], err_msg=n)
+        np.testing.assert_array_equal(t["anc"][b], vt["anc"])
+    return excused
+
+
+def test_c1_tiny_cycle_greedy_and_sample(lib):
+    w = C1_TINY
+    say("C1 cycle")
+    Wt, W, ci = _cycle_and_oracle(w)
+    gc = GpuCycle(w, Wt, ci)
+    L = gen.target_logits(1, 1, w.keep + 1, w.shape.vocab, w.target_sigma)
+    ut, ur = gen.uniforms(1, 1, w.keep + 1)
+    gc.run(L, 0)
+    assert _compare_cycle(gc, w, W, ci, (TOL_F32, TOL_F32)) == 0
+    vt, _ = oracle_cycle(w, W, ci)
+    ra, rb = O.verify_greedy(vt["tok"], vt["parent"], L[0])
+    assert gc.buf.accept_len[0].item() == len(ra) and gc.buf.bonus[0].item() == rb
+    # sampling verify on the same tree
+    gc.run(L, 1, 1.0, ut, ur)
+    ra, rb = O.verify_sample(vt["tok"], vt["parent"], L[0], ut[0], ur[0])
+    assert gc.buf.accept_len[0].item() == len(ra) and gc.buf.bonus[0].item() == rb
+    # planted agreement from the oracle's own tree exercises acceptance
+    Lp = gen.plant_agreement(L.copy(), vt["tok"][None], vt["parent"][None], np.array([0.9]), seed=5)
+    gc.run(Lp, 0)
+    ra, rb = O.verify_greedy(vt["tok"], vt["parent"], Lp[0])
+    assert len(ra) >= 1
+    assert gc.buf.accept_len[0].item() == len(ra) and gc.buf.bonus[0].item() == rb
+    acc = gc.buf.accepted[0].cpu().numpy()
+    assert list(acc[: len(ra)]) == ra
+
+
+def test_c1_cycle_is_deterministic(lib):
+    w = C1_TINY
+    Wt, W, ci = _cycle_and_oracle(w, seed=2)
+    gc = GpuCycle(w, Wt, ci)
+    gc.run()
+    a = [t.clone() for t in (gc.buf.h_tree, gc.buf.round_logits[0], gc.buf.v_tok)]
+    gc.run()
+    for x, y in zip(a, (gc.buf.h_tree, gc.buf.round_logits[0], gc.buf.v_tok)):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("hkv,commit,ctx", [(2, 24, 0), (1, 5, 40), (4, 1, 100)])
+def test_bf16_small_cycle(lib, hkv, commit, ctx):
+    """bf16 drafter (d=256) with synthetic prefix KV, multi-row commit and GQA."""
+    say("bf16 small cycle", hkv, commit, ctx)
+    shape = tiny_shape(d=256, hq=4, hkv=hkv, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
+    w = scaled(C1_TINY, shape=shape, depth=4, topk=3, keep=12, prefix=ctx, commit_rows=commit,
+               synthetic_prefix_kv=ctx > 0, feat_scale=1.0)
+    Wt, W, ci = _cycle_and_oracle(w, seed=3)
+    gc = GpuCycle(w, Wt, ci)
+    gc.run()
+    exc = _compare_cycle(gc, w, W, ci, TOL_BF16)
+    assert exc <= 1

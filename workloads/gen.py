@@ -265,8 +265,7 @@ def random_topk_rows(seed: int, rows: int, k: int, V: int, tie_every: int = 0):
     lp = np.empty((rows, k), dtype=np.float32)
     for r in range(rows):
         ids[r] = g.choice(V, size=k, replace=False)
-        v = -np.sort(g.exponential(1.5, size=k)).astype(np.float32)[::-1]
-        v = np.sort(v)[::-1].astype(np.float32)
+        v = np.sort(-g.exponential(1.5, size=k).astype(np.float32))[::-1].copy()
         if tie_every:
             for i in range(1, k):
                 if g.integers(tie_every) == 0:
@@ -287,7 +286,6 @@ def random_verify_tree(seed: int, m: int, V: int, depth: int, root_tok: int = 0)
         p = int(g.choice(cand))
         parents.append(p)
         depths.append(depths[p] + 1)
-    order = sorted(range(1, m + 1), key=lambda i: (depths[i], 0))
     # canonicalise: BFS by depth, children grouped by parent's new index
     new_index = {0: 0}
     out_par = [-1]
