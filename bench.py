@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: EAGLE-3 draft-tree cycles on one MI355X.
+
+One step = one full draft-tree cycle of the Llama-3.1-8B-shaped drafter at
+batch 1 (d=4096, 32/8 heads x 128, SwiGLU 14336, vocab 128256, bf16 weights,
+fp32 accumulation; prefix KV 2048): fusion of the root's 3-layer features,
+the COMMIT round, 5 tree rounds (top-10 each), dynamic-tree expansion and
+top-60 rerank, and greedy verification against synthetic target logits
+(N(0,3), planted argmax agreement 0.8).  Inputs sit in HBM before timing.
+
+Prints one JSON line: draft-tree steps/s (value), verified tokens/s, the LM
+head's HBM roofline (the dominant kernel; bytes/launch / HIP-event-measured
+launch time), the whole cycle's algorithmic-bytes roofline, a per-kernel-class
+breakdown, and the CPU oracle timed on the host (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10)
+
+
+def kernel_source_hash():
+    """Hash of the sources that build the LM-head kernel (for the traffic record)."""
+    h = hashlib.sha256()
+    for f in ("gemm_rows.hpp", "draft.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "eagle_draft_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, src_hash):
+    """Counter-measured HBM bytes per LM-head launch, if recorded for these sources."""
+    path = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(workload)
+    if not r or r.get("source_hash") != src_hash:
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
+    """The oracle as it stands: one full cycle of request 0 on the host cores."""
+    import numpy as np
+
+    from oracle import eagle3_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    n = w.commit_rows
+    Kc = ci.kv_k.f32()[0].astype(np.float64)
+    Vc = ci.kv_v.f32()[0].astype(np.float64)
+    t0 = time.time()
+    O.draft_cycle(w.shape, W, ci.feats.f32()[:n], ci.tokens[0], Kc, Vc, int(ci.ctx_len[0]), w.topk, w.depth,
+                  w.keep)
+    dt = time.time() - t0
+    try:
+        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except Exception:
+        model = "unknown"
+    return {"value": 1.0 / dt, "unit": "draft-tree steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full cycle (fuse + commit + {w.depth - 1} tree rounds + rerank) of request 0, "
+                      f"fp64 NumPy, {dt:.1f} s; cpu_count={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}, {model}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.cycle import CycleBuffers, CycleSpec, Drafter, KVCache, run_cycle
+    from workloads import gen
+    from workloads.configs import C2_8B_TREE
+
+    w = C2_8B_TREE
+    s = w.shape
+    Bd.load()
+    t0 = time.time()
+    Wt = gen.gen_weights(s, seed=0)
+    ci = gen.gen_cycle_inputs(w, seed=1)
+    dr = Drafter(s, Wt)
+    Bn, n, k, D, m = w.batch, w.commit_rows, w.topk, w.depth, w.keep
+    spec = CycleSpec(Bn, n, k, D, m, ci.cap)
+    buf = CycleBuffers(dr, spec)
+    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    tk = torch.zeros(Bn, Bd.MAX_TREE_SLOTS, s.n_kv_heads, s.head_dim, dtype=torch.bfloat16, device="cuda")
+    kv = KVCache(ci.kv_k.torch("cuda"), ci.kv_v.torch("cuda"), tk, torch.zeros_like(tk), i32(ci.ctx_len),
+                 cap=ci.cap)
+    ctx_after = i32(ci.ctx_len + n)
+    feats = ci.feats.torch("cuda")
+    tokens = i32(ci.tokens)
+    pos = i32(ci.ctx_len[:, None] + np.arange(n)[None, :])
+    root_tok = i32(ci.tokens[:, -1])
+    root_pos = i32(ci.ctx_len + n - 1)
+    setup_s = time.time() - t0
+
+    def cycle(L):
+        run_cycle(dr, buf, kv, feats, tokens, pos, ctx_after, root_tok, root_pos, L, Bd.GREEDY)
+
+    # first cycle: plant agreement into the target logits along the drafted tree
+    cycle(None)
+    torch.cuda.synchronize()
+    L = gen.target_logits(1, Bn, m + 1, s.vocab, w.target_sigma)
+    gen.plant_agreement(L, buf.v_tok.cpu().numpy(), buf.v_parent.cpu().numpy(), ci.accept_prob, seed=1)
+    Ld = torch.as_tensor(L).cuda()
+    for _ in range(max(args.warmup - 1, 0)):
+        cycle(Ld)
+    torch.cuda.synchronize()
+
+    launches_per_cycle = D + 2
+    for c in KC.values():
+        Bd.timing_enable(c, launches_per_cycle * (args.steps + 1))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        cycle(Ld)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_class = {}
+    for name, c in KC.items():
+        per_class[name] = Bd.timing_read(c)
+        Bd.timing_enable(c, 0)
+    ms_per_step = total_ms / args.steps
+    cycles_per_s = 1000.0 / ms_per_step
+    acc = buf.accept_len.cpu().numpy()
+    tokens_per_cycle = float(np.mean(acc + 1)) * Bn
+    assert int(buf.status.cpu().numpy().max()) == 0
+
+    # algorithmic bytes (bf16 weights read once per round, KV read once per round)
+    es = 2
+    d, F, V, hq, hkv, hd = s.d, s.ffn, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim
+    w_fc = d * 3 * d * es
+    w_layer = ((hq + 2 * hkv) * hd * 2 * d + d * hq * hd + 2 * F * d + d * F) * es
+    w_lm = V * d * es
+    ctx = int(ci.ctx_len[0]) + n
+    kv_round = ctx * hkv * hd * 2 * es
+    bytes_cycle = w_fc + D * (w_layer + w_lm + kv_round)
+    cycle_gbs = bytes_cycle / (ms_per_step * 1e-3) / 1e9
+
+    # LM head: bytes per launch (commit launch: 1 row; tree launches: k rows)
+    lm_bytes = [w_lm + 1 * d * es + 1 * V * 4] + [w_lm + k * d * es + k * V * 4] * (D - 1)
+    lm_ms, lm_cnt = per_class["lm_head"]
+    lm_bytes_total = sum(lm_bytes) * (lm_cnt // len(lm_bytes))
+    lm_gbs = lm_bytes_total / (lm_ms * 1e-3) / 1e9 if lm_ms > 0 else None
+    src_hash = kernel_source_hash()
+    traffic = load_traffic("llama3.1-8b-b1-tree", src_hash)
+
+    out = {
+        "metric": "draft-tree steps/s + verified tokens/s at 1 GPU; % peak HBM GB/s / MFMA",
+        "value": round(cycles_per_s, 2),
+        "unit": "draft-tree steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) features/KV, N(0,3) target logits planted 0.8)",
+        "config": {"workload": w.name, "batch": Bn, "prefix": int(ci.ctx_len[0]), "depth": D, "topk": k,
+                   "keep": m, "verify": "greedy", "graph": False},
+        "verified_tokens_per_s": round(cycles_per_s * tokens_per_cycle, 1),
+        "tokens_per_cycle": tokens_per_cycle,
+        "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1) if lm_gbs else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4) if lm_gbs else None,
+                     "traffic": traffic, "kernel": "lm_head rows GEMM",
+                     "bytes_per_launch": round(sum(lm_bytes) / len(lm_bytes)),
+                     "avg_launch_us": round(lm_ms / lm_cnt * 1e3, 2) if lm_cnt else None},
+        "cycle_roofline": {"bytes": bytes_cycle, "achieved_GBs": round(cycle_gbs, 1),
+                           "frac": round(cycle_gbs / HBM_PEAK_GBS, 4)},
+        "kernel_ms_per_cycle": {kk: round(v[0] / args.steps, 4) for kk, v in per_class.items()},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, Wt, ci)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
         "eagle3_verify": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P], I),
         "eagle3_ttt_forward": ([P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
         "eagle3_topk": ([P, I, I, I, P, P, P, P, SZ, P], I),
+        "eagle3_timing_enable": ([I, I], I),
+        "eagle3_timing_read": ([I, P, P], I),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -178,3 +180,20 @@ def eagle3_ttt_forward(dims, weights, feats, tokens, B, S, R, forced_tokens, pre
 def eagle3_topk(logits, rows, V, k, ids, lp, lse, ws, stream=None):
     _check("eagle3_topk", load().eagle3_topk(ptr(logits), rows, V, k, ptr(ids), ptr(lp), ptr(lse), ptr(ws),
                                              ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+# ---------------------------------------------------------------- kernel timing
+KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10,
+          ttt_gemm=11, ttt_attn=12, ttt_ce=13)
+
+
+def timing_enable(kc: int, max_launches: int):
+    _check("eagle3_timing_enable", load().eagle3_timing_enable(kc, max_launches))
+
+
+def timing_read(kc: int):
+    """(total milliseconds, launches) recorded for kernel class kc."""
+    ms = ctypes.c_double(0)
+    cnt = ctypes.c_int(0)
+    _check("eagle3_timing_read", load().eagle3_timing_read(kc, ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value

@@ -8,6 +8,7 @@
 #include "draft.hpp"
 #include "eagle3.h"
 #include "kernels.hpp"
+#include "timing.hpp"
 #include "ttt.hpp"
 
 namespace {
@@ -185,6 +186,7 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t* roo
   } else {
     REQUIRE(v_tok && v_parent && v_depth && v_pos && v_anc, EAGLE3_EINVAL, "v_* is NULL");
   }
+  e3::TimedScope ts(EAGLE3_KC_TREE, (hipStream_t)stream);
   return hip_status(e3::launch_tree_expand(phase, B, k, D, m, root_tok, root_pos, tree_state, topk_id,
                                            topk_lp, next_tok, next_parent_slot, next_pos, next_anc,
                                            v_tok, v_parent, v_depth, v_pos, v_anc, (hipStream_t)stream),
@@ -204,6 +206,7 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int
     REQUIRE(temperature > 0.f, EAGLE3_EINVAL, "temperature must be > 0 for sampling");
     REQUIRE(u_try && u_res, EAGLE3_EINVAL, "sampling needs u_try/u_res");
   }
+  e3::TimedScope ts(EAGLE3_KC_VERIFY, (hipStream_t)stream);
   return hip_status(e3::launch_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature,
                                       u_try, u_res, accept_len, accepted, bonus, status,
                                       (hipStream_t)stream),

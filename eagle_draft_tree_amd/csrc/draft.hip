@@ -20,6 +20,7 @@
 #include "draft.hpp"
 #include "gemm_rows.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace e3 {
 
@@ -192,6 +193,7 @@ static hipError_t fuse_impl(const eagle3_dims& dm, const eagle3_weights& w, cons
                             int n, void* g, hipStream_t st) {
   const int K = 3 * dm.d;
   RowMap map{MAP_PLAIN, dm.head_dim, dm.ffn};
+  TimedScope ts(EAGLE3_KC_FUSE, st);
   for (int r0 = 0; r0 < n; r0 += 64) {
     const int R = n - r0 < 64 ? n - r0 : 64;
     EpiStore<T> epi{(T*)g + (size_t)r0 * dm.d, dm.d, map};
@@ -221,13 +223,18 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   layout_draft(dm, R, cap_rows, c.ws, &ws);
   hipError_t e;
 
+  {
+  TimedScope ts(EAGLE3_KC_ROWOPS, st);
   prologue_kernel<T><<<R, ROW_THREADS, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree,
                                                 c.parent_slot, c.mode, c.rows, d, w.norm_e, w.norm_s,
                                                 dm.rms_eps, ws.S, (T*)ws.x);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 
   // QKV + RoPE + KV write, in chunks of <= 64 rows
   const int nqkv = (hq + 2 * hkv) * hd;
+  {
+  TimedScope ts(EAGLE3_KC_QKV, st);
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int Rc = R - r0 < 64 ? R - r0 : 64;
     RowMap map{MAP_PAIR_HEAD, hd, F};
@@ -242,6 +249,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * 2 * d, 2 * d, Rc, (const T*)w.qkv, 2 * d, nqkv,
                           map, epi, st)) != hipSuccess)
       return e;
+  }
   }
   // attention
   AttnLaunch al;
@@ -267,8 +275,12 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   al.part_o = ws.part_o;
   al.part_ml = ws.part_ml;
   al.out = ws.a;
-  if ((e = launch_attention(al, st)) != hipSuccess) return e;
-
+  {
+    TimedScope ts(EAGLE3_KC_ATTN, st);
+    if ((e = launch_attention(al, st)) != hipSuccess) return e;
+  }
+  {
+  TimedScope ts(EAGLE3_KC_O, st);
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int Rc = R - r0 < 64 ? R - r0 : 64;
     RowMap plain{MAP_PLAIN, hd, F};
@@ -277,8 +289,14 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
         hipSuccess)
       return e;
   }
-  rms_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h1, d, w.norm_ffn, dm.rms_eps, (T*)ws.u);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    TimedScope ts(EAGLE3_KC_ROWOPS, st);
+    rms_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h1, d, w.norm_ffn, dm.rms_eps, (T*)ws.u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+  TimedScope ts(EAGLE3_KC_GATEUP, st);
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int Rc = R - r0 < 64 ? R - r0 : 64;
     RowMap pf{MAP_PAIR_FFN, hd, F};
@@ -287,6 +305,9 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
                           st)) != hipSuccess)
       return e;
   }
+  }
+  {
+  TimedScope ts(EAGLE3_KC_DOWN, st);
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int Rc = R - r0 < 64 ? R - r0 : 64;
     RowMap plain{MAP_PLAIN, hd, F};
@@ -295,12 +316,18 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
         hipSuccess)
       return e;
   }
+  }
   const int topk_last = c.topk_rows == EAGLE3_TOPK_LAST;
-  final_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h2, d, w.norm_out, dm.rms_eps, c.mode, c.rows,
-                                                  c.slot_base, topk_last, c.h_tree, (T*)ws.y);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    TimedScope ts(EAGLE3_KC_ROWOPS, st);
+    final_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h2, d, w.norm_out, dm.rms_eps, c.mode, c.rows,
+                                                    c.slot_base, topk_last, c.h_tree, (T*)ws.y);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int Rl = topk_last ? c.B : R;
   float* logits = c.logits_out ? c.logits_out : ws.logits;
+  {
+  TimedScope ts(EAGLE3_KC_LMHEAD, st);
   for (int r0 = 0; r0 < Rl; r0 += 64) {
     const int Rc = Rl - r0 < 64 ? Rl - r0 : 64;
     RowMap plain{MAP_PLAIN, hd, F};
@@ -309,6 +336,8 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
         hipSuccess)
       return e;
   }
+  }
+  TimedScope ts(EAGLE3_KC_TOPK, st);
   return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, st);
 }
 

@@ -256,6 +256,36 @@ int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const v
 int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float *lp, float *lse,
                 void *ws, size_t ws_bytes, eagle3_stream_t stream);
 
+/* ---- kernel timing (diagnostics) ---------------------------------------
+ * Kernel classes of the draft/verify path.  When timing is enabled for a
+ * class, every launch of that class records a HIP event pair on the stream
+ * it is launched on; eagle3_timing_read synchronises on the last event and
+ * returns the summed elapsed time and the number of launches recorded since
+ * the class was enabled.  Event creation happens in eagle3_timing_enable
+ * (host memory/handles only); recording adds two hipEventRecord calls per
+ * launch.  Not thread safe; meant for benchmarks and profiling. */
+#define EAGLE3_KC_FUSE 0
+#define EAGLE3_KC_ROWOPS 1  /* prologue and RMSNorm row kernels      */
+#define EAGLE3_KC_QKV 2     /* QKV GEMM with RoPE / KV scatter        */
+#define EAGLE3_KC_ATTN 3    /* attention partials + merge            */
+#define EAGLE3_KC_O 4
+#define EAGLE3_KC_GATEUP 5
+#define EAGLE3_KC_DOWN 6
+#define EAGLE3_KC_LMHEAD 7
+#define EAGLE3_KC_TOPK 8
+#define EAGLE3_KC_TREE 9
+#define EAGLE3_KC_VERIFY 10
+#define EAGLE3_KC_TTT_GEMM 11
+#define EAGLE3_KC_TTT_ATTN 12
+#define EAGLE3_KC_TTT_CE 13
+#define EAGLE3_KC_COUNT 14
+
+/* max_launches > 0 enables class `kc` with room for that many launches
+ * (counters reset); 0 disables it and frees its events. */
+int eagle3_timing_enable(int kc, int max_launches);
+/* Total milliseconds and launch count recorded for class `kc`. */
+int eagle3_timing_read(int kc, double *total_ms, int *launches);
+
 #ifdef __cplusplus
 }
 #endif
