@@ -106,7 +106,7 @@ def main():
     t0 = time.time()
     Wt = gen.gen_weights(s, seed=0)
     ci = gen.gen_cycle_inputs(w, seed=1)
-    dr = Drafter(s, Wt)
+    dr = Drafter(s, Wt, pack=True)
     Bn, n, k, D, m = w.batch, w.commit_rows, w.topk, w.depth, w.keep
     spec = CycleSpec(Bn, n, k, D, m, ci.cap)
     buf = CycleBuffers(dr, spec)
@@ -189,7 +189,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) features/KV, N(0,3) target logits planted 0.8)",
         "config": {"workload": w.name, "batch": Bn, "prefix": int(ci.ctx_len[0]), "depth": D, "topk": k,
-                   "keep": m, "verify": "greedy", "graph": False},
+                   "keep": m, "verify": "greedy", "graph": False, "weights": "packed"},
         "verified_tokens_per_s": round(cycles_per_s * tokens_per_cycle, 1),
         "tokens_per_cycle": tokens_per_cycle,
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1) if lm_gbs else None, "peak": HBM_PEAK_GBS,

@@ -32,9 +32,12 @@ class Dims(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
 
 
+LAYOUT_ROWMAJOR, LAYOUT_PACKED = 0, 1
+
+
 class Weights(ctypes.Structure):
     _fields_ = [(n, vp) for n in ("fc", "emb", "qkv", "o", "gate_up", "down", "lm",
-                                  "norm_e", "norm_s", "norm_ffn", "norm_out")]
+                                  "norm_e", "norm_s", "norm_ffn", "norm_out")] + [("layout", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -71,10 +74,13 @@ def load(path: str = LIB_PATH):
         "eagle3_fuse": ([P, P, P, I, P, P, SZ, P], I),
         "eagle3_draft_step": ([P, P, P, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
         "eagle3_tree_expand": ([I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
-        "eagle3_verify": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P], I),
+        "eagle3_verify": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P, SZ, P], I),
+        "eagle3_verify_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
         "eagle3_ttt_forward": ([P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
         "eagle3_topk": ([P, I, I, I, P, P, P, P, SZ, P], I),
         "eagle3_timing_enable": ([I, I], I),
+        "eagle3_packed_weights_size": ([P, ctypes.POINTER(SZ)], I),
+        "eagle3_pack_weights": ([P, P, P, SZ, P, P], I),
         "eagle3_timing_read": ([I, P, P], I),
     }
     for name, (args, res) in sigs.items():
@@ -113,7 +119,7 @@ def dims_of(shape) -> Dims:
 def weights_of(t: dict) -> Weights:
     """eagle3_weights from a dict of device tensors (keeps no references)."""
     return Weights(*(t[n].data_ptr() for n in ("fc", "emb", "qkv", "o", "gate_up", "down", "lm",
-                                                "norm_e", "norm_s", "norm_ffn", "norm_out")))
+                                                "norm_e", "norm_s", "norm_ffn", "norm_out")), LAYOUT_ROWMAJOR)
 
 
 # ---------------------------------------------------------------- queries
@@ -135,6 +141,21 @@ def ttt_workspace_size(dims: Dims, B: int, S: int, R: int) -> int:
     _check("eagle3_ttt_workspace_size", load().eagle3_ttt_workspace_size(ctypes.byref(dims), B, S, R,
                                                                          ctypes.byref(out)))
     return out.value
+
+
+def packed_weights_size(dims: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check("eagle3_packed_weights_size", load().eagle3_packed_weights_size(ctypes.byref(dims), ctypes.byref(out)))
+    return out.value
+
+
+def eagle3_pack_weights(dims, weights, dst, stream=None) -> Weights:
+    """Pack the GEMM matrices into `dst` (device uint8 tensor); returns the packed eagle3_weights."""
+    packed = Weights()
+    _check("eagle3_pack_weights", load().eagle3_pack_weights(
+        ctypes.byref(dims), ctypes.byref(weights), ptr(dst), dst.numel() * dst.element_size(),
+        ctypes.byref(packed), stream_ptr(stream)))
+    return packed
 
 
 # ---------------------------------------------------------------- the five calls (+ topk)
@@ -162,12 +183,18 @@ def eagle3_tree_expand(phase, B, k, D, m, root_tok, root_pos, tree_state, topk_i
         ptr(v_depth), ptr(v_pos), ptr(v_anc), stream_ptr(stream)))
 
 
+def verify_workspace_size(B: int, m: int, V: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("eagle3_verify_workspace_size", load().eagle3_verify_workspace_size(B, m, V, ctypes.byref(out)))
+    return out.value
+
+
 def eagle3_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature, u_try, u_res,
-                  accept_len, accepted, bonus, status, stream=None):
+                  accept_len, accepted, bonus, status, ws, stream=None):
     _check("eagle3_verify", load().eagle3_verify(
         B, m, V, Dmax, ptr(v_tok), ptr(v_parent), ptr(target_logits), mode, float(temperature),
         ptr(u_try), ptr(u_res), ptr(accept_len), ptr(accepted), ptr(bonus), ptr(status),
-        stream_ptr(stream)))
+        ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
 
 
 def eagle3_ttt_forward(dims, weights, feats, tokens, B, S, R, forced_tokens, pred, ce, loss, ws,

@@ -8,6 +8,7 @@
 #include "draft.hpp"
 #include "eagle3.h"
 #include "kernels.hpp"
+#include "pack.hpp"
 #include "timing.hpp"
 #include "ttt.hpp"
 
@@ -51,6 +52,7 @@ int check_dims(const eagle3_dims* dm) {
   REQUIRE(dm->d % 32 == 0 && dm->ffn % 32 == 0 && dm->vocab % 16 == 0, EAGLE3_EUNSUPPORTED,
           "d and ffn must be multiples of 32, vocab of 16");
   REQUIRE(dm->rms_eps >= 0.f && dm->rope_theta > 0.f, EAGLE3_EINVAL, "rms_eps/rope_theta");
+  REQUIRE(dm->vocab <= 262144, EAGLE3_EUNSUPPORTED, "vocab %d > 262144", dm->vocab);
   return EAGLE3_OK;
 }
 
@@ -59,6 +61,8 @@ int check_weights(const eagle3_weights* w) {
   REQUIRE(w->fc && w->emb && w->qkv && w->o && w->gate_up && w->down && w->lm, EAGLE3_EINVAL,
           "a weight pointer is NULL");
   REQUIRE(w->norm_e && w->norm_s && w->norm_ffn && w->norm_out, EAGLE3_EINVAL, "a norm gain is NULL");
+  REQUIRE(w->layout == EAGLE3_LAYOUT_ROWMAJOR || w->layout == EAGLE3_LAYOUT_PACKED, EAGLE3_EINVAL, "layout %d",
+          w->layout);
   return EAGLE3_OK;
 }
 
@@ -82,6 +86,28 @@ const char* eagle3_strerror(int code) {
 const char* eagle3_last_error(void) { return g_last_error; }
 
 const char* eagle3_version(void) { return "eagle3-gfx950 0.1"; }
+
+int eagle3_packed_weights_size(const eagle3_dims* dims, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(bytes, EAGLE3_EINVAL, "bytes is NULL");
+  REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "packing needs bf16 weights");
+  *bytes = e3::packed_bytes(*dims);
+  return ok();
+}
+
+int eagle3_pack_weights(const eagle3_dims* dims, const eagle3_weights* src, void* dst, size_t dst_bytes,
+                        eagle3_weights* packed, eagle3_stream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_weights(src))) return rc;
+  REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "packing needs bf16 weights");
+  REQUIRE(src->layout == EAGLE3_LAYOUT_ROWMAJOR, EAGLE3_EINVAL, "src must be row-major");
+  REQUIRE(dst && packed, EAGLE3_EINVAL, "dst/packed is NULL");
+  REQUIRE(dst_bytes >= e3::packed_bytes(*dims), EAGLE3_EWORKSPACE, "dst %zu < %zu bytes", dst_bytes,
+          e3::packed_bytes(*dims));
+  return hip_status(e3::pack_weights(*dims, *src, dst, packed, (hipStream_t)stream), "eagle3_pack_weights");
+}
 
 int eagle3_workspace_size(const eagle3_dims* dims, int B, int max_rows, int max_ctx, size_t* bytes) {
   int rc = check_dims(dims);
@@ -115,11 +141,13 @@ int eagle3_fuse(const eagle3_dims* dims, const eagle3_weights* w, const void* fe
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
+  REQUIRE(w->layout == EAGLE3_LAYOUT_ROWMAJOR || dims->dtype == EAGLE3_BF16, EAGLE3_EINVAL, "packed fp32");
   REQUIRE(feats && g, EAGLE3_EINVAL, "feats/g is NULL");
   REQUIRE(n >= 1, EAGLE3_EINVAL, "n=%d", n);
-  (void)ws;
-  (void)ws_bytes;
-  return hip_status(e3::fuse_rows(*dims, *w, feats, n, g, (hipStream_t)stream), "eagle3_fuse");
+  REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
+  const size_t need = e3::fuse_ws_bytes(*dims, n);
+  REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(e3::fuse_rows(*dims, *w, feats, n, g, ws, (hipStream_t)stream), "eagle3_fuse");
 }
 
 int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const eagle3_kv* kv, int mode,
@@ -130,6 +158,7 @@ int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const ea
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
+  REQUIRE(w->layout == EAGLE3_LAYOUT_ROWMAJOR || dims->dtype == EAGLE3_BF16, EAGLE3_EINVAL, "packed fp32");
   REQUIRE(kv && kv->k && kv->v && kv->ctx_len, EAGLE3_EINVAL, "kv/k/v/ctx_len is NULL");
   REQUIRE(mode == EAGLE3_COMMIT || mode == EAGLE3_TREE, EAGLE3_EINVAL, "mode %d", mode);
   REQUIRE(B >= 1, EAGLE3_EINVAL, "B=%d", B);
@@ -156,6 +185,7 @@ int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const ea
     REQUIRE(kv->cap >= 1, EAGLE3_EINVAL, "cap=%d", kv->cap);
     cap_rows = kv->cap;
   }
+  REQUIRE(cap_rows <= 32000, EAGLE3_EUNSUPPORTED, "KV capacity %d rows > 32000", cap_rows);
   const size_t need = e3::draft_ws_bytes(*dims, B, rows, cap_rows - rows > 0 ? cap_rows - rows : 0);
   REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
   REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -193,10 +223,17 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t* roo
                     "eagle3_tree_expand");
 }
 
+int eagle3_verify_workspace_size(int B, int m, int V, size_t* bytes) {
+  REQUIRE(bytes, EAGLE3_EINVAL, "bytes is NULL");
+  REQUIRE(B >= 1 && m >= 0 && V >= 1, EAGLE3_EINVAL, "B/m/V");
+  *bytes = e3::verify_ws_bytes(B, m, V);
+  return ok();
+}
+
 int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int32_t* v_parent,
                   const float* target_logits, int mode, float temperature, const double* u_try,
                   const double* u_res, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
-                  int32_t* status, eagle3_stream_t stream) {
+                  int32_t* status, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
   REQUIRE(B >= 1 && m >= 0 && V >= 1 && Dmax >= 1, EAGLE3_EINVAL, "B/m/V/Dmax");
   REQUIRE(m + 1 <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "m+1=%d > 64", m + 1);
   REQUIRE(v_tok && v_parent && target_logits && accept_len && accepted && bonus && status, EAGLE3_EINVAL,
@@ -206,9 +243,12 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int
     REQUIRE(temperature > 0.f, EAGLE3_EINVAL, "temperature must be > 0 for sampling");
     REQUIRE(u_try && u_res, EAGLE3_EINVAL, "sampling needs u_try/u_res");
   }
+  REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
+  REQUIRE(ws_bytes >= e3::verify_ws_bytes(B, m, V), EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
+          e3::verify_ws_bytes(B, m, V));
   e3::TimedScope ts(EAGLE3_KC_VERIFY, (hipStream_t)stream);
   return hip_status(e3::launch_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature,
-                                      u_try, u_res, accept_len, accepted, bonus, status,
+                                      u_try, u_res, accept_len, accepted, bonus, status, ws,
                                       (hipStream_t)stream),
                     "eagle3_verify");
 }
@@ -217,6 +257,7 @@ int eagle3_topk(const float* logits, int rows, int V, int k, int32_t* ids, float
                 void* ws, size_t ws_bytes, eagle3_stream_t stream) {
   REQUIRE(logits && ids && lp && ws, EAGLE3_EINVAL, "a required pointer is NULL");
   REQUIRE(rows >= 1 && V >= 1 && k >= 1 && k <= V, EAGLE3_EINVAL, "rows/V/k");
+  REQUIRE(V <= 262144, EAGLE3_EUNSUPPORTED, "V %d > 262144", V);
   REQUIRE(k <= EAGLE3_MAX_TOPK, EAGLE3_ECAPACITY, "k=%d > %d", k, EAGLE3_MAX_TOPK);
   const size_t need = e3::topk_ws_bytes(rows, V);
   REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -33,14 +33,38 @@ struct AttnArgs {
   float* part_ml;  // [Rtot*Hq][nchunks][2]
 };
 
+// 16-byte vector of T elements, unpacked to float.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+};
+
 template <typename T, int HD>
 __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
-  constexpr int KP = HD + 8;  // padded LDS row (elements)
-  __shared__ T ks[CH * KP];
-  __shared__ T vs[CH * HD];
+  constexpr int EPV = Vec16<T>::N;         // elements per 16-byte vector
+  constexpr int VPR = HD / EPV;            // vectors per key row
+  constexpr int KPV = VPR + 1;             // padded LDS row (vectors): spreads banks
+  __shared__ uint4 ks[CH * KPV];
+  __shared__ uint4 vs[CH * VPR];
   __shared__ float qs[QG * HD];
   __shared__ float sc[QG * CH];
-  __shared__ int nvis_s;
 
   const int chunk = blockIdx.x;
   const int g = blockIdx.y / a.n_qgroups, qgrp = blockIdx.y - g * a.n_qgroups;
@@ -56,7 +80,8 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
   if (nq <= 0) return;
 
   // Keys of this chunk and how many exist.
-  int p0 = chunk * CH, nkeys;
+  const int p0 = chunk * CH;
+  int nkeys;
   if (tree_chunk) {
     nkeys = a.mode == EAGLE3_TREE ? EAGLE3_MAX_TREE_SLOTS : 0;
   } else {
@@ -87,50 +112,52 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
     any_vis = 0ull;
     for (int rr = 0; rr < a.rows; ++rr) any_vis |= a.anc[b * a.rows + rr];
   }
-  // Stage K/V rows of the chunk.
-  const T* K = (const T*)a.kc;
-  const T* V = (const T*)a.vc;
-  for (int e = threadIdx.x; e < nkeys * HD; e += ATT_THREADS) {
-    const int p = e / HD, i = e - p * HD;
-    if (!((any_vis >> p) & 1ull)) {
-      ks[p * KP + i] = T(0);
-      vs[p * HD + i] = T(0);
-      continue;
-    }
-    size_t off;
-    const T *kb, *vb;
-    if (tree_chunk) {
-      off = ((size_t)(b * EAGLE3_MAX_TREE_SLOTS + p) * a.hkv + g) * HD + i;
-      kb = (const T*)a.tk;
-      vb = (const T*)a.tv;
-    } else {
-      const int pos = p0 + p;
-      if (a.block_table) {
-        const int blk = a.block_table[(size_t)b * a.max_blocks + pos / a.block_size];
-        off = (((size_t)blk * a.block_size + pos % a.block_size) * a.hkv + g) * HD + i;
+  // Stage K/V rows of the chunk with 16-byte loads.
+  for (int e = threadIdx.x; e < nkeys * VPR; e += ATT_THREADS) {
+    const int p = e / VPR, c = e - p * VPR;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if ((any_vis >> p) & 1ull) {
+      size_t off;
+      const T *kb, *vb;
+      if (tree_chunk) {
+        off = ((size_t)(b * EAGLE3_MAX_TREE_SLOTS + p) * a.hkv + g) * HD;
+        kb = (const T*)a.tk;
+        vb = (const T*)a.tv;
       } else {
-        off = (((size_t)b * a.cap + pos) * a.hkv + g) * HD + i;
+        const int pos = p0 + p;
+        if (a.block_table) {
+          const int blk = a.block_table[(size_t)b * a.max_blocks + pos / a.block_size];
+          off = (((size_t)blk * a.block_size + pos % a.block_size) * a.hkv + g) * HD;
+        } else {
+          off = (((size_t)b * a.cap + pos) * a.hkv + g) * HD;
+        }
+        kb = (const T*)a.kc;
+        vb = (const T*)a.vc;
       }
-      kb = K;
-      vb = V;
+      kv = *((const uint4*)(kb + off) + c);
+      vv = *((const uint4*)(vb + off) + c);
     }
-    ks[p * KP + i] = kb[off];
-    vs[p * HD + i] = vb[off];
+    ks[p * KPV + c] = kv;
+    vs[p * VPR + c] = vv;
   }
-  // Stage the query vectors (q head h = g*G + gi of row rr).
+  // Stage the query vectors (q head h = g*G + gi of row rr) as float.
   const T* Q = (const T*)a.q;
-  for (int e = threadIdx.x; e < nq * HD; e += ATT_THREADS) {
-    const int qi = e / HD, i = e - qi * HD;
+  for (int e = threadIdx.x; e < nq * VPR; e += ATT_THREADS) {
+    const int qi = e / VPR, c = e - qi * VPR;
     const int rr = (q0 + qi) / G, gi = (q0 + qi) - rr * G;
     const size_t row = (size_t)b * a.rows + rr;
-    qs[qi * HD + i] = Elem<T>::ld(Q, (row * a.hq + g * G + gi) * HD + i);
+    const uint4 u = *((const uint4*)(Q + (row * a.hq + g * G + gi) * HD) + c);
+    float f[EPV];
+    Vec16<T>::unpack(u, f);
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) qs[qi * HD + c * EPV + j] = f[j];
   }
   __syncthreads();
   // Scores: lane = key, waves split the query vectors.
   if (lane < nkeys) {
-    float kreg[HD];
+    float kf[HD];
 #pragma unroll
-    for (int i = 0; i < HD; ++i) kreg[i] = Elem<T>::ld(ks, (size_t)lane * KP + i);
+    for (int c = 0; c < VPR; ++c) Vec16<T>::unpack(ks[lane * KPV + c], kf + c * EPV);
     for (int qi = wave; qi < nq; qi += ATT_THREADS / 64) {
       const int rr = (q0 + qi) / G;
       bool vis;
@@ -140,10 +167,21 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
         const int lim = a.mode == EAGLE3_TREE ? ctx : ctx + rr + 1;
         vis = p0 + lane < lim;
       }
-      float s = 0.f;
+      const float4* q4 = (const float4*)(qs + qi * HD);
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < HD; ++i) s = fmaf(qs[qi * HD + i], kreg[i], s);
-      sc[qi * CH + lane] = vis ? s * a.scale : -INFINITY;
+      for (int i = 0; i < HD / 4; i += 2) {
+        const float4 x = q4[i], y = q4[i + 1];
+        s0 = fmaf(x.x, kf[4 * i], s0);
+        s0 = fmaf(x.y, kf[4 * i + 1], s0);
+        s0 = fmaf(x.z, kf[4 * i + 2], s0);
+        s0 = fmaf(x.w, kf[4 * i + 3], s0);
+        s1 = fmaf(y.x, kf[4 * i + 4], s1);
+        s1 = fmaf(y.y, kf[4 * i + 5], s1);
+        s1 = fmaf(y.z, kf[4 * i + 6], s1);
+        s1 = fmaf(y.w, kf[4 * i + 7], s1);
+      }
+      sc[qi * CH + lane] = vis ? (s0 + s1) * a.scale : -INFINITY;
     }
   } else {
     for (int qi = wave; qi < nq; qi += ATT_THREADS / 64) sc[qi * CH + lane] = -INFINITY;
@@ -163,35 +201,68 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-  // o[qi][i] = sum_p P[qi][p] V[p][i]
-  for (int e = threadIdx.x; e < nq * HD; e += ATT_THREADS) {
-    const int qi = e / HD, i = e - qi * HD;
-    float acc = 0.f;
-    for (int p = 0; p < nkeys; ++p) acc = fmaf(sc[qi * CH + p], Elem<T>::ld(vs, (size_t)p * HD + i), acc);
-    a.part_o[out_index(qi) * HD + i] = acc;
+  // o[qi][i..i+EPV) = sum_p P[qi][p] V[p][i..i+EPV): VPR threads per query.
+  for (int e = threadIdx.x; e < nq * VPR; e += ATT_THREADS) {
+    const int qi = e / VPR, c = e - qi * VPR;
+    float acc[EPV];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) acc[j] = 0.f;
+    for (int p = 0; p < nkeys; ++p) {
+      const float w = sc[qi * CH + p];
+      float f[EPV];
+      Vec16<T>::unpack(vs[p * VPR + c], f);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) acc[j] = fmaf(w, f[j], acc[j]);
+    }
+    float* dst = a.part_o + out_index(qi) * HD + c * EPV;
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) dst[j] = acc[j];
   }
 }
 
-// out[row][h*hd + i] = merged attention output, rounded to T.
+// out[row][h*hd + i] = merged attention output, rounded to T.  One wave per
+// (row, head): chunk maxima and weights first (lanes over chunks), then the
+// weighted sum of the chunk partials in chunk order.
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float* part_o, const float* part_ml,
-                                                        int nchunks, int hq, T* out) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml, int nchunks, int hq,
+                                                        T* __restrict__ out) {
+  constexpr int MAXC = 512;
+  __shared__ float wc[MAXC];
   const size_t rh = blockIdx.x;  // row*hq + h
   const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part_ml[2 * (rh * nchunks + c)]);
-  float L = 0.f;
+  const float* ml = part_ml + 2 * rh * nchunks;
+  float mloc = -INFINITY;
+  for (int c = lane; c < nchunks; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
+  const float M = wave_max(mloc);
+  float lloc = 0.f;
+  for (int c = lane; c < nchunks; c += 64) {
+    const float m = ml[2 * c];
+    const float w = m == -INFINITY ? 0.f : expf(m - M);
+    wc[c] = w;
+    lloc += ml[2 * c + 1] * w;
+  }
+  const float L = wave_sum(lloc);
+  __syncthreads();
   float acc[HD / 64];
 #pragma unroll
   for (int j = 0; j < HD / 64; ++j) acc[j] = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float m = part_ml[2 * (rh * nchunks + c)];
-    if (m == -INFINITY) continue;
-    const float w = expf(m - M);
-    L += part_ml[2 * (rh * nchunks + c) + 1] * w;
+  const float* po = part_o + rh * nchunks * HD;
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    float v[8][HD / 64];
 #pragma unroll
-    for (int j = 0; j < HD / 64; ++j) acc[j] += part_o[(rh * nchunks + c) * HD + lane + 64 * j] * w;
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < HD / 64; ++j) v[u][j] = po[(size_t)(c + u) * HD + lane + 64 * j];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < HD / 64; ++j) acc[j] = fmaf(v[u][j], wc[c + u], acc[j]);
   }
+  for (; c < nchunks; ++c)
+#pragma unroll
+    for (int j = 0; j < HD / 64; ++j) acc[j] = fmaf(po[(size_t)c * HD + lane + 64 * j], wc[c], acc[j]);
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int j = 0; j < HD / 64; ++j) Elem<T>::st(out, rh * HD + lane + 64 * j, acc[j] * inv);

@@ -41,20 +41,58 @@ template <> struct Elem<bf16> {
   static __device__ __forceinline__ float rnd(float v) { return round_bf(v); }
 };
 
+// ---------------------------------------------------------------------------
+// Wave64 reductions on the ALU path: DPP exchanges inside each 16-lane row
+// (quad_perm 1032, quad_perm 2301, row_half_mirror, row_mirror), then the
+// four row results are read with v_readlane and combined.  The result is
+// uniform across the wave and the combination order is fixed.
+constexpr int DPP_QUAD_1032 = 0xB1;
+constexpr int DPP_QUAD_2301 = 0x4E;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const int lo = dpp_i<CTRL>((int)(u & 0xffffffffu)), hi = dpp_i<CTRL>((int)(u >> 32));
+  return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ float rdl_f(float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); }
+__device__ __forceinline__ double rdl_d(double x, int l) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffu), l);
+  const unsigned hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+  return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);
+  return (rdl_f(v, 0) + rdl_f(v, 16)) + (rdl_f(v, 32) + rdl_f(v, 48));
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_d<DPP_QUAD_1032>(v);
+  v += dpp_d<DPP_QUAD_2301>(v);
+  v += dpp_d<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_d<DPP_ROW_MIRROR>(v);
+  return (rdl_d(v, 0) + rdl_d(v, 16)) + (rdl_d(v, 32) + rdl_d(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  return fmaxf(fmaxf(rdl_f(v, 0), rdl_f(v, 16)), fmaxf(rdl_f(v, 32), rdl_f(v, 48)));
 }
 
 // Block-wide sum in a fixed order (deterministic).  `red` holds >= nwaves floats.
@@ -73,6 +111,71 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // then lower id.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
+}
+
+// Wave argmax of (value, id) under `better`; uniform result.
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+#define E3_ARG_STEP(CTRL)                              \
+  {                                                    \
+    const float ov = dpp_f<CTRL>(v);                   \
+    const int oi = dpp_i<CTRL>(id);                    \
+    if (better(ov, oi, v, id)) {                       \
+      v = ov;                                          \
+      id = oi;                                         \
+    }                                                  \
+  }
+  E3_ARG_STEP(DPP_QUAD_1032)
+  E3_ARG_STEP(DPP_QUAD_2301)
+  E3_ARG_STEP(DPP_ROW_HALF_MIRROR)
+  E3_ARG_STEP(DPP_ROW_MIRROR)
+#undef E3_ARG_STEP
+  float bv = rdl_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) {
+    const float ov = rdl_f(v, l);
+    const int oi = __builtin_amdgcn_readlane(id, l);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  v = bv;
+  id = bi;
+}
+
+// Wave minimum of a 64-bit key with a payload; uniform result.
+__device__ __forceinline__ void wave_argmin_u64(unsigned long long& key, int& pay) {
+#define E3_MIN_STEP(CTRL)                                                                       \
+  {                                                                                             \
+    const unsigned lo = dpp_i<CTRL>((int)(key & 0xffffffffu)), hi = dpp_i<CTRL>((int)(key >> 32)); \
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;                          \
+    const int op = dpp_i<CTRL>(pay);                                                            \
+    if (o < key) {                                                                              \
+      key = o;                                                                                  \
+      pay = op;                                                                                 \
+    }                                                                                           \
+  }
+  E3_MIN_STEP(DPP_QUAD_1032)
+  E3_MIN_STEP(DPP_QUAD_2301)
+  E3_MIN_STEP(DPP_ROW_HALF_MIRROR)
+  E3_MIN_STEP(DPP_ROW_MIRROR)
+#undef E3_MIN_STEP
+  unsigned long long bk = ~0ull;
+  int bp = 0;
+#pragma unroll
+  for (int l = 0; l < 64; l += 16) {
+    const unsigned lo = __builtin_amdgcn_readlane((int)(key & 0xffffffffu), l);
+    const unsigned hi = __builtin_amdgcn_readlane((int)(key >> 32), l);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    const int op = __builtin_amdgcn_readlane(pay, l);
+    if (o < bk) {
+      bk = o;
+      bp = op;
+    }
+  }
+  key = bk;
+  pay = bp;
 }
 
 }  // namespace e3

@@ -4,16 +4,19 @@
 // embedding; the frozen LM head gives the draft distribution).
 //
 // Kernel sequence of eagle3_draft_step (R = B*rows query rows):
-//   prologue   x = [rms(emb[t]); rms(s)] (dtype), S = s (fp32)
-//   qkv        rows GEMM, paired-RoPE epilogue; q -> ws, k/v -> cache/slots
-//   attention  split-K partials + ordered merge -> a (dtype)
-//   o          rows GEMM, residual epilogue: h1 = S + o.a
-//   norm       u = rms(h1) (dtype)
-//   gate/up    rows GEMM, paired SwiGLU epilogue: z = silu(gate.u)*(up.u)
-//   down       rows GEMM, residual epilogue: h2 = h1 + down.z
-//   final norm h2 -> h_tree slots; y = rms(h2) of the top-k rows (dtype)
-//   lm head    rows GEMM -> fp32 logits
-//   top-k      partition top-k + LSE, ordered merge -> ids, lp
+//   prologue    x = [rms(emb[t]); rms(s)] (dtype), S = s (fp32)
+//   qkv         rows GEMM (split-K partials) + qkv_finish: sum, RoPE, q -> ws,
+//               k/v -> cache or tree slots   (unsplit: fused paired-RoPE epilogue)
+//   attention   split-K partials + ordered merge -> a (dtype)
+//   o           rows GEMM (split-K partials)
+//   norm        h1 = S + sum(o partials); u = rms(h1) (dtype)
+//   gate/up     rows GEMM, paired SwiGLU epilogue: z = silu(gate.u)*(up.u)
+//   down        rows GEMM (split-K partials)
+//   final norm  h2 = h1 + sum(down partials) -> h_tree; y = rms(h2) (dtype)
+//   lm head     rows GEMM -> fp32 logits
+//   top-k       partition top-k + LSE, ordered merge -> ids, lp
+// Split-K partials are added in split order by the consumer, so every
+// result is deterministic.
 #include <string.h>
 
 #include "common.hpp"
@@ -24,109 +27,251 @@
 
 namespace e3 {
 
-constexpr int ROW_THREADS = 256;
+constexpr int RT = 1024;      // threads of the row kernels
+constexpr int EPT_MAX = 8;    // elements per thread: d <= 8192
 
 // ---------------------------------------------------------------------------
-// row kernels
+// row kernels: every thread owns elements i = threadIdx.x + RT*j, j < EPT_MAX,
+// and issues all of its loads before using any of them.
+
+// v[j] += sum over splits of part[s][row][i] (fixed split order)
+__device__ __forceinline__ void add_partials(float (&v)[EPT_MAX], const float* __restrict__ part, int splits,
+                                             size_t split_stride, size_t row_off, int d) {
+  for (int s = 0; s < splits; ++s) {
+    float p[EPT_MAX];
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      p[j] = i < d ? part[(size_t)s * split_stride + row_off + i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) v[j] += p[j];
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(ROW_THREADS) void prologue_kernel(
+__global__ __launch_bounds__(RT) void prologue_kernel(
     const T* __restrict__ emb, const int32_t* __restrict__ tokens, const T* __restrict__ state,
     const float* __restrict__ h_tree, const int32_t* __restrict__ parent_slot, int mode, int rows,
     int d, const float* __restrict__ ge, const float* __restrict__ gs, float eps,
     float* __restrict__ S, T* __restrict__ x) {
-  __shared__ float red[ROW_THREADS / 64];
+  __shared__ float red[RT / 64];
   const int r = blockIdx.x;
   const int b = r / rows;
   const T* e = emb + (size_t)tokens[r] * d;
   const float* hs = nullptr;
   if (mode == EAGLE3_TREE) hs = h_tree + ((size_t)b * (EAGLE3_MAX_TREE_SLOTS + 1) + parent_slot[r]) * d;
+  float ev[EPT_MAX], sv[EPT_MAX];
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    ev[j] = i < d ? Elem<T>::ld(e, i) : 0.f;
+    sv[j] = i < d ? (mode == EAGLE3_TREE ? hs[i] : Elem<T>::ld(state, (size_t)r * d + i)) : 0.f;
+  }
   float se = 0.f, ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) {
-    const float ev = Elem<T>::ld(e, i);
-    const float sv = mode == EAGLE3_TREE ? hs[i] : Elem<T>::ld(state, (size_t)r * d + i);
-    se = fmaf(ev, ev, se);
-    ss = fmaf(sv, sv, ss);
-    S[(size_t)r * d + i] = sv;
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    se = fmaf(ev[j], ev[j], se);
+    ss = fmaf(sv[j], sv[j], ss);
   }
   se = block_sum(se, red);
   ss = block_sum(ss, red);
   const float ie = (float)(1.0 / sqrt((double)se / d + (double)eps));
   const float is = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) {
-    const float ev = Elem<T>::ld(e, i);
-    const float sv = mode == EAGLE3_TREE ? hs[i] : Elem<T>::ld(state, (size_t)r * d + i);
-    Elem<T>::st(x, (size_t)r * 2 * d + i, ev * ie * ge[i]);
-    Elem<T>::st(x, (size_t)r * 2 * d + d + i, sv * is * gs[i]);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) {
+      S[(size_t)r * d + i] = sv[j];
+      Elem<T>::st(x, (size_t)r * 2 * d + i, ev[j] * ie * ge[i]);
+      Elem<T>::st(x, (size_t)r * 2 * d + d + i, sv[j] * is * gs[i]);
+    }
   }
 }
 
-// out[r] = rms(in[r]) * gain (dtype)
+// h1 = res + sum of o partials (splits > 0), or h1 already complete;
+// u = rms(h1) * gain (dtype)
 template <typename T>
-__global__ __launch_bounds__(ROW_THREADS) void rms_rows_kernel(const float* __restrict__ in, int d,
-                                                               const float* __restrict__ gain,
-                                                               float eps, T* __restrict__ out) {
-  __shared__ float red[ROW_THREADS / 64];
+__global__ __launch_bounds__(RT) void ffn_norm_kernel(const float* __restrict__ res, const float* __restrict__ part,
+                                                      int splits, int R, int d, const float* __restrict__ gain,
+                                                      float eps, float* __restrict__ h1, T* __restrict__ u) {
+  __shared__ float red[RT / 64];
   const int r = blockIdx.x;
-  const float* v = in + (size_t)r * d;
+  float v[EPT_MAX];
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    v[j] = i < d ? (splits > 0 ? res[(size_t)r * d + i] : h1[(size_t)r * d + i]) : 0.f;
+  }
+  if (splits > 0) add_partials(v, part, splits, (size_t)R * d, (size_t)r * d, d);
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) ss = fmaf(v[i], v[i], ss);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
   ss = block_sum(ss, red);
   const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) Elem<T>::st(out, (size_t)r * d + i, v[i] * inv * gain[i]);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) {
+      if (splits > 0) h1[(size_t)r * d + i] = v[j];
+      Elem<T>::st(u, (size_t)r * d + i, v[j] * inv * gain[i]);
+    }
+  }
 }
 
+// h2 = h1 + sum of down partials (splits > 0), or h2 already complete;
 // h2 rows -> h_tree (COMMIT: last row of each request -> slot 0; TREE: row
-// rr -> 1 + slot_base + rr) and y = rms(h2)*gain for the rows whose top-k is
+// rr -> 1 + slot_base + rr); y = rms(h2)*gain for the rows whose top-k is
 // taken (all rows, or the last row of each request), packed.
 template <typename T>
-__global__ __launch_bounds__(ROW_THREADS) void final_rows_kernel(
-    const float* __restrict__ h2, int d, const float* __restrict__ gain, float eps, int mode,
-    int rows, int slot_base, int topk_last, float* __restrict__ h_tree, T* __restrict__ y) {
-  __shared__ float red[ROW_THREADS / 64];
+__global__ __launch_bounds__(RT) void final_norm_kernel(
+    const float* __restrict__ h1, const float* __restrict__ part, int splits, int R, const float* __restrict__ h2buf,
+    int d, const float* __restrict__ gain, float eps, int mode, int rows, int slot_base, int topk_last,
+    float* __restrict__ h_tree, T* __restrict__ y) {
+  __shared__ float red[RT / 64];
   const int r = blockIdx.x;
   const int b = r / rows, rr = r - b * rows;
-  const float* v = h2 + (size_t)r * d;
   const bool last = rr == rows - 1;
   int hslot = -1;
   if (mode == EAGLE3_TREE) hslot = 1 + slot_base + rr;
   else if (last) hslot = 0;
+  if (hslot < 0 && topk_last && !last) return;
+  float v[EPT_MAX];
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    v[j] = i < d ? (splits > 0 ? h1[(size_t)r * d + i] : h2buf[(size_t)r * d + i]) : 0.f;
+  }
+  if (splits > 0) add_partials(v, part, splits, (size_t)R * d, (size_t)r * d, d);
   if (hslot >= 0) {
     float* dst = h_tree + ((size_t)b * (EAGLE3_MAX_TREE_SLOTS + 1) + hslot) * d;
-    for (int i = threadIdx.x; i < d; i += ROW_THREADS) dst[i] = v[i];
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      if (i < d) dst[i] = v[j];
+    }
   }
   if (topk_last && !last) return;
   const int yr = topk_last ? b : r;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) ss = fmaf(v[i], v[i], ss);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
   ss = block_sum(ss, red);
   const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-  for (int i = threadIdx.x; i < d; i += ROW_THREADS) Elem<T>::st(y, (size_t)yr * d + i, v[i] * inv * gain[i]);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) Elem<T>::st(y, (size_t)yr * d + i, v[j] * inv * gain[i]);
+  }
+}
+
+// QKV after split-K: one workgroup per (row, head); thread i < hd/2 owns the
+// RoPE pair (i, i + hd/2).  Sum partials in split order, rotate q and k at
+// the row's position, round, write q to ws and k/v to the KV destination.
+template <typename T>
+__global__ __launch_bounds__(64) void qkv_finish_kernel(const float* __restrict__ part, int splits, int R,
+                                                        int N, const int32_t* __restrict__ pos,
+                                                        KVDest dst, T* __restrict__ q_out, int hq,
+                                                        float theta) {
+  const int r = blockIdx.x, head = blockIdx.y;
+  const int hd = dst.hd, half = hd >> 1;
+  for (int i = threadIdx.x; i < half; i += 64) {
+    const size_t n0 = (size_t)head * hd + i;
+    float p0[16], p1[16];
+    float a = 0.f, b = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      const int ns = min(16, splits - s0);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        if (s < ns) {
+          p0[s] = part[(size_t)(s0 + s) * R * N + (size_t)r * N + n0];
+          p1[s] = part[(size_t)(s0 + s) * R * N + (size_t)r * N + n0 + half];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < ns) {
+          a += p0[s];
+          b += p1[s];
+        }
+    }
+    if (head < hq + dst.hkv) {  // q or k: rotate
+      const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
+      const double ang = (double)pos[r] * inv;
+      const float c = (float)cos(ang), sn = (float)sin(ang);
+      const float a2 = a * c - b * sn, b2 = b * c + a * sn;
+      a = a2;
+      b = b2;
+    }
+    if (head < hq) {
+      const size_t o = (size_t)r * hq * hd + (size_t)head * hd;
+      Elem<T>::st(q_out, o + i, a);
+      Elem<T>::st(q_out, o + i + half, b);
+    } else {
+      const bool isk = head < hq + dst.hkv;
+      const int g = isk ? head - hq : head - hq - dst.hkv;
+      bool tree;
+      const size_t o = dst.off(r, g, tree);
+      T* base = (T*)(isk ? (tree ? dst.tk : dst.k) : (tree ? dst.tv : dst.v));
+      Elem<T>::st(base, o + i, a);
+      Elem<T>::st(base, o + i + half, b);
+    }
+  }
+}
+
+// g = round(sum of fusion partials)
+template <typename T>
+__global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restrict__ part, int splits, int n, int d,
+                                                          T* __restrict__ g) {
+  const size_t total = (size_t)n * d;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    float p[16];
+    float acc = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      const int ns = min(16, splits - s0);
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < ns) p[s] = part[(size_t)(s0 + s) * total + e];
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < ns) acc += p[s];
+    }
+    Elem<T>::st(g, e, acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // rows-GEMM dispatch.  The epilogue sees rows 0..R-1 of one launch; row
-// chunks beyond 64 are launched separately with shifted pointers.
+// chunks beyond 64 are launched separately with shifted pointers (no split).
 template <typename TW, int T, int NT, int U, int WAVES, class Epi>
-static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int K, int N,
-                                   RowMap map, const Epi& epi, hipStream_t st) {
+static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
+                                   const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
   const int nt16 = N / 16;
-  const int grid = (nt16 + T - 1) / T;
+  const int grid = p.tiles * p.splits;
   const size_t lds = sizeof(TW) == 2 ? (size_t)WAVES * T * NT * 256 * sizeof(float) : 0;
-  rows_gemm_kernel<TW, T, NT, U, WAVES, Epi><<<grid, WAVES * 64, lds, st>>>(X, ldx, R, W, K, K, nt16, map, epi);
+  if (packed)
+    rows_gemm_kernel<TW, T, NT, U, WAVES, true, Epi>
+        <<<grid, WAVES * 64, lds, st>>>(X, ldx, R, W, K, nt16, p.splits, map, epi);
+  else
+    rows_gemm_kernel<TW, T, NT, U, WAVES, false, Epi>
+        <<<grid, WAVES * 64, lds, st>>>(X, ldx, R, W, K, nt16, p.splits, map, epi);
   return hipGetLastError();
 }
 
+// The template arguments below must match plan_rows (T, U, waves per NT).
 template <typename TW, class Epi>
 static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
-                            const Epi& epi, hipStream_t st) {
+                            const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
   if (sizeof(TW) == 2) {
-    if (R <= 16) return rows_gemm_launch<TW, 2, 1, 8, 4>(X, ldx, R, W, K, N, map, epi, st);
-    if (R <= 32) return rows_gemm_launch<TW, 1, 2, 8, 4>(X, ldx, R, W, K, N, map, epi, st);
-    if (R <= 48) return rows_gemm_launch<TW, 1, 3, 8, 4>(X, ldx, R, W, K, N, map, epi, st);
-    return rows_gemm_launch<TW, 1, 4, 8, 4>(X, ldx, R, W, K, N, map, epi, st);
+    switch (p.nt) {
+      case 1: return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+      case 2: return rows_gemm_launch<TW, 4, 2, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+      case 3: return rows_gemm_launch<TW, 4, 3, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+      default: return rows_gemm_launch<TW, 4, 4, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+    }
   }
-  if (R <= 16) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, st);
-  return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, st);
+  if (p.nt == 1) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st);
+  return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -142,7 +287,31 @@ struct Bump {
   }
 };
 
+// GEMM shapes of a draft step: qkv, o, gate_up, down, lm, and the fusion fc.
+struct Shapes {
+  int n[6], k[6];
+  bool split[6];
+};
+static Shapes shapes_of(const eagle3_dims& dm) {
+  const int d = dm.d, F = dm.ffn, qd = dm.n_q_heads * dm.head_dim;
+  const int nqkv = (dm.n_q_heads + 2 * dm.n_kv_heads) * dm.head_dim;
+  Shapes s{{nqkv, d, 2 * F, d, dm.vocab, d}, {2 * d, qd, d, F, d, 3 * d}, {true, true, false, true, false, true}};
+  return s;
+}
+
+static size_t max_partials(const eagle3_dims& dm, int R) {
+  const bool bf = dm.dtype == EAGLE3_BF16;
+  const Shapes sh = shapes_of(dm);
+  size_t m = 0;
+  for (int i = 0; i < 6; ++i) {
+    const size_t f = rows_partial_floats(plan_rows(R, sh.n[i], sh.k[i], bf, sh.split[i]), R, sh.n[i]);
+    if (f > m) m = f;
+  }
+  return m;
+}
+
 struct DraftWS {
+  float* part;
   float* S;
   void* x;
   void* q;
@@ -165,6 +334,7 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   Bump bp;
   bp.base = (unsigned char*)base;
   DraftWS t;
+  t.part = (float*)bp.take(max_partials(dm, R) * 4);
   t.S = (float*)bp.take((size_t)R * dm.d * 4);
   t.x = bp.take((size_t)R * 2 * dm.d * es);
   t.q = bp.take((size_t)R * qd * es);
@@ -178,35 +348,50 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   t.y = bp.take((size_t)R * dm.d * es);
   t.logits = (float*)bp.take((size_t)R * dm.vocab * 4);
   t.topk = bp.take(topk_ws_bytes(R, dm.vocab));
-  // fusion reuses the same memory: g needs nothing beyond the GEMM itself
   if (w) *w = t;
   return bp.off + 256;
 }
 
 size_t draft_ws_bytes(const eagle3_dims& dm, int B, int max_rows, int max_ctx) {
-  return layout_draft(dm, B * max_rows, max_ctx + max_rows, nullptr, nullptr);
+  const size_t a = layout_draft(dm, B * max_rows, max_ctx + max_rows, nullptr, nullptr);
+  const size_t f = fuse_ws_bytes(dm, B * max_rows);
+  return a > f ? a : f;
 }
+
+size_t fuse_ws_bytes(const eagle3_dims& dm, int n) { return max_partials(dm, n) * 4 + 512; }
 
 // ---------------------------------------------------------------------------
 template <typename T>
 static hipError_t fuse_impl(const eagle3_dims& dm, const eagle3_weights& w, const void* feats,
-                            int n, void* g, hipStream_t st) {
+                            int n, void* g, void* ws, hipStream_t st) {
   const int K = 3 * dm.d;
   RowMap map{MAP_PLAIN, dm.head_dim, dm.ffn};
+  const bool pk = w.layout == EAGLE3_LAYOUT_PACKED;
   TimedScope ts(EAGLE3_KC_FUSE, st);
+  const RowsPlan p = plan_rows(n, dm.d, K, sizeof(T) == 2, true);
+  if (p.splits > 1) {  // n <= 64
+    EpiPartial epi{(float*)ws, dm.d, map};
+    hipError_t e = rows_gemm<T>((const T*)feats, K, n, (const T*)w.fc, K, dm.d, map, epi, p, pk, st);
+    if (e != hipSuccess) return e;
+    int blocks = (int)(((size_t)n * dm.d + 255) / 256);
+    if (blocks > 1024) blocks = 1024;
+    fuse_finish_kernel<T><<<blocks, 256, 0, st>>>((const float*)ws, p.splits, n, dm.d, (T*)g);
+    return hipGetLastError();
+  }
   for (int r0 = 0; r0 < n; r0 += 64) {
     const int R = n - r0 < 64 ? n - r0 : 64;
+    const RowsPlan pc = plan_rows(R, dm.d, K, sizeof(T) == 2, false);
     EpiStore<T> epi{(T*)g + (size_t)r0 * dm.d, dm.d, map};
-    hipError_t e = rows_gemm<T>((const T*)feats + (size_t)r0 * K, K, R, (const T*)w.fc, K, dm.d, map, epi, st);
+    hipError_t e = rows_gemm<T>((const T*)feats + (size_t)r0 * K, K, R, (const T*)w.fc, K, dm.d, map, epi, pc, pk, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t fuse_rows(const eagle3_dims& dm, const eagle3_weights& w, const void* feats, int n,
-                     void* g, hipStream_t st) {
-  return dm.dtype == EAGLE3_BF16 ? fuse_impl<bf16>(dm, w, feats, n, g, st)
-                                 : fuse_impl<float>(dm, w, feats, n, g, st);
+                     void* g, void* ws, hipStream_t st) {
+  return dm.dtype == EAGLE3_BF16 ? fuse_impl<bf16>(dm, w, feats, n, g, ws, st)
+                                 : fuse_impl<float>(dm, w, feats, n, g, ws, st);
 }
 
 template <typename T>
@@ -214,6 +399,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   const eagle3_dims& dm = *c.dims;
   const eagle3_weights& w = *c.w;
   const eagle3_kv& kv = *c.kv;
+  const bool bf = sizeof(T) == 2;
   const int d = dm.d, hd = dm.head_dim, hq = dm.n_q_heads, hkv = dm.n_kv_heads, F = dm.ffn;
   const int V = dm.vocab;
   const int R = c.B * c.rows;
@@ -222,36 +408,51 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   DraftWS ws;
   layout_draft(dm, R, cap_rows, c.ws, &ws);
   hipError_t e;
+  const RowMap plain{MAP_PLAIN, hd, F};
+  const RowMap pair_head{MAP_PAIR_HEAD, hd, F};
+  const bool pk = w.layout == EAGLE3_LAYOUT_PACKED;
 
   {
-  TimedScope ts(EAGLE3_KC_ROWOPS, st);
-  prologue_kernel<T><<<R, ROW_THREADS, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree,
-                                                c.parent_slot, c.mode, c.rows, d, w.norm_e, w.norm_s,
-                                                dm.rms_eps, ws.S, (T*)ws.x);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+    TimedScope ts(EAGLE3_KC_ROWOPS, st);
+    prologue_kernel<T><<<R, RT, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree, c.parent_slot,
+                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  // QKV + RoPE + KV write, in chunks of <= 64 rows
+  // ---- QKV + RoPE + KV write
   const int nqkv = (hq + 2 * hkv) * hd;
+  KVDest dst{kv.k, kv.v, kv.tk, kv.tv, kv.ctx_len, kv.block_table, kv.cap, kv.max_blocks, kv.block_size,
+             c.rows, c.mode, c.slot_base, hkv, hd, 0};
   {
-  TimedScope ts(EAGLE3_KC_QKV, st);
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int Rc = R - r0 < 64 ? R - r0 : 64;
-    RowMap map{MAP_PAIR_HEAD, hd, F};
-    EpiQKV<T> epi;
-    epi.q_out = (T*)ws.q + (size_t)r0 * qd;
-    epi.pos = c.pos + r0;
-    epi.dst = KVDest{kv.k, kv.v, kv.tk, kv.tv, kv.ctx_len, kv.block_table, kv.cap, kv.max_blocks,
-                     kv.block_size, c.rows, c.mode, c.slot_base, hkv, hd};
-    epi.dst.row0 = r0;
-    epi.hq = hq;
-    epi.theta = dm.rope_theta;
-    if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * 2 * d, 2 * d, Rc, (const T*)w.qkv, 2 * d, nqkv,
-                          map, epi, st)) != hipSuccess)
-      return e;
+    TimedScope ts(EAGLE3_KC_QKV, st);
+    const RowsPlan p = plan_rows(R, nqkv, 2 * d, bf, true);
+    if (p.splits > 1) {
+      EpiPartial epi{ws.part, nqkv, pair_head};
+      if ((e = rows_gemm<T>((const T*)ws.x, 2 * d, R, (const T*)w.qkv, 2 * d, nqkv, pair_head, epi, p, pk, st)) !=
+          hipSuccess)
+        return e;
+      qkv_finish_kernel<T><<<dim3(R, hq + 2 * hkv), 64, 0, st>>>(ws.part, p.splits, R, nqkv, c.pos, dst, (T*)ws.q,
+                                                                 hq, dm.rope_theta);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      for (int r0 = 0; r0 < R; r0 += 64) {
+        const int Rc = R - r0 < 64 ? R - r0 : 64;
+        RowMap map{MAP_PAIR_HEAD, hd, F};
+        EpiQKV<T> epi;
+        epi.q_out = (T*)ws.q + (size_t)r0 * qd;
+        epi.pos = c.pos + r0;
+        epi.dst = dst;
+        epi.dst.row0 = r0;
+        epi.hq = hq;
+        epi.theta = dm.rope_theta;
+        const RowsPlan pc = plan_rows(Rc, nqkv, 2 * d, bf, false);
+        if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * 2 * d, 2 * d, Rc, (const T*)w.qkv, 2 * d, nqkv, map, epi,
+                              pc, pk, st)) != hipSuccess)
+          return e;
+      }
+    }
   }
-  }
-  // attention
+  // ---- attention
   AttnLaunch al;
   al.q = ws.q;
   al.kc = kv.k;
@@ -271,7 +472,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   al.hkv = hkv;
   al.hd = hd;
   al.mode = c.mode;
-  al.bf16 = sizeof(T) == 2;
+  al.bf16 = bf;
   al.part_o = ws.part_o;
   al.part_ml = ws.part_ml;
   al.out = ws.a;
@@ -279,63 +480,84 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     TimedScope ts(EAGLE3_KC_ATTN, st);
     if ((e = launch_attention(al, st)) != hipSuccess) return e;
   }
+  // ---- O projection (+ residual in the FFN norm)
+  int o_splits = 0;
   {
-  TimedScope ts(EAGLE3_KC_O, st);
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int Rc = R - r0 < 64 ? R - r0 : 64;
-    RowMap plain{MAP_PLAIN, hd, F};
-    EpiResidual epi{ws.h1 + (size_t)r0 * d, ws.S + (size_t)r0 * d, d};
-    if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)w.o, qd, d, plain, epi, st)) !=
-        hipSuccess)
-      return e;
-  }
+    TimedScope ts(EAGLE3_KC_O, st);
+    const RowsPlan p = plan_rows(R, d, qd, bf, true);
+    if (p.splits > 1) {
+      EpiPartial epi{ws.part, d, plain};
+      if ((e = rows_gemm<T>((const T*)ws.a, qd, R, (const T*)w.o, qd, d, plain, epi, p, pk, st)) != hipSuccess) return e;
+      o_splits = p.splits;
+    } else {
+      for (int r0 = 0; r0 < R; r0 += 64) {
+        const int Rc = R - r0 < 64 ? R - r0 : 64;
+        EpiResidual epi{ws.h1 + (size_t)r0 * d, ws.S + (size_t)r0 * d, d};
+        const RowsPlan pc = plan_rows(Rc, d, qd, bf, false);
+        if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)w.o, qd, d, plain, epi, pc, pk, st)) !=
+            hipSuccess)
+          return e;
+      }
+    }
   }
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
-    rms_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h1, d, w.norm_ffn, dm.rms_eps, (T*)ws.u);
+    ffn_norm_kernel<T><<<R, RT, 0, st>>>(ws.S, ws.part, o_splits, R, d, w.norm_ffn, dm.rms_eps, ws.h1, (T*)ws.u);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // ---- gate/up + SwiGLU
   {
-  TimedScope ts(EAGLE3_KC_GATEUP, st);
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int Rc = R - r0 < 64 ? R - r0 : 64;
-    RowMap pf{MAP_PAIR_FFN, hd, F};
-    EpiSwiGLU<T> epi{(T*)ws.z + (size_t)r0 * F, F};
-    if ((e = rows_gemm<T>((const T*)ws.u + (size_t)r0 * d, d, Rc, (const T*)w.gate_up, d, 2 * F, pf, epi,
-                          st)) != hipSuccess)
-      return e;
+    TimedScope ts(EAGLE3_KC_GATEUP, st);
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      RowMap pf{MAP_PAIR_FFN, hd, F};
+      EpiSwiGLU<T> epi{(T*)ws.z + (size_t)r0 * F, F};
+      const RowsPlan pc = plan_rows(Rc, 2 * F, d, bf, false);
+      if ((e = rows_gemm<T>((const T*)ws.u + (size_t)r0 * d, d, Rc, (const T*)w.gate_up, d, 2 * F, pf, epi, pc, pk, st)) !=
+          hipSuccess)
+        return e;
+    }
   }
-  }
+  // ---- down (+ residual in the final norm)
+  int down_splits = 0;
   {
-  TimedScope ts(EAGLE3_KC_DOWN, st);
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int Rc = R - r0 < 64 ? R - r0 : 64;
-    RowMap plain{MAP_PLAIN, hd, F};
-    EpiResidual epi{ws.h2 + (size_t)r0 * d, ws.h1 + (size_t)r0 * d, d};
-    if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)w.down, F, d, plain, epi, st)) !=
-        hipSuccess)
-      return e;
-  }
+    TimedScope ts(EAGLE3_KC_DOWN, st);
+    const RowsPlan p = plan_rows(R, d, F, bf, true);
+    if (p.splits > 1) {
+      EpiPartial epi{ws.part, d, plain};
+      if ((e = rows_gemm<T>((const T*)ws.z, F, R, (const T*)w.down, F, d, plain, epi, p, pk, st)) != hipSuccess) return e;
+      down_splits = p.splits;
+    } else {
+      for (int r0 = 0; r0 < R; r0 += 64) {
+        const int Rc = R - r0 < 64 ? R - r0 : 64;
+        EpiResidual epi{ws.h2 + (size_t)r0 * d, ws.h1 + (size_t)r0 * d, d};
+        const RowsPlan pc = plan_rows(Rc, d, F, bf, false);
+        if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)w.down, F, d, plain, epi, pc, pk, st)) !=
+            hipSuccess)
+          return e;
+      }
+    }
   }
   const int topk_last = c.topk_rows == EAGLE3_TOPK_LAST;
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
-    final_rows_kernel<T><<<R, ROW_THREADS, 0, st>>>(ws.h2, d, w.norm_out, dm.rms_eps, c.mode, c.rows,
-                                                    c.slot_base, topk_last, c.h_tree, (T*)ws.y);
+    final_norm_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, down_splits, R, ws.h2, d, w.norm_out, dm.rms_eps, c.mode,
+                                           c.rows, c.slot_base, topk_last, c.h_tree, (T*)ws.y);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // ---- LM head + top-k
   const int Rl = topk_last ? c.B : R;
   float* logits = c.logits_out ? c.logits_out : ws.logits;
   {
-  TimedScope ts(EAGLE3_KC_LMHEAD, st);
-  for (int r0 = 0; r0 < Rl; r0 += 64) {
-    const int Rc = Rl - r0 < 64 ? Rl - r0 : 64;
-    RowMap plain{MAP_PLAIN, hd, F};
-    EpiStore<float> epi{logits + (size_t)r0 * V, V, plain};
-    if ((e = rows_gemm<T>((const T*)ws.y + (size_t)r0 * d, d, Rc, (const T*)w.lm, d, V, plain, epi, st)) !=
-        hipSuccess)
-      return e;
-  }
+    TimedScope ts(EAGLE3_KC_LMHEAD, st);
+    for (int r0 = 0; r0 < Rl; r0 += 64) {
+      const int Rc = Rl - r0 < 64 ? Rl - r0 : 64;
+      EpiStore<float> epi{logits + (size_t)r0 * V, V, plain};
+      const RowsPlan pc = plan_rows(Rc, V, d, bf, false);
+      if ((e = rows_gemm<T>((const T*)ws.y + (size_t)r0 * d, d, Rc, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) !=
+          hipSuccess)
+        return e;
+    }
   }
   TimedScope ts(EAGLE3_KC_TOPK, st);
   return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, st);

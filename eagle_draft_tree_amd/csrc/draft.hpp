@@ -26,7 +26,8 @@ struct DraftCall {
 
 size_t draft_ws_bytes(const eagle3_dims& dm, int B, int max_rows, int max_ctx);
 hipError_t draft_step(const DraftCall& c, hipStream_t st);
+size_t fuse_ws_bytes(const eagle3_dims& dm, int n);
 hipError_t fuse_rows(const eagle3_dims& dm, const eagle3_weights& w, const void* feats, int n,
-                     void* g, hipStream_t st);
+                     void* g, void* ws, hipStream_t st);
 
 }  // namespace e3

@@ -43,27 +43,88 @@ union U4 {
 };
 
 // ---------------------------------------------------------------------------
-// Compute a [16*T x R] tile into LDS `tile_out` (layout [16*T][RP], RP =
-// 16*NT), bf16 operands on MFMA.
-template <int T, int NT, int U, int WAVES>
+// Plan: tiles per workgroup (T), MFMAs per k-group (U), column tiles (NT =
+// ceil(R/16)) and the split-K factor S (workgroups per tile).  Small-N
+// matrices are split along K so that the grid fills the chip; the partial
+// tiles are summed by the last workgroup of each tile, in split order.
+struct RowsPlan {
+  int nt, t, u, waves, splits, tiles;
+};
+
+static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_split = true) {
+  RowsPlan p;
+  p.waves = 4;
+  p.nt = (R + 15) / 16;
+  if (!bf16) {
+    p.t = 1;
+    p.u = 1;
+    p.splits = 1;
+    p.tiles = N / 16;
+    return p;
+  }
+  p.t = p.nt == 1 ? 2 : 4;
+  p.u = p.nt == 1 ? 4 : 2;
+  p.waves = p.nt == 1 ? 8 : 4;
+  p.tiles = (N / 16 + p.t - 1) / p.t;
+  const int ngroups = K / (32 * p.u);
+  int smax = ngroups / p.waves;
+  if (smax < 1) smax = 1;
+  int s = (1024 + p.tiles - 1) / p.tiles;
+  if (s > smax) s = smax;
+  if (s < 1 || !allow_split || R > 64) s = 1;
+  p.splits = s;
+  return p;
+}
+
+// fp32 floats of the split-K partials of a plan: [splits][R][N]
+static inline size_t rows_partial_floats(const RowsPlan& p, int R, int N) {
+  return p.splits > 1 ? (size_t)p.splits * R * N : 0;
+}
+
+// Compute a [16*T x R] tile over k in [k0, k1) into LDS `tile_out` (layout
+// [16*T][RP], RP = 16*NT), bf16 operands on MFMA.  k-group g (32*U wide)
+// feeds U MFMAs; MFMA j covers k in [kb+32j, kb+32j+32) and lane l brings
+// the 8 elements at kb + 32j + 8*(l/16) of weight row l%16 (A) and of X row
+// l%16 (B): the four lanes of a row read 64 contiguous bytes.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Weight fragment loads bypass reuse-oriented caching (nontemporal): every
+// weight byte is read exactly once per launch.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int T, int NT, int U, int WAVES, bool PACKED>
 __device__ __forceinline__ void rows_tile_bf16(const bf16* __restrict__ X, int ldx, int R,
-                                               const bf16* __restrict__ W, int ldw, int K,
-                                               const int* wrows /*[16*T] in LDS*/,
-                                               float* red /*[WAVES][T][NT][256]*/,
+                                               const bf16* __restrict__ W, int ldw, int k0, int k1,
+                                               const int* wrows /*[16*T] in LDS*/, int tile0,
+                                               int ntiles16, float* red /*[WAVES][T][NT][256]*/,
                                                float* tile_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, q4 = lane >> 4;
   constexpr int KG = 32 * U;
+  // row-major: lane reads W[row][k + 8*q4 ..]; packed: fragment (tile, chunk) is
+  // a contiguous 1 KB block and lane l reads its 16 bytes at l*16.
   const bf16* wp[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) wp[t] = W + (size_t)wrows[t * 16 + m] * ldw;
+  for (int t = 0; t < T; ++t) {
+    if (PACKED) {
+      const int t16 = min(tile0 + t, ntiles16 - 1);
+      wp[t] = W + ((size_t)t16 * (ldw / 32) * 64 + lane) * 8;
+    } else {
+      wp[t] = W + (size_t)wrows[t * 16 + m] * ldw + q4 * 8;
+    }
+  }
+  // element offset of k (a multiple of 32) inside a lane's stream
+  auto woff = [&](int k) -> size_t { return PACKED ? (size_t)(k / 32) * 64 * 8 : (size_t)k; };
   const bf16* xp[NT];
   bool xv[NT];
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
     const int r = c * 16 + m;
     xv[c] = r < R;
-    xp[c] = X + (size_t)(xv[c] ? r : 0) * ldx;
+    xp[c] = X + (size_t)(xv[c] ? r : 0) * ldx + q4 * 8;
   }
   f32x4 acc[T][NT];
 #pragma unroll
@@ -71,19 +132,19 @@ __device__ __forceinline__ void rows_tile_bf16(const bf16* __restrict__ X, int l
 #pragma unroll
     for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ngroups = K / KG;
+  const int ngroups = (k1 - k0) / KG;
   for (int g = wave; g < ngroups; g += WAVES) {
-    const int kb = g * KG + q4 * (8 * U);
+    const int kb = k0 + g * KG;
     U4 a[T][U], b[NT][U];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int j = 0; j < U; ++j) a[t][j].u = *(const uint4*)(wp[t] + kb + j * 8);
+      for (int t = 0; t < T; ++t) a[t][j].u = ld_stream(wp[t] + woff(kb + j * 32));
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        if (xv[c]) b[c][j].u = *(const uint4*)(xp[c] + kb + j * 8);
+        if (xv[c]) b[c][j].u = *(const uint4*)(xp[c] + kb + j * 32);
         else b[c][j].u = make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
@@ -94,14 +155,14 @@ __device__ __forceinline__ void rows_tile_bf16(const bf16* __restrict__ X, int l
         for (int c = 0; c < NT; ++c)
           acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][j].v, b[c][j].v, acc[t][c], 0, 0, 0);
   }
-  // K tail in 32-wide chunks (one MFMA each), spread over the waves.
-  const int kdone = ngroups * KG;
-  const int ntail = (K - kdone) / 32;
+  // k tail in 32-wide chunks (one MFMA each), spread over the waves.
+  const int kdone = k0 + ngroups * KG;
+  const int ntail = (k1 - kdone) / 32;
   for (int c32 = wave; c32 < ntail; c32 += WAVES) {
-    const int kb = kdone + c32 * 32 + q4 * 8;
+    const int kb = kdone + c32 * 32;
     U4 a[T], b[NT];
 #pragma unroll
-    for (int t = 0; t < T; ++t) a[t].u = *(const uint4*)(wp[t] + kb);
+    for (int t = 0; t < T; ++t) a[t].u = ld_stream(wp[t] + woff(kb));
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       if (xv[c]) b[c].u = *(const uint4*)(xp[c] + kb);
@@ -153,29 +214,38 @@ __device__ __forceinline__ void rows_tile_f32(const float* __restrict__ X, int l
 }
 
 // ---------------------------------------------------------------------------
-// The kernel: grid.x = number of workgroup tiles (16*T weight rows each).
-template <typename TW, int T, int NT, int U, int WAVES, class Epi>
+// The kernel: blockIdx.x = tile * splits + split.  With splits > 1 each
+// workgroup covers 1/splits of K and its epilogue (EpiPartial) stores the
+// partial tile; the consumer kernel adds the partials in split order.
+template <typename TW, int T, int NT, int U, int WAVES, bool PACKED, class Epi>
 __global__ __launch_bounds__(WAVES * 64) void rows_gemm_kernel(const TW* __restrict__ X, int ldx,
                                                                int R, const TW* __restrict__ W,
-                                                               int ldw, int K, int ntiles16,
+                                                               int K, int ntiles16, int splits,
                                                                RowMap map, Epi epi) {
   constexpr int RP = 16 * NT;
+  constexpr int TILE = 16 * T * RP;
   __shared__ int wrows[16 * T];
-  __shared__ float tile[16 * T * RP];
+  __shared__ float tile[TILE];
   extern __shared__ float red[];
-  const int wg_tile = blockIdx.x;
+  const int wg_tile = blockIdx.x / splits, split = blockIdx.x - wg_tile * splits;
   for (int i = threadIdx.x; i < 16 * T; i += WAVES * 64) {
     const int t16 = wg_tile * T + i / 16;
     wrows[i] = t16 < ntiles16 ? map(t16, i & 15) : map(0, i & 15);
   }
   __syncthreads();
-  if constexpr (sizeof(TW) == 2)
-    rows_tile_bf16<T, NT, U, WAVES>((const bf16*)X, ldx, R, (const bf16*)W, ldw, K, wrows, red, tile);
-  else
-    rows_tile_f32<T, NT, WAVES>((const float*)X, ldx, R, (const float*)W, ldw, K, wrows, tile);
+  if constexpr (sizeof(TW) == 2) {
+    constexpr int KG = 32 * U;
+    const int ng = K / KG;
+    const int g0 = (int)((long)ng * split / splits), g1 = (int)((long)ng * (split + 1) / splits);
+    const int k0 = g0 * KG, k1 = split == splits - 1 ? K : g1 * KG;
+    rows_tile_bf16<T, NT, U, WAVES, PACKED>((const bf16*)X, ldx, R, (const bf16*)W, K, k0, k1, wrows,
+                                            wg_tile * T, ntiles16, red, tile);
+  } else {
+    rows_tile_f32<T, NT, WAVES>((const float*)X, ldx, R, (const float*)W, K, K, wrows, tile);
+  }
   for (int t = 0; t < T; ++t) {
     const int t16 = wg_tile * T + t;
-    if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R);
+    if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split);
   }
 }
 
@@ -189,10 +259,25 @@ struct EpiStore {
   TO* out;
   int ldo;
   RowMap map;
-  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int m = e / R, r = e - m * R;
       Elem<TO>::st(out, (size_t)r * ldo + map(tile16, m), tile[m * RP + r]);
+    }
+  }
+};
+
+// Split-K partial: part[split][r][n] = v with n = map(tile, m) (natural
+// output order whatever the tile's row pairing).
+struct EpiPartial {
+  float* part;
+  int N;
+  RowMap map;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int split) const {
+    float* out = part + (size_t)split * R * N;
+    for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
+      const int r = e / 16, m = e - r * 16;
+      out[(size_t)r * N + map(tile16, m)] = tile[m * RP + r];
     }
   }
 };
@@ -202,7 +287,7 @@ struct EpiResidual {
   float* out;
   const float* res;
   int ld;
-  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int m = e / R, r = e - m * R;
       const size_t i = (size_t)r * ld + tile16 * 16 + m;
@@ -217,7 +302,7 @@ template <typename TO>
 struct EpiSwiGLU {
   TO* z;
   int ffn;
-  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
       const int m = e / R, r = e - m * R;
       const float g = tile[m * RP + r], u = tile[(m + 8) * RP + r];
@@ -266,7 +351,7 @@ struct EpiQKV {
   KVDest dst;
   int hq;
   float theta;
-  __device__ void operator()(int tile16, const float* tile, int RP, int R) const {
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     const int hd = dst.hd, tph = hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
     const int half = hd >> 1;
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {

@@ -39,9 +39,11 @@ hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32
                               hipStream_t st);
 
 // ---- verification (verify.hip)
+size_t verify_ws_bytes(int B, int m, int V);
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
                          const int32_t* v_parent, const float* logits, int mode, float temperature,
                          const double* u_try, const double* u_res, int32_t* accept_len,
-                         int32_t* accepted, int32_t* bonus, int32_t* status, hipStream_t st);
+                         int32_t* accepted, int32_t* bonus, int32_t* status, void* ws,
+                         hipStream_t st);
 
 }  // namespace e3

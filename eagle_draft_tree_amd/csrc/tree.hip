@@ -117,7 +117,6 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
   Pool P = pool_of(state, b, k, D);
   __shared__ int front[EAGLE3_MAX_TOPK];
   __shared__ int newfront[EAGLE3_MAX_TOPK];
-  __shared__ float csc[EAGLE3_MAX_TOPK * EAGLE3_MAX_TOPK];
   const int j = P.hdr[0] + 1;
   if (j > D) return;  // the tree already has depth D
   const int base = P.hdr[3];
@@ -125,26 +124,52 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
   for (int i = threadIdx.x; i < k; i += blockDim.x) front[i] = P.hdr[4 + i];
   __syncthreads();
   const int kk = k * k;
-  for (int c = threadIdx.x; c < kk; c += blockDim.x) {
-    const int rho = c / k, i = c - rho * k;
-    const int par = front[rho];
-    const float sc = P.score[par] + lp[(size_t)(b * k + rho) * k + i];  // one fp32 add
-    const int n = base + c;
-    P.tok[n] = ids[(size_t)(b * k + rho) * k + i];
-    P.parent[n] = par;
-    P.depth[n] = j;
-    P.flat[n] = c;
-    P.rank[n] = i;
-    P.slot[n] = -1;
-    P.score[n] = sc;
-    P.anc[n] = 0ull;
-    csc[c] = sc;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < kk; c += blockDim.x) {
-    int r = 0;
-    for (int o = 0; o < kk; ++o) r += front_better(csc[o], o, csc[c], c);
-    if (r < k) newfront[r] = base + c;
+  // wave 0: lane l owns candidates c = l + 64*q (q < 4, kk <= 256)
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float cs[4];
+    int cf[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lane + 64 * q;
+      cs[q] = -INFINITY;
+      cf[q] = INT_MAX;
+      if (c < kk) {
+        const int rho = c / k, i = c - rho * k;
+        const int par = front[rho];
+        const float sc = P.score[par] + lp[(size_t)(b * k + rho) * k + i];  // one fp32 add
+        const int n = base + c;
+        P.tok[n] = ids[(size_t)(b * k + rho) * k + i];
+        P.parent[n] = par;
+        P.depth[n] = j;
+        P.flat[n] = c;
+        P.rank[n] = i;
+        P.slot[n] = -1;
+        P.score[n] = sc;
+        P.anc[n] = 0ull;
+        cs[q] = sc;
+        cf[q] = c;
+      }
+    }
+    // k rounds of wave argmax by (score desc, flat asc)
+    for (int r = 0; r < k; ++r) {
+      float bs = -INFINITY;
+      int bf = INT_MAX;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (front_better(cs[q], cf[q], bs, bf)) {
+          bs = cs[q];
+          bf = cf[q];
+        }
+      wave_argmax(bs, bf);  // (score desc, flat asc) is the same order as (value desc, id asc)
+      if (lane == 0) newfront[r] = base + bf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (cf[q] == bf) {
+          cs[q] = -INFINITY;
+          cf[q] = INT_MAX;
+        }
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < k; i += blockDim.x) P.hdr[4 + i] = newfront[i];
@@ -152,99 +177,102 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     P.hdr[0] = j;
     P.hdr[3] = base + kk;
   }
-  __syncthreads();
   if (j < D) emit_frontier(P, newfront, b, k, j, root_pos, next_tok, next_parent_slot, next_pos, next_anc);
 }
 
 constexpr int MAX_POOL = EAGLE3_MAX_TOPK + (EAGLE3_MAX_TREE_SLOTS)*EAGLE3_MAX_TOPK;
 
-__global__ __launch_bounds__(TREE_THREADS) void tree_final_kernel(
-    int k, int D, int m, void* state, int32_t* v_tok, int32_t* v_parent, int32_t* v_depth,
-    int32_t* v_pos, uint64_t* v_anc) {
+// Rerank key: smaller = better.  (score desc, depth asc, flat asc) packed
+// into one 64-bit integer (the float's order-preserving bit image, negated).
+__device__ __forceinline__ unsigned long long rerank_key(float score, int depth, int flat) {
+  if (score == 0.f) score = 0.f;  // -0 and +0 compare equal
+  uint32_t u = __float_as_uint(score);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending in score
+  return ((unsigned long long)(~u) << 32) | ((unsigned long long)depth << 16) | (unsigned)flat;
+}
+
+constexpr int FIN_PER_LANE = (MAX_POOL + 63) / 64;  // 17
+
+__global__ __launch_bounds__(64) void tree_final_kernel(int k, int D, int m, void* state, int32_t* v_tok,
+                                                        int32_t* v_parent, int32_t* v_depth, int32_t* v_pos,
+                                                        uint64_t* v_anc) {
   const int b = blockIdx.x;
+  const int lane = threadIdx.x;
   Pool P = pool_of(state, b, k, D);
-  __shared__ float sc[MAX_POOL];
-  __shared__ short dp[MAX_POOL];
-  __shared__ short fl[MAX_POOL];
-  __shared__ short rk[MAX_POOL];
-  __shared__ short par[MAX_POOL];
-  __shared__ short vidx[MAX_POOL];  // -1 dropped, -2 kept (index pending), else verify index
-  __shared__ short vnew[MAX_POOL];
+  __shared__ short vidx_of[MAX_POOL];  // verify index of each kept pool node
   __shared__ uint64_t anc_s[EAGLE3_MAX_TREE_SLOTS];
-  __shared__ int cnt_s[EAGLE3_MAX_TREE_SLOTS + 2];
   const int n = P.hdr[3];
   const int root_pos = P.hdr[2];
   const int M1 = m + 1;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    sc[i] = P.score[i];
-    dp[i] = (short)P.depth[i];
-    fl[i] = (short)P.flat[i];
-    rk[i] = (short)P.rank[i];
-    par[i] = (short)P.parent[i];
+  // 1. top-m of the pool: lane-strided keys in registers, m rounds of wave argmin
+  unsigned long long key[FIN_PER_LANE];
+#pragma unroll
+  for (int j = 0; j < FIN_PER_LANE; ++j) {
+    const int i = lane + 64 * j;
+    key[j] = i < n ? rerank_key(P.score[i], P.depth[i], P.flat[i]) : ~0ull;
   }
-  __syncthreads();
-  // keep the first m by (score desc, depth asc, flat asc)
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    int r = 0;
-    const float s = sc[i];
-    const int d = dp[i], f = fl[i];
-    for (int o = 0; o < n; ++o) r += pool_better(sc[o], dp[o], fl[o], s, d, f);
-    vidx[i] = r < m ? -2 : -1;
-  }
-  __syncthreads();
-  // kept nodes per depth -> first verify index of each depth
-  if (threadIdx.x == 0) {
-    for (int d = 0; d <= D; ++d) cnt_s[d] = 0;
-    for (int i = 0; i < n; ++i)
-      if (vidx[i] == -2) cnt_s[dp[i]]++;
-    int acc = 1;
-    for (int d = 1; d <= D; ++d) {
-      const int c = cnt_s[d];
-      cnt_s[d] = acc;
-      acc += c;
-    }
-  }
-  __syncthreads();
-  // canonical order, one depth at a time: (parent's verify index, child rank)
-  for (int dep = 1; dep <= D; ++dep) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      if (vidx[i] != -2 || dp[i] != dep) continue;
-      const int pv = par[i] < 0 ? 0 : vidx[par[i]];
-      int pos = 0;
-      for (int o = 0; o < n; ++o) {
-        if (vidx[o] != -2 || dp[o] != dep) continue;
-        const int pvo = par[o] < 0 ? 0 : vidx[par[o]];
-        pos += (pvo < pv) || (pvo == pv && rk[o] < rk[i]);
+  int my_node = -1;  // lane e holds the e-th kept node (rerank order)
+  for (int r = 0; r < m; ++r) {
+    unsigned long long best = ~0ull;
+    int bj = 0;
+#pragma unroll
+    for (int j = 0; j < FIN_PER_LANE; ++j)
+      if (key[j] < best) {
+        best = key[j];
+        bj = j;
       }
-      vnew[i] = (short)(cnt_s[dep] + pos);
+    unsigned long long wbest = best;
+    int wnode = lane + 64 * bj;
+    wave_argmin_u64(wbest, wnode);
+    if (lane == r) my_node = wnode;
+    const bool mine = (wnode & 63) == lane;
+    const int wj = wnode >> 6;
+#pragma unroll
+    for (int j = 0; j < FIN_PER_LANE; ++j)
+      if (mine && j == wj) key[j] = ~0ull;
+  }
+  // 2. canonical order, depth by depth: (parent's verify index, child rank)
+  int my_dep = 0, my_par = -1, my_rank = 0;
+  if (my_node >= 0) {
+    my_dep = P.depth[my_node];
+    my_par = P.parent[my_node];
+    my_rank = P.rank[my_node];
+  }
+  int base = 1;
+  int my_vidx = -1, my_pv = 0;
+  for (int dep = 1; dep <= D; ++dep) {
+    if (my_node >= 0 && my_dep == dep) my_pv = my_par < 0 ? 0 : vidx_of[my_par];
+    int pos = 0, cnt = 0;
+    for (int e = 0; e < m; ++e) {
+      const int de = __builtin_amdgcn_readlane(my_dep, e);
+      if (de != dep) continue;
+      const int pve = __builtin_amdgcn_readlane(my_pv, e);
+      const int re = __builtin_amdgcn_readlane(my_rank, e);
+      ++cnt;
+      pos += (pve < my_pv) || (pve == my_pv && re < my_rank);
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
-      if (vidx[i] == -2 && dp[i] == dep) vidx[i] = vnew[i];
+    if (my_node >= 0 && my_dep == dep) {
+      my_vidx = base + pos;
+      vidx_of[my_node] = (short)my_vidx;
+    }
+    base += cnt;
     __syncthreads();
   }
-  // bitsets: parents first (their indices are smaller), one depth at a time
-  if (threadIdx.x == 0) anc_s[0] = 1ull;
+  // 3. ancestor bitsets (parents first), then emit
+  if (lane == 0) anc_s[0] = 1ull;
   __syncthreads();
   for (int dep = 1; dep <= D; ++dep) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      if (vidx[i] < 0 || dp[i] != dep) continue;
-      const int vi = vidx[i];
-      const int pv = par[i] < 0 ? 0 : vidx[par[i]];
-      anc_s[vi] = anc_s[pv] | (1ull << vi);
-    }
+    if (my_node >= 0 && my_dep == dep) anc_s[my_vidx] = anc_s[my_pv] | (1ull << my_vidx);
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    if (vidx[i] < 0) continue;
-    const int vi = vidx[i];
-    v_tok[b * M1 + vi] = P.tok[i];
-    v_parent[b * M1 + vi] = par[i] < 0 ? 0 : vidx[par[i]];
-    v_depth[b * M1 + vi] = dp[i];
-    v_pos[b * M1 + vi] = root_pos + dp[i];
-    v_anc[b * M1 + vi] = anc_s[vi];
+  if (my_node >= 0) {
+    v_tok[b * M1 + my_vidx] = P.tok[my_node];
+    v_parent[b * M1 + my_vidx] = my_pv;
+    v_depth[b * M1 + my_vidx] = my_dep;
+    v_pos[b * M1 + my_vidx] = root_pos + my_dep;
+    v_anc[b * M1 + my_vidx] = anc_s[my_vidx];
   }
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     v_tok[b * M1] = P.hdr[1];
     v_parent[b * M1] = -1;
     v_depth[b * M1] = 0;
@@ -266,8 +294,7 @@ hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32
     tree_step_kernel<<<B, TREE_THREADS, 0, st>>>(k, D, state, topk_id, topk_lp, next_tok,
                                                  next_parent_slot, next_pos, next_anc);
   else
-    tree_final_kernel<<<B, TREE_THREADS, 0, st>>>(k, D, m, state, v_tok, v_parent, v_depth, v_pos,
-                                                  v_anc);
+    tree_final_kernel<<<B, 64, 0, st>>>(k, D, m, state, v_tok, v_parent, v_depth, v_pos, v_anc);
   return hipGetLastError();
 }
 

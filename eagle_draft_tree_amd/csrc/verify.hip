@@ -2,13 +2,17 @@
 // drafter treated as a proposal, the standard verifier keeps the greedy
 // sequence, or -- with the residual correction -- the sampling distribution).
 //
-// One workgroup per request walks the tree from the root: at every visited
-// node it reduces that node's target-logit row (argmax, or fp64 weights and
-// their total), tries the node's children in sibling order and either moves
-// on or emits the bonus token.  Tree children are deterministic top-k picks,
-// so each candidate's proposal is a point mass: candidate x is accepted with
-// probability p(x) of the remaining support, and a rejected token leaves the
-// support -- the residual max(p - q, 0) renormalised.
+// Tree children are deterministic top-k picks, so each candidate's proposal
+// is a point mass: candidate x is accepted with probability p(x) of the
+// remaining support, and a rejected token leaves the support -- the
+// residual max(p - q, 0) renormalised.
+//
+// Kernel A (grid: requests x rows x partitions) reduces every verify row in
+// 4096-token partitions: argmax (value desc, id asc), NaN flag and, for
+// sampling, the partition max and sum of exp((L - max)/T) in fp64.
+// Kernel B (one workgroup per request) walks the tree on those partials; at
+// the last node of a sampling walk it locates the partition where the
+// residual CDF crosses u_res * Rm and scans only that partition.
 #include <limits.h>
 
 #include "common.hpp"
@@ -16,8 +20,10 @@
 
 namespace e3 {
 
-constexpr int VF_THREADS = 1024;
-constexpr int VF_WAVES = VF_THREADS / 64;
+constexpr int VR_THREADS = 256;
+constexpr int VR_PS = 4096;  // tokens per partition (16 per thread)
+constexpr int VW_THREADS = 1024;
+constexpr int VW_WAVES = VW_THREADS / 64;
 
 struct ArgRed {
   float v;
@@ -28,60 +34,149 @@ __device__ __forceinline__ ArgRed arg_better(ArgRed a, ArgRed b) {
   return better(b.v, b.id, a.v, a.id) ? b : a;
 }
 
-__global__ __launch_bounds__(VF_THREADS) void verify_kernel(int m, int V, int Dmax,
-                                                            const int32_t* v_tok,
-                                                            const int32_t* v_parent,
-                                                            const float* logits, int mode,
-                                                            float temperature, const double* u_try,
-                                                            const double* u_res,
-                                                            int32_t* accept_len, int32_t* accepted,
-                                                            int32_t* bonus, int32_t* status) {
+__device__ __forceinline__ ArgRed wave_arg(ArgRed a) {
+  wave_argmax(a.v, a.id);
+  return a;
+}
+
+// ---------------------------------------------------------------- kernel A
+__global__ __launch_bounds__(VR_THREADS) void verify_rows_kernel(
+    int V, int nparts, const float* __restrict__ logits, int sample, double invT,
+    float* __restrict__ pa_v, int* __restrict__ pa_id, float* __restrict__ pmax,
+    double* __restrict__ psum, int* __restrict__ pnan) {
+  const int part = blockIdx.x;
+  const size_t row = blockIdx.y;  // request * (m+1) + node
+  const float* x = logits + row * V;
+  const int lo = part * VR_PS;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float v[16];
+  const bool vec_ok = (V & 3) == 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int y0 = lo + 4 * (threadIdx.x + VR_THREADS * j);
+    if (vec_ok && y0 + 3 < V) {
+      const float4 f = *(const float4*)(x + y0);
+      v[4 * j] = f.x;
+      v[4 * j + 1] = f.y;
+      v[4 * j + 2] = f.z;
+      v[4 * j + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * j + c] = y0 + c < V ? x[y0 + c] : -INFINITY;
+    }
+  }
+  ArgRed best{-INFINITY, INT_MAX};
+  int nan = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int y = lo + 4 * (threadIdx.x + VR_THREADS * (e >> 2)) + (e & 3);
+    if (v[e] != v[e]) nan = 1;
+    else if (y < V && better(v[e], y, best.v, best.id)) best = ArgRed{v[e], y};
+  }
+  __shared__ ArgRed ared[VR_THREADS / 64];
+  __shared__ double dred[VR_THREADS / 64];
+  __shared__ int nred[VR_THREADS / 64];
+  best = wave_arg(best);
+  const int wn = __any(nan) ? 1 : 0;
+  if (lane == 0) {
+    ared[w] = best;
+    nred[w] = wn;
+  }
+  __syncthreads();
+  ArgRed b = ared[0];
+  int anynan = nred[0];
+#pragma unroll
+  for (int i = 1; i < VR_THREADS / 64; ++i) {
+    b = arg_better(b, ared[i]);
+    anynan |= nred[i];
+  }
+  const size_t o = row * nparts + part;
+  if (sample && !anynan) {
+    const double mx = (double)b.v;
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int y = lo + 4 * (threadIdx.x + VR_THREADS * (e >> 2)) + (e & 3);
+      if (y < V && v[e] > -INFINITY) s += exp(((double)v[e] - mx) * invT);
+    }
+    s = wave_sum_d(s);
+    if (lane == 0) dred[w] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int i = 0; i < VR_THREADS / 64; ++i) t += dred[i];
+      psum[o] = t;
+    }
+  }
+  if (threadIdx.x == 0) {
+    pa_v[o] = b.v;
+    pa_id[o] = b.id;
+    pmax[o] = b.v;
+    pnan[o] = anynan;
+  }
+}
+
+// ---------------------------------------------------------------- kernel B
+__global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
+    int m, int V, int Dmax, int nparts, const int32_t* __restrict__ v_tok,
+    const int32_t* __restrict__ v_parent, const float* __restrict__ logits, int mode, double invT,
+    const double* __restrict__ u_try, const double* __restrict__ u_res, const float* __restrict__ pa_v,
+    const int* __restrict__ pa_id, const float* __restrict__ pmax, const double* __restrict__ psum,
+    const int* __restrict__ pnan, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+    int32_t* status) {
   const int b = blockIdx.x;
   const int M1 = m + 1;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __shared__ ArgRed ared[VF_WAVES];
-  __shared__ double dred[VF_WAVES];
-  __shared__ int nan_s;
   __shared__ int kids[EAGLE3_MAX_TREE_SLOTS];
   __shared__ int nkids_s;
   __shared__ int rejected[EAGLE3_MAX_TREE_SLOTS];
-  __shared__ int nrej_s;
-  __shared__ double seg_s[VF_THREADS];
+  __shared__ double wpart[64];  // remaining weight of each partition (<= 64 partitions handled per pass)
+  __shared__ double wsum[VW_WAVES];
   __shared__ int bonus_s;
+  __shared__ ArgRed rowbest_s;
+  __shared__ double rm_s, mx_s;
+  __shared__ int nan_s;
 
   const int32_t* tok = v_tok + (size_t)b * M1;
   const int32_t* par = v_parent + (size_t)b * M1;
   int node = 0, nacc = 0, out_bonus = -1, st = 0;
-  const double invT = 1.0 / (double)temperature;
   for (int iter = 0; iter <= M1; ++iter) {
-    const float* row = logits + ((size_t)b * M1 + node) * V;
-    if (threadIdx.x == 0) nan_s = 0;
-    // children of `node` in sibling (= verify index) order
-    if (threadIdx.x == 0) {
-      int c = 0;
-      for (int i = 1; i < M1; ++i)
-        if (par[i] == node) kids[c++] = i;
-      nkids_s = c;
+    const size_t row = (size_t)b * M1 + node;
+    const float* L = logits + row * V;
+    if (w == 0) {
+      // children of `node` in verify-index order: ballot over the parent array
+      const int pi = (lane >= 1 && lane < M1) ? par[lane] : -2;
+      const unsigned long long km = __ballot(pi == node);
+      if (pi == node) kids[__popcll(km & ((1ull << lane) - 1ull))] = lane;
+      // the row's partitions: lanes own p = lane, lane + 64, ...
+      ArgRed bb{-INFINITY, INT_MAX};
+      int nn = 0;
+      for (int p = lane; p < nparts; p += 64) {
+        bb = arg_better(bb, ArgRed{pa_v[row * nparts + p], pa_id[row * nparts + p]});
+        nn |= pnan[row * nparts + p];
+      }
+      bb = wave_arg(bb);
+      const int anynan = __any(nn) ? 1 : 0;
+      double R = 0.0;
+      if (mode == EAGLE3_SAMPLE && !anynan) {
+        const double M = (double)bb.v;
+        for (int p = lane; p < nparts; p += 64) {
+          const float mp = pmax[row * nparts + p];
+          if (mp > -INFINITY) R += psum[row * nparts + p] * exp(((double)mp - M) * invT);
+        }
+        R = wave_sum_d(R);
+      }
+      if (lane == 0) {
+        nkids_s = __popcll(km);
+        rowbest_s = bb;
+        nan_s = anynan;
+        rm_s = R;
+        mx_s = (double)bb.v;
+      }
     }
     __syncthreads();
-    // argmax / max of the row (NaN flagged)
-    ArgRed best{-INFINITY, INT_MAX};
-    int hasnan = 0;
-    for (int y = threadIdx.x; y < V; y += VF_THREADS) {
-      const float v = row[y];
-      if (v != v) hasnan = 1;
-      else if (better(v, y, best.v, best.id)) best = ArgRed{v, y};
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      ArgRed d{__shfl_xor(best.v, o, 64), __shfl_xor(best.id, o, 64)};
-      best = arg_better(best, d);
-    }
-    if (hasnan) nan_s = 1;
-    if (lane == 0) ared[w] = best;
-    __syncthreads();
-    best = ared[0];
-    for (int i = 1; i < VF_WAVES; ++i) best = arg_better(best, ared[i]);
+    const ArgRed best = rowbest_s;
     if (nan_s) {
       st = EAGLE3_ENUMERIC;
       nacc = 0;
@@ -103,20 +198,14 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(int m, int V, int Dm
       out_bonus = best.id;
       break;
     }
-    // ---- sampling: w(y) = exp((L[y] - max) / T) in fp64
-    const double mx = (double)best.v;
-    double part = 0.0;
-    for (int y = threadIdx.x; y < V; y += VF_THREADS) part += exp(((double)row[y] - mx) * invT);
-    part = wave_sum_d(part);
-    if (lane == 0) dred[w] = part;
-    __syncthreads();
-    double Rm = 0.0;
-    for (int i = 0; i < VF_WAVES; ++i) Rm += dred[i];
+    // ---- sampling: w(y) = exp((L[y] - max) / T) in fp64; Rm = remaining mass
+    const double mx = mx_s;
+    double Rm = rm_s;
     int next = -1, nrej = 0;
     for (int c = 0; c < nk; ++c) {
       const int ci = kids[c];
       const int t = tok[ci];
-      const double wt = exp(((double)row[t] - mx) * invT);
+      const double wt = exp(((double)L[t] - mx) * invT);
       if (u_try[(size_t)b * M1 + ci] * Rm < wt) {
         next = ci;
         break;
@@ -125,54 +214,83 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(int m, int V, int Dm
       ++nrej;
       Rm = Rm - wt;
     }
+    __syncthreads();
     if (next >= 0) {
-      __syncthreads();
       if (threadIdx.x == 0) accepted[(size_t)b * Dmax + nacc] = next;
       ++nacc;
       node = next;
       continue;
     }
-    if (threadIdx.x == 0) nrej_s = nrej;
-    __syncthreads();
-    // bonus: inverse CDF over the remaining support in token-id order.
-    // Thread t owns the contiguous id segment [t*seg, (t+1)*seg); the
-    // cumulative weight of y is (sum of the earlier segments, in order) +
-    // (running sum inside y's segment).  The bonus is the smallest y whose
-    // cumulative weight exceeds u_res * Rm.
+    // bonus: the smallest y outside the rejected set whose cumulative weight
+    // (partitions in order; inside a partition, per-thread 4-token segments
+    // in order) exceeds u_res[node] * Rm.
     const double thr = u_res[(size_t)b * M1 + node] * Rm;
-    const int seg = (V + VF_THREADS - 1) / VF_THREADS;
-    const int lo = min(V, threadIdx.x * seg), hi = min(V, lo + seg);
-    const int nrj = nrej_s;
     auto weight = [&](int y) -> double {
-      for (int r = 0; r < nrj; ++r)
+      for (int r = 0; r < nrej; ++r)
         if (rejected[r] == y) return 0.0;
-      return exp(((double)row[y] - mx) * invT);
+      return exp(((double)L[y] - mx) * invT);
     };
-    double s = 0.0;
-    for (int y = lo; y < hi; ++y) s += weight(y);
-    seg_s[threadIdx.x] = s;
     if (threadIdx.x == 0) bonus_s = INT_MAX;
-    __syncthreads();
-    if (threadIdx.x == 0) {  // exclusive prefix over segments, in order
-      double acc = 0.0;
-      for (int t = 0; t < VF_THREADS; ++t) {
-        const double v = seg_s[t];
-        seg_s[t] = acc;
-        acc += v;
+    double before = 0.0;  // cumulative weight of the partitions already passed
+    for (int p0 = 0; p0 < nparts; p0 += 64) {
+      const int np = min(64, nparts - p0);
+      // remaining weight of each partition: its sum rescaled, minus rejected tokens in it
+      if (threadIdx.x < np) {
+        const int p = p0 + threadIdx.x;
+        const float mp = pmax[row * nparts + p];
+        double s = mp > -INFINITY ? psum[row * nparts + p] * exp(((double)mp - mx) * invT) : 0.0;
+        for (int r = 0; r < nrej; ++r)
+          if (rejected[r] / VR_PS == p) s -= exp(((double)L[rejected[r]] - mx) * invT);
+        wpart[threadIdx.x] = s > 0.0 ? s : 0.0;
       }
-    }
-    __syncthreads();
-    {
-      double acc = seg_s[threadIdx.x];
-      int first = INT_MAX;
-      for (int y = lo; y < hi; ++y) {
-        acc += weight(y);
-        if (acc > thr) {
-          first = y;
-          break;
+      __syncthreads();
+      bool done = false;
+      for (int q = 0; q < np && !done; ++q) {
+        const double s = wpart[q];
+        if (before + s <= thr) {
+          before += s;
+          continue;
         }
+        // the crossing lies in partition p0 + q (or just after, by rounding): scan it
+        const int lo = (p0 + q) * VR_PS;
+        const int y0 = lo + 4 * threadIdx.x;
+        double seg = 0.0;
+        double wy[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          wy[c] = y0 + c < V ? weight(y0 + c) : 0.0;
+          seg += wy[c];
+        }
+        // exclusive scan of the 1024 segment sums (waves, then wave totals)
+        double incl = seg;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        if (lane == 63) wsum[w] = incl;
+        __syncthreads();
+        double wbase = 0.0;
+        for (int i = 0; i < w; ++i) wbase += wsum[i];
+        double acc = before + wbase + (incl - seg);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc += wy[c];
+          if (wy[c] > 0.0 && acc > thr) {
+            atomicMin(&bonus_s, y0 + c);
+            break;
+          }
+        }
+        __syncthreads();
+        if (bonus_s != INT_MAX) {
+          done = true;
+        } else {
+          before += s;
+        }
+        __syncthreads();
       }
-      if (first != INT_MAX) atomicMin(&bonus_s, first);
+      if (done) break;
+      __syncthreads();
     }
     __syncthreads();
     if (bonus_s == INT_MAX && threadIdx.x == 0) {  // no crossing: last y with w > 0
@@ -196,12 +314,31 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(int m, int V, int Dm
   }
 }
 
+size_t verify_ws_bytes(int B, int m, int V) {
+  const size_t nparts = (V + VR_PS - 1) / VR_PS;
+  const size_t n = (size_t)B * (m + 1) * nparts;
+  return n * (4 + 4 + 4 + 8 + 4) + 1024;
+}
+
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
                          const int32_t* v_parent, const float* logits, int mode, float temperature,
                          const double* u_try, const double* u_res, int32_t* accept_len,
-                         int32_t* accepted, int32_t* bonus, int32_t* status, hipStream_t st) {
-  verify_kernel<<<B, VF_THREADS, 0, st>>>(m, V, Dmax, v_tok, v_parent, logits, mode, temperature,
-                                          u_try, u_res, accept_len, accepted, bonus, status);
+                         int32_t* accepted, int32_t* bonus, int32_t* status, void* ws,
+                         hipStream_t st) {
+  const int nparts = (V + VR_PS - 1) / VR_PS;
+  const size_t n = (size_t)B * (m + 1) * nparts;
+  double* psum = (double*)ws;
+  float* pa_v = (float*)(psum + n);
+  int* pa_id = (int*)(pa_v + n);
+  float* pmax = (float*)(pa_id + n);
+  int* pnan = (int*)(pmax + n);
+  const double invT = mode == EAGLE3_SAMPLE ? 1.0 / (double)temperature : 1.0;
+  dim3 ga(nparts, B * (m + 1));
+  verify_rows_kernel<<<ga, VR_THREADS, 0, st>>>(V, nparts, logits, mode == EAGLE3_SAMPLE, invT, pa_v, pa_id,
+                                                pmax, psum, pnan);
+  verify_walk_kernel<<<B, VW_THREADS, 0, st>>>(m, V, Dmax, nparts, v_tok, v_parent, logits, mode, invT, u_try,
+                                               u_res, pa_v, pa_id, pmax, psum, pnan, accept_len, accepted,
+                                               bonus, status);
   return hipGetLastError();
 }
 

@@ -16,9 +16,12 @@ from . import binding as B
 
 
 class Drafter:
-    """Device-resident drafter weights plus their eagle3_dims/eagle3_weights."""
+    """Device-resident drafter weights plus their eagle3_dims/eagle3_weights.
 
-    def __init__(self, shape, weights: dict, device="cuda"):
+    pack=True (bf16 only) converts the GEMM matrices once into the library's
+    MFMA fragment order (eagle3_pack_weights) and drops the row-major copies."""
+
+    def __init__(self, shape, weights: dict, device="cuda", pack=False):
         self.shape = shape
         self.tensors = {}
         for name, w in weights.items():
@@ -29,6 +32,13 @@ class Drafter:
         self.dims = B.dims_of(shape)
         self.weights = B.weights_of(self.tensors)
         self.torch_dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        self.packed = None
+        if pack and shape.dtype == "bf16":
+            self.packed = torch.empty(B.packed_weights_size(self.dims), dtype=torch.uint8, device=device)
+            self.weights = B.eagle3_pack_weights(self.dims, self.weights, self.packed)
+            torch.cuda.synchronize()
+            for n in ("fc", "qkv", "o", "gate_up", "down", "lm"):
+                del self.tensors[n]
 
 
 @dataclass
@@ -52,7 +62,8 @@ class CycleBuffers:
         self.g = torch.empty(Bn * n, s.d, dtype=drafter.torch_dtype, device=dv)
         self.h_tree = torch.zeros(Bn, B.MAX_TREE_SLOTS + 1, s.d, dtype=torch.float32, device=dv)
         max_rows = max(n, k)
-        self.ws = torch.empty(B.workspace_size(drafter.dims, Bn, max_rows, spec.cap_rows), dtype=torch.uint8,
+        # zero-filled once: holds split-K counters the library keeps at zero
+        self.ws = torch.zeros(B.workspace_size(drafter.dims, Bn, max_rows, spec.cap_rows), dtype=torch.uint8,
                               device=dv)
         self.root_ids = torch.empty(Bn, 1, k, **i32)
         self.root_lp = torch.empty(Bn, 1, k, dtype=torch.float32, device=dv)
@@ -72,6 +83,7 @@ class CycleBuffers:
         self.accepted = torch.empty(Bn, D, **i32)
         self.bonus = torch.empty(Bn, **i32)
         self.status = torch.empty(Bn, **i32)
+        self.vws = torch.empty(B.verify_workspace_size(Bn, m, s.vocab), dtype=torch.uint8, device=dv)
         self.commit_logits = None
         self.round_logits = None
 
@@ -109,7 +121,7 @@ def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit
     ctx_after [B] (committed rows incl. the new ones), root_tok/root_pos [B]."""
     sp = buf.spec
     Bn, n, k, D, m = sp.batch, sp.commit_rows, sp.k, sp.depth, sp.keep
-    B.eagle3_fuse(dr.dims, dr.weights, feats, Bn * n, buf.g)
+    B.eagle3_fuse(dr.dims, dr.weights, feats, Bn * n, buf.g, buf.ws)
     kv_commit = kv.struct()
     kv_tree = kv.struct(ctx_after)
     B.eagle3_draft_step(dr.dims, dr.weights, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos,
@@ -132,4 +144,4 @@ def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit
                          buf.v_tok, buf.v_parent, buf.v_depth, buf.v_pos, buf.v_anc)
     if verify and target_logits is not None:
         B.eagle3_verify(Bn, m, dr.shape.vocab, D, buf.v_tok, buf.v_parent, target_logits, mode, temperature,
-                        u_try, u_res, buf.accept_len, buf.accepted, buf.bonus, buf.status)
+                        u_try, u_res, buf.accept_len, buf.accepted, buf.bonus, buf.status, buf.vws)

@@ -36,6 +36,8 @@
  *    gives a thread-local message for the most recent failure.
  *  - Calls that share a workspace or tree-state buffer must be ordered on
  *    one stream; concurrent calls on one buffer race.
+ *  - Workspaces must be zero-filled once after allocation: their first
+ *    bytes hold split-K arrival counters that every call leaves at zero.
  */
 #ifndef EAGLE3_H
 #define EAGLE3_H
@@ -89,7 +91,11 @@ typedef struct eagle3_dims {
   float rms_eps, rope_theta;
 } eagle3_dims;
 
-/* Drafter weights (device, dtype of dims, [out, in] row-major):
+#define EAGLE3_LAYOUT_ROWMAJOR 0 /* matrices [out, in] row-major                       */
+#define EAGLE3_LAYOUT_PACKED 1   /* fc/qkv/o/gate_up/down/lm in MFMA fragment order     */
+
+/* Drafter weights (device, dtype of dims, [out, in] row-major unless
+ * layout == EAGLE3_LAYOUT_PACKED, see eagle3_pack_weights):
  *  fc      [d, 3d]           fusion projection (rows: output features; the
  *                            3d inputs are [f_low | f_mid | f_high])
  *  emb     [vocab, d]        frozen target token embedding
@@ -103,6 +109,7 @@ typedef struct eagle3_dims {
 typedef struct eagle3_weights {
   const void *fc, *emb, *qkv, *o, *gate_up, *down, *lm;
   const float *norm_e, *norm_s, *norm_ffn, *norm_out;
+  int32_t layout; /* EAGLE3_LAYOUT_ROWMAJOR or EAGLE3_LAYOUT_PACKED */
 } eagle3_weights;
 
 /* Draft KV cache of a batch of requests (device, dtype of dims).
@@ -122,6 +129,22 @@ typedef struct eagle3_kv {
   void *tk, *tv;
 } eagle3_kv;
 
+/* Bytes of the packed copy of fc, qkv, o, gate_up, down and lm (bf16 only). */
+int eagle3_packed_weights_size(const eagle3_dims *dims, size_t *bytes);
+
+/* Copy the six GEMM matrices of `src` (row-major, bf16) into `dst` (device,
+ * dst_bytes >= eagle3_packed_weights_size) in MFMA fragment order, and fill
+ * `packed` (host) with pointers into dst plus src's emb and norm gains,
+ * layout = EAGLE3_LAYOUT_PACKED.  Fragment order of a matrix W [N][K]: for
+ * each 16-row tile t, each 32-wide k chunk c and lane l < 64, the 16 bytes
+ * W[row(t, l%16)][32c + 8(l/16) .. +8], where row() is the identity except
+ * for qkv (rows i and i+hd/2 of one head share a tile at m and m+8) and
+ * gate_up (gate row j and up row F+j share a tile at m and m+8).  A weight
+ * streaming wave then reads each MFMA A operand as one contiguous 1 KB
+ * block.  Enqueued on `stream`; src must stay valid until it completes. */
+int eagle3_pack_weights(const eagle3_dims *dims, const eagle3_weights *src, void *dst, size_t dst_bytes,
+                        eagle3_weights *packed, eagle3_stream_t stream);
+
 /* Message for a return code (static string). */
 const char *eagle3_strerror(int code);
 /* Detail of the most recent failure on the calling thread ("" if none). */
@@ -130,9 +153,9 @@ const char *eagle3_last_error(void);
 const char *eagle3_version(void);
 
 /* Workspace bytes needed by eagle3_fuse / eagle3_draft_step / eagle3_topk for
- * batch B with at most max_rows query rows per request (fuse: n = B*max_rows
+ * batch B with at most max_rows query rows per request (fuse: n <= B*max_rows
  * feature rows).  Contiguous KV prefixes up to max_ctx rows (paged: the
- * largest logical length) are covered. */
+ * largest logical length) are covered.  Zero-fill a new workspace once. */
 int eagle3_workspace_size(const eagle3_dims *dims, int B, int max_rows, int max_ctx,
                           size_t *bytes);
 
@@ -146,8 +169,9 @@ int eagle3_ttt_workspace_size(const eagle3_dims *dims, int B, int S, int R, size
 /* Step 1 -- multi-layer feature fusion ("EAGLE-3 精读" §1):
  *   g[i] = [f_low(i) ; f_mid(i) ; f_high(i)] . fc^T       (no bias, no norm)
  * feats [n][3][d] (dtype), g [n][d] (dtype; bf16 rounds once, RNE).
- * fp32 accumulation.  n >= 1; up to 64 rows use the weight-streaming kernel,
- * more rows the tiled MFMA GEMM (bf16 only). */
+ * fp32 accumulation.  n >= 1, processed in 64-row chunks by the
+ * weight-streaming kernel.  ws: a zero-initialised workspace (see
+ * eagle3_workspace_size). */
 int eagle3_fuse(const eagle3_dims *dims, const eagle3_weights *w, const void *feats, int n,
                 void *g, void *ws, size_t ws_bytes, eagle3_stream_t stream);
 
@@ -229,11 +253,16 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t *roo
  *   leaves none: the last y with w > 0).  u_try, u_res [B][m+1] float64.
  * Outputs: accept_len [B], accepted [B][Dmax] (verify-node indices, -1
  * padded), bonus [B], status [B] (0, or EAGLE3_ENUMERIC when a visited row
- * holds a NaN; -inf logits mean probability 0). */
+ * holds a NaN; -inf logits mean probability 0; every row needs one finite
+ * logit).  A walk that reaches Dmax accepted nodes ends there as at a leaf.
+ * ws: scratch of eagle3_verify_workspace_size bytes (no initialisation). */
 int eagle3_verify(int B, int m, int V, int Dmax, const int32_t *v_tok, const int32_t *v_parent,
                   const float *target_logits, int mode, float temperature, const double *u_try,
                   const double *u_res, int32_t *accept_len, int32_t *accepted, int32_t *bonus,
-                  int32_t *status, eagle3_stream_t stream);
+                  int32_t *status, void *ws, size_t ws_bytes, eagle3_stream_t stream);
+
+/* Scratch bytes eagle3_verify needs for B requests, m kept nodes, vocab V. */
+int eagle3_verify_workspace_size(int B, int m, int V, size_t *bytes);
 
 /* Step 5 -- training-time-test forward ("EAGLE-3 精读" §2 and §5).
  * feats [B][S][3][d] (dtype), tokens [B][S].  Rows (j,i), j = 1..R: step 1
@@ -252,7 +281,8 @@ int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const v
 
 /* The top-k/log-prob reduction of eagle3_draft_step on caller logits:
  * logits [rows][V] float32 -> ids [rows][k], lp [rows][k], lse [rows] (lse
- * may be NULL).  Same order and tie rule.  k in 1..16. */
+ * may be NULL).  Same order and tie rule.  k in 1..16, V <= 262144 (also
+ * the vocabulary limit of eagle3_draft_step). */
 int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float *lp, float *lse,
                 void *ws, size_t ws_bytes, eagle3_stream_t stream);
 

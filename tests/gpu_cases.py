@@ -28,10 +28,10 @@ def say(*a):
 class GpuCycle:
     """Inputs of one cycle on the device plus the GPU run."""
 
-    def __init__(self, w, Wt, ci, keep_logits=True):
+    def __init__(self, w, Wt, ci, keep_logits=True, pack=False):
         s = w.shape
         self.w, self.s, self.ci = w, s, ci
-        self.dr = Drafter(s, Wt)
+        self.dr = Drafter(s, Wt, pack=pack)
         Bn, n = w.batch, w.commit_rows
         cap_rows = ci.cap
         self.spec = CycleSpec(Bn, n, w.topk, w.depth, w.keep, cap_rows)

@@ -19,16 +19,18 @@ TOL_BF16 = (2e-2, 1e-2)  # bf16 logits / fusion: atol, rtol
 
 # ---------------------------------------------------------------- fusion
 @pytest.mark.parametrize("n", [1, 10, 64, 130])
-def test_fuse_bf16(lib, n):
+@pytest.mark.parametrize("pack", [False, True])
+def test_fuse_bf16(lib, n, pack):
     from eagle_draft_tree_amd import binding as Bd
     from eagle_draft_tree_amd.cycle import Drafter
     shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=1024, dtype=BF16)
     Wt = gen.gen_weights(shape, seed=0)
-    say("fuse bf16 n", n)
-    dr = Drafter(shape, Wt)
+    say("fuse bf16 n", n, "pack", pack)
+    dr = Drafter(shape, Wt, pack=pack)
     feats = gen.draw(5, 1, (n, 3, 256), 1.0, BF16)
     g = torch.empty(n, 256, dtype=torch.bfloat16, device="cuda")
-    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), n, g)
+    ws = torch.zeros(Bd.workspace_size(dr.dims, 1, n, 0), dtype=torch.uint8, device="cuda")
+    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), n, g, ws)
     torch.cuda.synchronize()
     ref = O.fuse(shape, feats.f32(), Wt["fc"].f32())
     np.testing.assert_allclose(g.float().cpu().numpy(), ref, atol=TOL_BF16[0], rtol=TOL_BF16[1])
@@ -42,7 +44,8 @@ def test_fuse_fp32_tiny(lib):
     dr = Drafter(shape, Wt)
     feats = gen.draw(1, 11, (64, 3, 256), 1 / 16, F32)
     g = torch.empty(64, 256, dtype=torch.float32, device="cuda")
-    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), 64, g)
+    ws = torch.zeros(Bd.workspace_size(dr.dims, 1, 64, 0), dtype=torch.uint8, device="cuda")
+    Bd.eagle3_fuse(dr.dims, dr.weights, feats.torch("cuda"), 64, g, ws)
     torch.cuda.synchronize()
     ref = O.fuse(shape, feats.f32(), Wt["fc"].f32())
     np.testing.assert_allclose(g.cpu().numpy(), ref, atol=TOL_F32, rtol=TOL_F32)
@@ -132,9 +135,10 @@ def _run_verify(Bn, m, V, tok, par, L, mode, T=1.0, ut=None, ur=None, Dmax=None)
     i32 = dict(dtype=torch.int32, device="cuda")
     al = torch.empty(Bn, **i32); acc = torch.empty(Bn, Dmax, **i32)
     bo = torch.empty(Bn, **i32); st = torch.empty(Bn, **i32)
+    vws = torch.empty(Bd.verify_workspace_size(Bn, m, V), dtype=torch.uint8, device="cuda")
     Bd.eagle3_verify(Bn, m, V, Dmax, dev_i32(tok), dev_i32(par), torch.as_tensor(L).cuda(), mode, T,
                      torch.as_tensor(ut).cuda() if ut is not None else None,
-                     torch.as_tensor(ur).cuda() if ur is not None else None, al, acc, bo, st)
+                     torch.as_tensor(ur).cuda() if ur is not None else None, al, acc, bo, st, vws)
     torch.cuda.synchronize()
     return al.cpu().numpy(), acc.cpu().numpy(), bo.cpu().numpy(), st.cpu().numpy()
 
@@ -286,14 +290,16 @@ def test_c1_cycle_is_deterministic(lib):
 
 
 @pytest.mark.parametrize("hkv,commit,ctx", [(2, 24, 0), (1, 5, 40), (4, 1, 100)])
-def test_bf16_small_cycle(lib, hkv, commit, ctx):
-    """bf16 drafter (d=256) with synthetic prefix KV, multi-row commit and GQA."""
-    say("bf16 small cycle", hkv, commit, ctx)
+@pytest.mark.parametrize("pack", [False, True])
+def test_bf16_small_cycle(lib, hkv, commit, ctx, pack):
+    """bf16 drafter (d=256) with synthetic prefix KV, multi-row commit and GQA,
+    row-major and packed weight layouts."""
+    say("bf16 small cycle", hkv, commit, ctx, pack)
     shape = tiny_shape(d=256, hq=4, hkv=hkv, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
     w = scaled(C1_TINY, shape=shape, depth=4, topk=3, keep=12, prefix=ctx, commit_rows=commit,
                synthetic_prefix_kv=ctx > 0, feat_scale=1.0)
     Wt, W, ci = _cycle_and_oracle(w, seed=3)
-    gc = GpuCycle(w, Wt, ci)
+    gc = GpuCycle(w, Wt, ci, pack=pack)
     gc.run()
     exc = _compare_cycle(gc, w, W, ci, TOL_BF16)
     assert exc <= 1
