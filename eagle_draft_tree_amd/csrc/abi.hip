@@ -275,6 +275,8 @@ int eagle3_ttt_forward(const eagle3_dims* dims, const eagle3_weights* w, const v
   REQUIRE(feats && tokens && pred && ce && loss && ws, EAGLE3_EINVAL, "a required pointer is NULL");
   REQUIRE(B >= 1 && S >= 1 && R >= 1, EAGLE3_EINVAL, "B/S/R");
   REQUIRE(S % 64 == 0, EAGLE3_EUNSUPPORTED, "S=%d must be a multiple of 64", S);
+  REQUIRE(dims->d % 64 == 0 && dims->ffn % 64 == 0 && dims->d <= 8192, EAGLE3_EUNSUPPORTED,
+          "TTT needs d and ffn multiples of 64 and d <= 8192");
   const size_t need = e3::ttt_ws_bytes(*dims, B, S, R);
   REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rc = e3::ttt_forward(*dims, *w, feats, tokens, B, S, R, forced_tokens, pred, ce, loss, ws,

@@ -273,7 +273,12 @@ int eagle3_verify_workspace_size(int B, int m, int V, size_t *bytes);
  * Outputs: pred [B][R][S] (argmax of logits(j,i)), ce [B][R][S] = logsumexp
  * - logit[x_{i+j}] where i+j <= S-1 (0 elsewhere), loss[0] = mean of the
  * valid ce.  Logits are never materialised.  Requires dtype BF16, head_dim
- * 128 or 64, S a multiple of 64. */
+ * 128 or 64, d and ffn multiples of 64, d <= 8192, S a multiple of 64
+ * (EAGLE3_EUNSUPPORTED otherwise); token ids must lie in [0, vocab).
+ * Precision: bf16 operands, fp32 accumulation; the attention probabilities
+ * enter P.V as a bf16 hi + lo pair; log-sum-exp merged in fp64.
+ * ws: eagle3_ttt_workspace_size bytes, no initialisation needed.  All
+ * outputs are written with fixed reduction orders (bit-reproducible). */
 int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const void *feats,
                        const int32_t *tokens, int B, int S, int R, const int32_t *forced_tokens,
                        int32_t *pred, float *ce, float *loss, void *ws, size_t ws_bytes,
