@@ -1,0 +1,165 @@
+"""Full-size GPU parity at the benchmark shapes, in the launch configuration
+the benchmark times (packed weights, the same buffers and batch).
+
+The oracle cannot afford every output at these sizes, so each check samples
+requests or positions and compares stage by stage: the oracle decodes
+exactly the rows the GPU drafted (so a top-k near-tie cannot send the two
+sides down different trees), each stage from the GPU's own inputs to that
+stage (its g and parent states; the bf16 rounding cascade of an unisolated
+chain is described in gpu_cases.oracle_on_gpu_rows), logits agree within
+the bf16 tolerance, every
+GPU top-k is the oracle's top-k rule applied to the GPU's own float32 logits
+and a valid top-k of the oracle's logits, the tree built by the oracle from
+the GPU's own top-k equals the GPU tree bit for bit, and verification equals
+the oracle's on that tree."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import eagle3_oracle as O
+from workloads import gen
+from workloads.configs import C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT
+
+from gpu_cases import GpuCycle, check_cycle_stagewise, dev_i32, host_weights, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = (2e-2, 1e-2)  # bf16 logits / fusion / CE: atol, rtol
+
+
+def _setup(w, seed=1):
+    say("full size:", w.name, "generating weights")
+    Wt = gen.gen_weights(w.shape, seed=0)
+    ci = gen.gen_cycle_inputs(w, seed=seed)
+    gc = GpuCycle(w, Wt, ci, keep_logits=True, pack=True)
+    return Wt, ci, gc
+
+
+def _rerun_without_kept_logits(gc, L, mode, ut=None, ur=None):
+    """The benchmark runs without logits_out; the tree and the verification
+    outcome must not depend on it."""
+    before = (gc.tree(), gc.buf.accept_len.cpu().numpy(), gc.buf.accepted.cpu().numpy(), gc.buf.bonus.cpu().numpy())
+    saved = gc.buf.commit_logits, gc.buf.round_logits
+    gc.buf.commit_logits, gc.buf.round_logits = None, None
+    gc.run(L, mode, 1.0, ut, ur)
+    gc.buf.commit_logits, gc.buf.round_logits = saved
+    after = (gc.tree(), gc.buf.accept_len.cpu().numpy(), gc.buf.accepted.cpu().numpy(), gc.buf.bonus.cpu().numpy())
+    for name in before[0]:
+        np.testing.assert_array_equal(before[0][name], after[0][name])
+    for x, y in zip(before[1:], after[1:]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.timeout(600)
+def test_c2_8b_tree_full_size(lib):
+    w = C2_8B_TREE
+    Wt, ci, gc = _setup(w)
+    say("GPU cycle (draft), then plant agreement on the drafted tree")
+    gc.run()
+    t = gc.tree()
+    L = gen.target_logits(1, w.batch, w.keep + 1, w.shape.vocab, w.target_sigma)
+    gen.plant_agreement(L, t["tok"], t["parent"], ci.accept_prob, seed=1)
+    gc.run(L, 0)
+    assert int(gc.buf.status.max().item()) == 0
+    W = host_weights(Wt)
+    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=0)
+    say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+    _rerun_without_kept_logits(gc, L, 0)
+    say("sampling verification on the same tree")
+    ut, ur = gen.uniforms(2, w.batch, w.keep + 1)
+    gc.run(L, 1, 1.0, ut, ur)
+    t = gc.tree()
+    ra, rb = O.verify_sample(t["tok"][0], t["parent"][0], L[0], ut[0], ur[0])
+    assert int(gc.buf.accept_len[0].item()) == len(ra) and int(gc.buf.bonus[0].item()) == rb
+    np.testing.assert_array_equal(gc.buf.accepted[0, :len(ra)].cpu().numpy(), ra)
+
+
+@pytest.mark.timeout(600)
+def test_c3_8b_chain_paged_batch64_full_size(lib):
+    w = C3_8B_CHAIN
+    Wt, ci, gc = _setup(w)
+    gc.run()
+    t = gc.tree()
+    L = gen.target_logits(1, w.batch, w.keep + 1, w.shape.vocab, w.target_sigma)
+    gen.plant_agreement(L, t["tok"], t["parent"], ci.accept_prob, seed=1)
+    gc.run(L, 0)
+    assert int(gc.buf.status.max().item()) == 0
+    W = host_weights(Wt)
+    # sampled requests: first, last and one in between (prefix lengths differ)
+    reqs = [0, 37, w.batch - 1]
+    say("prefix lengths of the sampled requests:", [int(ci.ctx_len[b]) for b in reqs])
+    exc = check_cycle_stagewise(gc, w, W, ci, reqs, TOL, L=L, mode=0)
+    say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+    # every request: the verification outcome equals the oracle's on the GPU tree
+    t = gc.tree()
+    al = gc.buf.accept_len.cpu().numpy()
+    bonus = gc.buf.bonus.cpu().numpy()
+    for b in range(w.batch):
+        ra, rb = O.verify_greedy(t["tok"][b], t["parent"][b], L[b])
+        assert al[b] == len(ra) and bonus[b] == rb, f"request {b}"
+    _rerun_without_kept_logits(gc, L, 0)
+
+
+@pytest.mark.timeout(900)
+def test_c4_70b_tree_sampling_full_size(lib):
+    w = C4_70B_TREE
+    Wt, ci, gc = _setup(w)
+    gc.run()
+    L = gen.target_logits(1, w.batch, w.keep + 1, w.shape.vocab, w.target_sigma)
+    ut, ur = gen.uniforms(1, w.batch, w.keep + 1)
+    gc.run(L, 1, w.temperature, ut, ur)
+    assert int(gc.buf.status.max().item()) == 0
+    W = host_weights(Wt)
+    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=1, u_try=ut, u_res=ur)
+    say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+
+
+@pytest.mark.timeout(900)
+def test_c5_ttt_full_size_sampled(lib):
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.cycle import Drafter
+    w = C5_8B_TTT
+    s = w.shape
+    B, S, R = w.batch, w.ttt_seq, w.ttt_steps
+    say("full size TTT: weights")
+    Wt = gen.gen_weights(s, seed=0)
+    ti = gen.gen_ttt_inputs(s, B, S, R, seed=1)
+    dr = Drafter(s, Wt, pack=True)
+    pred = torch.empty(B, R, S, dtype=torch.int32, device="cuda")
+    ce = torch.empty(B, R, S, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(Bd.ttt_workspace_size(dr.dims, B, S, R), dtype=torch.uint8, device="cuda")
+    say("GPU TTT forward B", B, "S", S, "R", R)
+    Bd.eagle3_ttt_forward(dr.dims, dr.weights, ti.feats.torch("cuda"), dev_i32(ti.tokens), B, S, R, None, pred, ce,
+                          loss, ws)
+    torch.cuda.synchronize()
+    gp, gce = pred.cpu().numpy(), ce.cpu().numpy()
+    # properties at every position: ce >= 0 where a target exists, 0 elsewhere, loss = their mean
+    valid = np.zeros((R, S), bool)
+    for j in range(1, R + 1):
+        valid[j - 1, :S - j] = True
+    assert np.all(gce[:, ~valid] == 0.0)
+    assert np.all(gce[:, valid] > -1e-3)
+    assert np.all((gp >= 0) & (gp < s.vocab))
+    np.testing.assert_allclose(loss.item(), gce[:, valid].astype(np.float64).mean(), rtol=1e-5)
+    del dr
+    torch.cuda.empty_cache()
+    W = host_weights(Wt)
+    tie = 1e-2
+    for b, positions in ((0, [3, 1029, 2040]), (B - 1, [0, 700, 2047])):
+        say("  oracle TTT sequence", b, "positions", positions)
+        o = O.ttt_forward(s, W, ti.feats.f32()[b], ti.tokens[b], R, positions=positions)
+        for col, i in enumerate(positions):
+            for j in range(R):
+                if o["valid"][j, col]:
+                    np.testing.assert_allclose(gce[b, j, i], o["ce"][j, col], atol=TOL[0], rtol=TOL[1],
+                                               err_msg=f"ce b={b} step={j + 1} i={i}")
+                else:
+                    assert gce[b, j, i] == 0.0
+                if gp[b, j, i] != o["pred"][j, col]:
+                    l32 = np.asarray(o["logits"][col * R + j], np.float64).astype(np.float32)
+                    srt = np.sort(l32)[::-1]
+                    assert srt[0] - srt[1] <= tie and l32[gp[b, j, i]] >= srt[0] - tie, \
+                        f"pred b={b} step={j + 1} i={i} differs without a near-tie"
+                    say("   near-tie at step", j + 1, "position", i, ": later steps follow another chain")
+                    break

@@ -9,7 +9,7 @@ from oracle import eagle3_oracle as O
 from workloads import gen
 from workloads.configs import BF16, C1_TINY, F32, scaled, tiny_shape
 
-from gpu_cases import GpuCycle, dev_i32, host_weights, oracle_cycle, say, topk_agrees
+from gpu_cases import GpuCycle, compare_cycle, cycle_and_oracle, dev_i32, host_weights, oracle_cycle, say, topk_agrees
 
 pytestmark = pytest.mark.gpu
 
@@ -206,61 +206,15 @@ def test_verify_nan_and_neg_inf(lib):
 
 
 # ---------------------------------------------------------------- whole cycles
-def _cycle_and_oracle(w, seed=1):
-    Wt = gen.gen_weights(w.shape, seed=0)
-    W = host_weights(Wt)
-    ci = gen.gen_cycle_inputs(w, seed=seed)
-    return Wt, W, ci
-
-
-def _compare_cycle(gc, w, W, ci, tol, logit_check=True):
-    """Compare every stage of request 0..B-1; returns number of excused near-ties."""
-    excused = 0
-    buf = gc.buf
-    for b in range(w.batch):
-        vt, rec = oracle_cycle(w, W, ci, b)
-        atol, rtol = tol
-        g_gpu = buf.g.float().cpu().numpy()[b * w.commit_rows:(b + 1) * w.commit_rows]
-        np.testing.assert_allclose(g_gpu, rec["g"], atol=atol, rtol=rtol)
-        cl = buf.commit_logits[b, 0].cpu().numpy()
-        np.testing.assert_allclose(cl, rec["commit_logits"][-1], atol=atol, rtol=rtol)
-        np.testing.assert_allclose(buf.h_tree[b, 0].cpu().numpy(), rec["commit_h2"][-1], atol=atol, rtol=rtol)
-        exact, exc = topk_agrees(buf.root_ids[b, 0].cpu().numpy(), rec["commit_logits"][-1], w.topk, 2 * atol)
-        if not exact:
-            assert exc, "root top-k differs without a near-tie"
-            excused += 1
-            continue
-        diverged = False
-        for r, rd in enumerate(rec["rounds"]):
-            gl = buf.round_logits[r][b].cpu().numpy()
-            np.testing.assert_allclose(gl, rd["logits"], atol=atol, rtol=rtol)
-            for row in range(w.topk):
-                exact, exc = topk_agrees(buf.round_ids[r][b, row].cpu().numpy(), rd["logits"][row], w.topk,
-                                         2 * atol)
-                if not exact:
-                    assert exc, f"round {r} row {row} top-k differs without a near-tie"
-                    diverged = True
-            if diverged:
-                break
-        if diverged:
-            excused += 1
-            continue
-        t = gc.tree()
-        for n in ("tok", "parent", "depth", "pos"):
-            np.testing.assert_array_equal(t[n][b], vt[n], err_msg=n)
-        np.testing.assert_array_equal(t["anc"][b], vt["anc"])
-    return excused
-
-
 def test_c1_tiny_cycle_greedy_and_sample(lib):
     w = C1_TINY
     say("C1 cycle")
-    Wt, W, ci = _cycle_and_oracle(w)
+    Wt, W, ci = cycle_and_oracle(w)
     gc = GpuCycle(w, Wt, ci)
     L = gen.target_logits(1, 1, w.keep + 1, w.shape.vocab, w.target_sigma)
     ut, ur = gen.uniforms(1, 1, w.keep + 1)
     gc.run(L, 0)
-    assert _compare_cycle(gc, w, W, ci, (TOL_F32, TOL_F32)) == 0
+    assert compare_cycle(gc, w, W, ci, (TOL_F32, TOL_F32)) == 0
     vt, _ = oracle_cycle(w, W, ci)
     ra, rb = O.verify_greedy(vt["tok"], vt["parent"], L[0])
     assert gc.buf.accept_len[0].item() == len(ra) and gc.buf.bonus[0].item() == rb
@@ -280,7 +234,7 @@ def test_c1_tiny_cycle_greedy_and_sample(lib):
 
 def test_c1_cycle_is_deterministic(lib):
     w = C1_TINY
-    Wt, W, ci = _cycle_and_oracle(w, seed=2)
+    Wt, W, ci = cycle_and_oracle(w, seed=2)
     gc = GpuCycle(w, Wt, ci)
     gc.run()
     a = [t.clone() for t in (gc.buf.h_tree, gc.buf.round_logits[0], gc.buf.v_tok)]
@@ -298,8 +252,8 @@ def test_bf16_small_cycle(lib, hkv, commit, ctx, pack):
     shape = tiny_shape(d=256, hq=4, hkv=hkv, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
     w = scaled(C1_TINY, shape=shape, depth=4, topk=3, keep=12, prefix=ctx, commit_rows=commit,
                synthetic_prefix_kv=ctx > 0, feat_scale=1.0)
-    Wt, W, ci = _cycle_and_oracle(w, seed=3)
+    Wt, W, ci = cycle_and_oracle(w, seed=3)
     gc = GpuCycle(w, Wt, ci, pack=pack)
     gc.run()
-    exc = _compare_cycle(gc, w, W, ci, TOL_BF16)
+    exc = compare_cycle(gc, w, W, ci, TOL_BF16)
     assert exc <= 1
