@@ -651,12 +651,15 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     {
       TimedScope ts(EAGLE3_KC_TTT_CE, st);
       E3_CHECK(bg_launch(L.x, d, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st));
+    }
+    {
+      TimedScope ts(EAGLE3_KC_ROWOPS, st);
       ce_merge_kernel<<<M, 256, 0, st>>>(L.part, nblk, L.lab, forced, S, R, j, pred, ce, j < R ? L.tok : nullptr);
       E3_CHECK(hipGetLastError());
     }
   }
   {
-    TimedScope ts(EAGLE3_KC_TTT_CE, st);
+    TimedScope ts(EAGLE3_KC_ROWOPS, st);
     double count = 0;
     for (int j = 1; j <= R; ++j) count += (double)B * (S - j > 0 ? S - j : 0);
     ttt_loss_kernel<<<1, 1024, 0, st>>>(ce, (size_t)B * R * S, count, loss);

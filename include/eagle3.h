@@ -300,7 +300,7 @@ int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float
  * (host memory/handles only); recording adds two hipEventRecord calls per
  * launch.  Not thread safe; meant for benchmarks and profiling. */
 #define EAGLE3_KC_FUSE 0
-#define EAGLE3_KC_ROWOPS 1  /* prologue and RMSNorm row kernels      */
+#define EAGLE3_KC_ROWOPS 1  /* prologue, RMSNorm and other row kernels (TTT: also the CE merge) */
 #define EAGLE3_KC_QKV 2     /* QKV GEMM with RoPE / KV scatter        */
 #define EAGLE3_KC_ATTN 3    /* attention partials + merge            */
 #define EAGLE3_KC_O 4
@@ -310,9 +310,9 @@ int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float
 #define EAGLE3_KC_TOPK 8
 #define EAGLE3_KC_TREE 9
 #define EAGLE3_KC_VERIFY 10
-#define EAGLE3_KC_TTT_GEMM 11
-#define EAGLE3_KC_TTT_ATTN 12
-#define EAGLE3_KC_TTT_CE 13
+#define EAGLE3_KC_TTT_GEMM 11 /* TTT fusion, QKV, O, gate/up, down GEMMs  */
+#define EAGLE3_KC_TTT_ATTN 12 /* TTT rollout-mask attention              */
+#define EAGLE3_KC_TTT_CE 13   /* TTT LM-head GEMM with the CE epilogue    */
 #define EAGLE3_KC_COUNT 14
 
 /* max_launches > 0 enables class `kc` with room for that many launches
