@@ -4,14 +4,15 @@
 // (eagle3_pack_weights) or row-major read through a row map.  fp32
 // accumulation on v_mfma_f32_16x16x32_bf16.
 //
-// Workgroup tile 256 x 256, four waves in a 2 x 2 grid (wave tile 128 x 128
-// = 8 x 8 MFMA tiles, 256 accumulator registers), K step 64.  Both operands
-// are staged in LDS in MFMA fragment order (a 16 x 32 fragment is 64 lanes x
-// 16 bytes; lane l holds row l%16, k-slice 8(l/16)), so an MFMA operand is
-// one 16-byte LDS read per lane.  A-tile fragments are stored with an XOR
-// swizzle on the lane slot that keeps both the row-wise stores and the
-// fragment reads free of bank conflicts.  LDS is double-buffered: the
-// global loads of step s+1 are in flight during the MFMAs of step s.
+// Workgroup tile 256 x 256, eight waves in a 2 x 4 grid (wave tile 128 x 64
+// = 8 x 4 MFMA tiles, 128 accumulator registers, two waves per SIMD), K
+// step 32.  Both operands are staged in LDS in MFMA fragment order (a 16 x
+// 32 fragment is 64 lanes x 16 bytes; lane l holds row l%16, k-slice
+// 8(l/16)) by direct global -> LDS copies (no VGPR staging), so an MFMA
+// operand is one linear, conflict-free 16-byte LDS read per lane.  Four
+// stages of LDS (128 KB) keep three k steps of copies in flight while one
+// is computed; inside a step the next A fragment is read while the current
+// one feeds its MFMAs.
 //
 // Block order: 8 row tiles share a column tile (grouped order), and block
 // ids are remapped so that consecutive logical tiles run on the same XCD
@@ -22,24 +23,56 @@
 
 namespace e3 {
 
-constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64;
-constexpr int BG_THREADS = 256;
-constexpr int BG_FRAGS = (BG_BM / 16) * (BG_BK / 32);  // 32 fragments per operand per stage
-constexpr int BG_STAGE_U4 = 2 * BG_FRAGS * 64;           // A + B of one stage, in uint4
+constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32;
+constexpr int BG_THREADS = 512;                   // 8 waves: 2 (rows) x 4 (columns)
+constexpr int BG_NJ = 4;                          // 16-column tiles per wave (64 columns)
+constexpr int BG_FRAGS = BG_BM / 16;              // 16 fragments per operand per stage
+constexpr int BG_STAGE_U4 = 2 * BG_FRAGS * 64;    // A + B of one stage, in uint4 (32 KB)
+constexpr int BG_NSTAGE = 4;                      // 128 KB of LDS, three stages in flight
 
 static inline int bg_grid(int M, int N) { return ((M + BG_BM - 1) / BG_BM) * ((N / 16 + 15) / 16); }
 
-// Lane slot of fragment lane `pos` (row pos%16, k-slice pos/16) of k-chunk
-// `cc` in the swizzled A layout.
-__device__ __forceinline__ int bg_swz(int pos, int cc) { return pos ^ ((pos >> 4) | (cc << 2) | ((pos & 1) << 3)); }
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
+// of the wave lands at LDS byte address lds + 16 l (lds wave-uniform, in
+// M0, restored afterwards).  Issued from inline assembly so that the
+// compiler does not insert conservative vmcnt waits before unrelated LDS
+// reads; completion is awaited explicitly (bg_wait_copies), and extra copies
+// in flight only make the compiler's own vmcnt waits stricter.  The
+// instruction has no register results.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void bg_wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Every LDS read of this wave has completed, then the workgroup barrier.
+__device__ __forceinline__ void bg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef f32x4 BGAcc[8][BG_NJ];
 
 template <bool PACKED, class Epi>
 __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __restrict__ A, int lda, int M,
                                                               const bf16* __restrict__ W, int N, int K, RowMap map,
                                                               Epi epi) {
-  __shared__ uint4 smem[2 * BG_STAGE_U4];  // 128 KB
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  __shared__ uint4 smem[BG_NSTAGE * BG_STAGE_U4];  // 128 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int nt16 = N / 16;
   const int ntn = (nt16 + 15) / 16;
   const int ntm = (M + BG_BM - 1) / BG_BM;
@@ -54,79 +87,79 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   const int bn = (bid % per_group) / gsz;
   const int nchunks = K / 32;
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][BG_NJ];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < BG_NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Per-thread global sources.  A: element e = tid + 256 j is row e/8 =
-  // tid/8 + 32 j, 16-byte segment tid%8 of the 64-wide k step; its LDS slot
-  // advances by 256 per j.  B: element e is fragment e/64 (n-tile
-  // tid/128 + 2 j, k-chunk (tid/64)%2), lane tid%64.
-  const int ar0 = tid >> 3, as = tid & 7;
-  const int arow0 = bm * BG_BM + ar0;
-  const bf16* abase = A + (size_t)arow0 * lda + 8 * as;
-  const int adst0 = (((ar0 >> 4) * 2 + (as >> 2)) << 6) + bg_swz((ar0 & 15) + 16 * (as & 3), as >> 2);
-  const int bt0 = bn * 16 + (tid >> 7), bcc = (tid >> 6) & 1, bl = tid & 63;
-  const bf16* bbase = W + (((size_t)bt0 * nchunks + bcc) * 64 + bl) * 8;  // packed
-  const size_t bstep = (size_t)2 * nchunks * 512;                         // packed, per j
-
-  uint4 ra[8], rb[8];
-  auto load_stage = [&](int ks) {
-    const int k0 = ks * BG_BK;
+  // Copy sources.  Per stage (32 k) wave w copies A fragments (m-tiles 2w,
+  // 2w+1) and B fragments (n-tiles 2w, 2w+1); lane l of a fragment is row
+  // (or weight row) l%16, k-slice 8(l/16).  Rows past M and n-tiles past N
+  // read the last valid ones (their results are dropped by the epilogue).
+  const bf16* asrc[2];
+  const bf16* bsrc[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ra[j] = arow0 + 32 * j < M ? *(const uint4*)(abase + (size_t)32 * j * lda + k0) : make_uint4(0, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) {
+    const int mt = wave * 2 + h;
+    const int row = min(bm * BG_BM + mt * 16 + (lane & 15), M - 1);
+    asrc[h] = A + (size_t)row * lda + 8 * (lane >> 4);
+    const int ntile = min(bn * 16 + wave * 2 + h, nt16 - 1);
+    if (PACKED)
+      bsrc[h] = W + ((size_t)ntile * nchunks * 64 + lane) * 8;
+    else
+      bsrc[h] = W + (size_t)map(ntile, lane & 15) * K + 8 * (lane >> 4);
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue_stage = [&](int ks) {
+    const uint32_t sa = lds0 + (uint32_t)((ks % BG_NSTAGE) * BG_STAGE_U4 * 16);
+    const uint32_t sb = sa + BG_FRAGS * 64 * 16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int nt = bt0 + 2 * j;
-      if (nt >= nt16) {
-        rb[j] = make_uint4(0, 0, 0, 0);
-      } else if (PACKED) {
-        rb[j] = ld_stream(bbase + j * bstep + (size_t)(k0 / 32) * 512);
-      } else {
-        rb[j] = *(const uint4*)(W + (size_t)map(nt, bl & 15) * K + k0 + bcc * 32 + 8 * (bl >> 4));
-      }
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t f = (uint32_t)(wave * 2 + h) * 1024u;
+      dma16(asrc[h] + ks * BG_BK, sa + f);
+      if (PACKED)
+        dma16(bsrc[h] + (size_t)ks * 512, sb + f);
+      else
+        dma16(bsrc[h] + ks * BG_BK, sb + f);
     }
   };
-  auto store_stage = [&](int buf) {
-    uint4* sa = smem + (size_t)buf * BG_STAGE_U4;
-    uint4* sb = sa + BG_FRAGS * 64;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sa[adst0 + 256 * j] = ra[j];
-      sb[tid + BG_THREADS * j] = rb[j];
-    }
-  };
-
-  const int nk = K / BG_BK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) load_stage(ks + 1);
-    const uint4* sa = smem + (size_t)(ks & 1) * BG_STAGE_U4;
+  // One stage: 8 steps (m-tile i) of BG_NJ MFMAs; the next A fragment is
+  // read while the current one feeds its MFMAs.
+  auto compute_stage = [&](int ks) {
+    const uint4* sa = smem + (size_t)(ks % BG_NSTAGE) * BG_STAGE_U4 + lane;
     const uint4* sb = sa + BG_FRAGS * 64;
+    U4 b[BG_NJ], a[2];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      U4 a[8], b[8];
-      const int aslot = bg_swz(lane, cc);
+    for (int j = 0; j < BG_NJ; ++j) b[j].u = sb[(wn * BG_NJ + j) << 6];
+    a[0].u = sa[(wm * 8) << 6];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i].u = sa[(((wm * 8 + i) * 2 + cc) << 6) + aslot];
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8) a[(i + 1) & 1].u = sa[(wm * 8 + i + 1) << 6];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j].u = sb[(((wn * 8 + j) * 2 + cc) << 6) + lane];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i].v, b[j].v, acc[i][j], 0, 0, 0);
+      for (int j = 0; j < BG_NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1].v, b[j].v, acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < nk) store_stage((ks + 1) & 1);
-    __syncthreads();
+  };
+
+  // Pipeline: stages s+1..s+3 are being copied while stage s is computed.
+  // Each wave has 4 copies per stage in flight; before the barrier that
+  // ends step s it waits until stage s+1's copies have landed.
+  const int nk = K / BG_BK;
+  const int npre = nk < BG_NSTAGE - 1 ? nk : BG_NSTAGE - 1;
+  for (int ks = 0; ks < npre; ++ks) issue_stage(ks);
+  if (npre >= 3) bg_wait_copies<8>();
+  else bg_wait_copies<0>();
+  bg_barrier();
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + BG_NSTAGE - 1 < nk) issue_stage(ks + BG_NSTAGE - 1);
+    compute_stage(ks);
+    if (ks + BG_NSTAGE - 1 < nk) bg_wait_copies<8>();  // stages ks+2, ks+3 may still be in flight
+    else bg_wait_copies<0>();
+    bg_barrier();
   }
   // lane l holds C[rowbase + 16 i + 4(l/16) + e][n of column tile colbase16 + j, slot l%16]
-  epi(acc, bm * BG_BM + wm * 128, bn * 16 + wn * 8, lane, M, nt16);
+  epi(acc, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
 }
 
 // Lane l receives lane l^8 of its 16-lane row (DPP row_ror:8).
@@ -156,8 +189,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_f<DPP_ROW_MIRROR>(v);
 }
 
-typedef f32x4 BGAcc[8][8];
-
 // --------------------------------------------------------------------------- epilogues
 // C (plain map) -> float buffer, rounded to bf16 values when `round` is set.
 struct BEpiStoreF {
@@ -171,7 +202,7 @@ struct BEpiStoreF {
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < BG_NJ; ++j) {
         const int col16 = colbase16 + j;
         if (col16 >= nt16) continue;
 #pragma unroll
@@ -196,7 +227,7 @@ struct BEpiResid {
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < BG_NJ; ++j) {
         const int col16 = colbase16 + j;
         if (col16 >= nt16) continue;
 #pragma unroll
@@ -222,7 +253,7 @@ struct BEpiSwiGLU {
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < BG_NJ; ++j) {
         f32x4 up;
 #pragma unroll
         for (int e = 0; e < 4; ++e) up[e] = xor8(acc[i][j][e]);

@@ -45,14 +45,14 @@ struct TLayout {
   bf16* v1t;     // [B][hkv][hd][S] step-1 values, transposed
   bf16* kc;      // [R-1][M][hkv][hd] chain keys of steps 2..R
   bf16* vc;      // [R-1][M][hkv][hd] chain values
-  float4* part;  // [M][nblk] LM-head partials {max, sum exp, argmax id, 0}
+  float4* part;  // [M][nblk] LM-head partials per 64 columns {max, sum exp, argmax id, 0}
   float* lab;    // [M] target logit
   int32_t* tok;  // [M] input tokens of the next step
   float2* rope;  // [S+R][hd/2] (cos, sin)
   size_t bytes;
 };
 
-inline int ce_blocks(int V) { return (V / 16 + 7) / 8; }
+inline int ce_blocks(int V) { return (V / 16 + BG_NJ - 1) / BG_NJ; }
 
 TLayout layout_of(const eagle3_dims& dm, int B, int S, int R, void* base) {
   Carve c;
@@ -214,7 +214,7 @@ struct TEpiQKV {
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < BG_NJ; ++j) {
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = xor8(acc[i][j][e]);
@@ -267,7 +267,7 @@ struct TEpiQKV {
   }
 };
 
-// LM head with the cross entropy folded in: for every row and each 128-column
+// LM head with the cross entropy folded in: for every row and each 64-column
 // block (one wave's tile width) write {max, sum exp(x - max), argmax id};
 // the lane that owns a row's target column writes the target logit.
 struct TEpiCE {
@@ -277,7 +277,7 @@ struct TEpiCE {
   int S, step, nblk;
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
-    const int m = lane & 15, blk = colbase16 >> 3;
+    const int m = lane & 15, blk = colbase16 / BG_NJ;
     if (blk >= nblk) return;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -289,7 +289,7 @@ struct TEpiCE {
         float mx = -INFINITY;
         int id = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < BG_NJ; ++j) {
           const int col16 = colbase16 + j, n = col16 * 16 + m;
           if (col16 < nt16) {
             const float xv = acc[i][j][e];
@@ -303,7 +303,7 @@ struct TEpiCE {
         row16_argmax(mx, id);
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < BG_NJ; ++j)
           if (colbase16 + j < nt16) s += __expf(acc[i][j][e] - mx);
         s = row16_sum(s);
         if (m == 0 && row < M) part[(size_t)row * nblk + blk] = make_float4(mx, s, __int_as_float(id), 0.f);
@@ -323,12 +323,12 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
   __shared__ double ws[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float4* p = part + (size_t)row * nblk;
-  float4 loc[8];
+  float4 loc[16];  // nblk <= 4096 (vocab <= 262144 in 64-column blocks)
   int nl = 0;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < 16; ++c) {
     const int k = tid + 256 * c;
     loc[c] = k < nblk ? p[k] : make_float4(-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f);
     if (k < nblk) nl = c + 1;
@@ -352,7 +352,9 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
       gi = wi[c];
     }
   double s = 0.0;
-  for (int c = 0; c < nl; ++c) s += (double)loc[c].y * exp((double)loc[c].x - (double)gv);
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    if (c < nl) s += (double)loc[c].y * exp((double)loc[c].x - (double)gv);
   s = wave_sum_d(s);
   if (lane == 0) ws[w] = s;
   __syncthreads();
