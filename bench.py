@@ -85,11 +85,17 @@ def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
                       f"affinity={len(os.sched_getaffinity(0))}, {model}"}
 
 
-def cycle_bench(w, dr, steps, warmup, n_plant=8):
+def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
     """Time `steps` cycles of workload w; returns the measurement dict and the
     cycle inputs.  Target logits: n_plant seeded sets, each planted (when the
     workload plants agreement) on the tree the drafter builds; the timed loop
-    cycles through them, and tokens/cycle is their mean accept length + 1."""
+    cycles through them, and tokens/cycle is their mean accept length + 1.
+
+    Two timed passes: eager launches with per-kernel-class HIP-event timing
+    (the breakdown and the LM-head roofline), then, with graph=True, the same
+    cycles replayed from one captured HIP graph per target-logit set (the
+    step rate).  Every replay's verification outcome is checked against the
+    eager one."""
     import numpy as np
     import torch
 
@@ -153,7 +159,32 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8):
     for name, c in KC.items():
         per_class[name] = Bd.timing_read(c)
         Bd.timing_enable(c, 0)
-    ms = total_ms / steps
+    ms_eager = total_ms / steps
+    ms = ms_eager
+    if graph:
+        graphs = []
+        for L in Ls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cycle(L)
+            graphs.append(g)
+        for p in range(n_plant):  # every graph reproduces the eager outcome
+            graphs[p].replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(buf.accept_len.cpu().numpy().astype(np.float64), accepted[p]), "graph replay differs"
+        for i in range(warmup):
+            graphs[i % n_plant].replay()
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            graphs[i % n_plant].replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        graphs[(steps - 1) % n_plant].replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.accept_len.cpu().numpy().astype(np.float64), accepted[(steps - 1) % n_plant])
+        del graphs
 
     # algorithmic bytes: bf16 weights read once per round, every request's KV once per round
     es = 2
@@ -175,6 +206,8 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8):
         "workload": w.name,
         "steps": steps,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "graph": graph,
         "draft_tree_steps_per_s": round(1000.0 / ms, 2),
         "verified_tokens_per_s": round(1000.0 / ms * tokens_per_cycle, 1),
         "tokens_per_cycle": round(tokens_per_cycle, 3),
@@ -269,6 +302,7 @@ def main():
     ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt"], default=None,
                     help="run one workload only (profiling); the main line is then that workload's")
     ap.add_argument("--main-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -307,12 +341,12 @@ def main():
     if args.only in ("c3", "c4"):
         w = C3_8B_CHAIN if args.only == "c3" else C4_70B_TREE
         dr = dr8 if args.only == "c3" else Drafter(w.shape, gen.gen_weights(w.shape, seed=0), pack=True)
-        r, _ = cycle_bench(w, dr, args.steps, args.warmup)
+        r, _ = cycle_bench(w, dr, args.steps, args.warmup, graph=not args.no_graph)
         print(json.dumps(r), flush=True)
         return
 
     w = C2_8B_TREE
-    r, ci = cycle_bench(w, dr8, args.steps, args.warmup)
+    r, ci = cycle_bench(w, dr8, args.steps, args.warmup, graph=not args.no_graph)
     lm = r["lm_head"]
     src_hash = kernel_source_hash()
     traffic = load_traffic("llama3.1-8b-b1-tree", src_hash)
@@ -324,13 +358,14 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": r["ms_per_step"],
+        "ms_per_step_eager": r["ms_per_step_eager"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) features/KV, N(0,3) target logits planted 0.8)",
         "config": {"workload": w.name, "batch": w.batch, "prefix": int(ci.ctx_len[0]), "depth": w.depth,
-                   "topk": w.topk, "keep": w.keep, "verify": "greedy", "graph": False, "weights": "packed"},
+                   "topk": w.topk, "keep": w.keep, "verify": "greedy", "graph": r["graph"], "weights": "packed"},
         "verified_tokens_per_s": r["verified_tokens_per_s"],
         "tokens_per_cycle": r["tokens_per_cycle"],
         "roofline": {"bound": "hbm", "achieved": lm["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -342,14 +377,14 @@ def main():
     }
     if not args.main_only:
         wl = {}
-        r3, _ = cycle_bench(C3_8B_CHAIN, dr8, max(args.steps // 2, 1), args.warmup)
+        r3, _ = cycle_bench(C3_8B_CHAIN, dr8, max(args.steps // 2, 1), args.warmup, graph=not args.no_graph)
         wl[C3_8B_CHAIN.name] = r3
         r5 = ttt_bench(C5_8B_TTT, dr8, 5, 1)
         wl[C5_8B_TTT.name] = r5
         del dr8
         torch.cuda.empty_cache()
         dr70 = Drafter(C4_70B_TREE.shape, gen.gen_weights(C4_70B_TREE.shape, seed=0), pack=True)
-        r4, _ = cycle_bench(C4_70B_TREE, dr70, max(args.steps // 3, 1), args.warmup)
+        r4, _ = cycle_bench(C4_70B_TREE, dr70, max(args.steps // 3, 1), args.warmup, graph=not args.no_graph)
         wl[C4_70B_TREE.name] = r4
         del dr70
         out["workloads"] = wl
