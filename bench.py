@@ -338,6 +338,8 @@ def main():
         r = ttt_bench(C5_8B_TTT, dr8, max(1, min(args.steps, 10)), 1)
         print(json.dumps(r), flush=True)
         return
+    if args.only == "c2":
+        args.main_only = True
     if args.only in ("c3", "c4"):
         w = C3_8B_CHAIN if args.only == "c3" else C4_70B_TREE
         dr = dr8 if args.only == "c3" else Drafter(w.shape, gen.gen_weights(w.shape, seed=0), pack=True)

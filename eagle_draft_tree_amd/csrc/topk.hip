@@ -4,9 +4,9 @@
 // draft forward).
 //
 // Phase 1 (grid: partitions x rows): a workgroup loads its TK_PS logits with
-// 16-byte loads into registers (all loads in flight at once), keeps a sorted
-// top-KMAX list per thread, then each wave pops its k best heads with
-// wavefront shuffles and wave 0 pops the k best of the 4 wave lists.
+// 16-byte loads into registers (all loads in flight at once); each wave
+// selects its k best in k rounds of wavefront argmax over the lanes' bests,
+// and wave 0 pops the k best of the 4 wave lists.
 // It also writes the partition's (max, sum exp(x - max)).
 // Phase 2 (grid: rows, one wave each): the partitions' candidates sit in
 // registers and k rounds of wave argmax select the top-k; the LSE merges the
@@ -29,36 +29,19 @@ struct Cand {
   int id;
 };
 
-template <int KMAX>
-__device__ __forceinline__ void list_insert(float (&lv)[KMAX], int (&li)[KMAX], float v, int y) {
-  if (!better(v, y, lv[KMAX - 1], li[KMAX - 1])) return;
-  lv[KMAX - 1] = v;
-  li[KMAX - 1] = y;
-#pragma unroll
-  for (int j = KMAX - 1; j > 0; --j) {
-    if (better(lv[j], li[j], lv[j - 1], li[j - 1])) {
-      const float tv = lv[j];
-      lv[j] = lv[j - 1];
-      lv[j - 1] = tv;
-      const int ti = li[j];
-      li[j] = li[j - 1];
-      li[j - 1] = ti;
-    }
-  }
-}
-
-template <int KMAX>
-__global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* __restrict__ logits,
-                                                                  int V, int k, int nparts,
-                                                                  float* __restrict__ pv,
-                                                                  int* __restrict__ pid,
-                                                                  float* __restrict__ pm,
+// Phase 1.  Lane-level selection keeps no sorted lists: each lane tracks the
+// best of its 16 values not yet taken (a removal bit mask, so every register
+// index is static), each of the k rounds is one wavefront argmax, and only
+// the lane that owned the winner rescans its 16 values.
+__global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* __restrict__ logits, int V, int k,
+                                                                  int nparts, float* __restrict__ pv,
+                                                                  int* __restrict__ pid, float* __restrict__ pm,
                                                                   float* __restrict__ ps) {
   const int part = blockIdx.x, row = blockIdx.y;
   const float* x = logits + (size_t)row * V;
   const int lo = part * TK_PS;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // element e of this thread: lo + 4*(threadIdx.x + 256*j) + c, j < 4, c < 4
+  // element e of this thread: id lo + 4*(threadIdx.x + 256*(e/4)) + e%4 (ids rise with e)
   float v[TK_PER_THREAD];
   const bool vec_ok = (V & 3) == 0;
 #pragma unroll
@@ -75,28 +58,38 @@ __global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* _
       for (int c = 0; c < 4; ++c) v[4 * j + c] = y0 + c < V ? x[y0 + c] : -INFINITY;
     }
   }
-  float lv[KMAX];
-  int li[KMAX];
+  auto id_of = [&](int e) { return lo + 4 * (threadIdx.x + TK_THREADS * (e >> 2)) + (e & 3); };
+  uint32_t taken = 0;  // removed or past V
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    lv[j] = -INFINITY;
-    li[j] = INT_MAX;
-  }
+  for (int e = 0; e < TK_PER_THREAD; ++e)
+    if (id_of(e) >= V) taken |= 1u << e;
   float m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < TK_PER_THREAD; ++e) m = fmaxf(m, v[e]);
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < TK_PER_THREAD; ++e) {
-    const int y = lo + 4 * (threadIdx.x + TK_THREADS * (e >> 2)) + (e & 3);
-    if (y < V) {
-      if (v[e] > -INFINITY) s += expf(v[e] - m);
-      list_insert<KMAX>(lv, li, v[e], y);
+  for (int e = 0; e < TK_PER_THREAD; ++e)
+    if (!((taken >> e) & 1u) && v[e] > -INFINITY) s += expf(v[e] - m);
+  float bv;
+  int bi, be;
+  auto rescan = [&]() {
+    bv = -INFINITY;
+    bi = INT_MAX;
+    be = 0;
+#pragma unroll
+    for (int e = 0; e < TK_PER_THREAD; ++e) {
+      const int y = id_of(e);
+      if (!((taken >> e) & 1u) && better(v[e], y, bv, bi)) {
+        bv = v[e];
+        bi = y;
+        be = e;
+      }
     }
-  }
+  };
+  rescan();
   __shared__ float mred[TK_THREADS / 64];
   __shared__ float sred[TK_THREADS / 64];
-  __shared__ Cand wl[TK_THREADS / 64][KMAX];
+  __shared__ Cand wl[TK_THREADS / 64][EAGLE3_MAX_TOPK];
   // (max, sum): max first, then sums rescaled to it, added in a fixed order
   const float wm = wave_max(m);
   if (lane == 0) mred[w] = wm;
@@ -107,19 +100,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* _
   const float mine = (m == -INFINITY) ? 0.f : s * expf(m - M);
   const float ws = wave_sum(mine);
   if (lane == 0) sred[w] = ws;
-  // per-wave top-k: k rounds of wavefront argmax over the list heads
+  // per-wave top-k: k rounds of wavefront argmax over the lanes' bests
   for (int r = 0; r < k; ++r) {
-    Cand c{lv[0], li[0]};
+    Cand c{bv, bi};
     wave_argmax(c.v, c.id);
     if (lane == 0) wl[w][r] = c;
-    if (li[0] == c.id && c.id != INT_MAX) {  // the owner pops its head
-#pragma unroll
-      for (int j = 0; j < KMAX - 1; ++j) {
-        lv[j] = lv[j + 1];
-        li[j] = li[j + 1];
-      }
-      lv[KMAX - 1] = -INFINITY;
-      li[KMAX - 1] = INT_MAX;
+    if (bi == c.id && c.id != INT_MAX) {  // the owner takes it and rescans
+      taken |= 1u << be;
+      rescan();
     }
   }
   __syncthreads();
@@ -134,28 +122,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* _
     }
     // lane i holds candidate i of the 4 wave lists; k rounds of wave argmax
     const int nc = (TK_THREADS / 64) * k;  // <= 64
-    Cand mine{-INFINITY, INT_MAX};
+    Cand mc{-INFINITY, INT_MAX};
     if (lane < nc) {
       const int ww = lane / k;
-      mine = wl[ww][lane - ww * k];
+      mc = wl[ww][lane - ww * k];
     }
     for (int r = 0; r < k; ++r) {
-      Cand c = mine;
+      Cand c = mc;
       wave_argmax(c.v, c.id);
       if (lane == 0) {
         pv[o * k + r] = c.v;
         pid[o * k + r] = c.id;
       }
-      if (mine.id == c.id) mine = Cand{-INFINITY, INT_MAX};
+      if (mc.id == c.id) mc = Cand{-INFINITY, INT_MAX};
     }
   }
 }
 
-// Phase 2: one wave per row.  Lane l holds candidates l, l+64, ... (<= 16
+// Phase 2: one wave per row.  Lane l holds candidates l, l+64, ... (SLOTS
 // per lane), then k rounds of wave argmax pop the best; the LSE merges the
 // partition (max, sum) pairs with shuffle reductions (fixed order).
-constexpr int TK_MERGE_PER_LANE = 16;
-
+template <int SLOTS>
 __global__ __launch_bounds__(64) void topk_merge_kernel(int k, int nparts, const float* __restrict__ pv,
                                                         const int* __restrict__ pid, const float* __restrict__ pm,
                                                         const float* __restrict__ ps, int32_t* __restrict__ ids,
@@ -163,36 +150,32 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int k, int nparts, const
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
   const int n = nparts * k;
-  float cv[TK_MERGE_PER_LANE];
-  int ci[TK_MERGE_PER_LANE];
+  float cv[SLOTS];
+  int ci[SLOTS];
 #pragma unroll
-  for (int j = 0; j < TK_MERGE_PER_LANE; ++j) {
+  for (int j = 0; j < SLOTS; ++j) {
     const int i = lane + 64 * j;
     cv[j] = i < n ? pv[(size_t)row * n + i] : -INFINITY;
     ci[j] = i < n ? pid[(size_t)row * n + i] : INT_MAX;
   }
-  float pmv[2], psv[2];
+  float pmv = lane < nparts ? pm[(size_t)row * nparts + lane] : -INFINITY;
+  float psv = lane < nparts ? ps[(size_t)row * nparts + lane] : 0.f;
+  const float M = wave_max(pmv);
+  const float L = M + logf(wave_sum(pmv == -INFINITY ? 0.f : psv * expf(pmv - M)));
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  auto rescan = [&]() {
+    bv = -INFINITY;
+    bi = INT_MAX;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = lane + 64 * j;
-    pmv[j] = p < nparts ? pm[(size_t)row * nparts + p] : -INFINITY;
-    psv[j] = p < nparts ? ps[(size_t)row * nparts + p] : 0.f;
-  }
-  const float M = wave_max(fmaxf(pmv[0], pmv[1]));
-  float sl = 0.f;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) sl += pmv[j] == -INFINITY ? 0.f : psv[j] * expf(pmv[j] - M);
-  const float L = M + logf(wave_sum(sl));
-  for (int r = 0; r < k; ++r) {
-    // this lane's best remaining candidate
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < TK_MERGE_PER_LANE; ++j)
+    for (int j = 0; j < SLOTS; ++j)
       if (better(cv[j], ci[j], bv, bi)) {
         bv = cv[j];
         bi = ci[j];
       }
+  };
+  rescan();
+  for (int r = 0; r < k; ++r) {
     float wv = bv;
     int wi = bi;
     wave_argmax(wv, wi);
@@ -200,12 +183,15 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int k, int nparts, const
       ids[(size_t)row * k + r] = wi;
       lp[(size_t)row * k + r] = wv - L;
     }
+    if (bi == wi) {
 #pragma unroll
-    for (int j = 0; j < TK_MERGE_PER_LANE; ++j)
-      if (ci[j] == wi) {
-        cv[j] = -INFINITY;
-        ci[j] = INT_MAX;
-      }
+      for (int j = 0; j < SLOTS; ++j)
+        if (ci[j] == wi) {
+          cv[j] = -INFINITY;
+          ci[j] = INT_MAX;
+        }
+      rescan();
+    }
   }
   if (lse_out && lane == 0) lse_out[row] = L;
 }
@@ -223,12 +209,12 @@ hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids
   float* pm = (float*)(pid + (size_t)rows * nparts * k);
   float* ps = pm + (size_t)rows * nparts;
   dim3 g1(nparts, rows);
-  if (k <= 1) topk_partial_kernel<1><<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  else if (k <= 2) topk_partial_kernel<2><<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  else if (k <= 4) topk_partial_kernel<4><<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  else if (k <= 8) topk_partial_kernel<8><<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  else topk_partial_kernel<16><<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  topk_merge_kernel<<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
+  topk_partial_kernel<<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
+  const int n = nparts * k;  // nparts <= 64 (V <= 262144), k <= 16
+  if (n <= 128) topk_merge_kernel<2><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
+  else if (n <= 256) topk_merge_kernel<4><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
+  else if (n <= 512) topk_merge_kernel<8><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
+  else topk_merge_kernel<16><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ import torch
 
 from oracle import eagle3_oracle as O
 from workloads import gen
-from workloads.configs import BF16, C1_TINY, F32, scaled, tiny_shape
+from workloads.configs import BF16, C1_TINY, C3_8B_CHAIN, F32, scaled, tiny_shape
 
 from gpu_cases import GpuCycle, compare_cycle, cycle_and_oracle, dev_i32, host_weights, oracle_cycle, say, topk_agrees
 
@@ -257,3 +257,17 @@ def test_bf16_small_cycle(lib, hkv, commit, ctx, pack):
     gc.run()
     exc = compare_cycle(gc, w, W, ci, TOL_BF16)
     assert exc <= 1
+
+
+@pytest.mark.parametrize("bs", [4, 16])
+def test_bf16_small_paged_cycle(lib, bs):
+    """Paged KV (block tables, per-request prefix lengths) on a small bf16
+    drafter, batch 6, tree 3 x 2."""
+    say("bf16 small paged cycle, block size", bs)
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
+    w = scaled(C3_8B_CHAIN, shape=shape, batch=6, depth=3, topk=2, keep=6, prefix=90, prefix_range=(10, 90),
+               block_size=bs, feat_scale=1.0)
+    Wt, W, ci = cycle_and_oracle(w, seed=5)
+    gc = GpuCycle(w, Wt, ci, pack=True)
+    gc.run()
+    assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
