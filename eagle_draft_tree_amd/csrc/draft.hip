@@ -22,6 +22,7 @@
 #include "common.hpp"
 #include "draft.hpp"
 #include "gemm_rows.hpp"
+#include "rows_dma.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -262,6 +263,16 @@ static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int
 template <typename TW, class Epi>
 static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
                             const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
+  if (sizeof(TW) == 2 && sk_ok(R, K, packed)) {
+    const int nt16 = N / 16;
+    const int bn = sk_bn(nt16, p.splits);
+    const int grid = (nt16 + bn / 16 - 1) / (bn / 16) * p.splits;
+    const bf16* Xb = (const bf16*)X;
+    const bf16* Wb = (const bf16*)W;
+    if (bn == 128) skinny_gemm_kernel<128, Epi><<<grid, 256, 0, st>>>(Xb, ldx, R, Wb, K, nt16, p.splits, epi);
+    else skinny_gemm_kernel<64, Epi><<<grid, 256, 0, st>>>(Xb, ldx, R, Wb, K, nt16, p.splits, epi);
+    return hipGetLastError();
+  }
   if (sizeof(TW) == 2) {
     switch (p.nt) {
       case 1: return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);

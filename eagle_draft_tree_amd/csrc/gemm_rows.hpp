@@ -183,7 +183,7 @@ __device__ __forceinline__ void rows_tile_bf16(const bf16* __restrict__ X, int l
       for (int i = 0; i < 4; ++i)
         red[(((wave * T + t) * NT + c) << 8) + ((q4 * 4 + i) << 4) + m] = acc[t][c][i];
   __syncthreads();
-  constexpr int RP = 16 * NT;
+  constexpr int RP = 16 * NT + 1;  // padded: column reads of a tile row stay conflict-free
   for (int e = threadIdx.x; e < T * NT * 256; e += WAVES * 64) {
     const int t = e / (NT * 256), rem = e - t * NT * 256, c = rem >> 8, mm = (rem >> 4) & 15,
               n = rem & 15;
@@ -201,7 +201,7 @@ template <int T, int NT, int WAVES>
 __device__ __forceinline__ void rows_tile_f32(const float* __restrict__ X, int ldx, int R,
                                               const float* __restrict__ W, int ldw, int K,
                                               const int* wrows, float* tile_out) {
-  constexpr int RP = 16 * NT;
+  constexpr int RP = 16 * NT + 1;  // padded: column reads of a tile row stay conflict-free
   for (int e = threadIdx.x; e < 16 * T * R; e += WAVES * 64) {
     const int mm = e / R, r = e - mm * R;
     const float* wp = W + (size_t)wrows[mm] * ldw;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WAVES * 64) void rows_gemm_kernel(const TW* __restr
                                                                int R, const TW* __restrict__ W,
                                                                int K, int ntiles16, int splits,
                                                                RowMap map, Epi epi) {
-  constexpr int RP = 16 * NT;
+  constexpr int RP = 16 * NT + 1;  // padded: column reads of a tile row stay conflict-free
   constexpr int TILE = 16 * T * RP;
   __shared__ int wrows[16 * T];
   __shared__ float tile[TILE];
@@ -261,7 +261,7 @@ struct EpiStore {
   RowMap map;
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
-      const int m = e / R, r = e - m * R;
+      const int r = e >> 4, m = e & 15;  // 16 threads write one output row's 16 columns
       Elem<TO>::st(out, (size_t)r * ldo + map(tile16, m), tile[m * RP + r]);
     }
   }
@@ -289,7 +289,7 @@ struct EpiResidual {
   int ld;
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
-      const int m = e / R, r = e - m * R;
+      const int r = e >> 4, m = e & 15;
       const size_t i = (size_t)r * ld + tile16 * 16 + m;
       out[i] = res[i] + tile[m * RP + r];
     }
@@ -304,7 +304,7 @@ struct EpiSwiGLU {
   int ffn;
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
-      const int m = e / R, r = e - m * R;
+      const int r = e >> 3, m = e & 7;
       const float g = tile[m * RP + r], u = tile[(m + 8) * RP + r];
       const float s = g / (1.f + expf(-g));
       Elem<TO>::st(z, (size_t)r * ffn + tile16 * 8 + m, s * u);
@@ -355,7 +355,7 @@ struct EpiQKV {
     const int hd = dst.hd, tph = hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
     const int half = hd >> 1;
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
-      const int m = e / R, r = e - m * R;
+      const int r = e >> 3, m = e & 7;
       const int i = t * 8 + m;  // pair index within the head
       float a = tile[m * RP + r], b = tile[(m + 8) * RP + r];
       if (head < hq + dst.hkv) {  // q or k: rotate
