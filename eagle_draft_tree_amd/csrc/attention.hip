@@ -76,7 +76,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
   constexpr int KPR = CH / KSPL;               // keys per range
   __shared__ uint4 ks[CH * KPV];
   __shared__ uint4 vs[CH * VPR];
-  __shared__ uint4 qs[QG * VPR];
+  __shared__ float4 qs[QG * HD / 4];  // query vectors as float
   __shared__ float sc[QG * CH];
   __shared__ float alpha_s[QG];
   __shared__ int blk_s[MAX_SPLIT_BLOCKS];
@@ -157,14 +157,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
       }
     }
   };
-  // query vectors (q head h = g*G + gi of row rr), native type
+  // query vectors (q head h = g*G + gi of row rr), unpacked to float
   {
     const T* Q = (const T*)a.q;
     for (int e = threadIdx.x; e < nq * VPR; e += ATT_THREADS) {
       const int qi = e / VPR, c = e - qi * VPR;
       const int rr = (q0 + qi) / G, gi = (q0 + qi) - rr * G;
       const size_t row = (size_t)b * a.rows + rr;
-      qs[qi * VPR + c] = *((const uint4*)(Q + (row * a.hq + g * G + gi) * HD) + c);
+      float f[EPV];
+      Vec16<T>::unpack(*((const uint4*)(Q + (row * a.hq + g * G + gi) * HD) + c), f);
+#pragma unroll
+      for (int i = 0; i < EPV; i += 4) qs[(qi * HD + c * EPV + i) / 4] = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
     }
   }
   float m_run[QPW], l_run[QPW];
@@ -206,10 +209,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
       for (int t = 0; t < QPW; ++t) {
         const int qi = wave + 4 * t;
         if (qi < nq) {
-          float qf[EPV];
-          Vec16<T>::unpack(qs[qi * VPR + c], qf);
 #pragma unroll
-          for (int i = 0; i < EPV; ++i) s[t] = fmaf(qf[i], kf[i], s[t]);
+          for (int i = 0; i < EPV; i += 4) {
+            const float4 q4v = qs[(qi * HD + c * EPV + i) / 4];
+            s[t] = fmaf(q4v.x, kf[i], s[t]);
+            s[t] = fmaf(q4v.y, kf[i + 1], s[t]);
+            s[t] = fmaf(q4v.z, kf[i + 2], s[t]);
+            s[t] = fmaf(q4v.w, kf[i + 3], s[t]);
+          }
         }
       }
     }
