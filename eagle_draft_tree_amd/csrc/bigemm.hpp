@@ -65,7 +65,16 @@ __device__ __forceinline__ void bg_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 
 typedef f32x4 BGAcc[8][BG_NJ];
 
-template <bool PACKED, class Epi>
+// Element offset of (r, k) in a fragment-ordered [M][K] bf16 matrix (nkc =
+// K/32): fragment (r/16, k/32) is 512 contiguous elements, lane slot
+// (r%16) + 16*((k%32)/8) holds 8 consecutive k.  Used for activations that
+// feed the A operand, so A copies read whole kilobytes like packed weights.
+__device__ __forceinline__ size_t frag_off(int r, int k, int nkc) {
+  return ((size_t)(r >> 4) * nkc + (k >> 5)) * 512 + ((((r & 15) + 16 * ((k & 31) >> 3))) << 3) + (k & 7);
+}
+
+// APACK: A in fragment order (frag_off) instead of row-major with stride lda.
+template <bool PACKED, bool APACK, class Epi>
 __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __restrict__ A, int lda, int M,
                                                               const bf16* __restrict__ W, int N, int K, RowMap map,
                                                               Epi epi) {
@@ -102,8 +111,13 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int mt = wave * 2 + h;
-    const int row = min(bm * BG_BM + mt * 16 + (lane & 15), M - 1);
-    asrc[h] = A + (size_t)row * lda + 8 * (lane >> 4);
+    if (APACK) {
+      const int mtc = min(bm * (BG_BM / 16) + mt, (M - 1) >> 4);
+      asrc[h] = A + ((size_t)mtc * nchunks * 64 + lane) * 8;
+    } else {
+      const int row = min(bm * BG_BM + mt * 16 + (lane & 15), M - 1);
+      asrc[h] = A + (size_t)row * lda + 8 * (lane >> 4);
+    }
     const int ntile = min(bn * 16 + wave * 2 + h, nt16 - 1);
     if (PACKED)
       bsrc[h] = W + ((size_t)ntile * nchunks * 64 + lane) * 8;
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t f = (uint32_t)(wave * 2 + h) * 1024u;
-      dma16(asrc[h] + ks * BG_BK, sa + f);
+      dma16(asrc[h] + (APACK ? (size_t)ks * 512 : (size_t)ks * BG_BK), sa + f);
       if (PACKED)
         dma16(bsrc[h] + (size_t)ks * 512, sb + f);
       else
@@ -242,9 +256,10 @@ struct BEpiResid {
 };
 
 // SwiGLU on MAP_PAIR_FFN tiles: slot m < 8 is gate column 8t+m, slot m+8
-// the matching up column.  z = silu(gate) * up, rounded to bf16.
+// the matching up column.  z = silu(gate) * up, rounded to bf16, written in
+// fragment order for the down projection's A operand.
 struct BEpiSwiGLU {
-  bf16* z;
+  bf16* z;  // fragment order [M][ffn] (frag_off)
   int ffn;
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
@@ -263,7 +278,7 @@ struct BEpiSwiGLU {
           for (int e = 0; e < 4; ++e)
             if (row0 + e < M) {
               const float g = acc[i][j][e];
-              z[(size_t)(row0 + e) * ffn + col16 * 8 + m] = f2bf(g / (1.f + expf(-g)) * up[e]);
+              z[frag_off(row0 + e, col16 * 8 + m, ffn >> 5)] = f2bf(g / (1.f + expf(-g)) * up[e]);
             }
         }
       }

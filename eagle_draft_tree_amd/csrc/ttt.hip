@@ -37,22 +37,22 @@ struct Carve {
 
 struct TLayout {
   float* hs;     // [M][d] state stream s -> h1 -> h2 (fp32)
-  bf16* x;       // [M][2d] decoder input; reused as u [M][d] and y [M][d]
-  bf16* a;       // [M][hq*hd] attention output
-  bf16* z;       // [M][F] silu(gate) * up
+  bf16* x;       // [M][2d] decoder input; reused as u [M][d] and y [M][d] (fragment order)
+  bf16* a;       // [M][hq*hd] attention output (fragment order)
+  bf16* z;       // [M][F] silu(gate) * up (fragment order)
   bf16* q;       // [M][hq][hd]
   bf16* k1;      // [M][hkv][hd] step-1 keys
   bf16* v1t;     // [B][hkv][hd][S] step-1 values, transposed
   bf16* kc;      // [R-1][M][hkv][hd] chain keys of steps 2..R
   bf16* vc;      // [R-1][M][hkv][hd] chain values
-  float4* part;  // [M][nblk] LM-head partials per 64 columns {max, sum exp, argmax id, 0}
+  float4* part;  // [M][nblk] LM-head partials per 256 columns {max, sum exp, argmax id, 0}
   float* lab;    // [M] target logit
   int32_t* tok;  // [M] input tokens of the next step
   float2* rope;  // [S+R][hd/2] (cos, sin)
   size_t bytes;
 };
 
-inline int ce_blocks(int V) { return (V / 16 + BG_NJ - 1) / BG_NJ; }
+inline int ce_blocks(int V) { return (V / 16 + 15) / 16; }  // 256-column blocks
 
 TLayout layout_of(const eagle3_dims& dm, int B, int S, int R, void* base) {
   Carve c;
@@ -91,8 +91,6 @@ __global__ void rope_table_kernel(float2* tab, int npos, int hd, float theta) {
   tab[e] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-constexpr int TR = 512;  // row-kernel threads; 8 elements per thread per pass, d <= 8192
-
 __device__ __forceinline__ void unpack8(uint4 u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -108,90 +106,88 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// x = [rms(emb[t]) * norm_e ; rms(s) * norm_s] (bf16)
+// Row kernels over 16-row blocks (one MFMA m-tile): 256 threads, the 16
+// threads of a DPP row own one matrix row for the sums of squares, then every
+// thread writes whole 16-byte slots of the block's fragments (consecutive
+// threads -> consecutive slots, 1 KB per fragment).
+constexpr int TR = 256;
+
+// sum of squares of row r0 + (tid/16) over n elements of src (fp32 or bf16),
+// reduced over the 16 threads of the DPP row
+template <typename TS>
+__device__ __forceinline__ float row_ss(const TS* src, size_t ld, int r, int n) {
+  const int c = threadIdx.x & 15;
+  const TS* p = src + (size_t)r * ld;
+  float ss = 0.f;
+  for (int k = c * 8; k < n; k += 128) {
+    float v[8];
+    if (sizeof(TS) == 4) {
+      const float4 a = *(const float4*)((const float*)p + k), b = *(const float4*)((const float*)p + k + 4);
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    } else {
+      unpack8(*(const uint4*)((const bf16*)p + k), v);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+  }
+  return row16_sum(ss);
+}
+
+// x = [rms(emb[t]) * norm_e ; rms(s) * norm_s] (bf16, fragment order, K = 2d)
 __global__ __launch_bounds__(TR) void ttt_prologue_kernel(const bf16* __restrict__ emb, const int32_t* __restrict__ tok,
                                                           const float* __restrict__ hs, int d,
                                                           const float* __restrict__ ge, const float* __restrict__ gs,
                                                           float eps, bf16* __restrict__ x) {
-  __shared__ float red[TR / 64];
-  const size_t r = blockIdx.x;
-  const bf16* e = emb + (size_t)tok[r] * d;
-  const float* s = hs + r * d;
-  float ev[2][8], sv[2][8];
-  float se = 0.f, ss = 0.f;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = (threadIdx.x + TR * it) * 8;
-    if (i < d) {
-      unpack8(*(const uint4*)(e + i), ev[it]);
-      const float4 s0 = *(const float4*)(s + i), s1 = *(const float4*)(s + i + 4);
-      sv[it][0] = s0.x, sv[it][1] = s0.y, sv[it][2] = s0.z, sv[it][3] = s0.w;
-      sv[it][4] = s1.x, sv[it][5] = s1.y, sv[it][6] = s1.z, sv[it][7] = s1.w;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) ev[it][c] = sv[it][c] = 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      se = fmaf(ev[it][c], ev[it][c], se);
-      ss = fmaf(sv[it][c], sv[it][c], ss);
-    }
+  __shared__ float ie_s[16], is_s[16];
+  __shared__ int tok_s[16];
+  const int mt = blockIdx.x, r0 = mt * 16, rr = threadIdx.x >> 4;
+  const int t = tok[r0 + rr];
+  const float se = row_ss(emb, (size_t)d, t, d);
+  const float ss = row_ss(hs, (size_t)d, r0 + rr, d);
+  if ((threadIdx.x & 15) == 0) {
+    ie_s[rr] = (float)(1.0 / sqrt((double)se / d + (double)eps));
+    is_s[rr] = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+    tok_s[rr] = t;
   }
-  se = block_sum(se, red);
-  ss = block_sum(ss, red);
-  const float ie = (float)(1.0 / sqrt((double)se / d + (double)eps));
-  const float is = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-  bf16* xr = x + r * 2 * d;
+  __syncthreads();
+  const int nkc = (2 * d) >> 5;
+  for (int sl = threadIdx.x; sl < nkc * 64; sl += TR) {
+    const int kc = sl >> 6, l = sl & 63, r = l & 15, k = kc * 32 + 8 * (l >> 4);
+    float v[8], o[8];
+    if (k < d) {
+      unpack8(*(const uint4*)(emb + (size_t)tok_s[r] * d + k), v);
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = (threadIdx.x + TR * it) * 8;
-    if (i < d) {
-      float o1[8], o2[8];
+      for (int c = 0; c < 8; ++c) o[c] = v[c] * ie_s[r] * ge[k + c];
+    } else {
+      const float* p = hs + (size_t)(r0 + r) * d + (k - d);
+      const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        o1[c] = ev[it][c] * ie * ge[i + c];
-        o2[c] = sv[it][c] * is * gs[i + c];
-      }
-      *(uint4*)(xr + i) = pack8(o1);
-      *(uint4*)(xr + d + i) = pack8(o2);
+      for (int c = 0; c < 8; ++c) o[c] = v[c] * is_s[r] * gs[k - d + c];
     }
+    *(uint4*)(x + ((size_t)mt * nkc * 64 + sl) * 8) = pack8(o);
   }
 }
 
-// y = rms(h) * gain (bf16, [M][d])
+// y = rms(h) * gain (bf16, [M][d] in fragment order)
 __global__ __launch_bounds__(TR) void ttt_norm_kernel(const float* __restrict__ hs, int d,
                                                       const float* __restrict__ gain, float eps,
                                                       bf16* __restrict__ y) {
-  __shared__ float red[TR / 64];
-  const size_t r = blockIdx.x;
-  const float* s = hs + r * d;
-  float v[2][8];
-  float ss = 0.f;
+  __shared__ float inv_s[16];
+  const int mt = blockIdx.x, r0 = mt * 16, rr = threadIdx.x >> 4;
+  const float ss = row_ss(hs, (size_t)d, r0 + rr, d);
+  if ((threadIdx.x & 15) == 0) inv_s[rr] = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+  __syncthreads();
+  const int nkc = d >> 5;
+  for (int sl = threadIdx.x; sl < nkc * 64; sl += TR) {
+    const int kc = sl >> 6, l = sl & 63, r = l & 15, k = kc * 32 + 8 * (l >> 4);
+    const float* p = hs + (size_t)(r0 + r) * d + k;
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float o[8];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = (threadIdx.x + TR * it) * 8;
-    if (i < d) {
-      const float4 s0 = *(const float4*)(s + i), s1 = *(const float4*)(s + i + 4);
-      v[it][0] = s0.x, v[it][1] = s0.y, v[it][2] = s0.z, v[it][3] = s0.w;
-      v[it][4] = s1.x, v[it][5] = s1.y, v[it][6] = s1.z, v[it][7] = s1.w;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) v[it][c] = 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) ss = fmaf(v[it][c], v[it][c], ss);
-  }
-  ss = block_sum(ss, red);
-  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = (threadIdx.x + TR * it) * 8;
-    if (i < d) {
-      float o[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] = v[it][c] * inv * gain[i + c];
-      *(uint4*)(y + r * d + i) = pack8(o);
-    }
+    for (int c = 0; c < 8; ++c) o[c] = v[c] * inv_s[r] * gain[k + c];
+    *(uint4*)(y + ((size_t)mt * nkc * 64 + sl) * 8) = pack8(o);
   }
 }
 
@@ -267,9 +263,11 @@ struct TEpiQKV {
   }
 };
 
-// LM head with the cross entropy folded in: for every row and each 64-column
-// block (one wave's tile width) write {max, sum exp(x - max), argmax id};
-// the lane that owns a row's target column writes the target logit.
+// LM head with the cross entropy folded in: for every row and each
+// 256-column block (one workgroup tile) write {max, sum exp(x - max), argmax
+// id}; the lane that owns a row's target column writes the target logit.
+// Each wave reduces its 64 columns per row with DPP, then the four column
+// waves' results meet in LDS and are combined in wave order.
 struct TEpiCE {
   float4* part;
   float* lab;
@@ -277,15 +275,29 @@ struct TEpiCE {
   int S, step, nblk;
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
-    const int m = lane & 15, blk = colbase16 / BG_NJ;
-    if (blk >= nblk) return;
+    __shared__ float4 cs[BG_BM][4];  // [row in tile][column wave]
+    const int m = lane & 15, wave = threadIdx.x >> 6, wm = wave >> 2, wn = wave & 3;
+    // targets of this lane's 32 rows, loaded together (one division per lane;
+    // S >= 64, so a row offset of at most 115 wraps a sequence at most once)
+    const int r0 = rowbase + 4 * (lane >> 4);
+    const int p0 = r0 % S;
+    int tg[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = r0 + 16 * i + e;
+        int pos = p0 + 16 * i + e;
+        if (pos >= S) pos -= S;
+        if (pos >= S) pos -= S;
+        tg[i][e] = row < M && pos + step <= S - 1 ? tokens[row + step] : -1;
+      }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = rowbase + 16 * i + 4 * (lane >> 4) + e;
-        int target = -1;
-        if (row < M && (row % S) + step <= S - 1) target = tokens[row + step];
+        const int row = r0 + 16 * i + e;
+        const int target = tg[i][e];
         float mx = -INFINITY;
         int id = 0x7fffffff;
 #pragma unroll
@@ -302,11 +314,37 @@ struct TEpiCE {
         }
         row16_argmax(mx, id);
         float s = 0.f;
+        if (mx > -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < BG_NJ; ++j)
-          if (colbase16 + j < nt16) s += __expf(acc[i][j][e] - mx);
+          for (int j = 0; j < BG_NJ; ++j)
+            if (colbase16 + j < nt16) s += __expf(acc[i][j][e] - mx);
+        }
         s = row16_sum(s);
-        if (m == 0 && row < M) part[(size_t)row * nblk + blk] = make_float4(mx, s, __int_as_float(id), 0.f);
+        if (m == 0) cs[wm * 128 + 16 * i + 4 * (lane >> 4) + e][wn] = make_float4(mx, s, __int_as_float(id), 0.f);
+      }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < BG_BM) {
+      const int row = rowbase - wm * 128 + t, blk = colbase16 / 16;
+      if (row < M && blk < nblk) {
+        float gm = -INFINITY;
+        int gi = 0x7fffffff;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float4 c = cs[t][w];
+          if (better(c.x, __float_as_int(c.z), gm, gi)) {
+            gm = c.x;
+            gi = __float_as_int(c.z);
+          }
+        }
+        float gs = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float4 c = cs[t][w];
+          if (c.x > -INFINITY) gs += c.y * __expf(c.x - gm);
+        }
+        part[(size_t)row * nblk + blk] = make_float4(gm, gs, __int_as_float(gi), 0.f);
       }
     }
   }
@@ -323,12 +361,12 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
   __shared__ double ws[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float4* p = part + (size_t)row * nblk;
-  float4 loc[16];  // nblk <= 4096 (vocab <= 262144 in 64-column blocks)
+  float4 loc[4];  // nblk <= 1024 (vocab <= 262144 in 256-column blocks)
   int nl = 0;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
+  for (int c = 0; c < 4; ++c) {
     const int k = tid + 256 * c;
     loc[c] = k < nblk ? p[k] : make_float4(-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f);
     if (k < nblk) nl = c + 1;
@@ -353,7 +391,7 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
     }
   double s = 0.0;
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
+  for (int c = 0; c < 4; ++c)
     if (c < nl) s += (double)loc[c].y * exp((double)loc[c].x - (double)gv);
   s = wave_sum_d(s);
   if (lane == 0) ws[w] = s;
@@ -551,25 +589,28 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
     const float inv = 1.f / L;
-    const size_t row = (size_t)b * S + i0 + 16 * nt + ml;
-    bf16* op = out + (row * hq + h) * HD + 4 * q4;
+    const int row = b * S + i0 + 16 * nt + ml;
+    const int nkc = (hq * HD) >> 5;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const f32x4 r = o[t][nt] * inv;
-      *(uint2*)(op + 16 * t) = make_uint2((uint32_t)f2bf(r[0]) | ((uint32_t)f2bf(r[1]) << 16),
-                                          (uint32_t)f2bf(r[2]) | ((uint32_t)f2bf(r[3]) << 16));
+      *(uint2*)(out + frag_off(row, h * HD + 16 * t + 4 * q4, nkc)) =
+          make_uint2((uint32_t)f2bf(r[0]) | ((uint32_t)f2bf(r[1]) << 16), (uint32_t)f2bf(r[2]) | ((uint32_t)f2bf(r[3]) << 16));
     }
   }
 }
 
+// apack: A in fragment order (every A operand the TTT kernels produce); the
+// fusion GEMM reads the caller's row-major features.
 template <class Epi>
-hipError_t bg_launch(const bf16* A, int lda, int M, const void* W, bool packed, int N, int K, RowMap map, Epi epi,
-                     hipStream_t st) {
+hipError_t bg_launch(const bf16* A, int lda, bool apack, int M, const void* W, bool packed, int N, int K, RowMap map,
+                     Epi epi, hipStream_t st) {
   const int grid = bg_grid(M, N);
-  if (packed)
-    big_gemm_kernel<true, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, (const bf16*)W, N, K, map, epi);
-  else
-    big_gemm_kernel<false, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, (const bf16*)W, N, K, map, epi);
+  const bf16* Wb = (const bf16*)W;
+  if (packed && apack) big_gemm_kernel<true, true, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
+  else if (packed) big_gemm_kernel<true, false, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
+  else if (apack) big_gemm_kernel<false, true, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
+  else big_gemm_kernel<false, false, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
   return hipGetLastError();
 }
 
@@ -601,13 +642,13 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
   }
   {
     TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-    E3_CHECK(bg_launch((const bf16*)feats, 3 * d, M, w.fc, pk, d, 3 * d, plain, BEpiStoreF{L.hs, d, true}, st));
+    E3_CHECK(bg_launch((const bf16*)feats, 3 * d, false, M, w.fc, pk, d, 3 * d, plain, BEpiStoreF{L.hs, d, true}, st));
   }
   for (int j = 1; j <= R; ++j) {
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_prologue_kernel<<<M, TR, 0, st>>>((const bf16*)w.emb, j == 1 ? tokens : L.tok, L.hs, d, w.norm_e, w.norm_s,
-                                            eps, L.x);
+      ttt_prologue_kernel<<<M / 16, TR, 0, st>>>((const bf16*)w.emb, j == 1 ? tokens : L.tok, L.hs, d, w.norm_e,
+                                                 w.norm_s, eps, L.x);
       E3_CHECK(hipGetLastError());
     }
     bf16* kdst = j == 1 ? L.k1 : L.kc + (size_t)(j - 2) * M * kvd;
@@ -615,7 +656,7 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
       TEpiQKV epi{L.q, kdst, vdst, j == 1, L.rope, hq, hkv, hd, S, j - 1};
-      E3_CHECK(bg_launch(L.x, 2 * d, M, w.qkv, pk, qd + 2 * kvd, 2 * d, pair_head, epi, st));
+      E3_CHECK(bg_launch(L.x, 2 * d, true, M, w.qkv, pk, qd + 2 * kvd, 2 * d, pair_head, epi, st));
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_ATTN, st);
@@ -633,26 +674,26 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      E3_CHECK(bg_launch(L.a, qd, M, w.o, pk, d, qd, plain, BEpiResid{L.hs, d}, st));
+      E3_CHECK(bg_launch(L.a, qd, true, M, w.o, pk, d, qd, plain, BEpiResid{L.hs, d}, st));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M, TR, 0, st>>>(L.hs, d, w.norm_ffn, eps, L.x);
+      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(L.hs, d, w.norm_ffn, eps, L.x);
       E3_CHECK(hipGetLastError());
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      E3_CHECK(bg_launch(L.x, d, M, w.gate_up, pk, 2 * F, d, pair_ffn, BEpiSwiGLU{L.z, F}, st));
-      E3_CHECK(bg_launch(L.z, F, M, w.down, pk, d, F, plain, BEpiResid{L.hs, d}, st));
+      E3_CHECK(bg_launch(L.x, d, true, M, w.gate_up, pk, 2 * F, d, pair_ffn, BEpiSwiGLU{L.z, F}, st));
+      E3_CHECK(bg_launch(L.z, F, true, M, w.down, pk, d, F, plain, BEpiResid{L.hs, d}, st));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M, TR, 0, st>>>(L.hs, d, w.norm_out, eps, L.x);
+      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(L.hs, d, w.norm_out, eps, L.x);
       E3_CHECK(hipGetLastError());
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_CE, st);
-      E3_CHECK(bg_launch(L.x, d, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st));
+      E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
