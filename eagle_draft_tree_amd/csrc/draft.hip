@@ -55,9 +55,10 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
     const T* __restrict__ emb, const int32_t* __restrict__ tokens, const T* __restrict__ state,
     const float* __restrict__ h_tree, const int32_t* __restrict__ parent_slot, int mode, int rows,
     int d, const float* __restrict__ ge, const float* __restrict__ gs, float eps,
-    float* __restrict__ S, T* __restrict__ x) {
+    float* __restrict__ S, T* __restrict__ x, unsigned* __restrict__ topk_ctr, int n_ctr) {
   __shared__ float red[RT / 64];
   const int r = blockIdx.x;
+  if (threadIdx.x == 0 && r < n_ctr) topk_ctr[r] = 0u;  // the step's top-k arrival counters
   const int b = r / rows;
   const T* e = emb + (size_t)tokens[r] * d;
   const float* hs = nullptr;
@@ -423,10 +424,13 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   const RowMap pair_head{MAP_PAIR_HEAD, hd, F};
   const bool pk = w.layout == EAGLE3_LAYOUT_PACKED;
 
+  const int topk_last = c.topk_rows == EAGLE3_TOPK_LAST;
+  const int Rl = topk_last ? c.B : R;  // rows through the LM head and top-k
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
     prologue_kernel<T><<<R, RT, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree, c.parent_slot,
-                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x);
+                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x,
+                                         topk_counters(ws.topk, Rl, V), Rl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
@@ -549,7 +553,6 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       }
     }
   }
-  const int topk_last = c.topk_rows == EAGLE3_TOPK_LAST;
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
     final_norm_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, down_splits, R, ws.h2, d, w.norm_out, dm.rms_eps, c.mode,
@@ -557,7 +560,6 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // ---- LM head + top-k
-  const int Rl = topk_last ? c.B : R;
   float* logits = c.logits_out ? c.logits_out : ws.logits;
   {
     TimedScope ts(EAGLE3_KC_LMHEAD, st);
@@ -571,7 +573,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     }
   }
   TimedScope ts(EAGLE3_KC_TOPK, st);
-  return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, st);
+  return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, true, st);
 }
 
 hipError_t draft_step(const DraftCall& c, hipStream_t st) {

@@ -26,8 +26,10 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
 
 // ---- top-k + log-probs over vocab rows (topk.hip)
 size_t topk_ws_bytes(int rows, int V);
-hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp,
-                       float* lse, void* ws, hipStream_t st);
+// per-row arrival counters inside a top-k workspace (must be zero at launch)
+unsigned* topk_counters(void* ws, int rows, int V);
+hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse, void* ws,
+                       bool counters_zeroed, hipStream_t st);
 
 // ---- dynamic tree (tree.hip)
 size_t tree_state_bytes_per_req(int k, int D);

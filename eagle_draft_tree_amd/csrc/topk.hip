@@ -3,16 +3,26 @@
 // blog, 关于 Efficient LM Head: the draft LM head is a large share of the
 // draft forward).
 //
-// Phase 1 (grid: partitions x rows): a workgroup loads its TK_PS logits with
-// 16-byte loads into registers (all loads in flight at once); each wave
-// selects its k best in k rounds of wavefront argmax over the lanes' bests,
-// and wave 0 pops the k best of the 4 wave lists.
-// It also writes the partition's (max, sum exp(x - max)).
-// Phase 2 (grid: rows, one wave each): the partitions' candidates sit in
-// registers and k rounds of wave argmax select the top-k; the LSE merges the
-// partition pairs with shuffle reductions.  Order everywhere: value desc, id
-// asc.  Every selection is a register/shuffle computation, so no step waits
-// on a chain of dependent memory accesses.
+// One kernel, grid (partitions of 4096 logits) x rows.  A workgroup loads
+// its logits with 16-byte loads (all in flight at once) and writes the
+// partition's (max, sum exp(x - max)) and its k best (value desc, id asc).
+// Selection by threshold and rank: each wave finds the k-th largest of its
+// 64 lanes' maxima, so at least k of the partition's logits reach the
+// largest of the four wave thresholds and the partition's k best are all
+// among the logits at or above it (about 3k of 4096 for Gaussian logits);
+// those candidates go to LDS and each one's rank is counted against the
+// others.  The last workgroup of a row to finish (a per-row arrival counter,
+// zeroed before the launch) merges the partitions the same way: the
+// threshold is the larger of the k-th largest partition maximum and the
+// largest partition k-th value.  A candidate set larger than the LDS list
+// (many equal logits) falls back to k rounds of wavefront argmax, which
+// gives the same result.  Ties: value desc, then id asc, everywhere.
+//
+// Cross-workgroup hand-off without an L2 write-back: the partials are
+// written with agent-scope atomic stores (write-through to the device's
+// coherence point), each wave waits for its stores to complete before the
+// barrier that precedes the counter increment, and the merging workgroup
+// reads them with agent-scope atomic loads.
 #include <limits.h>
 
 #include "common.hpp"
@@ -23,30 +33,106 @@ namespace e3 {
 constexpr int TK_THREADS = 256;
 constexpr int TK_PER_THREAD = 16;
 constexpr int TK_PS = TK_THREADS * TK_PER_THREAD;  // 4096 elements per partition
+constexpr int TK_CMAX = 256;                       // candidates ranked in LDS
 
 struct Cand {
   float v;
   int id;
 };
 
-// Phase 1.  Lane-level selection keeps no sorted lists: each lane tracks the
-// best of its 16 values not yet taken (a removal bit mask, so every register
-// index is static), each of the k rounds is one wavefront argmax, and only
-// the lane that owned the winner rescans its 16 values.
-__global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* __restrict__ logits, int V, int k,
-                                                                  int nparts, float* __restrict__ pv,
-                                                                  int* __restrict__ pid, float* __restrict__ pm,
-                                                                  float* __restrict__ ps) {
+template <typename X>
+__device__ __forceinline__ void st_dev(X* p, X v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename X>
+__device__ __forceinline__ X ld_dev(const X* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// k-th largest of the wave's values counted with multiplicity (at least k
+// lanes hold a value >= the result), or -inf when fewer than k lanes hold a
+// finite value.  Uniform result.
+__device__ __forceinline__ float wave_kth_largest(float x, int k) {
+  int got = 0;
+  float t = -INFINITY;
+  while (got < k) {
+    const float mx = wave_max(x);
+    if (mx == -INFINITY) return -INFINITY;
+    got += __popcll(__ballot(x == mx));
+    if (x == mx) x = -INFINITY;
+    t = mx;
+  }
+  return t;
+}
+
+// Rank each of the C <= TK_CMAX candidates (value, id bits) among the others
+// and write the k best in order; slots past C get (-inf, INT_MAX).  The list
+// is padded with (-inf, INT_MAX) entries to a multiple of 8, which are never
+// better than a candidate.
+template <bool DEV>
+__device__ __forceinline__ void rank_and_write(const float2* cand, int C, int k, float* ov, int32_t* oi, float sub) {
+  auto put = [&](int r, float v, int id) {
+    if (DEV) {
+      st_dev(ov + r, v);
+      st_dev(oi + r, id);
+    } else {
+      ov[r] = v;
+      oi[r] = id;
+    }
+  };
+  const int t = threadIdx.x;
+  if (t < C) {
+    const float2 me = cand[t];
+    const int id = __float_as_int(me.y);
+    int r = 0;
+    for (int j0 = 0; j0 < C; j0 += 8) {
+      float2 c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = cand[j0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += better(c[u].x, __float_as_int(c[u].y), me.x, id) ? 1 : 0;
+    }
+    if (r < k) put(r, me.x - sub, id);
+  } else if (t < k) {
+    put(t, -INFINITY - sub, INT_MAX);
+  }
+}
+
+// Append (v, id) to the LDS candidate list (dropped past TK_CMAX; the
+// caller then takes the fallback).
+__device__ __forceinline__ void push_cand(float2* cand, int* ncand, float v, int id) {
+  const int pos = atomicAdd(ncand, 1);
+  if (pos < TK_CMAX) cand[pos] = make_float2(v, __int_as_float(id));
+}
+
+// Pad the list read back as C entries to a multiple of 8 (call between two
+// barriers).
+__device__ __forceinline__ void pad_cand(float2* cand, int C) {
+  const int t = threadIdx.x;
+  if (C <= TK_CMAX && t >= C && t < ((C + 7) & ~7)) cand[t] = make_float2(-INFINITY, __int_as_float(INT_MAX));
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ logits, int V, int k, int nparts,
+                                                          float* pv, int* pid, float* pm, float* ps,
+                                                          unsigned* done, int32_t* __restrict__ ids,
+                                                          float* __restrict__ lp, float* __restrict__ lse_out) {
   const int part = blockIdx.x, row = blockIdx.y;
   const float* x = logits + (size_t)row * V;
   const int lo = part * TK_PS;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // element e of this thread: id lo + 4*(threadIdx.x + 256*(e/4)) + e%4 (ids rise with e)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ float2 cand[TK_CMAX + 8];
+  __shared__ float mred[TK_THREADS / 64], sred[TK_THREADS / 64], tred[TK_THREADS / 64];
+  __shared__ Cand wl[TK_THREADS / 64][EAGLE3_MAX_TOPK];
+  __shared__ int ncand, last;
+  __shared__ float rowL, rowT;
+  if (tid == 0) ncand = 0;
+
+  // element e of this thread: id lo + 4*(tid + 256*(e/4)) + e%4 (ids rise with e)
   float v[TK_PER_THREAD];
   const bool vec_ok = (V & 3) == 0;
 #pragma unroll
   for (int j = 0; j < TK_PER_THREAD / 4; ++j) {
-    const int y0 = lo + 4 * (threadIdx.x + TK_THREADS * j);
+    const int y0 = lo + 4 * (tid + TK_THREADS * j);
     if (vec_ok && y0 + 3 < V) {
       const float4 f = *(const float4*)(x + y0);
       v[4 * j] = f.x;
@@ -58,8 +144,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* _
       for (int c = 0; c < 4; ++c) v[4 * j + c] = y0 + c < V ? x[y0 + c] : -INFINITY;
     }
   }
-  auto id_of = [&](int e) { return lo + 4 * (threadIdx.x + TK_THREADS * (e >> 2)) + (e & 3); };
-  uint32_t taken = 0;  // removed or past V
+  auto id_of = [&](int e) { return lo + 4 * (tid + TK_THREADS * (e >> 2)) + (e & 3); };
+  uint32_t taken = 0;  // past V (and, in the fallback, removed)
 #pragma unroll
   for (int e = 0; e < TK_PER_THREAD; ++e)
     if (id_of(e) >= V) taken |= 1u << e;
@@ -70,151 +156,205 @@ __global__ __launch_bounds__(TK_THREADS) void topk_partial_kernel(const float* _
 #pragma unroll
   for (int e = 0; e < TK_PER_THREAD; ++e)
     if (!((taken >> e) & 1u) && v[e] > -INFINITY) s += expf(v[e] - m);
-  float bv;
-  int bi, be;
-  auto rescan = [&]() {
-    bv = -INFINITY;
-    bi = INT_MAX;
-    be = 0;
-#pragma unroll
-    for (int e = 0; e < TK_PER_THREAD; ++e) {
-      const int y = id_of(e);
-      if (!((taken >> e) & 1u) && better(v[e], y, bv, bi)) {
-        bv = v[e];
-        bi = y;
-        be = e;
-      }
-    }
-  };
-  rescan();
-  __shared__ float mred[TK_THREADS / 64];
-  __shared__ float sred[TK_THREADS / 64];
-  __shared__ Cand wl[TK_THREADS / 64][EAGLE3_MAX_TOPK];
   // (max, sum): max first, then sums rescaled to it, added in a fixed order
   const float wm = wave_max(m);
-  if (lane == 0) mred[w] = wm;
+  const float tw = wave_kth_largest(m, k);
+  if (lane == 0) {
+    mred[w] = wm;
+    tred[w] = tw;
+  }
   __syncthreads();
-  float M = -INFINITY;
+  float M = -INFINITY, T = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < TK_THREADS / 64; ++i) M = fmaxf(M, mred[i]);
+  for (int i = 0; i < TK_THREADS / 64; ++i) {
+    M = fmaxf(M, mred[i]);
+    T = fmaxf(T, tred[i]);
+  }
   const float mine = (m == -INFINITY) ? 0.f : s * expf(m - M);
   const float ws = wave_sum(mine);
   if (lane == 0) sred[w] = ws;
-  // per-wave top-k: k rounds of wavefront argmax over the lanes' bests
-  for (int r = 0; r < k; ++r) {
-    Cand c{bv, bi};
-    wave_argmax(c.v, c.id);
-    if (lane == 0) wl[w][r] = c;
-    if (bi == c.id && c.id != INT_MAX) {  // the owner takes it and rescans
-      taken |= 1u << be;
-      rescan();
+  // candidates: every logit at or above the threshold
+#pragma unroll
+  for (int e = 0; e < TK_PER_THREAD; ++e)
+    if (!((taken >> e) & 1u) && v[e] >= T) push_cand(cand, &ncand, v[e], id_of(e));
+  __syncthreads();
+  const int C = ncand;
+  pad_cand(cand, C);
+  __syncthreads();
+  const size_t o = (size_t)row * nparts + part;
+  if (tid == 0) {
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < TK_THREADS / 64; ++i) S += sred[i];
+    st_dev(pm + o, M);
+    st_dev(ps + o, S);
+  }
+  if (C <= TK_CMAX) {
+    rank_and_write<true>(cand, C, k, pv + o * k, pid + o * k, 0.f);
+  } else {
+    // fallback: per-wave k best by k rounds of wavefront argmax over the
+    // lanes' bests, then wave 0 pops the k best of the four wave lists
+    float bv;
+    int bi, be;
+    auto rescan = [&]() {
+      bv = -INFINITY;
+      bi = INT_MAX;
+      be = 0;
+#pragma unroll
+      for (int e = 0; e < TK_PER_THREAD; ++e) {
+        const int y = id_of(e);
+        if (!((taken >> e) & 1u) && better(v[e], y, bv, bi)) {
+          bv = v[e];
+          bi = y;
+          be = e;
+        }
+      }
+    };
+    rescan();
+    for (int r = 0; r < k; ++r) {
+      Cand c{bv, bi};
+      wave_argmax(c.v, c.id);
+      if (lane == 0) wl[w][r] = c;
+      if (bi == c.id && c.id != INT_MAX) {
+        taken |= 1u << be;
+        rescan();
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int nc = (TK_THREADS / 64) * k;  // <= 64
+      Cand mc{-INFINITY, INT_MAX};
+      if (lane < nc) {
+        const int ww = lane / k;
+        mc = wl[ww][lane - ww * k];
+      }
+      for (int r = 0; r < k; ++r) {
+        Cand c = mc;
+        wave_argmax(c.v, c.id);
+        if (lane == 0) {
+          st_dev(pv + o * k + r, c.v);
+          st_dev(pid + o * k + r, c.id);
+        }
+        if (mc.id == c.id) mc = Cand{-INFINITY, INT_MAX};
+      }
+    }
+  }
+
+  // ---- the row's last workgroup merges the partitions
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&done[row], 1u) == (unsigned)(nparts - 1);
+  __syncthreads();
+  if (!last) return;
+  const int n = nparts * k;  // <= 64 * 16
+  const float* rv = pv + (size_t)row * n;
+  const int* ri = pid + (size_t)row * n;
+  // every list entry of the row, loaded at once (4 per thread)
+  float lv[4];
+  int li[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + TK_THREADS * j;
+    lv[j] = i < n ? ld_dev(rv + i) : -INFINITY;
+    li[j] = i < n ? ld_dev(ri + i) : INT_MAX;
+  }
+  if (w == 0) {
+    // LSE over the partitions' (max, sum) pairs (nparts <= 64), fixed order
+    const float pmv = lane < nparts ? ld_dev(pm + (size_t)row * nparts + lane) : -INFINITY;
+    const float psv = lane < nparts ? ld_dev(ps + (size_t)row * nparts + lane) : 0.f;
+    const float head = lane < nparts ? ld_dev(rv + lane * k) : -INFINITY;
+    const float kth = lane < nparts ? ld_dev(rv + lane * k + k - 1) : -INFINITY;
+    const float M2 = wave_max(pmv);
+    const float L = M2 + logf(wave_sum(pmv == -INFINITY ? 0.f : psv * expf(pmv - M2)));
+    // threshold: at least k list entries reach it
+    const float T2 = fmaxf(wave_kth_largest(head, k), wave_max(kth));
+    if (lane == 0) {
+      rowL = L;
+      rowT = T2;
+      ncand = 0;
+      if (lse_out) lse_out[row] = L;
     }
   }
   __syncthreads();
-  const size_t o = (size_t)row * nparts + part;
-  if (w == 0) {
-    if (lane == 0) {
-      float S = 0.f;
+  const float L = rowL, T2 = rowT;
 #pragma unroll
-      for (int i = 0; i < TK_THREADS / 64; ++i) S += sred[i];
-      pm[o] = M;
-      ps[o] = S;
-    }
-    // lane i holds candidate i of the 4 wave lists; k rounds of wave argmax
-    const int nc = (TK_THREADS / 64) * k;  // <= 64
-    Cand mc{-INFINITY, INT_MAX};
-    if (lane < nc) {
-      const int ww = lane / k;
-      mc = wl[ww][lane - ww * k];
-    }
-    for (int r = 0; r < k; ++r) {
-      Cand c = mc;
-      wave_argmax(c.v, c.id);
-      if (lane == 0) {
-        pv[o * k + r] = c.v;
-        pid[o * k + r] = c.id;
-      }
-      if (mc.id == c.id) mc = Cand{-INFINITY, INT_MAX};
-    }
-  }
-}
-
-// Phase 2: one wave per row.  Lane l holds candidates l, l+64, ... (SLOTS
-// per lane), then k rounds of wave argmax pop the best; the LSE merges the
-// partition (max, sum) pairs with shuffle reductions (fixed order).
-template <int SLOTS>
-__global__ __launch_bounds__(64) void topk_merge_kernel(int k, int nparts, const float* __restrict__ pv,
-                                                        const int* __restrict__ pid, const float* __restrict__ pm,
-                                                        const float* __restrict__ ps, int32_t* __restrict__ ids,
-                                                        float* __restrict__ lp, float* __restrict__ lse_out) {
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int n = nparts * k;
-  float cv[SLOTS];
-  int ci[SLOTS];
+  for (int j = 0; j < 4; ++j)
+    if (li[j] != INT_MAX && lv[j] >= T2) push_cand(cand, &ncand, lv[j], li[j]);
+  __syncthreads();
+  const int C2 = ncand;
+  pad_cand(cand, C2);
+  __syncthreads();
+  if (C2 <= TK_CMAX) {
+    rank_and_write<false>(cand, C2, k, lp + (size_t)row * k, ids + (size_t)row * k, L);
+  } else if (w == 0) {
+    // fallback: lane l holds list entries l, l+64, ...; k rounds of argmax
+    constexpr int SLOTS = 16;
+    float cv[SLOTS];
+    int ci[SLOTS];
 #pragma unroll
-  for (int j = 0; j < SLOTS; ++j) {
-    const int i = lane + 64 * j;
-    cv[j] = i < n ? pv[(size_t)row * n + i] : -INFINITY;
-    ci[j] = i < n ? pid[(size_t)row * n + i] : INT_MAX;
-  }
-  float pmv = lane < nparts ? pm[(size_t)row * nparts + lane] : -INFINITY;
-  float psv = lane < nparts ? ps[(size_t)row * nparts + lane] : 0.f;
-  const float M = wave_max(pmv);
-  const float L = M + logf(wave_sum(pmv == -INFINITY ? 0.f : psv * expf(pmv - M)));
-  float bv = -INFINITY;
-  int bi = INT_MAX;
-  auto rescan = [&]() {
-    bv = -INFINITY;
-    bi = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < SLOTS; ++j)
-      if (better(cv[j], ci[j], bv, bi)) {
-        bv = cv[j];
-        bi = ci[j];
-      }
-  };
-  rescan();
-  for (int r = 0; r < k; ++r) {
-    float wv = bv;
-    int wi = bi;
-    wave_argmax(wv, wi);
-    if (lane == 0) {
-      ids[(size_t)row * k + r] = wi;
-      lp[(size_t)row * k + r] = wv - L;
+    for (int j = 0; j < SLOTS; ++j) {
+      const int i = lane + 64 * j;
+      cv[j] = i < n ? ld_dev(rv + i) : -INFINITY;
+      ci[j] = i < n ? ld_dev(ri + i) : INT_MAX;
     }
-    if (bi == wi) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    auto rescan = [&]() {
+      bv = -INFINITY;
+      bi = INT_MAX;
 #pragma unroll
       for (int j = 0; j < SLOTS; ++j)
-        if (ci[j] == wi) {
-          cv[j] = -INFINITY;
-          ci[j] = INT_MAX;
+        if (better(cv[j], ci[j], bv, bi)) {
+          bv = cv[j];
+          bi = ci[j];
         }
-      rescan();
+    };
+    rescan();
+    for (int r = 0; r < k; ++r) {
+      float wv = bv;
+      int wi = bi;
+      wave_argmax(wv, wi);
+      if (lane == 0) {
+        ids[(size_t)row * k + r] = wi;
+        lp[(size_t)row * k + r] = wv - L;
+      }
+      if (bi == wi) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j)
+          if (ci[j] == wi) {
+            cv[j] = -INFINITY;
+            ci[j] = INT_MAX;
+          }
+        rescan();
+      }
     }
   }
-  if (lse_out && lane == 0) lse_out[row] = L;
 }
+
+__global__ void topk_zero_kernel(unsigned* done, int rows) {
+  for (int i = threadIdx.x; i < rows; i += blockDim.x) done[i] = 0u;
+}
+
+static size_t topk_parts(int V) { return (V + TK_PS - 1) / TK_PS; }
 
 size_t topk_ws_bytes(int rows, int V) {
-  const size_t nparts = (V + TK_PS - 1) / TK_PS;
-  return (size_t)rows * nparts * (EAGLE3_MAX_TOPK * 8 + 8) + 256;
+  return (size_t)rows * topk_parts(V) * (EAGLE3_MAX_TOPK * 8 + 8) + (size_t)rows * 4 + 256;
 }
 
-hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp,
-                       float* lse, void* ws, hipStream_t st) {
-  const int nparts = (V + TK_PS - 1) / TK_PS;
+unsigned* topk_counters(void* ws, int rows, int V) {
+  return (unsigned*)((unsigned char*)ws + (size_t)rows * topk_parts(V) * (EAGLE3_MAX_TOPK * 8 + 8));
+}
+
+hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse, void* ws,
+                       bool counters_zeroed, hipStream_t st) {
+  const int nparts = (int)topk_parts(V);  // <= 64 (V <= 262144)
   float* pv = (float*)ws;
   int* pid = (int*)(pv + (size_t)rows * nparts * k);
   float* pm = (float*)(pid + (size_t)rows * nparts * k);
   float* ps = pm + (size_t)rows * nparts;
-  dim3 g1(nparts, rows);
-  topk_partial_kernel<<<g1, TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps);
-  const int n = nparts * k;  // nparts <= 64 (V <= 262144), k <= 16
-  if (n <= 128) topk_merge_kernel<2><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
-  else if (n <= 256) topk_merge_kernel<4><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
-  else if (n <= 512) topk_merge_kernel<8><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
-  else topk_merge_kernel<16><<<rows, 64, 0, st>>>(k, nparts, pv, pid, pm, ps, ids, lp, lse);
+  unsigned* done = topk_counters(ws, rows, V);
+  if (!counters_zeroed) topk_zero_kernel<<<1, 256, 0, st>>>(done, rows);
+  topk_kernel<<<dim3(nparts, rows), TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps, done, ids, lp, lse);
   return hipGetLastError();
 }
 

@@ -62,6 +62,10 @@ def test_topk(lib, V, k, rows):
     L[0, V - 1] = L[0, 5]                          # three-way tie across partitions
     if rows > 1:
         L[1, :] = np.round(L[1, :], 1)             # many ties everywhere
+    if rows > 2:
+        L[2, :] = 0.25                             # all equal: ids 0..k-1
+    if rows > 3:
+        L[3, :] = np.minimum(L[3, :], 3.0)         # hundreds of equal values at the top of every partition
     ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
     ids = torch.empty(rows, k, dtype=torch.int32, device="cuda")
     lp = torch.empty(rows, k, dtype=torch.float32, device="cuda")
