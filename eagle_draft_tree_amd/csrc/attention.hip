@@ -10,6 +10,11 @@
 // group's query heads; the next chunk's K/V loads are in flight while the
 // current chunk is computed.  Each workgroup writes a partial (max, sum,
 // o[hd]); a merge kernel combines the splits in index order (deterministic).
+//
+// bf16 caches use attn_mfma_kernel (below): matrix-core scores and P.V with
+// each wave streaming its own 32-key sub-chunks; fp32 caches use the
+// vector-ALU attn_partial_kernel.
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,6 +34,7 @@ struct AttnArgs {
   const uint64_t* anc;  // [Rtot] (TREE) or NULL
   int cap, max_blocks, block_size;
   int B, rows, hq, hkv, mode, n_commit_splits, cpw, n_qgroups;
+  int n_cache_sub, spw, nsplits;  // attn_mfma_kernel: cache sub-chunks, sub-chunks per wave, partial slots
   float scale;
   float* part_o;   // [Rtot*Hq][nsplits][hd]
   float* part_ml;  // [Rtot*Hq][nsplits][2]
@@ -303,55 +309,339 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// out[row][h*hd + i] = merged attention output, rounded to T.  One wave per
-// (row, head): chunk maxima and weights first (lanes over chunks), then the
-// weighted sum of the chunk partials in chunk order.
-template <typename T, int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml, int nchunks, int hq,
-                                                        T* __restrict__ out) {
-  constexpr int MAXC = 512;
-  __shared__ float wc[MAXC];
-  const size_t rh = blockIdx.x;  // row*hq + h
-  const int lane = threadIdx.x;
-  const float* ml = part_ml + 2 * rh * nchunks;
-  float mloc = -INFINITY;
-  for (int c = lane; c < nchunks; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
-  const float M = wave_max(mloc);
-  float lloc = 0.f;
-  for (int c = lane; c < nchunks; c += 64) {
-    const float m = ml[2 * c];
-    const float w = m == -INFINITY ? 0.f : expf(m - M);
-    wc[c] = w;
-    lloc += ml[2 * c + 1] * w;
+// ---------------------------------------------------------------------------
+// Matrix-core decode attention for bf16 caches.
+//
+// Work unit: one wave = (request b, KV head g, group of 16 query vectors,
+// wave split w < nsplits); consecutive waves are the KV heads of one split.  A request's key space is its committed cache rows
+// in 32-key sub-chunks followed, in TREE mode, by the 64 tree slots as two
+// more sub-chunks; the sub-chunks holding visible keys are dealt out in equal
+// contiguous runs over the nsplits waves of (b, g, group), so short prefixes
+// do not leave a few waves with all of the work.  Each wave keeps an online
+// softmax over its run and writes one partial per query vector (an empty run
+// writes an empty partial); attn_merge_kernel combines them.  The four waves
+// of a workgroup are independent units: no workgroup barrier.
+//
+// Per sub-chunk, with the 16x16x32 bf16 MFMA:
+//   S^T[key][query] = K Q^T: the K fragment (16 keys x 32 head dims) is read
+//     straight from the cache (16 contiguous bytes per lane), Q^T is loaded
+//     once per wave;
+//   online softmax on S^T: lane l holds query l%16 and keys 4(l/16)+i of
+//     each 16-key tile, so a query's maximum needs two cross-row shuffles;
+//   O^T[dim][query] += V^T P^T: P^T is already in B-operand layout if the
+//     k-slots of lane group j are taken as keys {4j..4j+3, 16+4j..16+4j+3};
+//     V^T takes the same key order with the LDS transpose read
+//     (ds_read_b64_tr_b16) from the wave's V tile, two reads per 16 dims.
+//   P is split into bf16 hi + lo halves (two MFMAs), so the probabilities
+//     keep about 16 significant bits; K, Q and V are bf16 already, products
+//     are exact and accumulate in fp32.
+// Keys that are out of range or never visible read the cache's first row
+// (always mapped) and are zeroed in registers, so stale rows never feed NaN
+// into P.V; their scores are set to -inf.  The registers fit two waves per
+// SIMD: latency is hidden by the other waves rather than by a deeper
+// per-wave pipeline.
+constexpr int SUB = 32;  // keys per sub-chunk
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+__device__ __forceinline__ float xor_max16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float xor_sum16_32(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 a, s16x4 b) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// 8 floats -> bf16 hi (round to nearest even) and lo = bf16(x - hi)
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h[t] = f2bf(x[t]);
+    l[t] = f2bf(x[t] - bf2f(h[t]));
   }
-  const float L = wave_sum(lloc);
-  __syncthreads();
-  float acc[HD / 64];
-#pragma unroll
-  for (int j = 0; j < HD / 64; ++j) acc[j] = 0.f;
-  const float* po = part_o + rh * nchunks * HD;
-  int c = 0;
-  for (; c + 8 <= nchunks; c += 8) {
-    float v[8][HD / 64];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int j = 0; j < HD / 64; ++j) v[u][j] = po[(size_t)(c + u) * HD + lane + 64 * j];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int j = 0; j < HD / 64; ++j) acc[j] = fmaf(v[u][j], wc[c + u], acc[j]);
-  }
-  for (; c < nchunks; ++c)
-#pragma unroll
-    for (int j = 0; j < HD / 64; ++j) acc[j] = fmaf(po[(size_t)c * HD + lane + 64 * j], wc[c], acc[j]);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int j = 0; j < HD / 64; ++j) Elem<T>::st(out, rh * HD + lane + 64 * j, acc[j] * inv);
+  uint4 uh, ul;
+  __builtin_memcpy(&uh, h, 16);
+  __builtin_memcpy(&ul, l, 16);
+  hi = __builtin_bit_cast(bf16x8, uh);
+  lo = __builtin_bit_cast(bf16x8, ul);
 }
 
-int attn_num_chunks(int cap_rows) { return (cap_rows + CH - 1) / CH + 1; }
+// KVM: cache addressing, 0 = contiguous, 1 = paged with the wave's block
+// entries staged in lanes (at most 64), 2 = paged with a table load per key.
+template <int HD, int KVM>
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int KS = HD / 32;             // k-steps of S
+  constexpr int HT = HD / 16;             // head-dim tiles of O^T
+  constexpr int VROW = HD + 16;           // padded V tile row (elements)
+  constexpr int VLD = SUB * HD / 8 / 64;  // 16-byte V loads per lane per sub-chunk
+  __shared__ __attribute__((aligned(16))) bf16 vtile[4][SUB * VROW];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
+  const int c16 = lane & 15, g16 = lane >> 4;
+  // wave -> (split, KV head) with the head fastest: the waves reading the
+  // same cache rows (all heads of a position range) run side by side
+  const int wid = blockIdx.x * 4 + w;
+  const int wsplit = wid / a.hkv, g = wid - wsplit * a.hkv;
+  const int qgrp = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.hq / a.hkv;
+  const int nq_total = a.rows * G;
+  const int q0 = qgrp * 16;
+  if (q0 >= nq_total || wsplit >= a.nsplits) return;
+  const int ctx = a.ctx_len[b];
+  const bool tree = a.mode == EAGLE3_TREE;
+  const int maxvis = tree ? ctx : ctx + a.rows;  // cache rows visible to some query
+  // active sub-chunks: cache 0..ncs-1, then (TREE) tree slots 0-31, 32-63
+  const int ncs = min((maxvis + SUB - 1) / SUB, a.n_cache_sub);
+  const int n_act = ncs + (tree ? 2 : 0);
+  const int per = (n_act + a.nsplits - 1) / a.nsplits;
+  const int i0 = min(wsplit * per, n_act), i1 = min(i0 + per, n_act);
+  bf16* vt = vtile[w];
+
+  // the lane's query vector: row rr = qi / G, head g*G + qi % G (none past nq)
+  const int qi = q0 + c16;
+  const int qrow = qi < nq_total ? qi / G : -1;
+  bf16x8 qf[KS];
+  {
+    const int h = g * G + (qi - (qi / G) * G);
+    const bf16* qp = (const bf16*)a.q + ((size_t)(b * a.rows + max(qrow, 0)) * a.hq + h) * HD + 8 * g16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 v = *(const u32x4*)(qp + ks * 32);
+      qf[ks] = as_bf16x8(qrow >= 0 ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  const uint64_t vis_tree = (tree && qrow >= 0) ? a.anc[b * a.rows + qrow] : 0ull;
+  // tree slots some row can see (others are never loaded): the rows' masks
+  // are loaded across the lanes and OR-reduced
+  uint64_t any_vis = ~0ull;
+  if (tree && i1 > ncs) {
+    uint64_t v = 0ull;
+    for (int rr = lane; rr < a.rows; rr += 64) v |= a.anc[b * a.rows + rr];
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      lo |= (uint32_t)__shfl_xor((int)lo, sh);
+      hi |= (uint32_t)__shfl_xor((int)hi, sh);
+    }
+    any_vis = ((uint64_t)hi << 32) | lo;
+  }
+  // paged cache (KVM 1): the run's block-table entries, one per lane, read
+  // with a lane shuffle (no dependent global load before a sub-chunk's copies)
+  int blk0 = 0, blk_reg = 0;
+  if (KVM == 1 && i0 < ncs) {
+    blk0 = (i0 * SUB) / a.block_size;
+    const int blk_end = min((min(i1, ncs) * SUB + a.block_size - 1) / a.block_size, a.max_blocks);
+    if (blk0 + lane < blk_end) blk_reg = a.block_table[(size_t)b * a.max_blocks + blk0 + lane];
+    // an identity DPP move: the wait for the table load happens once, here,
+    // instead of before every shuffle of it
+    blk_reg = __builtin_amdgcn_update_dpp(0, blk_reg, 0xE4, 0xF, 0xF, false);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) o[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Source row of key p (0..31) of active sub-chunk i, and whether it is a
+  // real, possibly visible key.  Every lane calls it (the block shuffle
+  // reads other lanes' registers).
+  auto key_row = [&](int i, int p, const void* cache, const void* tslots, bool& ok)
+                     __attribute__((always_inline)) -> const bf16* {
+    if (i < ncs) {
+      const int pos = i * SUB + p;
+      ok = pos < maxvis;
+      size_t off;
+      if (KVM == 0) {
+        off = (((size_t)b * a.cap + pos) * a.hkv + g) * HD;
+      } else {
+        const int bi = pos / a.block_size;
+        int blk;
+        if (KVM == 1) blk = __shfl(blk_reg, min(max(bi - blk0, 0), 63));
+        else blk = ok ? a.block_table[(size_t)b * a.max_blocks + bi] : 0;
+        off = (((size_t)blk * a.block_size + pos % a.block_size) * a.hkv + g) * HD;
+      }
+      return ok ? (const bf16*)cache + off : (const bf16*)cache;
+    }
+    const int slot = (i - ncs) * SUB + p;
+    ok = ((any_vis >> slot) & 1ull) != 0;
+    return ok ? (const bf16*)tslots + ((size_t)(b * EAGLE3_MAX_TREE_SLOTS + slot) * a.hkv + g) * HD
+              : (const bf16*)tslots;
+  };
+
+  for (int i = i0; i < i1; ++i) {
+    // copies: K fragments (keys kt*16 + c16) and V rows, all issued at once
+    const bf16* kr[2];
+    const bf16* vr[VLD];
+    uint32_t okm = 0;  // bit kt: K row real; bit 2 + v: V row real
+    bool ok;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      kr[kt] = key_row(i, kt * 16 + c16, a.kc, a.tk, ok);
+      okm |= (uint32_t)ok << kt;
+    }
+#pragma unroll
+    for (int v = 0; v < VLD; ++v) {
+      const int e = v * 64 + lane, pk = e / (HD / 8), c = e - pk * (HD / 8);
+      vr[v] = key_row(i, pk, a.vc, a.tv, ok) + 8 * c;
+      okm |= (uint32_t)ok << (2 + v);
+    }
+    u32x4 kf[2][KS], vf[VLD];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = *(const u32x4*)(kr[kt] + ks * 32 + 8 * g16);
+#pragma unroll
+    for (int v = 0; v < VLD; ++v) vf[v] = *(const u32x4*)vr[v];
+    // V into the wave's tile (rows in key order), masked rows as zeros
+#pragma unroll
+    for (int v = 0; v < VLD; ++v) {
+      const int e = v * 64 + lane, pk = e / (HD / 8), c = e - pk * (HD / 8);
+      const uint32_t keep = 0u - ((okm >> (2 + v)) & 1u);
+      *(u32x4*)(vt + pk * VROW + 8 * c) = vf[v] & keep;
+    }
+    // S^T = K Q^T for the two 16-key tiles
+    f32x4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t keep = 0u - ((okm >> kt) & 1u);
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kt][ks] & keep), qf[ks], sc[kt], 0, 0, 0);
+    }
+    // mask and scale: key p0 + kt*16 + 4*g16 + t for the lane's query row
+    const bool is_tree = i >= ncs;
+    const int p0 = is_tree ? (i - ncs) * SUB : i * SUB;
+    const int lim = tree ? ctx : ctx + qrow + 1;
+    float x[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pk = p0 + kt * 16 + 4 * g16 + t;
+        const bool vis = qrow >= 0 && (is_tree ? ((vis_tree >> pk) & 1ull) != 0 : pk < lim);
+        x[kt * 4 + t] = vis ? sc[kt][t] * a.scale : -INFINITY;
+        mloc = fmaxf(mloc, x[kt * 4 + t]);
+      }
+    const float m_new = fmaxf(m_run, xor_max16_32(mloc));
+    const float al = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      x[t] = m_new == -INFINITY ? 0.f : expf(x[t] - m_new);
+      psum += x[t];
+    }
+    l_run = l_run * al + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) o[ht] *= al;
+    bf16x8 phi, plo;
+    split_bf16x8(x, phi, plo);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      // V^T fragment: dims ht*16 + c16, keys {4*g16 + t} and {16 + 4*g16 + t}, t < 4
+      const bf16* src = vt + (4 * g16 + (c16 >> 2)) * VROW + ht * 16 + 4 * (c16 & 3);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)src);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(src + 16 * VROW));
+      const bf16x8 vfr = cat_bf16x8(va, vb);
+      o[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, phi, o[ht], 0, 0, 0);
+      o[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, plo, o[ht], 0, 0, 0);
+    }
+  }
+  // partial of the lane's query vector: (m, l) and o (unnormalised, relative to m)
+  const float l = xor_sum16_32(l_run);
+  if (qrow < 0) return;
+  const int h = g * G + (qi - qrow * G);
+  const size_t oi = ((size_t)(b * a.rows + qrow) * a.hq + h) * a.nsplits + wsplit;
+  if (g16 == 0) {
+    a.part_ml[2 * oi] = m_run;
+    a.part_ml[2 * oi + 1] = l;
+  }
+  float* dst = a.part_o + oi * HD + 4 * g16;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) *(float4*)(dst + ht * 16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
+}
+
+// out[row][h*hd + i] = merged attention output, rounded to T.  One
+// workgroup per (row, head): wave 0 computes the partials' weights
+// exp(m_c - M) (lanes over partials) and L; wave w then sums the weighted
+// partial vectors c = w, w+4, ... and the four sums are added in wave order.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml, int nchunks, int hq,
+                                                         T* __restrict__ out) {
+  constexpr int MAXC = 512;
+  constexpr int EPL = HD / 64;  // elements per lane
+  __shared__ float wc[MAXC];
+  __shared__ float red[4][HD];
+  __shared__ float sL;
+  const size_t rh = blockIdx.x;  // row*hq + h
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (w == 0) {
+    const float* ml = part_ml + 2 * rh * nchunks;
+    float mloc = -INFINITY;
+    for (int c = lane; c < nchunks; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
+    const float M = wave_max(mloc);
+    float lloc = 0.f;
+    for (int c = lane; c < nchunks; c += 64) {
+      const float m = ml[2 * c];
+      const float wgt = m == -INFINITY ? 0.f : expf(m - M);
+      wc[c] = wgt;
+      lloc += ml[2 * c + 1] * wgt;
+    }
+    const float L = wave_sum(lloc);
+    if (lane == 0) sL = L;
+  }
+  __syncthreads();
+  float acc[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+  const float* po = part_o + rh * nchunks * HD;
+  int c = w;
+  for (; c + 12 < nchunks; c += 16) {
+    float v[4][EPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[u][j] = po[(size_t)(c + 4 * u) * HD + lane + 64 * j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) acc[j] = fmaf(v[u][j], wc[c + 4 * u], acc[j]);
+  }
+  for (; c < nchunks; c += 4)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] = fmaf(po[(size_t)c * HD + lane + 64 * j], wc[c], acc[j]);
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) red[w][lane + 64 * j] = acc[j];
+  __syncthreads();
+  if (w == 0) {
+    const float L = sL;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int i = lane + 64 * j;
+      Elem<T>::st(out, rh * HD + i, ((red[0][i] + red[1][i]) + red[2][i] + red[3][i]) * inv);
+    }
+  }
+}
+
+// partial slots per (row, head): the 32-key sub-chunks plus the two tree
+// sub-chunks, at most 512 (the merge kernel's limit); covers the fp32 kernel's
+// 64-key chunks too
+int attn_num_chunks(int cap_rows) {
+  const int n = (cap_rows + SUB - 1) / SUB + 2;
+  return n < 512 ? n : 512;
+}
 
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
   AttnArgs a;
@@ -373,6 +663,46 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
   a.mode = L.mode;
   const int G = L.hq / L.hkv;
   const int nq = L.rows * G;
+  const int rtot = L.B * L.rows;
+  a.scale = 1.0f / sqrtf((float)L.hd);
+  a.part_o = L.part_o;
+  a.part_ml = L.part_ml;
+  if (L.bf16) {
+    // waves: (split, KV head, 16-query group, request).  A request's visible
+    // sub-chunks are dealt out over its nsplits waves; nsplits is sized so
+    // that the launch holds about 8192 waves of capacity-sized work.
+    a.n_qgroups = (nq + 15) / 16;
+    a.n_cache_sub = (L.cap_rows + SUB - 1) / SUB;
+    const int n_sub = a.n_cache_sub + (L.mode == EAGLE3_TREE ? 2 : 0);
+    const long units = (long)n_sub * L.hkv * a.n_qgroups * L.B;
+    int spw = (int)((units + 8191) / 8192);
+    const int spw_min = (n_sub + 511) / 512;
+    spw = spw < spw_min ? spw_min : spw;
+    a.spw = spw;
+    a.nsplits = (n_sub + spw - 1) / spw;  // <= attn_num_chunks(cap_rows)
+    a.cpw = 0;
+    a.n_commit_splits = 0;
+    // paged: a wave's run spans at most 32*ceil(n_sub/nsplits)/block_size + 1 blocks
+    const int run = (n_sub + a.nsplits - 1) / a.nsplits;
+    const int kvm = !L.block_table ? 0 : ((SUB * run + L.block_size - 1) / L.block_size + 1 <= 64 ? 1 : 2);
+    dim3 grid((a.nsplits * L.hkv + 3) / 4, a.n_qgroups, L.B);
+#define E3_MFMA(HD)                                                                    \
+  do {                                                                                 \
+    if (kvm == 0) attn_mfma_kernel<HD, 0><<<grid, ATT_THREADS, 0, st>>>(a);            \
+    else if (kvm == 1) attn_mfma_kernel<HD, 1><<<grid, ATT_THREADS, 0, st>>>(a);       \
+    else attn_mfma_kernel<HD, 2><<<grid, ATT_THREADS, 0, st>>>(a);                     \
+  } while (0)
+    if (L.hd == 128) {
+      E3_MFMA(128);
+      attn_merge_kernel<bf16, 128><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, a.nsplits, L.hq, (bf16*)L.out);
+    } else {
+      E3_MFMA(64);
+      attn_merge_kernel<bf16, 64><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, a.nsplits, L.hq, (bf16*)L.out);
+    }
+#undef E3_MFMA
+    return hipGetLastError();
+  }
+  // fp32 caches (head_dim 64, validated by the caller): vector-ALU kernel
   const int qg = nq <= 8 ? 8 : 32;
   a.n_qgroups = (nq + qg - 1) / qg;
   // chunks per workgroup: one while the (chunk, head group, request) tasks
@@ -383,25 +713,14 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
   cpw = cpw < 1 ? 1 : (cpw > 8 ? 8 : cpw);
   a.cpw = cpw;
   a.n_commit_splits = (nchunks + cpw - 1) / cpw;
-  a.scale = 1.0f / sqrtf((float)L.hd);
-  a.part_o = L.part_o;
-  a.part_ml = L.part_ml;
+  a.n_cache_sub = 0;
+  a.spw = 0;
   const int nsplits = a.n_commit_splits + 1;  // <= attn_num_chunks(cap_rows): the workspace bound
+  a.nsplits = nsplits;
   dim3 grid(nsplits, L.hkv * a.n_qgroups, L.B);
-  const int rtot = L.B * L.rows;
 #define E3_ATTN(T, HD, QGV) attn_partial_kernel<T, HD, QGV><<<grid, ATT_THREADS, 0, st>>>(a)
-  if (L.bf16) {
-    if (L.hd == 128) {
-      if (qg == 8) E3_ATTN(bf16, 128, 8); else E3_ATTN(bf16, 128, 32);
-      attn_merge_kernel<bf16, 128><<<rtot * L.hq, 64, 0, st>>>(L.part_o, L.part_ml, nsplits, L.hq, (bf16*)L.out);
-    } else {
-      if (qg == 8) E3_ATTN(bf16, 64, 8); else E3_ATTN(bf16, 64, 32);
-      attn_merge_kernel<bf16, 64><<<rtot * L.hq, 64, 0, st>>>(L.part_o, L.part_ml, nsplits, L.hq, (bf16*)L.out);
-    }
-  } else {  // fp32 drafters: head_dim 64 (validated by the caller)
-    if (qg == 8) E3_ATTN(float, 64, 8); else E3_ATTN(float, 64, 32);
-    attn_merge_kernel<float, 64><<<rtot * L.hq, 64, 0, st>>>(L.part_o, L.part_ml, nsplits, L.hq, (float*)L.out);
-  }
+  if (qg == 8) E3_ATTN(float, 64, 8); else E3_ATTN(float, 64, 32);
+  attn_merge_kernel<float, 64><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, nsplits, L.hq, (float*)L.out);
 #undef E3_ATTN
   return hipGetLastError();
 }
