@@ -21,6 +21,7 @@ struct Pool {
   int *tok, *parent, *depth, *flat, *rank, *slot;
   float* score;
   uint64_t* anc;
+  uint64_t* path;  // child ranks along the root path, base k, the depth-1 ancestor's rank first
 };
 
 static __host__ __device__ inline int pool_max(int k, int D) { return k + (D - 1) * k * k; }
@@ -29,7 +30,7 @@ static __host__ __device__ inline size_t state_bytes(int k, int D) {
   const size_t P = pool_max(k, D);
   size_t b = HDR_INTS * 4 + P * (6 * 4 + 4) ;
   b = (b + 7) & ~(size_t)7;
-  b += P * 8;
+  b += P * 16;  // anc, path
   return (b + 255) & ~(size_t)255;
 }
 
@@ -50,6 +51,7 @@ __device__ inline Pool pool_of(void* state, int b, int k, int D) {
   size_t off = HDR_INTS * 4 + (size_t)P * 28;
   off = (off + 7) & ~(size_t)7;
   p.anc = (uint64_t*)(base + off);
+  p.path = p.anc + P;
   return p;
 }
 
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     P.slot[i] = -1;
     P.score[i] = lp[b * k + i];
     P.anc[i] = 0ull;
+    P.path[i] = (uint64_t)i;
     P.hdr[4 + i] = i;
   }
   if (threadIdx.x == 0) {
@@ -147,6 +150,7 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
         P.slot[n] = -1;
         P.score[n] = sc;
         P.anc[n] = 0ull;
+        P.path[n] = P.path[par] * (uint64_t)k + (uint64_t)i;
         cs[q] = sc;
         cf[q] = c;
       }
@@ -191,76 +195,75 @@ __device__ __forceinline__ unsigned long long rerank_key(float score, int depth,
   return ((unsigned long long)(~u) << 32) | ((unsigned long long)depth << 16) | (unsigned)flat;
 }
 
-constexpr int FIN_PER_LANE = (MAX_POOL + 63) / 64;  // 17
+constexpr int FIN_THREADS = 256;
+constexpr int FIN_SORT_MAX = 2048;  // power of two >= MAX_POOL
 
-__global__ __launch_bounds__(64) void tree_final_kernel(int k, int D, int m, void* state, int32_t* v_tok,
-                                                        int32_t* v_parent, int32_t* v_depth, int32_t* v_pos,
-                                                        uint64_t* v_anc) {
+// Rerank and layout.  The whole pool's rerank keys (unique: (depth, flat)
+// names a node) are sorted ascending with a bitonic network in LDS and the
+// first m are kept.  The kept set holds every kept node's parent (a child's
+// score is its parent's plus a log-probability <= 0, and ties prefer the
+// shallower node), so the canonical verify order -- depth by depth, by
+// (parent's verify index, child rank) -- is the order of (depth, path key):
+// a node's path key lists the child ranks along its root path, most
+// significant first, and the parents' verify order is their own path order.
+// Wave 0 ranks the kept nodes by that key, then builds the ancestor bitsets
+// depth by depth.
+__global__ __launch_bounds__(FIN_THREADS) void tree_final_kernel(int k, int D, int m, void* state, int32_t* v_tok,
+                                                                 int32_t* v_parent, int32_t* v_depth, int32_t* v_pos,
+                                                                 uint64_t* v_anc) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   Pool P = pool_of(state, b, k, D);
+  __shared__ unsigned long long sk[FIN_SORT_MAX];
+  __shared__ unsigned long long ck[EAGLE3_MAX_TREE_SLOTS];
   __shared__ short vidx_of[MAX_POOL];  // verify index of each kept pool node
   __shared__ uint64_t anc_s[EAGLE3_MAX_TREE_SLOTS];
   const int n = P.hdr[3];
   const int root_pos = P.hdr[2];
   const int M1 = m + 1;
-  // 1. top-m of the pool: lane-strided keys in registers, m rounds of wave argmin
-  unsigned long long key[FIN_PER_LANE];
-#pragma unroll
-  for (int j = 0; j < FIN_PER_LANE; ++j) {
-    const int i = lane + 64 * j;
-    key[j] = i < n ? rerank_key(P.score[i], P.depth[i], P.flat[i]) : ~0ull;
-  }
-  int my_node = -1;  // lane e holds the e-th kept node (rerank order)
-  for (int r = 0; r < m; ++r) {
-    unsigned long long best = ~0ull;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < FIN_PER_LANE; ++j)
-      if (key[j] < best) {
-        best = key[j];
-        bj = j;
-      }
-    unsigned long long wbest = best;
-    int wnode = lane + 64 * bj;
-    wave_argmin_u64(wbest, wnode);
-    if (lane == r) my_node = wnode;
-    const bool mine = (wnode & 63) == lane;
-    const int wj = wnode >> 6;
-#pragma unroll
-    for (int j = 0; j < FIN_PER_LANE; ++j)
-      if (mine && j == wj) key[j] = ~0ull;
-  }
-  // 2. canonical order, depth by depth: (parent's verify index, child rank)
-  int my_dep = 0, my_par = -1, my_rank = 0;
-  if (my_node >= 0) {
-    my_dep = P.depth[my_node];
-    my_par = P.parent[my_node];
-    my_rank = P.rank[my_node];
-  }
-  int base = 1;
-  int my_vidx = -1, my_pv = 0;
-  for (int dep = 1; dep <= D; ++dep) {
-    if (my_node >= 0 && my_dep == dep) my_pv = my_par < 0 ? 0 : vidx_of[my_par];
-    int pos = 0, cnt = 0;
-    for (int e = 0; e < m; ++e) {
-      const int de = __builtin_amdgcn_readlane(my_dep, e);
-      if (de != dep) continue;
-      const int pve = __builtin_amdgcn_readlane(my_pv, e);
-      const int re = __builtin_amdgcn_readlane(my_rank, e);
-      ++cnt;
-      pos += (pve < my_pv) || (pve == my_pv && re < my_rank);
-    }
-    if (my_node >= 0 && my_dep == dep) {
-      my_vidx = base + pos;
-      vidx_of[my_node] = (short)my_vidx;
-    }
-    base += cnt;
-    __syncthreads();
-  }
-  // 3. ancestor bitsets (parents first), then emit
-  if (lane == 0) anc_s[0] = 1ull;
+  const int mk = min(m, n);  // nodes kept
+  int N = 64;
+  while (N < n) N <<= 1;
+  // 1. sort the pool's rerank keys (padding ~0 sorts last)
+  for (int i = tid; i < N; i += FIN_THREADS) sk[i] = i < n ? rerank_key(P.score[i], P.depth[i], P.flat[i]) : ~0ull;
   __syncthreads();
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < (N >> 1); t += FIN_THREADS) {
+        const int i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1)), j = i | stride;
+        const unsigned long long x = sk[i], y = sk[j];
+        if ((x > y) == ((i & size) == 0)) {
+          sk[i] = y;
+          sk[j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // 2. lane e < mk of wave 0: the e-th kept node and its canonical key
+  int my_node = -1, my_dep = 0, my_par = -1;
+  unsigned long long my_ck = ~0ull;
+  if (tid < 64 && lane < mk) {
+    const unsigned long long key = sk[lane];
+    my_dep = (int)((key >> 16) & 0xffff);
+    const int flat = (int)(key & 0xffff);
+    my_node = my_dep == 1 ? flat : k + (my_dep - 2) * k * k + flat;
+    my_par = P.parent[my_node];
+    my_ck = ((unsigned long long)my_dep << 58) | P.path[my_node];
+    ck[lane] = my_ck;
+  }
+  __syncthreads();
+  int my_vidx = -1;
+  if (my_node >= 0) {
+    int r = 0;
+    for (int e = 0; e < mk; ++e) r += ck[e] < my_ck ? 1 : 0;
+    my_vidx = 1 + r;
+    vidx_of[my_node] = (short)my_vidx;
+  }
+  if (tid == 0) anc_s[0] = 1ull;
+  __syncthreads();
+  const int my_pv = my_node >= 0 ? (my_par < 0 ? 0 : vidx_of[my_par]) : 0;
+  // 3. ancestor bitsets, parents first
   for (int dep = 1; dep <= D; ++dep) {
     if (my_node >= 0 && my_dep == dep) anc_s[my_vidx] = anc_s[my_pv] | (1ull << my_vidx);
     __syncthreads();
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(64) void tree_final_kernel(int k, int D, int m, voi
     v_pos[b * M1 + my_vidx] = root_pos + my_dep;
     v_anc[b * M1 + my_vidx] = anc_s[my_vidx];
   }
-  if (lane == 0) {
+  if (tid == 0) {
     v_tok[b * M1] = P.hdr[1];
     v_parent[b * M1] = -1;
     v_depth[b * M1] = 0;
@@ -294,7 +297,7 @@ hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32
     tree_step_kernel<<<B, TREE_THREADS, 0, st>>>(k, D, state, topk_id, topk_lp, next_tok,
                                                  next_parent_slot, next_pos, next_anc);
   else
-    tree_final_kernel<<<B, 64, 0, st>>>(k, D, m, state, v_tok, v_parent, v_depth, v_pos, v_anc);
+    tree_final_kernel<<<B, FIN_THREADS, 0, st>>>(k, D, m, state, v_tok, v_parent, v_depth, v_pos, v_anc);
   return hipGetLastError();
 }
 
