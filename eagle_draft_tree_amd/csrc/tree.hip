@@ -14,10 +14,24 @@
 namespace e3 {
 
 constexpr int TREE_THREADS = 256;
-constexpr int HDR_INTS = 64;  // round, root_tok, root_pos, npool, frontier[16], ...
+
+// Per-request header: the round, the root, the pool size and the current
+// frontier with everything the next step needs from it (its nodes' scores,
+// tree slots, ancestor bits and path keys), so a step reads one header
+// instead of chasing pool entries.
+struct Hdr {
+  int round, root_tok, root_pos, npool;
+  int front[EAGLE3_MAX_TOPK];
+  float fscore[EAGLE3_MAX_TOPK];
+  int fslot[EAGLE3_MAX_TOPK];
+  int pad[EAGLE3_MAX_TOPK % 2 + 2];
+  uint64_t fanc[EAGLE3_MAX_TOPK];
+  uint64_t fpath[EAGLE3_MAX_TOPK];
+};
+constexpr int HDR_BYTES = ((int)sizeof(Hdr) + 255) & ~255;
 
 struct Pool {
-  int* hdr;
+  Hdr* hdr;
   int *tok, *parent, *depth, *flat, *rank, *slot;
   float* score;
   uint64_t* anc;
@@ -28,7 +42,7 @@ static __host__ __device__ inline int pool_max(int k, int D) { return k + (D - 1
 
 static __host__ __device__ inline size_t state_bytes(int k, int D) {
   const size_t P = pool_max(k, D);
-  size_t b = HDR_INTS * 4 + P * (6 * 4 + 4) ;
+  size_t b = HDR_BYTES + P * (6 * 4 + 4);
   b = (b + 7) & ~(size_t)7;
   b += P * 16;  // anc, path
   return (b + 255) & ~(size_t)255;
@@ -40,15 +54,15 @@ __device__ inline Pool pool_of(void* state, int b, int k, int D) {
   unsigned char* base = (unsigned char*)state + (size_t)b * state_bytes(k, D);
   const int P = pool_max(k, D);
   Pool p;
-  p.hdr = (int*)base;
-  p.tok = p.hdr + HDR_INTS;
+  p.hdr = (Hdr*)base;
+  p.tok = (int*)(base + HDR_BYTES);
   p.parent = p.tok + P;
   p.depth = p.parent + P;
   p.flat = p.depth + P;
   p.rank = p.flat + P;
   p.slot = p.rank + P;
   p.score = (float*)(p.slot + P);
-  size_t off = HDR_INTS * 4 + (size_t)P * 28;
+  size_t off = HDR_BYTES + (size_t)P * 28;
   off = (off + 7) & ~(size_t)7;
   p.anc = (uint64_t*)(base + off);
   p.path = p.anc + P;
@@ -64,22 +78,29 @@ __device__ __forceinline__ bool pool_better(float sa, int da, int fa, float sb, 
   return sa > sb || (sa == sb && (da < db || (da == db && fa < fb)));
 }
 
-// Give the frontier nodes of depth j their tree slots (j-1)k + rank and emit
-// the rows of the next draft step.
-__device__ void emit_frontier(Pool& P, const int* front, int b, int k, int j, int root_pos,
+// Give the frontier nodes of depth j their tree slots (j-1)k + rank, emit
+// the rows of the next draft step and record the frontier in the header.
+// front[rho] = pool node, fpar[rho] = its parent's frontier index in the
+// previous header (-1 for depth 1), with that header's slot/anc (pslot, panc).
+__device__ void emit_frontier(Pool& P, const int* front, const int* fpar, const float* fsc, const uint64_t* fpath,
+                              const int* pslot, const uint64_t* panc, int b, int k, int j, int root_pos,
                               int32_t* next_tok, int32_t* next_parent_slot, int32_t* next_pos,
                               uint64_t* next_anc) {
   for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {
     const int n = front[rho];
     const int s = (j - 1) * k + rho;
-    const int par = P.parent[n];
-    const uint64_t pa = par >= 0 ? P.anc[par] : 0ull;
-    P.slot[n] = s;
-    P.anc[n] = pa | (1ull << s);
+    const int pr = fpar[rho];
+    const uint64_t pa = pr >= 0 ? panc[pr] : 0ull;
+    const uint64_t a = pa | (1ull << s);
+    P.hdr->front[rho] = n;
+    P.hdr->fscore[rho] = fsc[rho];
+    P.hdr->fslot[rho] = s;
+    P.hdr->fanc[rho] = a;
+    P.hdr->fpath[rho] = fpath[rho];
     next_tok[b * k + rho] = P.tok[n];
-    next_parent_slot[b * k + rho] = par >= 0 ? 1 + P.slot[par] : 0;
+    next_parent_slot[b * k + rho] = pr >= 0 ? 1 + pslot[pr] : 0;
     next_pos[b * k + rho] = root_pos + j;
-    next_anc[b * k + rho] = pa | (1ull << s);
+    next_anc[b * k + rho] = a;
   }
 }
 
@@ -89,28 +110,42 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     int32_t* next_pos, uint64_t* next_anc) {
   const int b = blockIdx.x;
   Pool P = pool_of(state, b, k, D);
-  __shared__ int front[EAGLE3_MAX_TOPK];
+  __shared__ int front[EAGLE3_MAX_TOPK], fpar[EAGLE3_MAX_TOPK];
+  __shared__ float fsc[EAGLE3_MAX_TOPK];
+  __shared__ uint64_t fpath[EAGLE3_MAX_TOPK];
+  const int rp = root_pos[b];
   for (int i = threadIdx.x; i < k; i += blockDim.x) {
+    const int t = ids[b * k + i];
+    const float sc = lp[b * k + i];
     front[i] = i;
-    P.tok[i] = ids[b * k + i];
+    fpar[i] = -1;
+    fsc[i] = sc;
+    fpath[i] = (uint64_t)i;
+    P.tok[i] = t;
     P.parent[i] = -1;
     P.depth[i] = 1;
     P.flat[i] = i;
     P.rank[i] = i;
-    P.slot[i] = -1;
-    P.score[i] = lp[b * k + i];
-    P.anc[i] = 0ull;
+    P.score[i] = sc;
     P.path[i] = (uint64_t)i;
-    P.hdr[4 + i] = i;
   }
   if (threadIdx.x == 0) {
-    P.hdr[0] = 1;
-    P.hdr[1] = root_tok[b];
-    P.hdr[2] = root_pos[b];
-    P.hdr[3] = k;
+    P.hdr->round = 1;
+    P.hdr->root_tok = root_tok[b];
+    P.hdr->root_pos = rp;
+    P.hdr->npool = k;
   }
   __syncthreads();
-  if (D > 1) emit_frontier(P, front, b, k, 1, root_pos[b], next_tok, next_parent_slot, next_pos, next_anc);
+  if (D > 1) emit_frontier(P, front, fpar, fsc, fpath, nullptr, nullptr, b, k, 1, rp, next_tok, next_parent_slot,
+                           next_pos, next_anc);
+  else
+    for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {  // depth-1 tree: the header still lists the frontier
+      P.hdr->front[rho] = rho;
+      P.hdr->fscore[rho] = fsc[rho];
+      P.hdr->fslot[rho] = -1;
+      P.hdr->fanc[rho] = 0ull;
+      P.hdr->fpath[rho] = fpath[rho];
+    }
 }
 
 __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
@@ -118,13 +153,23 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     int32_t* next_parent_slot, int32_t* next_pos, uint64_t* next_anc) {
   const int b = blockIdx.x;
   Pool P = pool_of(state, b, k, D);
-  __shared__ int front[EAGLE3_MAX_TOPK];
-  __shared__ int newfront[EAGLE3_MAX_TOPK];
-  const int j = P.hdr[0] + 1;
+  __shared__ int front[EAGLE3_MAX_TOPK], pslot[EAGLE3_MAX_TOPK];
+  __shared__ float pscore[EAGLE3_MAX_TOPK];
+  __shared__ uint64_t panc[EAGLE3_MAX_TOPK], ppath[EAGLE3_MAX_TOPK];
+  __shared__ int newfront[EAGLE3_MAX_TOPK], newpar[EAGLE3_MAX_TOPK];
+  __shared__ float newsc[EAGLE3_MAX_TOPK];
+  __shared__ uint64_t newpath[EAGLE3_MAX_TOPK];
+  const int j = P.hdr->round + 1;
   if (j > D) return;  // the tree already has depth D
-  const int base = P.hdr[3];
-  const int root_pos = P.hdr[2];
-  for (int i = threadIdx.x; i < k; i += blockDim.x) front[i] = P.hdr[4 + i];
+  const int base = P.hdr->npool;
+  const int root_pos = P.hdr->root_pos;
+  for (int i = threadIdx.x; i < k; i += blockDim.x) {
+    front[i] = P.hdr->front[i];
+    pscore[i] = P.hdr->fscore[i];
+    pslot[i] = P.hdr->fslot[i];
+    panc[i] = P.hdr->fanc[i];
+    ppath[i] = P.hdr->fpath[i];
+  }
   __syncthreads();
   const int kk = k * k;
   // wave 0: lane l owns candidates c = l + 64*q (q < 4, kk <= 256)
@@ -132,27 +177,28 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     const int lane = threadIdx.x;
     float cs[4];
     int cf[4];
+    uint64_t cp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = lane + 64 * q;
       cs[q] = -INFINITY;
       cf[q] = INT_MAX;
+      cp[q] = 0ull;
       if (c < kk) {
         const int rho = c / k, i = c - rho * k;
-        const int par = front[rho];
-        const float sc = P.score[par] + lp[(size_t)(b * k + rho) * k + i];  // one fp32 add
+        const float sc = pscore[rho] + lp[(size_t)(b * k + rho) * k + i];  // one fp32 add
+        const uint64_t path = ppath[rho] * (uint64_t)k + (uint64_t)i;
         const int n = base + c;
         P.tok[n] = ids[(size_t)(b * k + rho) * k + i];
-        P.parent[n] = par;
+        P.parent[n] = front[rho];
         P.depth[n] = j;
         P.flat[n] = c;
         P.rank[n] = i;
-        P.slot[n] = -1;
         P.score[n] = sc;
-        P.anc[n] = 0ull;
-        P.path[n] = P.path[par] * (uint64_t)k + (uint64_t)i;
+        P.path[n] = path;
         cs[q] = sc;
         cf[q] = c;
+        cp[q] = path;
       }
     }
     // k rounds of wave argmax by (score desc, flat asc)
@@ -166,22 +212,35 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
           bf = cf[q];
         }
       wave_argmax(bs, bf);  // (score desc, flat asc) is the same order as (value desc, id asc)
-      if (lane == 0) newfront[r] = base + bf;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (cf[q] == bf) {
+          newfront[r] = base + bf;
+          newpar[r] = bf / k;
+          newsc[r] = bs;
+          newpath[r] = cp[q];
           cs[q] = -INFINITY;
           cf[q] = INT_MAX;
         }
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < k; i += blockDim.x) P.hdr[4 + i] = newfront[i];
   if (threadIdx.x == 0) {
-    P.hdr[0] = j;
-    P.hdr[3] = base + kk;
+    P.hdr->round = j;
+    P.hdr->npool = base + kk;
   }
-  if (j < D) emit_frontier(P, newfront, b, k, j, root_pos, next_tok, next_parent_slot, next_pos, next_anc);
+  if (j < D) {
+    emit_frontier(P, newfront, newpar, newsc, newpath, pslot, panc, b, k, j, root_pos, next_tok, next_parent_slot,
+                  next_pos, next_anc);
+  } else {
+    for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {  // last depth: no more rows to draft
+      P.hdr->front[rho] = newfront[rho];
+      P.hdr->fscore[rho] = newsc[rho];
+      P.hdr->fslot[rho] = -1;
+      P.hdr->fanc[rho] = 0ull;
+      P.hdr->fpath[rho] = newpath[rho];
+    }
+  }
 }
 
 constexpr int MAX_POOL = EAGLE3_MAX_TOPK + (EAGLE3_MAX_TREE_SLOTS)*EAGLE3_MAX_TOPK;
@@ -218,8 +277,8 @@ __global__ __launch_bounds__(FIN_THREADS) void tree_final_kernel(int k, int D, i
   __shared__ unsigned long long ck[EAGLE3_MAX_TREE_SLOTS];
   __shared__ short vidx_of[MAX_POOL];  // verify index of each kept pool node
   __shared__ uint64_t anc_s[EAGLE3_MAX_TREE_SLOTS];
-  const int n = P.hdr[3];
-  const int root_pos = P.hdr[2];
+  const int n = P.hdr->npool;
+  const int root_pos = P.hdr->root_pos;
   const int M1 = m + 1;
   const int mk = min(m, n);  // nodes kept
   int N = 64;
@@ -276,7 +335,7 @@ __global__ __launch_bounds__(FIN_THREADS) void tree_final_kernel(int k, int D, i
     v_anc[b * M1 + my_vidx] = anc_s[my_vidx];
   }
   if (tid == 0) {
-    v_tok[b * M1] = P.hdr[1];
+    v_tok[b * M1] = P.hdr->root_tok;
     v_parent[b * M1] = -1;
     v_depth[b * M1] = 0;
     v_pos[b * M1] = root_pos;
