@@ -18,6 +18,8 @@
 // ids are remapped so that consecutive logical tiles run on the same XCD
 // (hardware dispatch places block b on XCD b % 8) and share its L2.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm_rows.hpp"
 
@@ -74,6 +76,29 @@ __device__ __forceinline__ size_t frag_off(int r, int k, int nkc) {
 }
 
 // APACK: A in fragment order (frag_off) instead of row-major with stride lda.
+// Optional epilogue hook run before the k loop (e.g. loading per-row data
+// whose latency would otherwise sit in the epilogue): an epilogue that
+// defines `Pre` and `pre(rowbase, lane, M)` receives the value as its second
+// argument.
+template <class E, class = void>
+struct EpiHook {
+  struct T {};
+  static __device__ __forceinline__ T pre(const E&, int, int, int) { return T{}; }
+  static __device__ __forceinline__ void run(const E& e, const BGAcc& acc, const T&, int r, int c, int l, int M,
+                                             int n) {
+    e(acc, r, c, l, M, n);
+  }
+};
+template <class E>
+struct EpiHook<E, std::void_t<typename E::Pre>> {
+  using T = typename E::Pre;
+  static __device__ __forceinline__ T pre(const E& e, int r, int l, int M) { return e.pre(r, l, M); }
+  static __device__ __forceinline__ void run(const E& e, const BGAcc& acc, const T& p, int r, int c, int l, int M,
+                                             int n) {
+    e(acc, p, r, c, l, M, n);
+  }
+};
+
 template <bool PACKED, bool APACK, class Epi>
 __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __restrict__ A, int lda, int M,
                                                               const bf16* __restrict__ W, int N, int K, RowMap map,
@@ -101,6 +126,7 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < BG_NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const typename EpiHook<Epi>::T pre = EpiHook<Epi>::pre(epi, bm * BG_BM + wm * 128, lane, M);
 
   // Copy sources.  Per stage (32 k) wave w copies A fragments (m-tiles 2w,
   // 2w+1) and B fragments (n-tiles 2w, 2w+1); lane l of a fragment is row
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
     bg_barrier();
   }
   // lane l holds C[rowbase + 16 i + 4(l/16) + e][n of column tile colbase16 + j, slot l%16]
-  epi(acc, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
+  EpiHook<Epi>::run(epi, acc, pre, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
 }
 
 // Lane l receives lane l^8 of its 16-lane row (DPP row_ror:8).
@@ -195,6 +221,18 @@ __device__ __forceinline__ void row16_argmax(float& v, int& id) {
   E3_ROW_STEP(DPP_ROW_HALF_MIRROR)
   E3_ROW_STEP(DPP_ROW_MIRROR)
 #undef E3_ROW_STEP
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_i<DPP_QUAD_1032>(v));
+  v = min(v, dpp_i<DPP_QUAD_2301>(v));
+  v = min(v, dpp_i<DPP_ROW_HALF_MIRROR>(v));
+  return min(v, dpp_i<DPP_ROW_MIRROR>(v));
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<DPP_QUAD_1032>(v);

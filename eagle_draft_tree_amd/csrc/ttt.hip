@@ -266,22 +266,24 @@ struct TEpiQKV {
 // LM head with the cross entropy folded in: for every row and each
 // 256-column block (one workgroup tile) write {max, sum exp(x - max), argmax
 // id}; the lane that owns a row's target column writes the target logit.
-// Each wave reduces its 64 columns per row with DPP, then the four column
-// waves' results meet in LDS and are combined in wave order.
+// Each wave reduces its 64 columns per row (maximum, then the lowest column
+// holding it, then the sum of exponentials, each a 16-lane DPP reduction),
+// then the four column waves' results meet in LDS and are combined in wave
+// order.  The targets of the lane's 32 rows are loaded before the k loop.
 struct TEpiCE {
   float4* part;
   float* lab;
   const int32_t* tokens;  // [M], targets are tokens[row + step] inside the sequence
   int S, step, nblk;
-  __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
-                                             int nt16) const {
-    __shared__ float4 cs[BG_BM][4];  // [row in tile][column wave]
-    const int m = lane & 15, wave = threadIdx.x >> 6, wm = wave >> 2, wn = wave & 3;
-    // targets of this lane's 32 rows, loaded together (one division per lane;
-    // S >= 64, so a row offset of at most 115 wraps a sequence at most once)
+  struct Pre {
+    int tg[8][4];
+  };
+  __device__ __forceinline__ Pre pre(int rowbase, int lane, int M) const {
+    // one division per lane; S >= 64, so a row offset of at most 115 wraps a
+    // sequence at most once
+    Pre p;
     const int r0 = rowbase + 4 * (lane >> 4);
     const int p0 = r0 % S;
-    int tg[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -290,35 +292,43 @@ struct TEpiCE {
         int pos = p0 + 16 * i + e;
         if (pos >= S) pos -= S;
         if (pos >= S) pos -= S;
-        tg[i][e] = row < M && pos + step <= S - 1 ? tokens[row + step] : -1;
+        p.tg[i][e] = row < M && pos + step <= S - 1 ? tokens[row + step] : -1;
       }
+    return p;
+  }
+  __device__ __forceinline__ void operator()(const BGAcc& acc, const Pre& pr, int rowbase, int colbase16, int lane,
+                                             int M, int nt16) const {
+    __shared__ float4 cs[BG_BM][4];  // [row in tile][column wave]
+    const int m = lane & 15, wave = threadIdx.x >> 6, wm = wave >> 2, wn = wave & 3;
+    const int r0 = rowbase + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = r0 + 16 * i + e;
-        const int target = tg[i][e];
+        const int target = pr.tg[i][e];
         float mx = -INFINITY;
-        int id = 0x7fffffff;
 #pragma unroll
         for (int j = 0; j < BG_NJ; ++j) {
           const int col16 = colbase16 + j, n = col16 * 16 + m;
           if (col16 < nt16) {
             const float xv = acc[i][j][e];
-            if (xv > mx) {
-              mx = xv;
-              id = n;
-            }
+            mx = fmaxf(mx, xv);
             if (n == target) lab[row] = xv;
           }
         }
-        row16_argmax(mx, id);
+        mx = row16_max(mx);
+        int id = 0x7fffffff;
         float s = 0.f;
         if (mx > -INFINITY) {
+#pragma unroll
+          for (int j = BG_NJ - 1; j >= 0; --j)  // lowest column of this lane holding the maximum
+            if (colbase16 + j < nt16 && acc[i][j][e] == mx) id = (colbase16 + j) * 16 + m;
 #pragma unroll
           for (int j = 0; j < BG_NJ; ++j)
             if (colbase16 + j < nt16) s += __expf(acc[i][j][e] - mx);
         }
+        id = row16_min(id);
         s = row16_sum(s);
         if (m == 0) cs[wm * 128 + 16 * i + 4 * (lane >> 4) + e][wn] = make_float4(mx, s, __int_as_float(id), 0.f);
       }
