@@ -42,7 +42,7 @@ struct TLayout {
   bf16* z;       // [M][F] silu(gate) * up (fragment order)
   bf16* q;       // [M][hq][hd]
   bf16* k1;      // [M][hkv][hd] step-1 keys
-  bf16* v1t;     // [B][hkv][hd][S] step-1 values, transposed
+  bf16* v1t;     // step-1 values: [M][hkv][hd] (LDS attention kernel) or [B][hkv][hd][S] (transposed)
   bf16* kc;      // [R-1][M][hkv][hd] chain keys of steps 2..R
   bf16* vc;      // [R-1][M][hkv][hd] chain values
   float4* part;  // [M][nblk] LM-head partials per 256 columns {max, sum exp, argmax id, 0}
@@ -610,6 +610,230 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
   }
 }
 
+// Step-1 causal attention with the K/V blocks shared through LDS: workgroup
+// = (sequence b, KV head g, block of QB query rows) with all G query heads of
+// the group, eight waves (head g*G + w%G, 32 rows of the block each).  Keys
+// come in blocks of 64; the block's K and V rows ([M][Hkv][hd] row-major)
+// are copied once into LDS by direct global -> LDS copies (two stages, the
+// next block in flight while this one is computed) and read by every wave:
+// K fragments with ds_read_b128, V^T fragments with the transpose read
+// ds_read_b64_tr_b16.  16-byte chunk c of key row r sits at slot
+// c ^ (r % chunks-per-row), so the 16 rows of a fragment read distinct
+// banks.  The per-wave arithmetic (MFMA operands, the online softmax, the P
+// hi/lo split, the chain keys) is that of ttt_attn_kernel, in the same order.
+constexpr int TA_WAVES = 8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* tta_lds_s16x4;
+
+template <int HD, int G>
+__global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K1, const bf16* __restrict__ V1,
+    const bf16* __restrict__ KC, const bf16* __restrict__ VC, int nchain, size_t chain_stride,
+    bf16* __restrict__ out, int S, int hq, int hkv, float scale) {
+  constexpr int NC = HD / 32, NT = HD / 16, CPR = HD / 8;  // 16-byte chunks per row
+  constexpr int RG = TA_WAVES / G, QB = 32 * RG, KB = 64;
+  constexpr int BLK = KB * CPR;                    // 16-byte chunks per K (or V) block
+  constexpr int NDMA = 2 * BLK / 64 / TA_WAVES;    // copies per wave per stage
+  static_assert(NDMA * 64 * TA_WAVES == 2 * BLK, "copies split evenly over the waves");
+  __shared__ uint4 sm[2][2][BLK];  // [stage][K, V][row * CPR + slot]
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = w % G, rg = w / G;
+  const int nqb = (S + QB - 1) / QB;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // longest rows first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int h = g * G + hl;
+  const int i0 = qb * QB + 32 * rg;  // the wave's first row
+  const bool active = i0 < S;
+  const int nkb = (min(qb * QB + QB, S) + KB - 1) / KB;
+  const int ml = lane & 15, q4 = lane >> 4;
+  const size_t kstride = (size_t)hkv * HD;
+
+  const uint32_t lds0 = lds_addr(&sm[0][0][0]);
+  auto issue = [&](int kb) {
+    const uint32_t st_base = lds0 + (uint32_t)((kb & 1) * 2 * BLK * 16);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) {
+      const int d = w * NDMA + u;               // copy index within the stage
+      const int kv = d / (BLK / 64), part = d - kv * (BLK / 64);
+      const int e = part * 64 + lane;           // chunk index within the block
+      const int r = e / CPR, slot = e - r * CPR;
+      const int key = min(kb * KB + r, S - 1);  // rows past S are masked by causality
+      const bf16* src = (kv ? V1 : K1) + ((size_t)b * S + key) * kstride + (size_t)g * HD + 8 * (slot ^ (r % CPR));
+      dma16(src, st_base + (uint32_t)(kv * BLK * 16 + part * 1024));
+    }
+  };
+
+  U4 qf[2][NC];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int i = min(i0 + 16 * nt + ml, S - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[nt][c].u = *(const uint4*)(Q + ((size_t)(b * S + i) * hq + h) * HD + 32 * c + 8 * q4);
+  }
+  f32x4 o[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+
+  issue(0);
+  bg_wait_copies<0>();
+  bg_barrier();
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) issue(kb + 1);
+    if (active && kb * KB <= i0 + 31) {
+      const uint4* ks = &sm[kb & 1][0][0];
+      const bf16* vs = (const bf16*)&sm[kb & 1][1][0];
+      f32x4 st[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) st[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        U4 kf[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int r = 16 * mt + ml, ch = 4 * c + q4;
+          kf[mt].u = ks[r * CPR + (ch ^ (r % CPR))];
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt].v, qf[nt][c].v, st[mt][nt], 0, 0, 0);
+      }
+      const bool diag = kb * KB + 63 > i0;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int qi = i0 + 16 * nt + ml;
+        float bm = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sv = st[mt][nt][e] * scale;
+            if (diag && kb * KB + 16 * mt + 4 * q4 + e > qi) sv = -INFINITY;
+            st[mt][nt][e] = sv;
+            bm = fmaxf(bm, sv);
+          }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mnew = fmaxf(mrun[nt], bm);
+        const float alpha = __expf(mrun[nt] - mnew);
+        mrun[nt] = mnew;
+        lsum[nt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t][nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __expf(st[mt][nt][e] - mnew);
+            st[mt][nt][e] = pv;
+            lsum[nt] += pv;
+          }
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        // B operand P^T: k-slots 8 q4 + e <- key 32kc + 4 q4 + e, slots 8 q4 + 4 + e <- key 32kc + 16 + 4 q4 + e
+        U4 phi[2], plo[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const float p0 = st[2 * kc + hh][nt][2 * e2], p1 = st[2 * kc + hh][nt][2 * e2 + 1];
+              const bf16 h0 = f2bf(p0), h1 = f2bf(p1);
+              const bf16 l0 = f2bf(p0 - bf2f(h0)), l1 = f2bf(p1 - bf2f(h1));
+              hw[2 * hh + e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+              lw[2 * hh + e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+          }
+          phi[nt].u = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          plo[nt].u = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          // V^T fragment: dim 16t + ml, keys 32kc + 4q4 + j and 32kc + 16 + 4q4 + j (j < 4): source lane
+          // s = ml of this lane group points at key 32kc + 4q4 + s/4, dims 16t + 4(s%4) .. +4
+          const int r0 = 32 * kc + 4 * q4 + (ml >> 2), r1 = r0 + 16;
+          const int dim = 16 * t + 4 * (ml & 3), ch = dim >> 3, off = dim & 7;
+          const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (tta_lds_s16x4)(vs + (r0 * CPR + (ch ^ (r0 % CPR))) * 8 + off));
+          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (tta_lds_s16x4)(vs + (r1 * CPR + (ch ^ (r1 % CPR))) * 8 + off));
+          U4 vf;
+          __builtin_memcpy(&vf.u.x, &va, 8);
+          __builtin_memcpy(&vf.u.z, &vb, 8);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, phi[nt].v, o[t][nt], 0, 0, 0);
+            o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, plo[nt].v, o[t][nt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    bg_wait_copies<0>();
+    bg_barrier();
+  }
+  if (!active) return;
+  // chain keys (j', i), j' = 2..j: lane holds dims 16t + 4 q4 + e of its query
+  for (int c = 0; c < nchain; ++c) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const size_t row = (size_t)b * S + i0 + 16 * nt + ml;
+      const bf16* qp = Q + (row * hq + h) * HD + 4 * q4;
+      const bf16* kp = KC + c * chain_stride + (row * hkv + g) * HD + 4 * q4;
+      const bf16* vp = VC + c * chain_stride + (row * hkv + g) * HD + 4 * q4;
+      float dot = 0.f;
+      float vv[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint2 qa = *(const uint2*)(qp + 16 * t), ka = *(const uint2*)(kp + 16 * t), va = *(const uint2*)(vp + 16 * t);
+        const uint32_t qw[2] = {qa.x, qa.y}, kw[2] = {ka.x, ka.y}, vw[2] = {va.x, va.y};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          dot = fmaf(__uint_as_float(qw[u] << 16), __uint_as_float(kw[u] << 16), dot);
+          dot = fmaf(__uint_as_float(qw[u] & 0xffff0000u), __uint_as_float(kw[u] & 0xffff0000u), dot);
+          vv[t][2 * u] = __uint_as_float(vw[u] << 16);
+          vv[t][2 * u + 1] = __uint_as_float(vw[u] & 0xffff0000u);
+        }
+      }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float sv = dot * scale;
+      const float mnew = fmaxf(mrun[nt], sv);
+      const float alpha = __expf(mrun[nt] - mnew), pv = __expf(sv - mnew);
+      mrun[nt] = mnew;
+      lsum[nt] = lsum[nt] * alpha + (q4 == 0 ? pv : 0.f);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t][nt][e] = fmaf(pv, vv[t][e], o[t][nt][e] * alpha);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float L = lsum[nt];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const float inv = 1.f / L;
+    const int row = b * S + i0 + 16 * nt + ml;
+    const int nkc = (hq * HD) >> 5;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 r = o[t][nt] * inv;
+      *(uint2*)(out + frag_off(row, h * HD + 16 * t + 4 * q4, nkc)) =
+          make_uint2((uint32_t)f2bf(r[0]) | ((uint32_t)f2bf(r[1]) << 16), (uint32_t)f2bf(r[2]) | ((uint32_t)f2bf(r[3]) << 16));
+    }
+  }
+}
+
 // apack: A in fragment order (every A operand the TTT kernels produce); the
 // fusion GEMM reads the caller's row-major features.
 template <class Epi>
@@ -663,17 +887,38 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     }
     bf16* kdst = j == 1 ? L.k1 : L.kc + (size_t)(j - 2) * M * kvd;
     bf16* vdst = j == 1 ? L.v1t : L.vc + (size_t)(j - 2) * M * kvd;
+    const int gq = hq / hkv;
+    const bool lds_attn = 8 % gq == 0;  // step-1 values stay row-major for the LDS kernel
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      TEpiQKV epi{L.q, kdst, vdst, j == 1, L.rope, hq, hkv, hd, S, j - 1};
+      TEpiQKV epi{L.q, kdst, vdst, j == 1 && !lds_attn, L.rope, hq, hkv, hd, S, j - 1};
       E3_CHECK(bg_launch(L.x, 2 * d, true, M, w.qkv, pk, qd + 2 * kvd, 2 * d, pair_head, epi, st));
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_ATTN, st);
-      const int gq = hq / hkv, wpb = gq % 4 == 0 ? 4 : (gq % 2 == 0 ? 2 : 1);
+      const float scale = (float)(1.0 / sqrt((double)hd));
+      if (lds_attn) {
+        const int qbr = 32 * (TA_WAVES / gq);
+        const dim3 grid((S + qbr - 1) / qbr, hkv, B);
+#define E3_TTA(HDV, GV) \
+  ttt_attn_lds_kernel<HDV, GV><<<grid, TA_WAVES * 64, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S, hq, hkv, scale)
+        if (hd == 128) {
+          if (gq == 1) E3_TTA(128, 1);
+          else if (gq == 2) E3_TTA(128, 2);
+          else if (gq == 4) E3_TTA(128, 4);
+          else E3_TTA(128, 8);
+        } else {
+          if (gq == 1) E3_TTA(64, 1);
+          else if (gq == 2) E3_TTA(64, 2);
+          else if (gq == 4) E3_TTA(64, 4);
+          else E3_TTA(64, 8);
+        }
+#undef E3_TTA
+        E3_CHECK(hipGetLastError());
+      } else {
+      const int wpb = gq % 4 == 0 ? 4 : (gq % 2 == 0 ? 2 : 1);
       const dim3 grid(S / 32, hq / wpb, B);
       const int threads = 64 * wpb;
-      const float scale = (float)(1.0 / sqrt((double)hd));
       if (hd == 128)
         ttt_attn_kernel<128><<<grid, threads, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S,
                                                        hq, hkv, scale);
@@ -681,6 +926,7 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
         ttt_attn_kernel<64><<<grid, threads, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S,
                                                       hq, hkv, scale);
       E3_CHECK(hipGetLastError());
+      }
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);

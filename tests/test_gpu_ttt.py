@@ -77,6 +77,8 @@ CASES = [
     ("hd64-gqa2-self", dict(d=256, hq=4, hkv=2, hd=64, ffn=768, vocab=4112), 2, 192, 3, False, True),
     ("hd128-gqa4-self", dict(d=512, hq=4, hkv=1, hd=128, ffn=512, vocab=2048), 1, 128, 4, False, True),
     ("r1", dict(d=256, hq=2, hkv=2, hd=64, ffn=512, vocab=1040), 1, 64, 1, False, True),
+    # query-head groups of 3 take the attention kernel without LDS staging
+    ("hd64-gqa3-self", dict(d=384, hq=6, hkv=2, hd=64, ffn=512, vocab=2064), 1, 128, 2, False, True),
 ]
 
 
