@@ -360,15 +360,13 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 a, s16x4 b) {
 }
 // 8 floats -> bf16 hi (round to nearest even) and lo = bf16(x - hi)
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
-  uint16_t h[8], l[8];
+  u32x4 uh, ul;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    h[t] = f2bf(x[t]);
-    l[t] = f2bf(x[t] - bf2f(h[t]));
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t h2 = f2bf2(x[2 * t], x[2 * t + 1]);
+    uh[t] = h2;
+    ul[t] = f2bf2(x[2 * t] - __uint_as_float(h2 << 16), x[2 * t + 1] - __uint_as_float(h2 & 0xffff0000u));
   }
-  uint4 uh, ul;
-  __builtin_memcpy(&uh, h, 16);
-  __builtin_memcpy(&ul, l, 16);
   hi = __builtin_bit_cast(bf16x8, uh);
   lo = __builtin_bit_cast(bf16x8, ul);
 }

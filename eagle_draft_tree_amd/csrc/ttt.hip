@@ -748,10 +748,9 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
 #pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
               const float p0 = st[2 * kc + hh][nt][2 * e2], p1 = st[2 * kc + hh][nt][2 * e2 + 1];
-              const bf16 h0 = f2bf(p0), h1 = f2bf(p1);
-              const bf16 l0 = f2bf(p0 - bf2f(h0)), l1 = f2bf(p1 - bf2f(h1));
-              hw[2 * hh + e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-              lw[2 * hh + e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+              const uint32_t hh2 = f2bf2(p0, p1);
+              hw[2 * hh + e2] = hh2;
+              lw[2 * hh + e2] = f2bf2(p0 - __uint_as_float(hh2 << 16), p1 - __uint_as_float(hh2 & 0xffff0000u));
             }
           }
           phi[nt].u = make_uint4(hw[0], hw[1], hw[2], hw[3]);
