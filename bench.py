@@ -196,7 +196,19 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
     bytes_cycle = w_fc + D * (w_layer + w_lm + kv_round)
     # LM head launches: COMMIT (top-k of the last row of each request) then D-1 tree rounds (k rows each)
     rows = [Bn] + [Bn * k] * (D - 1)
-    lm_bytes = [w_lm + r * d * es + r * V * 4 for r in rows]
+
+    def lm_out_bytes(r):
+        # top-1 on 17..64 rows without kept logits: the LM head writes per-workgroup
+        # (max, sum exp, argmax) partials (16 B per row per 128 or 64 vocabulary rows)
+        # instead of fp32 logits
+        if k == 1 and 16 < r <= 64:
+            nwg = -(-(V // 16) // 8)
+            if nwg < 192:
+                nwg = -(-(V // 16) // 4)
+            return r * nwg * 16
+        return r * V * 4
+
+    lm_bytes = [w_lm + r * d * es + lm_out_bytes(r) for r in rows]
     lm_flops = [2.0 * r * V * d for r in rows]
     lm_ms, lm_cnt = per_class["lm_head"]
     reps = lm_cnt // len(rows) if lm_cnt else 0

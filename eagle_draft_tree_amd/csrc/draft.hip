@@ -243,6 +243,60 @@ __global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
+// LM head with top-1 folded in (skinny GEMM, no split-K, logits not kept):
+// per X row and workgroup (its NB*16 vocabulary columns) write {max,
+// sum exp(x - max), lowest column holding the max}.  Thread t takes row t%64
+// and column quarter t/64 (a wave reads one LDS column slice of all rows:
+// conflict-free); the quarters meet in LDS and are combined in order.
+struct EpiTop1Part {
+  static constexpr bool kWhole = true;
+  float4* part;  // [R][nwg]
+  int nwg;
+  __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float* scratch) const {
+    float4* red = (float4*)scratch;  // [4][64]
+    const int t = threadIdx.x, r = t & 63, q = t >> 6;
+    const int qw = NB * 4;  // columns per quarter
+    float mx = -INFINITY;
+    int id = 0x7fffffff;
+    float s = 0.f;
+    if (r < R) {
+      for (int c = q * qw; c < (q + 1) * qw; ++c)
+        if (wg * NB + (c >> 4) < ntiles16) {
+          const float v = tile[c * RP + r];
+          if (v > mx) {
+            mx = v;
+            id = (wg * NB) * 16 + c;
+          }
+        }
+      if (mx > -INFINITY)
+        for (int c = q * qw; c < (q + 1) * qw; ++c)
+          if (wg * NB + (c >> 4) < ntiles16) s += __expf(tile[c * RP + r] - mx);
+    }
+    red[q * 64 + r] = make_float4(mx, s, __int_as_float(id), 0.f);
+    __syncthreads();
+    if (q == 0 && r < R) {
+      float gm = -INFINITY;
+      int gi = 0x7fffffff;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 c = red[u * 64 + r];
+        if (better(c.x, __float_as_int(c.z), gm, gi)) {
+          gm = c.x;
+          gi = __float_as_int(c.z);
+        }
+      }
+      float gs = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 c = red[u * 64 + r];
+        if (c.x > -INFINITY) gs += c.y * __expf(c.x - gm);
+      }
+      part[(size_t)r * nwg + wg] = make_float4(gm, gs, __int_as_float(gi), 0.f);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // rows-GEMM dispatch.  The epilogue sees rows 0..R-1 of one launch; row
 // chunks beyond 64 are launched separately with shifted pointers (no split).
 template <typename TW, int T, int NT, int U, int WAVES, class Epi>
@@ -337,6 +391,7 @@ struct DraftWS {
   void* y;
   float* logits;
   void* topk;
+  float4* lmpart;  // top-1 partials of the fused LM head, [R][V/64]
 };
 
 static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* base, DraftWS* w) {
@@ -360,6 +415,7 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   t.y = bp.take((size_t)R * dm.d * es);
   t.logits = (float*)bp.take((size_t)R * dm.vocab * 4);
   t.topk = bp.take(topk_ws_bytes(R, dm.vocab));
+  t.lmpart = (float4*)bp.take((size_t)R * ((dm.vocab / 16 + 3) / 4) * sizeof(float4));
   if (w) *w = t;
   return bp.off + 256;
 }
@@ -561,6 +617,24 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   }
   // ---- LM head + top-k
   float* logits = c.logits_out ? c.logits_out : ws.logits;
+  // top-1 without kept logits on the skinny GEMM: the LM head writes per-
+  // workgroup (max, sum exp, argmax) partials instead of the logits
+  if (c.k == 1 && !c.logits_out && bf && Rl <= 64 && sk_ok(Rl, d, pk)) {
+    const int nt16 = V / 16;
+    const int bn = sk_bn(nt16, 1);
+    const int nwg = (nt16 + bn / 16 - 1) / (bn / 16);
+    {
+      TimedScope ts(EAGLE3_KC_LMHEAD, st);
+      EpiTop1Part epi{ws.lmpart, nwg};
+      const bf16* Xb = (const bf16*)ws.y;
+      const bf16* Wb = (const bf16*)w.lm;
+      if (bn == 128) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+      else skinny_gemm_kernel<64, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    TimedScope ts(EAGLE3_KC_TOPK, st);
+    return launch_top1_merge(ws.lmpart, Rl, nwg, c.topk_id, c.topk_lp, st);
+  }
   {
     TimedScope ts(EAGLE3_KC_LMHEAD, st);
     for (int r0 = 0; r0 < Rl; r0 += 64) {

@@ -30,6 +30,8 @@ size_t topk_ws_bytes(int rows, int V);
 unsigned* topk_counters(void* ws, int rows, int V);
 hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse, void* ws,
                        bool counters_zeroed, hipStream_t st);
+// top-1 and log-probability from per-workgroup (max, sum exp, argmax) partials [rows][nparts]
+hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* ids, float* lp, hipStream_t st);
 
 // ---- dynamic tree (tree.hip)
 size_t tree_state_bytes_per_req(int k, int D);

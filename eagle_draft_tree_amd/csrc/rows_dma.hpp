@@ -12,12 +12,26 @@
 // epilogue interface is the rows GEMM's ([16][RP] fp32 tiles of weight rows
 // x X rows, RP = 65 with one float of padding).
 #pragma once
+#include <type_traits>
+
 #include "bigemm.hpp"
 #include "gemm_rows.hpp"
 
 namespace e3 {
 
 constexpr int SK_NSTAGE = 6;
+
+// An epilogue that defines kWhole = true receives the workgroup's whole tile
+// (whole(wg, tile, RP, R, NB, ntiles16, scratch)) instead of one call per
+// 16-row weight tile.  Used without split-K only.
+template <class E, class = void>
+struct EpiWhole {
+  static constexpr bool value = false;
+};
+template <class E>
+struct EpiWhole<E, std::void_t<decltype(E::kWhole)>> {
+  static constexpr bool value = E::kWhole;
+};
 
 static inline bool sk_ok(int R, int K, bool packed) { return packed && R > 16 && R <= 64 && K % 32 == 0; }
 // weight rows per workgroup: 128 (measured best on the 8B shapes) unless that
@@ -38,7 +52,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const bf16* __restrict
   constexpr int STAGE_U4 = NF * 64;
   constexpr int RP = 65;  // padded tile rows (conflict-free column reads in the epilogue)
   __shared__ uint4 smem[SK_NSTAGE * STAGE_U4];
-  static_assert(NB * 16 * RP * 4 <= SK_NSTAGE * STAGE_U4 * 16, "epilogue tile fits");
+  static_assert(NB * 16 * RP * 4 + 4096 <= SK_NSTAGE * STAGE_U4 * 16, "epilogue tile and 4 KB scratch fit");
   float* tile = (float*)smem;  // after the k loop: [NB*16][RP]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,9 +121,15 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const bf16* __restrict
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[((wave * WT + j) * 16 + m) * RP + c * 16 + q4 * 4 + e] = acc[c][j][e];
   __syncthreads();
-  for (int t = 0; t < NB; ++t) {
-    const int t16 = wgt * NB + t;
-    if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split);
+  if constexpr (EpiWhole<Epi>::value) {
+    // whole-workgroup epilogue: all NB*16 weight rows at once, with the LDS
+    // past the tile as scratch
+    epi.whole(wgt, tile, RP, R, NB, ntiles16, tile + NB * 16 * RP);
+  } else {
+    for (int t = 0; t < NB; ++t) {
+      const int t16 = wgt * NB + t;
+      if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split);
+    }
   }
 }
 

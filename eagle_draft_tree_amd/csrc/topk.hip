@@ -331,6 +331,59 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
   }
 }
 
+// Top-1 from (max, sum exp(x - max), argmax) partials: one workgroup per
+// row; the maximum and its lowest id by (value desc, id asc), then the LSE
+// with each thread's partials added in index order and the threads' sums in
+// a fixed order.
+__global__ __launch_bounds__(256) void top1_merge_kernel(const float4* __restrict__ part, int nparts,
+                                                         int32_t* __restrict__ ids, float* __restrict__ lp) {
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float4* p = part + (size_t)row * nparts;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int i = tid; i < nparts; i += 256) {
+    const float4 c = p[i];
+    if (better(c.x, __float_as_int(c.z), bv, bi)) {
+      bv = c.x;
+      bi = __float_as_int(c.z);
+    }
+  }
+  wave_argmax(bv, bi);
+  if (lane == 0) {
+    wv[w] = bv;
+    wi[w] = bi;
+  }
+  __syncthreads();
+  float M = wv[0];
+  int id = wi[0];
+  for (int u = 1; u < 4; ++u)
+    if (better(wv[u], wi[u], M, id)) {
+      M = wv[u];
+      id = wi[u];
+    }
+  float s = 0.f;
+  for (int i = tid; i < nparts; i += 256) {
+    const float4 c = p[i];
+    if (c.x > -INFINITY) s += c.y * expf(c.x - M);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  if (tid == 0) {
+    const float L = M + logf((red[0] + red[1]) + (red[2] + red[3]));
+    ids[row] = id;
+    lp[row] = M - L;
+  }
+}
+
+hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* ids, float* lp, hipStream_t st) {
+  top1_merge_kernel<<<rows, 256, 0, st>>>(part, nparts, ids, lp);
+  return hipGetLastError();
+}
+
 __global__ void topk_zero_kernel(unsigned* done, int rows) {
   for (int i = threadIdx.x; i < rows; i += blockDim.x) done[i] = 0u;
 }

@@ -275,3 +275,33 @@ def test_bf16_small_paged_cycle(lib, bs):
     gc = GpuCycle(w, Wt, ci, pack=True)
     gc.run()
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
+
+
+def test_top1_lm_head_without_logits_matches_logits_path(lib):
+    """Top-1 drafting (k = 1) with more than 16 rows per step and no kept
+    logits: the LM head reduces its columns to per-workgroup (max, sum exp,
+    argmax) partials instead of writing logits.  The top-1 ids equal the
+    kept-logits path bit for bit (same GEMM arithmetic) and are the argmax of
+    those logits (lowest id on ties); log-probabilities agree to fp32
+    rounding; the tree is identical."""
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=4112, dtype=BF16, theta=500000.0)
+    w = scaled(C3_8B_CHAIN, shape=shape, batch=20, depth=3, topk=1, keep=2, prefix=90, prefix_range=(10, 90),
+               block_size=16, feat_scale=1.0)
+    say("top-1 LM head without logits, batch", w.batch)
+    Wt = gen.gen_weights(shape, seed=7)
+    ci = gen.gen_cycle_inputs(w, seed=8)
+    a = GpuCycle(w, Wt, ci, keep_logits=True, pack=True)
+    a.run()
+    b = GpuCycle(w, Wt, ci, keep_logits=False, pack=True)
+    b.run()
+    pairs = [(a.buf.root_ids, b.buf.root_ids, a.buf.root_lp, b.buf.root_lp, a.buf.commit_logits)]
+    pairs += [(a.buf.round_ids[r], b.buf.round_ids[r], a.buf.round_lp[r], b.buf.round_lp[r], a.buf.round_logits[r])
+              for r in range(len(a.buf.round_ids))]
+    for ia, ib, la, lb, lg in pairs:
+        ia, ib = ia.cpu().numpy(), ib.cpu().numpy()
+        np.testing.assert_array_equal(ia, ib)
+        np.testing.assert_allclose(lb.cpu().numpy(), la.cpu().numpy(), atol=1e-5, rtol=1e-6)
+        np.testing.assert_array_equal(ia[..., 0], np.argmax(lg.cpu().numpy(), axis=-1))
+    ta, tb = a.tree(), b.tree()
+    for n in ta:
+        np.testing.assert_array_equal(ta[n], tb[n], err_msg=n)
