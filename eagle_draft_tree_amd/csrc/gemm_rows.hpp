@@ -71,6 +71,13 @@ static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_spli
   if (smax < 1) smax = 1;
   int s = (1024 + p.tiles - 1) / p.tiles;
   if (s > smax) s = smax;
+  // more than 16 rows: eight splits, halved while a split would hold fewer
+  // than 16 k-steps of 32 (measured best on the 8B batch-64 QKV, O, down and
+  // fusion shapes; odd counts leave uneven k ranges)
+  if (p.nt >= 2) {
+    s = 8;
+    while (s > 1 && K / 32 / s < 16) s >>= 1;
+  }
   if (s < 1 || !allow_split || R > 64) s = 1;
   p.splits = s;
   return p;

@@ -34,9 +34,11 @@ struct EpiWhole<E, std::void_t<decltype(E::kWhole)>> {
 };
 
 static inline bool sk_ok(int R, int K, bool packed) { return packed && R > 16 && R <= 64 && K % 32 == 0; }
-// weight rows per workgroup: 128 (measured best on the 8B shapes) unless that
-// leaves fewer than 192 workgroups
+// weight rows per workgroup: 64 for split-K matrices up to 6144 rows (QKV and
+// O of the 8B drafter), else 128 unless that leaves fewer than 192
+// workgroups (measured on the 8B batch-64 shapes)
 static inline int sk_bn(int ntiles16, int splits) {
+  if (splits > 1 && ntiles16 <= 384) return 64;
   return (long)((ntiles16 + 7) / 8) * splits >= 192 ? 128 : 64;
 }
 
