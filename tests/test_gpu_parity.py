@@ -263,6 +263,22 @@ def test_bf16_small_cycle(lib, hkv, commit, ctx, pack):
     assert exc <= 1
 
 
+@pytest.mark.parametrize("commit,ctx", [(24, 70), (1, 300)])
+def test_bf16_small_cycle_hd128(lib, commit, ctx):
+    """Head dim 128 (the 8B/70B drafters' head size) at a size the oracle runs
+    whole: 4 query heads on one KV head, a 24-row commit (6 groups of 16 query
+    vectors) or a long prefix with one root row; packed weights."""
+    say("bf16 small cycle hd128", commit, ctx)
+    shape = tiny_shape(d=512, hq=4, hkv=1, hd=128, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
+    w = scaled(C1_TINY, shape=shape, depth=4, topk=3, keep=12, prefix=ctx, commit_rows=commit,
+               synthetic_prefix_kv=True, feat_scale=1.0)
+    Wt, W, ci = cycle_and_oracle(w, seed=9)
+    gc = GpuCycle(w, Wt, ci, pack=True)
+    gc.run()
+    exc = compare_cycle(gc, w, W, ci, TOL_BF16)
+    assert exc <= 1
+
+
 @pytest.mark.parametrize("bs", [4, 16])
 def test_bf16_small_paged_cycle(lib, bs):
     """Paged KV (block tables, per-request prefix lengths) on a small bf16
