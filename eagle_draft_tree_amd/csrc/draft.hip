@@ -260,17 +260,40 @@ struct EpiTop1Part {
     int id = 0x7fffffff;
     float s = 0.f;
     if (r < R) {
-      for (int c = q * qw; c < (q + 1) * qw; ++c)
-        if (wg * NB + (c >> 4) < ntiles16) {
-          const float v = tile[c * RP + r];
+      // columns past the vocabulary exist only in the last workgroup
+      const int c0 = q * qw, c1 = min((q + 1) * qw, (ntiles16 - wg * NB) * 16);
+      const float* col = tile + r;
+      if (c1 - c0 == qw && (qw & 7) == 0) {
+        for (int c = c0; c < c1; c += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = col[(c + u) * RP];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (v[u] > mx) {
+              mx = v[u];
+              id = (wg * NB) * 16 + c + u;
+            }
+        }
+        if (mx > -INFINITY)
+          for (int c = c0; c < c1; c += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = col[(c + u) * RP];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += __expf(v[u] - mx);
+          }
+      } else {
+        for (int c = c0; c < c1; ++c) {
+          const float v = col[c * RP];
           if (v > mx) {
             mx = v;
             id = (wg * NB) * 16 + c;
           }
         }
-      if (mx > -INFINITY)
-        for (int c = q * qw; c < (q + 1) * qw; ++c)
-          if (wg * NB + (c >> 4) < ntiles16) s += __expf(tile[c * RP + r] - mx);
+        if (mx > -INFINITY)
+          for (int c = c0; c < c1; ++c) s += __expf(col[c * RP] - mx);
+      }
     }
     red[q * 64 + r] = make_float4(mx, s, __int_as_float(id), 0.f);
     __syncthreads();
