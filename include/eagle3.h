@@ -38,6 +38,7 @@
  *    one stream; concurrent calls on one buffer race.
  *  - Workspaces must be zero-filled once after allocation: their first
  *    bytes hold split-K arrival counters that every call leaves at zero.
+ *    (Top-k arrival counters further in are cleared by each call itself.)
  */
 #ifndef EAGLE3_H
 #define EAGLE3_H
@@ -202,7 +203,10 @@ int eagle3_fuse(const eagle3_dims *dims, const eagle3_weights *w, const void *fe
  *   [B][1][k].  Order: logit desc, token id asc; lp = logit - logsumexp in
  *   float32.
  * logits_out: optional (NULL) float32 [B][rows or 1][vocab] copy of the
- *   logits of the rows whose top-k is taken.
+ *   logits of the rows whose top-k is taken.  With k = 1, bf16 weights,
+ *   logits_out = NULL and at most 64 such rows, the logits are never stored:
+ *   the LM head keeps per-block {max, sum of exp, lowest argmax} and merges
+ *   them; ids are identical and lp agrees to float32 summation order.
  * Requires rows <= 64, head_dim in {64,128}; paged KV requires bf16. */
 int eagle3_draft_step(const eagle3_dims *dims, const eagle3_weights *w, const eagle3_kv *kv,
                       int mode, int B, int rows, const void *state, const int32_t *parent_slot,
