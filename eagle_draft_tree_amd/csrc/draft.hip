@@ -353,7 +353,9 @@ static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int
   }
   if (sizeof(TW) == 2) {
     switch (p.nt) {
-      case 1: return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+      case 1:
+        if (p.t == 1) return rows_gemm_launch<TW, 1, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+        return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
       case 2: return rows_gemm_launch<TW, 4, 2, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
       case 3: return rows_gemm_launch<TW, 4, 3, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
       default: return rows_gemm_launch<TW, 4, 4, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);

@@ -65,12 +65,20 @@ static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_spli
   p.t = p.nt == 1 ? 2 : 4;
   p.u = p.nt == 1 ? 4 : 2;
   p.waves = p.nt == 1 ? 8 : 4;
+  // up to 16 rows: one 16-row tile per workgroup when two would leave fewer
+  // than 192 workgroups (8B O, down and fusion: 256 workgroups)
+  if (p.nt == 1 && N / 32 < 192) p.t = 1;
   p.tiles = (N / 16 + p.t - 1) / p.t;
   const int ngroups = K / (32 * p.u);
   int smax = ngroups / p.waves;
   if (smax < 1) smax = 1;
   int s = (1024 + p.tiles - 1) / p.tiles;
   if (s > smax) s = smax;
+  // up to 16 rows, at most one workgroup per CU: no split.  The tile streams
+  // as fast whole as split (measured on the 8B QKV, O, down and fusion and
+  // the 70B O, down and fusion shapes), and the fused epilogue replaces a
+  // partial-sum pass.  More tiles than CUs (70B QKV, 320) keep the split.
+  if (p.nt == 1 && p.tiles <= 256) s = 1;
   // more than 16 rows: eight splits, halved while a split would hold fewer
   // than 16 k-steps of 32 (measured best on the 8B batch-64 QKV, O, down and
   // fusion shapes; odd counts leave uneven k ranges)
