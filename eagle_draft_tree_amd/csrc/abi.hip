@@ -261,7 +261,7 @@ int eagle3_topk(const float* logits, int rows, int V, int k, int32_t* ids, float
   REQUIRE(k <= EAGLE3_MAX_TOPK, EAGLE3_ECAPACITY, "k=%d > %d", k, EAGLE3_MAX_TOPK);
   const size_t need = e3::topk_ws_bytes(rows, V);
   REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(e3::launch_topk(logits, rows, V, k, ids, lp, lse, ws, false, (hipStream_t)stream), "eagle3_topk");
+  return hip_status(e3::launch_topk(logits, rows, V, k, ids, lp, lse, ws, (hipStream_t)stream), "eagle3_topk");
 }
 
 int eagle3_ttt_forward(const eagle3_dims* dims, const eagle3_weights* w, const void* feats,

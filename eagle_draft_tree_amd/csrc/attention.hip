@@ -34,10 +34,10 @@ struct AttnArgs {
   const uint64_t* anc;  // [Rtot] (TREE) or NULL
   int cap, max_blocks, block_size;
   int B, rows, hq, hkv, mode, n_commit_splits, cpw, n_qgroups;
-  int n_cache_sub, spw, nsplits;  // attn_mfma_kernel: cache sub-chunks, sub-chunks per wave, partial slots
+  int n_cache_sub, spw, nsplits;  // attn_mfma_kernel: cache sub-chunks, sub-chunks per wave, wave splits
   float scale;
-  float* part_o;   // [Rtot*Hq][nsplits][hd]
-  float* part_ml;  // [Rtot*Hq][nsplits][2]
+  float* part_o;   // [Rtot*Hq][partials][hd]: partials = nsplits, or ceil(nsplits/4) merged
+  float* part_ml;  // [Rtot*Hq][partials][2]
 };
 
 // 16-byte vector of T elements, unpacked to float.
@@ -313,14 +313,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
 // Matrix-core decode attention for bf16 caches.
 //
 // Work unit: one wave = (request b, KV head g, group of 16 query vectors,
-// wave split w < nsplits); consecutive waves are the KV heads of one split.  A request's key space is its committed cache rows
-// in 32-key sub-chunks followed, in TREE mode, by the 64 tree slots as two
-// more sub-chunks; the sub-chunks holding visible keys are dealt out in equal
-// contiguous runs over the nsplits waves of (b, g, group), so short prefixes
-// do not leave a few waves with all of the work.  Each wave keeps an online
-// softmax over its run and writes one partial per query vector (an empty run
-// writes an empty partial); attn_merge_kernel combines them.  The four waves
-// of a workgroup are independent units: no workgroup barrier.
+// wave split w < nsplits).  A request's key space is its committed cache
+// rows in 32-key sub-chunks followed, in TREE mode, by the 64 tree slots as
+// two more sub-chunks; the sub-chunks holding visible keys are dealt out in
+// equal contiguous runs over the nsplits waves of (b, g, group), so short
+// prefixes do not leave a few waves with all of the work.  Each wave keeps an
+// online softmax over its run.  A workgroup's four waves are four
+// consecutive splits of one (b, g, group), and consecutive workgroups are
+// the KV heads of one split group; after the key loop the four waves'
+// (m, l, o) are merged in LDS in wave order and the workgroup writes one
+// partial per query vector (an empty run counts as m = -inf); the
+// attn_merge_kernel combines the split groups' partials.
 //
 // Per sub-chunk, with the 16x16x32 bf16 MFMA:
 //   S^T[key][query] = K Q^T: the K fragment (16 keys x 32 head dims) is read
@@ -373,26 +376,42 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
 
 // KVM: cache addressing, 0 = contiguous, 1 = paged with the wave's block
 // entries staged in lanes (at most 64), 2 = paged with a table load per key.
-template <int HD, int KVM>
+// MERGE: a workgroup's four waves are four splits merged before the store.
+template <int HD, int KVM, bool MERGE>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = HD / 32;             // k-steps of S
   constexpr int HT = HD / 16;             // head-dim tiles of O^T
   constexpr int VROW = HD + 16;           // padded V tile row (elements)
   constexpr int VLD = SUB * HD / 8 / 64;  // 16-byte V loads per lane per sub-chunk
   __shared__ __attribute__((aligned(16))) bf16 vtile[4][SUB * VROW];
+  __shared__ float mred[4][16], lred[4][16];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
   const int c16 = lane & 15, g16 = lane >> 4;
-  // wave -> (split, KV head) with the head fastest: the waves reading the
-  // same cache rows (all heads of a position range) run side by side
-  const int wid = blockIdx.x * 4 + w;
-  const int wsplit = wid / a.hkv, g = wid - wsplit * a.hkv;
+  // MERGE: workgroup -> (split group, KV head) with the head fastest (the
+  // workgroups reading the same cache rows run side by side); its four waves
+  // take the group's four consecutive splits and merge them before the
+  // store.  Otherwise wave -> (split, KV head) with the head fastest, and
+  // every wave stores its own partial.
+  constexpr bool merge4 = MERGE;
+  const int nsg = (a.nsplits + 3) >> 2;
+  int wsplit, g;
+  if constexpr (merge4) {
+    const int sgi = blockIdx.x / a.hkv;
+    g = blockIdx.x - sgi * a.hkv;
+    wsplit = sgi * 4 + w;  // past the last split: an empty key range
+  } else {
+    const int wid = blockIdx.x * 4 + w;
+    wsplit = wid / a.hkv;
+    g = wid - wsplit * a.hkv;
+  }
   const int qgrp = blockIdx.y;
   const int b = blockIdx.z;
   const int G = a.hq / a.hkv;
   const int nq_total = a.rows * G;
   const int q0 = qgrp * 16;
-  if (q0 >= nq_total || wsplit >= a.nsplits) return;
+  if (q0 >= nq_total) return;                   // uniform over the workgroup
+  if (!merge4 && wsplit >= a.nsplits) return;  // no workgroup barrier without MERGE
   const int ctx = a.ctx_len[b];
   const bool tree = a.mode == EAGLE3_TREE;
   const int maxvis = tree ? ctx : ctx + a.rows;  // cache rows visible to some query
@@ -555,18 +574,78 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       o[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, plo, o[ht], 0, 0, 0);
     }
   }
-  // partial of the lane's query vector: (m, l) and o (unnormalised, relative to m)
+  // the wave's split: (m, l) per query and o (unnormalised, relative to m)
   const float l = xor_sum16_32(l_run);
-  if (qrow < 0) return;
-  const int h = g * G + (qi - qrow * G);
-  const size_t oi = ((size_t)(b * a.rows + qrow) * a.hq + h) * a.nsplits + wsplit;
-  if (g16 == 0) {
-    a.part_ml[2 * oi] = m_run;
-    a.part_ml[2 * oi + 1] = l;
-  }
-  float* dst = a.part_o + oi * HD + 4 * g16;
+  if constexpr (!merge4) {
+    if (qrow < 0) return;
+    const int h = g * G + (qi - qrow * G);
+    const size_t oi = ((size_t)(b * a.rows + qrow) * a.hq + h) * a.nsplits + wsplit;
+    if (g16 == 0) {
+      a.part_ml[2 * oi] = m_run;
+      a.part_ml[2 * oi + 1] = l;
+    }
+    float* dst = a.part_o + oi * HD + 4 * g16;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) *(float4*)(dst + ht * 16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
+    for (int ht = 0; ht < HT; ++ht) *(float4*)(dst + ht * 16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
+    return;
+  }
+  // MERGE: into the wave's own V-tile space as [query][HD + 4] floats
+  constexpr int OROW = HD + 4;  // padded: the 16 queries' float4 stores hit distinct banks
+  static_assert(16 * OROW * 4 <= SUB * VROW * 2, "merge rows fit the V tile");
+  const int sgi = wsplit >> 2;
+  asm volatile("" ::: "memory");  // the last V-tile reads stay before the stores below
+  float* ow = (float*)vt;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+    *(float4*)(ow + c16 * OROW + ht * 16 + 4 * g16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
+  if (g16 == 0) {
+    mred[w][c16] = m_run;
+    lred[w][c16] = l;
+  }
+  __syncthreads();
+  // merge the four splits in wave order: thread t takes query t/16 and dims
+  // DPT*(t%16) ..; the merged partial is the split group's
+  constexpr int DPT = HD / 16;
+  const int qc = threadIdx.x >> 4, j = threadIdx.x & 15;
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    mw[u] = mred[u][qc];
+    M = fmaxf(M, mw[u]);
+  }
+  float wt[4], L = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    wt[u] = mw[u] == -INFINITY ? 0.f : expf(mw[u] - M);
+    L += lred[u][qc] * wt[u];
+  }
+  float acc[DPT];
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) acc[d] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float* src = (const float*)vtile[u] + qc * OROW + DPT * j;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4) {
+      const float4 v = *(const float4*)(src + d);
+      acc[d] = fmaf(v.x, wt[u], acc[d]);
+      acc[d + 1] = fmaf(v.y, wt[u], acc[d + 1]);
+      acc[d + 2] = fmaf(v.z, wt[u], acc[d + 2]);
+      acc[d + 3] = fmaf(v.w, wt[u], acc[d + 3]);
+    }
+  }
+  const int qim = q0 + qc;
+  if (qim >= nq_total) return;
+  const int qrm = qim / G;
+  const int h = g * G + (qim - qrm * G);
+  const size_t oi = ((size_t)(b * a.rows + qrm) * a.hq + h) * nsg + sgi;
+  if (j == 0) {
+    a.part_ml[2 * oi] = M;
+    a.part_ml[2 * oi + 1] = L;
+  }
+  float* dst = a.part_o + oi * HD + DPT * j;
+#pragma unroll
+  for (int d = 0; d < DPT; d += 4) *(float4*)(dst + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
 }
 
 // out[row][h*hd + i] = merged attention output, rounded to T.  One
@@ -666,9 +745,10 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
   a.part_o = L.part_o;
   a.part_ml = L.part_ml;
   if (L.bf16) {
-    // waves: (split, KV head, 16-query group, request).  A request's visible
-    // sub-chunks are dealt out over its nsplits waves; nsplits is sized so
-    // that the launch holds about 8192 waves of capacity-sized work.
+    // workgroups: (split group of 4 waves, KV head, 16-query group, request).
+    // A request's visible sub-chunks are dealt out over its nsplits waves;
+    // nsplits is sized so that the launch holds about 8192 waves of
+    // capacity-sized work.
     a.n_qgroups = (nq + 15) / 16;
     a.n_cache_sub = (L.cap_rows + SUB - 1) / SUB;
     const int n_sub = a.n_cache_sub + (L.mode == EAGLE3_TREE ? 2 : 0);
@@ -683,21 +763,32 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     // paged: a wave's run spans at most 32*ceil(n_sub/nsplits)/block_size + 1 blocks
     const int run = (n_sub + a.nsplits - 1) / a.nsplits;
     const int kvm = !L.block_table ? 0 : ((SUB * run + L.block_size - 1) / L.block_size + 1 <= 64 ? 1 : 2);
-    dim3 grid((a.nsplits * L.hkv + 3) / 4, a.n_qgroups, L.B);
-#define E3_MFMA(HD)                                                                    \
+    // many splits (short runs, batch-1 shapes): a workgroup merges its four
+    // waves' splits, so four times fewer partials are written and merged
+    const bool merge4 = a.nsplits >= 32;
+    const int nsg = (a.nsplits + 3) / 4;
+    const int nparts = merge4 ? nsg : a.nsplits;
+    dim3 grid(merge4 ? nsg * L.hkv : (a.nsplits * L.hkv + 3) / 4, a.n_qgroups, L.B);
+#define E3_MFMA_K(HD, M)                                                               \
   do {                                                                                 \
-    if (kvm == 0) attn_mfma_kernel<HD, 0><<<grid, ATT_THREADS, 0, st>>>(a);            \
-    else if (kvm == 1) attn_mfma_kernel<HD, 1><<<grid, ATT_THREADS, 0, st>>>(a);       \
-    else attn_mfma_kernel<HD, 2><<<grid, ATT_THREADS, 0, st>>>(a);                     \
+    if (kvm == 0) attn_mfma_kernel<HD, 0, M><<<grid, ATT_THREADS, 0, st>>>(a);         \
+    else if (kvm == 1) attn_mfma_kernel<HD, 1, M><<<grid, ATT_THREADS, 0, st>>>(a);    \
+    else attn_mfma_kernel<HD, 2, M><<<grid, ATT_THREADS, 0, st>>>(a);                  \
+  } while (0)
+#define E3_MFMA(HD)              \
+  do {                           \
+    if (merge4) E3_MFMA_K(HD, true); \
+    else E3_MFMA_K(HD, false);   \
   } while (0)
     if (L.hd == 128) {
       E3_MFMA(128);
-      attn_merge_kernel<bf16, 128><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, a.nsplits, L.hq, (bf16*)L.out);
+      attn_merge_kernel<bf16, 128><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, nparts, L.hq, (bf16*)L.out);
     } else {
       E3_MFMA(64);
-      attn_merge_kernel<bf16, 64><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, a.nsplits, L.hq, (bf16*)L.out);
+      attn_merge_kernel<bf16, 64><<<rtot * L.hq, 256, 0, st>>>(L.part_o, L.part_ml, nparts, L.hq, (bf16*)L.out);
     }
 #undef E3_MFMA
+#undef E3_MFMA_K
     return hipGetLastError();
   }
   // fp32 caches (head_dim 64, validated by the caller): vector-ALU kernel

@@ -205,42 +205,6 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
 // Lane l receives lane l^8 of its 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float xor8(float v) { return dpp_f<0x128>(v); }
 
-// Reductions over the 16 lanes of a DPP row (the 16 columns of one C row).
-__device__ __forceinline__ void row16_argmax(float& v, int& id) {
-#define E3_ROW_STEP(CTRL)              \
-  {                                    \
-    const float ov = dpp_f<CTRL>(v);   \
-    const int oi = dpp_i<CTRL>(id);    \
-    if (better(ov, oi, v, id)) {       \
-      v = ov;                          \
-      id = oi;                         \
-    }                                  \
-  }
-  E3_ROW_STEP(DPP_QUAD_1032)
-  E3_ROW_STEP(DPP_QUAD_2301)
-  E3_ROW_STEP(DPP_ROW_HALF_MIRROR)
-  E3_ROW_STEP(DPP_ROW_MIRROR)
-#undef E3_ROW_STEP
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
-  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
-  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
-}
-__device__ __forceinline__ int row16_min(int v) {
-  v = min(v, dpp_i<DPP_QUAD_1032>(v));
-  v = min(v, dpp_i<DPP_QUAD_2301>(v));
-  v = min(v, dpp_i<DPP_ROW_HALF_MIRROR>(v));
-  return min(v, dpp_i<DPP_ROW_MIRROR>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<DPP_QUAD_1032>(v);
-  v += dpp_f<DPP_QUAD_2301>(v);
-  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
-  return v + dpp_f<DPP_ROW_MIRROR>(v);
-}
-
 // --------------------------------------------------------------------------- epilogues
 // C (plain map) -> float buffer, rounded to bf16 values when `round` is set.
 struct BEpiStoreF {

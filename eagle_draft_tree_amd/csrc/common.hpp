@@ -119,6 +119,43 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16q..16q+15);
+// every lane of the row gets the same, bit-identical result.
+__device__ __forceinline__ void row16_argmax(float& v, int& id) {
+#define E3_ROW_STEP(CTRL)              \
+  {                                    \
+    const float ov = dpp_f<CTRL>(v);   \
+    const int oi = dpp_i<CTRL>(id);    \
+    if (better(ov, oi, v, id)) {       \
+      v = ov;                          \
+      id = oi;                         \
+    }                                  \
+  }
+  E3_ROW_STEP(DPP_QUAD_1032)
+  E3_ROW_STEP(DPP_QUAD_2301)
+  E3_ROW_STEP(DPP_ROW_HALF_MIRROR)
+  E3_ROW_STEP(DPP_ROW_MIRROR)
+#undef E3_ROW_STEP
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_i<DPP_QUAD_1032>(v));
+  v = min(v, dpp_i<DPP_QUAD_2301>(v));
+  v = min(v, dpp_i<DPP_ROW_HALF_MIRROR>(v));
+  return min(v, dpp_i<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  return v + dpp_f<DPP_ROW_MIRROR>(v);
+}
+
 // Wave argmax of (value, id) under `better`; uniform result.
 __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 #define E3_ARG_STEP(CTRL)                              \

@@ -55,10 +55,9 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
     const T* __restrict__ emb, const int32_t* __restrict__ tokens, const T* __restrict__ state,
     const float* __restrict__ h_tree, const int32_t* __restrict__ parent_slot, int mode, int rows,
     int d, const float* __restrict__ ge, const float* __restrict__ gs, float eps,
-    float* __restrict__ S, T* __restrict__ x, unsigned* __restrict__ topk_ctr, int n_ctr) {
+    float* __restrict__ S, T* __restrict__ x) {
   __shared__ float red[RT / 64];
   const int r = blockIdx.x;
-  if (threadIdx.x == 0 && r < n_ctr) topk_ctr[r] = 0u;  // the step's top-k arrival counters
   const int b = r / rows;
   const T* e = emb + (size_t)tokens[r] * d;
   const float* hs = nullptr;
@@ -415,8 +414,8 @@ struct DraftWS {
   float* h2;
   void* y;
   float* logits;
-  void* topk;
-  float4* lmpart;  // top-1 partials of the fused LM head, [R][V/64]
+  void* topk;  // not used by the draft step: keeps eagle3_topk covered for R rows
+  void* lmpart;  // LM-head partials: top-1 float4 [R][V/64], or tile float2 [R][V/16]
 };
 
 static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* base, DraftWS* w) {
@@ -440,7 +439,8 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   t.y = bp.take((size_t)R * dm.d * es);
   t.logits = (float*)bp.take((size_t)R * dm.vocab * 4);
   t.topk = bp.take(topk_ws_bytes(R, dm.vocab));
-  t.lmpart = (float4*)bp.take((size_t)R * ((dm.vocab / 16 + 3) / 4) * sizeof(float4));
+  // top-1 float4 [R][V/64] or tile pairs float2 [R][V/16 + up to 63 slots of padding]
+  t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 64) * sizeof(float2));
   if (w) *w = t;
   return bp.off + 256;
 }
@@ -510,8 +510,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
     prologue_kernel<T><<<R, RT, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree, c.parent_slot,
-                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x,
-                                         topk_counters(ws.topk, Rl, V), Rl);
+                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
@@ -650,7 +649,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     const int nwg = (nt16 + bn / 16 - 1) / (bn / 16);
     {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
-      EpiTop1Part epi{ws.lmpart, nwg};
+      EpiTop1Part epi{(float4*)ws.lmpart, nwg};
       const bf16* Xb = (const bf16*)ws.y;
       const bf16* Wb = (const bf16*)w.lm;
       if (bn == 128) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
@@ -658,7 +657,24 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     TimedScope ts(EAGLE3_KC_TOPK, st);
-    return launch_top1_merge(ws.lmpart, Rl, nwg, c.topk_id, c.topk_lp, st);
+    return launch_top1_merge((const float4*)ws.lmpart, Rl, nwg, c.topk_id, c.topk_lp, st);
+  }
+  // up to 64 rows: the LM head writes the logits and each 16-column tile's
+  // {max, sum exp} per row; the top-k reads the pairs and only the logits of
+  // the tiles that can hold one of the k best
+  if (Rl <= 64) {
+    const int nt16 = V / 16;
+    const RowsPlan pc = plan_rows(Rl, V, d, bf, false);
+    const int tpw = bf && sk_ok(Rl, d, pk) ? sk_bn(nt16, 1) / 16 : pc.t;  // tiles per workgroup, as dispatched
+    float2* tpart = (float2*)ws.lmpart;
+    {
+      TimedScope ts(EAGLE3_KC_LMHEAD, st);
+      EpiLogitsTiles epi{logits, V, tpart, tile_slots(nt16, tpw)};
+      if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) != hipSuccess)
+        return e;
+    }
+    TimedScope ts(EAGLE3_KC_TOPK, st);
+    return launch_topk_tiles(logits, tpart, tpw, Rl, V, c.k, c.topk_id, c.topk_lp, st);
   }
   {
     TimedScope ts(EAGLE3_KC_LMHEAD, st);
@@ -672,7 +688,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     }
   }
   TimedScope ts(EAGLE3_KC_TOPK, st);
-  return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, true, st);
+  return launch_topk(logits, Rl, V, c.k, c.topk_id, c.topk_lp, nullptr, ws.topk, st);
 }
 
 hipError_t draft_step(const DraftCall& c, hipStream_t st) {

@@ -15,6 +15,8 @@
 // RoPE partners (i, i+hd/2) of one head, or the gate/up rows of one FFN
 // column.  The epilogue then sees both halves in the same workgroup.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace e3 {
@@ -45,8 +47,8 @@ union U4 {
 // ---------------------------------------------------------------------------
 // Plan: tiles per workgroup (T), MFMAs per k-group (U), column tiles (NT =
 // ceil(R/16)) and the split-K factor S (workgroups per tile).  Small-N
-// matrices are split along K so that the grid fills the chip; the partial
-// tiles are summed by the last workgroup of each tile, in split order.
+// matrices are split along K so that the grid fills the chip; the consumer
+// kernel adds the partial tiles in split order.
 struct RowsPlan {
   int nt, t, u, waves, splits, tiles;
 };
@@ -228,6 +230,17 @@ __device__ __forceinline__ void rows_tile_f32(const float* __restrict__ X, int l
   __syncthreads();
 }
 
+// Epilogues with a `Pre` type do part of their work before the k loop
+// (epi.pre(tile16, R) for each of the workgroup's tiles), where its latency
+// hides behind the weight stream; the result comes back with the tile.
+struct EpiNoPre {
+  struct Pre {};
+};
+template <class E, class = void>
+struct RowsPre : std::false_type {};
+template <class E>
+struct RowsPre<E, std::void_t<typename E::Pre>> : std::true_type {};
+
 // ---------------------------------------------------------------------------
 // The kernel: blockIdx.x = tile * splits + split.  With splits > 1 each
 // workgroup covers 1/splits of K and its epilogue (EpiPartial) stores the
@@ -248,6 +261,12 @@ __global__ __launch_bounds__(WAVES * 64) void rows_gemm_kernel(const TW* __restr
     wrows[i] = t16 < ntiles16 ? map(t16, i & 15) : map(0, i & 15);
   }
   __syncthreads();
+  using PreT = typename std::conditional<RowsPre<Epi>::value, Epi, EpiNoPre>::type::Pre;
+  PreT pre[T];
+  if constexpr (RowsPre<Epi>::value) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) pre[t] = epi.pre(min(wg_tile * T + t, ntiles16 - 1), R);
+  }
   if constexpr (sizeof(TW) == 2) {
     constexpr int KG = 32 * U;
     const int ng = K / KG;
@@ -258,9 +277,14 @@ __global__ __launch_bounds__(WAVES * 64) void rows_gemm_kernel(const TW* __restr
   } else {
     rows_tile_f32<T, NT, WAVES>((const float*)X, ldx, R, (const float*)W, K, K, wrows, tile);
   }
+#pragma unroll
   for (int t = 0; t < T; ++t) {
     const int t16 = wg_tile * T + t;
-    if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split);
+    if constexpr (RowsPre<Epi>::value) {
+      if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split, pre[t]);
+    } else {
+      if (t16 < ntiles16) epi(t16, tile + t * 16 * RP, RP, R, split);
+    }
   }
 }
 
@@ -278,6 +302,62 @@ struct EpiStore {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int r = e >> 4, m = e & 15;  // 16 threads write one output row's 16 columns
       Elem<TO>::st(out, (size_t)r * ldo + map(tile16, m), tile[m * RP + r]);
+    }
+  }
+};
+
+// LM head for the top-k: fp32 logits out[r, n] (plain map) and, per X row
+// and 16-column tile, {max, sum of exp(v - max)} over the tile's 16 logits
+// (sum 0 for an all -inf tile).  The 16 threads of one row are the 16 lanes
+// of a DPP row, so both go through the fixed row16 trees.
+//
+// The pairs of row r sit at part[r][slot] with slots grouped by XCD:
+// workgroups are dealt to the 8 XCDs in turn, so workgroup g (tiles g*tpw..)
+// writes slot (g%8)*per_x + (g/8)*tpw + t.  Each cache line of the array is
+// then written from one XCD's L2; interleaved 16-byte pieces from all eight
+// cost the LM head 8 us per launch (measured, 8B shape).  The slots of the
+// tile numbers past the last tile (up to 8*per_x) get {-inf, 0}, written by
+// the workgroup of the last tile, so a reader needs no validity test.
+struct TileSlots {
+  int nt16, tpw, per_x;  // per_x = tpw * ceil(ceil(nt16/tpw) / 8)
+  __host__ __device__ int count() const { return 8 * per_x; }
+  __device__ __forceinline__ int slot(int tile16) const {
+    const int g = tile16 / tpw, t = tile16 - g * tpw;
+    return (g & 7) * per_x + (g >> 3) * tpw + t;
+  }
+  // tile of a slot, or -1 for a slot no workgroup writes
+  __device__ __forceinline__ int tile(int s) const {
+    const int x = s / per_x, rem = s - x * per_x, q = rem / tpw, t = rem - q * tpw;
+    const int t16 = (q * 8 + x) * tpw + t;
+    return t16 < nt16 ? t16 : -1;
+  }
+};
+static inline TileSlots tile_slots(int nt16, int tpw) {
+  const int nwg = (nt16 + tpw - 1) / tpw;
+  return TileSlots{nt16, tpw, tpw * ((nwg + 7) / 8)};
+}
+
+struct EpiLogitsTiles {
+  float* out;
+  int ldo;
+  float2* part;  // [R][slots.count()]
+  TileSlots slots;
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
+    const int s = slots.slot(tile16);
+    for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
+      const int r = e >> 4, m = e & 15;
+      const float v = tile[m * RP + r];
+      out[(size_t)r * ldo + tile16 * 16 + m] = v;
+      const float mx = row16_max(v);
+      const float sm = row16_sum(mx == -INFINITY ? 0.f : expf(v - mx));
+      if (m == 0) part[(size_t)r * slots.count() + s] = make_float2(mx, sm);
+    }
+    if (tile16 == slots.nt16 - 1) {
+      const int npad = slots.count() - slots.nt16;
+      for (int e = threadIdx.x; e < npad * R; e += blockDim.x) {
+        const int i = e / R, r = e - i * R;
+        part[(size_t)r * slots.count() + slots.slot(slots.nt16 + i)] = make_float2(-INFINITY, 0.f);
+      }
     }
   }
 };
@@ -358,7 +438,10 @@ struct KVDest {
 
 // QKV epilogue for a MAP_PAIR_HEAD tile: rows m and m+8 are the RoPE pair
 // (i, i + hd/2) of one head, i = t*8 + m.  q goes to q_out [R][Hq*hd];
-// k/v go to the KV destination.  Values are rounded to TO after RoPE.
+// k/v go to the KV destination.  Values are rounded to TO after RoPE.  The
+// rotation's cos/sin (fp64 angle pos * theta^(-2i/hd)) depend only on the
+// row's position and i: the rows GEMM computes them before its k loop (Pre,
+// thread elements e = tid and tid + blockDim), the skinny kernel inline.
 template <typename TO>
 struct EpiQKV {
   TO* q_out;
@@ -366,34 +449,67 @@ struct EpiQKV {
   KVDest dst;
   int hq;
   float theta;
-  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
+  struct Pre {
+    float c[2], s[2];
+  };
+  __device__ __forceinline__ void rope(int r, int i, float& c, float& s) const {
+    const double inv = pow((double)theta, -(2.0 * i) / (double)dst.hd);
+    const double ang = (double)pos[r] * inv;
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
+  }
+  __device__ Pre pre(int tile16, int R) const {
+    const int tph = dst.hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
+    Pre p;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = threadIdx.x + u * blockDim.x;
+      p.c[u] = 1.f;
+      p.s[u] = 0.f;
+      if (e < 8 * R && head < hq + dst.hkv) rope(e >> 3, t * 8 + (e & 7), p.c[u], p.s[u]);
+    }
+    return p;
+  }
+  __device__ void store(int tile16, const float* tile, int RP, int R, int e, float c, float s) const {
     const int hd = dst.hd, tph = hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
     const int half = hd >> 1;
+    const int r = e >> 3, m = e & 7;
+    const int i = t * 8 + m;  // pair index within the head
+    float a = tile[m * RP + r], b = tile[(m + 8) * RP + r];
+    if (head < hq + dst.hkv) {  // q or k: rotate
+      const float a2 = a * c - b * s, b2 = b * c + a * s;
+      a = a2;
+      b = b2;
+    }
+    if (head < hq) {
+      const size_t o = (size_t)r * hq * hd + (size_t)head * hd;
+      Elem<TO>::st(q_out, o + i, a);
+      Elem<TO>::st(q_out, o + i + half, b);
+    } else {
+      const bool isk = head < hq + dst.hkv;
+      const int g = isk ? head - hq : head - hq - dst.hkv;
+      bool tree;
+      const size_t o = dst.off(r, g, tree);
+      TO* base = (TO*)(isk ? (tree ? dst.tk : dst.k) : (tree ? dst.tv : dst.v));
+      Elem<TO>::st(base, o + i, a);
+      Elem<TO>::st(base, o + i + half, b);
+    }
+  }
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int, const Pre& p) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = threadIdx.x + u * blockDim.x;
+      if (e < 8 * R) store(tile16, tile, RP, R, e, p.c[u], p.s[u]);
+    }
+  }
+  __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
+    const int tph = dst.hd >> 4, head = tile16 / tph, t = tile16 - head * tph;
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
-      const int r = e >> 3, m = e & 7;
-      const int i = t * 8 + m;  // pair index within the head
-      float a = tile[m * RP + r], b = tile[(m + 8) * RP + r];
-      if (head < hq + dst.hkv) {  // q or k: rotate
-        const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
-        const double ang = (double)pos[r] * inv;
-        const float c = (float)cos(ang), s = (float)sin(ang);
-        const float a2 = a * c - b * s, b2 = b * c + a * s;
-        a = a2;
-        b = b2;
-      }
-      if (head < hq) {
-        const size_t o = (size_t)r * hq * hd + (size_t)head * hd;
-        Elem<TO>::st(q_out, o + i, a);
-        Elem<TO>::st(q_out, o + i + half, b);
-      } else {
-        const bool isk = head < hq + dst.hkv;
-        const int g = isk ? head - hq : head - hq - dst.hkv;
-        bool tree;
-        const size_t o = dst.off(r, g, tree);
-        TO* base = (TO*)(isk ? (tree ? dst.tk : dst.k) : (tree ? dst.tv : dst.v));
-        Elem<TO>::st(base, o + i, a);
-        Elem<TO>::st(base, o + i + half, b);
-      }
+      float c = 1.f, s = 0.f;
+      if (head < hq + dst.hkv) rope(e >> 3, t * 8 + (e & 7), c, s);
+      store(tile16, tile, RP, R, e, c, s);
     }
   }
 };

@@ -26,12 +26,15 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
 
 // ---- top-k + log-probs over vocab rows (topk.hip)
 size_t topk_ws_bytes(int rows, int V);
-// per-row arrival counters inside a top-k workspace (must be zero at launch)
-unsigned* topk_counters(void* ws, int rows, int V);
 hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse, void* ws,
-                       bool counters_zeroed, hipStream_t st);
+                       hipStream_t st);
 // top-1 and log-probability from per-workgroup (max, sum exp, argmax) partials [rows][nparts]
 hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* ids, float* lp, hipStream_t st);
+// top-k from fp32 logits [rows][V] (rows <= 64, V a multiple of 16) and the
+// per-16-column-tile {max, sum exp} pairs EpiLogitsTiles wrote with
+// `tiles_per_wg` tiles per LM-head workgroup
+hipError_t launch_topk_tiles(const float* logits, const float2* part, int tiles_per_wg, int rows, int V, int k,
+                             int32_t* ids, float* lp, hipStream_t st);
 
 // ---- dynamic tree (tree.hip)
 size_t tree_state_bytes_per_req(int k, int D);

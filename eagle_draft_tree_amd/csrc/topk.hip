@@ -11,10 +11,10 @@
 // largest of the four wave thresholds and the partition's k best are all
 // among the logits at or above it (about 3k of 4096 for Gaussian logits);
 // those candidates go to LDS and each one's rank is counted against the
-// others.  The last workgroup of a row to finish (a per-row arrival counter,
-// zeroed before the launch) merges the partitions the same way: the
-// threshold is the larger of the k-th largest partition maximum and the
-// largest partition k-th value.  A candidate set larger than the LDS list
+// others.  The last workgroup of a row to finish (a per-row arrival
+// counter, zeroed by a small kernel before the launch) merges the
+// partitions the same way: the threshold is the larger of the k-th largest
+// partition maximum and the largest partition k-th value.  A candidate set larger than the LDS list
 // (many equal logits) falls back to k rounds of wavefront argmax, which
 // gives the same result.  Ties: value desc, then id asc, everywhere.
 //
@@ -26,6 +26,7 @@
 #include <limits.h>
 
 #include "common.hpp"
+#include "gemm_rows.hpp"
 #include "kernels.hpp"
 
 namespace e3 {
@@ -384,6 +385,215 @@ hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* 
   return hipGetLastError();
 }
 
+// Top-k from the LM head's per-tile statistics (EpiLogitsTiles, one launch
+// of at most 64 rows): one workgroup per row.  Thread t holds the
+// {max, sum exp} pairs of slots t, t + 512, ... (padding slots hold
+// {-inf, 0}).  The threshold T is the k-th largest of the 512 thread maxima
+// (each wave's k largest go to LDS and one wave takes the k-th of those): k
+// distinct threads hold a logit >= T, so the k best logits are all >= T and
+// lie in the tiles whose maximum reaches T, usually k to 2k tiles.  Only
+// those tiles' logits are read back (16 bytes per thread, all loads in
+// flight together); the ones >= T are ranked in LDS.  The LSE adds each
+// thread's pairs in slot order and the wave sums in a fixed order.  Too many
+// candidate tiles or logits (many equal values) take k rounds of block
+// argmax over the whole row, each restricted to what ranks after the
+// previous pick: the same result.
+constexpr int TT_THREADS = 512;
+constexpr int TT_TPT = 33;      // slots per thread: vocab <= 262144 plus slot padding
+constexpr int TT_TILES = 1024;  // candidate tiles
+constexpr int TT_CMAX = 1024;   // candidate logits
+
+__global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __restrict__ logits,
+                                                                const float2* __restrict__ part, TileSlots sl,
+                                                                int V, int k, int32_t* __restrict__ ids,
+                                                                float* __restrict__ lp) {
+  constexpr int NW = TT_THREADS / 64;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* x = logits + (size_t)row * V;
+  const int ns = sl.count();
+  const float2* p = part + (size_t)row * ns;
+  __shared__ float2 cand[TT_CMAX + 8];
+  __shared__ int tlist[TT_TILES];
+  __shared__ float wtop[NW * EAGLE3_MAX_TOPK];
+  __shared__ float mred[NW], sred[NW];
+  __shared__ float bval[NW];
+  __shared__ int bidx[NW];
+  __shared__ int ncand, ntile;
+  __shared__ float rowT;
+  if (tid == 0) {
+    ncand = 0;
+    ntile = 0;
+  }
+  float mx[TT_TPT], sx[TT_TPT];
+#pragma unroll
+  for (int j = 0; j < TT_TPT; ++j) {
+    const int s = tid + TT_THREADS * j;
+    const float2 pr = s < ns ? p[s] : make_float2(-INFINITY, 0.f);
+    mx[j] = pr.x;
+    sx[j] = pr.y;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < TT_TPT; ++j) m = fmaxf(m, mx[j]);
+  const float wm = wave_max(m);
+  {
+    // this wave's k largest thread maxima, with multiplicity
+    float xv = m;
+    int got = 0;
+    while (got < k) {
+      const float top = wave_max(xv);
+      const int cnt = __popcll(__ballot(xv == top));
+      if (lane == 0)
+        for (int i = got; i < min(got + cnt, k); ++i) wtop[w * k + i] = top;
+      got += cnt;
+      if (xv == top) xv = -INFINITY;
+    }
+  }
+  if (lane == 0) mred[w] = wm;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, mred[i]);
+  if (w == 0) {
+    // the k-th largest of the NW*k <= 128 values
+    float a = lane < NW * k ? wtop[lane] : -INFINITY;
+    float b = lane + 64 < NW * k ? wtop[lane + 64] : -INFINITY;
+    int got = 0;
+    float t = -INFINITY;
+    while (got < k) {
+      t = wave_max(fmaxf(a, b));
+      got += __popcll(__ballot(a == t)) + __popcll(__ballot(b == t));
+      if (a == t) a = -INFINITY;
+      if (b == t) b = -INFINITY;
+    }
+    if (lane == 0) rowT = t;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < TT_TPT; ++j)
+    if (mx[j] > -INFINITY) s += sx[j] * expf(mx[j] - M);
+  s = wave_sum(s);
+  if (lane == 0) sred[w] = s;
+  __syncthreads();
+  const float T = rowT;
+#pragma unroll
+  for (int j = 0; j < TT_TPT; ++j) {
+    const int sj = tid + TT_THREADS * j;
+    if (sj < ns && mx[j] >= T) {
+      const int t = sl.tile(sj);
+      if (t >= 0) {
+        const int pos = atomicAdd(&ntile, 1);
+        if (pos < TT_TILES) tlist[pos] = t;
+      }
+    }
+  }
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; i += 2) S += sred[i] + sred[i + 1];
+  const float L = M + logf(S);
+  const int NT = ntile;
+  if (NT <= TT_TILES) {
+    // quarter q of candidate tile i: 4 logits from one 16-byte load, two
+    // loads per thread in flight per pass
+    for (int e0 = 0; e0 < 4 * NT; e0 += 2 * TT_THREADS) {
+      float4 f[2];
+      int id0[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = e0 + tid + u * TT_THREADS;
+        id0[u] = e < 4 * NT ? tlist[e >> 2] * 16 + (e & 3) * 4 : -1;
+        f[u] = id0[u] >= 0 ? *(const float4*)(x + id0[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (id0[u] < 0) continue;
+        const float v4[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (v4[c] >= T) {
+            const int pos = atomicAdd(&ncand, 1);
+            if (pos < TT_CMAX) cand[pos] = make_float2(v4[c], __int_as_float(id0[u] + c));
+          }
+      }
+    }
+  }
+  __syncthreads();
+  const int C = ncand;
+  int32_t* oi = ids + (size_t)row * k;
+  float* ov = lp + (size_t)row * k;
+  if (NT <= TT_TILES && C <= TT_CMAX) {
+    const int C8 = (C + 7) & ~7;
+    for (int i = C + tid; i < C8; i += TT_THREADS) cand[i] = make_float2(-INFINITY, __int_as_float(INT_MAX));
+    __syncthreads();
+    for (int c = tid; c < C; c += TT_THREADS) {
+      const float2 me = cand[c];
+      const int id = __float_as_int(me.y);
+      int r = 0;
+      for (int j0 = 0; j0 < C8; j0 += 8) {
+        float2 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = cand[j0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += better(o[u].x, __float_as_int(o[u].y), me.x, id) ? 1 : 0;
+      }
+      if (r < k) {
+        oi[r] = id;
+        ov[r] = me.x - L;
+      }
+    }
+    for (int r = C + tid; r < k; r += TT_THREADS) {
+      oi[r] = INT_MAX;
+      ov[r] = -INFINITY;
+    }
+    return;
+  }
+  // fallback: k rounds of block argmax; round r takes the best (value desc,
+  // id asc) among the logits that rank after round r-1's pick
+  float pv = INFINITY;
+  int pi = -1;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int id = tid; id < V; id += TT_THREADS) {
+      const float v = x[id];
+      if (better(pv, pi, v, id) && better(v, id, bv, bi)) {
+        bv = v;
+        bi = id;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      bval[w] = bv;
+      bidx[w] = bi;
+    }
+    __syncthreads();
+    bv = bval[0];
+    bi = bidx[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i)
+      if (better(bval[i], bidx[i], bv, bi)) {
+        bv = bval[i];
+        bi = bidx[i];
+      }
+    __syncthreads();
+    if (tid == 0) {
+      oi[r] = bi;
+      ov[r] = bv - L;
+    }
+    pv = bv;
+    pi = bi;
+  }
+}
+
+hipError_t launch_topk_tiles(const float* logits, const float2* part, int tiles_per_wg, int rows, int V, int k,
+                             int32_t* ids, float* lp, hipStream_t st) {
+  const TileSlots sl = tile_slots(V / 16, tiles_per_wg);
+  if (rows > 64 || sl.count() > TT_THREADS * TT_TPT) return hipErrorInvalidValue;
+  topk_tiles_kernel<<<rows, TT_THREADS, 0, st>>>(logits, part, sl, V, k, ids, lp);
+  return hipGetLastError();
+}
+
 __global__ void topk_zero_kernel(unsigned* done, int rows) {
   for (int i = threadIdx.x; i < rows; i += blockDim.x) done[i] = 0u;
 }
@@ -394,19 +604,19 @@ size_t topk_ws_bytes(int rows, int V) {
   return (size_t)rows * topk_parts(V) * (EAGLE3_MAX_TOPK * 8 + 8) + (size_t)rows * 4 + 256;
 }
 
-unsigned* topk_counters(void* ws, int rows, int V) {
+static unsigned* topk_counters(void* ws, int rows, int V) {
   return (unsigned*)((unsigned char*)ws + (size_t)rows * topk_parts(V) * (EAGLE3_MAX_TOPK * 8 + 8));
 }
 
 hipError_t launch_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse, void* ws,
-                       bool counters_zeroed, hipStream_t st) {
+                       hipStream_t st) {
   const int nparts = (int)topk_parts(V);  // <= 64 (V <= 262144)
   float* pv = (float*)ws;
   int* pid = (int*)(pv + (size_t)rows * nparts * k);
   float* pm = (float*)(pid + (size_t)rows * nparts * k);
   float* ps = pm + (size_t)rows * nparts;
   unsigned* done = topk_counters(ws, rows, V);
-  if (!counters_zeroed) topk_zero_kernel<<<1, 256, 0, st>>>(done, rows);
+  topk_zero_kernel<<<1, 256, 0, st>>>(done, rows);
   topk_kernel<<<dim3(nparts, rows), TK_THREADS, 0, st>>>(logits, V, k, nparts, pv, pid, pm, ps, done, ids, lp, lse);
   return hipGetLastError();
 }

@@ -263,11 +263,13 @@ def test_bf16_small_cycle(lib, hkv, commit, ctx, pack):
     assert exc <= 1
 
 
-@pytest.mark.parametrize("commit,ctx", [(24, 70), (1, 300)])
+@pytest.mark.parametrize("commit,ctx", [(24, 70), (1, 300), (1, 1100)])
 def test_bf16_small_cycle_hd128(lib, commit, ctx):
     """Head dim 128 (the 8B/70B drafters' head size) at a size the oracle runs
     whole: 4 query heads on one KV head, a 24-row commit (6 groups of 16 query
-    vectors) or a long prefix with one root row; packed weights."""
+    vectors) or a long prefix with one root row; packed weights.  The
+    1100-row prefix gives the attention 32 or more splits, where a
+    workgroup merges its four waves' splits before the store."""
     say("bf16 small cycle hd128", commit, ctx)
     shape = tiny_shape(d=512, hq=4, hkv=1, hd=128, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
     w = scaled(C1_TINY, shape=shape, depth=4, topk=3, keep=12, prefix=ctx, commit_rows=commit,
@@ -291,6 +293,47 @@ def test_bf16_small_paged_cycle(lib, bs):
     gc = GpuCycle(w, Wt, ci, pack=True)
     gc.run()
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
+
+
+@pytest.mark.parametrize("batch,k,zero_lm", [(1, 6, False), (1, 6, True), (9, 2, False), (9, 2, True)])
+def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
+    """Up to 64 rows per step: the LM head writes each 16-column tile's
+    {max, sum exp} per row beside the logits, and the top-k reads those pairs
+    and only the tiles that can hold one of the k best.  Its ids must be the
+    k best of the kept logits (value desc, id asc) and its log-probabilities
+    logit minus the logsumexp of the row.  Batch 1 (6 rows, 2 tiles per LM-head
+    workgroup) and batch 9 x 2 (18 rows: the skinny GEMM, 8 tiles per
+    workgroup).  With a zero LM head every logit is 0 and all 2049 tiles
+    reach the threshold, more than the candidate-tile list holds: the k-round
+    argmax path must give ids 0..k-1 and lp = -log V."""
+    say("tile top-k, batch", batch, "k", k, "zero LM head" if zero_lm else "random LM head")
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=32784, dtype=BF16, theta=500000.0)
+    w = scaled(C1_TINY, shape=shape, batch=batch, depth=3, topk=k, keep=2 * k, prefix=40, commit_rows=3,
+               synthetic_prefix_kv=True, feat_scale=1.0)
+    Wt = gen.gen_weights(shape, seed=11)
+    if zero_lm:
+        Wt["lm"] = gen.Tensor(np.zeros_like(Wt["lm"].raw), Wt["lm"].dtype)
+    ci = gen.gen_cycle_inputs(w, seed=12)
+    gc = GpuCycle(w, Wt, ci, keep_logits=True, pack=True)
+    gc.run()
+    b = gc.buf
+    steps = [(b.root_ids, b.root_lp, b.commit_logits)]
+    steps += [(b.round_ids[r], b.round_lp[r], b.round_logits[r]) for r in range(len(b.round_ids))]
+    for ids, lp, lg in steps:
+        lg = lg.cpu().numpy().astype(np.float64)
+        lg = lg.reshape(-1, lg.shape[-1])
+        ids = ids.cpu().numpy().reshape(lg.shape[0], -1)
+        lp = lp.cpu().numpy().reshape(lg.shape[0], -1)
+        k = ids.shape[1]
+        for r in range(lg.shape[0]):
+            row = lg[r]
+            best = np.lexsort((np.arange(row.size), -row))[:k]
+            np.testing.assert_array_equal(ids[r], best)
+            m = row.max()
+            lse = m + np.log(np.exp(row - m).sum())
+            np.testing.assert_allclose(lp[r], row[best] - lse, atol=2e-5, rtol=0)
+            if zero_lm:
+                np.testing.assert_array_equal(ids[r], np.arange(k))
 
 
 def test_top1_lm_head_without_logits_matches_logits_path(lib):
