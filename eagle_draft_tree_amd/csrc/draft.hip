@@ -56,7 +56,7 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
     const float* __restrict__ h_tree, const int32_t* __restrict__ parent_slot, int mode, int rows,
     int d, const float* __restrict__ ge, const float* __restrict__ gs, float eps,
     float* __restrict__ S, T* __restrict__ x) {
-  __shared__ float red[RT / 64];
+  __shared__ float red[RT / 64], red2[RT / 64];
   const int r = blockIdx.x;
   const int b = r / rows;
   const T* e = emb + (size_t)tokens[r] * d;
@@ -75,8 +75,20 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
     se = fmaf(ev[j], ev[j], se);
     ss = fmaf(sv[j], sv[j], ss);
   }
-  se = block_sum(se, red);
-  ss = block_sum(ss, red);
+  // both block sums through one LDS exchange, waves added in a fixed order
+  se = wave_sum(se);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = se;
+    red2[threadIdx.x >> 6] = ss;
+  }
+  __syncthreads();
+  se = 0.f;
+  ss = 0.f;
+  for (int i = 0; i < RT / 64; ++i) {
+    se += red[i];
+    ss += red2[i];
+  }
   const float ie = (float)(1.0 / sqrt((double)se / d + (double)eps));
   const float is = (float)(1.0 / sqrt((double)ss / d + (double)eps));
 #pragma unroll

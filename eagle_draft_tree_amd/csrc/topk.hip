@@ -388,11 +388,12 @@ hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* 
 // Top-k from the LM head's per-tile statistics (EpiLogitsTiles, one launch
 // of at most 64 rows): one workgroup per row.  Thread t holds the
 // {max, sum exp} pairs of slots t, t + 512, ... (padding slots hold
-// {-inf, 0}).  The threshold T is the k-th largest of the 512 thread maxima
-// (each wave's k largest go to LDS and one wave takes the k-th of those): k
-// distinct threads hold a logit >= T, so the k best logits are all >= T and
-// lie in the tiles whose maximum reaches T, usually k to 2k tiles.  Only
-// those tiles' logits are read back (16 bytes per thread, all loads in
+// {-inf, 0}).  Each 16-lane row of threads takes its maximum: 32 group
+// maxima, each a logit of a different group.  The threshold T is the largest
+// group maximum that at least k group maxima reach (every wave counts this
+// itself from LDS, no serial k rounds): k distinct logits are >= T, so the k
+// best logits are all >= T and lie in the tiles whose maximum reaches T.
+// Only those tiles' logits are read back (16 bytes per thread, all loads in
 // flight together); the ones >= T are ranked in LDS.  The LSE adds each
 // thread's pairs in slot order and the wave sums in a fixed order.  Too many
 // candidate tiles or logits (many equal values) take k rounds of block
@@ -408,18 +409,19 @@ __global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __r
                                                                 int V, int k, int32_t* __restrict__ ids,
                                                                 float* __restrict__ lp) {
   constexpr int NW = TT_THREADS / 64;
+  constexpr int NG = TT_THREADS / 16;  // 16-lane groups
+  static_assert(NG == 32 && NG >= EAGLE3_MAX_TOPK, "one wave counts the group maxima; k <= groups");
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* x = logits + (size_t)row * V;
   const int ns = sl.count();
   const float2* p = part + (size_t)row * ns;
   __shared__ float2 cand[TT_CMAX + 8];
   __shared__ int tlist[TT_TILES];
-  __shared__ float wtop[NW * EAGLE3_MAX_TOPK];
-  __shared__ float mred[NW], sred[NW];
+  __shared__ __attribute__((aligned(16))) float gmax[NG];
+  __shared__ float sred[NW];
   __shared__ float bval[NW];
   __shared__ int bidx[NW];
   __shared__ int ncand, ntile;
-  __shared__ float rowT;
   if (tid == 0) {
     ncand = 0;
     ntile = 0;
@@ -435,38 +437,21 @@ __global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __r
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < TT_TPT; ++j) m = fmaxf(m, mx[j]);
-  const float wm = wave_max(m);
-  {
-    // this wave's k largest thread maxima, with multiplicity
-    float xv = m;
-    int got = 0;
-    while (got < k) {
-      const float top = wave_max(xv);
-      const int cnt = __popcll(__ballot(xv == top));
-      if (lane == 0)
-        for (int i = got; i < min(got + cnt, k); ++i) wtop[w * k + i] = top;
-      got += cnt;
-      if (xv == top) xv = -INFINITY;
-    }
-  }
-  if (lane == 0) mred[w] = wm;
+  const float gm = row16_max(m);
+  if ((lane & 15) == 0) gmax[tid >> 4] = gm;
   __syncthreads();
-  float M = -INFINITY;
+  // every wave: lane l < 32 counts the group maxima >= group maximum l
+  float T, M;
+  {
+    const float mine = gmax[lane & (NG - 1)];
+    int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) M = fmaxf(M, mred[i]);
-  if (w == 0) {
-    // the k-th largest of the NW*k <= 128 values
-    float a = lane < NW * k ? wtop[lane] : -INFINITY;
-    float b = lane + 64 < NW * k ? wtop[lane + 64] : -INFINITY;
-    int got = 0;
-    float t = -INFINITY;
-    while (got < k) {
-      t = wave_max(fmaxf(a, b));
-      got += __popcll(__ballot(a == t)) + __popcll(__ballot(b == t));
-      if (a == t) a = -INFINITY;
-      if (b == t) b = -INFINITY;
+    for (int q = 0; q < NG; q += 4) {
+      const float4 o = *(const float4*)(gmax + q);
+      cnt += (o.x >= mine) + (o.y >= mine) + (o.z >= mine) + (o.w >= mine);
     }
-    if (lane == 0) rowT = t;
+    T = wave_max(cnt >= k ? mine : -INFINITY);
+    M = wave_max(mine);
   }
   float s = 0.f;
 #pragma unroll
@@ -474,8 +459,6 @@ __global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __r
     if (mx[j] > -INFINITY) s += sx[j] * expf(mx[j] - M);
   s = wave_sum(s);
   if (lane == 0) sred[w] = s;
-  __syncthreads();
-  const float T = rowT;
 #pragma unroll
   for (int j = 0; j < TT_TPT; ++j) {
     const int sj = tid + TT_THREADS * j;

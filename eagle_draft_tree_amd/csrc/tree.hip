@@ -80,11 +80,12 @@ __device__ __forceinline__ bool pool_better(float sa, int da, int fa, float sb, 
 
 // Give the frontier nodes of depth j their tree slots (j-1)k + rank, emit
 // the rows of the next draft step and record the frontier in the header.
-// front[rho] = pool node, fpar[rho] = its parent's frontier index in the
-// previous header (-1 for depth 1), with that header's slot/anc (pslot, panc).
-__device__ void emit_frontier(Pool& P, const int* front, const int* fpar, const float* fsc, const uint64_t* fpath,
-                              const int* pslot, const uint64_t* panc, int b, int k, int j, int root_pos,
-                              int32_t* next_tok, int32_t* next_parent_slot, int32_t* next_pos,
+// front[rho] = pool node with token ftok[rho], fpar[rho] = its parent's
+// frontier index in the previous header (-1 for depth 1), with that header's
+// slot/anc (pslot, panc).
+__device__ void emit_frontier(Pool& P, const int* front, const int* ftok, const int* fpar, const float* fsc,
+                              const uint64_t* fpath, const int* pslot, const uint64_t* panc, int b, int k, int j,
+                              int root_pos, int32_t* next_tok, int32_t* next_parent_slot, int32_t* next_pos,
                               uint64_t* next_anc) {
   for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {
     const int n = front[rho];
@@ -97,7 +98,7 @@ __device__ void emit_frontier(Pool& P, const int* front, const int* fpar, const 
     P.hdr->fslot[rho] = s;
     P.hdr->fanc[rho] = a;
     P.hdr->fpath[rho] = fpath[rho];
-    next_tok[b * k + rho] = P.tok[n];
+    next_tok[b * k + rho] = ftok[rho];
     next_parent_slot[b * k + rho] = pr >= 0 ? 1 + pslot[pr] : 0;
     next_pos[b * k + rho] = root_pos + j;
     next_anc[b * k + rho] = a;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     int32_t* next_pos, uint64_t* next_anc) {
   const int b = blockIdx.x;
   Pool P = pool_of(state, b, k, D);
-  __shared__ int front[EAGLE3_MAX_TOPK], fpar[EAGLE3_MAX_TOPK];
+  __shared__ int front[EAGLE3_MAX_TOPK], ftok[EAGLE3_MAX_TOPK], fpar[EAGLE3_MAX_TOPK];
   __shared__ float fsc[EAGLE3_MAX_TOPK];
   __shared__ uint64_t fpath[EAGLE3_MAX_TOPK];
   const int rp = root_pos[b];
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     const int t = ids[b * k + i];
     const float sc = lp[b * k + i];
     front[i] = i;
+    ftok[i] = t;
     fpar[i] = -1;
     fsc[i] = sc;
     fpath[i] = (uint64_t)i;
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     P.hdr->npool = k;
   }
   __syncthreads();
-  if (D > 1) emit_frontier(P, front, fpar, fsc, fpath, nullptr, nullptr, b, k, 1, rp, next_tok, next_parent_slot,
-                           next_pos, next_anc);
+  if (D > 1) emit_frontier(P, front, ftok, fpar, fsc, fpath, nullptr, nullptr, b, k, 1, rp, next_tok,
+                           next_parent_slot, next_pos, next_anc);
   else
     for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {  // depth-1 tree: the header still lists the frontier
       P.hdr->front[rho] = rho;
@@ -148,19 +150,34 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_init_kernel(
     }
 }
 
+// One depth step: the k*k candidates (frontier row rho, its i-th best token)
+// get score = frontier score + lp, in one fp32 add; the k best by (score
+// desc, flat index asc) become the next frontier.  Thread c owns candidate
+// c (kk <= 256 = TREE_THREADS) and loads its id and log-prob before the
+// header arrives; the selection counts each candidate's rank in LDS.
 __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     int k, int D, void* state, const int32_t* ids, const float* lp, int32_t* next_tok,
     int32_t* next_parent_slot, int32_t* next_pos, uint64_t* next_anc) {
+  static_assert(TREE_THREADS >= EAGLE3_MAX_TOPK * EAGLE3_MAX_TOPK, "one thread per candidate");
   const int b = blockIdx.x;
   Pool P = pool_of(state, b, k, D);
   __shared__ int front[EAGLE3_MAX_TOPK], pslot[EAGLE3_MAX_TOPK];
   __shared__ float pscore[EAGLE3_MAX_TOPK];
   __shared__ uint64_t panc[EAGLE3_MAX_TOPK], ppath[EAGLE3_MAX_TOPK];
-  __shared__ int newfront[EAGLE3_MAX_TOPK], newpar[EAGLE3_MAX_TOPK];
+  __shared__ int newfront[EAGLE3_MAX_TOPK], newtok[EAGLE3_MAX_TOPK], newpar[EAGLE3_MAX_TOPK];
   __shared__ float newsc[EAGLE3_MAX_TOPK];
   __shared__ uint64_t newpath[EAGLE3_MAX_TOPK];
+  __shared__ __attribute__((aligned(16))) float csc[EAGLE3_MAX_TOPK * EAGLE3_MAX_TOPK];
+  const int kk = k * k;
+  const int c = threadIdx.x;
+  int ctok = 0;
+  float clp = 0.f;
+  if (c < kk) {  // ids/lp rows b*k + rho, column i: element b*kk + c
+    ctok = ids[(size_t)b * kk + c];
+    clp = lp[(size_t)b * kk + c];
+  }
   const int j = P.hdr->round + 1;
-  if (j > D) return;  // the tree already has depth D
+  if (j > D) return;  // the tree already has depth D (same value in every thread)
   const int base = P.hdr->npool;
   const int root_pos = P.hdr->root_pos;
   for (int i = threadIdx.x; i < k; i += blockDim.x) {
@@ -171,57 +188,38 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     ppath[i] = P.hdr->fpath[i];
   }
   __syncthreads();
-  const int kk = k * k;
-  // wave 0: lane l owns candidates c = l + 64*q (q < 4, kk <= 256)
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    float cs[4];
-    int cf[4];
-    uint64_t cp[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = lane + 64 * q;
-      cs[q] = -INFINITY;
-      cf[q] = INT_MAX;
-      cp[q] = 0ull;
-      if (c < kk) {
-        const int rho = c / k, i = c - rho * k;
-        const float sc = pscore[rho] + lp[(size_t)(b * k + rho) * k + i];  // one fp32 add
-        const uint64_t path = ppath[rho] * (uint64_t)k + (uint64_t)i;
-        const int n = base + c;
-        P.tok[n] = ids[(size_t)(b * k + rho) * k + i];
-        P.parent[n] = front[rho];
-        P.depth[n] = j;
-        P.flat[n] = c;
-        P.rank[n] = i;
-        P.score[n] = sc;
-        P.path[n] = path;
-        cs[q] = sc;
-        cf[q] = c;
-        cp[q] = path;
-      }
+  float sc = -INFINITY;
+  uint64_t path = 0ull;
+  if (c < kk) {
+    const int rho = c / k, i = c - rho * k;
+    sc = pscore[rho] + clp;  // one fp32 add
+    path = ppath[rho] * (uint64_t)k + (uint64_t)i;
+    const int n = base + c;
+    P.tok[n] = ctok;
+    P.parent[n] = front[rho];
+    P.depth[n] = j;
+    P.flat[n] = c;
+    P.rank[n] = i;
+    P.score[n] = sc;
+    P.path[n] = path;
+    csc[c] = sc;
+  }
+  for (int e = kk + c; e < ((kk + 3) & ~3); e += TREE_THREADS) csc[e] = -INFINITY;  // pad to a multiple of 4
+  __syncthreads();
+  if (c < kk) {
+    // rank: candidates better by (score desc, flat asc); pads (-inf, flat >= kk) never are
+    int r = 0;
+    for (int q = 0; q < kk; q += 4) {
+      const float4 o = *(const float4*)(csc + q);
+      r += front_better(o.x, q, sc, c) + front_better(o.y, q + 1, sc, c) + front_better(o.z, q + 2, sc, c) +
+           front_better(o.w, q + 3, sc, c);
     }
-    // k rounds of wave argmax by (score desc, flat asc)
-    for (int r = 0; r < k; ++r) {
-      float bs = -INFINITY;
-      int bf = INT_MAX;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (front_better(cs[q], cf[q], bs, bf)) {
-          bs = cs[q];
-          bf = cf[q];
-        }
-      wave_argmax(bs, bf);  // (score desc, flat asc) is the same order as (value desc, id asc)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (cf[q] == bf) {
-          newfront[r] = base + bf;
-          newpar[r] = bf / k;
-          newsc[r] = bs;
-          newpath[r] = cp[q];
-          cs[q] = -INFINITY;
-          cf[q] = INT_MAX;
-        }
+    if (r < k) {
+      newfront[r] = base + c;
+      newtok[r] = ctok;
+      newpar[r] = c / k;
+      newsc[r] = sc;
+      newpath[r] = path;
     }
   }
   __syncthreads();
@@ -230,8 +228,8 @@ __global__ __launch_bounds__(TREE_THREADS) void tree_step_kernel(
     P.hdr->npool = base + kk;
   }
   if (j < D) {
-    emit_frontier(P, newfront, newpar, newsc, newpath, pslot, panc, b, k, j, root_pos, next_tok, next_parent_slot,
-                  next_pos, next_anc);
+    emit_frontier(P, newfront, newtok, newpar, newsc, newpath, pslot, panc, b, k, j, root_pos, next_tok,
+                  next_parent_slot, next_pos, next_anc);
   } else {
     for (int rho = threadIdx.x; rho < k; rho += blockDim.x) {  // last depth: no more rows to draft
       P.hdr->front[rho] = newfront[rho];
