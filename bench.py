@@ -206,7 +206,14 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
             if nwg < 192:
                 nwg = -(-(V // 16) // 4)
             return r * nwg * 16
-        return r * V * 4
+        out = r * V * 4
+        if r <= 64:
+            # plus each 16-column tile's (max, sum exp) per row, 8 B, in slots grouped
+            # by XCD (tpw tiles per workgroup: 2 up to 16 rows, 8 for the skinny GEMM)
+            nt16 = V // 16
+            tpw = 2 if r <= 16 else 8
+            out += r * 8 * tpw * -(-(-(-nt16 // tpw)) // 8) * 8
+        return out
 
     lm_bytes = [w_lm + r * d * es + lm_out_bytes(r) for r in rows]
     lm_flops = [2.0 * r * V * d for r in rows]
