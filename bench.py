@@ -100,7 +100,7 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
     import torch
 
     from eagle_draft_tree_amd import binding as Bd
-    from eagle_draft_tree_amd.cycle import CycleBuffers, CycleSpec, KVCache, run_cycle
+    from eagle_draft_tree_amd.cycle import CycleBuffers, CycleSpec, KVCache, run_cycle, run_draft_steps
     from workloads import gen
 
     s = w.shape
@@ -185,6 +185,21 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         torch.cuda.synchronize()
         assert np.array_equal(buf.accept_len.cpu().numpy().astype(np.float64), accepted[(steps - 1) % n_plant])
         del graphs
+        # the cycle's D draft steps alone (COMMIT + D-1 TREE rounds), replayed on
+        # the inputs the last cycle left in place
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            run_draft_steps(dr, buf, kv, tokens, pos, ctx_after)
+        for i in range(warmup):
+            gs.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            gs.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_steps = start.elapsed_time(end) / steps
+        del gs
 
     # algorithmic bytes: bf16 weights read once per round, every request's KV once per round
     es = 2
@@ -216,6 +231,7 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         return out
 
     lm_bytes = [w_lm + r * d * es + lm_out_bytes(r) for r in rows]
+    bytes_steps = D * (w_layer + kv_round) + sum(lm_bytes)  # the D draft steps
     lm_flops = [2.0 * r * V * d for r in rows]
     lm_ms, lm_cnt = per_class["lm_head"]
     reps = lm_cnt // len(rows) if lm_cnt else 0
@@ -241,6 +257,11 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
                            "frac": round(bytes_cycle / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernel_ms_per_cycle": {kk: round(v[0] / steps, 4) for kk, v in per_class.items()},
     }
+    if graph:
+        gbs = bytes_steps / (ms_steps * 1e-3) / 1e9
+        res["draft_step_roofline"] = {"steps": D, "bytes_per_step": round(bytes_steps / D),
+                                      "us_per_step": round(ms_steps * 1e3 / D, 2), "achieved_GBs": round(gbs, 1),
+                                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
     return res, ci
 
 
@@ -393,6 +414,7 @@ def main():
                      "frac": lm["hbm_frac"], "traffic": traffic, "kernel": "lm_head rows GEMM",
                      "bytes_per_launch": lm["bytes_per_launch"], "avg_launch_us": lm["avg_launch_us"]},
         "cycle_roofline": r["cycle_roofline"],
+        "draft_step_roofline": r.get("draft_step_roofline"),
         "kernel_ms_per_cycle": r["kernel_ms_per_cycle"],
         "setup_s": round(setup_s, 1),
     }

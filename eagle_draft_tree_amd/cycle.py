@@ -114,6 +114,26 @@ class KVCache:
                     cl.data_ptr(), self.tk.data_ptr(), self.tv.data_ptr())
 
 
+def run_draft_steps(dr: Drafter, buf: CycleBuffers, kv: KVCache, tokens, commit_pos, ctx_after):
+    """Enqueue only the cycle's draft steps (COMMIT, then the D-1 TREE rounds)
+    on the inputs a previous run_cycle left in `buf` (fused rows, frontier
+    rows): the same calls as run_cycle, without fusion, tree expansion or
+    verification."""
+    sp = buf.spec
+    Bn, n, k, D = sp.batch, sp.commit_rows, sp.k, sp.depth
+    kv_commit = kv.struct()
+    kv_tree = kv.struct(ctx_after)
+    B.eagle3_draft_step(dr.dims, dr.weights, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos,
+                        None, 0, k, B.TOPK_LAST, buf.h_tree, buf.root_ids, buf.root_lp,
+                        buf.commit_logits, buf.ws)
+    for j in range(2, D + 1):
+        r = j - 2
+        B.eagle3_draft_step(dr.dims, dr.weights, kv_tree, B.TREE, Bn, k, None, buf.next_par[r],
+                            buf.next_tok[r], buf.next_pos[r], buf.next_anc[r], r * k, k, B.TOPK_ALL,
+                            buf.h_tree, buf.round_ids[r], buf.round_lp[r],
+                            buf.round_logits[r] if buf.round_logits is not None else None, buf.ws)
+
+
 def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit_pos, ctx_after,
               root_tok, root_pos, target_logits=None, mode=B.GREEDY, temperature=1.0, u_try=None,
               u_res=None, verify=True):
