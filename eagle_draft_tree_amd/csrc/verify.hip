@@ -7,12 +7,16 @@
 // remaining support, and a rejected token leaves the support -- the
 // residual max(p - q, 0) renormalised.
 //
-// Kernel A (grid: requests x rows x partitions) reduces every verify row in
-// 4096-token partitions: argmax (value desc, id asc), NaN flag and, for
-// sampling, the partition max and sum of exp((L - max)/T) in fp64.
-// Kernel B (one workgroup per request) walks the tree on those partials; at
-// the last node of a sampling walk it locates the partition where the
-// residual CDF crosses u_res * Rm and scans only that partition.
+// One kernel, grid (partition pairs x requests * rows).  Every workgroup
+// reduces two 4096-token partitions of one verify row: argmax (value
+// desc, id asc), NaN flag and, for sampling, the partition max and sum of
+// exp((L - max)/T) in fp64.  The last workgroup of a request to finish (a
+// per-request arrival counter, reset by that workgroup) walks the request's
+// tree on those partials; at the last node of a sampling walk it locates the
+// partition where the residual CDF crosses u_res * Rm and scans only that
+// partition.  The partials cross workgroups (and XCDs) through agent-scope
+// stores and loads, each wave waiting for its stores before the barrier that
+// precedes the counter increment: no L2 write-back.
 #include <limits.h>
 
 #include "common.hpp"
@@ -20,10 +24,20 @@
 
 namespace e3 {
 
-constexpr int VR_THREADS = 256;
-constexpr int VR_PS = 4096;  // tokens per partition (16 per thread)
-constexpr int VW_THREADS = 1024;
+constexpr int VR_THREADS = 256;  // threads per partition
+constexpr int VR_PS = 4096;      // tokens per partition (16 per thread)
+constexpr int VR_PARTS = 4;      // partitions per workgroup
+constexpr int VW_THREADS = VR_THREADS * VR_PARTS;
 constexpr int VW_WAVES = VW_THREADS / 64;
+
+template <typename X>
+__device__ __forceinline__ void st_dev(X* p, X v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename X>
+__device__ __forceinline__ X ld_dev(const X* p) {
+  return __hip_atomic_load((X*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct ArgRed {
   float v;
@@ -39,22 +53,29 @@ __device__ __forceinline__ ArgRed wave_arg(ArgRed a) {
   return a;
 }
 
-// ---------------------------------------------------------------- kernel A
-__global__ __launch_bounds__(VR_THREADS) void verify_rows_kernel(
+// ---------------------------------------------------------------- the rows
+// A workgroup of VW_THREADS reduces VR_PARTS partitions of one row: part
+// sg (VR_THREADS threads, 16 tokens each) takes partition blockIdx.x *
+// VR_PARTS + sg.  Every barrier is reached by all parts (a part past the
+// last partition reduces nothing).
+__device__ __forceinline__ void verify_rows(
     int V, int nparts, const float* __restrict__ logits, int sample, double invT,
     float* __restrict__ pa_v, int* __restrict__ pa_id, float* __restrict__ pmax,
     double* __restrict__ psum, int* __restrict__ pnan) {
-  const int part = blockIdx.x;
+  constexpr int QW = VR_THREADS / 64;  // waves per quarter
+  const int sg = threadIdx.x / VR_THREADS, lt = threadIdx.x - sg * VR_THREADS;
+  const int part = blockIdx.x * VR_PARTS + sg;
+  const bool valid = part < nparts;
   const size_t row = blockIdx.y;  // request * (m+1) + node
   const float* x = logits + row * V;
   const int lo = part * VR_PS;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = lt & 63, w = lt >> 6;
   float v[16];
   const bool vec_ok = (V & 3) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int y0 = lo + 4 * (threadIdx.x + VR_THREADS * j);
-    if (vec_ok && y0 + 3 < V) {
+    const int y0 = lo + 4 * (lt + VR_THREADS * j);
+    if (valid && vec_ok && y0 + 3 < V) {
       const float4 f = *(const float4*)(x + y0);
       v[4 * j] = f.x;
       v[4 * j + 1] = f.y;
@@ -62,70 +83,71 @@ __global__ __launch_bounds__(VR_THREADS) void verify_rows_kernel(
       v[4 * j + 3] = f.w;
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[4 * j + c] = y0 + c < V ? x[y0 + c] : -INFINITY;
+      for (int c = 0; c < 4; ++c) v[4 * j + c] = valid && y0 + c < V ? x[y0 + c] : -INFINITY;
     }
   }
   ArgRed best{-INFINITY, INT_MAX};
   int nan = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int y = lo + 4 * (threadIdx.x + VR_THREADS * (e >> 2)) + (e & 3);
+    const int y = lo + 4 * (lt + VR_THREADS * (e >> 2)) + (e & 3);
     if (v[e] != v[e]) nan = 1;
     else if (y < V && better(v[e], y, best.v, best.id)) best = ArgRed{v[e], y};
   }
-  __shared__ ArgRed ared[VR_THREADS / 64];
-  __shared__ double dred[VR_THREADS / 64];
-  __shared__ int nred[VR_THREADS / 64];
+  __shared__ ArgRed ared[VR_PARTS * QW];
+  __shared__ double dred[VR_PARTS * QW];
+  __shared__ int nred[VR_PARTS * QW];
   best = wave_arg(best);
   const int wn = __any(nan) ? 1 : 0;
   if (lane == 0) {
-    ared[w] = best;
-    nred[w] = wn;
+    ared[sg * QW + w] = best;
+    nred[sg * QW + w] = wn;
   }
   __syncthreads();
-  ArgRed b = ared[0];
-  int anynan = nred[0];
+  ArgRed b = ared[sg * QW];
+  int anynan = nred[sg * QW];
 #pragma unroll
-  for (int i = 1; i < VR_THREADS / 64; ++i) {
-    b = arg_better(b, ared[i]);
-    anynan |= nred[i];
+  for (int i = 1; i < QW; ++i) {
+    b = arg_better(b, ared[sg * QW + i]);
+    anynan |= nred[sg * QW + i];
   }
   const size_t o = row * nparts + part;
-  if (sample && !anynan) {
+  if (sample) {  // uniform over the workgroup: the barrier below is too
     const double mx = (double)b.v;
     double s = 0.0;
+    if (!anynan) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int y = lo + 4 * (threadIdx.x + VR_THREADS * (e >> 2)) + (e & 3);
-      if (y < V && v[e] > -INFINITY) s += exp(((double)v[e] - mx) * invT);
+      for (int e = 0; e < 16; ++e) {
+        const int y = lo + 4 * (lt + VR_THREADS * (e >> 2)) + (e & 3);
+        if (y < V && v[e] > -INFINITY) s += exp(((double)v[e] - mx) * invT);
+      }
     }
     s = wave_sum_d(s);
-    if (lane == 0) dred[w] = s;
+    if (lane == 0) dred[sg * QW + w] = s;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (lt == 0 && valid && !anynan) {
       double t = 0.0;
 #pragma unroll
-      for (int i = 0; i < VR_THREADS / 64; ++i) t += dred[i];
-      psum[o] = t;
+      for (int i = 0; i < QW; ++i) t += dred[sg * QW + i];
+      st_dev(psum + o, t);
     }
   }
-  if (threadIdx.x == 0) {
-    pa_v[o] = b.v;
-    pa_id[o] = b.id;
-    pmax[o] = b.v;
-    pnan[o] = anynan;
+  if (lt == 0 && valid) {
+    st_dev(pa_v + o, b.v);
+    st_dev(pa_id + o, b.id);
+    st_dev(pmax + o, b.v);
+    st_dev(pnan + o, anynan);
   }
 }
 
-// ---------------------------------------------------------------- kernel B
-__global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
-    int m, int V, int Dmax, int nparts, const int32_t* __restrict__ v_tok,
+// ---------------------------------------------------------------- the walk
+__device__ void verify_walk(
+    int b, int m, int V, int Dmax, int nparts, const int32_t* __restrict__ v_tok,
     const int32_t* __restrict__ v_parent, const float* __restrict__ logits, int mode, double invT,
     const double* __restrict__ u_try, const double* __restrict__ u_res, const float* __restrict__ pa_v,
     const int* __restrict__ pa_id, const float* __restrict__ pmax, const double* __restrict__ psum,
     const int* __restrict__ pnan, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
     int32_t* status) {
-  const int b = blockIdx.x;
   const int M1 = m + 1;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ int kids[EAGLE3_MAX_TREE_SLOTS];
@@ -153,8 +175,8 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
       ArgRed bb{-INFINITY, INT_MAX};
       int nn = 0;
       for (int p = lane; p < nparts; p += 64) {
-        bb = arg_better(bb, ArgRed{pa_v[row * nparts + p], pa_id[row * nparts + p]});
-        nn |= pnan[row * nparts + p];
+        bb = arg_better(bb, ArgRed{ld_dev(pa_v + row * nparts + p), ld_dev(pa_id + row * nparts + p)});
+        nn |= ld_dev(pnan + row * nparts + p);
       }
       bb = wave_arg(bb);
       const int anynan = __any(nn) ? 1 : 0;
@@ -162,8 +184,8 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
       if (mode == EAGLE3_SAMPLE && !anynan) {
         const double M = (double)bb.v;
         for (int p = lane; p < nparts; p += 64) {
-          const float mp = pmax[row * nparts + p];
-          if (mp > -INFINITY) R += psum[row * nparts + p] * exp(((double)mp - M) * invT);
+          const float mp = ld_dev(pmax + row * nparts + p);
+          if (mp > -INFINITY) R += ld_dev(psum + row * nparts + p) * exp(((double)mp - M) * invT);
         }
         R = wave_sum_d(R);
       }
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
       continue;
     }
     // bonus: the smallest y outside the rejected set whose cumulative weight
-    // (partitions in order; inside a partition, per-thread 4-token segments
+    // (partitions in order; inside a partition, per-thread 8-token segments
     // in order) exceeds u_res[node] * Rm.
     const double thr = u_res[(size_t)b * M1 + node] * Rm;
     auto weight = [&](int y) -> double {
@@ -237,8 +259,8 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
       // remaining weight of each partition: its sum rescaled, minus rejected tokens in it
       if (threadIdx.x < np) {
         const int p = p0 + threadIdx.x;
-        const float mp = pmax[row * nparts + p];
-        double s = mp > -INFINITY ? psum[row * nparts + p] * exp(((double)mp - mx) * invT) : 0.0;
+        const float mp = ld_dev(pmax + row * nparts + p);
+        double s = mp > -INFINITY ? ld_dev(psum + row * nparts + p) * exp(((double)mp - mx) * invT) : 0.0;
         for (int r = 0; r < nrej; ++r)
           if (rejected[r] / VR_PS == p) s -= exp(((double)L[rejected[r]] - mx) * invT);
         wpart[threadIdx.x] = s > 0.0 ? s : 0.0;
@@ -253,15 +275,16 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
         }
         // the crossing lies in partition p0 + q (or just after, by rounding): scan it
         const int lo = (p0 + q) * VR_PS;
-        const int y0 = lo + 4 * threadIdx.x;
+        constexpr int SEG = VR_PS / VW_THREADS;  // tokens per thread
+        const int y0 = lo + SEG * threadIdx.x;
         double seg = 0.0;
-        double wy[4];
+        double wy[SEG];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < SEG; ++c) {
           wy[c] = y0 + c < V ? weight(y0 + c) : 0.0;
           seg += wy[c];
         }
-        // exclusive scan of the 1024 segment sums (waves, then wave totals)
+        // exclusive scan of the segment sums (waves, then wave totals)
         double incl = seg;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -274,7 +297,7 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
         for (int i = 0; i < w; ++i) wbase += wsum[i];
         double acc = before + wbase + (incl - seg);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < SEG; ++c) {
           acc += wy[c];
           if (wy[c] > 0.0 && acc > thr) {
             atomicMin(&bonus_s, y0 + c);
@@ -314,10 +337,32 @@ __global__ __launch_bounds__(VW_THREADS) void verify_walk_kernel(
   }
 }
 
+__global__ __launch_bounds__(VW_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void verify_kernel(
+    int m, int V, int Dmax, int nparts, const int32_t* __restrict__ v_tok, const int32_t* __restrict__ v_parent,
+    const float* __restrict__ logits, int mode, double invT, const double* __restrict__ u_try,
+    const double* __restrict__ u_res, float* pa_v, int* pa_id, float* pmax, double* psum, int* pnan,
+    unsigned* arrive, int32_t* accept_len, int32_t* accepted, int32_t* bonus, int32_t* status) {
+  verify_rows(V, nparts, logits, mode == EAGLE3_SAMPLE, invT, pa_v, pa_id, pmax, psum, pnan);
+  __shared__ int last;
+  const int b = blockIdx.y / (m + 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    last = atomicAdd(&arrive[b], 1u) == (unsigned)(gridDim.x * (m + 1) - 1);
+    if (last) arrive[b] = 0u;  // every arrival has been counted: ready for the next call
+  }
+  __syncthreads();
+  if (!last) return;
+  verify_walk(b, m, V, Dmax, nparts, v_tok, v_parent, logits, mode, invT, u_try, u_res, pa_v, pa_id, pmax, psum,
+              pnan, accept_len, accepted, bonus, status);
+}
+
+// Partials [B*(m+1)][nparts] (psum fp64, argmax value and id, max, NaN flag),
+// then B arrival counters at the end.
 size_t verify_ws_bytes(int B, int m, int V) {
   const size_t nparts = (V + VR_PS - 1) / VR_PS;
   const size_t n = (size_t)B * (m + 1) * nparts;
-  return n * (4 + 4 + 4 + 8 + 4) + 1024;
+  return n * (4 + 4 + 4 + 8 + 4) + (size_t)B * 4 + 1024;
 }
 
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
@@ -332,13 +377,12 @@ hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
   int* pa_id = (int*)(pa_v + n);
   float* pmax = (float*)(pa_id + n);
   int* pnan = (int*)(pmax + n);
+  unsigned* arrive = (unsigned*)(pnan + n);
   const double invT = mode == EAGLE3_SAMPLE ? 1.0 / (double)temperature : 1.0;
-  dim3 ga(nparts, B * (m + 1));
-  verify_rows_kernel<<<ga, VR_THREADS, 0, st>>>(V, nparts, logits, mode == EAGLE3_SAMPLE, invT, pa_v, pa_id,
-                                                pmax, psum, pnan);
-  verify_walk_kernel<<<B, VW_THREADS, 0, st>>>(m, V, Dmax, nparts, v_tok, v_parent, logits, mode, invT, u_try,
-                                               u_res, pa_v, pa_id, pmax, psum, pnan, accept_len, accepted,
-                                               bonus, status);
+  dim3 ga((nparts + VR_PARTS - 1) / VR_PARTS, B * (m + 1));
+  verify_kernel<<<ga, VW_THREADS, 0, st>>>(m, V, Dmax, nparts, v_tok, v_parent, logits, mode, invT, u_try, u_res,
+                                           pa_v, pa_id, pmax, psum, pnan, arrive, accept_len, accepted, bonus,
+                                           status);
   return hipGetLastError();
 }
 

@@ -83,7 +83,8 @@ class CycleBuffers:
         self.accepted = torch.empty(Bn, D, **i32)
         self.bonus = torch.empty(Bn, **i32)
         self.status = torch.empty(Bn, **i32)
-        self.vws = torch.empty(B.verify_workspace_size(Bn, m, s.vocab), dtype=torch.uint8, device=dv)
+        # zero-filled once: per-request arrival counters the library keeps at zero
+        self.vws = torch.zeros(B.verify_workspace_size(Bn, m, s.vocab), dtype=torch.uint8, device=dv)
         self.commit_logits = None
         self.round_logits = None
 

@@ -259,7 +259,9 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t *roo
  * padded), bonus [B], status [B] (0, or EAGLE3_ENUMERIC when a visited row
  * holds a NaN; -inf logits mean probability 0; every row needs one finite
  * logit).  A walk that reaches Dmax accepted nodes ends there as at a leaf.
- * ws: scratch of eagle3_verify_workspace_size bytes (no initialisation). */
+ * ws: eagle3_verify_workspace_size bytes, zero-filled once after allocation:
+ *   its last bytes hold per-request arrival counters that every call leaves
+ *   at zero (calls sharing a workspace must be ordered on one stream). */
 int eagle3_verify(int B, int m, int V, int Dmax, const int32_t *v_tok, const int32_t *v_parent,
                   const float *target_logits, int mode, float temperature, const double *u_try,
                   const double *u_res, int32_t *accept_len, int32_t *accepted, int32_t *bonus,

@@ -139,7 +139,7 @@ def _run_verify(Bn, m, V, tok, par, L, mode, T=1.0, ut=None, ur=None, Dmax=None)
     i32 = dict(dtype=torch.int32, device="cuda")
     al = torch.empty(Bn, **i32); acc = torch.empty(Bn, Dmax, **i32)
     bo = torch.empty(Bn, **i32); st = torch.empty(Bn, **i32)
-    vws = torch.empty(Bd.verify_workspace_size(Bn, m, V), dtype=torch.uint8, device="cuda")
+    vws = torch.zeros(Bd.verify_workspace_size(Bn, m, V), dtype=torch.uint8, device="cuda")
     Bd.eagle3_verify(Bn, m, V, Dmax, dev_i32(tok), dev_i32(par), torch.as_tensor(L).cuda(), mode, T,
                      torch.as_tensor(ut).cuda() if ut is not None else None,
                      torch.as_tensor(ur).cuda() if ur is not None else None, al, acc, bo, st, vws)
