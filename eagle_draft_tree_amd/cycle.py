@@ -62,7 +62,6 @@ class CycleBuffers:
         self.g = torch.empty(Bn * n, s.d, dtype=drafter.torch_dtype, device=dv)
         self.h_tree = torch.zeros(Bn, B.MAX_TREE_SLOTS + 1, s.d, dtype=torch.float32, device=dv)
         max_rows = max(n, k)
-        # zero-filled once: holds split-K counters the library keeps at zero
         self.ws = torch.zeros(B.workspace_size(drafter.dims, Bn, max_rows, spec.cap_rows), dtype=torch.uint8,
                               device=dv)
         self.root_ids = torch.empty(Bn, 1, k, **i32)

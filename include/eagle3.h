@@ -36,9 +36,11 @@
  *    gives a thread-local message for the most recent failure.
  *  - Calls that share a workspace or tree-state buffer must be ordered on
  *    one stream; concurrent calls on one buffer race.
- *  - Workspaces must be zero-filled once after allocation: their first
- *    bytes hold split-K arrival counters that every call leaves at zero.
- *    (Top-k arrival counters further in are cleared by each call itself.)
+ *  - Workspaces of eagle3_fuse / eagle3_draft_step / eagle3_topk / the TTT
+ *    forward need no initialisation (the top-k arrival counters are cleared
+ *    by each call itself).  The verify workspace must be zero-filled once
+ *    after allocation: it ends in per-request arrival counters that every
+ *    call leaves at zero.
  */
 #ifndef EAGLE3_H
 #define EAGLE3_H
@@ -156,7 +158,7 @@ const char *eagle3_version(void);
 /* Workspace bytes needed by eagle3_fuse / eagle3_draft_step / eagle3_topk for
  * batch B with at most max_rows query rows per request (fuse: n <= B*max_rows
  * feature rows).  Contiguous KV prefixes up to max_ctx rows (paged: the
- * largest logical length) are covered.  Zero-fill a new workspace once. */
+ * largest logical length) are covered.  No initialisation is needed. */
 int eagle3_workspace_size(const eagle3_dims *dims, int B, int max_rows, int max_ctx,
                           size_t *bytes);
 
@@ -171,8 +173,8 @@ int eagle3_ttt_workspace_size(const eagle3_dims *dims, int B, int S, int R, size
  *   g[i] = [f_low(i) ; f_mid(i) ; f_high(i)] . fc^T       (no bias, no norm)
  * feats [n][3][d] (dtype), g [n][d] (dtype; bf16 rounds once, RNE).
  * fp32 accumulation.  n >= 1, processed in 64-row chunks by the
- * weight-streaming kernel.  ws: a zero-initialised workspace (see
- * eagle3_workspace_size). */
+ * weight-streaming kernel.  ws: a workspace of eagle3_workspace_size
+ * bytes. */
 int eagle3_fuse(const eagle3_dims *dims, const eagle3_weights *w, const void *feats, int n,
                 void *g, void *ws, size_t ws_bytes, eagle3_stream_t stream);
 
