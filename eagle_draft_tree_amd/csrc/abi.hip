@@ -249,7 +249,7 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int
   e3::TimedScope ts(EAGLE3_KC_VERIFY, (hipStream_t)stream);
   return hip_status(e3::launch_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature,
                                       u_try, u_res, accept_len, accepted, bonus, status, ws,
-                                      (hipStream_t)stream),
+                                      ws_bytes, (hipStream_t)stream),
                     "eagle3_verify");
 }
 

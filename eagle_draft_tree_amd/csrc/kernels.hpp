@@ -51,6 +51,6 @@ hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
                          const int32_t* v_parent, const float* logits, int mode, float temperature,
                          const double* u_try, const double* u_res, int32_t* accept_len,
                          int32_t* accepted, int32_t* bonus, int32_t* status, void* ws,
-                         hipStream_t st);
+                         size_t ws_bytes, hipStream_t st);
 
 }  // namespace e3

@@ -357,19 +357,27 @@ __global__ __launch_bounds__(VW_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
               pnan, accept_len, accepted, bonus, status);
 }
 
-// Partials [B*(m+1)][nparts] (psum fp64, argmax value and id, max, NaN flag),
-// then B arrival counters at the end.
+// Partials [B*(m+1)][nparts] (psum fp64, argmax value and id, max, NaN flag)
+// from the start of the buffer; per-request arrival counters in its last
+// sixth, from byte verify_cnt_off(ws_bytes).  The counter region depends on
+// the buffer size alone, never on (B, m, V): calls of any shape that fit the
+// buffer keep their partials below it, and every call leaves the counters it
+// used at zero, so one zero fill serves every later call.
+static size_t verify_cnt_off(size_t ws_bytes) { return (ws_bytes / 6 * 5) & ~(size_t)255; }
+
 size_t verify_ws_bytes(int B, int m, int V) {
   const size_t nparts = (V + VR_PS - 1) / VR_PS;
   const size_t n = (size_t)B * (m + 1) * nparts;
-  return n * (4 + 4 + 4 + 8 + 4) + (size_t)B * 4 + 1024;
+  // S >= 1.2 (24 n + 1024) gives verify_cnt_off(S) >= 24 n, and S / 6 >= 4 B
+  // since n >= B.
+  return (n * (4 + 4 + 4 + 8 + 4) + 1024) * 6 / 5 + 1024;
 }
 
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
                          const int32_t* v_parent, const float* logits, int mode, float temperature,
                          const double* u_try, const double* u_res, int32_t* accept_len,
                          int32_t* accepted, int32_t* bonus, int32_t* status, void* ws,
-                         hipStream_t st) {
+                         size_t ws_bytes, hipStream_t st) {
   const int nparts = (V + VR_PS - 1) / VR_PS;
   const size_t n = (size_t)B * (m + 1) * nparts;
   double* psum = (double*)ws;
@@ -377,7 +385,7 @@ hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
   int* pa_id = (int*)(pa_v + n);
   float* pmax = (float*)(pa_id + n);
   int* pnan = (int*)(pmax + n);
-  unsigned* arrive = (unsigned*)(pnan + n);
+  unsigned* arrive = (unsigned*)((unsigned char*)ws + verify_cnt_off(ws_bytes));
   const double invT = mode == EAGLE3_SAMPLE ? 1.0 / (double)temperature : 1.0;
   dim3 ga((nparts + VR_PARTS - 1) / VR_PARTS, B * (m + 1));
   verify_kernel<<<ga, VW_THREADS, 0, st>>>(m, V, Dmax, nparts, v_tok, v_parent, logits, mode, invT, u_try, u_res,

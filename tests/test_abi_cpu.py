@@ -80,3 +80,19 @@ def test_call_validation_happens_before_launch(blib):
     assert lib.eagle3_tree_expand(7, 1, 2, 3, 4, *([None] * 14), None) == blib.EINVAL
     assert lib.eagle3_topk(None, 1, 10, 2, None, None, None, None, 0, None) == blib.EINVAL
     assert b"NULL" in lib.eagle3_last_error() or lib.eagle3_last_error() != b""
+
+
+def test_verify_workspace_layout(blib):
+    """The verify workspace keeps its arrival counters from byte
+    (ws_bytes / 6 * 5) & ~255 on: for every shape, a buffer of the queried
+    size holds that call's partials (24 bytes per row and 4096-wide vocab
+    slice) below the counter region and one 4-byte counter per request inside
+    it, and so does any larger buffer."""
+    for B in (1, 2, 3, 8, 64, 257, 1000):
+        for m in (0, 3, 12, 59, 63):
+            for V in (1, 100, 4096, 5000, 32000, 128256):
+                S = blib.verify_workspace_size(B, m, V)
+                n = B * (m + 1) * (-(-V // 4096))
+                for size in (S, S + 1, S + 255, 3 * S + 7):
+                    off = (size // 6 * 5) & ~255
+                    assert 24 * n <= off and off + 4 * B <= size, (B, m, V, size)

@@ -175,6 +175,38 @@ def test_verify(lib, V, m, depth, Bn, mode, T):
         assert bo[b] == rb
 
 
+def test_verify_reuses_its_workspace(lib):
+    """One zero-filled verify workspace serves consecutive calls of different
+    shapes (batch 8, then 3, then 8 again; greedy and sampling): the
+    per-request arrival counters that hand the partials to the tree walk are
+    left at zero by every call, so each call still matches the oracle."""
+    from eagle_draft_tree_amd import binding as Bd
+    V, m, depth = 5000, 12, 4
+    i32 = dict(dtype=torch.int32, device="cuda")
+    vws = torch.zeros(Bd.verify_workspace_size(8, m, V), dtype=torch.uint8, device="cuda")
+    for call, (Bn, mode) in enumerate([(8, "greedy"), (3, "sample"), (8, "sample"), (8, "greedy")]):
+        say("verify workspace reuse, call", call, Bn, mode)
+        toks, pars = zip(*[gen.random_verify_tree(100 * call + b, m, V, depth) for b in range(Bn)])
+        toks, pars = np.array(toks), np.array(pars)
+        L = gen.target_logits(50 + call, Bn, m + 1, V, 3.0)
+        gen.plant_agreement(L, toks, pars, np.full(Bn, 0.8), seed=50 + call)
+        ut, ur = gen.uniforms(50 + call, Bn, m + 1)
+        md = Bd.GREEDY if mode == "greedy" else Bd.SAMPLE
+        al = torch.empty(Bn, **i32); acc = torch.empty(Bn, m + 1, **i32)
+        bo = torch.empty(Bn, **i32); st = torch.empty(Bn, **i32)
+        Bd.eagle3_verify(Bn, m, V, m + 1, dev_i32(toks), dev_i32(pars), torch.as_tensor(L).cuda(), md, 1.0,
+                         torch.as_tensor(ut).cuda(), torch.as_tensor(ur).cuda(), al, acc, bo, st, vws)
+        torch.cuda.synchronize()
+        al, acc, bo, st = al.cpu().numpy(), acc.cpu().numpy(), bo.cpu().numpy(), st.cpu().numpy()
+        for b in range(Bn):
+            if mode == "greedy":
+                ra, rb = O.verify_greedy(toks[b], pars[b], L[b])
+            else:
+                ra, rb = O.verify_sample(toks[b], pars[b], L[b], ut[b], ur[b], 1.0)
+            assert st[b] == 0
+            assert al[b] == len(ra) and list(acc[b][: al[b]]) == ra and bo[b] == rb, (call, b)
+
+
 def test_verify_golden(lib):
     import json, os
     from eagle_draft_tree_amd import binding as Bd
