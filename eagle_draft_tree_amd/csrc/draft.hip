@@ -23,6 +23,7 @@
 #include "draft.hpp"
 #include "gemm_rows.hpp"
 #include "rows_dma.hpp"
+#include "rows_rx.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -330,6 +331,14 @@ struct EpiTop1Part {
   }
 };
 
+// LM head for 17..64 rows: weights straight into registers (rx_gemm_kernel),
+// four 16-row weight tiles per wave, so 16 tiles (256 vocabulary columns)
+// per workgroup.  The 8B batch-64 LM head streams 16 % faster this way than
+// through the LDS-copy skinny kernel (measured); the smaller layer GEMMs
+// keep the skinny kernel, which is faster on their few workgroups.
+constexpr int LM_RX_WT = 4, LM_RX_KU = 2;
+static inline bool lm_rx_ok(int R, int K, bool packed) { return sk_ok(R, K, packed) && K % (32 * LM_RX_KU) == 0; }
+
 // ---------------------------------------------------------------------------
 // rows-GEMM dispatch.  The epilogue sees rows 0..R-1 of one launch; row
 // chunks beyond 64 are launched separately with shifted pointers (no split).
@@ -427,7 +436,7 @@ struct DraftWS {
   void* y;
   float* logits;
   void* topk;  // not used by the draft step: keeps eagle3_topk covered for R rows
-  void* lmpart;  // LM-head partials: top-1 float4 [R][V/64], or tile float2 [R][V/16]
+  void* lmpart;  // LM-head partials: top-1 float4 [R][V/128 or V/256], or tile float2 [R][V/16 + pad]
 };
 
 static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* base, DraftWS* w) {
@@ -451,8 +460,9 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   t.y = bp.take((size_t)R * dm.d * es);
   t.logits = (float*)bp.take((size_t)R * dm.vocab * 4);
   t.topk = bp.take(topk_ws_bytes(R, dm.vocab));
-  // top-1 float4 [R][V/64] or tile pairs float2 [R][V/16 + up to 63 slots of padding]
-  t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 64) * sizeof(float2));
+  // top-1 float4 [R][one per workgroup of 8 or 16 tiles] or tile pairs
+  // float2 [R][V/16 + up to 8*tpw - 1 slots of padding, tpw <= 16]
+  t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 128) * sizeof(float2));
   if (w) *w = t;
   return bp.off + 256;
 }
@@ -657,14 +667,16 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   // workgroup (max, sum exp, argmax) partials instead of the logits
   if (c.k == 1 && !c.logits_out && bf && Rl <= 64 && sk_ok(Rl, d, pk)) {
     const int nt16 = V / 16;
-    const int bn = sk_bn(nt16, 1);
-    const int nwg = (nt16 + bn / 16 - 1) / (bn / 16);
+    const bool rx = lm_rx_ok(Rl, d, pk);
+    const int tpw = rx ? 4 * LM_RX_WT : sk_bn(nt16, 1) / 16;
+    const int nwg = (nt16 + tpw - 1) / tpw;
     {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
       EpiTop1Part epi{(float4*)ws.lmpart, nwg};
       const bf16* Xb = (const bf16*)ws.y;
       const bf16* Wb = (const bf16*)w.lm;
-      if (bn == 128) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+      if (rx) rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+      else if (tpw == 8) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
       else skinny_gemm_kernel<64, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -677,13 +689,21 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   if (Rl <= 64) {
     const int nt16 = V / 16;
     const RowsPlan pc = plan_rows(Rl, V, d, bf, false);
-    const int tpw = bf && sk_ok(Rl, d, pk) ? sk_bn(nt16, 1) / 16 : pc.t;  // tiles per workgroup, as dispatched
+    const bool rx = bf && lm_rx_ok(Rl, d, pk);
+    // tiles per workgroup, as dispatched
+    const int tpw = rx ? 4 * LM_RX_WT : bf && sk_ok(Rl, d, pk) ? sk_bn(nt16, 1) / 16 : pc.t;
     float2* tpart = (float2*)ws.lmpart;
     {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
       EpiLogitsTiles epi{logits, V, tpart, tile_slots(nt16, tpw)};
-      if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) != hipSuccess)
+      if (rx) {
+        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles><<<(nt16 + tpw - 1) / tpw, 256, 0, st>>>(
+            (const bf16*)ws.y, d, Rl, (const bf16*)w.lm, d, nt16, 1, epi);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      } else if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) !=
+                 hipSuccess) {
         return e;
+      }
     }
     TimedScope ts(EAGLE3_KC_TOPK, st);
     return launch_topk_tiles(logits, tpart, tpw, Rl, V, c.k, c.topk_id, c.topk_lp, st);
