@@ -7,14 +7,17 @@
 // remaining support, and a rejected token leaves the support -- the
 // residual max(p - q, 0) renormalised.
 //
-// One kernel, grid (partition pairs x requests * rows).  Every workgroup
+// One kernel, grid (partition groups x requests * rows).  Every workgroup
 // reduces two 4096-token partitions of one verify row: argmax (value
 // desc, id asc), NaN flag and, for sampling, the partition max and sum of
-// exp((L - max)/T) in fp64.  The last workgroup of a request to finish (a
-// per-request arrival counter, reset by that workgroup) walks the request's
+// exp((L - max)/T) in fp64.  The last workgroup of a request to finish
+// (arrival counters, each reset by its last arrival) walks the request's
 // tree on those partials; at the last node of a sampling walk it locates the
 // partition where the residual CDF crosses u_res * Rm and scans only that
-// partition.  The partials cross workgroups (and XCDs) through agent-scope
+// partition.  Arrival is counted in two levels, each counter on a 64-byte
+// line of its own: a row's workgroups count on the row's counter, and the
+// last of them on the request's counter (same-line atomics from hundreds
+// of workgroups serialise).  The partials cross workgroups (and XCDs) through agent-scope
 // stores and loads, each wave waiting for its stores before the barrier that
 // precedes the counter increment: no L2 write-back.
 #include <limits.h>
@@ -25,10 +28,12 @@
 namespace e3 {
 
 constexpr int VR_THREADS = 256;  // threads per partition
-constexpr int VR_PS = 4096;      // tokens per partition (16 per thread)
-constexpr int VR_PARTS = 4;      // partitions per workgroup
+constexpr int VR_EPT = 16;                   // tokens per thread (four 16-byte loads)
+constexpr int VR_PS = VR_THREADS * VR_EPT;  // tokens per partition
+constexpr int VR_PARTS = 2;      // partitions per workgroup
 constexpr int VW_THREADS = VR_THREADS * VR_PARTS;
 constexpr int VW_WAVES = VW_THREADS / 64;
+constexpr int VCNT_STRIDE = 16;  // uints between arrival counters (one 64-byte line each)
 
 template <typename X>
 __device__ __forceinline__ void st_dev(X* p, X v) {
@@ -55,7 +60,7 @@ __device__ __forceinline__ ArgRed wave_arg(ArgRed a) {
 
 // ---------------------------------------------------------------- the rows
 // A workgroup of VW_THREADS reduces VR_PARTS partitions of one row: part
-// sg (VR_THREADS threads, 16 tokens each) takes partition blockIdx.x *
+// sg (VR_THREADS threads, VR_EPT tokens each) takes partition blockIdx.x *
 // VR_PARTS + sg.  Every barrier is reached by all parts (a part past the
 // last partition reduces nothing).
 __device__ __forceinline__ void verify_rows(
@@ -70,10 +75,10 @@ __device__ __forceinline__ void verify_rows(
   const float* x = logits + row * V;
   const int lo = part * VR_PS;
   const int lane = lt & 63, w = lt >> 6;
-  float v[16];
+  float v[VR_EPT];
   const bool vec_ok = (V & 3) == 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < VR_EPT / 4; ++j) {
     const int y0 = lo + 4 * (lt + VR_THREADS * j);
     if (valid && vec_ok && y0 + 3 < V) {
       const float4 f = *(const float4*)(x + y0);
@@ -89,7 +94,7 @@ __device__ __forceinline__ void verify_rows(
   ArgRed best{-INFINITY, INT_MAX};
   int nan = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < VR_EPT; ++e) {
     const int y = lo + 4 * (lt + VR_THREADS * (e >> 2)) + (e & 3);
     if (v[e] != v[e]) nan = 1;
     else if (y < V && better(v[e], y, best.v, best.id)) best = ArgRed{v[e], y};
@@ -117,7 +122,7 @@ __device__ __forceinline__ void verify_rows(
     double s = 0.0;
     if (!anynan) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < VR_EPT; ++e) {
         const int y = lo + 4 * (lt + VR_THREADS * (e >> 2)) + (e & 3);
         if (y < V && v[e] > -INFINITY) s += exp(((double)v[e] - mx) * invT);
       }
@@ -337,19 +342,29 @@ __device__ void verify_walk(
   }
 }
 
-__global__ __launch_bounds__(VW_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void verify_kernel(
+__global__ __launch_bounds__(VW_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void verify_kernel(
     int m, int V, int Dmax, int nparts, const int32_t* __restrict__ v_tok, const int32_t* __restrict__ v_parent,
     const float* __restrict__ logits, int mode, double invT, const double* __restrict__ u_try,
     const double* __restrict__ u_res, float* pa_v, int* pa_id, float* pmax, double* psum, int* pnan,
     unsigned* arrive, int32_t* accept_len, int32_t* accepted, int32_t* bonus, int32_t* status) {
   verify_rows(V, nparts, logits, mode == EAGLE3_SAMPLE, invT, pa_v, pa_id, pmax, psum, pnan);
   __shared__ int last;
-  const int b = blockIdx.y / (m + 1);
+  const int row = blockIdx.y, b = row / (m + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    last = atomicAdd(&arrive[b], 1u) == (unsigned)(gridDim.x * (m + 1) - 1);
-    if (last) arrive[b] = 0u;  // every arrival has been counted: ready for the next call
+    // counters: row r at arrive[16 r], request b at arrive[16 (rows + b)]
+    unsigned* rc = arrive + (size_t)row * VCNT_STRIDE;
+    unsigned* qc = arrive + ((size_t)gridDim.y + b) * VCNT_STRIDE;
+    int l = 0;
+    if (atomicAdd(rc, 1u) == gridDim.x - 1) {
+      *rc = 0u;  // every arrival of the row has been counted: ready for the next call
+      if (atomicAdd(qc, 1u) == (unsigned)m) {
+        *qc = 0u;
+        l = 1;
+      }
+    }
+    last = l;
   }
   __syncthreads();
   if (!last) return;
@@ -358,8 +373,9 @@ __global__ __launch_bounds__(VW_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 }
 
 // Partials [B*(m+1)][nparts] (psum fp64, argmax value and id, max, NaN flag)
-// from the start of the buffer; per-request arrival counters in its last
-// sixth, from byte verify_cnt_off(ws_bytes).  The counter region depends on
+// from the start of the buffer; arrival counters (one per row, then one per
+// request, 64 bytes apart) in its last sixth, from byte
+// verify_cnt_off(ws_bytes).  The counter region depends on
 // the buffer size alone, never on (B, m, V): calls of any shape that fit the
 // buffer keep their partials below it, and every call leaves the counters it
 // used at zero, so one zero fill serves every later call.
@@ -368,9 +384,11 @@ static size_t verify_cnt_off(size_t ws_bytes) { return (ws_bytes / 6 * 5) & ~(si
 size_t verify_ws_bytes(int B, int m, int V) {
   const size_t nparts = (V + VR_PS - 1) / VR_PS;
   const size_t n = (size_t)B * (m + 1) * nparts;
-  // S >= 1.2 (24 n + 1024) gives verify_cnt_off(S) >= 24 n, and S / 6 >= 4 B
-  // since n >= B.
-  return (n * (4 + 4 + 4 + 8 + 4) + 1024) * 6 / 5 + 1024;
+  // S >= 1.2 (24 n + 1024) gives verify_cnt_off(S) >= 24 n; S >= 6 C + 1024
+  // leaves the counters' C bytes in the last sixth.
+  const size_t cnt = ((size_t)B * (m + 1) + B) * VCNT_STRIDE * 4;
+  const size_t s1 = (n * (4 + 4 + 4 + 8 + 4) + 1024) * 6 / 5 + 1024, s2 = 6 * cnt + 1024;
+  return s1 > s2 ? s1 : s2;
 }
 
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,

@@ -39,8 +39,8 @@
  *  - Workspaces of eagle3_fuse / eagle3_draft_step / eagle3_topk / the TTT
  *    forward need no initialisation (the top-k arrival counters are cleared
  *    by each call itself).  The verify workspace must be zero-filled once
- *    after allocation: its last sixth holds per-request arrival counters
- *    that every call leaves at zero.
+ *    after allocation: its last sixth holds arrival counters that every
+ *    call leaves at zero.
  */
 #ifndef EAGLE3_H
 #define EAGLE3_H
@@ -262,13 +262,13 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t *roo
  * holds a NaN; -inf logits mean probability 0; every row needs one finite
  * logit).  A walk that reaches Dmax accepted nodes ends there as at a leaf.
  * ws: at least eagle3_verify_workspace_size bytes, zero-filled once after
- *   allocation.  Partials fill it from the start; one 32-bit arrival counter
- *   per request lives from byte (ws_bytes / 6 * 5) rounded down to a
- *   multiple of 256, a place that depends on ws_bytes only.  Every call
- *   leaves the counters it used at zero, so calls of any (B, m, V) that fit
- *   may share one buffer as long as they pass the same ws_bytes and are
- *   ordered on one stream; passing another ws_bytes for the same buffer
- *   needs a new zero fill. */
+ *   allocation.  Partials fill it from the start; 32-bit arrival counters
+ *   (one per verify row, then one per request, 64 bytes apart) live from
+ *   byte (ws_bytes / 6 * 5) rounded down to a multiple of 256, a place that
+ *   depends on ws_bytes only.  Every call leaves the counters it used at
+ *   zero, so calls of any (B, m, V) that fit may share one buffer as long as
+ *   they pass the same ws_bytes and are ordered on one stream; passing
+ *   another ws_bytes for the same buffer needs a new zero fill. */
 int eagle3_verify(int B, int m, int V, int Dmax, const int32_t *v_tok, const int32_t *v_parent,
                   const float *target_logits, int mode, float temperature, const double *u_try,
                   const double *u_res, int32_t *accept_len, int32_t *accepted, int32_t *bonus,

@@ -86,8 +86,9 @@ def test_verify_workspace_layout(blib):
     """The verify workspace keeps its arrival counters from byte
     (ws_bytes / 6 * 5) & ~255 on: for every shape, a buffer of the queried
     size holds that call's partials (24 bytes per row and 4096-wide vocab
-    slice) below the counter region and one 4-byte counter per request inside
-    it, and so does any larger buffer."""
+    slice) below the counter region and its counters inside it (one per
+    verify row and one per request, 64 bytes apart), and so does any larger
+    buffer."""
     for B in (1, 2, 3, 8, 64, 257, 1000):
         for m in (0, 3, 12, 59, 63):
             for V in (1, 100, 4096, 5000, 32000, 128256):
@@ -95,4 +96,4 @@ def test_verify_workspace_layout(blib):
                 n = B * (m + 1) * (-(-V // 4096))
                 for size in (S, S + 1, S + 255, 3 * S + 7):
                     off = (size // 6 * 5) & ~255
-                    assert 24 * n <= off and off + 4 * B <= size, (B, m, V, size)
+                    assert 24 * n <= off and off + 64 * (B * (m + 1) + B) <= size, (B, m, V, size)
