@@ -255,19 +255,19 @@ __global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// LM head with top-1 folded in (skinny GEMM, no split-K, logits not kept):
-// per X row and workgroup (its NB*16 vocabulary columns) write {max,
-// sum exp(x - max), lowest column holding the max}.  Thread t takes row t%64
-// and column quarter t/64 (a wave reads one LDS column slice of all rows:
-// conflict-free); the quarters meet in LDS and are combined in order.
+// LM head with top-1 folded in (no split-K, logits not kept): per X row and
+// workgroup (its NB*16 vocabulary columns) write {max, sum exp(x - max),
+// lowest column holding the max}.  Thread t takes row t%64 and column part
+// t/64 of blockDim/64 equal parts (a wave reads one LDS column slice of all
+// rows: conflict-free); the parts meet in LDS and are combined in order.
 struct EpiTop1Part {
   static constexpr bool kWhole = true;
   float4* part;  // [R][nwg]
   int nwg;
   __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float* scratch) const {
-    float4* red = (float4*)scratch;  // [4][64]
-    const int t = threadIdx.x, r = t & 63, q = t >> 6;
-    const int qw = NB * 4;  // columns per quarter
+    float4* red = (float4*)scratch;  // [blockDim/64][64]
+    const int t = threadIdx.x, r = t & 63, q = t >> 6, nq = blockDim.x >> 6;
+    const int qw = NB * 16 / nq;  // columns per part
     float mx = -INFINITY;
     int id = 0x7fffffff;
     float s = 0.f;
@@ -312,8 +312,7 @@ struct EpiTop1Part {
     if (q == 0 && r < R) {
       float gm = -INFINITY;
       int gi = 0x7fffffff;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < nq; ++u) {
         const float4 c = red[u * 64 + r];
         if (better(c.x, __float_as_int(c.z), gm, gi)) {
           gm = c.x;
@@ -321,8 +320,7 @@ struct EpiTop1Part {
         }
       }
       float gs = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < nq; ++u) {
         const float4 c = red[u * 64 + r];
         if (c.x > -INFINITY) gs += c.y * __expf(c.x - gm);
       }
@@ -332,11 +330,13 @@ struct EpiTop1Part {
 };
 
 // LM head for 17..64 rows: weights straight into registers (rx_gemm_kernel),
-// four 16-row weight tiles per wave, so 16 tiles (256 vocabulary columns)
-// per workgroup.  The 8B batch-64 LM head streams 16 % faster this way than
-// through the LDS-copy skinny kernel (measured); the smaller layer GEMMs
+// eight waves of four 16-row weight tiles, so 32 tiles (512 vocabulary
+// columns) per workgroup and one workgroup per CU.  The 8B batch-64 LM head
+// streams about 20 % faster this way than through the LDS-copy skinny kernel
+// (measured, 172 vs 215 us with partial stores); the smaller layer GEMMs
 // keep the skinny kernel, which is faster on their few workgroups.
-constexpr int LM_RX_WT = 4, LM_RX_KU = 2;
+constexpr int LM_RX_WT = 4, LM_RX_KU = 2, LM_RX_WAVES = 8;
+constexpr int LM_RX_TPW = LM_RX_WT * LM_RX_WAVES;  // tiles per workgroup
 static inline bool lm_rx_ok(int R, int K, bool packed) { return sk_ok(R, K, packed) && K % (32 * LM_RX_KU) == 0; }
 
 // ---------------------------------------------------------------------------
@@ -436,7 +436,7 @@ struct DraftWS {
   void* y;
   float* logits;
   void* topk;  // not used by the draft step: keeps eagle3_topk covered for R rows
-  void* lmpart;  // LM-head partials: top-1 float4 [R][V/128 or V/256], or tile float2 [R][V/16 + pad]
+  void* lmpart;  // LM-head partials: top-1 float4 [R][V/128 or V/512], or tile float2 [R][V/16 + pad]
 };
 
 static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* base, DraftWS* w) {
@@ -460,9 +460,9 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   t.y = bp.take((size_t)R * dm.d * es);
   t.logits = (float*)bp.take((size_t)R * dm.vocab * 4);
   t.topk = bp.take(topk_ws_bytes(R, dm.vocab));
-  // top-1 float4 [R][one per workgroup of 8 or 16 tiles] or tile pairs
-  // float2 [R][V/16 + up to 8*tpw - 1 slots of padding, tpw <= 16]
-  t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 128) * sizeof(float2));
+  // top-1 float4 [R][one per workgroup of 8 or 32 tiles] or tile pairs
+  // float2 [R][V/16 + up to 8*tpw - 1 slots of padding, tpw <= 32]
+  t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 256) * sizeof(float2));
   if (w) *w = t;
   return bp.off + 256;
 }
@@ -668,14 +668,16 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   if (c.k == 1 && !c.logits_out && bf && Rl <= 64 && sk_ok(Rl, d, pk)) {
     const int nt16 = V / 16;
     const bool rx = lm_rx_ok(Rl, d, pk);
-    const int tpw = rx ? 4 * LM_RX_WT : sk_bn(nt16, 1) / 16;
+    const int tpw = rx ? LM_RX_TPW : sk_bn(nt16, 1) / 16;
     const int nwg = (nt16 + tpw - 1) / tpw;
     {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
       EpiTop1Part epi{(float4*)ws.lmpart, nwg};
       const bf16* Xb = (const bf16*)ws.y;
       const bf16* Wb = (const bf16*)w.lm;
-      if (rx) rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+      if (rx)
+        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part, LM_RX_WAVES>
+            <<<nwg, LM_RX_WAVES * 64, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
       else if (tpw == 8) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
       else skinny_gemm_kernel<64, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -691,14 +693,15 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
     const RowsPlan pc = plan_rows(Rl, V, d, bf, false);
     const bool rx = bf && lm_rx_ok(Rl, d, pk);
     // tiles per workgroup, as dispatched
-    const int tpw = rx ? 4 * LM_RX_WT : bf && sk_ok(Rl, d, pk) ? sk_bn(nt16, 1) / 16 : pc.t;
+    const int tpw = rx ? LM_RX_TPW : bf && sk_ok(Rl, d, pk) ? sk_bn(nt16, 1) / 16 : pc.t;
     float2* tpart = (float2*)ws.lmpart;
     {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
       EpiLogitsTiles epi{logits, V, tpart, tile_slots(nt16, tpw)};
       if (rx) {
-        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles><<<(nt16 + tpw - 1) / tpw, 256, 0, st>>>(
-            (const bf16*)ws.y, d, Rl, (const bf16*)w.lm, d, nt16, 1, epi);
+        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>
+            <<<(nt16 + tpw - 1) / tpw, LM_RX_WAVES * 64, 0, st>>>((const bf16*)ws.y, d, Rl, (const bf16*)w.lm, d,
+                                                                   nt16, 1, epi);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       } else if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) !=
                  hipSuccess) {

@@ -2,8 +2,8 @@
 // Y[r, n] = sum_k X[r, k] W[n, k], X [R <= 64][K] bf16 row-major, W in
 // packed fragment order (eagle3_pack_weights).  Bound by the weight stream.
 //
-// Workgroup: 64 X rows x 64*WT weight rows, four waves, each owning WT
-// weight tiles of 16 rows.  Every weight fragment is read once, straight
+// Workgroup: 64 X rows x 16*WT*WAVES weight rows, WAVES waves, each owning
+// WT weight tiles of 16 rows.  Every weight fragment is read once, straight
 // from HBM into the MFMA operand registers (nontemporal loads: the path
 // that streams fastest); only the X operand, which every workgroup shares,
 // goes through LDS.  X is staged per chunk of KU k-steps (32 k each) by
@@ -11,20 +11,21 @@
 // the copies of chunk c+1 after computing chunk c, and they land (L2 hits)
 // while the weight loads of chunk c+1 are in flight.  Split-K partitions the k-steps per workgroup
 // as in the rows plan.  The epilogue interface is the skinny kernel's:
-// [16][RP] fp32 tiles (RP = 65), or the whole workgroup tile (EpiWhole).
+// [16][RP] fp32 tiles (RP = 65), or the whole workgroup tile (EpiWhole,
+// with 1 KB of LDS scratch per wave).
 #pragma once
 #include "rows_dma.hpp"
 
 namespace e3 {
 
-template <int WT, int KU, class Epi, bool PIPE = false>
-__global__ __launch_bounds__(256) void rx_gemm_kernel(const bf16* __restrict__ X, int ldx, int R,
+template <int WT, int KU, class Epi, int WAVES = 4>
+__global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restrict__ X, int ldx, int R,
                                                       const bf16* __restrict__ W, int K, int ntiles16,
                                                       int splits, Epi epi) {
-  constexpr int NB = 4 * WT;                // weight tiles per workgroup
+  constexpr int NB = WAVES * WT;            // weight tiles per workgroup
   constexpr int XCH_U4 = KU * 4 * 64;       // one X chunk: KU steps x 4 row groups x 1 KB
   constexpr int RP = 65;                    // padded epilogue tile rows
-  constexpr int TILE_U4 = (NB * 16 * RP * 4 + 4096 + 15) / 16;
+  constexpr int TILE_U4 = (NB * 16 * RP * 4 + WAVES * 1024 + 15) / 16;  // tile + 1 KB of scratch per wave
   constexpr int SMEM_U4 = 2 * XCH_U4 > TILE_U4 ? 2 * XCH_U4 : TILE_U4;
   __shared__ uint4 smem[SMEM_U4];
   float* tile = (float*)smem;  // after the k loop: [NB*16][RP]
@@ -35,15 +36,16 @@ __global__ __launch_bounds__(256) void rx_gemm_kernel(const bf16* __restrict__ X
   const int s0 = (int)((long)nsteps * split / splits), s1 = (int)((long)nsteps * (split + 1) / splits);
   const int nch = (s1 - s0) / KU;  // the host guarantees (s1 - s0) % KU == 0
 
-  // X copies: the wave copies row group `wave` of every step of a chunk
-  const int xrow = min(wave * 16 + (lane & 15), R - 1);
-  const bf16* xsrc = X + (size_t)xrow * ldx + 8 * (lane >> 4);
+  // X copies: fragment f = s * 4 + g (step s, row group g) of a chunk is
+  // copied by wave f % WAVES
   const uint32_t lds0 = lds_addr(smem);
   auto issue_x = [&](int c) {
     const uint32_t base = lds0 + (uint32_t)((c & 1) * XCH_U4 * 16);
-#pragma unroll
-    for (int s = 0; s < KU; ++s)
-      dma16(xsrc + (size_t)(s0 + c * KU + s) * 32, base + (uint32_t)((s * 4 + wave) * 1024));
+    for (int f = wave; f < KU * 4; f += WAVES) {
+      const int s = f >> 2, g = f & 3;
+      const int xrow = min(g * 16 + (lane & 15), R - 1);
+      dma16(X + (size_t)xrow * ldx + 8 * (lane >> 4) + (size_t)(s0 + c * KU + s) * 32, base + (uint32_t)(f * 1024));
+    }
   };
   // weight fragments: tile t16 = wgt*NB + wave*WT + j, lane's 16 bytes
   const bf16* wsrc[WT];
@@ -80,47 +82,17 @@ __global__ __launch_bounds__(256) void rx_gemm_kernel(const bf16* __restrict__ X
     }
   };
   if (nch > 0) issue_x(0);
-  if constexpr (!PIPE) {
-    for (int c = 0; c < nch; ++c) {
-      U4 wf[KU][WT];
-      load_w(c, wf);
-      // the X copies of chunk c were issued before these weight loads
-      bg_wait_copies<KU * WT>();
-      bg_barrier();  // chunk c is in LDS for every wave; chunk c-1 is no longer read
-      compute(c, wf);
-      // next chunk's X, into the buffer every wave left before the barrier
-      // above; issued after this chunk's weight waits so that the compiler's
-      // vmcnt counts for its own loads stay exact
-      if (c + 1 < nch) issue_x(c + 1);
-    }
-  } else {
-    // weight registers double-buffered: chunk c+1's loads are issued before
-    // chunk c is computed.  Order of a wave's loads: W(c), X(c), W(c+1),
-    // X(c+1), ... so waiting for all but the newest KU*WT leaves exactly
-    // W(c+1) in flight.
-    U4 wa[KU][WT], wb[KU][WT];
-    if (nch > 0) load_w(0, wa);
-    for (int c = 0; c < nch; c += 2) {
-      if (c + 1 < nch) {
-        load_w(c + 1, wb);
-        bg_wait_copies<KU * WT>();
-      } else {
-        bg_wait_copies<0>();
-      }
-      bg_barrier();
-      compute(c, wa);
-      if (c + 1 >= nch) break;
-      issue_x(c + 1);
-      if (c + 2 < nch) {
-        load_w(c + 2, wa);
-        bg_wait_copies<KU * WT>();
-      } else {
-        bg_wait_copies<0>();
-      }
-      bg_barrier();
-      compute(c + 1, wb);
-      if (c + 2 < nch) issue_x(c + 2);
-    }
+  for (int c = 0; c < nch; ++c) {
+    U4 wf[KU][WT];
+    load_w(c, wf);
+    // the X copies of chunk c were issued before these weight loads
+    bg_wait_copies<KU * WT>();
+    bg_barrier();  // chunk c is in LDS for every wave; chunk c-1 is no longer read
+    compute(c, wf);
+    // next chunk's X, into the buffer every wave left before the barrier
+    // above; issued after this chunk's weight waits so that the compiler's
+    // vmcnt counts for its own loads stay exact
+    if (c + 1 < nch) issue_x(c + 1);
   }
   bg_wait_copies<0>();
   __syncthreads();  // every wave is done with the X buffers

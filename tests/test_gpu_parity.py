@@ -334,7 +334,7 @@ def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
     and only the tiles that can hold one of the k best.  Its ids must be the
     k best of the kept logits (value desc, id asc) and its log-probabilities
     logit minus the logsumexp of the row.  Batch 1 (6 rows, 2 tiles per LM-head
-    workgroup) and batch 9 x 2 (18 rows: the register-weight GEMM, 16 tiles
+    workgroup) and batch 9 x 2 (18 rows: the register-weight GEMM, 32 tiles
     per workgroup, the last one partly past the vocabulary).  With a zero LM head every logit is 0 and all 2049 tiles
     reach the threshold, more than the candidate-tile list holds: the k-round
     argmax path must give ids 0..k-1 and lp = -log V."""
