@@ -9,10 +9,10 @@
 // goes through LDS.  X is staged per chunk of KU k-steps (32 k each) by
 // global -> LDS copies in fragment order, double-buffered: a wave issues
 // the copies of chunk c+1 after computing chunk c, and they land (L2 hits)
-// while the weight loads of chunk c+1 are in flight.  Split-K partitions the k-steps per workgroup
-// as in the rows plan.  The epilogue interface is the skinny kernel's:
-// [16][RP] fp32 tiles (RP = 65), or the whole workgroup tile (EpiWhole,
-// with 1 KB of LDS scratch per wave).
+// while the weight loads of chunk c+1 are in flight.  Split-K partitions
+// the k-steps per workgroup as in the rows plan.  The epilogue interface is
+// the skinny kernel's: [16][RP] fp32 tiles (RP = 65), or the whole
+// workgroup tile (EpiWhole, with 1 KB of LDS scratch per wave).
 #pragma once
 #include "rows_dma.hpp"
 
