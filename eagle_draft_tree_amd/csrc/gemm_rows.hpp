@@ -82,11 +82,13 @@ static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_spli
   // partial-sum pass.  More tiles than CUs (70B QKV, 320) keep the split.
   if (p.nt == 1 && p.tiles <= 256) s = 1;
   // more than 16 rows: eight splits, halved while a split would hold fewer
-  // than 16 k-steps of 32 (measured best on the 8B batch-64 QKV, O, down and
-  // fusion shapes; odd counts leave uneven k ranges)
+  // than 32 k-steps of 32 (measured on the 8B batch-64 shapes: QKV, down and
+  // fusion are fastest with eight splits; O streams as fast with four as
+  // with eight, and the norm kernel that adds its partials reads half as
+  // much; odd counts leave uneven k ranges)
   if (p.nt >= 2) {
     s = 8;
-    while (s > 1 && K / 32 / s < 16) s >>= 1;
+    while (s > 1 && K / 32 / s < 32) s >>= 1;
   }
   if (s < 1 || !allow_split || R > 64) s = 1;
   p.splits = s;
