@@ -51,54 +51,49 @@ __device__ __forceinline__ void add_partials(float (&v)[EPT_MAX], const float* _
   }
 }
 
+// x = [rms(emb[t]) * ge ; rms(s) * gs], S = s.  Workgroup (row, half):
+// half 0 normalises the token embedding, half 1 the state (and keeps its
+// fp32 copy); the two norms are independent, so each workgroup streams half
+// of the row's bytes.
 template <typename T>
 __global__ __launch_bounds__(RT) void prologue_kernel(
     const T* __restrict__ emb, const int32_t* __restrict__ tokens, const T* __restrict__ state,
     const float* __restrict__ h_tree, const int32_t* __restrict__ parent_slot, int mode, int rows,
     int d, const float* __restrict__ ge, const float* __restrict__ gs, float eps,
     float* __restrict__ S, T* __restrict__ x) {
-  __shared__ float red[RT / 64], red2[RT / 64];
-  const int r = blockIdx.x;
+  __shared__ float red[RT / 64];
+  const int r = blockIdx.x, half = blockIdx.y;
   const int b = r / rows;
-  const T* e = emb + (size_t)tokens[r] * d;
-  const float* hs = nullptr;
-  if (mode == EAGLE3_TREE) hs = h_tree + ((size_t)b * (EAGLE3_MAX_TREE_SLOTS + 1) + parent_slot[r]) * d;
-  float ev[EPT_MAX], sv[EPT_MAX];
+  float v[EPT_MAX];
+  if (half == 0) {
+    const T* e = emb + (size_t)tokens[r] * d;
 #pragma unroll
-  for (int j = 0; j < EPT_MAX; ++j) {
-    const int i = threadIdx.x + RT * j;
-    ev[j] = i < d ? Elem<T>::ld(e, i) : 0.f;
-    sv[j] = i < d ? (mode == EAGLE3_TREE ? hs[i] : Elem<T>::ld(state, (size_t)r * d + i)) : 0.f;
-  }
-  float se = 0.f, ss = 0.f;
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      v[j] = i < d ? Elem<T>::ld(e, i) : 0.f;
+    }
+  } else {
+    const float* hs = nullptr;
+    if (mode == EAGLE3_TREE) hs = h_tree + ((size_t)b * (EAGLE3_MAX_TREE_SLOTS + 1) + parent_slot[r]) * d;
 #pragma unroll
-  for (int j = 0; j < EPT_MAX; ++j) {
-    se = fmaf(ev[j], ev[j], se);
-    ss = fmaf(sv[j], sv[j], ss);
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      v[j] = i < d ? (mode == EAGLE3_TREE ? hs[i] : Elem<T>::ld(state, (size_t)r * d + i)) : 0.f;
+    }
   }
-  // both block sums through one LDS exchange, waves added in a fixed order
-  se = wave_sum(se);
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6] = se;
-    red2[threadIdx.x >> 6] = ss;
-  }
-  __syncthreads();
-  se = 0.f;
-  ss = 0.f;
-  for (int i = 0; i < RT / 64; ++i) {
-    se += red[i];
-    ss += red2[i];
-  }
-  const float ie = (float)(1.0 / sqrt((double)se / d + (double)eps));
-  const float is = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = block_sum(ss, red);
+  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+  const float* g = half == 0 ? ge : gs;
+  T* xo = x + (size_t)r * 2 * d + (size_t)half * d;
 #pragma unroll
   for (int j = 0; j < EPT_MAX; ++j) {
     const int i = threadIdx.x + RT * j;
     if (i < d) {
-      S[(size_t)r * d + i] = sv[j];
-      Elem<T>::st(x, (size_t)r * 2 * d + i, ev[j] * ie * ge[i]);
-      Elem<T>::st(x, (size_t)r * 2 * d + d + i, sv[j] * is * gs[i]);
+      if (half == 1) S[(size_t)r * d + i] = v[j];
+      Elem<T>::st(xo, i, v[j] * inv * g[i]);
     }
   }
 }
@@ -531,8 +526,9 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   const int Rl = topk_last ? c.B : R;  // rows through the LM head and top-k
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
-    prologue_kernel<T><<<R, RT, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree, c.parent_slot,
-                                         c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps, ws.S, (T*)ws.x);
+    prologue_kernel<T><<<dim3(R, 2), RT, 0, st>>>((const T*)w.emb, c.tokens, (const T*)c.state, c.h_tree,
+                                                  c.parent_slot, c.mode, c.rows, d, w.norm_e, w.norm_s, dm.rms_eps,
+                                                  ws.S, (T*)ws.x);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
