@@ -652,6 +652,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
 // workgroup per (row, head): wave 0 computes the partials' weights
 // exp(m_c - M) (lanes over partials) and L; wave w then sums the weighted
 // partial vectors c = w, w+4, ... and the four sums are added in wave order.
+// Each wave's first partial vectors are loaded before the weights, so the
+// two loads share one round trip.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int nchunks, int hq,
@@ -663,6 +665,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   __shared__ float sL;
   const size_t rh = blockIdx.x;  // row*hq + h
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // every wave's first PRE partial vectors (c = w, w+4, ...) are loaded
+  // before the weights are known, so their round trip overlaps wave 0's
+  const float* po = part_o + rh * nchunks * HD;
+  constexpr int PRE = 5;
+  float pv[PRE][EPL];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int c = w + 4 * u;
+      pv[u][j] = c < nchunks ? po[(size_t)c * HD + lane + 64 * j] : 0.f;
+    }
   if (w == 0) {
     const float* ml = part_ml + 2 * rh * nchunks;
     float mloc = -INFINITY;
@@ -679,11 +693,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     if (lane == 0) sL = L;
   }
   __syncthreads();
+  // partials in the order c = w, w+4, w+8, ...
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  const float* po = part_o + rh * nchunks * HD;
-  int c = w;
+#pragma unroll
+  for (int u = 0; u < PRE; ++u) {
+    const int c = w + 4 * u;
+    if (c < nchunks)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) acc[j] = fmaf(pv[u][j], wc[c], acc[j]);
+  }
+  int c = w + 4 * PRE;
   for (; c + 12 < nchunks; c += 16) {
     float v[4][EPL];
 #pragma unroll
