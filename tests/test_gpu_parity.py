@@ -327,7 +327,8 @@ def test_bf16_small_paged_cycle(lib, bs):
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
 
 
-@pytest.mark.parametrize("batch,k,zero_lm", [(1, 6, False), (1, 6, True), (9, 2, False), (9, 2, True)])
+@pytest.mark.parametrize("batch,k,zero_lm", [(1, 6, False), (1, 6, True), (9, 2, False), (9, 2, True), (16, 4, False),
+                                             (21, 3, False)])
 def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
     """Up to 64 rows per step: the LM head writes each 16-column tile's
     {max, sum exp} per row beside the logits, and the top-k reads those pairs
@@ -335,7 +336,8 @@ def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
     k best of the kept logits (value desc, id asc) and its log-probabilities
     logit minus the logsumexp of the row.  Batch 1 (6 rows, 2 tiles per LM-head
     workgroup) and batch 9 x 2 (18 rows: the register-weight GEMM, 32 tiles
-    per workgroup, the last one partly past the vocabulary).  With a zero LM head every logit is 0 and all 2049 tiles
+    per workgroup, the last one partly past the vocabulary); tree rounds of
+    16 x 4 = 64 rows (the most one launch takes) and 21 x 3 = 63 rows.  With a zero LM head every logit is 0 and all 2049 tiles
     reach the threshold, more than the candidate-tile list holds: the k-round
     argmax path must give ids 0..k-1 and lp = -log V."""
     say("tile top-k, batch", batch, "k", k, "zero LM head" if zero_lm else "random LM head")
