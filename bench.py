@@ -184,6 +184,18 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         graphs[(steps - 1) % n_plant].replay()
         torch.cuda.synchronize()
         assert np.array_equal(buf.accept_len.cpu().numpy().astype(np.float64), accepted[(steps - 1) % n_plant])
+        # per-cycle spread, in a pass of its own (one event between replays),
+        # so that the rate above stays an uninterrupted loop
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
+        for i in range(steps):
+            graphs[i % n_plant].replay()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per_cycle = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+        cycle_pct = {"p10": round(float(np.percentile(per_cycle, 10)), 4),
+                     "median": round(float(np.median(per_cycle)), 4),
+                     "p90": round(float(np.percentile(per_cycle, 90)), 4)}
         del graphs
         # the cycle's D draft steps alone (COMMIT + D-1 TREE rounds), replayed on
         # the inputs the last cycle left in place
@@ -213,20 +225,17 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
     rows = [Bn] + [Bn * k] * (D - 1)
 
     def lm_out_bytes(r):
+        # tiles per LM-head workgroup: 2 up to 16 rows (rows GEMM), 32 for 17..64
+        # rows (register-weight GEMM, model width a multiple of 64)
+        nt16 = V // 16
+        tpw = 2 if r <= 16 else 32
         # top-1 on 17..64 rows without kept logits: the LM head writes per-workgroup
-        # (max, sum exp, argmax) partials (16 B per row per 128 or 64 vocabulary rows)
-        # instead of fp32 logits
+        # (max, sum exp, argmax) partials (16 B per row) instead of fp32 logits
         if k == 1 and 16 < r <= 64:
-            nwg = -(-(V // 16) // 8)
-            if nwg < 192:
-                nwg = -(-(V // 16) // 4)
-            return r * nwg * 16
+            return r * -(-nt16 // tpw) * 16
         out = r * V * 4
         if r <= 64:
-            # plus each 16-column tile's (max, sum exp) per row, 8 B, in slots grouped
-            # by XCD (tpw tiles per workgroup: 2 up to 16 rows, 8 for the skinny GEMM)
-            nt16 = V // 16
-            tpw = 2 if r <= 16 else 8
+            # plus each 16-column tile's (max, sum exp) per row, 8 B, in slots grouped by XCD
             out += r * 8 * tpw * -(-(-(-nt16 // tpw)) // 8) * 8
         return out
 
@@ -258,6 +267,7 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         "kernel_ms_per_cycle": {kk: round(v[0] / steps, 4) for kk, v in per_class.items()},
     }
     if graph:
+        res["cycle_ms_percentiles"] = cycle_pct
         gbs = bytes_steps / (ms_steps * 1e-3) / 1e9
         res["draft_step_roofline"] = {"steps": D, "bytes_per_step": round(bytes_steps / D),
                                       "us_per_step": round(ms_steps * 1e3 / D, 2), "achieved_GBs": round(gbs, 1),
@@ -413,6 +423,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": lm["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": lm["hbm_frac"], "traffic": traffic, "kernel": "lm_head rows GEMM",
                      "bytes_per_launch": lm["bytes_per_launch"], "avg_launch_us": lm["avg_launch_us"]},
+        "cycle_ms_percentiles": r.get("cycle_ms_percentiles"),
         "cycle_roofline": r["cycle_roofline"],
         "draft_step_roofline": r.get("draft_step_roofline"),
         "kernel_ms_per_cycle": r["kernel_ms_per_cycle"],
