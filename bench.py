@@ -62,12 +62,15 @@ def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
     import numpy as np
 
     from oracle import eagle3_oracle as O
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    np.dot(np.ones((64, 64)), np.ones((64, 64)))  # loads the BLAS, so that its thread pool can be read
     try:
         from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+        pools = threadpool_info()
+        threads = max(int(i.get("num_threads", 1)) for i in pools) if pools else 1
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)" for i in pools)
     except Exception:
-        threads = os.cpu_count() or 1
-    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+        threads, blas = os.cpu_count() or 1, "unknown"
     n = w.commit_rows
     Kc = ci.kv_k.f32()[0].astype(np.float64)
     Vc = ci.kv_v.f32()[0].astype(np.float64)
@@ -82,7 +85,7 @@ def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
     return {"value": 1.0 / dt, "unit": "draft-tree steps/s", "cores": threads, "kind": "oracle",
             "sample": f"one full cycle (fuse + commit + {w.depth - 1} tree rounds + rerank) of request 0, "
                       f"fp64 NumPy, {dt:.1f} s; cpu_count={os.cpu_count()}, "
-                      f"affinity={len(os.sched_getaffinity(0))}, {model}"}
+                      f"affinity={len(os.sched_getaffinity(0))}, {model}; BLAS: {blas or 'none detected'}"}
 
 
 def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
