@@ -327,6 +327,21 @@ def test_bf16_small_paged_cycle(lib, bs):
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
 
 
+def test_bf16_paged_cycle_more_than_64_rows(lib):
+    """Tree rounds of 12 requests x 6 frontier rows = 72 query rows per draft
+    step: the layer GEMMs run in 64-row chunks and the LM head keeps its
+    logits for the partition top-k.  Every stage against the oracle (up to
+    two requests excused by a near-tie in the oracle's own logits)."""
+    say("bf16 paged cycle, 72 rows per tree round")
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
+    w = scaled(C3_8B_CHAIN, shape=shape, batch=12, depth=3, topk=6, keep=12, prefix=90, prefix_range=(10, 90),
+               block_size=16, feat_scale=1.0)
+    Wt, W, ci = cycle_and_oracle(w, seed=13)
+    gc = GpuCycle(w, Wt, ci, pack=True)
+    gc.run()
+    assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 2
+
+
 @pytest.mark.parametrize("batch,k,zero_lm", [(1, 6, False), (1, 6, True), (9, 2, False), (9, 2, True), (16, 4, False),
                                              (21, 3, False)])
 def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
