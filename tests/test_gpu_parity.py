@@ -342,9 +342,10 @@ def test_bf16_paged_cycle_more_than_64_rows(lib):
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 2
 
 
-@pytest.mark.parametrize("batch,k,zero_lm", [(1, 6, False), (1, 6, True), (9, 2, False), (9, 2, True), (16, 4, False),
-                                             (21, 3, False)])
-def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
+@pytest.mark.parametrize("batch,k,zero_lm,d", [(1, 6, False, 256), (1, 6, True, 256), (9, 2, False, 256),
+                                               (9, 2, True, 256), (16, 4, False, 256), (21, 3, False, 256),
+                                               (9, 2, False, 288)])
+def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm, d):
     """Up to 64 rows per step: the LM head writes each 16-column tile's
     {max, sum exp} per row beside the logits, and the top-k reads those pairs
     and only the tiles that can hold one of the k best.  Its ids must be the
@@ -352,11 +353,12 @@ def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
     logit minus the logsumexp of the row.  Batch 1 (6 rows, 2 tiles per LM-head
     workgroup) and batch 9 x 2 (18 rows: the register-weight GEMM, 32 tiles
     per workgroup, the last one partly past the vocabulary); tree rounds of
-    16 x 4 = 64 rows (the most one launch takes) and 21 x 3 = 63 rows.  With a zero LM head every logit is 0 and all 2049 tiles
+    16 x 4 = 64 rows (the most one launch takes) and 21 x 3 = 63 rows.  Model
+    width 288 (not a multiple of 64) takes the skinny GEMM at 18 rows.  With a zero LM head every logit is 0 and all 2049 tiles
     reach the threshold, more than the candidate-tile list holds: the k-round
     argmax path must give ids 0..k-1 and lp = -log V."""
-    say("tile top-k, batch", batch, "k", k, "zero LM head" if zero_lm else "random LM head")
-    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=32784, dtype=BF16, theta=500000.0)
+    say("tile top-k, batch", batch, "k", k, "d", d, "zero LM head" if zero_lm else "random LM head")
+    shape = tiny_shape(d=d, hq=4, hkv=2, hd=64, ffn=512, vocab=32784, dtype=BF16, theta=500000.0)
     w = scaled(C1_TINY, shape=shape, batch=batch, depth=3, topk=k, keep=2 * k, prefix=40, commit_rows=3,
                synthetic_prefix_kv=True, feat_scale=1.0)
     Wt = gen.gen_weights(shape, seed=11)
@@ -385,14 +387,16 @@ def test_tile_topk_matches_kept_logits(lib, batch, k, zero_lm):
                 np.testing.assert_array_equal(ids[r], np.arange(k))
 
 
-def test_top1_lm_head_without_logits_matches_logits_path(lib):
+@pytest.mark.parametrize("d", [256, 288])
+def test_top1_lm_head_without_logits_matches_logits_path(lib, d):
     """Top-1 drafting (k = 1) with more than 16 rows per step and no kept
     logits: the LM head reduces its columns to per-workgroup (max, sum exp,
     argmax) partials instead of writing logits.  The top-1 ids equal the
     kept-logits path bit for bit (same GEMM arithmetic) and are the argmax of
     those logits (lowest id on ties); log-probabilities agree to fp32
-    rounding; the tree is identical."""
-    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=4112, dtype=BF16, theta=500000.0)
+    rounding; the tree is identical.  Model width 256 takes the
+    register-weight GEMM; 288 (not a multiple of 64) the skinny GEMM."""
+    shape = tiny_shape(d=d, hq=4, hkv=2, hd=64, ffn=512, vocab=4112, dtype=BF16, theta=500000.0)
     w = scaled(C3_8B_CHAIN, shape=shape, batch=20, depth=3, topk=1, keep=2, prefix=90, prefix_range=(10, 90),
                block_size=16, feat_scale=1.0)
     say("top-1 LM head without logits, batch", w.batch)
