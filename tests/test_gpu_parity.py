@@ -327,6 +327,21 @@ def test_bf16_small_paged_cycle(lib, bs):
     assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
 
 
+def test_bf16_paged_cycle_table_load_per_key(lib):
+    """Paged KV with one token per block and prefixes of 18000-20000 tokens:
+    a wave's run of keys spans more than 64 blocks, so the attention reads the
+    block table once per key instead of from lanes.  Every stage against the
+    oracle."""
+    say("bf16 paged cycle, block size 1, 20k-token prefixes")
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=2048, dtype=BF16, theta=500000.0)
+    w = scaled(C3_8B_CHAIN, shape=shape, batch=2, depth=3, topk=2, keep=4, prefix=20000,
+               prefix_range=(18000, 20000), block_size=1, feat_scale=1.0)
+    Wt, W, ci = cycle_and_oracle(w, seed=17)
+    gc = GpuCycle(w, Wt, ci, pack=True)
+    gc.run()
+    assert compare_cycle(gc, w, W, ci, TOL_BF16) <= 1
+
+
 def test_bf16_paged_cycle_more_than_64_rows(lib):
     """Tree rounds of 12 requests x 6 frontier rows = 72 query rows per draft
     step: the layer GEMMs run in 64-row chunks and the LM head keeps its
