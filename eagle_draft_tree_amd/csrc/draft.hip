@@ -259,7 +259,8 @@ struct EpiTop1Part {
   static constexpr bool kWhole = true;
   float4* part;  // [R][nwg]
   int nwg;
-  __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float* scratch) const {
+  __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float* scratch,
+                        int) const {
     float4* red = (float4*)scratch;  // [blockDim/64][64]
     const int t = threadIdx.x, r = t & 63, q = t >> 6, nq = blockDim.x >> 6;
     const int qw = NB * 16 / nq;  // columns per part
@@ -356,6 +357,17 @@ static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int
 template <typename TW, class Epi>
 static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
                             const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
+  if constexpr (std::is_same<Epi, EpiPartial>::value) {
+    // split-K layer GEMMs of 17..64 rows: weights streamed into registers
+    if (sizeof(TW) == 2 && sk_ok(R, K, packed) && p.splits > 1 && p.splits == rx_splits(K)) {
+      constexpr int WT = 2, WAVES = 4, NB = WT * WAVES;
+      const int nt16 = N / 16;
+      const int grid = (nt16 + NB - 1) / NB * p.splits;
+      rx_gemm_kernel<WT, RX_SPLIT_KU, Epi, WAVES><<<grid, WAVES * 64, 0, st>>>(
+          (const bf16*)X, ldx, R, (const bf16*)W, K, nt16, p.splits, epi);
+      return hipGetLastError();
+    }
+  }
   if (sizeof(TW) == 2 && sk_ok(R, K, packed)) {
     const int nt16 = N / 16;
     const int bn = sk_bn(nt16, p.splits);
@@ -410,8 +422,10 @@ static size_t max_partials(const eagle3_dims& dm, int R) {
   const Shapes sh = shapes_of(dm);
   size_t m = 0;
   for (int i = 0; i < 6; ++i) {
-    const size_t f = rows_partial_floats(plan_rows(R, sh.n[i], sh.k[i], bf, sh.split[i]), R, sh.n[i]);
-    if (f > m) m = f;
+    for (int pk = 0; pk < 2; ++pk) {
+      const size_t f = rows_partial_floats(plan_rows(R, sh.n[i], sh.k[i], bf, sh.split[i], pk), R, sh.n[i]);
+      if (f > m) m = f;
+    }
   }
   return m;
 }
@@ -478,7 +492,7 @@ static hipError_t fuse_impl(const eagle3_dims& dm, const eagle3_weights& w, cons
   RowMap map{MAP_PLAIN, dm.head_dim, dm.ffn};
   const bool pk = w.layout == EAGLE3_LAYOUT_PACKED;
   TimedScope ts(EAGLE3_KC_FUSE, st);
-  const RowsPlan p = plan_rows(n, dm.d, K, sizeof(T) == 2, true);
+  const RowsPlan p = plan_rows(n, dm.d, K, sizeof(T) == 2, true, pk);
   if (p.splits > 1) {  // n <= 64
     EpiPartial epi{(float*)ws, dm.d, map};
     hipError_t e = rows_gemm<T>((const T*)feats, K, n, (const T*)w.fc, K, dm.d, map, epi, p, pk, st);
@@ -538,7 +552,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
              c.rows, c.mode, c.slot_base, hkv, hd, 0};
   {
     TimedScope ts(EAGLE3_KC_QKV, st);
-    const RowsPlan p = plan_rows(R, nqkv, 2 * d, bf, true);
+    const RowsPlan p = plan_rows(R, nqkv, 2 * d, bf, true, pk);
     if (p.splits > 1) {
       EpiPartial epi{ws.part, nqkv, pair_head};
       if ((e = rows_gemm<T>((const T*)ws.x, 2 * d, R, (const T*)w.qkv, 2 * d, nqkv, pair_head, epi, p, pk, st)) !=
@@ -597,7 +611,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   int o_splits = 0;
   {
     TimedScope ts(EAGLE3_KC_O, st);
-    const RowsPlan p = plan_rows(R, d, qd, bf, true);
+    const RowsPlan p = plan_rows(R, d, qd, bf, true, pk);
     if (p.splits > 1) {
       EpiPartial epi{ws.part, d, plain};
       if ((e = rows_gemm<T>((const T*)ws.a, qd, R, (const T*)w.o, qd, d, plain, epi, p, pk, st)) != hipSuccess) return e;
@@ -635,7 +649,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   int down_splits = 0;
   {
     TimedScope ts(EAGLE3_KC_DOWN, st);
-    const RowsPlan p = plan_rows(R, d, F, bf, true);
+    const RowsPlan p = plan_rows(R, d, F, bf, true, pk);
     if (p.splits > 1) {
       EpiPartial epi{ws.part, d, plain};
       if ((e = rows_gemm<T>((const T*)ws.z, F, R, (const T*)w.down, F, d, plain, epi, p, pk, st)) != hipSuccess) return e;

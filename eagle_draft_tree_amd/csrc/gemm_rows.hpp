@@ -53,7 +53,22 @@ struct RowsPlan {
   int nt, t, u, waves, splits, tiles;
 };
 
-static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_split = true) {
+// k-steps of 32 per chunk of the register-weight kernel for 17..64 rows
+// (rows_rx.hpp) when it runs the split-K layer GEMMs
+constexpr int RX_SPLIT_KU = 4;
+
+// Splits for the register-weight kernel: 8, or 16 past 256 k-steps (8B
+// drafter, batch 64, cold weights: QKV and O fastest at 8, down and fusion
+// at 16), halved until every split holds whole chunks; 0 if none does.
+static inline int rx_splits(int K) {
+  if (K % 32) return 0;
+  const int ns = K / 32;
+  int s = ns > 256 ? 16 : 8;
+  while (s > 1 && (ns % s || (ns / s) % RX_SPLIT_KU)) s >>= 1;
+  return s > 1 ? s : 0;
+}
+
+static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_split = true, bool packed = false) {
   RowsPlan p;
   p.waves = 4;
   p.nt = (R + 15) / 16;
@@ -89,6 +104,8 @@ static inline RowsPlan plan_rows(int R, int N, int K, bool bf16, bool allow_spli
   if (p.nt >= 2) {
     s = 8;
     while (s > 1 && K / 32 / s < 32) s >>= 1;
+    // packed weights, up to 64 rows: the register-weight kernel's splits
+    if (packed && R <= 64 && rx_splits(K) > 0) s = rx_splits(K);
   }
   if (s < 1 || !allow_split || R > 64) s = 1;
   p.splits = s;
@@ -375,6 +392,27 @@ struct EpiPartial {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int r = e / 16, m = e - r * 16;
       out[(size_t)r * N + map(tile16, m)] = tile[m * RP + r];
+    }
+  }
+  // The kernels of 17..64 rows hand over the whole workgroup tile: a thread
+  // task (row r, tile t, half h) stores the 8 consecutive output columns
+  // map(t16, 8h) .. +7 as two 16-byte stores, so that a row's columns leave
+  // in runs of whole 32-byte sectors instead of 4-byte scatters (the
+  // epilogue of the split-K layer GEMMs is about twice as fast, measured).
+  // Every map keeps rows 8h..8h+7 of a tile on consecutive columns.
+  static constexpr bool kWhole = true;
+  __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float*, int split) const {
+    float* out = part + (size_t)split * R * N;
+    for (int e = threadIdx.x; e < R * NB * 2; e += blockDim.x) {
+      const int r = e / (NB * 2), q = e - r * (NB * 2), t = q >> 1, h = q & 1;
+      const int t16 = wg * NB + t;
+      if (t16 >= ntiles16) continue;
+      const float* src = tile + (t * 16 + h * 8) * RP + r;
+      const float4 a = make_float4(src[0], src[RP], src[2 * RP], src[3 * RP]);
+      const float4 b = make_float4(src[4 * RP], src[5 * RP], src[6 * RP], src[7 * RP]);
+      float4* dst = (float4*)(out + (size_t)r * N + map(t16, h * 8));
+      dst[0] = a;
+      dst[1] = b;
     }
   }
 };

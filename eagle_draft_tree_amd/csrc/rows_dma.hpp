@@ -22,8 +22,8 @@ namespace e3 {
 constexpr int SK_NSTAGE = 6;
 
 // An epilogue that defines kWhole = true receives the workgroup's whole tile
-// (whole(wg, tile, RP, R, NB, ntiles16, scratch)) instead of one call per
-// 16-row weight tile.  Used without split-K only.
+// (whole(wg, tile, RP, R, NB, ntiles16, scratch, split)) instead of one call
+// per 16-row weight tile.
 template <class E, class = void>
 struct EpiWhole {
   static constexpr bool value = false;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const bf16* __restrict
   if constexpr (EpiWhole<Epi>::value) {
     // whole-workgroup epilogue: all NB*16 weight rows at once, with the LDS
     // past the tile as scratch
-    epi.whole(wgt, tile, RP, R, NB, ntiles16, tile + NB * 16 * RP);
+    epi.whole(wgt, tile, RP, R, NB, ntiles16, tile + NB * 16 * RP, split);
   } else {
     for (int t = 0; t < NB; ++t) {
       const int t16 = wgt * NB + t;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restr
       for (int e = 0; e < 4; ++e) tile[((wave * WT + j) * 16 + m) * RP + g * 16 + q4 * 4 + e] = acc[g][j][e];
   __syncthreads();
   if constexpr (EpiWhole<Epi>::value) {
-    epi.whole(wgt, tile, RP, R, NB, ntiles16, tile + NB * 16 * RP);
+    epi.whole(wgt, tile, RP, R, NB, ntiles16, tile + NB * 16 * RP, split);
   } else {
     for (int t = 0; t < NB; ++t) {
       const int t16 = wgt * NB + t;
