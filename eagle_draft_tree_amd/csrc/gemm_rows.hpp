@@ -445,6 +445,36 @@ struct EpiSwiGLU {
       Elem<TO>::st(z, (size_t)r * ffn + tile16 * 8 + m, s * u);
     }
   }
+  // The kernels of 17..64 rows hand over the whole workgroup tile: a thread
+  // task (row r, tile t) computes the tile's 8 outputs of row r (the same
+  // arithmetic as above) and stores them together, one 16-byte store for
+  // bf16 (ffn is a multiple of 32, so every run is aligned).
+  static constexpr bool kWhole = true;
+  __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float*, int) const {
+    for (int e = threadIdx.x; e < R * NB; e += blockDim.x) {
+      const int r = e / NB, t = e - r * NB;
+      const int t16 = wg * NB + t;
+      if (t16 >= ntiles16) continue;
+      const float* c = tile + t * 16 * RP + r;
+      float o[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float g = c[m * RP], u = c[(m + 8) * RP];
+        const float s = g / (1.f + expf(-g));
+        o[m] = s * u;
+      }
+      TO* dst = z + (size_t)r * ffn + t16 * 8;
+      if constexpr (sizeof(TO) == 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(o[2 * i]) | ((uint32_t)f2bf(o[2 * i + 1]) << 16);
+        *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        ((float4*)dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+        ((float4*)dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    }
+  }
 };
 
 // Where the k/v of query row r go (draft step): committed cache row
