@@ -53,6 +53,8 @@ int check_dims(const eagle3_dims* dm) {
           "d and ffn must be multiples of 32, vocab of 16");
   REQUIRE(dm->rms_eps >= 0.f && dm->rope_theta > 0.f, EAGLE3_EINVAL, "rms_eps/rope_theta");
   REQUIRE(dm->vocab <= 262144, EAGLE3_EUNSUPPORTED, "vocab %d > 262144", dm->vocab);
+  // the row kernels (prologue, RMSNorms) hold a row in 1024 threads x 8 elements
+  REQUIRE(dm->d <= 8192, EAGLE3_EUNSUPPORTED, "d %d > 8192", dm->d);
   return EAGLE3_OK;
 }
 

@@ -213,7 +213,7 @@ __device__ void verify_walk(
     const int nk = nacc < Dmax ? nkids_s : 0;  // a walk cut at Dmax ends as at a leaf
     if (mode == EAGLE3_GREEDY) {
       int next = -1;
-      for (int c = 0; c < nk; ++c)
+      for (int c = 0; c < nk && next < 0; ++c)  // the first matching child in sibling order
         if (tok[kids[c]] == best.id) next = kids[c];
       __syncthreads();
       if (next >= 0) {
@@ -313,7 +313,11 @@ __device__ void verify_walk(
         if (bonus_s != INT_MAX) {
           done = true;
         } else {
-          before += s;
+          // no crossing after all: continue from the total just scanned, the
+          // same sum the scan compared against, not the partition's estimate
+          double tot = 0.0;
+          for (int i = 0; i < VW_WAVES; ++i) tot += wsum[i];
+          before += tot;
         }
         __syncthreads();
       }

@@ -85,7 +85,8 @@ extern "C" {
 typedef void *eagle3_stream_t; /* hipStream_t */
 
 /* Drafter dimensions.  head_dim must be 64 or 128; n_q_heads a multiple of
- * n_kv_heads (q-head h reads KV head floor(h*n_kv_heads/n_q_heads)).  With
+ * n_kv_heads (q-head h reads KV head floor(h*n_kv_heads/n_q_heads)); d at
+ * most 8192 and vocab at most 262144 (EAGLE3_EUNSUPPORTED otherwise).  With
  * dtype BF16 every GEMM K (3d, 2d, n_q_heads*head_dim, ffn) must be a
  * multiple of 32 and d a multiple of 16; ffn a multiple of 8.  rms_eps is
  * the RMSNorm epsilon; rope_theta the rotary base (rotate-half form). */
@@ -250,7 +251,8 @@ int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t *roo
  * v_tok, v_parent [B][m+1] (canonical order as emitted by FINAL);
  * target_logits [B][m+1][V] float32 (row i = target logits after node i).
  * GREEDY: at each node t* = argmax (lowest id on ties); follow the child
- *   whose token is t*, else stop: bonus = t*.
+ *   whose token is t* (the first in sibling order if several are), else
+ *   stop: bonus = t*.
  * SAMPLE (temperature T > 0): float64 weights w(y) = exp((L-max)/T) and
  *   remaining mass Rm; child c (sibling order) is accepted iff u_try[c]*Rm <
  *   w(tok c), otherwise its token leaves the support (Rm -= w).  With no

@@ -201,13 +201,6 @@ def topk_logprobs(logits_row, k):
     return order, lp, lse
 
 
-def topk_margin(logits_row, k):
-    """Gap between the k-th and (k+1)-th largest float32 logit (tie sensitivity)."""
-    l32 = np.sort(np.asarray(logits_row, dtype=np.float64).astype(np.float32))[::-1]
-    gaps = l32[:k] - l32[1:k + 1]
-    return float(np.min(gaps)) if len(gaps) else float("inf")
-
-
 # --------------------------------------------------------------------------
 # step 3b: EAGLE-2 confidence-value dynamic tree ("EAGLE-3 精读" §2; EAGLE-4
 # blog 几条技术路线正在收敛: confidence is the product of draft probabilities;

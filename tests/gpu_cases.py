@@ -238,7 +238,7 @@ def _same_rule(ids, lp, gpu_logits_row, k):
     np.testing.assert_allclose(lp, o_lp, atol=1e-4, rtol=0)
 
 
-def check_cycle_stagewise(gc, w, W, ci, reqs, tol, L=None, mode=None, u_try=None, u_res=None):
+def check_cycle_stagewise(gc, w, W, ci, reqs, tol, L=None, mode=None, u_try=None, u_res=None, keep=None):
     """Full-size parity of one GPU cycle, stage by stage, on the requests
     `reqs`: fusion, COMMIT and every tree round's logits against the oracle
     on the same rows and the same stage inputs (tolerance); each GPU top-k (ids exact, log-probs to
@@ -248,7 +248,8 @@ def check_cycle_stagewise(gc, w, W, ci, reqs, tol, L=None, mode=None, u_try=None
     the GPU tree bit for bit, frontier by frontier; the verification outcome
     equals the oracle's on that tree.  Returns the number of rows whose GPU
     top-k differs from the top-k of the oracle's own logits (each such row
-    must be a near-tie there)."""
+    must be a near-tie there).  keep: an optional dict that receives the
+    oracle's per-request results (request -> dict of logits)."""
     atol, rtol = tol
     buf = gc.buf
     k, D, m = w.topk, w.depth, w.keep
@@ -256,6 +257,8 @@ def check_cycle_stagewise(gc, w, W, ci, reqs, tol, L=None, mode=None, u_try=None
     for b in reqs:
         say("  stage-wise oracle, request", b)
         o = oracle_on_gpu_rows(w, W, ci, b, gc)
+        if keep is not None:
+            keep[b] = o
         n = w.commit_rows
         np.testing.assert_allclose(buf.g.float().cpu().numpy()[b * n:(b + 1) * n], o["g"], atol=atol, rtol=rtol)
         np.testing.assert_allclose(buf.commit_logits[b, 0].cpu().numpy(), o["commit_logits"], atol=atol, rtol=rtol)
@@ -292,3 +295,33 @@ def check_cycle_stagewise(gc, w, W, ci, reqs, tol, L=None, mode=None, u_try=None
             np.testing.assert_array_equal(buf.accepted[b, :len(ra)].cpu().numpy(), ra)
             assert int(buf.bonus[b].item()) == rb, f"request {b}: bonus"
     return excused
+
+
+def check_logits_free_topk(gc, w, oracle_by_req, tie_tol, lp_tol):
+    """The cycle just run without kept logits (the configuration the
+    benchmark times: for k = 1 at 17-64 rows the LM head keeps only
+    per-block (max, sum exp, argmax) partials) against the oracle's own
+    logits on the same rows: every top-k id list equals the oracle's top-k
+    unless the oracle has a near-tie (gap <= tie_tol) at that row, and every
+    log-probability matches the oracle's to lp_tol.  Returns (near-tie rows,
+    max |lp - oracle lp|)."""
+    buf = gc.buf
+    k, D = w.topk, w.depth
+    excused, worst = 0, 0.0
+    for b, o in oracle_by_req.items():
+        rows = [(buf.root_ids[b, 0].cpu().numpy(), buf.root_lp[b, 0].cpu().numpy(), o["commit_logits"], "root")]
+        for r in range(D - 1):
+            ids = buf.round_ids[r][b].cpu().numpy()
+            lps = buf.round_lp[r][b].cpu().numpy()
+            rows += [(ids[i], lps[i], o["rounds"][r][i], f"round {r} row {i}") for i in range(k)]
+        for ids, lp, ol, name in rows:
+            o_ids, o_lp, _ = O.topk_logprobs(ol, k)
+            exact, exc = topk_agrees(ids, ol, k, tie_tol)
+            assert exact or exc, f"request {b} {name}: top-{k} {ids} vs oracle {o_ids} without a near-tie"
+            if not exact:
+                excused += 1
+                continue
+            d = float(np.max(np.abs(lp.astype(np.float64) - o_lp.astype(np.float64))))
+            worst = max(worst, d)
+            assert d <= lp_tol, f"request {b} {name}: log-prob differs from the oracle's by {d}"
+    return excused, worst

@@ -97,3 +97,89 @@ def test_verify_workspace_layout(blib):
                 for size in (S, S + 1, S + 255, 3 * S + 7):
                     off = (size // 6 * 5) & ~255
                     assert 24 * n <= off and off + 64 * (B * (m + 1) + B) <= size, (B, m, V, size)
+
+
+# ---------------------------------------------------------------- documented error codes
+# Dummy non-NULL device pointers: every call below fails validation on the
+# host, before anything is launched or dereferenced.
+_P = ctypes.c_void_p(0x10000)
+
+
+def _fake_weights(blib, layout=0):
+    return blib.Weights(*([0x10000] * 11), layout)
+
+
+def _fake_kv(blib, paged=False):
+    return blib.KV(0x10000, 0x10000, 0 if paged else 4096, 0x10000 if paged else None, 256 if paged else 0,
+                   16 if paged else 0, 0x10000, 0x10000, 0x10000)
+
+
+def test_workspace_too_small_is_eworkspace(blib):
+    from workloads.configs import L8B_SHAPE
+    lib = blib.load()
+    d = blib.dims_of(L8B_SHAPE)
+    w = _fake_weights(blib)
+    kv = _fake_kv(blib)
+    assert lib.eagle3_fuse(ctypes.byref(d), ctypes.byref(w), _P, 1, _P, _P, 1, None) == blib.EWORKSPACE
+    need = blib.workspace_size(d, 1, 10, 4096 - 10)
+    assert lib.eagle3_draft_step(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), blib.TREE, 1, 10, None, _P, _P,
+                                 _P, _P, 0, 10, blib.TOPK_ALL, _P, _P, _P, None, _P, need - 1,
+                                 None) == blib.EWORKSPACE
+    assert b"workspace" in lib.eagle3_last_error()
+    vneed = blib.verify_workspace_size(1, 60, 128256)
+    assert lib.eagle3_verify(1, 60, 128256, 6, _P, _P, _P, blib.GREEDY, ctypes.c_float(1.0), None, None, _P, _P, _P,
+                             _P, _P, vneed - 1, None) == blib.EWORKSPACE
+    assert lib.eagle3_topk(_P, 4, 128256, 10, _P, _P, None, _P, 16, None) == blib.EWORKSPACE
+    tneed = blib.ttt_workspace_size(d, 1, 128, 2)
+    assert lib.eagle3_ttt_forward(ctypes.byref(d), ctypes.byref(w), _P, _P, 1, 128, 2, None, _P, _P, _P, _P,
+                                  tneed - 1, None) == blib.EWORKSPACE
+    assert lib.eagle3_pack_weights(ctypes.byref(d), ctypes.byref(w), _P, 100, ctypes.byref(blib.Weights()),
+                                   None) == blib.EWORKSPACE
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, float("nan")])
+def test_sampling_temperature_must_be_positive(blib, T):
+    lib = blib.load()
+    vneed = blib.verify_workspace_size(1, 8, 4096)
+    assert lib.eagle3_verify(1, 8, 4096, 3, _P, _P, _P, blib.SAMPLE, ctypes.c_float(T), _P, _P, _P, _P, _P, _P, _P,
+                             vneed, None) == blib.EINVAL
+    assert b"temperature" in lib.eagle3_last_error()
+
+
+def test_dtype_mismatches(blib):
+    from workloads.configs import L8B_SHAPE, TINY_SHAPE
+    lib = blib.load()
+    sz = ctypes.c_size_t(0)
+    bad = blib.dims_of(L8B_SHAPE)
+    bad.dtype = 7                                            # no such dtype
+    assert lib.eagle3_workspace_size(ctypes.byref(bad), 1, 1, 16, ctypes.byref(sz)) == blib.EINVAL
+    f32 = blib.dims_of(TINY_SHAPE)
+    packed = _fake_weights(blib, layout=blib.LAYOUT_PACKED)  # packed weights with an fp32 drafter
+    assert lib.eagle3_fuse(ctypes.byref(f32), ctypes.byref(packed), _P, 1, _P, _P, 1 << 30, None) == blib.EINVAL
+    w = _fake_weights(blib)
+    kv = _fake_kv(blib, paged=True)                          # paged KV needs bf16
+    assert lib.eagle3_draft_step(ctypes.byref(f32), ctypes.byref(w), ctypes.byref(kv), blib.COMMIT, 1, 1, _P, None,
+                                 _P, _P, None, 0, 2, blib.TOPK_LAST, _P, _P, _P, None, _P, 1 << 30,
+                                 None) == blib.EUNSUPPORTED
+    assert lib.eagle3_ttt_forward(ctypes.byref(f32), ctypes.byref(w), _P, _P, 1, 64, 2, None, _P, _P, _P, _P,
+                                  1 << 30, None) == blib.EUNSUPPORTED
+    assert lib.eagle3_packed_weights_size(ctypes.byref(f32), ctypes.byref(sz)) == blib.EUNSUPPORTED
+
+
+def test_model_width_above_row_kernel_limit(blib):
+    """The row kernels hold a row as 1024 threads x 8 elements: d = 8224 (a
+    multiple of 32 above 8192) is rejected by every call that takes dims."""
+    from workloads.configs import tiny_shape
+    lib = blib.load()
+    d = blib.dims_of(tiny_shape(d=8224, hq=64, hkv=8, hd=128, ffn=28672, vocab=128256, dtype="bf16"))
+    with pytest.raises(blib.Eagle3Error) as e:
+        blib.workspace_size(d, 1, 10, 4096)
+    assert e.value.code == blib.EUNSUPPORTED
+    w = _fake_weights(blib)
+    kv = _fake_kv(blib)
+    assert lib.eagle3_draft_step(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), blib.COMMIT, 1, 1, _P, None,
+                                 _P, _P, None, 0, 10, blib.TOPK_LAST, _P, _P, _P, None, _P, 1 << 40,
+                                 None) == blib.EUNSUPPORTED
+    assert lib.eagle3_fuse(ctypes.byref(d), ctypes.byref(w), _P, 1, _P, _P, 1 << 40, None) == blib.EUNSUPPORTED
+    d.d = 8192
+    assert blib.workspace_size(d, 1, 10, 4096) > 0

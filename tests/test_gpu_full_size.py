@@ -20,11 +20,14 @@ from oracle import eagle3_oracle as O
 from workloads import gen
 from workloads.configs import C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT
 
-from gpu_cases import GpuCycle, check_cycle_stagewise, dev_i32, host_weights, say
+from gpu_cases import GpuCycle, check_cycle_stagewise, check_logits_free_topk, dev_i32, host_weights, say
 
 pytestmark = pytest.mark.gpu
 
 TOL = (2e-2, 1e-2)  # bf16 logits / fusion / CE: atol, rtol
+# log-probabilities of the logits-free runs against the oracle's, stage-isolated
+LP_TOL = 1e-4
+LP_TOL_70B = 1e-4
 
 
 def _setup(w, seed=1):
@@ -37,7 +40,8 @@ def _setup(w, seed=1):
 
 def _rerun_without_kept_logits(gc, L, mode, ut=None, ur=None):
     """The benchmark runs without logits_out; the tree and the verification
-    outcome must not depend on it."""
+    outcome must not depend on it.  Leaves the logits-free run's top-k in
+    the buffers."""
     before = (gc.tree(), gc.buf.accept_len.cpu().numpy(), gc.buf.accepted.cpu().numpy(), gc.buf.bonus.cpu().numpy())
     saved = gc.buf.commit_logits, gc.buf.round_logits
     gc.buf.commit_logits, gc.buf.round_logits = None, None
@@ -62,9 +66,12 @@ def test_c2_8b_tree_full_size(lib):
     gc.run(L, 0)
     assert int(gc.buf.status.max().item()) == 0
     W = host_weights(Wt)
-    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=0)
+    orc = {}
+    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=0, keep=orc)
     say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
     _rerun_without_kept_logits(gc, L, 0)
+    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL)
+    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
     say("sampling verification on the same tree")
     ut, ur = gen.uniforms(2, w.batch, w.keep + 1)
     gc.run(L, 1, 1.0, ut, ur)
@@ -88,7 +95,8 @@ def test_c3_8b_chain_paged_batch64_full_size(lib):
     # sampled requests: first, last and one in between (prefix lengths differ)
     reqs = [0, 37, w.batch - 1]
     say("prefix lengths of the sampled requests:", [int(ci.ctx_len[b]) for b in reqs])
-    exc = check_cycle_stagewise(gc, w, W, ci, reqs, TOL, L=L, mode=0)
+    orc = {}
+    exc = check_cycle_stagewise(gc, w, W, ci, reqs, TOL, L=L, mode=0, keep=orc)
     say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
     # every request: the verification outcome equals the oracle's on the GPU tree
     t = gc.tree()
@@ -98,6 +106,9 @@ def test_c3_8b_chain_paged_batch64_full_size(lib):
         ra, rb = O.verify_greedy(t["tok"][b], t["parent"][b], L[b])
         assert al[b] == len(ra) and bonus[b] == rb, f"request {b}"
     _rerun_without_kept_logits(gc, L, 0)
+    # the benchmark's top-1 LM head (per-block partials, no logits) against the oracle
+    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL)
+    say("logits-free top-1 vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
 
 
 @pytest.mark.timeout(900)
@@ -110,8 +121,12 @@ def test_c4_70b_tree_sampling_full_size(lib):
     gc.run(L, 1, w.temperature, ut, ur)
     assert int(gc.buf.status.max().item()) == 0
     W = host_weights(Wt)
-    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=1, u_try=ut, u_res=ur)
+    orc = {}
+    exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=1, u_try=ut, u_res=ur, keep=orc)
     say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+    _rerun_without_kept_logits(gc, L, 1, ut, ur)
+    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL_70B)
+    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
 
 
 @pytest.mark.timeout(900)

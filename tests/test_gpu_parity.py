@@ -225,6 +225,44 @@ def test_verify_golden(lib):
         assert bo[0] == c["expect_bonus"], c["name"]
 
 
+def test_verify_sampling_exact_breakpoints_large_vocab(lib):
+    """Sampling decisions placed exactly on a breakpoint of the residual CDF,
+    and one ulp below it, at a vocabulary that spans 33 partitions of the
+    kernel.  All logits are 0, so every weight is exactly 1 and every sum on
+    either side is an exact integer: the thresholds u * Rm land exactly on
+    cumulative weights, including at partition boundaries and after
+    rejected tokens, and the GPU must take the oracle's decision in each."""
+    from eagle_draft_tree_amd import binding as Bd
+    V = 131074
+    tok = np.array([0, 100, 5000]); par = np.array([-1, 0, 0])   # both rejected: Rm = 2^17
+    js = [1, 100, 4094, 4095, 4096 * 5 - 2, 4096 * 5 - 1, 4096 * 32 - 3, 131071]
+    ur_vals = []
+    for j in js:
+        u = j / 131072.0
+        ur_vals += [u, np.nextafter(u, 0.0)]
+    Bn = len(ur_vals)
+    L = np.zeros((Bn, 3, V), np.float32)
+    ut = np.full((Bn, 3), 0.5)
+    ur = np.zeros((Bn, 3)); ur[:, 0] = ur_vals
+    toks, pars = np.stack([tok] * Bn), np.stack([par] * Bn)
+    say("verify exact breakpoints, V", V, "requests", Bn)
+    al, acc, bo, st = _run_verify(Bn, 2, V, toks, pars, L, Bd.SAMPLE, 1.0, ut, ur)
+    for b in range(Bn):
+        ra, rb = O.verify_sample(tok, par, L[b], ut[b], ur[b], 1.0)
+        assert st[b] == 0 and al[b] == len(ra) == 0 and bo[b] == rb, (b, ur[b, 0], bo[b], rb)
+    # the acceptance boundary: Rm = 2^17, u_try = 2^-17 rejects, one ulp below accepts
+    V2 = 131072
+    L2 = np.zeros((2, 2, V2), np.float32)
+    tok2, par2 = np.array([0, 5]), np.array([-1, 0])
+    ut2 = np.array([[0.0, 2.0 ** -17], [0.0, np.nextafter(2.0 ** -17, 0.0)]])
+    ur2 = np.array([[0.25, 0.75], [0.25, 0.75]])
+    al, acc, bo, st = _run_verify(2, 1, V2, np.stack([tok2] * 2), np.stack([par2] * 2), L2, Bd.SAMPLE, 1.0, ut2, ur2)
+    for b in range(2):
+        ra, rb = O.verify_sample(tok2, par2, L2[b], ut2[b], ur2[b], 1.0)
+        assert al[b] == len(ra) and list(acc[b][: al[b]]) == ra and bo[b] == rb, (b, al[b], bo[b], ra, rb)
+    assert al[0] == 0 and al[1] == 1
+
+
 def test_verify_nan_and_neg_inf(lib):
     from eagle_draft_tree_amd import binding as Bd
     V = 300

@@ -150,6 +150,127 @@ def test_decoder_attention_matches_torch_sdpa_with_gqa():
     np.testing.assert_allclose(h2, h2_ref, rtol=1e-10, atol=1e-10)
 
 
+def _torch_decoder_row_block(cfg, W, S, T, P, K, V, widx, vis, gains, bf16=False):
+    """The drafter layer written with torch's own operators, independent of
+    the oracle: rms_norm with each gain where it belongs, linear, RoPE as a
+    complex rotation of the half pairs, scaled_dot_product_attention with a
+    boolean mask and the KV heads repeated, silu.  With bf16=True the values
+    are cast to bfloat16 at the rounding points (x, q/k/v, a, u, the SwiGLU
+    output, the normalised final state)."""
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    rnd = (lambda z: z.to(torch.bfloat16).to(torch.float64)) if bf16 else (lambda z: z)
+    d, Hq, Hkv, hd, F, eps = cfg.d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.rms_eps
+    R = len(T)
+    s = t(S)
+    e = t(W["emb"])[torch.as_tensor(np.asarray(T, dtype=np.int64))]
+    rms = torch.nn.functional.rms_norm
+    x = rnd(torch.cat([rms(e, (d,), t(gains["norm_e"]), eps=eps), rms(s, (d,), t(gains["norm_s"]), eps=eps)], 1))
+    qkv = torch.nn.functional.linear(x, t(W["qkv"]))
+
+    def rot(z, pos):
+        zc = torch.complex(z[..., : hd // 2], z[..., hd // 2:])
+        ang = t(pos)[:, None, None] * cfg.rope_theta ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+        w = zc * torch.polar(torch.ones_like(ang), ang)
+        return torch.cat([w.real, w.imag], -1)
+    q = rnd(rot(qkv[:, : Hq * hd].reshape(R, Hq, hd), P))
+    k = rnd(rot(qkv[:, Hq * hd:(Hq + Hkv) * hd].reshape(R, Hkv, hd), P))
+    v = rnd(qkv[:, (Hq + Hkv) * hd:].reshape(R, Hkv, hd))
+    Kt, Vt = t(K).clone(), t(V).clone()
+    Kt[torch.as_tensor(widx)] = k
+    Vt[torch.as_tensor(widx)] = v
+    rep = Hq // Hkv
+    kk = Kt.repeat_interleave(rep, dim=1).transpose(0, 1)   # [Hq, N, hd]
+    vv = Vt.repeat_interleave(rep, dim=1).transpose(0, 1)
+    a = torch.empty(R, Hq, hd, dtype=torch.float64)
+    for r in range(R):
+        m = torch.as_tensor(vis[r])[None, None, :].expand(Hq, 1, -1)
+        a[r] = torch.nn.functional.scaled_dot_product_attention(q[r][:, None, :], kk, vv, attn_mask=m)[:, 0]
+    a = rnd(a.reshape(R, Hq * hd))
+    h1 = s + torch.nn.functional.linear(a, t(W["o"]))
+    u = rnd(rms(h1, (d,), t(gains["norm_ffn"]), eps=eps))
+    gu = torch.nn.functional.linear(u, t(W["gate_up"]))
+    z = rnd(torch.nn.functional.silu(gu[:, :F]) * gu[:, F:])
+    h2 = h1 + torch.nn.functional.linear(z, t(W["down"]))
+    y = rnd(rms(h2, (d,), t(gains["norm_out"]), eps=eps))
+    logits = torch.nn.functional.linear(y, t(W["lm"]))
+    return h2.numpy(), logits.numpy(), Kt.numpy(), Vt.numpy()
+
+
+@pytest.mark.parametrize("dtype,hkv", [(F32, 2), (F32, 4), (BF16, 1)])
+def test_decoder_layer_and_lm_head_match_torch_with_distinct_gains(dtype, hkv):
+    """decoder_rows (state h2, the K/V it writes and the LM-head logits)
+    equals the same layer written with torch's operators.  Every RMSNorm gain
+    is a different random vector, so feeding the LM head the wrong state
+    (h1 for h2), a gain to the wrong norm or a missing final norm fails."""
+    cfg = tiny_shape(d=32, hq=4, hkv=hkv, hd=8, ffn=48, vocab=40, dtype=dtype)
+    W = _layer_setup(cfg)
+    g = np.random.default_rng(31)
+    for name in ("norm_e", "norm_s", "norm_ffn", "norm_out"):
+        W[name] = 1.0 + 0.5 * g.standard_normal(32)
+    if dtype == BF16:
+        W = {kk: (O.bf16_round(vv) if not kk.startswith("norm") else vv) for kk, vv in W.items()}
+    R, N = 4, 12
+    K = g.standard_normal((N, hkv, 8))
+    V = g.standard_normal((N, hkv, 8))
+    if dtype == BF16:
+        K, V = O.bf16_round(K), O.bf16_round(V)
+    S = g.standard_normal((R, 32))
+    T = np.array([3, 17, 0, 39])
+    P = np.array([5, 9, 10, 11])
+    widx = np.array([5, 9, 10, 11])
+    vis = g.random((R, N)) < 0.5
+    vis[np.arange(R), widx] = True
+    Kc, Vc = K.copy(), V.copy()
+    h2, logits = O.decoder_rows(cfg, W, S, T, P, Kc, Vc, widx, vis)
+    h2_t, lg_t, K_t, V_t = _torch_decoder_row_block(cfg, W, S, T, P, K, V, widx, vis, W, bf16=(dtype == BF16))
+    tol = 1e-10 if dtype == F32 else 1e-9
+    np.testing.assert_allclose(Kc, K_t, rtol=tol, atol=tol)
+    np.testing.assert_allclose(Vc, V_t, rtol=tol, atol=tol)
+    np.testing.assert_allclose(h2, h2_t, rtol=tol, atol=tol)
+    np.testing.assert_allclose(logits, lg_t, rtol=tol, atol=tol)
+    # the gains matter at this size: unit gains give other logits
+    W1 = dict(W, norm_out=np.ones(32))
+    _, l1 = O.decoder_rows(cfg, W1, S, T, P, K.copy(), V.copy(), widx, vis)
+    assert np.max(np.abs(l1 - logits)) > 1e-3
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_gather_paged_equals_contiguous(bs):
+    """A request's rows scattered block by block into shuffled physical
+    blocks of a shared pool come back in logical order, and attention over
+    the gathered rows equals attention over the contiguous rows."""
+    g = np.random.default_rng(40 + bs)
+    Hkv, hd, L = 2, 8, 53
+    nb_req = -(-L // bs)
+    n_blocks = 3 * nb_req + 5
+    contig_k = g.standard_normal((L, Hkv, hd))
+    contig_v = g.standard_normal((L, Hkv, hd))
+    pool_k = g.standard_normal((n_blocks, bs, Hkv, hd))   # other requests' data everywhere else
+    pool_v = g.standard_normal((n_blocks, bs, Hkv, hd))
+    table = g.permutation(n_blocks)[:nb_req].astype(np.int32)
+    for j in range(nb_req):   # logical block j -> physical block table[j]
+        rows = contig_k[j * bs:(j + 1) * bs]
+        pool_k[table[j], : len(rows)] = rows
+        pool_v[table[j], : len(rows)] = contig_v[j * bs:(j + 1) * bs]
+    gk = O.gather_paged(pool_k, table, L, bs)
+    gv = O.gather_paged(pool_v, table, L, bs)
+    np.testing.assert_array_equal(gk, contig_k)
+    np.testing.assert_array_equal(gv, contig_v)
+    cfg = tiny_shape(d=32, hq=4, hkv=Hkv, hd=hd, ffn=48, vocab=16)
+    W = _layer_setup(cfg)
+    S = g.standard_normal((2, 32))
+    vis = np.zeros((2, L + 2), bool)
+    vis[0, : L + 1] = True
+    vis[1, : L + 2] = True
+    outs = []
+    for K0, V0 in ((contig_k, contig_v), (gk, gv)):
+        K = np.zeros((L + 2, Hkv, hd)); V = np.zeros((L + 2, Hkv, hd))
+        K[:L], V[:L] = K0, V0
+        outs.append(O.decoder_rows(cfg, W, S, [1, 2], [L, L + 1], K, V, [L, L + 1], vis))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
 def test_commit_in_two_batches_equals_one_batch():
     """Causal commit is incremental: rows [0,a) then [a,n) == rows [0,n) at once."""
     cfg = tiny_shape(d=32, hq=4, hkv=2, hd=8, ffn=48, vocab=16)
@@ -462,6 +583,147 @@ def test_sampling_verify_preserves_target_distribution_montecarlo():
         chi2 += (counts.get(key, 0) - e) ** 2 / e
     # 15 degrees of freedom: the 1e-4 upper quantile is about 44
     assert chi2 < 44.0, chi2
+
+
+def _bisect(pred, lo=0.0, hi=1.0):
+    """sup{u in [lo, hi] : pred(u)} for a predicate true below a threshold."""
+    if not pred(lo):
+        return lo
+    for _ in range(80):
+        mid = 0.5 * (lo + hi)
+        if mid in (lo, hi):
+            break
+        lo, hi = (mid, hi) if pred(mid) else (lo, mid)
+    return lo
+
+
+def _enumerate_verify_outcomes(run, v_tok, v_par, V):
+    """Exact distribution of (accepted nodes, bonus) of a verifier `run(u_try,
+    u_res) -> (accepted, bonus)` over independent U(0,1) uniforms.
+
+    Along any walk each uniform is consulted at most once: u_try[c] when
+    child c is tried (accepted below a threshold), u_res[n] at the node
+    where the walk stops (the bonus is non-decreasing in it).  Each
+    threshold is found by bisection on `run` itself, with the uniforms
+    already decided held inside their intervals, so the probability of an
+    outcome is the product of its interval lengths."""
+    M = len(v_tok)
+    kids = {}
+    for c in range(1, M):
+        kids.setdefault(int(v_par[c]), []).append(c)
+    out = {}
+
+    def visit(node, acc, ut, ur, prob):
+        ut = ut.copy()
+        for c in kids.get(node, []):
+            def accepts(u, c=c):
+                t = ut.copy(); t[c] = u
+                a, _ = run(t, ur)
+                return len(a) > len(acc) and a[len(acc)] == c
+            th = _bisect(accepts)
+            if th > 0.0:
+                t = ut.copy(); t[c] = 0.5 * th
+                visit(c, acc + [c], t, ur, prob * th)
+            prob *= (1.0 - th)
+            ut[c] = 0.5 * (1.0 + th)
+            if prob == 0.0:
+                return
+        lo = 0.0
+        for y in range(V):
+            def at_most(u, y=y):
+                r = ur.copy(); r[node] = u
+                a, b = run(ut, r)
+                assert a == acc
+                return b <= y
+            hi = 1.0 if y == V - 1 else _bisect(at_most)
+            if hi > lo:
+                key = (tuple(acc), y)
+                out[key] = out.get(key, 0.0) + prob * (hi - lo)
+                lo = hi
+    visit(0, [], np.full(M, 0.5), np.full(M, 0.5), 1.0)
+    return out
+
+
+def _first_tokens_distribution(outcomes, v_tok, p_next, n):
+    """Distribution of the first n emitted tokens when every cycle after this
+    one samples from the target (p_next(seq) = target probabilities after
+    the sequence): an outcome emitting fewer than n tokens is continued by
+    the target."""
+    dist = {}
+
+    def extend(seq, pr):
+        if len(seq) >= n:
+            key = tuple(seq[:n])
+            dist[key] = dist.get(key, 0.0) + pr
+            return
+        p = p_next(seq)
+        for y in range(len(p)):
+            if p[y] > 0:
+                extend(seq + [y], pr * p[y])
+    for (acc, bonus), pr in outcomes.items():
+        extend([int(v_tok[a]) for a in acc] + [bonus], pr)
+    return dist
+
+
+@pytest.mark.parametrize("T,tree", [
+    (1.0, ([0, 1, 3, 2, 0, 1], [-1, 0, 0, 1, 2, 2])),    # depth 2, siblings of 2 and 1 children
+    (0.7, ([0, 4, 2, 0, 3, 1], [-1, 0, 0, 0, 1, 1])),     # three root children
+    (1.6, ([0, 2, 2, 1], [-1, 0, 1, 1])),                 # a chain node with two children
+    (1.0, ([0, 3], [-1, 0])),                             # one candidate
+])
+def test_sampling_verify_exact_enumeration_preserves_target(T, tree):
+    """Exact enumeration on V = 5, depth <= 2: the probability of every
+    sequence of emitted tokens equals the target's autoregressive
+    probability to 1e-12.  A target logit of -inf (probability 0) is part of
+    the vocabulary.  The same enumeration of a verifier that draws the bonus
+    from p instead of the residual (a plausible mistake) is off by far more."""
+    V = 5
+    v_tok, v_par = np.array(tree[0]), np.array(tree[1])
+    tgt = _hash_target(V, seed=int(T * 10) + len(v_tok), sigma=1.3)
+
+    def logits_after(seq):
+        l = tgt(seq).copy()
+        if len(seq) == 2:
+            l[4] = -np.inf     # one token impossible after some prefixes
+        return l
+
+    def p_next(seq):
+        return softmax(logits_after([0] + list(seq)).astype(np.float64) / T)
+    L = []
+    for i in range(len(v_tok)):
+        path, nd = [], i
+        while nd > 0:
+            path.append(int(v_tok[nd])); nd = int(v_par[nd])
+        L.append(logits_after([0] + list(reversed(path))))
+    L = np.array(L)
+    run = lambda ut, ur: O.verify_sample(v_tok, v_par, L, ut, ur, T)
+    outcomes = _enumerate_verify_outcomes(run, v_tok, v_par, V)
+    assert abs(sum(outcomes.values()) - 1.0) < 1e-12
+    depth = int(max(len(a) for a, _ in outcomes)) + 1
+    got = _first_tokens_distribution(outcomes, v_tok, p_next, depth)
+    for seq in set(got) | set(_first_tokens_distribution({((), y): p_next([])[y] for y in range(V)},
+                                                          v_tok, p_next, depth)):
+        ref = 1.0
+        for i in range(len(seq)):
+            ref *= p_next(list(seq[:i]))[seq[i]]
+        assert abs(got.get(seq, 0.0) - ref) <= 1e-12, (seq, got.get(seq, 0.0), ref)
+
+    def no_residual(ut, ur):
+        """Mistaken verifier: after rejections the bonus is drawn from p itself."""
+        acc, b = O.verify_sample(v_tok, v_par, L, ut, ur, T)
+        node = acc[-1] if acc else 0
+        leaf_tok, leaf_par = np.array([v_tok[node]]), np.array([-1])
+        _, b2 = O.verify_sample(leaf_tok, leaf_par, L[node:node + 1], ut[:1], ur[node:node + 1], T)
+        return acc, b2
+    bad = _first_tokens_distribution(_enumerate_verify_outcomes(no_residual, v_tok, v_par, V), v_tok, p_next,
+                                     depth)
+    err = 0.0
+    for seq, pr in bad.items():
+        ref = 1.0
+        for i in range(len(seq)):
+            ref *= p_next(list(seq[:i]))[seq[i]]
+        err = max(err, abs(pr - ref))
+    assert err > 1e-3
 
 
 def test_sampling_wrong_rule_is_detected():
