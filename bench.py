@@ -34,35 +34,42 @@ KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, to
 KC_TTT = dict(rowops=1, ttt_gemm=11, ttt_attn=12, ttt_ce=13)
 
 
-def kernel_source_hash():
-    """Hash of the sources that build the LM-head kernel (for the traffic record)."""
+# sources that build each workload's dominant kernel (a traffic record is
+# used only while their hash is unchanged)
+KERNEL_SOURCES = {
+    "rows_gemm": ("gemm_rows.hpp", "draft.hip", "common.hpp"),
+    "rows_rx": ("rows_rx.hpp", "draft.hip", "common.hpp"),
+    "ttt_ce": ("bigemm.hpp", "ttt.hip", "common.hpp"),
+}
+
+
+def kernel_source_hash(kind="rows_gemm"):
+    """Hash of the sources that build a kernel (for the traffic record)."""
     h = hashlib.sha256()
-    for f in ("gemm_rows.hpp", "draft.hip", "common.hpp"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "eagle_draft_tree_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, src_hash):
-    """Counter-measured HBM bytes per LM-head launch, if recorded for these sources."""
-    path = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+def load_traffic(workload, kind):
+    """Counter-measured HBM bytes per launch of a workload's dominant kernel,
+    if recorded (profiles/traffic.json) for the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     r = rec.get(workload)
-    if not r or r.get("source_hash") != src_hash:
+    if not r or r.get("source_hash") != kernel_source_hash(kind):
         return None
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
-    """The oracle as it stands: one full cycle of request 0 on the host cores."""
+def _host_info():
+    """Threads the oracle's BLAS uses, a description of it, and the CPU model."""
     import numpy as np
-
-    from oracle import eagle3_oracle as O
-    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
     np.dot(np.ones((64, 64)), np.ones((64, 64)))  # loads the BLAS, so that its thread pool can be read
     try:
         from threadpoolctl import threadpool_info
@@ -71,21 +78,94 @@ def cpu_baseline(w, Wt, ci, seconds_cap=60.0):
         blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)" for i in pools)
     except Exception:
         threads, blas = os.cpu_count() or 1, "unknown"
-    n = w.commit_rows
-    Kc = ci.kv_k.f32()[0].astype(np.float64)
-    Vc = ci.kv_v.f32()[0].astype(np.float64)
-    t0 = time.time()
-    O.draft_cycle(w.shape, W, ci.feats.f32()[:n], ci.tokens[0], Kc, Vc, int(ci.ctx_len[0]), w.topk, w.depth,
-                  w.keep)
-    dt = time.time() - t0
     try:
         model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
     except Exception:
         model = "unknown"
-    return {"value": 1.0 / dt, "unit": "draft-tree steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full cycle (fuse + commit + {w.depth - 1} tree rounds + rerank) of request 0, "
-                      f"fp64 NumPy, {dt:.1f} s; cpu_count={os.cpu_count()}, "
-                      f"affinity={len(os.sched_getaffinity(0))}, {model}; BLAS: {blas or 'none detected'}"}
+    desc = (f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, {model}; "
+            f"BLAS: {blas or 'none detected'}")
+    return threads, desc
+
+
+def _oracle_request_kv(w, ci, b):
+    import numpy as np
+
+    from oracle import eagle3_oracle as O
+    n = w.commit_rows
+    if ci.block_table is not None:
+        L = int(ci.ctx_len[b])
+        return (O.gather_paged(ci.kv_k.f32(), ci.block_table[b], L + n, w.block_size).astype(np.float64),
+                O.gather_paged(ci.kv_v.f32(), ci.block_table[b], L + n, w.block_size).astype(np.float64))
+    return ci.kv_k.f32()[b].astype(np.float64), ci.kv_v.f32()[b].astype(np.float64)
+
+
+def cpu_baseline(w, Wt, ci, vin, reqs=None):
+    """The oracle as it stands, on the host cores: full cycles (fusion,
+    commit, D-1 tree rounds, rerank and verification) of the requests
+    `reqs` (default: all), scaled to whole-batch cycles per second.  vin =
+    (target logits [B, m+1, V], mode, temperature, u_try, u_res) of the
+    GPU's timed loop; the oracle verifies its own tree on them."""
+    from oracle import eagle3_oracle as O
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    threads, desc = _host_info()
+    L, mode, T, ut, ur = vin
+    reqs = list(range(w.batch)) if reqs is None else list(reqs)
+    n = w.commit_rows
+    t0 = time.time()
+    for b in reqs:
+        Kc, Vc = _oracle_request_kv(w, ci, b)
+        vt = O.draft_cycle(w.shape, W, ci.feats.f32()[b * n:(b + 1) * n], ci.tokens[b], Kc, Vc, int(ci.ctx_len[b]),
+                           w.topk, w.depth, w.keep)
+        if mode == "sample":
+            O.verify_sample(vt["tok"], vt["parent"], L[b], ut[b], ur[b], T)
+        else:
+            O.verify_greedy(vt["tok"], vt["parent"], L[b])
+    dt = time.time() - t0
+    per_cycle = dt * w.batch / len(reqs)
+    what = ("request 0" if w.batch == 1 else
+            f"requests {reqs} of {w.batch}, scaled by {w.batch}/{len(reqs)} (extrapolated)")
+    return {"value": 1.0 / per_cycle, "unit": "draft-tree steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"full cycle(s) (fuse + commit + {w.depth - 1} tree rounds + rerank + {mode} verify) of "
+                      f"{what}, fp64 NumPy, {dt:.1f} s; {desc}"}
+
+
+def cpu_baseline_ttt(w, Wt, ti, positions=(700, 2047)):
+    """The oracle's TTT forward on a bounded slice: sequence 0, the rollout
+    rows (j, i) of a few positions i (all R steps each; the step-1 keys of
+    every earlier position are computed too), timed on the host cores and
+    scaled to rows per second and to one whole forward (extrapolated)."""
+    from oracle import eagle3_oracle as O
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    threads, desc = _host_info()
+    R, B, S = w.ttt_steps, w.batch, w.ttt_seq
+    t0 = time.time()
+    O.ttt_forward(w.shape, W, ti.feats.f32()[0], ti.tokens[0], R, positions=list(positions))
+    dt = time.time() - t0
+    rows = len(positions) * R
+    rate = rows / dt
+    return {"value": rate, "unit": "TTT rollout rows/s", "cores": threads, "kind": "oracle",
+            "extrapolated_ms_per_forward": round(B * S * R / rate * 1e3, 1),
+            "sample": f"sequence 0, positions {list(positions)} x {R} steps = {rows} rollout rows (plus the step-1 "
+                      f"keys of positions <= {max(positions)}), fp64 NumPy, {dt:.1f} s; the per-forward time scales "
+                      f"this to {B} x {S} x {R} rows (extrapolated); {desc}"}
+
+
+def reporting_fields(w, ci=None):
+    """Quantities the pages ask a drafter evaluation to report: target-feature
+    bytes read per cycle (or per TTT forward) and the drafter's device
+    memory (weights, KV)."""
+    s = w.shape
+    es = 2 if s.dtype == "bf16" else 4
+    d, F, V = s.d, s.ffn, s.vocab
+    weights = (d * 3 * d + V * d + (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * 2 * d
+               + d * s.n_q_heads * s.head_dim + 2 * F * d + d * F + V * d) * es
+    if w.ttt_seq:
+        return {"target_feature_bytes_per_forward": w.batch * w.ttt_seq * 3 * d * es, "draft_weight_bytes": weights}
+    kv_rows = int(ci.kv_k.raw.size // (s.n_kv_heads * s.head_dim)) if ci is not None else 0
+    return {"target_feature_bytes_per_cycle": w.batch * w.commit_rows * 3 * d * es,
+            "draft_weight_bytes": weights,
+            "draft_kv_bytes": 2 * kv_rows * s.n_kv_heads * s.head_dim * es
+                              + 2 * w.batch * 64 * s.n_kv_heads * s.head_dim * es}
 
 
 def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
@@ -144,6 +224,7 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         assert int(buf.status.cpu().numpy().max()) == 0
         accepted.append(buf.accept_len.cpu().numpy().astype(np.float64))
     tokens_per_cycle = float(np.mean(np.stack(accepted) + 1.0)) * Bn
+    vin = (Ls[0].cpu().numpy(), w.verify_modes[0], w.temperature, ut, ur)
     for i in range(max(warmup - n_plant, 0)):
         cycle(Ls[i % n_plant])
     torch.cuda.synchronize()
@@ -269,13 +350,23 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
                            "frac": round(bytes_cycle / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernel_ms_per_cycle": {kk: round(v[0] / steps, 4) for kk, v in per_class.items()},
     }
+    # the dominant kernel (the LM head): bytes per launch over its HIP-event launch time
+    kind = "rows_rx" if k == 1 and 16 < Bn <= 64 else "rows_gemm"
+    res["roofline"] = {"bound": "hbm", "achieved": res["lm_head"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": res["lm_head"]["hbm_frac"], "traffic": load_traffic(w.name, kind),
+                       "kernel": "LM head (" + ("register-weight GEMM, top-1 partials" if kind == "rows_rx"
+                                                else "rows GEMM with tile statistics") + ")",
+                       "scope": "dominant kernel only; the whole draft step is draft_step_roofline",
+                       "bytes_per_launch": res["lm_head"]["bytes_per_launch"],
+                       "avg_launch_us": res["lm_head"]["avg_launch_us"]}
+    res["reporting"] = reporting_fields(w, ci)
     if graph:
         res["cycle_ms_percentiles"] = cycle_pct
         gbs = bytes_steps / (ms_steps * 1e-3) / 1e9
         res["draft_step_roofline"] = {"steps": D, "bytes_per_step": round(bytes_steps / D),
                                       "us_per_step": round(ms_steps * 1e3 / D, 2), "achieved_GBs": round(gbs, 1),
                                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    return res, ci
+    return res, ci, vin
 
 
 def ttt_bench(w, dr, steps, warmup):
@@ -337,13 +428,16 @@ def ttt_bench(w, dr, steps, warmup):
         "mfma_frac": round((f_gemm + f_lm + f_attn) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(lm_tf, 1) if lm_tf else None,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(lm_tf / MFMA_BF16_PEAK_TFLOPS, 4) if lm_tf else None, "traffic": None,
+                     "frac": round(lm_tf / MFMA_BF16_PEAK_TFLOPS, 4) if lm_tf else None,
+                     "traffic": load_traffic(w.name, "ttt_ce"),
                      "kernel": "LM-head GEMM with CE epilogue", "flops_per_launch": f_lm / R,
                      "avg_launch_us": round(lm_launch_us, 1) if lm_launch_us else None},
+        "flops_per_forward": f_gemm + f_lm + f_attn,
+        "reporting": reporting_fields(w),
         "class_TFLOPs": {"projection_gemms": round(tf(f_gemm, "ttt_gemm"), 1),
                          "lm_head_ce": round(lm_tf, 1), "attention": round(tf(f_attn, "ttt_attn"), 1)},
         "kernel_ms_per_step": {kk: round(v[0] / steps, 3) for kk, v in per_class.items()},
-    }
+    }, ti
 
 
 def main():
@@ -387,24 +481,29 @@ def main():
     dr8 = Drafter(s8, Wt8, pack=True) if Wt8 is not None else None
     setup_s = time.time() - t0
 
+    # sampled requests of the batch-64 chain for its CPU baseline (the oracle
+    # drafts one request at a time)
+    c3_reqs = (0, 21, 42, 63)
     if args.only == "ttt":
-        r = ttt_bench(C5_8B_TTT, dr8, max(1, min(args.steps, 10)), 1)
+        r, ti = ttt_bench(C5_8B_TTT, dr8, max(1, min(args.steps, 10)), 1)
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline_ttt(C5_8B_TTT, Wt8, ti)
         print(json.dumps(r), flush=True)
         return
     if args.only == "c2":
         args.main_only = True
     if args.only in ("c3", "c4"):
         w = C3_8B_CHAIN if args.only == "c3" else C4_70B_TREE
-        dr = dr8 if args.only == "c3" else Drafter(w.shape, gen.gen_weights(w.shape, seed=0), pack=True)
-        r, _ = cycle_bench(w, dr, args.steps, args.warmup, graph=not args.no_graph)
+        Wt = Wt8 if args.only == "c3" else gen.gen_weights(w.shape, seed=0)
+        dr = dr8 if args.only == "c3" else Drafter(w.shape, Wt, pack=True)
+        r, ci, vin = cycle_bench(w, dr, args.steps, args.warmup, graph=not args.no_graph)
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline(w, Wt, ci, vin, c3_reqs if args.only == "c3" else None)
         print(json.dumps(r), flush=True)
         return
 
     w = C2_8B_TREE
-    r, ci = cycle_bench(w, dr8, args.steps, args.warmup, graph=not args.no_graph)
-    lm = r["lm_head"]
-    src_hash = kernel_source_hash()
-    traffic = load_traffic("llama3.1-8b-b1-tree", src_hash)
+    r, ci, vin = cycle_bench(w, dr8, args.steps, args.warmup, graph=not args.no_graph)
     out = {
         "metric": "draft-tree steps/s + verified tokens/s at 1 GPU; % peak HBM GB/s / MFMA",
         "value": r["draft_tree_steps_per_s"],
@@ -423,30 +522,42 @@ def main():
                    "topk": w.topk, "keep": w.keep, "verify": "greedy", "graph": r["graph"], "weights": "packed"},
         "verified_tokens_per_s": r["verified_tokens_per_s"],
         "tokens_per_cycle": r["tokens_per_cycle"],
-        "roofline": {"bound": "hbm", "achieved": lm["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": lm["hbm_frac"], "traffic": traffic, "kernel": "lm_head rows GEMM",
-                     "bytes_per_launch": lm["bytes_per_launch"], "avg_launch_us": lm["avg_launch_us"]},
+        "roofline": r["roofline"],
         "cycle_ms_percentiles": r.get("cycle_ms_percentiles"),
         "cycle_roofline": r["cycle_roofline"],
         "draft_step_roofline": r.get("draft_step_roofline"),
         "kernel_ms_per_cycle": r["kernel_ms_per_cycle"],
+        "reporting": r["reporting"],
         "setup_s": round(setup_s, 1),
     }
+    # the GPU legs first, then every CPU baseline (host work only)
+    cpu_jobs = [("main", w, Wt8, ci, vin, None)]
     if not args.main_only:
         wl = {}
-        r3, _ = cycle_bench(C3_8B_CHAIN, dr8, max(args.steps // 2, 1), args.warmup, graph=not args.no_graph)
+        r3, ci3, vin3 = cycle_bench(C3_8B_CHAIN, dr8, max(args.steps // 2, 1), args.warmup, graph=not args.no_graph)
         wl[C3_8B_CHAIN.name] = r3
-        r5 = ttt_bench(C5_8B_TTT, dr8, 5, 1)
+        cpu_jobs.append((C3_8B_CHAIN.name, C3_8B_CHAIN, Wt8, ci3, vin3, c3_reqs))
+        r5, ti = ttt_bench(C5_8B_TTT, dr8, 5, 1)
         wl[C5_8B_TTT.name] = r5
+        cpu_jobs.append((C5_8B_TTT.name, C5_8B_TTT, Wt8, ti, None, None))
         del dr8
         torch.cuda.empty_cache()
-        dr70 = Drafter(C4_70B_TREE.shape, gen.gen_weights(C4_70B_TREE.shape, seed=0), pack=True)
-        r4, _ = cycle_bench(C4_70B_TREE, dr70, max(args.steps // 3, 1), args.warmup, graph=not args.no_graph)
+        Wt70 = gen.gen_weights(C4_70B_TREE.shape, seed=0)
+        dr70 = Drafter(C4_70B_TREE.shape, Wt70, pack=True)
+        r4, ci4, vin4 = cycle_bench(C4_70B_TREE, dr70, max(args.steps // 3, 1), args.warmup, graph=not args.no_graph)
         wl[C4_70B_TREE.name] = r4
+        cpu_jobs.append((C4_70B_TREE.name, C4_70B_TREE, Wt70, ci4, vin4, None))
         del dr70
+        torch.cuda.empty_cache()
         out["workloads"] = wl
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, Wt8, ci)
+        for name, wk, Wt, inp, vi, reqs in cpu_jobs:
+            print(f"cpu baseline: {wk.name}", file=sys.stderr, flush=True)
+            cb = cpu_baseline_ttt(wk, Wt, inp) if wk.ttt_seq else cpu_baseline(wk, Wt, inp, vi, reqs)
+            if name == "main":
+                out["cpu_baseline"] = cb
+            else:
+                out["workloads"][name]["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

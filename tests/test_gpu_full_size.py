@@ -20,14 +20,12 @@ from oracle import eagle3_oracle as O
 from workloads import gen
 from workloads.configs import C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT
 
-from gpu_cases import GpuCycle, check_cycle_stagewise, check_logits_free_topk, dev_i32, host_weights, say
+from gpu_cases import (GpuCycle, check_cycle_stagewise, check_logits_free_topk, dev_i32, host_weights, say,
+                       snapshot_topk)
 
 pytestmark = pytest.mark.gpu
 
 TOL = (2e-2, 1e-2)  # bf16 logits / fusion / CE: atol, rtol
-# log-probabilities of the logits-free runs against the oracle's, stage-isolated
-LP_TOL = 1e-4
-LP_TOL_70B = 1e-4
 
 
 def _setup(w, seed=1):
@@ -69,9 +67,10 @@ def test_c2_8b_tree_full_size(lib):
     orc = {}
     exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=0, keep=orc)
     say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+    kept = snapshot_topk(gc, w, [0])
     _rerun_without_kept_logits(gc, L, 0)
-    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL)
-    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
+    exc, wlp, wl = check_logits_free_topk(gc, w, orc, kept, 2 * TOL[0])
+    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", wlp, "max |logit diff|", wl)
     say("sampling verification on the same tree")
     ut, ur = gen.uniforms(2, w.batch, w.keep + 1)
     gc.run(L, 1, 1.0, ut, ur)
@@ -105,10 +104,11 @@ def test_c3_8b_chain_paged_batch64_full_size(lib):
     for b in range(w.batch):
         ra, rb = O.verify_greedy(t["tok"][b], t["parent"][b], L[b])
         assert al[b] == len(ra) and bonus[b] == rb, f"request {b}"
+    kept = snapshot_topk(gc, w, reqs)
     _rerun_without_kept_logits(gc, L, 0)
     # the benchmark's top-1 LM head (per-block partials, no logits) against the oracle
-    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL)
-    say("logits-free top-1 vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
+    exc, wlp, wl = check_logits_free_topk(gc, w, orc, kept, 2 * TOL[0])
+    say("logits-free top-1 vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", wlp, "max |logit diff|", wl)
 
 
 @pytest.mark.timeout(900)
@@ -124,9 +124,10 @@ def test_c4_70b_tree_sampling_full_size(lib):
     orc = {}
     exc = check_cycle_stagewise(gc, w, W, ci, [0], TOL, L=L, mode=1, u_try=ut, u_res=ur, keep=orc)
     say("rows whose top-k differs from the oracle's own logits (near-ties):", exc)
+    kept = snapshot_topk(gc, w, [0])
     _rerun_without_kept_logits(gc, L, 1, ut, ur)
-    exc, worst = check_logits_free_topk(gc, w, orc, 2 * TOL[0], LP_TOL_70B)
-    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", worst)
+    exc, wlp, wl = check_logits_free_topk(gc, w, orc, kept, 2 * TOL[0])
+    say("logits-free top-k vs the oracle: near-tie rows", exc, "max |lp - oracle lp|", wlp, "max |logit diff|", wl)
 
 
 @pytest.mark.timeout(900)
