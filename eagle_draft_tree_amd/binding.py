@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH):
         "eagle3_tree_expand": ([I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "eagle3_verify": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P, SZ, P], I),
         "eagle3_verify_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
+        "eagle3_verify_noalloc": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P], I),
         "eagle3_ttt_forward": ([P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
         "eagle3_topk": ([P, I, I, I, P, P, P, P, SZ, P], I),
         "eagle3_timing_enable": ([I, I], I),
@@ -195,6 +196,13 @@ def eagle3_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperatu
         B, m, V, Dmax, ptr(v_tok), ptr(v_parent), ptr(target_logits), mode, float(temperature),
         ptr(u_try), ptr(u_res), ptr(accept_len), ptr(accepted), ptr(bonus), ptr(status),
         ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def eagle3_verify_noalloc(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature, u_try, u_res,
+                          accept_len, accepted, bonus, status, stream=None):
+    _check("eagle3_verify_noalloc", load().eagle3_verify_noalloc(
+        B, m, V, Dmax, ptr(v_tok), ptr(v_parent), ptr(target_logits), mode, float(temperature),
+        ptr(u_try), ptr(u_res), ptr(accept_len), ptr(accepted), ptr(bonus), ptr(status), stream_ptr(stream)))
 
 
 def eagle3_ttt_forward(dims, weights, feats, tokens, B, S, R, forced_tokens, pred, ce, loss, ws,

@@ -232,10 +232,13 @@ int eagle3_verify_workspace_size(int B, int m, int V, size_t* bytes) {
   return ok();
 }
 
-int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int32_t* v_parent,
-                  const float* target_logits, int mode, float temperature, const double* u_try,
-                  const double* u_res, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
-                  int32_t* status, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+}  // extern "C"
+
+namespace {
+int check_verify_args(int B, int m, int V, int Dmax, const int32_t* v_tok, const int32_t* v_parent,
+                      const float* target_logits, int mode, float temperature, const double* u_try,
+                      const double* u_res, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                      int32_t* status) {
   REQUIRE(B >= 1 && m >= 0 && V >= 1 && Dmax >= 1, EAGLE3_EINVAL, "B/m/V/Dmax");
   REQUIRE(m + 1 <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "m+1=%d > 64", m + 1);
   REQUIRE(v_tok && v_parent && target_logits && accept_len && accepted && bonus && status, EAGLE3_EINVAL,
@@ -245,6 +248,19 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int
     REQUIRE(temperature > 0.f, EAGLE3_EINVAL, "temperature must be > 0 for sampling");
     REQUIRE(u_try && u_res, EAGLE3_EINVAL, "sampling needs u_try/u_res");
   }
+  return EAGLE3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int32_t* v_parent,
+                  const float* target_logits, int mode, float temperature, const double* u_try,
+                  const double* u_res, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                  int32_t* status, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+  int rc = check_verify_args(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature, u_try, u_res,
+                             accept_len, accepted, bonus, status);
+  if (rc) return rc;
   REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
   REQUIRE(ws_bytes >= e3::verify_ws_bytes(B, m, V), EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
           e3::verify_ws_bytes(B, m, V));
@@ -253,6 +269,26 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t* v_tok, const int
                                       u_try, u_res, accept_len, accepted, bonus, status, ws,
                                       ws_bytes, (hipStream_t)stream),
                     "eagle3_verify");
+}
+
+int eagle3_verify_noalloc(int B, int m, int V, int Dmax, const int32_t* v_tok, const int32_t* v_parent,
+                          const float* target_logits, int mode, float temperature, const double* u_try,
+                          const double* u_res, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                          int32_t* status, eagle3_stream_t stream) {
+  int rc = check_verify_args(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature, u_try, u_res,
+                             accept_len, accepted, bonus, status);
+  if (rc) return rc;
+  const size_t cap = e3::static_scratch_bytes();
+  REQUIRE(e3::verify_ws_bytes(B, m, V) <= cap, EAGLE3_ECAPACITY,
+          "B=%d m=%d V=%d needs %zu scratch bytes > the static %zu", B, m, V, e3::verify_ws_bytes(B, m, V), cap);
+  void* ws = nullptr;
+  if ((rc = hip_status(e3::static_scratch((hipStream_t)stream, &ws), "eagle3_verify_noalloc: static scratch")))
+    return rc;
+  e3::TimedScope ts(EAGLE3_KC_VERIFY, (hipStream_t)stream);
+  return hip_status(e3::launch_verify(B, m, V, Dmax, v_tok, v_parent, target_logits, mode, temperature,
+                                      u_try, u_res, accept_len, accepted, bonus, status, ws, cap,
+                                      (hipStream_t)stream),
+                    "eagle3_verify_noalloc");
 }
 
 int eagle3_topk(const float* logits, int rows, int V, int k, int32_t* ids, float* lp, float* lse,

@@ -47,6 +47,10 @@ hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32
 
 // ---- verification (verify.hip)
 size_t verify_ws_bytes(int B, int m, int V);
+// static per-device scratch of the allocation-free verify (noalloc.hip):
+// its size, and its device address on the current device (set up on first use)
+size_t static_scratch_bytes();
+hipError_t static_scratch(hipStream_t st, void** out);
 hipError_t launch_verify(int B, int m, int V, int Dmax, const int32_t* v_tok,
                          const int32_t* v_parent, const float* logits, int mode, float temperature,
                          const double* u_try, const double* u_res, int32_t* accept_len,

@@ -279,6 +279,23 @@ int eagle3_verify(int B, int m, int V, int Dmax, const int32_t *v_tok, const int
 /* Scratch bytes eagle3_verify needs for B requests, m kept nodes, vocab V. */
 int eagle3_verify_workspace_size(int B, int m, int V, size_t *bytes);
 
+/* eagle3_verify without a caller workspace, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics and outputs as
+ * eagle3_verify, minus ws/ws_bytes.  The scratch is a static device array
+ * of 8 MiB per GPU, held from the first call on that GPU until the process
+ * ends; the first call on a device looks up its address and enqueues one
+ * kernel that zero-fills it.  Nothing is allocated.  Shapes whose
+ * eagle3_verify_workspace_size exceeds 8 MiB return EAGLE3_ECAPACITY (the
+ * 8B batch-64 chain needs 0.3 MiB; B * (m+1) * ceil(V/4096) up to ~290k
+ * fits).  Every call on one GPU shares the array, which keeps the last
+ * call's contents: calls that overlap on one GPU (different streams, or
+ * threads) race; order them on one stream. */
+int eagle3_verify_noalloc(int B, int m, int V, int Dmax, const int32_t *v_tok, const int32_t *v_parent,
+                          const float *target_logits, int mode, float temperature, const double *u_try,
+                          const double *u_res, int32_t *accept_len, int32_t *accepted, int32_t *bonus,
+                          int32_t *status, eagle3_stream_t stream);
+
 /* Step 5 -- training-time-test forward ("EAGLE-3 精读" §2 and §5).
  * feats [B][S][3][d] (dtype), tokens [B][S].  Rows (j,i), j = 1..R: step 1
  * feeds (g_i, x_i) at position i; step j >= 2 feeds h2(j-1,i) and the
