@@ -31,7 +31,7 @@ argmax on float32 logits, tree scores as float32 sums of float32 log-probs,
 sampling verification in fp64.
 
 Where the pages are silent the oracle follows one explicit reading; each is
-named where it is used (R1..R26).
+named where it is used (R1..R32).
 """
 from __future__ import annotations
 
@@ -177,9 +177,14 @@ def decoder_rows(cfg, W, S, T, P, Kc, Vc, write_idx, visible, want_logits=True):
     h2 = h1 + matmul_wt(z, W["down"])
     logits = None
     if want_logits:
-        y = _rnd(cfg, rmsnorm(h2, W["norm_out"], eps))
-        logits = matmul_wt(y, W["lm"])
+        logits = matmul_wt(lm_input(cfg, W, h2), W["lm"])
     return h2, logits
+
+
+def lm_input(cfg, W, h2):
+    """The LM head's input y = rms(h2) * gamma_out, rounded to bfloat16 for
+    bf16 workloads (R4: the final norm acts on h2)."""
+    return _rnd(cfg, rmsnorm(h2, W["norm_out"], cfg.rms_eps))
 
 
 # --------------------------------------------------------------------------
@@ -199,6 +204,41 @@ def topk_logprobs(logits_row, k):
     lse = np.float32(logsumexp(l32.astype(np.float64)))
     lp = (l32[order] - lse).astype(np.float32)
     return order, lp, lse
+
+
+# --------------------------------------------------------------------------
+# step 3a': the efficient draft LM head (EAGLE-4 blog, the paragraph "EAGLE
+# Efficient LM Head" and the section 关于 Efficient LM Head: a low-rank head
+# first scores the whole vocabulary and keeps its top candidates; the full LM
+# head then computes exact logits for those candidates only; readings
+# R31-R32)
+
+
+def efficient_head_topk(cfg, W, y_row, A, Bm, c, k):
+    """Two-stage draft LM head for one row.
+
+    Stage 1 (recall): z = Bm . y, rounded to bfloat16 for bf16 workloads
+    like every GEMM input; scores s = A . z over the whole vocabulary.  The c
+    best float32 scores (value desc, id asc) are the candidates.
+    Stage 2 (exact): the full LM head's logits of the candidates only,
+    l_i = W_lm[cand_i] . y.
+    The top-k are the k best candidates by (float32 logit desc, id asc).
+    Log-probabilities are normalised over the candidate set (R31): lp = l -
+    logsumexp of the c candidate logits, in float32.
+
+    y_row [d]; A [V, r]; Bm [r, d].  Returns (ids [k] int32, lp [k] float32,
+    cand [c] int32 in score order, cand_logits [c] fp64).
+    """
+    y = np.asarray(y_row, dtype=np.float64)[None]
+    z = _rnd(cfg, matmul_wt(y, Bm))
+    s32 = matmul_wt(z, A)[0].astype(np.float32)
+    cand = np.argsort(-s32, kind="stable")[:c].astype(np.int32)
+    cl = (y @ np.asarray(W["lm"][cand], dtype=np.float64).T)[0]
+    l32 = cl.astype(np.float32)
+    order = np.array(sorted(range(c), key=lambda i: (-float(l32[i]), int(cand[i]))), dtype=np.int64)[:k]
+    lse = np.float32(logsumexp(l32.astype(np.float64)))
+    lp = (l32[order] - lse).astype(np.float32)
+    return cand[order].astype(np.int32), lp, cand, cl
 
 
 # --------------------------------------------------------------------------
@@ -395,13 +435,25 @@ def verify_sample(v_tok, v_parent, L, u_try, u_res, temperature=1.0):
 # the draft-tree cycle (fuse + commit + D-1 tree rounds + rerank), per request
 
 
-def draft_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, k, D, m, record=None):
+def _row_topk(cfg, W, h2_row, logits_row, k, head):
+    """Top-k of one drafted row: from the full logits, or through the
+    efficient head (head = dict(A=, B=, c=))."""
+    if head is None:
+        return topk_logprobs(logits_row, k)[:2]
+    ids, lp, _, _ = efficient_head_topk(cfg, W, lm_input(cfg, W, h2_row[None])[0], head["A"], head["B"],
+                                        head["c"], k)
+    return ids, lp
+
+
+def draft_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, k, D, m, record=None, head=None):
     """One EAGLE-3 draft cycle of one request, before verification.
 
     feats [n, 3, d] and tokens [n]: the n rows to commit (the last one is
     the root).  Kc, Vc [cap, Hkv, hd]: committed cache holding ctx_len rows
-    (copied, not modified).  Returns the verify tree (dict) and, if
-    ``record`` is a dict, per-round intermediate values.
+    (copied, not modified).  head: None for the full LM head, or dict(A=,
+    B=, c=) for the efficient head (efficient_head_topk).  Returns the
+    verify tree (dict) and, if ``record`` is a dict, per-round intermediate
+    values.
     """
     n = len(tokens)
     Hkv, hd = cfg.n_kv_heads, cfg.head_dim
@@ -421,7 +473,7 @@ def draft_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, k, D, m, record=None):
     h2, logits = decoder_rows(cfg, W, g, tokens, P, K, V, P, vis)
     root_pos = L0 + n - 1
     h_tree = {0: h2[-1]}
-    ids, lp, _ = topk_logprobs(logits[-1], k)
+    ids, lp = _row_topk(cfg, W, h2[-1], logits[-1], k, head)
     tree = DynamicTree(k, D, tokens[-1], root_pos)
     tree.init(ids, lp)
     if record is not None:
@@ -445,7 +497,7 @@ def draft_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, k, D, m, record=None):
         lps = np.zeros((len(rows), k), np.float32)
         for r in range(len(rows)):
             h_tree[1 + slot_base + r] = h2[r]
-            ids[r], lps[r], _ = topk_logprobs(logits[r], k)
+            ids[r], lps[r] = _row_topk(cfg, W, h2[r], logits[r], k, head)
         if record is not None:
             record["rounds"].append(dict(rows=rows, h2=h2, logits=logits, ids=ids, lp=lps))
         tree.step(ids, lps)

@@ -878,3 +878,85 @@ def test_tree_nodes_equal_sequential_decode_along_root_path(dtype, k, D, m, hkv)
         np.testing.assert_allclose(rd["logits"][rho], lg[0], rtol=tol, atol=tol)
         checked += 1
     assert checked == (D - 1) * k
+
+
+# ---------------------------------------------------------------- efficient LM head (EAGLE-4)
+def _bf16_setup(V=300, d=32, seed=50):
+    cfg = tiny_shape(d=d, hq=4, hkv=2, hd=8, ffn=48, vocab=V, dtype=BF16)
+    W = weights_f(cfg, std=0.3)
+    g = np.random.default_rng(seed)
+    y = O.bf16_round(g.standard_normal(d))
+    return cfg, W, g, y
+
+
+@pytest.mark.parametrize("c", [300, 40, 7])
+def test_efficient_head_with_exact_factors_is_the_full_head(c):
+    """Special case: B = I (rank d) and A = W_lm make the stage-1 scores the
+    exact logits (z = y is already bf16), so the candidates are the exact
+    top-c (brute force) and the top-k is the full head's top-k; the
+    log-probs differ from the full head's by the log of the candidates'
+    share of the softmax mass (scipy logsumexp), and equal them at c = V."""
+    cfg, W, g, y = _bf16_setup()
+    k = 5
+    ids, lp, cand, cl = O.efficient_head_topk(cfg, W, y, W["lm"], np.eye(32), c, k)
+    lm = np.asarray(W["lm"], np.float64)
+    exact = torch.nn.functional.linear(torch.from_numpy(y[None]), torch.from_numpy(lm)).numpy()[0]
+    e32 = exact.astype(np.float32)
+    brute = sorted(range(300), key=lambda t: (-e32[t], t))
+    assert list(cand) == brute[:c]
+    assert list(ids) == brute[:k]
+    np.testing.assert_allclose(cl, exact[cand], rtol=1e-12, atol=1e-12)
+    full_ids, full_lp, _ = O.topk_logprobs(exact, k)
+    assert list(full_ids) == list(ids)
+    shift = logsumexp(e32.astype(np.float64)) - logsumexp(e32[np.array(brute[:c])].astype(np.float64))
+    np.testing.assert_allclose(lp.astype(np.float64), full_lp.astype(np.float64) + shift, atol=2e-6)
+    if c == 300:
+        np.testing.assert_array_equal(lp, full_lp)
+
+
+def test_efficient_head_stages_match_torch_and_brute_force():
+    """Random low-rank factors: the candidates are the brute-force top-c of
+    the low-rank scores computed with torch (z cast to bf16 between the two
+    products), the candidate logits equal torch's linear on the gathered LM
+    rows, and the top-k is the brute-force order of those logits."""
+    cfg, W, g, y = _bf16_setup(seed=51)
+    r, c, k = 8, 24, 6
+    A = O.bf16_round(g.standard_normal((300, r)))
+    Bm = O.bf16_round(g.standard_normal((r, 32)) * 0.3)
+    ids, lp, cand, cl = O.efficient_head_topk(cfg, W, y, A, Bm, c, k)
+    yt = torch.from_numpy(y[None])
+    z = torch.nn.functional.linear(yt, torch.from_numpy(Bm)).to(torch.bfloat16).double()
+    sc = torch.nn.functional.linear(z, torch.from_numpy(A)).numpy()[0].astype(np.float32)
+    brute = sorted(range(300), key=lambda t: (-sc[t], t))[:c]
+    assert list(cand) == brute
+    exact_c = torch.nn.functional.linear(yt, torch.from_numpy(np.asarray(W["lm"][np.array(brute)], np.float64))).numpy()[0]
+    np.testing.assert_allclose(cl, exact_c, rtol=1e-12, atol=1e-12)
+    e32 = exact_c.astype(np.float32)
+    order = sorted(range(c), key=lambda i: (-e32[i], brute[i]))[:k]
+    assert list(ids) == [brute[i] for i in order]
+    np.testing.assert_allclose(np.exp(lp.astype(np.float64)), softmax(e32.astype(np.float64))[order], rtol=1e-5)
+
+
+def test_efficient_head_ties_take_lowest_ids():
+    """An all-zero low-rank head scores every token equal: the candidates
+    are the c lowest ids, in id order."""
+    cfg, W, g, y = _bf16_setup(seed=52)
+    ids, lp, cand, cl = O.efficient_head_topk(cfg, W, y, np.zeros((300, 8)), np.zeros((8, 32)), 20, 4)
+    assert list(cand) == list(range(20))
+    assert set(ids.tolist()) <= set(range(20))
+
+
+def test_draft_cycle_with_exact_factor_head_equals_full_head():
+    """A whole draft cycle through the efficient head with B = I, A = W_lm
+    and c = V builds the same tree as the full head."""
+    cfg = tiny_shape(d=32, hq=4, hkv=2, hd=8, ffn=48, vocab=40, dtype=BF16)
+    W = {kk: (O.bf16_round(vv) if not kk.startswith("norm") else vv) for kk, vv in weights_f(cfg, std=0.25).items()}
+    g = np.random.default_rng(53)
+    n = 5
+    feats = O.bf16_round(g.standard_normal((n, 3, 32)) * 0.5)
+    toks = g.integers(0, 40, n)
+    Kc = np.zeros((n, 2, 8)); Vc = np.zeros((n, 2, 8))
+    a = O.draft_cycle(cfg, W, feats, toks, Kc, Vc, 0, 3, 3, 7)
+    b = O.draft_cycle(cfg, W, feats, toks, Kc, Vc, 0, 3, 3, 7, head=dict(A=W["lm"], B=np.eye(32), c=40))
+    for name in ("tok", "parent", "depth", "pos", "anc"):
+        np.testing.assert_array_equal(a[name], b[name])

@@ -141,6 +141,33 @@ def gen_weights(shape: DrafterShape, seed: int = 0, std: float = 0.02, only=None
     return W
 
 
+def gen_lowrank_head(shape: DrafterShape, rank: int, energy: float = 0.9, seed: int = 0,
+                     std: float = 0.02) -> dict:
+    """A synthetic LM head with a low-rank part, and that part's factors.
+
+    W_lm = a (P Q) + b E with P [V, rank] ~ N(0,1), Q [rank, d] ~ N(0,1)/sqrt(rank)
+    and E [V, d] ~ N(0,1), so every entry of P Q has unit variance; a^2 =
+    energy * std^2 and b^2 = (1 - energy) * std^2 keep the entries' standard
+    deviation at std while `energy` of it lies in the rank-`rank` part.  The
+    low-rank head is A = a P [V, rank] and B = Q [rank, d].  Returns dict(lm=,
+    a=, b=) as Tensors of the shape's dtype (each rounded once)."""
+    V, d = shape.vocab, shape.d
+    a = np.float32(std * math.sqrt(energy))
+    b = np.float32(std * math.sqrt(1.0 - energy))
+    P = normal_f32(seed, 41, (V, rank), 1.0)
+    Q = normal_f32(seed, 42, (rank, d), 1.0 / math.sqrt(rank))
+    lm = normal_f32(seed, 43, (V, d), 1.0)
+    lm *= b
+    step = 16384
+    for s0 in range(0, V, step):      # lm += a * P Q, row block by row block (float32)
+        lm[s0:s0 + step] += a * (P[s0:s0 + step] @ Q)
+    P *= a
+    if shape.dtype == BF16:
+        return dict(lm=Tensor(f32_to_bf16_bits(lm), BF16), a=Tensor(f32_to_bf16_bits(P), BF16),
+                    b=Tensor(f32_to_bf16_bits(Q), BF16))
+    return dict(lm=Tensor(lm, F32), a=Tensor(P, F32), b=Tensor(Q, F32))
+
+
 @dataclass
 class CycleInputs:
     """Inputs of one draft-tree cycle (batch B)."""
