@@ -99,7 +99,7 @@ def _oracle_request_kv(w, ci, b):
     return ci.kv_k.f32()[b].astype(np.float64), ci.kv_v.f32()[b].astype(np.float64)
 
 
-def cpu_baseline(w, Wt, ci, vin, reqs=None):
+def cpu_baseline(w, Wt, ci, vin, reqs=None, head=None):
     """The oracle as it stands, on the host cores: full cycles (fusion,
     commit, D-1 tree rounds, rerank and verification) of the requests
     `reqs` (default: all), scaled to whole-batch cycles per second.  vin =
@@ -109,13 +109,15 @@ def cpu_baseline(w, Wt, ci, vin, reqs=None):
     W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
     threads, desc = _host_info()
     L, mode, T, ut, ur = vin
+    if head is not None:
+        head = dict(A=head["A"].f32(), B=head["B"].f32(), c=head["c"])
     reqs = list(range(w.batch)) if reqs is None else list(reqs)
     n = w.commit_rows
     t0 = time.time()
     for b in reqs:
         Kc, Vc = _oracle_request_kv(w, ci, b)
         vt = O.draft_cycle(w.shape, W, ci.feats.f32()[b * n:(b + 1) * n], ci.tokens[b], Kc, Vc, int(ci.ctx_len[b]),
-                           w.topk, w.depth, w.keep)
+                           w.topk, w.depth, w.keep, head=head)
         if mode == "sample":
             O.verify_sample(vt["tok"], vt["parent"], L[b], ut[b], ur[b], T)
         else:
@@ -124,8 +126,9 @@ def cpu_baseline(w, Wt, ci, vin, reqs=None):
     per_cycle = dt * w.batch / len(reqs)
     what = ("request 0" if w.batch == 1 else
             f"requests {reqs} of {w.batch}, scaled by {w.batch}/{len(reqs)} (extrapolated)")
+    hd = " through the efficient LM head" if head is not None else ""
     return {"value": 1.0 / per_cycle, "unit": "draft-tree steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"full cycle(s) (fuse + commit + {w.depth - 1} tree rounds + rerank + {mode} verify) of "
+            "sample": f"full cycle(s) (fuse + commit + {w.depth - 1} tree rounds{hd} + rerank + {mode} verify) of "
                       f"{what}, fp64 NumPy, {dt:.1f} s; {desc}"}
 
 
@@ -168,7 +171,53 @@ def reporting_fields(w, ci=None):
                               + 2 * w.batch * 64 * s.n_kv_heads * s.head_dim * es}
 
 
-def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
+def make_drafter(w, Wt=None):
+    """Packed device drafter of workload w; with an efficient head the LM head
+    is drawn with its low-rank part (gen_lowrank_head) and the factors are
+    attached.  Returns (drafter, host weights, row-major LM head on the device
+    or None)."""
+    import torch
+
+    from eagle_draft_tree_amd.cycle import Drafter
+    from workloads import gen
+    Wt = dict(Wt) if Wt is not None else gen.gen_weights(w.shape, seed=0)
+    lm_rows = head = None
+    if w.lowrank_rank:
+        head = gen.gen_lowrank_head(w.shape, w.lowrank_rank, energy=w.lowrank_energy, seed=0)
+        Wt["lm"] = head["lm"]
+        lm_rows = head["lm"].torch("cuda")   # for the recall measurement only
+    dr = Drafter(w.shape, Wt, pack=True)
+    if w.lowrank_rank:
+        dr.set_lowrank_head(head["a"], head["b"], w.lowrank_rank, w.lowrank_candidates)
+        head = dict(A=head["a"], B=head["b"], c=w.lowrank_candidates)
+    torch.cuda.synchronize()
+    return dr, Wt, lm_rows, head
+
+
+def lowrank_recall(w, dr, buf, lm_rows):
+    """Recall of the efficient head on the cycle just run: for every drafted
+    LM-head row, the share of the full head's exact top-k (float32 logits of
+    torch's matmul on y = bf16(rms(h2) * gain), ties by lowest id) found
+    among the GPU's candidates."""
+    import torch
+    s, k = w.shape, w.topk
+    D = w.depth
+    h = [buf.h_tree[:, 0]] + [buf.h_tree[:, 1 + r * k:1 + (r + 1) * k].reshape(-1, s.d) for r in range(D - 1)]
+    cands = [buf.commit_cand[0][:, 0]] + [buf.round_cand[r][0].reshape(-1, w.lowrank_candidates)
+                                         for r in range(D - 1)]
+    hits = total = 0
+    gain = dr.tensors["norm_out"]
+    for hh, cc in zip(h, cands):
+        y = torch.nn.functional.rms_norm(hh.float(), (s.d,), gain, eps=s.rms_eps).to(torch.bfloat16).float()
+        logits = y @ lm_rows.float().t()
+        top = torch.topk(logits, k, dim=1, sorted=True).indices
+        for i in range(top.shape[0]):
+            hits += len(set(top[i].tolist()) & set(cc[i].tolist()))
+            total += k
+    return hits / max(total, 1)
+
+
+def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True, lm_rows=None):
     """Time `steps` cycles of workload w; returns the measurement dict and the
     cycle inputs.  Target logits: n_plant seeded sets, each planted (when the
     workload plants agreement) on the tree the drafter builds; the timed loop
@@ -297,6 +346,13 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         ms_steps = start.elapsed_time(end) / steps
         del gs
 
+    recall = None
+    if w.lowrank_rank and lm_rows is not None:
+        buf.keep_candidates(w.lowrank_candidates)
+        cycle(Ls[0])
+        torch.cuda.synchronize()
+        recall = lowrank_recall(w, dr, buf, lm_rows)
+        buf.commit_cand = buf.round_cand = None
     # algorithmic bytes: bf16 weights read once per round, every request's KV once per round
     es = 2
     d, F, V, hq, hkv, hd = s.d, s.ffn, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim
@@ -324,7 +380,18 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
         return out
 
     lm_bytes = [w_lm + r * d * es + lm_out_bytes(r) for r in rows]
+    if w.lowrank_rank:
+        # efficient head, stage 1 (the LM-head class): both low-rank factors, y,
+        # z written and read, the scores and their tile pairs; stage 2 (the top-k
+        # class) reads c rows of the full LM head per row
+        rr, cc = w.lowrank_rank, w.lowrank_candidates
+        lm_bytes = [V * rr * es + rr * d * es + r * d * es + 2 * r * rr * es + r * V * 4 + r * (V // 16) * 8
+                    for r in rows]
+        w_lm = V * rr * es + rr * d * es
+        bytes_cycle = w_fc + D * (w_layer + kv_round) + sum(lm_bytes) + sum(rows) * cc * d * es
     bytes_steps = D * (w_layer + kv_round) + sum(lm_bytes)  # the D draft steps
+    if w.lowrank_rank:
+        bytes_steps += sum(rows) * w.lowrank_candidates * d * es
     lm_flops = [2.0 * r * V * d for r in rows]
     lm_ms, lm_cnt = per_class["lm_head"]
     reps = lm_cnt // len(rows) if lm_cnt else 0
@@ -360,6 +427,13 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True):
                        "bytes_per_launch": res["lm_head"]["bytes_per_launch"],
                        "avg_launch_us": res["lm_head"]["avg_launch_us"]}
     res["reporting"] = reporting_fields(w, ci)
+    if w.lowrank_rank:
+        res["efficient_head"] = {"rank": w.lowrank_rank, "candidates": w.lowrank_candidates,
+                                 "lm_head_energy_in_rank": w.lowrank_energy,
+                                 "recall_at_k": round(recall, 4) if recall is not None else None,
+                                 "note": "LM-head class = both low-rank GEMMs + candidate selection; the exact "
+                                         "candidate logits and their top-k are in the top-k class"}
+        res["roofline"]["kernel"] = "efficient LM head, stage 1 (low-rank GEMMs + candidate selection)"
     if graph:
         res["cycle_ms_percentiles"] = cycle_pct
         gbs = bytes_steps / (ms_steps * 1e-3) / 1e9
@@ -446,7 +520,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e"], default=None,
                     help="run one workload only (profiling); the main line is then that workload's")
     ap.add_argument("--main-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
@@ -472,14 +546,23 @@ def main():
     from eagle_draft_tree_amd import binding as Bd
     from eagle_draft_tree_amd.cycle import Drafter
     from workloads import gen
-    from workloads.configs import C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT
+    from workloads.configs import (C2_8B_TREE, C2E_8B_TREE_LOWRANK, C3_8B_CHAIN, C4_70B_TREE, C4E_70B_TREE_LOWRANK,
+                                   C5_8B_TTT)
 
     Bd.load()
     t0 = time.time()
     s8 = C2_8B_TREE.shape
-    Wt8 = gen.gen_weights(s8, seed=0) if args.only != "c4" else None
-    dr8 = Drafter(s8, Wt8, pack=True) if Wt8 is not None else None
+    Wt8 = gen.gen_weights(s8, seed=0) if args.only not in ("c4", "c4e") else None
+    dr8 = Drafter(s8, Wt8, pack=True) if Wt8 is not None and args.only not in ("c2e",) else None
     setup_s = time.time() - t0
+    if args.only in ("c2e", "c4e"):
+        w = C2E_8B_TREE_LOWRANK if args.only == "c2e" else C4E_70B_TREE_LOWRANK
+        dr, Wt, lm_rows, head = make_drafter(w, Wt8)
+        r, ci, vin = cycle_bench(w, dr, args.steps, args.warmup, graph=not args.no_graph, lm_rows=lm_rows)
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline(w, Wt, ci, vin, None, head)
+        print(json.dumps(r), flush=True)
+        return
 
     # sampled requests of the batch-64 chain for its CPU baseline (the oracle
     # drafts one request at a time)
@@ -531,29 +614,45 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     # the GPU legs first, then every CPU baseline (host work only)
-    cpu_jobs = [("main", w, Wt8, ci, vin, None)]
+    cpu_jobs = [("main", w, Wt8, ci, vin, None, None)]
     if not args.main_only:
         wl = {}
         r3, ci3, vin3 = cycle_bench(C3_8B_CHAIN, dr8, max(args.steps // 2, 1), args.warmup, graph=not args.no_graph)
         wl[C3_8B_CHAIN.name] = r3
-        cpu_jobs.append((C3_8B_CHAIN.name, C3_8B_CHAIN, Wt8, ci3, vin3, c3_reqs))
+        cpu_jobs.append((C3_8B_CHAIN.name, C3_8B_CHAIN, Wt8, ci3, vin3, c3_reqs, None))
         r5, ti = ttt_bench(C5_8B_TTT, dr8, 5, 1)
         wl[C5_8B_TTT.name] = r5
-        cpu_jobs.append((C5_8B_TTT.name, C5_8B_TTT, Wt8, ti, None, None))
+        cpu_jobs.append((C5_8B_TTT.name, C5_8B_TTT, Wt8, ti, None, None, None))
         del dr8
+        torch.cuda.empty_cache()
+        # the 8B tree through the efficient LM head (same drafter, structured LM head)
+        w2e = C2E_8B_TREE_LOWRANK
+        dr2e, Wt2e, lm_rows, head2e = make_drafter(w2e, Wt8)
+        r2e, ci2e, vin2e = cycle_bench(w2e, dr2e, args.steps, args.warmup, graph=not args.no_graph, lm_rows=lm_rows)
+        wl[w2e.name] = r2e
+        cpu_jobs.append((w2e.name, w2e, Wt2e, ci2e, vin2e, None, head2e))
+        del dr2e, lm_rows
         torch.cuda.empty_cache()
         Wt70 = gen.gen_weights(C4_70B_TREE.shape, seed=0)
         dr70 = Drafter(C4_70B_TREE.shape, Wt70, pack=True)
         r4, ci4, vin4 = cycle_bench(C4_70B_TREE, dr70, max(args.steps // 3, 1), args.warmup, graph=not args.no_graph)
         wl[C4_70B_TREE.name] = r4
-        cpu_jobs.append((C4_70B_TREE.name, C4_70B_TREE, Wt70, ci4, vin4, None))
+        cpu_jobs.append((C4_70B_TREE.name, C4_70B_TREE, Wt70, ci4, vin4, None, None))
         del dr70
+        torch.cuda.empty_cache()
+        w4e = C4E_70B_TREE_LOWRANK
+        dr4e, Wt4e, lm_rows, head4e = make_drafter(w4e, Wt70)
+        r4e, ci4e, vin4e = cycle_bench(w4e, dr4e, max(args.steps // 3, 1), args.warmup, graph=not args.no_graph,
+                                       lm_rows=lm_rows)
+        wl[w4e.name] = r4e
+        cpu_jobs.append((w4e.name, w4e, Wt4e, ci4e, vin4e, None, head4e))
+        del dr4e, lm_rows
         torch.cuda.empty_cache()
         out["workloads"] = wl
     if not args.no_cpu_baseline:
-        for name, wk, Wt, inp, vi, reqs in cpu_jobs:
+        for name, wk, Wt, inp, vi, reqs, hd in cpu_jobs:
             print(f"cpu baseline: {wk.name}", file=sys.stderr, flush=True)
-            cb = cpu_baseline_ttt(wk, Wt, inp) if wk.ttt_seq else cpu_baseline(wk, Wt, inp, vi, reqs)
+            cb = cpu_baseline_ttt(wk, Wt, inp) if wk.ttt_seq else cpu_baseline(wk, Wt, inp, vi, reqs, hd)
             if name == "main":
                 out["cpu_baseline"] = cb
             else:

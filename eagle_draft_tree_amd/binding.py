@@ -46,6 +46,11 @@ class KV(ctypes.Structure):
                 ("ctx_len", vp), ("tk", vp), ("tv", vp)]
 
 
+class LowrankHead(ctypes.Structure):
+    _fields_ = [("a", vp), ("b", vp), ("rank", ctypes.c_int32), ("candidates", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
+
+
 class Eagle3Error(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__(f"{fn} failed: {code} ({msg})")
@@ -73,6 +78,8 @@ def load(path: str = LIB_PATH):
         "eagle3_ttt_workspace_size": ([P, I, I, I, ctypes.POINTER(SZ)], I),
         "eagle3_fuse": ([P, P, P, I, P, P, SZ, P], I),
         "eagle3_draft_step": ([P, P, P, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
+        "eagle3_draft_step_lowrank": ([P, P, P, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, P, P, P, SZ, P], I),
+        "eagle3_pack_matrix": ([P, I, I, P, SZ, P], I),
         "eagle3_tree_expand": ([I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "eagle3_verify": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P, SZ, P], I),
         "eagle3_verify_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
@@ -173,6 +180,22 @@ def eagle3_draft_step(dims, weights, kv, mode, B, rows, state, parent_slot, toke
         ptr(parent_slot), ptr(tokens), ptr(pos), ptr(anc), slot_base, k, topk_rows, ptr(h_tree),
         ptr(topk_id), ptr(topk_lp), ptr(logits_out), ptr(ws), ws.numel() * ws.element_size(),
         stream_ptr(stream)))
+
+
+def eagle3_draft_step_lowrank(dims, weights, kv, mode, B, rows, state, parent_slot, tokens, pos, anc, slot_base,
+                              k, topk_rows, h_tree, topk_id, topk_lp, logits_out, head, cand_out, cand_logits_out, ws,
+                              stream=None):
+    _check("eagle3_draft_step_lowrank", load().eagle3_draft_step_lowrank(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(kv), mode, B, rows, ptr(state),
+        ptr(parent_slot), ptr(tokens), ptr(pos), ptr(anc), slot_base, k, topk_rows, ptr(h_tree),
+        ptr(topk_id), ptr(topk_lp), ptr(logits_out), ctypes.byref(head), ptr(cand_out), ptr(cand_logits_out),
+        ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def eagle3_pack_matrix(src, n, k, dst, stream=None):
+    """Pack a bf16 matrix src [n][k] into dst (device tensor, n*k*2 bytes) in MFMA fragment order."""
+    _check("eagle3_pack_matrix", load().eagle3_pack_matrix(ptr(src), n, k, ptr(dst), dst.numel() * dst.element_size(),
+                                                           stream_ptr(stream)))
 
 
 def eagle3_tree_expand(phase, B, k, D, m, root_tok, root_pos, tree_state, topk_id, topk_lp,

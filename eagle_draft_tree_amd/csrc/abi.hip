@@ -152,11 +152,14 @@ int eagle3_fuse(const eagle3_dims* dims, const eagle3_weights* w, const void* fe
   return hip_status(e3::fuse_rows(*dims, *w, feats, n, g, ws, (hipStream_t)stream), "eagle3_fuse");
 }
 
-int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const eagle3_kv* kv, int mode,
-                      int B, int rows, const void* state, const int32_t* parent_slot,
-                      const int32_t* tokens, const int32_t* pos, const uint64_t* anc, int slot_base,
-                      int k, int topk_rows, float* h_tree, int32_t* topk_id, float* topk_lp,
-                      float* logits_out, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+}  // extern "C"
+
+namespace {
+int draft_step_impl(const eagle3_dims* dims, const eagle3_weights* w, const eagle3_kv* kv, int mode, int B,
+                    int rows, const void* state, const int32_t* parent_slot, const int32_t* tokens,
+                    const int32_t* pos, const uint64_t* anc, int slot_base, int k, int topk_rows, float* h_tree,
+                    int32_t* topk_id, float* topk_lp, float* logits_out, const eagle3_lowrank_head* lr,
+                    int32_t* cand_out, float* cand_logits_out, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
@@ -191,9 +194,53 @@ int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const ea
   const size_t need = e3::draft_ws_bytes(*dims, B, rows, cap_rows - rows > 0 ? cap_rows - rows : 0);
   REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
   REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (lr) {
+    REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "the efficient head needs bf16");
+    REQUIRE(lr->a && lr->b, EAGLE3_EINVAL, "low-rank factors a/b are NULL");
+    REQUIRE(lr->layout == EAGLE3_LAYOUT_ROWMAJOR || lr->layout == EAGLE3_LAYOUT_PACKED, EAGLE3_EINVAL,
+            "low-rank layout %d", lr->layout);
+    REQUIRE(lr->rank >= 64 && lr->rank % 64 == 0 && lr->rank <= dims->d, EAGLE3_EUNSUPPORTED,
+            "rank %d (a multiple of 64, at most d)", lr->rank);
+    REQUIRE(lr->candidates >= k && lr->candidates <= 256 && lr->candidates <= dims->vocab / 16, EAGLE3_EINVAL,
+            "candidates %d (k <= c <= 256, c <= vocab/16)", lr->candidates);
+    const int Rl = topk_rows == EAGLE3_TOPK_LAST ? B : B * rows;
+    REQUIRE(Rl <= 64, EAGLE3_EUNSUPPORTED, "the efficient head takes at most 64 LM-head rows (%d)", Rl);
+  }
   e3::DraftCall c{dims, w, kv, mode, B, rows, state, parent_slot, tokens, pos, anc, slot_base, k,
-                  topk_rows, h_tree, topk_id, topk_lp, logits_out, ws};
-  return hip_status(e3::draft_step(c, (hipStream_t)stream), "eagle3_draft_step");
+                  topk_rows, h_tree, topk_id, topk_lp, logits_out, ws, lr, cand_out, cand_logits_out};
+  return hip_status(e3::draft_step(c, (hipStream_t)stream), lr ? "eagle3_draft_step_lowrank" : "eagle3_draft_step");
+}
+}  // namespace
+
+extern "C" {
+
+int eagle3_draft_step(const eagle3_dims* dims, const eagle3_weights* w, const eagle3_kv* kv, int mode,
+                      int B, int rows, const void* state, const int32_t* parent_slot,
+                      const int32_t* tokens, const int32_t* pos, const uint64_t* anc, int slot_base,
+                      int k, int topk_rows, float* h_tree, int32_t* topk_id, float* topk_lp,
+                      float* logits_out, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+  return draft_step_impl(dims, w, kv, mode, B, rows, state, parent_slot, tokens, pos, anc, slot_base, k, topk_rows,
+                         h_tree, topk_id, topk_lp, logits_out, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int eagle3_draft_step_lowrank(const eagle3_dims* dims, const eagle3_weights* w, const eagle3_kv* kv, int mode,
+                              int B, int rows, const void* state, const int32_t* parent_slot,
+                              const int32_t* tokens, const int32_t* pos, const uint64_t* anc, int slot_base,
+                              int k, int topk_rows, float* h_tree, int32_t* topk_id, float* topk_lp,
+                              float* logits_out, const eagle3_lowrank_head* head, int32_t* cand_out,
+                              float* cand_logits_out, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+  REQUIRE(head, EAGLE3_EINVAL, "head is NULL");
+  return draft_step_impl(dims, w, kv, mode, B, rows, state, parent_slot, tokens, pos, anc, slot_base, k, topk_rows,
+                         h_tree, topk_id, topk_lp, logits_out, head, cand_out, cand_logits_out, ws, ws_bytes,
+                         stream);
+}
+
+int eagle3_pack_matrix(const void* src, int n, int k, void* dst, size_t dst_bytes, eagle3_stream_t stream) {
+  REQUIRE(src && dst, EAGLE3_EINVAL, "src/dst is NULL");
+  REQUIRE(n >= 16 && k >= 32 && n % 16 == 0 && k % 32 == 0, EAGLE3_EINVAL, "n=%d k=%d (multiples of 16 and 32)", n,
+          k);
+  REQUIRE(dst_bytes >= (size_t)n * k * 2, EAGLE3_EWORKSPACE, "dst %zu < %zu bytes", dst_bytes, (size_t)n * k * 2);
+  return hip_status(e3::pack_matrix(src, n, k, dst, (hipStream_t)stream), "eagle3_pack_matrix");
 }
 
 int eagle3_tree_expand(int phase, int B, int k, int D, int m, const int32_t* root_tok,

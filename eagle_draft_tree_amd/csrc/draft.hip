@@ -446,6 +446,9 @@ struct DraftWS {
   float* logits;
   void* topk;  // not used by the draft step: keeps eagle3_topk covered for R rows
   void* lmpart;  // LM-head partials: top-1 float4 [R][V/128 or V/512], or tile float2 [R][V/16 + pad]
+  void* lrz;     // efficient head: z = B y [R][rank <= d] (dtype)
+  int32_t* cand;  // efficient head: candidate ids [R][c <= 256]
+  float* cand_l;  // efficient head: their exact logits [R][c]
 };
 
 static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* base, DraftWS* w) {
@@ -472,6 +475,9 @@ static size_t layout_draft(const eagle3_dims& dm, int R, int cap_rows, void* bas
   // top-1 float4 [R][one per workgroup of 8 or 32 tiles] or tile pairs
   // float2 [R][V/16 + up to 8*tpw - 1 slots of padding, tpw <= 32]
   t.lmpart = bp.take((size_t)R * (dm.vocab / 16 + 256) * sizeof(float2));
+  t.lrz = bp.take((size_t)R * dm.d * es);
+  t.cand = (int32_t*)bp.take((size_t)R * LOWRANK_MAX_CAND * 4);
+  t.cand_l = (float*)bp.take((size_t)R * LOWRANK_MAX_CAND * 4);
   if (w) *w = t;
   return bp.off + 256;
 }
@@ -673,6 +679,63 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   }
   // ---- LM head + top-k
   float* logits = c.logits_out ? c.logits_out : ws.logits;
+  if (c.lr) {
+    // efficient head: z = B y, scores = A z with tile statistics, the c best
+    // scores as candidates, exact logits of the candidates, their top-k
+    const eagle3_lowrank_head& lr = *c.lr;
+    const bool lpk = lr.layout == EAGLE3_LAYOUT_PACKED;
+    const int r = lr.rank, nt16 = V / 16;
+    int32_t* cand = c.cand_out ? c.cand_out : ws.cand;
+    float* cand_l = c.cand_logits_out ? c.cand_logits_out : ws.cand_l;
+    {
+      TimedScope ts(EAGLE3_KC_LMHEAD, st);
+      const RowsPlan pz = plan_rows(Rl, r, d, bf, false);
+      EpiStore<T> ez{(T*)ws.lrz, r, plain};
+      if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)lr.b, d, r, plain, ez, pz, lpk, st)) != hipSuccess)
+        return e;
+      RowsPlan ps = plan_rows(Rl, V, r, bf, false);
+      // packed factors, up to 16 rows, rank 64/128/256: wave-owned tiles over
+      // the short K (the rank), no cross-wave reduction (lowrank.hip)
+      const bool own = bf && lpk && Rl <= 16 && (r == 64 || r == 128 || r == 256);
+      // packed factors, 17..64 rows: the register-weight kernel
+      const bool rx = !own && bf && lpk && Rl <= 64 && r % (32 * LM_RX_KU) == 0;
+      // row-major factors up to 16 rows: eight tiles per workgroup, one 32-wide
+      // k-group per wave, so that all eight waves stream
+      const bool small_k = !own && !rx && bf && Rl <= 16;
+      if (small_k) {
+        ps.t = 8;
+        ps.u = 1;
+        ps.waves = 8;
+        ps.splits = 1;
+        ps.tiles = (nt16 + 7) / 8;
+      }
+      const int tpw = own ? lowrank_scores_tpw() : rx ? LM_RX_TPW : bf && sk_ok(Rl, r, lpk) ? sk_bn(nt16, 1) / 16
+                                                                                              : ps.t;
+      float2* tpart = (float2*)ws.lmpart;
+      EpiLogitsTiles es{logits, V, tpart, tile_slots(nt16, tpw)};
+      if (own) {
+        if ((e = launch_lowrank_scores(lr.a, ws.lrz, Rl, r, V, logits, tpart, st)) != hipSuccess) return e;
+      } else if (rx) {
+        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>
+            <<<(nt16 + tpw - 1) / tpw, LM_RX_WAVES * 64, 0, st>>>((const bf16*)ws.lrz, r, Rl, (const bf16*)lr.a, r,
+                                                                   nt16, 1, es);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      } else if (small_k) {
+        if constexpr (sizeof(T) == 2) {
+          if ((e = rows_gemm_launch<T, 8, 1, 1, 8>((const T*)ws.lrz, r, Rl, (const T*)lr.a, r, V, plain, es, ps, lpk,
+                                                   st)) != hipSuccess)
+            return e;
+        }
+      } else if ((e = rows_gemm<T>((const T*)ws.lrz, r, Rl, (const T*)lr.a, r, V, plain, es, ps, lpk, st)) !=
+                 hipSuccess) {
+        return e;
+      }
+      if ((e = launch_lowrank_select(logits, tpart, tpw, Rl, V, lr.candidates, cand, st)) != hipSuccess) return e;
+    }
+    TimedScope ts(EAGLE3_KC_TOPK, st);
+    return launch_lowrank_exact(w.lm, pk, ws.y, Rl, d, V, lr.candidates, c.k, cand, cand_l, c.topk_id, c.topk_lp,
+                                st);
+  }
   // top-1 without kept logits on the skinny GEMM: the LM head writes per-
   // workgroup (max, sum exp, argmax) partials instead of the logits
   if (c.k == 1 && !c.logits_out && bf && Rl <= 64 && sk_ok(Rl, d, pk)) {

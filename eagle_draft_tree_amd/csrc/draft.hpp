@@ -22,6 +22,10 @@ struct DraftCall {
   float* topk_lp;
   float* logits_out;
   void* ws;
+  // efficient LM head (NULL: the full head); optional candidate outputs
+  const eagle3_lowrank_head* lr = nullptr;
+  int32_t* cand_out = nullptr;
+  float* cand_logits_out = nullptr;
 };
 
 size_t draft_ws_bytes(const eagle3_dims& dm, int B, int max_rows, int max_ctx);

@@ -36,6 +36,24 @@ hipError_t launch_top1_merge(const float4* part, int rows, int nparts, int32_t* 
 hipError_t launch_topk_tiles(const float* logits, const float2* part, int tiles_per_wg, int rows, int V, int k,
                              int32_t* ids, float* lp, hipStream_t st);
 
+// ---- efficient LM head (lowrank.hip)
+constexpr int LOWRANK_MAX_CAND = 256;
+// stage-1 scores of up to 16 rows from packed A [V][rank] (rank 64, 128 or
+// 256) and z [rows][rank], with per-tile row maxima in the slots of
+// tile_slots(V/16, lowrank_scores_tpw())
+int lowrank_scores_tpw();
+hipError_t launch_lowrank_scores(const void* A, const void* z, int rows, int rank, int V, float* scores,
+                                 float2* part, hipStream_t st);
+// candidates [rows][c]: the c best low-rank scores [rows][V] by (value desc,
+// id asc), from the scores and the per-tile pairs EpiLogitsTiles wrote
+hipError_t launch_lowrank_select(const float* scores, const float2* part, int tiles_per_wg, int rows, int V, int c,
+                                 int32_t* cand, hipStream_t st);
+// exact logits of the candidates (bf16 LM head, packed or row-major, and
+// bf16 y [rows][d]) -> cand_logits [rows][c]; then the top-k of the
+// candidates and lp normalised over them -> ids/lp [rows][k]
+hipError_t launch_lowrank_exact(const void* W_lm, bool packed, const void* y, int rows, int d, int V, int c, int k,
+                                const int32_t* cand, float* cand_logits, int32_t* ids, float* lp, hipStream_t st);
+
 // ---- dynamic tree (tree.hip)
 size_t tree_state_bytes_per_req(int k, int D);
 hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32_t* root_tok,

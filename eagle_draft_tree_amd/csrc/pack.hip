@@ -76,4 +76,13 @@ hipError_t pack_weights(const eagle3_dims& dm, const eagle3_weights& src, void* 
   return hipSuccess;
 }
 
+hipError_t pack_matrix(const void* src, int n, int k, void* dst, hipStream_t st) {
+  RowMap map{MAP_PLAIN, 0, 0};
+  const size_t total = (size_t)(n / 16) * (k / 32) * 64;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 65535) blocks = 65535;
+  pack_kernel<<<blocks, 256, 0, st>>>((const bf16*)src, k, n, map, (uint4*)dst);
+  return hipGetLastError();
+}
+
 }  // namespace e3

@@ -459,17 +459,22 @@ __global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __r
     if (mx[j] > -INFINITY) s += sx[j] * expf(mx[j] - M);
   s = wave_sum(s);
   if (lane == 0) sred[w] = s;
+  // the unrolled loop only compares and appends slot indices; the tile of a
+  // slot (two integer divisions) is taken in a rolled pass over the listed
+  // slots, which keeps the kernel's code (fetched cold by each of its few
+  // workgroups) small
 #pragma unroll
   for (int j = 0; j < TT_TPT; ++j) {
     const int sj = tid + TT_THREADS * j;
     if (sj < ns && mx[j] >= T) {
-      const int t = sl.tile(sj);
-      if (t >= 0) {
-        const int pos = atomicAdd(&ntile, 1);
-        if (pos < TT_TILES) tlist[pos] = t;
-      }
+      const int pos = atomicAdd(&ntile, 1);
+      if (pos < TT_TILES) tlist[pos] = sj;
     }
   }
+  __syncthreads();
+  // a padding slot (no tile) becomes -1, skipped below: it holds -inf, so it
+  // reaches T only when T is -inf
+  for (int i = tid; i < min(ntile, TT_TILES); i += TT_THREADS) tlist[i] = sl.tile(tlist[i]);
   __syncthreads();
   float S = 0.f;
 #pragma unroll
@@ -485,7 +490,8 @@ __global__ __launch_bounds__(TT_THREADS) void topk_tiles_kernel(const float* __r
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int e = e0 + tid + u * TT_THREADS;
-        id0[u] = e < 4 * NT ? tlist[e >> 2] * 16 + (e & 3) * 4 : -1;
+        const int tt = e < 4 * NT ? tlist[e >> 2] : -1;  // -1: past the list, or a padding slot
+        id0[u] = tt >= 0 ? tt * 16 + (e & 3) * 4 : -1;
         f[u] = id0[u] >= 0 ? *(const float4*)(x + id0[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll

@@ -39,6 +39,23 @@ class Drafter:
             torch.cuda.synchronize()
             for n in ("fc", "qkv", "o", "gate_up", "down", "lm"):
                 del self.tensors[n]
+        self.head = None
+
+    def set_lowrank_head(self, a, b, rank, candidates, device="cuda"):
+        """Use the efficient LM head (EAGLE-4): low-rank factors a [V, rank]
+        and b [rank, d] (generator Tensors or arrays), the `candidates` best
+        low-rank scores per row re-scored exactly.  Packed like the drafter."""
+        ta = a.torch(device) if hasattr(a, "torch") else torch.as_tensor(a).to(device)
+        tb = b.torch(device) if hasattr(b, "torch") else torch.as_tensor(b).to(device)
+        layout = B.LAYOUT_ROWMAJOR
+        if self.packed is not None:
+            pa, pb = torch.empty_like(ta), torch.empty_like(tb)
+            B.eagle3_pack_matrix(ta, ta.shape[0], ta.shape[1], pa)
+            B.eagle3_pack_matrix(tb, tb.shape[0], tb.shape[1], pb)
+            torch.cuda.synchronize()
+            ta, tb, layout = pa, pb, B.LAYOUT_PACKED
+        self.head_tensors = (ta, tb)
+        self.head = B.LowrankHead(ta.data_ptr(), tb.data_ptr(), rank, candidates, layout)
 
 
 @dataclass
@@ -86,6 +103,15 @@ class CycleBuffers:
         self.vws = torch.zeros(B.verify_workspace_size(Bn, m, s.vocab), dtype=torch.uint8, device=dv)
         self.commit_logits = None
         self.round_logits = None
+        self.commit_cand = self.round_cand = None  # efficient head: candidate ids and exact logits (tests)
+
+    def keep_candidates(self, c, device="cuda"):
+        """Also write the efficient head's candidates and their exact logits (tests)."""
+        Bn, k, D = self.spec.batch, self.spec.k, self.spec.depth
+        mk = lambda rows: (torch.empty(Bn, rows, c, dtype=torch.int32, device=device),
+                           torch.empty(Bn, rows, c, dtype=torch.float32, device=device))
+        self.commit_cand = mk(1)
+        self.round_cand = [mk(k) for _ in range(max(D - 1, 0))]
 
     def keep_logits(self, vocab, device="cuda"):
         """Also write LM-head logits (for parity checks; not on the hot path)."""
@@ -93,6 +119,19 @@ class CycleBuffers:
         self.commit_logits = torch.empty(Bn, 1, vocab, dtype=torch.float32, device=device)
         self.round_logits = [torch.empty(Bn, k, vocab, dtype=torch.float32, device=device)
                              for _ in range(max(D - 1, 0))]
+
+
+def draft_step(dr: Drafter, buf: CycleBuffers, kv, mode, Bn, rows, state, parent, tokens, pos, anc, slot_base, k,
+               topk_rows, ids, lp, logits, cand=None):
+    """One eagle3_draft_step, through the efficient head when the drafter has one."""
+    if dr.head is None:
+        B.eagle3_draft_step(dr.dims, dr.weights, kv, mode, Bn, rows, state, parent, tokens, pos, anc, slot_base, k,
+                            topk_rows, buf.h_tree, ids, lp, logits, buf.ws)
+    else:
+        B.eagle3_draft_step_lowrank(dr.dims, dr.weights, kv, mode, Bn, rows, state, parent, tokens, pos, anc,
+                                    slot_base, k, topk_rows, buf.h_tree, ids, lp, logits, dr.head,
+                                    cand[0] if cand is not None else None, cand[1] if cand is not None else None,
+                                    buf.ws)
 
 
 class KVCache:
@@ -123,15 +162,14 @@ def run_draft_steps(dr: Drafter, buf: CycleBuffers, kv: KVCache, tokens, commit_
     Bn, n, k, D = sp.batch, sp.commit_rows, sp.k, sp.depth
     kv_commit = kv.struct()
     kv_tree = kv.struct(ctx_after)
-    B.eagle3_draft_step(dr.dims, dr.weights, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos,
-                        None, 0, k, B.TOPK_LAST, buf.h_tree, buf.root_ids, buf.root_lp,
-                        buf.commit_logits, buf.ws)
+    draft_step(dr, buf, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos, None, 0, k, B.TOPK_LAST,
+               buf.root_ids, buf.root_lp, buf.commit_logits, buf.commit_cand)
     for j in range(2, D + 1):
         r = j - 2
-        B.eagle3_draft_step(dr.dims, dr.weights, kv_tree, B.TREE, Bn, k, None, buf.next_par[r],
-                            buf.next_tok[r], buf.next_pos[r], buf.next_anc[r], r * k, k, B.TOPK_ALL,
-                            buf.h_tree, buf.round_ids[r], buf.round_lp[r],
-                            buf.round_logits[r] if buf.round_logits is not None else None, buf.ws)
+        draft_step(dr, buf, kv_tree, B.TREE, Bn, k, None, buf.next_par[r], buf.next_tok[r], buf.next_pos[r],
+                   buf.next_anc[r], r * k, k, B.TOPK_ALL, buf.round_ids[r], buf.round_lp[r],
+                   buf.round_logits[r] if buf.round_logits is not None else None,
+                   buf.round_cand[r] if buf.round_cand is not None else None)
 
 
 def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit_pos, ctx_after,
@@ -144,18 +182,17 @@ def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit
     B.eagle3_fuse(dr.dims, dr.weights, feats, Bn * n, buf.g, buf.ws)
     kv_commit = kv.struct()
     kv_tree = kv.struct(ctx_after)
-    B.eagle3_draft_step(dr.dims, dr.weights, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos,
-                        None, 0, k, B.TOPK_LAST, buf.h_tree, buf.root_ids, buf.root_lp,
-                        buf.commit_logits, buf.ws)
+    draft_step(dr, buf, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos, None, 0, k, B.TOPK_LAST,
+               buf.root_ids, buf.root_lp, buf.commit_logits, buf.commit_cand)
     B.eagle3_tree_expand(B.INIT, Bn, k, D, m, root_tok, root_pos, buf.tree_state, buf.root_ids, buf.root_lp,
                          buf.next_tok[0] if D > 1 else buf.v_tok, buf.next_par[0] if D > 1 else buf.v_tok,
                          buf.next_pos[0] if D > 1 else buf.v_tok, buf.next_anc[0] if D > 1 else buf.v_anc)
     for j in range(2, D + 1):
         r = j - 2
-        B.eagle3_draft_step(dr.dims, dr.weights, kv_tree, B.TREE, Bn, k, None, buf.next_par[r],
-                            buf.next_tok[r], buf.next_pos[r], buf.next_anc[r], r * k, k, B.TOPK_ALL,
-                            buf.h_tree, buf.round_ids[r], buf.round_lp[r],
-                            buf.round_logits[r] if buf.round_logits is not None else None, buf.ws)
+        draft_step(dr, buf, kv_tree, B.TREE, Bn, k, None, buf.next_par[r], buf.next_tok[r], buf.next_pos[r],
+                   buf.next_anc[r], r * k, k, B.TOPK_ALL, buf.round_ids[r], buf.round_lp[r],
+                   buf.round_logits[r] if buf.round_logits is not None else None,
+                   buf.round_cand[r] if buf.round_cand is not None else None)
         nr = r + 1 if j < D else r  # the last STEP emits no rows (buffers unused)
         B.eagle3_tree_expand(B.STEP, Bn, k, D, m, None, None, buf.tree_state, buf.round_ids[r],
                              buf.round_lp[r], buf.next_tok[nr], buf.next_par[nr], buf.next_pos[nr],

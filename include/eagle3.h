@@ -218,6 +218,44 @@ int eagle3_draft_step(const eagle3_dims *dims, const eagle3_weights *w, const ea
                       float *topk_lp, float *logits_out, void *ws, size_t ws_bytes,
                       eagle3_stream_t stream);
 
+/* Step 3, efficient variant -- the two-stage draft LM head of EAGLE-4 (EAGLE-4
+ * blog, 10100.com: the paragraph "EAGLE Efficient LM Head" and the section
+ * 关于 Efficient LM Head).  Stage 1: a low-rank head scores every token,
+ * s = a . (b . y) with y = rms(h2)*norm_out (b . y rounded to bf16 like every
+ * GEMM input), and the `candidates` best float32 scores (score desc, id asc)
+ * become the candidates.  Stage 2: the full LM head computes the exact logits
+ * of the candidates only.  The top-k are the k best candidates by (exact
+ * logit desc, id asc); lp = logit - logsumexp over the candidates (the draft
+ * distribution restricted to the candidate set).
+ *  a           [vocab, rank] bf16, b [rank, d] bf16, row-major or packed
+ *              (eagle3_pack_matrix) as `layout` says
+ *  rank        a multiple of 64, at most d
+ *  candidates  k <= candidates <= 256 and <= vocab/16 */
+typedef struct eagle3_lowrank_head {
+  const void *a, *b;
+  int32_t rank, candidates, layout;
+} eagle3_lowrank_head;
+
+/* eagle3_draft_step with the LM head replaced by the efficient head `head`
+ * (same arguments and outputs otherwise; the full LM head `w->lm` is only
+ * read for the candidates' rows).  logits_out, if not NULL, receives the
+ * stage-1 scores [B][rows or 1][vocab]; cand_out / cand_logits_out, if not
+ * NULL, the candidate ids (by score) [..][candidates] and their exact
+ * logits.  Requires bf16, at most 64 LM-head rows (EAGLE3_EUNSUPPORTED
+ * otherwise). */
+int eagle3_draft_step_lowrank(const eagle3_dims *dims, const eagle3_weights *w, const eagle3_kv *kv,
+                              int mode, int B, int rows, const void *state, const int32_t *parent_slot,
+                              const int32_t *tokens, const int32_t *pos, const uint64_t *anc,
+                              int slot_base, int k, int topk_rows, float *h_tree, int32_t *topk_id,
+                              float *topk_lp, float *logits_out, const eagle3_lowrank_head *head,
+                              int32_t *cand_out, float *cand_logits_out, void *ws, size_t ws_bytes,
+                              eagle3_stream_t stream);
+
+/* Copy one bf16 matrix src [n][k] (row-major, device) into dst (device,
+ * dst_bytes >= n*k*2) in the MFMA fragment order of eagle3_pack_weights
+ * (plain row order).  n a multiple of 16, k of 32.  Enqueued on `stream`. */
+int eagle3_pack_matrix(const void *src, int n, int k, void *dst, size_t dst_bytes, eagle3_stream_t stream);
+
 /* Step 3b -- EAGLE-2 confidence-value dynamic tree and rerank ("EAGLE-3 精读"
  * §2; EAGLE-4 blog, 几条技术路线正在收敛: confidence = product of draft
  * probabilities, kept here as a float32 sum of log-probs).

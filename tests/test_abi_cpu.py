@@ -183,3 +183,32 @@ def test_model_width_above_row_kernel_limit(blib):
     assert lib.eagle3_fuse(ctypes.byref(d), ctypes.byref(w), _P, 1, _P, _P, 1 << 40, None) == blib.EUNSUPPORTED
     d.d = 8192
     assert blib.workspace_size(d, 1, 10, 4096) > 0
+
+
+def test_efficient_head_argument_checks(blib):
+    """eagle3_draft_step_lowrank rejects bad low-rank heads on the host."""
+    from workloads.configs import L8B_SHAPE, TINY_SHAPE
+    lib = blib.load()
+    d = blib.dims_of(L8B_SHAPE)
+    w = _fake_weights(blib)
+    kv = _fake_kv(blib)
+    ws = 1 << 40
+
+    def call(head, dims=d, rows=10, k=10, topk_rows=None):
+        return lib.eagle3_draft_step_lowrank(
+            ctypes.byref(dims), ctypes.byref(w), ctypes.byref(kv), blib.TREE, 1, rows, None, _P, _P, _P, _P, 0, k,
+            blib.TOPK_ALL if topk_rows is None else topk_rows, _P, _P, _P, None,
+            ctypes.byref(head) if head is not None else None, None, None, _P, ws, None)
+    H = lambda rank=256, c=64, layout=0, a=0x10000: blib.LowrankHead(a, 0x10000, rank, c, layout)
+    assert call(None) == blib.EINVAL                      # no head
+    assert call(H(a=0)) == blib.EINVAL                    # NULL factor
+    assert call(H(rank=96)) == blib.EUNSUPPORTED          # rank not a multiple of 64
+    assert call(H(rank=8192)) == blib.EUNSUPPORTED        # rank above d
+    assert call(H(c=8)) == blib.EINVAL                    # fewer candidates than k
+    assert call(H(c=300)) == blib.EINVAL                  # more than 256 candidates
+    assert call(H(layout=5)) == blib.EINVAL
+    assert call(H(), rows=65) == blib.ECAPACITY           # more than 64 rows (draft-step limit)
+    f32 = blib.dims_of(TINY_SHAPE)
+    assert call(H(rank=64), dims=f32, k=2) == blib.EUNSUPPORTED  # fp32 drafter
+    assert lib.eagle3_pack_matrix(_P, 100, 64, _P, 1 << 20, None) == blib.EINVAL
+    assert lib.eagle3_pack_matrix(_P, 128, 64, _P, 100, None) == blib.EWORKSPACE

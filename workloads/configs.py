@@ -59,6 +59,12 @@ class Workload:
     # TTT
     ttt_seq: int = 0
     ttt_steps: int = 5
+    # efficient LM head (EAGLE-4): low-rank rank and candidates (0 = the full
+    # head); the LM head is then drawn with a rank-`lowrank_rank` part holding
+    # `lowrank_energy` of its entry variance, and that part is the low-rank head
+    lowrank_rank: int = 0
+    lowrank_candidates: int = 0
+    lowrank_energy: float = 0.9
 
 
 TINY_SHAPE = DrafterShape("tiny-d256", d=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
@@ -98,6 +104,13 @@ C5_8B_TTT = Workload(
     "llama3.1-8b-drafter-ttt-b8x2048-r5", L8B_SHAPE, batch=8, ttt_seq=2048, ttt_steps=5)
 
 CONFIGS = [C1_TINY, C2_8B_TREE, C3_8B_CHAIN, C4_70B_TREE, C5_8B_TTT]
+
+# The 8B and 70B trees through EAGLE-4's efficient LM head: rank 256, the 64
+# best low-rank scores re-scored exactly (an opt-in mode beside the full head).
+C2E_8B_TREE_LOWRANK = replace(C2_8B_TREE, name="llama3.1-8b-drafter-b1-tree6x10-keep60-lowrank256-c64",
+                              lowrank_rank=256, lowrank_candidates=64)
+C4E_70B_TREE_LOWRANK = replace(C4_70B_TREE, name="llama3.3-70b-drafter-b1-tree6x10-keep60-lowrank256-c64",
+                               lowrank_rank=256, lowrank_candidates=64)
 
 
 def tiny_shape(d=16, hq=2, hkv=1, hd=8, ffn=32, vocab=8, dtype=F32, theta=10000.0, name=None):
