@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
         "eagle3_packed_weights_size": ([P, ctypes.POINTER(SZ)], I),
         "eagle3_pack_weights": ([P, P, P, SZ, P, P], I),
         "eagle3_timing_read": ([I, P, P], I),
+        "eagle3_timing_mode": ([I, I], I),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -242,11 +243,16 @@ def eagle3_topk(logits, rows, V, k, ids, lp, lse, ws, stream=None):
 
 # ---------------------------------------------------------------- kernel timing
 KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10,
-          ttt_gemm=11, ttt_attn=12, ttt_ce=13)
+          ttt_gemm=11, ttt_attn=12, ttt_ce=13, lr_scores=14)
 
 
 def timing_enable(kc: int, max_launches: int):
     _check("eagle3_timing_enable", load().eagle3_timing_enable(kc, max_launches))
+
+
+def timing_mode(kc: int, mode: int):
+    """0: events around each launch scope of the class; 1: the class's principal kernel's own start/stop."""
+    _check("eagle3_timing_mode", load().eagle3_timing_mode(kc, mode))
 
 
 def timing_read(kc: int):

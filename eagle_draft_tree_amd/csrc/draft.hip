@@ -340,23 +340,24 @@ static inline bool lm_rx_ok(int R, int K, bool packed) { return sk_ok(R, K, pack
 // chunks beyond 64 are launched separately with shifted pointers (no split).
 template <typename TW, int T, int NT, int U, int WAVES, class Epi>
 static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
-                                   const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
+                                   const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st, int kc = -1) {
   const int nt16 = N / 16;
   const int grid = p.tiles * p.splits;
   const size_t lds = sizeof(TW) == 2 ? (size_t)WAVES * T * NT * 256 * sizeof(float) : 0;
   if (packed)
-    rows_gemm_kernel<TW, T, NT, U, WAVES, true, Epi>
-        <<<grid, WAVES * 64, lds, st>>>(X, ldx, R, W, K, nt16, p.splits, map, epi);
+    launch_timed(kc, rows_gemm_kernel<TW, T, NT, U, WAVES, true, Epi>, dim3(grid), dim3(WAVES * 64), lds, st, X, ldx,
+                 R, W, K, nt16, p.splits, map, epi);
   else
-    rows_gemm_kernel<TW, T, NT, U, WAVES, false, Epi>
-        <<<grid, WAVES * 64, lds, st>>>(X, ldx, R, W, K, nt16, p.splits, map, epi);
+    launch_timed(kc, rows_gemm_kernel<TW, T, NT, U, WAVES, false, Epi>, dim3(grid), dim3(WAVES * 64), lds, st, X, ldx,
+                 R, W, K, nt16, p.splits, map, epi);
   return hipGetLastError();
 }
 
 // The template arguments below must match plan_rows (T, U, waves per NT).
+// kc >= 0: the launch is the principal kernel of timing class kc (kernel mode)
 template <typename TW, class Epi>
 static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
-                            const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st) {
+                            const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st, int kc = -1) {
   if constexpr (std::is_same<Epi, EpiPartial>::value) {
     // split-K layer GEMMs of 17..64 rows: weights streamed into registers
     if (sizeof(TW) == 2 && sk_ok(R, K, packed) && p.splits > 1 && p.splits == rx_splits(K)) {
@@ -374,22 +375,24 @@ static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int
     const int grid = (nt16 + bn / 16 - 1) / (bn / 16) * p.splits;
     const bf16* Xb = (const bf16*)X;
     const bf16* Wb = (const bf16*)W;
-    if (bn == 128) skinny_gemm_kernel<128, Epi><<<grid, 256, 0, st>>>(Xb, ldx, R, Wb, K, nt16, p.splits, epi);
-    else skinny_gemm_kernel<64, Epi><<<grid, 256, 0, st>>>(Xb, ldx, R, Wb, K, nt16, p.splits, epi);
+    if (bn == 128)
+      launch_timed(kc, skinny_gemm_kernel<128, Epi>, dim3(grid), dim3(256), 0, st, Xb, ldx, R, Wb, K, nt16, p.splits, epi);
+    else
+      launch_timed(kc, skinny_gemm_kernel<64, Epi>, dim3(grid), dim3(256), 0, st, Xb, ldx, R, Wb, K, nt16, p.splits, epi);
     return hipGetLastError();
   }
   if (sizeof(TW) == 2) {
     switch (p.nt) {
       case 1:
-        if (p.t == 1) return rows_gemm_launch<TW, 1, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
-        return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st);
-      case 2: return rows_gemm_launch<TW, 4, 2, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
-      case 3: return rows_gemm_launch<TW, 4, 3, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
-      default: return rows_gemm_launch<TW, 4, 4, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st);
+        if (p.t == 1) return rows_gemm_launch<TW, 1, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
+        return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
+      case 2: return rows_gemm_launch<TW, 4, 2, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
+      case 3: return rows_gemm_launch<TW, 4, 3, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
+      default: return rows_gemm_launch<TW, 4, 4, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
     }
   }
-  if (p.nt == 1) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st);
-  return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st);
+  if (p.nt == 1) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
+  return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
 }
 
 // ---------------------------------------------------------------------------
@@ -714,6 +717,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       float2* tpart = (float2*)ws.lmpart;
       EpiLogitsTiles es{logits, V, tpart, tile_slots(nt16, tpw)};
       if (own) {
+        TimedScope ts2(EAGLE3_KC_LR_SCORES, st);
         if ((e = launch_lowrank_scores(lr.a, ws.lrz, Rl, r, V, logits, tpart, st)) != hipSuccess) return e;
       } else if (rx) {
         rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>
@@ -748,11 +752,16 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       EpiTop1Part epi{(float4*)ws.lmpart, nwg};
       const bf16* Xb = (const bf16*)ws.y;
       const bf16* Wb = (const bf16*)w.lm;
+      constexpr int KL = EAGLE3_KC_LMHEAD;
       if (rx)
-        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part, LM_RX_WAVES>
-            <<<nwg, LM_RX_WAVES * 64, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
-      else if (tpw == 8) skinny_gemm_kernel<128, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
-      else skinny_gemm_kernel<64, EpiTop1Part><<<nwg, 256, 0, st>>>(Xb, d, Rl, Wb, d, nt16, 1, epi);
+        launch_timed(KL, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part, LM_RX_WAVES>, dim3(nwg),
+                     dim3(LM_RX_WAVES * 64), 0, st, Xb, d, Rl, Wb, d, nt16, 1, epi);
+      else if (tpw == 8)
+        launch_timed(KL, skinny_gemm_kernel<128, EpiTop1Part>, dim3(nwg), dim3(256), 0, st, Xb, d, Rl, Wb, d, nt16, 1,
+                     epi);
+      else
+        launch_timed(KL, skinny_gemm_kernel<64, EpiTop1Part>, dim3(nwg), dim3(256), 0, st, Xb, d, Rl, Wb, d, nt16, 1,
+                     epi);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     TimedScope ts(EAGLE3_KC_TOPK, st);
@@ -772,12 +781,12 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       TimedScope ts(EAGLE3_KC_LMHEAD, st);
       EpiLogitsTiles epi{logits, V, tpart, tile_slots(nt16, tpw)};
       if (rx) {
-        rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>
-            <<<(nt16 + tpw - 1) / tpw, LM_RX_WAVES * 64, 0, st>>>((const bf16*)ws.y, d, Rl, (const bf16*)w.lm, d,
-                                                                   nt16, 1, epi);
+        launch_timed(EAGLE3_KC_LMHEAD, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>,
+                     dim3((nt16 + tpw - 1) / tpw), dim3(LM_RX_WAVES * 64), 0, st, (const bf16*)ws.y, d, Rl,
+                     (const bf16*)w.lm, d, nt16, 1, epi);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-      } else if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) !=
-                 hipSuccess) {
+      } else if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st,
+                                   EAGLE3_KC_LMHEAD)) != hipSuccess) {
         return e;
       }
     }
@@ -790,8 +799,8 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       const int Rc = Rl - r0 < 64 ? Rl - r0 : 64;
       EpiStore<float> epi{logits + (size_t)r0 * V, V, plain};
       const RowsPlan pc = plan_rows(Rc, V, d, bf, false);
-      if ((e = rows_gemm<T>((const T*)ws.y + (size_t)r0 * d, d, Rc, (const T*)w.lm, d, V, plain, epi, pc, pk, st)) !=
-          hipSuccess)
+      if ((e = rows_gemm<T>((const T*)ws.y + (size_t)r0 * d, d, Rc, (const T*)w.lm, d, V, plain, epi, pc, pk, st,
+                            EAGLE3_KC_LMHEAD)) != hipSuccess)
         return e;
     }
   }

@@ -15,6 +15,7 @@
 #include "common.hpp"
 #include "gemm_rows.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace e3 {
 
@@ -472,16 +473,16 @@ hipError_t launch_lowrank_scores(const void* A, const void* z, int rows, int ran
   if (rows > 16) return hipErrorInvalidValue;
   switch (rank) {
     case 64:
-      lowrank_scores_kernel<2><<<grid, SC_WAVES * 64, 0, st>>>((const bf16*)A, (const bf16*)z, rows, nt16, V, scores,
-                                                                part, sl);
+      launch_timed(EAGLE3_KC_LR_SCORES, lowrank_scores_kernel<2>, dim3(grid), dim3(SC_WAVES * 64), 0, st,
+                   (const bf16*)A, (const bf16*)z, rows, nt16, V, scores, part, sl);
       break;
     case 128:
-      lowrank_scores_kernel<4><<<grid, SC_WAVES * 64, 0, st>>>((const bf16*)A, (const bf16*)z, rows, nt16, V, scores,
-                                                                part, sl);
+      launch_timed(EAGLE3_KC_LR_SCORES, lowrank_scores_kernel<4>, dim3(grid), dim3(SC_WAVES * 64), 0, st,
+                   (const bf16*)A, (const bf16*)z, rows, nt16, V, scores, part, sl);
       break;
     case 256:
-      lowrank_scores_kernel<8><<<grid, SC_WAVES * 64, 0, st>>>((const bf16*)A, (const bf16*)z, rows, nt16, V, scores,
-                                                                part, sl);
+      launch_timed(EAGLE3_KC_LR_SCORES, lowrank_scores_kernel<8>, dim3(grid), dim3(SC_WAVES * 64), 0, st,
+                   (const bf16*)A, (const bf16*)z, rows, nt16, V, scores, part, sl);
       break;
     default:
       return hipErrorInvalidValue;

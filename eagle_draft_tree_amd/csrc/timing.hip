@@ -8,6 +8,7 @@ namespace e3 {
 namespace {
 struct ClassTiming {
   bool on = false;
+  int mode = 0;  // 0: events around the class's scopes; 1: the principal kernel's own start/stop
   int n = 0;  // completed pairs
   bool open = false;
   std::vector<hipEvent_t> ev;  // 2 per launch
@@ -17,21 +18,36 @@ ClassTiming g_t[EAGLE3_KC_COUNT];
 
 void timing_begin(int kc, hipStream_t st) {
   ClassTiming& t = g_t[kc];
-  if (!t.on || 2 * t.n + 1 >= (int)t.ev.size()) return;
+  if (!t.on || t.mode != 0 || 2 * t.n + 1 >= (int)t.ev.size()) return;
   hipEventRecord(t.ev[2 * t.n], st);
   t.open = true;
 }
 
 void timing_end(int kc, hipStream_t st) {
   ClassTiming& t = g_t[kc];
-  if (!t.on || !t.open) return;
+  if (!t.on || t.mode != 0 || !t.open) return;
   hipEventRecord(t.ev[2 * t.n + 1], st);
   t.open = false;
   ++t.n;
 }
+bool timing_kernel_events(int kc, hipEvent_t* start, hipEvent_t* stop) {
+  if (kc < 0 || kc >= EAGLE3_KC_COUNT) return false;
+  ClassTiming& t = g_t[kc];
+  if (!t.on || t.mode != 1 || 2 * t.n + 1 >= (int)t.ev.size()) return false;
+  *start = t.ev[2 * t.n];
+  *stop = t.ev[2 * t.n + 1];
+  ++t.n;
+  return true;
+}
 }  // namespace e3
 
 extern "C" {
+
+int eagle3_timing_mode(int kc, int mode) {
+  if (kc < 0 || kc >= EAGLE3_KC_COUNT || (mode != 0 && mode != 1)) return EAGLE3_EINVAL;
+  e3::g_t[kc].mode = mode;
+  return EAGLE3_OK;
+}
 
 int eagle3_timing_enable(int kc, int max_launches) {
   if (kc < 0 || kc >= EAGLE3_KC_COUNT || max_launches < 0) return EAGLE3_EINVAL;

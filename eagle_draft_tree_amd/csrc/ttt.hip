@@ -837,13 +837,14 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
 // fusion GEMM reads the caller's row-major features.
 template <class Epi>
 hipError_t bg_launch(const bf16* A, int lda, bool apack, int M, const void* W, bool packed, int N, int K, RowMap map,
-                     Epi epi, hipStream_t st) {
+                     Epi epi, hipStream_t st, int kc = -1) {
   const int grid = bg_grid(M, N);
   const bf16* Wb = (const bf16*)W;
-  if (packed && apack) big_gemm_kernel<true, true, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
-  else if (packed) big_gemm_kernel<true, false, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
-  else if (apack) big_gemm_kernel<false, true, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
-  else big_gemm_kernel<false, false, Epi><<<grid, BG_THREADS, 0, st>>>(A, lda, M, Wb, N, K, map, epi);
+  const dim3 g(grid), b(BG_THREADS);
+  if (packed && apack) launch_timed(kc, big_gemm_kernel<true, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else if (packed) launch_timed(kc, big_gemm_kernel<true, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else if (apack) launch_timed(kc, big_gemm_kernel<false, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else launch_timed(kc, big_gemm_kernel<false, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
   return hipGetLastError();
 }
 
@@ -948,7 +949,8 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_CE, st);
-      E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st));
+      E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st,
+                         EAGLE3_KC_TTT_CE));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);

@@ -383,13 +383,22 @@ int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float
 #define EAGLE3_KC_TTT_GEMM 11 /* TTT fusion, QKV, O, gate/up, down GEMMs  */
 #define EAGLE3_KC_TTT_ATTN 12 /* TTT rollout-mask attention              */
 #define EAGLE3_KC_TTT_CE 13   /* TTT LM-head GEMM with the CE epilogue    */
-#define EAGLE3_KC_COUNT 14
+#define EAGLE3_KC_LR_SCORES 14 /* efficient head: the low-rank scores kernel (the rest of
+                                  stage 1 stays in EAGLE3_KC_LMHEAD, stage 2 in _TOPK) */
+#define EAGLE3_KC_COUNT 15
 
 /* max_launches > 0 enables class `kc` with room for that many launches
  * (counters reset); 0 disables it and frees its events. */
 int eagle3_timing_enable(int kc, int max_launches);
 /* Total milliseconds and launch count recorded for class `kc`. */
 int eagle3_timing_read(int kc, double *total_ms, int *launches);
+/* mode 0 (default): an event pair around each launch scope of the class.
+ * mode 1: only the class's principal kernel is timed, each launch recording
+ * its own start and end (hipExtLaunchKernel events, the dispatch timestamps
+ * a profiler reads): the LM-head GEMM for EAGLE3_KC_LMHEAD, the scores
+ * kernel for EAGLE3_KC_LR_SCORES, the CE GEMM for EAGLE3_KC_TTT_CE; other
+ * classes then record nothing. */
+int eagle3_timing_mode(int kc, int mode);
 
 #ifdef __cplusplus
 }
