@@ -31,7 +31,7 @@ argmax on float32 logits, tree scores as float32 sums of float32 log-probs,
 sampling verification in fp64.
 
 Where the pages are silent the oracle follows one explicit reading; each is
-named where it is used (R1..R32).
+named where it is used (R1..R36).
 """
 from __future__ import annotations
 
@@ -120,34 +120,18 @@ def fuse(cfg, feats, W_fc):
 # step 2: the one-layer draft decoder ("EAGLE-3 精读" §1; readings R1-R8)
 
 
-def decoder_rows(cfg, W, S, T, P, Kc, Vc, write_idx, visible, want_logits=True):
-    """Run the drafter layer on R query rows.
+def _self_attention(cfg, W_qkv, x, P, Kc, Vc, write_idx, visible):
+    """The attention block shared by the drafter and the target layers.
 
-    S [R, d]: state of each row (g for committed rows, the parent's h_out
-    for tree rows); T [R]: token ids; P [R]: positions.
-    Kc, Vc [N, Hkv, hd]: the key/value cache the rows can see (modified in
-    place: row r writes its k, v at index write_idx[r] before attention).
-    visible [R, N] bool: the keys row r attends to.
-
-    Returns (h2 [R, d], logits [R, V] or None).
-
-    Per row (R1: combine = concatenate the two normed halves; R3: residual on
-    the state stream; R4: children receive h2; R8: frozen target embedding):
-      x  = [rms(Emb[t]) ; rms(s)]                      (2d)
-      q, k, v = split(W_qkv x); RoPE(q, k) at position p
+    x [R, K]: the rows' (already rounded) attention input.  q, k, v =
+    split(W_qkv x); RoPE on q and k at positions P; bf16 workloads round
+    q/k/v; row r stores its k, v at cache index write_idx[r] (in place), then
+    attends over the keys visible[r] marks:
       a_h = softmax(q_h . K_g(h)^T / sqrt(hd)) V_g(h),  g(h) = floor(h Hkv / Hq)  (R7)
-      h1 = s + W_o a
-      h2 = h1 + W_down (silu(W_gate u) * W_up u),  u = rms(h1)
-      logits = W_lm rms(h2)
-    """
-    d, Hq, Hkv, hd = cfg.d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    F, eps = cfg.ffn, cfg.rms_eps
-    R = len(T)
-    S = np.asarray(S, dtype=np.float64)
-    e = np.asarray(W["emb"][np.asarray(T)], dtype=np.float64)
-    x = np.concatenate([rmsnorm(e, W["norm_e"], eps), rmsnorm(S, W["norm_s"], eps)], axis=1)
-    x = _rnd(cfg, x)
-    qkv = matmul_wt(x, W["qkv"])
+    Returns a [R, Hq*hd], rounded like every GEMM input."""
+    Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    R = x.shape[0]
+    qkv = matmul_wt(x, W_qkv)
     q = qkv[:, : Hq * hd].reshape(R, Hq, hd)
     k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(R, Hkv, hd)
     v = qkv[:, (Hq + Hkv) * hd:].reshape(R, Hkv, hd)
@@ -169,12 +153,46 @@ def decoder_rows(cfg, W, S, T, P, Kc, Vc, write_idx, visible, want_logits=True):
             p = np.exp(sc - sc.max())
             p /= p.sum()
             a[r, h] = p @ Vr[:, g, :]
-    a = _rnd(cfg, a.reshape(R, Hq * hd))
-    h1 = S + matmul_wt(a, W["o"])
-    u = _rnd(cfg, rmsnorm(h1, W["norm_ffn"], eps))
-    gu = matmul_wt(u, W["gate_up"])
+    return _rnd(cfg, a.reshape(R, Hq * hd))
+
+
+def _ffn_residual(cfg, gain, W_gate_up, W_down, h1):
+    """h2 = h1 + W_down (silu(W_gate u) * W_up u),  u = rms(h1) * gain; bf16
+    workloads round u and the SwiGLU product (GEMM inputs)."""
+    F = cfg.ffn
+    u = _rnd(cfg, rmsnorm(h1, gain, cfg.rms_eps))
+    gu = matmul_wt(u, W_gate_up)
     z = _rnd(cfg, silu(gu[:, :F]) * gu[:, F:])
-    h2 = h1 + matmul_wt(z, W["down"])
+    return h1 + matmul_wt(z, W_down)
+
+
+def decoder_rows(cfg, W, S, T, P, Kc, Vc, write_idx, visible, want_logits=True):
+    """Run the drafter layer on R query rows.
+
+    S [R, d]: state of each row (g for committed rows, the parent's h_out
+    for tree rows); T [R]: token ids; P [R]: positions.
+    Kc, Vc [N, Hkv, hd]: the key/value cache the rows can see (modified in
+    place: row r writes its k, v at index write_idx[r] before attention).
+    visible [R, N] bool: the keys row r attends to.
+
+    Returns (h2 [R, d], logits [R, V] or None).
+
+    Per row (R1: combine = concatenate the two normed halves; R3: residual on
+    the state stream; R4: children receive h2; R8: frozen target embedding):
+      x  = [rms(Emb[t]) ; rms(s)]                      (2d)
+      q, k, v = split(W_qkv x); RoPE(q, k) at position p
+      a_h = softmax(q_h . K_g(h)^T / sqrt(hd)) V_g(h),  g(h) = floor(h Hkv / Hq)  (R7)
+      h1 = s + W_o a
+      h2 = h1 + W_down (silu(W_gate u) * W_up u),  u = rms(h1)
+      logits = W_lm rms(h2)
+    """
+    eps = cfg.rms_eps
+    S = np.asarray(S, dtype=np.float64)
+    e = np.asarray(W["emb"][np.asarray(T)], dtype=np.float64)
+    x = np.concatenate([rmsnorm(e, W["norm_e"], eps), rmsnorm(S, W["norm_s"], eps)], axis=1)
+    a = _self_attention(cfg, W["qkv"], _rnd(cfg, x), P, Kc, Vc, write_idx, visible)
+    h1 = S + matmul_wt(a, W["o"])
+    h2 = _ffn_residual(cfg, W["norm_ffn"], W["gate_up"], W["down"], h1)
     logits = None
     if want_logits:
         logits = matmul_wt(lm_input(cfg, W, h2), W["lm"])
@@ -633,3 +651,104 @@ def gather_paged(pool, table, n_rows, block_size):
     for p in range(n_rows):
         out[p] = pool[table[p // block_size], p % block_size]
     return out
+
+
+# --------------------------------------------------------------------------
+# the target's tree-verification forward ("EAGLE-3 精读" §2: inference keeps
+# strict target verification; §5: the target's standard verifier; §1: the
+# target exposes low/mid/high hidden states; the "EAGLE-3" quote page
+# (scholarfeed): verification is the larger part of the computation).
+# Readings R33-R36.
+
+
+def target_layer(cfg, Lw, h, P, Kc, Vc, write_idx, visible):
+    """One target decoder layer on rows h [R, d] (R33: pre-norm, the
+    drafter's layer shape with a d-wide attention input):
+      x  = rms(h) * norm_attn                       (rounded for bf16)
+      a  = attention of x as in the drafter (q/k/v, RoPE, GQA, visible keys)
+      h1 = h + W_o a
+      h2 = h1 + W_down (silu(W_gate u) * W_up u),  u = rms(h1) * norm_ffn
+    Kc, Vc [N, Hkv, hd] are this layer's keys/values (row r writes index
+    write_idx[r]).  Returns h2 [R, d] (fp64, not rounded)."""
+    h = np.asarray(h, dtype=np.float64)
+    x = _rnd(cfg, rmsnorm(h, Lw["norm_attn"], cfg.rms_eps))
+    a = _self_attention(cfg, Lw["qkv"], x, P, Kc, Vc, write_idx, visible)
+    h1 = h + matmul_wt(a, Lw["o"])
+    return _ffn_residual(cfg, Lw["norm_ffn"], Lw["gate_up"], Lw["down"], h1)
+
+
+def target_forward(cfg, Tw, tokens, P, Ks, Vs, write_idx, visible, feat_layers, begin=0, end=None, h=None):
+    """Target layers begin..end-1 on R rows (R33, R34).
+
+    Tw: dict(emb, lm, norm_out, layers=[dict(qkv, o, gate_up, down, norm_attn,
+    norm_ffn)]); Ks[l], Vs[l] [N, Hkv, hd]: layer l's keys/values (written in
+    place); visible [R, N] as in decoder_rows.  begin == 0 starts the residual
+    stream at the token embedding emb[tokens]; otherwise h [R, d] is the state
+    after `begin` layers.  feat_layers (l_low, l_mid, l_high), counted from 1:
+    feature j is the state after layer feat_layers[j], rounded to bf16 for bf16
+    workloads (the fusion input's dtype); features of layers outside the range
+    stay NaN.  With end == n_layers the logits W_lm (rms(h) * norm_out) are
+    returned too.  Returns (h [R, d], feats [R, 3, d], logits or None)."""
+    n_layers = len(Tw["layers"])
+    end = n_layers if end is None else end
+    R = len(tokens)
+    if begin == 0:
+        h = np.asarray(Tw["emb"][np.asarray(tokens)], dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    feats = np.full((R, 3, cfg.d), np.nan)
+    for l in range(begin, end):
+        h = target_layer(cfg, Tw["layers"][l], h, P, Ks[l], Vs[l], write_idx, visible)
+        for j, fl in enumerate(feat_layers):
+            if fl == l + 1:
+                feats[:, j] = _rnd(cfg, h)
+    logits = None
+    if end == n_layers:
+        logits = matmul_wt(_rnd(cfg, rmsnorm(h, Tw["norm_out"], cfg.rms_eps)), Tw["lm"])
+    return h, feats, logits
+
+
+def target_tree_visibility(v_anc, ctx_len, cap):
+    """Keys seen by the verify rows (R35): the key space is `cap` committed
+    rows followed by MAX_TREE_SLOTS tree slots; row i sees committed rows
+    0..ctx_len-1 and every slot j with bit j of v_anc[i] set (its ancestors
+    and itself; row i's own k/v go to slot i)."""
+    n = len(v_anc)
+    vis = np.zeros((n, cap + MAX_TREE_SLOTS), dtype=bool)
+    vis[:, :ctx_len] = True
+    for i in range(n):
+        bits = int(v_anc[i])
+        for j in range(MAX_TREE_SLOTS):
+            if (bits >> j) & 1:
+                vis[i, cap + j] = True
+    return vis
+
+
+def target_verify_forward(cfg, Tw, v_tok, v_pos, v_anc, Ks, Vs, ctx_len, feat_layers, begin=0, end=None, h=None):
+    """The verification forward of one request (R35): the m+1 verify rows
+    (root first) through target layers begin..end-1.  Ks[l], Vs[l] [cap + 64,
+    Hkv, hd]: committed rows then the tree slots (row i writes slot i).
+    Returns target_forward's (h, feats, logits); logits row i are the target
+    logits after node i, the input of verify_greedy / verify_sample."""
+    cap = Ks[begin].shape[0] - MAX_TREE_SLOTS
+    vis = target_tree_visibility(v_anc, ctx_len, cap)
+    widx = cap + np.arange(len(v_tok))
+    return target_forward(cfg, Tw, v_tok, v_pos, Ks, Vs, widx, vis, feat_layers, begin, end, h)
+
+
+def commit_rows(accept_len, accepted):
+    """Verify rows whose keys/values and features are committed after
+    verification (R36): the root, then the accepted nodes in path order."""
+    return [0] + [int(a) for a in accepted[:accept_len]]
+
+
+def kv_commit(Ks, Vs, ctx_len, accept_len, accepted):
+    """Move the committed rows' keys/values from the tree slots to committed
+    rows ctx_len, ctx_len+1, ... of every layer (R36), in place.  Returns the
+    new committed length ctx_len + accept_len + 1."""
+    rows = commit_rows(accept_len, accepted)
+    for K, V in zip(Ks, Vs):
+        cap = K.shape[0] - MAX_TREE_SLOTS
+        for j, i in enumerate(rows):
+            K[ctx_len + j] = K[cap + i]
+            V[ctx_len + j] = V[cap + i]
+    return ctx_len + len(rows)

@@ -65,6 +65,20 @@ class Workload:
     lowrank_rank: int = 0
     lowrank_candidates: int = 0
     lowrank_energy: float = 0.9
+    # target verification forward: the target model scoring the m+1 verify rows
+    target: Optional["TargetModel"] = None
+
+
+@dataclass(frozen=True)
+class TargetModel:
+    """A target model: n_layers pre-norm decoder layers of `shape`'s layer
+    shape with a d-wide attention input, sharing the drafter's embedding and
+    LM head.  feat_layers: the low/mid/high feature layers, counted from 1
+    (the hidden state after that many layers)."""
+    name: str
+    shape: DrafterShape
+    n_layers: int
+    feat_layers: tuple
 
 
 TINY_SHAPE = DrafterShape("tiny-d256", d=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
@@ -111,6 +125,20 @@ C2E_8B_TREE_LOWRANK = replace(C2_8B_TREE, name="llama3.1-8b-drafter-b1-tree6x10-
                               lowrank_rank=256, lowrank_candidates=64)
 C4E_70B_TREE_LOWRANK = replace(C4_70B_TREE, name="llama3.3-70b-drafter-b1-tree6x10-keep60-lowrank256-c64",
                                lowrank_rank=256, lowrank_candidates=64)
+
+
+# The targets of the two drafters: Llama-3.1-8B (32 layers) and Llama-3.3-70B
+# (80 layers) layer stacks with the drafters' layer shapes; features after
+# layers 2, L/2 and L-3.
+L8B_TARGET = TargetModel("llama3.1-8b-target", L8B_SHAPE, 32, (2, 16, 29))
+L70B_TARGET = TargetModel("llama3.3-70b-target", L70B_SHAPE, 80, (2, 40, 77))
+
+# Target verification forward over the verify rows of the 8B/70B trees and of
+# the batch-64 chains: root + kept nodes through every target layer, logits
+# and the three feature layers out.
+C2V_8B_TARGET_TREE = replace(C2_8B_TREE, name="llama3.1-8b-target32-b1-tree61rows-ctx2048", target=L8B_TARGET)
+C3V_8B_TARGET_CHAIN = replace(C3_8B_CHAIN, name="llama3.1-8b-target32-b64-chain4rows-paged16", target=L8B_TARGET)
+C4V_70B_TARGET_TREE = replace(C4_70B_TREE, name="llama3.3-70b-target80-b1-tree61rows-ctx4096", target=L70B_TARGET)
 
 
 def tiny_shape(d=16, hq=2, hkv=1, hd=8, ffn=32, vocab=8, dtype=F32, theta=10000.0, name=None):

@@ -141,6 +141,58 @@ def gen_weights(shape: DrafterShape, seed: int = 0, std: float = 0.02, only=None
     return W
 
 
+def gen_target_weights(shape: DrafterShape, n_layers: int, seed: int = 0, std: float = 0.02,
+                       layers=None, gains: str = "ones") -> dict:
+    """A target model of `n_layers` decoder layers of the drafter's layer
+    shape with a d-wide attention input: per layer qkv [(Hq+2Hkv)hd, d],
+    o [d, Hq hd], gate_up [2F, d], down [d, F], N(0, std); emb and lm are the
+    drafter's (same stream ids, so gen_weights(shape, seed) gives the same
+    matrices).  `layers` limits which layers are drawn (others are None);
+    gains "ones" or "random" (1 + 0.5 N(0,1), a distinct vector per norm)."""
+    d, F = shape.d, shape.ffn
+    shapes = dict(qkv=(shape.qkv_rows, d), o=(d, shape.n_q_heads * shape.head_dim), gate_up=(2 * F, d),
+                  down=(d, F))
+    g = _rng(seed, 49)
+    gain = (lambda: np.ones(d, dtype=np.float32)) if gains == "ones" else \
+        (lambda: (1.0 + 0.5 * g.standard_normal(d)).astype(np.float32))
+    out = dict(layers=[])
+    for l in range(n_layers):
+        Lw = dict(norm_attn=gain(), norm_ffn=gain())
+        if layers is None or l in layers:
+            for j, (name, shp) in enumerate(shapes.items()):
+                Lw[name] = draw(seed, 1000 + 8 * l + j, shp, std, shape.dtype)
+        out["layers"].append(Lw)
+    out["norm_out"] = gain()
+    shared = gen_weights(shape, seed, std, only=("emb", "lm"))
+    out["emb"], out["lm"] = shared["emb"], shared["lm"]
+    return out
+
+
+def target_weights_cuda(shape: DrafterShape, n_layers: int, seed: int = 0, std: float = 0.02):
+    """Device-resident target layer matrices for throughput runs, drawn on
+    the GPU with torch's seeded generator (the host generator would take
+    minutes at 70B scale).  Same shapes and N(0, std) as gen_target_weights,
+    bf16; not the same values.  Returns a list of per-layer dicts of torch
+    tensors, gains on the device as float32 ones."""
+    import torch
+    d, F = shape.d, shape.ffn
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7919 * (seed + 1))
+    shapes = dict(qkv=(shape.qkv_rows, d), o=(d, shape.n_q_heads * shape.head_dim), gate_up=(2 * F, d),
+                  down=(d, F))
+    layers = []
+    for _ in range(n_layers):
+        Lw = {}
+        for name, shp in shapes.items():
+            t = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+            t.normal_(0.0, std, generator=gen)
+            Lw[name] = t
+        Lw["norm_attn"] = torch.ones(d, dtype=torch.float32, device="cuda")
+        Lw["norm_ffn"] = torch.ones(d, dtype=torch.float32, device="cuda")
+        layers.append(Lw)
+    return layers
+
+
 def gen_lowrank_head(shape: DrafterShape, rank: int, energy: float = 0.9, seed: int = 0,
                      std: float = 0.02) -> dict:
     """A synthetic LM head with a low-rank part, and that part's factors.
