@@ -51,6 +51,15 @@ class LowrankHead(ctypes.Structure):
                 ("layout", ctypes.c_int32)]
 
 
+class TargetLayer(ctypes.Structure):
+    _fields_ = [(n, vp) for n in ("qkv", "o", "gate_up", "down", "norm_attn", "norm_ffn")]
+
+
+class Target(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("layers", ctypes.POINTER(TargetLayer)), ("emb", vp), ("lm", vp),
+                ("norm_out", vp), ("layout", ctypes.c_int32), ("feat_layers", ctypes.c_int32 * 3)]
+
+
 class Eagle3Error(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__(f"{fn} failed: {code} ({msg})")
@@ -91,6 +100,11 @@ def load(path: str = LIB_PATH):
         "eagle3_pack_weights": ([P, P, P, SZ, P, P], I),
         "eagle3_timing_read": ([I, P, P], I),
         "eagle3_timing_mode": ([I, I], I),
+        "eagle3_target_layer_packed_size": ([P, ctypes.POINTER(SZ)], I),
+        "eagle3_pack_target_layer": ([P, P, P, SZ, P, P], I),
+        "eagle3_target_workspace_size": ([P, I, I, I, ctypes.POINTER(SZ)], I),
+        "eagle3_target_forward": ([P, P, P, I, I, P, P, P, I, I, P, P, P, P, SZ, P], I),
+        "eagle3_kv_commit": ([P, I, P, I, I, P, P, I, P, P, P, P, P], I),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -241,9 +255,55 @@ def eagle3_topk(logits, rows, V, k, ids, lp, lse, ws, stream=None):
                                              ws.numel() * ws.element_size(), stream_ptr(stream)))
 
 
+# ---------------------------------------------------------------- the target's verification forward
+def target_layer_packed_size(dims: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check("eagle3_target_layer_packed_size", load().eagle3_target_layer_packed_size(ctypes.byref(dims),
+                                                                                     ctypes.byref(out)))
+    return out.value
+
+
+def eagle3_pack_target_layer(dims, layer: TargetLayer, dst, stream=None) -> TargetLayer:
+    """Pack one target layer's matrices into `dst` (device uint8 tensor); returns the packed layer."""
+    packed = TargetLayer()
+    _check("eagle3_pack_target_layer", load().eagle3_pack_target_layer(
+        ctypes.byref(dims), ctypes.byref(layer), ptr(dst), dst.numel() * dst.element_size(), ctypes.byref(packed),
+        stream_ptr(stream)))
+    return packed
+
+
+def target_workspace_size(dims: Dims, B: int, rows: int, max_cap: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("eagle3_target_workspace_size", load().eagle3_target_workspace_size(ctypes.byref(dims), B, rows, max_cap,
+                                                                               ctypes.byref(out)))
+    return out.value
+
+
+def kv_array(kvs):
+    """A host array of eagle3_kv structs (one per layer)."""
+    arr = (KV * len(kvs))()
+    for i, k in enumerate(kvs):
+        arr[i] = k
+    return arr
+
+
+def eagle3_target_forward(dims, target: Target, kv_arr, B, rows, tokens, pos, anc, layer_begin, layer_end, hidden,
+                          feats, logits, ws, stream=None):
+    _check("eagle3_target_forward", load().eagle3_target_forward(
+        ctypes.byref(dims), ctypes.byref(target), kv_arr, B, rows, ptr(tokens), ptr(pos), ptr(anc), layer_begin,
+        layer_end, ptr(hidden), ptr(feats), ptr(logits), ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def eagle3_kv_commit(dims, n_layers, kv_arr, B, rows, accept_len, accepted, Dmax, feats, feats_next, ctx_len_out,
+                     status, stream=None):
+    _check("eagle3_kv_commit", load().eagle3_kv_commit(
+        ctypes.byref(dims), n_layers, kv_arr, B, rows, ptr(accept_len), ptr(accepted), Dmax, ptr(feats),
+        ptr(feats_next), ptr(ctx_len_out), ptr(status), stream_ptr(stream)))
+
+
 # ---------------------------------------------------------------- kernel timing
 KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10,
-          ttt_gemm=11, ttt_attn=12, ttt_ce=13, lr_scores=14)
+          ttt_gemm=11, ttt_attn=12, ttt_ce=13, lr_scores=14, target=15, tgt_gate_up=16, tgt_lm_head=17)
 
 
 def timing_enable(kc: int, max_launches: int):

@@ -9,6 +9,7 @@
 #include "eagle3.h"
 #include "kernels.hpp"
 #include "pack.hpp"
+#include "target.hpp"
 #include "timing.hpp"
 #include "ttt.hpp"
 
@@ -369,6 +370,116 @@ int eagle3_ttt_forward(const eagle3_dims* dims, const eagle3_weights* w, const v
   if (rc == 1) return fail(EAGLE3_EUNSUPPORTED, "TTT forward: shape not supported");
   if (rc < 0) return fail(EAGLE3_EHIP, "eagle3_ttt_forward: HIP launch failed");
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+// capacity rows of one layer's cache (contiguous cap or paged max_blocks *
+// block_size), after checking its fields
+int check_layer_kv(const eagle3_dims* dims, const eagle3_kv& kv, int l, int* cap_rows) {
+  REQUIRE(kv.k && kv.v && kv.tk && kv.tv && kv.ctx_len, EAGLE3_EINVAL, "kv[%d]: k/v/tk/tv/ctx_len is NULL", l);
+  if (kv.block_table) {
+    REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "paged KV needs bf16");
+    REQUIRE(kv.block_size >= 1 && kv.max_blocks >= 1, EAGLE3_EINVAL, "kv[%d]: block_size/max_blocks", l);
+    *cap_rows = kv.max_blocks * kv.block_size;
+  } else {
+    REQUIRE(kv.cap >= 1, EAGLE3_EINVAL, "kv[%d]: cap=%d", l, kv.cap);
+    *cap_rows = kv.cap;
+  }
+  REQUIRE(*cap_rows <= 32000, EAGLE3_EUNSUPPORTED, "kv[%d]: capacity %d rows > 32000", l, *cap_rows);
+  return EAGLE3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int eagle3_target_layer_packed_size(const eagle3_dims* dims, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(bytes, EAGLE3_EINVAL, "bytes is NULL");
+  REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "packing needs bf16 weights");
+  *bytes = e3::target_layer_packed_bytes(*dims);
+  return ok();
+}
+
+int eagle3_pack_target_layer(const eagle3_dims* dims, const eagle3_target_layer* src, void* dst, size_t dst_bytes,
+                             eagle3_target_layer* packed, eagle3_stream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "packing needs bf16 weights");
+  REQUIRE(src && src->qkv && src->o && src->gate_up && src->down, EAGLE3_EINVAL, "src or a matrix is NULL");
+  REQUIRE(dst && packed, EAGLE3_EINVAL, "dst/packed is NULL");
+  const size_t need = e3::target_layer_packed_bytes(*dims);
+  REQUIRE(dst_bytes >= need, EAGLE3_EWORKSPACE, "dst %zu < %zu bytes", dst_bytes, need);
+  return hip_status(e3::pack_target_layer(*dims, *src, dst, packed, (hipStream_t)stream), "eagle3_pack_target_layer");
+}
+
+int eagle3_target_workspace_size(const eagle3_dims* dims, int B, int rows, int max_cap, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(bytes, EAGLE3_EINVAL, "bytes is NULL");
+  REQUIRE(B >= 1 && rows >= 1 && max_cap >= 1, EAGLE3_EINVAL, "B/rows/max_cap");
+  REQUIRE(rows <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "rows=%d > %d", rows, EAGLE3_MAX_TREE_SLOTS);
+  *bytes = e3::target_ws_bytes(*dims, B, rows, max_cap);
+  return ok();
+}
+
+int eagle3_target_forward(const eagle3_dims* dims, const eagle3_target* target, const eagle3_kv* kv, int B,
+                          int rows, const int32_t* tokens, const int32_t* pos, const uint64_t* anc, int layer_begin,
+                          int layer_end, float* hidden, void* feats, float* logits, void* ws, size_t ws_bytes,
+                          eagle3_stream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(target && kv, EAGLE3_EINVAL, "target/kv is NULL");
+  const eagle3_target& t = *target;
+  REQUIRE(t.n_layers >= 1 && t.layers, EAGLE3_EINVAL, "n_layers=%d / layers", t.n_layers);
+  REQUIRE(t.emb && t.lm && t.norm_out, EAGLE3_EINVAL, "emb/lm/norm_out is NULL");
+  REQUIRE(t.layout == EAGLE3_LAYOUT_ROWMAJOR || t.layout == EAGLE3_LAYOUT_PACKED, EAGLE3_EINVAL, "layout %d",
+          t.layout);
+  REQUIRE(t.layout == EAGLE3_LAYOUT_ROWMAJOR || dims->dtype == EAGLE3_BF16, EAGLE3_EINVAL, "packed fp32");
+  REQUIRE(0 <= layer_begin && layer_begin <= layer_end && layer_end <= t.n_layers, EAGLE3_EINVAL,
+          "layer range [%d, %d) of %d layers", layer_begin, layer_end, t.n_layers);
+  REQUIRE(B >= 1 && rows >= 1, EAGLE3_EINVAL, "B=%d rows=%d", B, rows);
+  REQUIRE(rows <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "rows=%d > %d", rows, EAGLE3_MAX_TREE_SLOTS);
+  REQUIRE(tokens && pos && anc && hidden, EAGLE3_EINVAL, "tokens/pos/anc/hidden is NULL");
+  if (feats)
+    for (int j = 0; j < 3; ++j)
+      REQUIRE(t.feat_layers[j] >= 1 && t.feat_layers[j] <= t.n_layers, EAGLE3_EINVAL, "feat_layers[%d]=%d", j,
+              t.feat_layers[j]);
+  int cap_max = 1;
+  for (int l = layer_begin; l < layer_end; ++l) {
+    const eagle3_target_layer& L = t.layers[l];
+    REQUIRE(L.qkv && L.o && L.gate_up && L.down && L.norm_attn && L.norm_ffn, EAGLE3_EINVAL,
+            "layer %d: a matrix or gain is NULL", l);
+    int cap_rows = 0;
+    if ((rc = check_layer_kv(dims, kv[l], l, &cap_rows))) return rc;
+    cap_max = cap_rows > cap_max ? cap_rows : cap_max;
+  }
+  REQUIRE(ws, EAGLE3_EINVAL, "workspace is NULL");
+  const size_t need = e3::target_ws_bytes(*dims, B, rows, cap_max);
+  REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  e3::TargetCall c{dims, target, kv, B, rows, tokens, pos, anc, layer_begin, layer_end, hidden, feats, logits, ws};
+  return hip_status(e3::target_forward(c, (hipStream_t)stream), "eagle3_target_forward");
+}
+
+int eagle3_kv_commit(const eagle3_dims* dims, int n_layers, const eagle3_kv* kv, int B, int rows,
+                     const int32_t* accept_len, const int32_t* accepted, int Dmax, const void* feats,
+                     void* feats_next, int32_t* ctx_len_out, int32_t* status, eagle3_stream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(kv && n_layers >= 1, EAGLE3_EINVAL, "kv is NULL or n_layers=%d", n_layers);
+  REQUIRE(B >= 1 && rows >= 1 && Dmax >= 1, EAGLE3_EINVAL, "B/rows/Dmax");
+  REQUIRE(rows <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "rows=%d > %d", rows, EAGLE3_MAX_TREE_SLOTS);
+  REQUIRE(accept_len && accepted, EAGLE3_EINVAL, "accept_len/accepted is NULL");
+  REQUIRE((feats == nullptr) == (feats_next == nullptr), EAGLE3_EINVAL, "feats and feats_next go together");
+  for (int l = 0; l < n_layers; ++l) {
+    int cap_rows = 0;
+    if ((rc = check_layer_kv(dims, kv[l], l, &cap_rows))) return rc;
+  }
+  return hip_status(e3::kv_commit(*dims, n_layers, kv, B, rows, accept_len, accepted, Dmax, feats, feats_next,
+                                  ctx_len_out, status, (hipStream_t)stream),
+                    "eagle3_kv_commit");
 }
 
 }  // extern "C"

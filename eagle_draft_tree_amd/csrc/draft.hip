@@ -25,31 +25,10 @@
 #include "rows_dma.hpp"
 #include "rows_rx.hpp"
 #include "kernels.hpp"
+#include "layer_ops.hpp"
 #include "timing.hpp"
 
 namespace e3 {
-
-constexpr int RT = 1024;      // threads of the row kernels
-constexpr int EPT_MAX = 8;    // elements per thread: d <= 8192
-
-// ---------------------------------------------------------------------------
-// row kernels: every thread owns elements i = threadIdx.x + RT*j, j < EPT_MAX,
-// and issues all of its loads before using any of them.
-
-// v[j] += sum over splits of part[s][row][i] (fixed split order)
-__device__ __forceinline__ void add_partials(float (&v)[EPT_MAX], const float* __restrict__ part, int splits,
-                                             size_t split_stride, size_t row_off, int d) {
-  for (int s = 0; s < splits; ++s) {
-    float p[EPT_MAX];
-#pragma unroll
-    for (int j = 0; j < EPT_MAX; ++j) {
-      const int i = threadIdx.x + RT * j;
-      p[j] = i < d ? part[(size_t)s * split_stride + row_off + i] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < EPT_MAX; ++j) v[j] += p[j];
-  }
-}
 
 // x = [rms(emb[t]) * ge ; rms(s) * gs], S = s.  Workgroup (row, half):
 // half 0 normalises the token embedding, half 1 the state (and keeps its
@@ -98,36 +77,6 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
   }
 }
 
-// h1 = res + sum of o partials (splits > 0), or h1 already complete;
-// u = rms(h1) * gain (dtype)
-template <typename T>
-__global__ __launch_bounds__(RT) void ffn_norm_kernel(const float* __restrict__ res, const float* __restrict__ part,
-                                                      int splits, int R, int d, const float* __restrict__ gain,
-                                                      float eps, float* __restrict__ h1, T* __restrict__ u) {
-  __shared__ float red[RT / 64];
-  const int r = blockIdx.x;
-  float v[EPT_MAX];
-#pragma unroll
-  for (int j = 0; j < EPT_MAX; ++j) {
-    const int i = threadIdx.x + RT * j;
-    v[j] = i < d ? (splits > 0 ? res[(size_t)r * d + i] : h1[(size_t)r * d + i]) : 0.f;
-  }
-  if (splits > 0) add_partials(v, part, splits, (size_t)R * d, (size_t)r * d, d);
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
-  ss = block_sum(ss, red);
-  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
-#pragma unroll
-  for (int j = 0; j < EPT_MAX; ++j) {
-    const int i = threadIdx.x + RT * j;
-    if (i < d) {
-      if (splits > 0) h1[(size_t)r * d + i] = v[j];
-      Elem<T>::st(u, (size_t)r * d + i, v[j] * inv * gain[i]);
-    }
-  }
-}
-
 // h2 = h1 + sum of down partials (splits > 0), or h2 already complete;
 // h2 rows -> h_tree (COMMIT: last row of each request -> slot 0; TREE: row
 // rr -> 1 + slot_base + rr); y = rms(h2)*gain for the rows whose top-k is
@@ -171,60 +120,6 @@ __global__ __launch_bounds__(RT) void final_norm_kernel(
   for (int j = 0; j < EPT_MAX; ++j) {
     const int i = threadIdx.x + RT * j;
     if (i < d) Elem<T>::st(y, (size_t)yr * d + i, v[j] * inv * gain[i]);
-  }
-}
-
-// QKV after split-K: one workgroup per (row, head); thread i < hd/2 owns the
-// RoPE pair (i, i + hd/2).  Sum partials in split order, rotate q and k at
-// the row's position, round, write q to ws and k/v to the KV destination.
-template <typename T>
-__global__ __launch_bounds__(64) void qkv_finish_kernel(const float* __restrict__ part, int splits, int R,
-                                                        int N, const int32_t* __restrict__ pos,
-                                                        KVDest dst, T* __restrict__ q_out, int hq,
-                                                        float theta) {
-  const int r = blockIdx.x, head = blockIdx.y;
-  const int hd = dst.hd, half = hd >> 1;
-  for (int i = threadIdx.x; i < half; i += 64) {
-    const size_t n0 = (size_t)head * hd + i;
-    float p0[16], p1[16];
-    float a = 0.f, b = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 16) {
-      const int ns = min(16, splits - s0);
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if (s < ns) {
-          p0[s] = part[(size_t)(s0 + s) * R * N + (size_t)r * N + n0];
-          p1[s] = part[(size_t)(s0 + s) * R * N + (size_t)r * N + n0 + half];
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (s < ns) {
-          a += p0[s];
-          b += p1[s];
-        }
-    }
-    if (head < hq + dst.hkv) {  // q or k: rotate
-      const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
-      const double ang = (double)pos[r] * inv;
-      const float c = (float)cos(ang), sn = (float)sin(ang);
-      const float a2 = a * c - b * sn, b2 = b * c + a * sn;
-      a = a2;
-      b = b2;
-    }
-    if (head < hq) {
-      const size_t o = (size_t)r * hq * hd + (size_t)head * hd;
-      Elem<T>::st(q_out, o + i, a);
-      Elem<T>::st(q_out, o + i + half, b);
-    } else {
-      const bool isk = head < hq + dst.hkv;
-      const int g = isk ? head - hq : head - hq - dst.hkv;
-      bool tree;
-      const size_t o = dst.off(r, g, tree);
-      T* base = (T*)(isk ? (tree ? dst.tk : dst.k) : (tree ? dst.tv : dst.v));
-      Elem<T>::st(base, o + i, a);
-      Elem<T>::st(base, o + i + half, b);
-    }
   }
 }
 
@@ -322,89 +217,6 @@ struct EpiTop1Part {
       }
       part[(size_t)r * nwg + wg] = make_float4(gm, gs, __int_as_float(gi), 0.f);
     }
-  }
-};
-
-// LM head for 17..64 rows: weights straight into registers (rx_gemm_kernel),
-// eight waves of four 16-row weight tiles, so 32 tiles (512 vocabulary
-// columns) per workgroup and one workgroup per CU.  The 8B batch-64 LM head
-// streams about 20 % faster this way than through the LDS-copy skinny kernel
-// (measured, 172 vs 215 us with partial stores); the smaller layer GEMMs
-// keep the skinny kernel, which is faster on their few workgroups.
-constexpr int LM_RX_WT = 4, LM_RX_KU = 2, LM_RX_WAVES = 8;
-constexpr int LM_RX_TPW = LM_RX_WT * LM_RX_WAVES;  // tiles per workgroup
-static inline bool lm_rx_ok(int R, int K, bool packed) { return sk_ok(R, K, packed) && K % (32 * LM_RX_KU) == 0; }
-
-// ---------------------------------------------------------------------------
-// rows-GEMM dispatch.  The epilogue sees rows 0..R-1 of one launch; row
-// chunks beyond 64 are launched separately with shifted pointers (no split).
-template <typename TW, int T, int NT, int U, int WAVES, class Epi>
-static hipError_t rows_gemm_launch(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
-                                   const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st, int kc = -1) {
-  const int nt16 = N / 16;
-  const int grid = p.tiles * p.splits;
-  const size_t lds = sizeof(TW) == 2 ? (size_t)WAVES * T * NT * 256 * sizeof(float) : 0;
-  if (packed)
-    launch_timed(kc, rows_gemm_kernel<TW, T, NT, U, WAVES, true, Epi>, dim3(grid), dim3(WAVES * 64), lds, st, X, ldx,
-                 R, W, K, nt16, p.splits, map, epi);
-  else
-    launch_timed(kc, rows_gemm_kernel<TW, T, NT, U, WAVES, false, Epi>, dim3(grid), dim3(WAVES * 64), lds, st, X, ldx,
-                 R, W, K, nt16, p.splits, map, epi);
-  return hipGetLastError();
-}
-
-// The template arguments below must match plan_rows (T, U, waves per NT).
-// kc >= 0: the launch is the principal kernel of timing class kc (kernel mode)
-template <typename TW, class Epi>
-static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int N, RowMap map,
-                            const Epi& epi, const RowsPlan& p, bool packed, hipStream_t st, int kc = -1) {
-  if constexpr (std::is_same<Epi, EpiPartial>::value) {
-    // split-K layer GEMMs of 17..64 rows: weights streamed into registers
-    if (sizeof(TW) == 2 && sk_ok(R, K, packed) && p.splits > 1 && p.splits == rx_splits(K)) {
-      constexpr int WT = 2, WAVES = 4, NB = WT * WAVES;
-      const int nt16 = N / 16;
-      const int grid = (nt16 + NB - 1) / NB * p.splits;
-      rx_gemm_kernel<WT, RX_SPLIT_KU, Epi, WAVES><<<grid, WAVES * 64, 0, st>>>(
-          (const bf16*)X, ldx, R, (const bf16*)W, K, nt16, p.splits, epi);
-      return hipGetLastError();
-    }
-  }
-  if (sizeof(TW) == 2 && sk_ok(R, K, packed)) {
-    const int nt16 = N / 16;
-    const int bn = sk_bn(nt16, p.splits);
-    const int grid = (nt16 + bn / 16 - 1) / (bn / 16) * p.splits;
-    const bf16* Xb = (const bf16*)X;
-    const bf16* Wb = (const bf16*)W;
-    if (bn == 128)
-      launch_timed(kc, skinny_gemm_kernel<128, Epi>, dim3(grid), dim3(256), 0, st, Xb, ldx, R, Wb, K, nt16, p.splits, epi);
-    else
-      launch_timed(kc, skinny_gemm_kernel<64, Epi>, dim3(grid), dim3(256), 0, st, Xb, ldx, R, Wb, K, nt16, p.splits, epi);
-    return hipGetLastError();
-  }
-  if (sizeof(TW) == 2) {
-    switch (p.nt) {
-      case 1:
-        if (p.t == 1) return rows_gemm_launch<TW, 1, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
-        return rows_gemm_launch<TW, 2, 1, 4, 8>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
-      case 2: return rows_gemm_launch<TW, 4, 2, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
-      case 3: return rows_gemm_launch<TW, 4, 3, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
-      default: return rows_gemm_launch<TW, 4, 4, 2, 4>(X, ldx, R, W, K, N, map, epi, p, packed, st, kc);
-    }
-  }
-  if (p.nt == 1) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
-  return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
-}
-
-// ---------------------------------------------------------------------------
-// Workspace layout (shared by the size query and the calls).
-struct Bump {
-  size_t off = 0;
-  unsigned char* base = nullptr;
-  void* take(size_t bytes) {
-    off = (off + 255) & ~(size_t)255;
-    void* p = base ? base + off : nullptr;
-    off += bytes;
-    return p;
   }
 };
 

@@ -7,6 +7,7 @@
 #include "common.hpp"
 #include "gemm_rows.hpp"
 #include "pack.hpp"
+#include "target.hpp"
 
 namespace e3 {
 
@@ -83,6 +84,53 @@ hipError_t pack_matrix(const void* src, int n, int k, void* dst, hipStream_t st)
   if (blocks > 65535) blocks = 65535;
   pack_kernel<<<blocks, 256, 0, st>>>((const bf16*)src, k, n, map, (uint4*)dst);
   return hipGetLastError();
+}
+
+// one target layer: qkv [(Hq+2Hkv)hd, d] (RoPE pairs share a tile), o,
+// gate_up (gate/up rows share a tile), down
+namespace {
+void target_mats_of(const eagle3_dims& dm, Mat m[4]) {
+  const int d = dm.d, F = dm.ffn, qd = dm.n_q_heads * dm.head_dim;
+  const int nqkv = (dm.n_q_heads + 2 * dm.n_kv_heads) * dm.head_dim;
+  m[0] = {nqkv, d, MAP_PAIR_HEAD};
+  m[1] = {d, qd, MAP_PLAIN};
+  m[2] = {2 * F, d, MAP_PAIR_FFN};
+  m[3] = {d, F, MAP_PLAIN};
+}
+}  // namespace
+
+size_t target_layer_packed_bytes(const eagle3_dims& dm) {
+  Mat m[4];
+  target_mats_of(dm, m);
+  size_t b = 0;
+  for (int i = 0; i < 4; ++i) b += mat_bytes(m[i]);
+  return b;
+}
+
+hipError_t pack_target_layer(const eagle3_dims& dm, const eagle3_target_layer& src, void* dst,
+                             eagle3_target_layer* packed, hipStream_t st) {
+  Mat m[4];
+  target_mats_of(dm, m);
+  const void* in[4] = {src.qkv, src.o, src.gate_up, src.down};
+  const void* outp[4];
+  unsigned char* base = (unsigned char*)dst;
+  for (int i = 0; i < 4; ++i) {
+    RowMap map{m[i].map, dm.head_dim, dm.ffn};
+    const size_t total = (size_t)(m[i].n / 16) * (m[i].k / 32) * 64;
+    int blocks = (int)((total + 255) / 256);
+    if (blocks > 65535) blocks = 65535;
+    pack_kernel<<<blocks, 256, 0, st>>>((const bf16*)in[i], m[i].k, m[i].n, map, (uint4*)base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    outp[i] = base;
+    base += mat_bytes(m[i]);
+  }
+  *packed = src;
+  packed->qkv = outp[0];
+  packed->o = outp[1];
+  packed->gate_up = outp[2];
+  packed->down = outp[3];
+  return hipSuccess;
 }
 
 }  // namespace e3

@@ -1,0 +1,485 @@
+// The target's tree-verification forward and the KV commit after it.
+//
+// "EAGLE-3 精读" §2 and §5: drafting ends in strict target verification, the
+// target's standard verifier; §1: the target exposes low, mid and high
+// hidden states for the next fusion.  The "EAGLE-3" quote page (scholarfeed)
+// puts verification at the larger part of the computation: the target's
+// weights stream once per cycle, for all verify rows at once.
+//
+// The target is a stack of pre-norm decoder layers with the drafter's layer
+// shape (d-wide attention input).  Every verify row (root, then the kept
+// nodes) is one query row in the draft step's TREE mode with slot base 0:
+// row i writes its k/v to tree slot i and sees the committed rows plus the
+// slots of its ancestors-or-self (the verify tree's bitsets).  Per layer:
+//   start / previous layer end   x = rms(h) * norm_attn (dtype)
+//   qkv      rows GEMM, RoPE, k/v -> tree slots (split-K + finish, or the
+//            paired-RoPE epilogue)
+//   attention  the draft step's split-K tree attention
+//   o        rows GEMM (+ residual h in the FFN norm, or in its epilogue)
+//   FFN norm h1 = h + o; u = rms(h1) * norm_ffn
+//   gate/up  rows GEMM with the SwiGLU epilogue
+//   down     rows GEMM (+ residual h1)
+//   layer end  h = h1 + down -> hidden; the feature copy when the layer is a
+//            feature layer; x for the next layer (its norm_attn), or the LM
+//            head input (norm_out) after the model's last layer
+// and after the last layer the LM head writes float32 logits.  The residual
+// stream is float32 in `hidden`; GEMM inputs are rounded to the dtype.
+#include <string.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "layer_ops.hpp"
+#include "target.hpp"
+
+namespace e3 {
+
+// x = rms(h) * gain for the first layer of a call; h = emb[token] (stored
+// to `hidden`) when the call starts at layer 0, else the carried state.
+template <typename T>
+__global__ __launch_bounds__(RT) void target_start_kernel(const T* __restrict__ emb, const int32_t* __restrict__ tokens,
+                                                          int from_emb, int V, int d, const float* __restrict__ gain,
+                                                          float eps, float* __restrict__ hidden, T* __restrict__ x) {
+  __shared__ float red[RT / 64];
+  const int r = blockIdx.x;
+  float v[EPT_MAX];
+  if (from_emb) {
+    const int t = min(max(tokens[r], 0), V - 1);  // ids outside the vocabulary read row 0 or V-1
+    const T* e = emb + (size_t)t * d;
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      v[j] = i < d ? Elem<T>::ld(e, i) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      v[j] = i < d ? hidden[(size_t)r * d + i] : 0.f;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = block_sum(ss, red);
+  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) {
+      if (from_emb) hidden[(size_t)r * d + i] = v[j];
+      Elem<T>::st(x, (size_t)r * d + i, v[j] * inv * gain[i]);
+    }
+  }
+}
+
+// h = h1 + sum of down partials (splits > 0), or h2buf; h -> hidden;
+// feature j (bit j of feat_mask) -> feats[r][j] (dtype); x = rms(h) * gain
+// when gain is not NULL.
+template <typename T>
+__global__ __launch_bounds__(RT) void target_layer_end_kernel(const float* __restrict__ h1,
+                                                              const float* __restrict__ part, int splits, int R,
+                                                              const float* __restrict__ h2buf, int d, int feat_mask,
+                                                              T* __restrict__ feats, const float* __restrict__ gain,
+                                                              float eps, float* __restrict__ hidden,
+                                                              T* __restrict__ x) {
+  __shared__ float red[RT / 64];
+  const int r = blockIdx.x;
+  float v[EPT_MAX];
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    v[j] = i < d ? (splits > 0 ? h1[(size_t)r * d + i] : h2buf[(size_t)r * d + i]) : 0.f;
+  }
+  if (splits > 0) add_partials(v, part, splits, (size_t)R * d, (size_t)r * d, d);
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) hidden[(size_t)r * d + i] = v[j];
+  }
+  for (int f = 0; f < 3; ++f) {
+    if (!((feat_mask >> f) & 1)) continue;
+    T* fo = feats + ((size_t)r * 3 + f) * d;
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      if (i < d) Elem<T>::st(fo, i, v[j]);
+    }
+  }
+  if (!gain) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = block_sum(ss, red);
+  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) Elem<T>::st(x, (size_t)r * d + i, v[j] * inv * gain[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// workspace
+namespace {
+// GEMMs of a target layer: qkv, o, down may split K (<= 64 rows); gate/up
+// and the LM head do not.
+size_t target_partials(const eagle3_dims& dm, int R) {
+  const bool bf = dm.dtype == EAGLE3_BF16;
+  const int d = dm.d, qd = dm.n_q_heads * dm.head_dim;
+  const int nqkv = (dm.n_q_heads + 2 * dm.n_kv_heads) * dm.head_dim;
+  const int n[3] = {nqkv, d, d}, k[3] = {d, qd, dm.ffn};
+  size_t m = 0;
+  for (int i = 0; i < 3; ++i)
+    for (int pk = 0; pk < 2; ++pk) {
+      const size_t f = rows_partial_floats(plan_rows(R, n[i], k[i], bf, true, pk), R, n[i]);
+      if (f > m) m = f;
+    }
+  return m;
+}
+
+struct TargetWS {
+  float* part;
+  void* x;
+  void* q;
+  float* part_o;
+  float* part_ml;
+  void* a;
+  float* h1;
+  void* u;
+  void* z;
+  float* h2;
+};
+
+size_t layout_target(const eagle3_dims& dm, int R, int cap_rows, void* base, TargetWS* w) {
+  const size_t es = dm.dtype == EAGLE3_BF16 ? 2 : 4;
+  const int qd = dm.n_q_heads * dm.head_dim;
+  const int nch = attn_num_chunks(cap_rows);
+  Bump bp;
+  bp.base = (unsigned char*)base;
+  TargetWS t;
+  t.part = (float*)bp.take(target_partials(dm, R) * 4);
+  t.x = bp.take((size_t)R * dm.d * es);
+  t.q = bp.take((size_t)R * qd * es);
+  t.part_o = (float*)bp.take((size_t)R * dm.n_q_heads * nch * dm.head_dim * 4);
+  t.part_ml = (float*)bp.take((size_t)R * dm.n_q_heads * nch * 2 * 4);
+  t.a = bp.take((size_t)R * qd * es);
+  t.h1 = (float*)bp.take((size_t)R * dm.d * 4);
+  t.u = bp.take((size_t)R * dm.d * es);
+  t.z = bp.take((size_t)R * dm.ffn * es);
+  t.h2 = (float*)bp.take((size_t)R * dm.d * 4);
+  if (w) *w = t;
+  return bp.off + 256;
+}
+}  // namespace
+
+size_t target_ws_bytes(const eagle3_dims& dm, int B, int rows, int cap_rows) {
+  return layout_target(dm, B * rows, cap_rows, nullptr, nullptr);
+}
+
+static int cap_rows_of(const eagle3_kv& kv) { return kv.block_table ? kv.max_blocks * kv.block_size : kv.cap; }
+
+// ---------------------------------------------------------------------------
+template <typename T>
+static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
+  const eagle3_dims& dm = *c.dims;
+  const eagle3_target& tg = *c.t;
+  const bool bf = sizeof(T) == 2;
+  const int d = dm.d, hd = dm.head_dim, hq = dm.n_q_heads, hkv = dm.n_kv_heads, F = dm.ffn, V = dm.vocab;
+  const int R = c.B * c.rows, qd = hq * hd, nqkv = (hq + 2 * hkv) * hd;
+  const bool pk = tg.layout == EAGLE3_LAYOUT_PACKED;
+  int cap_max = 0;
+  for (int l = c.begin; l < c.end; ++l) cap_max = cap_rows_of(c.kv[l]) > cap_max ? cap_rows_of(c.kv[l]) : cap_max;
+  TargetWS ws;
+  layout_target(dm, R, cap_max, c.ws, &ws);
+  const RowMap plain{MAP_PLAIN, hd, F};
+  const RowMap pair_head{MAP_PAIR_HEAD, hd, F};
+  const bool last_layer = c.end == tg.n_layers;
+  const bool want_logits = last_layer && c.logits;
+  hipError_t e;
+  TimedScope total(EAGLE3_KC_TARGET, st);
+
+  // gain of the norm that follows layer l: the next layer's attention norm,
+  // or the final norm when the LM head follows
+  auto next_gain = [&](int l) -> const float* {
+    if (l + 1 < c.end) return tg.layers[l + 1].norm_attn;
+    return want_logits ? tg.norm_out : nullptr;
+  };
+  if (c.begin < c.end) {
+    target_start_kernel<T><<<R, RT, 0, st>>>((const T*)tg.emb, c.tokens, c.begin == 0, V, d,
+                                             tg.layers[c.begin].norm_attn, dm.rms_eps, c.hidden, (T*)ws.x);
+  } else {  // no layer in the range: the LM head on the carried state
+    target_start_kernel<T><<<R, RT, 0, st>>>((const T*)tg.emb, c.tokens, c.begin == 0, V, d, tg.norm_out, dm.rms_eps,
+                                             c.hidden, (T*)ws.x);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  for (int l = c.begin; l < c.end; ++l) {
+    const eagle3_target_layer& Lw = tg.layers[l];
+    const eagle3_kv& kv = c.kv[l];
+    const int cap_rows = cap_rows_of(kv);
+    // ---- QKV + RoPE + k/v -> tree slots
+    KVDest dst{kv.k, kv.v, kv.tk, kv.tv, kv.ctx_len, kv.block_table, kv.cap, kv.max_blocks, kv.block_size,
+               c.rows, EAGLE3_TREE, 0, hkv, hd, 0};
+    {
+      const RowsPlan p = plan_rows(R, nqkv, d, bf, true, pk);
+      if (p.splits > 1) {
+        EpiPartial epi{ws.part, nqkv, pair_head};
+        if ((e = rows_gemm<T>((const T*)ws.x, d, R, (const T*)Lw.qkv, d, nqkv, pair_head, epi, p, pk, st)) !=
+            hipSuccess)
+          return e;
+        qkv_finish_kernel<T><<<dim3(R, hq + 2 * hkv), 64, 0, st>>>(ws.part, p.splits, R, nqkv, c.pos, dst, (T*)ws.q,
+                                                                   hq, dm.rope_theta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      } else {
+        for (int r0 = 0; r0 < R; r0 += 64) {
+          const int Rc = R - r0 < 64 ? R - r0 : 64;
+          EpiQKV<T> epi;
+          epi.q_out = (T*)ws.q + (size_t)r0 * qd;
+          epi.pos = c.pos + r0;
+          epi.dst = dst;
+          epi.dst.row0 = r0;
+          epi.hq = hq;
+          epi.theta = dm.rope_theta;
+          const RowsPlan pc = plan_rows(Rc, nqkv, d, bf, false);
+          if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * d, d, Rc, (const T*)Lw.qkv, d, nqkv, pair_head, epi, pc,
+                                pk, st)) != hipSuccess)
+            return e;
+        }
+      }
+    }
+    // ---- attention over the committed rows and the ancestor slots
+    AttnLaunch al;
+    al.q = ws.q;
+    al.kc = kv.k;
+    al.vc = kv.v;
+    al.tk = kv.tk;
+    al.tv = kv.tv;
+    al.ctx_len = kv.ctx_len;
+    al.block_table = kv.block_table;
+    al.anc = c.anc;
+    al.cap = kv.cap;
+    al.max_blocks = kv.max_blocks;
+    al.block_size = kv.block_size;
+    al.cap_rows = cap_rows;
+    al.B = c.B;
+    al.rows = c.rows;
+    al.hq = hq;
+    al.hkv = hkv;
+    al.hd = hd;
+    al.mode = EAGLE3_TREE;
+    al.bf16 = bf;
+    al.part_o = ws.part_o;
+    al.part_ml = ws.part_ml;
+    al.out = ws.a;
+    if ((e = launch_attention(al, st)) != hipSuccess) return e;
+    // ---- O projection (+ residual)
+    int o_splits = 0;
+    {
+      const RowsPlan p = plan_rows(R, d, qd, bf, true, pk);
+      if (p.splits > 1) {
+        EpiPartial epi{ws.part, d, plain};
+        if ((e = rows_gemm<T>((const T*)ws.a, qd, R, (const T*)Lw.o, qd, d, plain, epi, p, pk, st)) != hipSuccess)
+          return e;
+        o_splits = p.splits;
+      } else {
+        for (int r0 = 0; r0 < R; r0 += 64) {
+          const int Rc = R - r0 < 64 ? R - r0 : 64;
+          EpiResidual epi{ws.h1 + (size_t)r0 * d, c.hidden + (size_t)r0 * d, d};
+          const RowsPlan pc = plan_rows(Rc, d, qd, bf, false);
+          if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)Lw.o, qd, d, plain, epi, pc, pk,
+                                st)) != hipSuccess)
+            return e;
+        }
+      }
+    }
+    ffn_norm_kernel<T><<<R, RT, 0, st>>>(c.hidden, ws.part, o_splits, R, d, Lw.norm_ffn, dm.rms_eps, ws.h1, (T*)ws.u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // ---- gate/up + SwiGLU
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      RowMap pf{MAP_PAIR_FFN, hd, F};
+      EpiSwiGLU<T> epi{(T*)ws.z + (size_t)r0 * F, F};
+      const RowsPlan pc = plan_rows(Rc, 2 * F, d, bf, false);
+      if ((e = rows_gemm<T>((const T*)ws.u + (size_t)r0 * d, d, Rc, (const T*)Lw.gate_up, d, 2 * F, pf, epi, pc, pk,
+                            st, EAGLE3_KC_TGT_GATEUP)) != hipSuccess)
+        return e;
+    }
+    // ---- down (+ residual)
+    int down_splits = 0;
+    {
+      const RowsPlan p = plan_rows(R, d, F, bf, true, pk);
+      if (p.splits > 1) {
+        EpiPartial epi{ws.part, d, plain};
+        if ((e = rows_gemm<T>((const T*)ws.z, F, R, (const T*)Lw.down, F, d, plain, epi, p, pk, st)) != hipSuccess)
+          return e;
+        down_splits = p.splits;
+      } else {
+        for (int r0 = 0; r0 < R; r0 += 64) {
+          const int Rc = R - r0 < 64 ? R - r0 : 64;
+          EpiResidual epi{ws.h2 + (size_t)r0 * d, ws.h1 + (size_t)r0 * d, d};
+          const RowsPlan pc = plan_rows(Rc, d, F, bf, false);
+          if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)Lw.down, F, d, plain, epi, pc, pk,
+                                st)) != hipSuccess)
+            return e;
+        }
+      }
+    }
+    // ---- layer end: state, features, next norm
+    int feat_mask = 0;
+    if (c.feats)
+      for (int f = 0; f < 3; ++f)
+        if (tg.feat_layers[f] == l + 1) feat_mask |= 1 << f;
+    target_layer_end_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, down_splits, R, ws.h2, d, feat_mask, (T*)c.feats,
+                                                 next_gain(l), dm.rms_eps, c.hidden, (T*)ws.x);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
+  // ---- LM head: float32 logits of every row
+  if (want_logits) {
+    const int nt16 = V / 16;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      EpiStore<float> epi{c.logits + (size_t)r0 * V, V, plain};
+      const T* X = (const T*)ws.x + (size_t)r0 * d;
+      if (bf && lm_rx_ok(Rc, d, pk)) {
+        launch_timed(EAGLE3_KC_TGT_LMHEAD, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiStore<float>, LM_RX_WAVES>,
+                     dim3((nt16 + LM_RX_TPW - 1) / LM_RX_TPW), dim3(LM_RX_WAVES * 64), 0, st, (const bf16*)X, d, Rc,
+                     (const bf16*)tg.lm, d, nt16, 1, epi);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      } else {
+        const RowsPlan pc = plan_rows(Rc, V, d, bf, false);
+        if ((e = rows_gemm<T>(X, d, Rc, (const T*)tg.lm, d, V, plain, epi, pc, pk, st, EAGLE3_KC_TGT_LMHEAD)) !=
+            hipSuccess)
+          return e;
+      }
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t target_forward(const TargetCall& c, hipStream_t st) {
+  return c.dims->dtype == EAGLE3_BF16 ? target_impl<bf16>(c, st) : target_impl<float>(c, st);
+}
+
+// ---------------------------------------------------------------------------
+// KV commit: per request, verify rows 0 (the root) and accepted[0..n-2]
+// move from the tree slots to committed rows ctx_len .. ctx_len+n-1 of every
+// layer, n = accept_len + 1.  A request whose rows do not fit the smallest
+// layer capacity is left alone (status EAGLE3_ECAPACITY, ctx_len unchanged).
+namespace {
+constexpr int COMMIT_LAYERS = 16;  // layers per launch (kernel-argument size)
+struct CommitLayer {
+  void* k;
+  void* v;
+  const void* tk;
+  const void* tv;
+  const int32_t* block_table;
+  int cap, max_blocks, block_size;
+};
+struct CommitArgs {
+  CommitLayer L[COMMIT_LAYERS];
+};
+
+// verify row of committed row j of request b, or -1 (invalid / beyond n)
+__device__ __forceinline__ int commit_src(int b, int j, int n, const int32_t* accepted, int Dmax, int rows) {
+  if (j >= n) return -1;
+  const int s = j == 0 ? 0 : accepted[(size_t)b * Dmax + j - 1];
+  return (s >= 0 && s < rows) ? s : -1;
+}
+
+__device__ __forceinline__ int commit_count(int b, const int32_t* accept_len, int Dmax, int rows) {
+  int n = accept_len[b] + 1;
+  n = n < 1 ? 1 : n;
+  n = n > Dmax + 1 ? Dmax + 1 : n;
+  return n > rows ? rows : n;
+}
+
+// grid (B * rows, layers of this launch, 2 = k/v); a workgroup copies one
+// row (hkv * hd elements) of one layer's k or v with 16-byte moves
+__global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a, const int32_t* __restrict__ ctx_len,
+                                                        const int32_t* __restrict__ accept_len,
+                                                        const int32_t* __restrict__ accepted, int Dmax, int rows,
+                                                        int row_u4, int min_cap) {
+  const int b = blockIdx.x / rows, j = blockIdx.x - b * rows;
+  const int n = commit_count(b, accept_len, Dmax, rows);
+  const int s = commit_src(b, j, n, accepted, Dmax, rows);
+  const int c0 = ctx_len[b];
+  if (s < 0 || c0 < 0 || c0 + n > min_cap) return;
+  const CommitLayer& L = a.L[blockIdx.y];
+  const int crow = c0 + j;
+  size_t drow;
+  if (L.block_table) {
+    const int blk = L.block_table[(size_t)b * L.max_blocks + crow / L.block_size];
+    if (blk < 0) return;
+    drow = (size_t)blk * L.block_size + crow % L.block_size;
+  } else {
+    drow = (size_t)b * L.cap + crow;
+  }
+  const uint4* src = (const uint4*)(blockIdx.z ? L.tv : L.tk) + ((size_t)b * EAGLE3_MAX_TREE_SLOTS + s) * row_u4;
+  uint4* dst = (uint4*)(blockIdx.z ? L.v : L.k) + drow * row_u4;
+  for (int i = threadIdx.x; i < row_u4; i += 256) dst[i] = src[i];
+}
+
+// features of the committed rows -> feats_next[b][j] (16-byte moves)
+__global__ __launch_bounds__(256) void feats_gather_kernel(const uint4* __restrict__ feats, uint4* __restrict__ next,
+                                                           const int32_t* __restrict__ accept_len,
+                                                           const int32_t* __restrict__ accepted, int Dmax, int rows,
+                                                           int row_u4) {
+  const int b = blockIdx.x / (Dmax + 1), j = blockIdx.x - b * (Dmax + 1);
+  const int n = commit_count(b, accept_len, Dmax, rows);
+  const int s = commit_src(b, j, n, accepted, Dmax, rows);
+  if (s < 0) return;
+  const uint4* src = feats + ((size_t)b * rows + s) * row_u4;
+  uint4* dst = next + ((size_t)b * (Dmax + 1) + j) * row_u4;
+  for (int i = threadIdx.x; i < row_u4; i += 256) dst[i] = src[i];
+}
+
+// after every copy: status and the new committed lengths (ctx_out may alias ctx_len)
+__global__ __launch_bounds__(64) void commit_status_kernel(const int32_t* __restrict__ ctx_len,
+                                                           const int32_t* __restrict__ accept_len, int B, int Dmax,
+                                                           int rows, int min_cap, int32_t* ctx_out,
+                                                           int32_t* status) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= B) return;
+  const int n = commit_count(b, accept_len, Dmax, rows);
+  const int c0 = ctx_len[b];
+  const bool fits = c0 >= 0 && c0 + n <= min_cap;
+  if (status) status[b] = fits ? 0 : EAGLE3_ECAPACITY;
+  if (ctx_out) ctx_out[b] = fits ? c0 + n : c0;
+}
+}  // namespace
+
+hipError_t kv_commit(const eagle3_dims& dm, int n_layers, const eagle3_kv* kv, int B, int rows,
+                     const int32_t* accept_len, const int32_t* accepted, int Dmax, const void* feats,
+                     void* feats_next, int32_t* ctx_len_out, int32_t* status, hipStream_t st) {
+  const size_t es = dm.dtype == EAGLE3_BF16 ? 2 : 4;
+  const int row_u4 = (int)((size_t)dm.n_kv_heads * dm.head_dim * es / 16);
+  int min_cap = 0x7fffffff;
+  for (int l = 0; l < n_layers; ++l) min_cap = cap_rows_of(kv[l]) < min_cap ? cap_rows_of(kv[l]) : min_cap;
+  const int32_t* ctx_len = kv[0].ctx_len;
+  for (int l0 = 0; l0 < n_layers; l0 += COMMIT_LAYERS) {
+    const int nl = n_layers - l0 < COMMIT_LAYERS ? n_layers - l0 : COMMIT_LAYERS;
+    CommitArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int i = 0; i < nl; ++i) {
+      const eagle3_kv& k = kv[l0 + i];
+      a.L[i] = CommitLayer{k.k, k.v, k.tk, k.tv, k.block_table, k.cap, k.max_blocks, k.block_size};
+    }
+    kv_commit_kernel<<<dim3(B * rows, nl, 2), 256, 0, st>>>(a, ctx_len, accept_len, accepted, Dmax, rows, row_u4,
+                                                            min_cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (feats && feats_next) {
+    const int frow_u4 = (int)((size_t)3 * dm.d * es / 16);
+    feats_gather_kernel<<<B * (Dmax + 1), 256, 0, st>>>((const uint4*)feats, (uint4*)feats_next, accept_len, accepted,
+                                                        Dmax, rows, frow_u4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  commit_status_kernel<<<(B + 63) / 64, 64, 0, st>>>(ctx_len, accept_len, B, Dmax, rows, min_cap, ctx_len_out,
+                                                     status);
+  return hipGetLastError();
+}
+
+}  // namespace e3

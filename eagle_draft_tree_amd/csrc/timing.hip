@@ -19,14 +19,14 @@ ClassTiming g_t[EAGLE3_KC_COUNT];
 void timing_begin(int kc, hipStream_t st) {
   ClassTiming& t = g_t[kc];
   if (!t.on || t.mode != 0 || 2 * t.n + 1 >= (int)t.ev.size()) return;
-  hipEventRecord(t.ev[2 * t.n], st);
+  (void)hipEventRecord(t.ev[2 * t.n], st);
   t.open = true;
 }
 
 void timing_end(int kc, hipStream_t st) {
   ClassTiming& t = g_t[kc];
   if (!t.on || t.mode != 0 || !t.open) return;
-  hipEventRecord(t.ev[2 * t.n + 1], st);
+  (void)hipEventRecord(t.ev[2 * t.n + 1], st);
   t.open = false;
   ++t.n;
 }
@@ -52,7 +52,7 @@ int eagle3_timing_mode(int kc, int mode) {
 int eagle3_timing_enable(int kc, int max_launches) {
   if (kc < 0 || kc >= EAGLE3_KC_COUNT || max_launches < 0) return EAGLE3_EINVAL;
   e3::ClassTiming& t = e3::g_t[kc];
-  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t.ev.clear();
   t.n = 0;
   t.open = false;

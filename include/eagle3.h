@@ -354,6 +354,106 @@ int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const v
                        int32_t *pred, float *ce, float *loss, void *ws, size_t ws_bytes,
                        eagle3_stream_t stream);
 
+/* ---- the target's verification forward ---------------------------------
+ * ("EAGLE-3 精读" §2 and §5: drafting ends in strict verification by the
+ * target's standard verifier, which needs the target's logits at every
+ * kept node; §1: the target exposes low/mid/high hidden states, the next
+ * fusion's input; the "EAGLE-3" quote page (scholarfeed): verification is
+ * the larger part of the computation.)
+ *
+ * The target: n_layers pre-norm decoder layers with the drafter's layer
+ * shape (eagle3_dims: d, heads, head_dim, ffn, vocab, dtype, rms_eps,
+ * rope_theta) and a d-wide attention input, then a final RMSNorm and the LM
+ * head.  Per layer, on the float32 residual stream h:
+ *   x = rms(h)*norm_attn; q,k,v = qkv.x; RoPE(q,k,pos); a = attention
+ *   h1 = h + o.a;  h = h1 + down.(silu(gate.u) * up.u), u = rms(h1)*norm_ffn
+ * The stream starts at the token embedding; logits = lm.(rms(h)*norm_out).
+ * bf16 targets round x, q/k/v, a, u, silu(gate)*up, rms(h)*norm_out and the
+ * features to bf16 like the drafter.
+ *
+ * One target layer (device matrices, dtype of dims, [out, in] row-major or
+ * packed by eagle3_pack_target_layer as eagle3_target.layout says):
+ *  qkv     [(Hq+2Hkv)hd, d]    o [d, Hq*hd]
+ *  gate_up [2*ffn, d]          down [d, ffn]
+ *  norm_attn, norm_ffn [d] float32 */
+typedef struct eagle3_target_layer {
+  const void *qkv, *o, *gate_up, *down;
+  const float *norm_attn, *norm_ffn;
+} eagle3_target_layer;
+
+/* The target model.  layers: HOST array [n_layers].  emb, lm [vocab, d]
+ * (lm packed by eagle3_pack_matrix when layout is PACKED); norm_out [d]
+ * float32.  feat_layers: the low, mid and high feature layers, each in
+ * 1..n_layers, counted from 1 (feature j = the state h after layer
+ * feat_layers[j]); they may repeat. */
+typedef struct eagle3_target {
+  int32_t n_layers;
+  const eagle3_target_layer *layers;
+  const void *emb, *lm;
+  const float *norm_out;
+  int32_t layout;
+  int32_t feat_layers[3];
+} eagle3_target;
+
+/* Bytes of one layer's packed copy (bf16 only). */
+int eagle3_target_layer_packed_size(const eagle3_dims *dims, size_t *bytes);
+/* Copy one layer's four matrices (row-major bf16) into dst in MFMA fragment
+ * order (qkv: RoPE pairs share a tile; gate_up: gate/up rows share a tile;
+ * as eagle3_pack_weights) and fill `packed` (host) with pointers into dst
+ * plus src's gains.  Enqueued on `stream`; src must stay valid until then. */
+int eagle3_pack_target_layer(const eagle3_dims *dims, const eagle3_target_layer *src, void *dst,
+                             size_t dst_bytes, eagle3_target_layer *packed, eagle3_stream_t stream);
+
+/* Workspace bytes of eagle3_target_forward for B requests of `rows` verify
+ * rows whose layers hold at most max_cap committed rows (contiguous cap, or
+ * max_blocks*block_size when paged).  No initialisation is needed. */
+int eagle3_target_workspace_size(const eagle3_dims *dims, int B, int rows, int max_cap, size_t *bytes);
+
+/* The verification forward: target layers layer_begin..layer_end-1 on
+ * B x rows verify rows.  Row i of request b is verify node i (0 = the root,
+ * the last committed token, whose k/v are not yet cached): token
+ * tokens[b][i], position pos[b][i]; in every layer it writes its k/v to tree
+ * slot i of kv[l] (tk/tv [B][64][Hkv][hd]) and attends over committed rows
+ * 0..ctx_len[b]-1 of kv[l] plus every tree slot j with bit j of anc[b][i]
+ * set (the verify tree's ancestor-or-self bitsets, v_anc of
+ * eagle3_tree_expand FINAL; a chain is the tree whose row i has bits 0..i).
+ * Bits at or above `rows` must be clear.
+ *  kv          HOST array [n_layers] of per-layer caches (eagle3_kv; paged
+ *              needs bf16).  Only tree slots 0..rows-1 are written.
+ *  hidden      [B][rows][d] float32: the residual stream.  layer_begin == 0
+ *              starts it at emb[tokens] (ids clamped to [0, vocab)); else
+ *              it must hold the state after layer_begin layers (a previous
+ *              call's output).  On return: the state after layer_end layers.
+ *  feats       [B][rows][3][d] dtype, or NULL: feature j of a row is written
+ *              when feat_layers[j] lies in (layer_begin, layer_end].
+ *  logits      [B][rows][vocab] float32, or NULL: written when layer_end ==
+ *              n_layers; row i = target logits after node i (the
+ *              target_logits of eagle3_verify).
+ * 0 <= layer_begin <= layer_end <= n_layers; rows <= 64; ws of
+ * eagle3_target_workspace_size bytes.  EAGLE3_EUNSUPPORTED: a shape the
+ * drafter step rejects (head_dim, d > 8192, ...). */
+int eagle3_target_forward(const eagle3_dims *dims, const eagle3_target *target, const eagle3_kv *kv, int B,
+                          int rows, const int32_t *tokens, const int32_t *pos, const uint64_t *anc,
+                          int layer_begin, int layer_end, float *hidden, void *feats, float *logits, void *ws,
+                          size_t ws_bytes, eagle3_stream_t stream);
+
+/* After verification: commit the root and the accepted nodes.  For request
+ * b, n = accept_len[b] + 1 (clamped to 1..min(Dmax+1, rows)) verify rows --
+ * row 0, then accepted[b][0..n-2] (eagle3_verify's outputs) -- move from
+ * tree slots to committed rows ctx_len[b] .. ctx_len[b]+n-1 of every layer
+ * (kv: HOST array [n_layers]; ctx_len is read from kv[0], and every layer
+ * must share those lengths).  feats / feats_next (optional, dtype):
+ * feats_next[b][j] ([B][Dmax+1][3][d]) = feats[b][row j] ([B][rows][3][d])
+ * for j < n, the fusion input of the next cycle.  ctx_len_out [B]
+ * (optional, may alias kv[0].ctx_len) = ctx_len + n; status [B] (optional)
+ * = 0.  A request whose rows do not fit the smallest layer capacity gets
+ * status EAGLE3_ECAPACITY and is left unchanged (ctx_len_out = ctx_len).
+ * Paged caches need the blocks of the new rows in the block table (a
+ * negative entry skips the row). */
+int eagle3_kv_commit(const eagle3_dims *dims, int n_layers, const eagle3_kv *kv, int B, int rows,
+                     const int32_t *accept_len, const int32_t *accepted, int Dmax, const void *feats,
+                     void *feats_next, int32_t *ctx_len_out, int32_t *status, eagle3_stream_t stream);
+
 /* The top-k/log-prob reduction of eagle3_draft_step on caller logits:
  * logits [rows][V] float32 -> ids [rows][k], lp [rows][k], lse [rows] (lse
  * may be NULL).  Same order and tie rule.  k in 1..16, V <= 262144 (also
@@ -385,7 +485,10 @@ int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float
 #define EAGLE3_KC_TTT_CE 13   /* TTT LM-head GEMM with the CE epilogue    */
 #define EAGLE3_KC_LR_SCORES 14 /* efficient head: the low-rank scores kernel (the rest of
                                   stage 1 stays in EAGLE3_KC_LMHEAD, stage 2 in _TOPK) */
-#define EAGLE3_KC_COUNT 15
+#define EAGLE3_KC_TARGET 15     /* eagle3_target_forward, whole call          */
+#define EAGLE3_KC_TGT_GATEUP 16 /* its gate/up GEMMs (principal kernel)       */
+#define EAGLE3_KC_TGT_LMHEAD 17 /* its LM-head GEMM (principal kernel)        */
+#define EAGLE3_KC_COUNT 18
 
 /* max_launches > 0 enables class `kc` with room for that many launches
  * (counters reset); 0 disables it and frees its events. */
@@ -396,8 +499,9 @@ int eagle3_timing_read(int kc, double *total_ms, int *launches);
  * mode 1: only the class's principal kernel is timed, each launch recording
  * its own start and end (hipExtLaunchKernel events, the dispatch timestamps
  * a profiler reads): the LM-head GEMM for EAGLE3_KC_LMHEAD, the scores
- * kernel for EAGLE3_KC_LR_SCORES, the CE GEMM for EAGLE3_KC_TTT_CE; other
- * classes then record nothing. */
+ * kernel for EAGLE3_KC_LR_SCORES, the CE GEMM for EAGLE3_KC_TTT_CE, the
+ * target's gate/up and LM-head GEMMs for EAGLE3_KC_TGT_GATEUP and
+ * EAGLE3_KC_TGT_LMHEAD; other classes then record nothing. */
 int eagle3_timing_mode(int kc, int mode);
 
 #ifdef __cplusplus

@@ -212,3 +212,63 @@ def test_efficient_head_argument_checks(blib):
     assert call(H(rank=64), dims=f32, k=2) == blib.EUNSUPPORTED  # fp32 drafter
     assert lib.eagle3_pack_matrix(_P, 100, 64, _P, 1 << 20, None) == blib.EINVAL
     assert lib.eagle3_pack_matrix(_P, 128, 64, _P, 100, None) == blib.EWORKSPACE
+
+
+def _fake_target(blib, n_layers=2, feat=(1, 2, 2), layout=0):
+    arr = (blib.TargetLayer * n_layers)()
+    for i in range(n_layers):
+        arr[i] = blib.TargetLayer(*([0x10000] * 6))
+    t = blib.Target(n_layers, ctypes.cast(arr, ctypes.POINTER(blib.TargetLayer)), 0x10000, 0x10000, 0x10000, layout,
+                    (ctypes.c_int32 * 3)(*feat))
+    return t, arr
+
+
+def test_target_forward_argument_checks(blib):
+    """eagle3_target_forward / eagle3_kv_commit / the target packing calls
+    reject bad arguments on the host with the documented codes."""
+    from workloads.configs import L8B_SHAPE, TINY_SHAPE
+    lib = blib.load()
+    d = blib.dims_of(L8B_SHAPE)
+    t, _arr = _fake_target(blib)
+    kv = blib.kv_array([_fake_kv(blib), _fake_kv(blib)])
+    ws = 1 << 40
+
+    def fwd(target=t, kvs=kv, B=1, rows=61, begin=0, end=2, feats=_P, ws_bytes=ws, dims=d):
+        return lib.eagle3_target_forward(ctypes.byref(dims), ctypes.byref(target) if target is not None else None,
+                                         kvs, B, rows, _P, _P, _P, begin, end, _P, feats, _P, _P, ws_bytes, None)
+    assert fwd(target=None) == blib.EINVAL
+    assert fwd(rows=65) == blib.ECAPACITY                     # more than 64 verify rows
+    assert fwd(begin=1, end=0) == blib.EINVAL                 # empty/negative range
+    assert fwd(end=3) == blib.EINVAL                          # past the last layer
+    t_bad, _a2 = _fake_target(blib, feat=(0, 1, 2))
+    assert fwd(target=t_bad) == blib.EINVAL                   # feature layer 0 (layers count from 1)
+    t_pk, _a3 = _fake_target(blib, layout=blib.LAYOUT_PACKED)
+    assert fwd(target=t_pk, dims=blib.dims_of(TINY_SHAPE), rows=8) == blib.EINVAL   # packed fp32
+    big = blib.kv_array([blib.KV(0x10000, 0x10000, 40000, None, 0, 0, 0x10000, 0x10000, 0x10000)] * 2)
+    assert fwd(kvs=big) == blib.EUNSUPPORTED                   # capacity above the attention's limit
+    no_slots = blib.kv_array([blib.KV(0x10000, 0x10000, 4096, None, 0, 0, 0x10000, None, None)] * 2)
+    assert fwd(kvs=no_slots) == blib.EINVAL                    # tree slots are required
+    need = blib.target_workspace_size(d, 1, 61, 4096)
+    assert fwd(ws_bytes=need - 1) == blib.EWORKSPACE
+    assert blib.target_workspace_size(d, 64, 4, 2048) > 0
+    with pytest.raises(blib.Eagle3Error) as e:
+        blib.target_workspace_size(d, 1, 65, 2048)
+    assert e.value.code == blib.ECAPACITY
+    # KV commit
+    assert lib.eagle3_kv_commit(ctypes.byref(d), 2, kv, 1, 61, _P, _P, 6, _P, None, None, None,
+                                None) == blib.EINVAL           # feats without feats_next
+    assert lib.eagle3_kv_commit(ctypes.byref(d), 2, kv, 1, 65, _P, _P, 6, None, None, None, None,
+                                None) == blib.ECAPACITY
+    assert lib.eagle3_kv_commit(ctypes.byref(d), 2, kv, 1, 61, None, _P, 6, None, None, None, None,
+                                None) == blib.EINVAL
+    assert lib.eagle3_kv_commit(ctypes.byref(d), 2, big, 1, 61, _P, _P, 6, None, None, None, None,
+                                None) == blib.EUNSUPPORTED
+    # packing
+    sz = ctypes.c_size_t(0)
+    assert lib.eagle3_target_layer_packed_size(ctypes.byref(d), ctypes.byref(sz)) == 0
+    assert sz.value == 2 * (6144 * 4096 + 4096 * 4096 + 2 * 14336 * 4096 + 4096 * 14336)
+    layer = blib.TargetLayer(*([0x10000] * 6))
+    assert lib.eagle3_pack_target_layer(ctypes.byref(d), ctypes.byref(layer), _P, sz.value - 1,
+                                        ctypes.byref(blib.TargetLayer()), None) == blib.EWORKSPACE
+    f32 = blib.dims_of(TINY_SHAPE)
+    assert lib.eagle3_target_layer_packed_size(ctypes.byref(f32), ctypes.byref(sz)) == blib.EUNSUPPORTED

@@ -388,3 +388,87 @@ def random_verify_tree(seed: int, m: int, V: int, depth: int, root_tok: int = 0)
         if len(kids):
             v_tok[kids] = g.choice(V, size=len(kids), replace=False)
     return v_tok, v_parent
+
+
+def ancestor_bits(v_parent) -> np.ndarray:
+    """uint64 ancestor-or-self bitsets of a tree whose parents precede
+    their children (bit i of node i set, plus every bit of its parent)."""
+    n = len(v_parent)
+    out = np.zeros(n, dtype=np.uint64)
+    for i in range(n):
+        p = int(v_parent[i])
+        out[i] = np.uint64(1 << i) | (out[p] if p >= 0 else np.uint64(0))
+    return out
+
+
+@dataclass
+class TargetInputs:
+    """Inputs of one verification forward of B requests (m+1 rows each)."""
+    kv_k: list                    # per layer: [B, cap, Hkv, hd] or paged pool [nb, bs, Hkv, hd] (None: not drawn)
+    kv_v: list
+    cap: int                      # contiguous capacity, or max_blocks * block_size
+    block_table: np.ndarray       # [B, max_blocks] int32 (paged) or None
+    n_blocks: int
+    ctx_len: np.ndarray           # [B] committed rows
+    v_tok: np.ndarray             # [B, m+1] int32, row 0 = root
+    v_parent: np.ndarray          # [B, m+1] int32
+    v_pos: np.ndarray             # [B, m+1] int32 = ctx_len + depth
+    v_anc: np.ndarray             # [B, m+1] uint64
+
+
+def gen_target_inputs(w: Workload, n_layers: int, layers=None, seed: int = 1) -> TargetInputs:
+    """Synthetic verification-forward inputs: committed prefixes of w.prefix
+    rows (or U[w.prefix_range] per request) with N(0,1) keys/values in every
+    layer (`layers` limits which layers are drawn), room for the m+1 rows a
+    commit may append, and one random verify tree per request (depth <=
+    w.depth, m = w.keep kept nodes; a chain when w.topk == 1)."""
+    s = w.shape
+    Bn, m = w.batch, w.keep
+    rows = m + 1
+    hkv, hd = s.n_kv_heads, s.head_dim
+    if w.prefix_range is not None:
+        lo, hi = w.prefix_range
+        ctx = _rng(seed, 51).integers(lo, hi + 1, size=Bn).astype(np.int32)
+    else:
+        ctx = np.full(Bn, w.prefix, dtype=np.int32)
+    v_tok = np.empty((Bn, rows), np.int32)
+    v_par = np.empty((Bn, rows), np.int32)
+    roots = _rng(seed, 52).integers(0, s.vocab, size=Bn)
+    g = _rng(seed, 53)
+    for b in range(Bn):
+        if w.topk == 1:
+            v_par[b] = np.arange(-1, m, dtype=np.int32)
+            v_tok[b] = g.integers(0, s.vocab, size=rows)
+            v_tok[b, 0] = roots[b]
+        else:
+            v_tok[b], v_par[b] = random_verify_tree(seed * 1000 + b, m, s.vocab, w.depth, root_tok=int(roots[b]))
+    depth = np.zeros((Bn, rows), np.int32)
+    v_anc = np.zeros((Bn, rows), np.uint64)
+    for b in range(Bn):
+        for i in range(1, rows):
+            depth[b, i] = depth[b, v_par[b, i]] + 1
+        v_anc[b] = ancestor_bits(v_par[b])
+    v_pos = (ctx[:, None] + depth).astype(np.int32)
+    want = range(n_layers) if layers is None else layers
+    kv_k, kv_v = [None] * n_layers, [None] * n_layers
+    table, nb = None, 0
+    if w.paged:
+        bs = w.block_size
+        need = [(int(c) + rows + bs - 1) // bs for c in ctx]
+        nb = int(sum(need))
+        perm = _rng(seed, 54).permutation(nb).astype(np.int32)
+        maxb = max(need)
+        table = np.full((Bn, maxb), -1, dtype=np.int32)
+        off = 0
+        for b in range(Bn):
+            table[b, :need[b]] = perm[off:off + need[b]]
+            off += need[b]
+        cap = maxb * bs
+        shp = (nb, bs, hkv, hd)
+    else:
+        cap = int(ctx.max()) + rows
+        shp = (Bn, cap, hkv, hd)
+    for l in want:
+        kv_k[l] = draw(seed, 2000 + 2 * l, shp, 1.0, s.dtype)
+        kv_v[l] = draw(seed, 2001 + 2 * l, shp, 1.0, s.dtype)
+    return TargetInputs(kv_k, kv_v, cap, table, nb, ctx, v_tok, v_par, v_pos, v_anc)
