@@ -38,10 +38,11 @@ KC_TTT = dict(rowops=1, ttt_gemm=11, ttt_attn=12, ttt_ce=13)
 # sources that build each workload's dominant kernel (a traffic record is
 # used only while their hash is unchanged)
 KERNEL_SOURCES = {
-    "rows_gemm": ("gemm_rows.hpp", "draft.hip", "common.hpp"),
-    "rows_rx": ("rows_rx.hpp", "draft.hip", "common.hpp"),
+    "rows_gemm": ("gemm_rows.hpp", "layer_ops.hpp", "draft.hip", "common.hpp"),
+    "rows_rx": ("rows_rx.hpp", "rows_dma.hpp", "layer_ops.hpp", "draft.hip", "common.hpp"),
     "lr_scores": ("lowrank.hip", "draft.hip", "common.hpp"),
     "ttt_ce": ("bigemm.hpp", "ttt.hip", "common.hpp"),
+    "target_gate_up": ("gemm_rows.hpp", "rows_dma.hpp", "layer_ops.hpp", "target.hip", "common.hpp"),
 }
 
 
@@ -534,13 +535,175 @@ def ttt_bench(w, dr, steps, warmup):
     }, ti
 
 
+def target_bench(w, Wt, steps, warmup):
+    """Time the target's verification step of workload w: the forward of
+    all target layers over the B x (m+1) verify rows (root + kept nodes)
+    with float32 logits and the three features, then verification of those
+    logits (w.verify_modes[0]) and the KV commit of the accepted rows
+    (lengths left unchanged, so every step sees the same inputs).  Target
+    layers and prefix keys/values are drawn on the GPU (torch's seeded
+    generator); embedding and LM head are the drafter's (Wt).  Returns the
+    measurement dict and what the CPU baseline needs."""
+    import numpy as np
+    import torch
+
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.target import TargetCache, TargetWeights, VerifyForward
+    from workloads import gen
+
+    s, tm = w.shape, w.target
+    L, Bn, m = tm.n_layers, w.batch, w.keep
+    rows = m + 1
+    ti = gen.gen_target_inputs(w, L, layers=[], seed=1)
+    t0 = time.time()
+    layers = gen.target_weights_cuda(s, L, seed=0)
+    tw = TargetWeights(s, layers, Wt["emb"], Wt["lm"], np.ones(s.d, np.float32), tm.feat_layers, pack=True)
+    del layers
+    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    if w.paged:
+        k, v = gen.target_kv_cuda(s, L, (ti.n_blocks, w.block_size), seed=0)
+        cache = TargetCache(s, L, Bn, 0, torch.bfloat16, paged=True, block_size=w.block_size,
+                            block_table=torch.as_tensor(ti.block_table), k=k, v=v)
+    else:
+        k, v = gen.target_kv_cuda(s, L, (Bn, ti.cap), seed=0)
+        cache = TargetCache(s, L, Bn, ti.cap, torch.bfloat16, k=k, v=v)
+    cache.ctx_len.copy_(torch.as_tensor(ti.ctx_len))
+    vf = VerifyForward(tw, cache, rows)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    tokens, pos = i32(ti.v_tok), i32(ti.v_pos)
+    anc = torch.as_tensor(ti.v_anc.view(np.int64)).cuda()
+    v_par = i32(ti.v_parent)
+    mode = Bd.SAMPLE if w.verify_modes[0] == "sample" else Bd.GREEDY
+    ut, ur = gen.uniforms(1, Bn, rows)
+    ut_d, ur_d = torch.as_tensor(ut).cuda(), torch.as_tensor(ur).cuda()
+    Dmax = m
+    acc_len = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    accepted = torch.zeros(Bn, Dmax, dtype=torch.int32, device="cuda")
+    bonus = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    status = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    vws = torch.zeros(Bd.verify_workspace_size(Bn, m, s.vocab), dtype=torch.uint8, device="cuda")
+    feats_next = torch.empty(Bn, Dmax + 1, 3, s.d, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        vf.run(tokens, pos, anc)
+        Bd.eagle3_verify(Bn, m, s.vocab, Dmax, tokens, v_par, vf.logits, mode, w.temperature,
+                         ut_d if mode == Bd.SAMPLE else None, ur_d if mode == Bd.SAMPLE else None, acc_len, accepted,
+                         bonus, status, vws)
+        vf.commit(acc_len, accepted, Dmax, feats_next=feats_next)
+
+    for _ in range(max(warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.max()) == 0
+    kc_t = {"target": 15, "tgt_gate_up": 16, "tgt_lm_head": 17}
+    for c in kc_t.values():
+        Bd.timing_enable(c, L * (steps + 1))
+    Bd.timing_mode(kc_t["tgt_gate_up"], 1)
+    Bd.timing_mode(kc_t["tgt_lm_head"], 1)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    per = {name: Bd.timing_read(c) for name, c in kc_t.items()}
+    for c in kc_t.values():
+        Bd.timing_enable(c, 0)
+    acc_mean = float(acc_len.float().mean())
+    # algorithmic bytes (bf16 weights and activations, fp32 logits)
+    es = 2
+    d, F, V, hq, hkv, hd = s.d, s.ffn, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim
+    R = Bn * rows
+    w_layer = ((hq + 2 * hkv) * hd * d + d * hq * hd + 2 * F * d + d * F) * es
+    kv_read = int(np.sum(ti.ctx_len)) * hkv * hd * 2 * es
+    fwd_bytes = L * (w_layer + kv_read + R * hkv * hd * 2 * es) + V * d * es + R * V * 4 + R * 3 * d * es
+    gu_bytes = 2 * F * d * es + R * d * es + R * F * es
+    lm_bytes = V * d * es + R * d * es + R * V * 4
+    gu_ms, gu_cnt = per["tgt_gate_up"]
+    lm_ms, lm_cnt = per["tgt_lm_head"]
+    fw_ms, fw_cnt = per["target"]
+    chunks = -(-R // 64)
+    gu_us = gu_ms / gu_cnt * 1e3 if gu_cnt else None
+    gu_gbs = gu_bytes / chunks / (gu_us * 1e-6) / 1e9 if gu_us else None
+    lm_gbs = lm_bytes / (lm_ms / lm_cnt * 1e-3) / 1e9 if lm_cnt else None
+    fw_ms_each = fw_ms / fw_cnt if fw_cnt else None
+    res = {
+        "workload": w.name,
+        "target": {"n_layers": L, "feat_layers": list(tm.feat_layers), "weight_bytes": L * w_layer + 2 * V * d * es},
+        "steps": steps,
+        "ms_per_step": round(ms, 4),
+        "verification_steps_per_s": round(1000.0 / ms, 2),
+        "verify_rows_per_s": round(R * 1000.0 / ms, 1),
+        "forward_ms": round(fw_ms_each, 4) if fw_ms_each else None,
+        "accepted_mean": round(acc_mean, 3),
+        "verify": w.verify_modes[0],
+        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1) if gu_gbs else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4) if gu_gbs else None,
+                     "traffic": load_traffic(w.name, "target_gate_up"),
+                     "kernel": "target gate/up GEMM with the SwiGLU epilogue (one launch per layer"
+                               + (f" and {chunks} row chunks)" if chunks > 1 else ")"),
+                     "scope": "dominant kernel only; the whole forward is forward_roofline",
+                     "bytes_per_launch": round(gu_bytes / chunks), "avg_launch_us": round(gu_us, 2) if gu_us else None},
+        "forward_roofline": {"bytes": fwd_bytes,
+                             "achieved_GBs": round(fwd_bytes / (fw_ms_each * 1e-3) / 1e9, 1) if fw_ms_each else None,
+                             "frac": round(fwd_bytes / (fw_ms_each * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                             if fw_ms_each else None},
+        "lm_head": {"GBs": round(lm_gbs, 1) if lm_gbs else None,
+                    "frac": round(lm_gbs / HBM_PEAK_GBS, 4) if lm_gbs else None,
+                    "avg_launch_us": round(lm_ms / lm_cnt * 1e3, 2) if lm_cnt else None},
+        "note": "random target weights: the kept nodes are random tokens, so acceptance is ~0 and the verify and "
+                "commit do minimal work; the forward's cost does not depend on the weights' values",
+        "setup_s": round(setup_s, 1),
+    }
+    del vf, cache, tw
+    torch.cuda.empty_cache()
+    return res, ti
+
+
+def cpu_baseline_target(w, Wt, ti):
+    """The oracle's verification forward on a bounded sample: request 0's
+    m+1 verify rows through one target layer (host-drawn weights of the
+    same shapes) plus the final norm and LM head, timed on the host cores;
+    the forward time scales the layer time by the layer count
+    (extrapolated)."""
+    import numpy as np
+
+    from oracle import eagle3_oracle as O
+    from workloads import gen
+    s, tm = w.shape, w.target
+    threads, desc = _host_info()
+    T1 = gen.gen_target_weights(s, 2, seed=0, layers=[0])
+    T1["layers"] = [{k: (v.f32() if hasattr(v, "f32") else v) for k, v in T1["layers"][0].items()}] * 2
+    T1["emb"], T1["lm"] = Wt["emb"].f32(), Wt["lm"].f32()
+    rows = w.keep + 1
+    cap = int(ti.ctx_len[0]) + rows
+    rng = np.random.default_rng(0)
+    Ks = [rng.standard_normal((cap + O.MAX_TREE_SLOTS, s.n_kv_heads, s.head_dim))] * 2
+    Vs = [rng.standard_normal((cap + O.MAX_TREE_SLOTS, s.n_kv_heads, s.head_dim))] * 2
+    t0 = time.time()
+    h, _, _ = O.target_verify_forward(s, T1, ti.v_tok[0], ti.v_pos[0], ti.v_anc[0], Ks, Vs, int(ti.ctx_len[0]),
+                                      (1, 1, 1), 0, 1)
+    t_layer = time.time() - t0
+    t0 = time.time()
+    O.matmul_wt(O._rnd(s, O.rmsnorm(h, T1["norm_out"], s.rms_eps)), T1["lm"])
+    t_lm = time.time() - t0
+    per_fwd = (t_layer * tm.n_layers + t_lm) * w.batch
+    return {"value": 1.0 / per_fwd, "unit": "verification forwards/s", "cores": threads, "kind": "oracle",
+            "extrapolated_ms_per_forward": round(per_fwd * 1e3, 1),
+            "sample": f"request 0's {rows} verify rows through 1 target layer ({t_layer:.1f} s) and the final norm + "
+                      f"LM head ({t_lm:.1f} s), fp64 NumPy; one forward = {tm.n_layers} layers + LM head"
+                      + (f", x {w.batch} requests" if w.batch > 1 else "") + f" (extrapolated); {desc}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e", "c2v", "c3v", "c4v"], default=None,
                     help="run one workload only (profiling); the main line is then that workload's")
     ap.add_argument("--main-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
@@ -566,8 +729,18 @@ def main():
     from eagle_draft_tree_amd import binding as Bd
     from eagle_draft_tree_amd.cycle import Drafter
     from workloads import gen
-    from workloads.configs import (C2_8B_TREE, C2E_8B_TREE_LOWRANK, C3_8B_CHAIN, C4_70B_TREE, C4E_70B_TREE_LOWRANK,
+    from workloads.configs import (C2_8B_TREE, C2E_8B_TREE_LOWRANK, C2V_8B_TARGET_TREE, C3_8B_CHAIN,
+                                   C3V_8B_TARGET_CHAIN, C4_70B_TREE, C4E_70B_TREE_LOWRANK, C4V_70B_TARGET_TREE,
                                    C5_8B_TTT)
+
+    if args.only in ("c2v", "c3v", "c4v"):
+        w = {"c2v": C2V_8B_TARGET_TREE, "c3v": C3V_8B_TARGET_CHAIN, "c4v": C4V_70B_TARGET_TREE}[args.only]
+        Wt = gen.gen_weights(w.shape, seed=0, only=("emb", "lm"))
+        r, ti = target_bench(w, Wt, max(1, min(args.steps, 20)), min(args.warmup, 3))
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline_target(w, Wt, ti)
+        print(json.dumps(r), flush=True)
+        return
 
     Bd.load()
     t0 = time.time()
@@ -668,11 +841,21 @@ def main():
         cpu_jobs.append((w4e.name, w4e, Wt4e, ci4e, vin4e, None, head4e))
         del dr4e, lm_rows
         torch.cuda.empty_cache()
+        # the target's verification step (forward over the verify rows + verify + KV commit)
+        for wv, Wt in ((C2V_8B_TARGET_TREE, Wt8), (C3V_8B_TARGET_CHAIN, Wt8), (C4V_70B_TARGET_TREE, Wt70)):
+            rv, tiv = target_bench(wv, Wt, max(args.steps // 5, 2), min(args.warmup, 3))
+            wl[wv.name] = rv
+            cpu_jobs.append((wv.name, wv, Wt, tiv, None, None, None))
         out["workloads"] = wl
     if not args.no_cpu_baseline:
         for name, wk, Wt, inp, vi, reqs, hd in cpu_jobs:
             print(f"cpu baseline: {wk.name}", file=sys.stderr, flush=True)
-            cb = cpu_baseline_ttt(wk, Wt, inp) if wk.ttt_seq else cpu_baseline(wk, Wt, inp, vi, reqs, hd)
+            if wk.target is not None:
+                cb = cpu_baseline_target(wk, Wt, inp)
+            elif wk.ttt_seq:
+                cb = cpu_baseline_ttt(wk, Wt, inp)
+            else:
+                cb = cpu_baseline(wk, Wt, inp, vi, reqs, hd)
             if name == "main":
                 out["cpu_baseline"] = cb
             else:

@@ -31,8 +31,10 @@ class TargetWeights:
     generator Tensors, arrays or device tensors; emb, lm, norm_out likewise
     (emb and lm may be the drafter's own device tensors).  pack=True (bf16)
     converts every layer into MFMA fragment order, one layer at a time, and
-    drops the row-major copies; the LM head is packed too unless lm_packed
-    (an already packed lm) is given."""
+    drops the row-major copies (entries of `layers` are set to None as they
+    are packed, so that device-resident inputs are freed one layer at a
+    time); the LM head is packed too unless lm_packed (an already packed
+    lm) is given."""
 
     def __init__(self, shape, layers, emb, lm, norm_out, feat_layers, device="cuda", pack=False, lm_packed=None):
         self.shape = shape
@@ -41,8 +43,8 @@ class TargetWeights:
         pack = pack and shape.dtype == "bf16"
         n = len(layers)
         self.layer_arr = (B.TargetLayer * n)()
-        for l, Lw in enumerate(layers):
-            t = {k: _dev(v, device) for k, v in Lw.items()}
+        for l in range(n):
+            t = {k: _dev(v, device) for k, v in layers[l].items()}
             lay = B.TargetLayer(*(t[k].data_ptr() for k in _MATS), t["norm_attn"].data_ptr(),
                                 t["norm_ffn"].data_ptr())
             if pack:
@@ -52,6 +54,7 @@ class TargetWeights:
                 for k in _MATS:
                     del t[k]
                 t["packed"] = buf
+                layers[l] = None
             self.layer_arr[l] = lay
             self.keep.append(t)
         self.emb = _dev(emb, device)

@@ -57,7 +57,7 @@ class Case:
         self.ti = gen.gen_target_inputs(w, n_layers, seed=seed)
         ti = self.ti
         self.rows = w.keep + 1
-        self.tw = TargetWeights(s, self.Tw["layers"], self.Tw["emb"], self.Tw["lm"], self.Tw["norm_out"],
+        self.tw = TargetWeights(s, list(self.Tw["layers"]), self.Tw["emb"], self.Tw["lm"], self.Tw["norm_out"],
                                 feat_layers, pack=pack)
         k = torch.stack([t.torch("cuda") for t in ti.kv_k])
         v = torch.stack([t.torch("cuda") for t in ti.kv_v])

@@ -193,6 +193,18 @@ def target_weights_cuda(shape: DrafterShape, n_layers: int, seed: int = 0, std: 
     return layers
 
 
+def target_kv_cuda(shape: DrafterShape, n_layers: int, rows_per_layer_shape, seed: int = 0):
+    """Device-resident N(0,1) bf16 keys and values [n_layers, *rows_per_layer_shape,
+    Hkv, hd] for throughput runs (torch's seeded generator)."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(104729 * (seed + 1))
+    shp = (n_layers,) + tuple(rows_per_layer_shape) + (shape.n_kv_heads, shape.head_dim)
+    k = torch.empty(shp, dtype=torch.bfloat16, device="cuda").normal_(0.0, 1.0, generator=gen)
+    v = torch.empty(shp, dtype=torch.bfloat16, device="cuda").normal_(0.0, 1.0, generator=gen)
+    return k, v
+
+
 def gen_lowrank_head(shape: DrafterShape, rank: int, energy: float = 0.9, seed: int = 0,
                      std: float = 0.02) -> dict:
     """A synthetic LM head with a low-rank part, and that part's factors.
