@@ -31,7 +31,7 @@ argmax on float32 logits, tree scores as float32 sums of float32 log-probs,
 sampling verification in fp64.
 
 Where the pages are silent the oracle follows one explicit reading; each is
-named where it is used (R1..R36).
+named where it is used (R1..R41).
 """
 from __future__ import annotations
 
@@ -104,16 +104,22 @@ def silu(x):
 # step 1: multi-layer feature fusion  ("EAGLE-3 精读" §1)
 
 
-def fuse(cfg, feats, W_fc):
+def fuse(cfg, feats, W_fc, norm_fc=None):
     """g = [f_low ; f_mid ; f_high] . W_fc^T.
 
     feats [n, 3, d] -> g [n, d].  No bias and no norm after the projection
     (reading R2: the FC norm first appears in EAGLE-3.1 per the EAGLE-4 blog).
-    bf16 workloads round g to bfloat16.
+    With norm_fc (EAGLE-3.1's FC Norm, which EAGLE-4 keeps -- EAGLE-4 blog,
+    the paragraph on what EAGLE-4 keeps of EAGLE-3.1; reading R37) the
+    projection is RMS-normalised: g = rms(FC x) * norm_fc.  bf16 workloads
+    round g to bfloat16 (once, after the norm).
     """
     n = feats.shape[0]
     cat = np.asarray(feats, dtype=np.float64).reshape(n, -1)
-    return _rnd(cfg, matmul_wt(cat, W_fc))
+    y = matmul_wt(cat, W_fc)
+    if norm_fc is not None:
+        y = rmsnorm(y, norm_fc, cfg.rms_eps)
+    return _rnd(cfg, y)
 
 
 # --------------------------------------------------------------------------
@@ -185,14 +191,27 @@ def decoder_rows(cfg, W, S, T, P, Kc, Vc, write_idx, visible, want_logits=True):
       h1 = s + W_o a
       h2 = h1 + W_down (silu(W_gate u) * W_up u),  u = rms(h1)
       logits = W_lm rms(h2)
+    With W["norm_post_attn"] and W["norm_post_ffn"] (the post-norm variant,
+    R38) instead:
+      h1 = rms(s + W_o a) * norm_post_attn
+      h2 = rms(h1 + W_down (silu(W_gate h1) * W_up h1)) * norm_post_ffn
     """
     eps = cfg.rms_eps
     S = np.asarray(S, dtype=np.float64)
     e = np.asarray(W["emb"][np.asarray(T)], dtype=np.float64)
     x = np.concatenate([rmsnorm(e, W["norm_e"], eps), rmsnorm(S, W["norm_s"], eps)], axis=1)
     a = _self_attention(cfg, W["qkv"], _rnd(cfg, x), P, Kc, Vc, write_idx, visible)
-    h1 = S + matmul_wt(a, W["o"])
-    h2 = _ffn_residual(cfg, W["norm_ffn"], W["gate_up"], W["down"], h1)
+    if W.get("norm_post_attn") is not None:
+        # EAGLE-3.1's Post-norm (EAGLE-4 blog; reading R38): every residual
+        # sum is RMS-normalised, and the FFN reads the normalised h1 directly
+        h1 = rmsnorm(S + matmul_wt(a, W["o"]), W["norm_post_attn"], eps)
+        F = cfg.ffn
+        gu = matmul_wt(_rnd(cfg, h1), W["gate_up"])
+        z = _rnd(cfg, silu(gu[:, :F]) * gu[:, F:])
+        h2 = rmsnorm(h1 + matmul_wt(z, W["down"]), W["norm_post_ffn"], eps)
+    else:
+        h1 = S + matmul_wt(a, W["o"])
+        h2 = _ffn_residual(cfg, W["norm_ffn"], W["gate_up"], W["down"], h1)
     logits = None
     if want_logits:
         logits = matmul_wt(lm_input(cfg, W, h2), W["lm"])
@@ -340,6 +359,12 @@ class DynamicTree:
         if j < self.D:
             self._assign_slots()
 
+    def sorted_scores(self):
+        """Pool scores in rerank order (score desc, depth asc, flat asc): the
+        confidences the harness's verify-count rule reads (R40)."""
+        order = sorted(range(len(self.tok)), key=lambda n: (-float(self.score[n]), self.depth[n], self.flat[n]))
+        return [self.score[n] for n in order]
+
     def final(self, m):
         """Keep the top-m of the pool by (score desc, depth asc, flat asc) and
         lay them out in canonical verify order: root 0, then by (depth asc,
@@ -475,7 +500,7 @@ def draft_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, k, D, m, record=None, he
     """
     n = len(tokens)
     Hkv, hd = cfg.n_kv_heads, cfg.head_dim
-    g = fuse(cfg, feats, W["fc"])
+    g = fuse(cfg, feats, W["fc"], W.get("norm_fc"))
     cap = Kc.shape[0]
     N = cap + MAX_TREE_SLOTS
     K = np.zeros((N, Hkv, hd))
@@ -752,3 +777,154 @@ def kv_commit(Ks, Vs, ctx_len, accept_len, accepted):
             K[ctx_len + j] = K[cap + i]
             V[ctx_len + j] = V[cap + i]
     return ctx_len + len(rows)
+
+
+# --------------------------------------------------------------------------
+# EAGLE-4 Harness: cost-aware control of the tree (EAGLE-4 blog, the
+# EAGLE-Harness paragraph: a warm-up measures draft and verify times over
+# batch sizes, context lengths and token counts into a lookup table; every
+# round asks, in three places, whether the expected extra accepted tokens
+# divided by the extra time exceed a threshold -- one more draft layer, how
+# many tokens to verify, and the branch cap per node, 8 at light load and 4
+# at heavy load; the section on converging trends: the confidence is the
+# product of draft probabilities, with a threshold that rises with depth).
+# Readings R39-R41.
+
+DRAFT, VERIFY = 0, 1
+
+
+def harness_cost(table, kind, B, ctx, n):
+    """Time (ms) of one drafter round (kind DRAFT, n rows per request) or
+    one verification step (kind VERIFY, n verify rows per request) from the
+    warm-up table (R39): table = dict(batch=[...], ctx=[...], tok=[...]
+    ascending, draft=[nb][nc][nt], verify=[nb][nc][nt]).  B and ctx take the
+    smallest measured value at or above them (the largest if none is); n is
+    interpolated linearly between the measured token counts and clamped to
+    their range."""
+    def snap(vals, x):
+        for i, v in enumerate(vals):
+            if v >= x:
+                return i
+        return len(vals) - 1
+    ib, ic = snap(table["batch"], B), snap(table["ctx"], ctx)
+    row = np.asarray(table["draft" if kind == DRAFT else "verify"], dtype=np.float64)[ib, ic]
+    tok = np.asarray(table["tok"], dtype=np.float64)
+    return float(np.interp(float(n), tok, row))
+
+
+def harness_continue(table, B, ctx, k, depth, frontier_logconf, tau0, alpha):
+    """One more draft layer?  (R40) Each frontier node j of request b
+    reaches its children with probability c = exp(log-confidence), so one
+    more layer can add at most sum_j c_bj expected accepted tokens to request
+    b; the layer costs one drafter round of k rows per request.  The rounds
+    are shared by the batch, so the batch drafts on while
+
+        sum_b sum_j c_bj / T_draft(B, ctx, k)  >  tau0 * (1 + alpha * depth)
+
+    (the threshold rising with depth).  Returns (decision, per-request
+    gains)."""
+    c = np.exp(np.asarray(frontier_logconf, dtype=np.float64))
+    gains = c.sum(axis=1)
+    t = harness_cost(table, DRAFT, B, ctx, k)
+    tau = tau0 * (1.0 + alpha * depth)
+    return bool(gains.sum() / t > tau) if t > 0 else True, gains
+
+
+def harness_verify_count(table, B, ctx, logconf_sorted, tau):
+    """How many drafted tokens to verify (R40): rank i (0-based) of every
+    request's rerank order (confidences descending) adds sum_b c_b,i
+    expected accepted tokens and raises the verify rows per request from
+    i+1 to i+2 (the root is row 0).  Ranks are taken in order while
+
+        sum_b c_b,i / (T_verify(B, ctx, i+2) - T_verify(B, ctx, i+1))  >  tau
+
+    (a rank whose extra time is not positive is always taken).  Returns the
+    number of ranks kept, 0..m_max."""
+    c = np.exp(np.asarray(logconf_sorted, dtype=np.float64))
+    m_max = c.shape[1]
+    n = 0
+    while n < m_max:
+        gain = c[:, n].sum()
+        dt = harness_cost(table, VERIFY, B, ctx, n + 2) - harness_cost(table, VERIFY, B, ctx, n + 1)
+        if dt > 0 and not gain / dt > tau:
+            break
+        n += 1
+    return n
+
+
+def harness_branch_cap(table, B, ctx, root_lp, tau):
+    """Branches per node, 8 or 4 (R41): the root's children of ranks 5..8
+    add sum_b sum_{i=4..7} p_b,i expected accepted tokens (p = the root's
+    draft probabilities, exp of its top-8 log-probs) for the extra time of
+    drafting 8 instead of 4 rows per request in a round; 8 while
+
+        gain / (T_draft(B, ctx, 8) - T_draft(B, ctx, 4))  >  tau
+
+    (or when the extra time is not positive), else 4.  Light load (small B)
+    makes the extra time small and keeps 8; heavy load makes it large and
+    drops to 4."""
+    p = np.exp(np.asarray(root_lp, dtype=np.float64))
+    gain = p[:, 4:8].sum()
+    dt = harness_cost(table, DRAFT, B, ctx, 8) - harness_cost(table, DRAFT, B, ctx, 4)
+    return 8 if dt <= 0 or gain / dt > tau else 4
+
+
+def harness_cycle(cfg, W, feats, tokens, Kc, Vc, ctx_len, table, m_max, D_max, tau_depth0, tau_alpha, tau_verify,
+                  tau_branch, B=1):
+    """A draft cycle of one request under the harness: the root's top-8
+    decides the branch cap k (R41); after every round the depth rule decides
+    whether to draft another layer (R40, at most D_max rounds); the verify
+    count rule picks m <= m_max from the pool's confidences.  B is the batch
+    size the cost table is read at (the request's share of a batch).
+    Returns (verify tree, dict(k=, rounds=, m=))."""
+    n = len(tokens)
+    Hkv, hd = cfg.n_kv_heads, cfg.head_dim
+    g = fuse(cfg, feats, W["fc"], W.get("norm_fc"))
+    cap = Kc.shape[0]
+    N = cap + MAX_TREE_SLOTS
+    K = np.zeros((N, Hkv, hd))
+    V = np.zeros((N, Hkv, hd))
+    K[:cap], V[:cap] = Kc, Vc
+    L0 = int(ctx_len)
+    vis = np.zeros((n, N), dtype=bool)
+    for r in range(n):
+        vis[r, : L0 + r + 1] = True
+    P = np.arange(L0, L0 + n)
+    h2, logits = decoder_rows(cfg, W, g, tokens, P, K, V, P, vis)
+    ids8, lp8, _ = topk_logprobs(logits[-1], 8)
+    k = harness_branch_cap(table, B, L0 + n, lp8[None], tau_branch)
+    tree = DynamicTree(k, D_max, tokens[-1], L0 + n - 1)
+    tree.init(ids8[:k], lp8[:k])
+    h_tree = {0: h2[-1]}
+    Lc = L0 + n
+    rounds = 1
+    for j in range(2, D_max + 1):
+        front = np.array([[tree.score[i] for i in tree.frontier]], dtype=np.float32)
+        go, _ = harness_continue(table, B, Lc, k, j - 1, front, tau_depth0, tau_alpha)
+        if not go:
+            break
+        rows = tree.next_rows()
+        slot_base = (j - 2) * k
+        S = np.stack([h_tree[pidx] for (_, pidx, _, _) in rows])
+        T = np.array([t for (t, _, _, _) in rows])
+        Pr = np.array([p for (_, _, p, _) in rows])
+        vis = np.zeros((len(rows), N), dtype=bool)
+        vis[:, :Lc] = True
+        for r, (_, _, _, anc) in enumerate(rows):
+            for s_ in range(MAX_TREE_SLOTS):
+                if (anc >> s_) & 1:
+                    vis[r, cap + s_] = True
+        widx = cap + slot_base + np.arange(len(rows))
+        h2, logits = decoder_rows(cfg, W, S, T, Pr, K, V, widx, vis)
+        ids = np.zeros((len(rows), k), np.int32)
+        lps = np.zeros((len(rows), k), np.float32)
+        for r in range(len(rows)):
+            h_tree[1 + slot_base + r] = h2[r]
+            ids[r], lps[r], _ = topk_logprobs(logits[r], k)
+        tree.step(ids, lps)
+        rounds += 1
+    sc = tree.sorted_scores()
+    m_cap = min(m_max, len(sc))
+    m = harness_verify_count(table, B, Lc, np.asarray(sc[:m_cap], np.float32)[None], tau_verify)
+    m = max(m, 1)
+    return tree.final(m), dict(k=k, rounds=rounds, m=m)
