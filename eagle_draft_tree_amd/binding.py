@@ -37,7 +37,8 @@ LAYOUT_ROWMAJOR, LAYOUT_PACKED = 0, 1
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, vp) for n in ("fc", "emb", "qkv", "o", "gate_up", "down", "lm",
-                                  "norm_e", "norm_s", "norm_ffn", "norm_out")] + [("layout", ctypes.c_int32)]
+                                  "norm_e", "norm_s", "norm_ffn", "norm_out")] + [("layout", ctypes.c_int32)] + \
+               [(n, vp) for n in ("norm_fc", "norm_post_attn", "norm_post_ffn")]
 
 
 class KV(ctypes.Structure):
@@ -58,6 +59,14 @@ class TargetLayer(ctypes.Structure):
 class Target(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("layers", ctypes.POINTER(TargetLayer)), ("emb", vp), ("lm", vp),
                 ("norm_out", vp), ("layout", ctypes.c_int32), ("feat_layers", ctypes.c_int32 * 3)]
+
+
+class CostTable(ctypes.Structure):
+    _fields_ = [("n_batch", ctypes.c_int32), ("n_ctx", ctypes.c_int32), ("n_tok", ctypes.c_int32),
+                ("batch", vp), ("ctx", vp), ("tok", vp), ("draft_ms", vp), ("verify_ms", vp)]
+
+
+COST_DRAFT, COST_VERIFY = 0, 1
 
 
 class Eagle3Error(RuntimeError):
@@ -105,6 +114,11 @@ def load(path: str = LIB_PATH):
         "eagle3_target_workspace_size": ([P, I, I, I, ctypes.POINTER(SZ)], I),
         "eagle3_target_forward": ([P, P, P, I, I, P, P, P, I, I, P, P, P, P, SZ, P], I),
         "eagle3_kv_commit": ([P, I, P, I, I, P, P, I, P, P, P, P, P], I),
+        "eagle3_harness_cost": ([P, I, I, I, ctypes.c_float, P], I),
+        "eagle3_harness_continue": ([P, I, I, I, I, P, ctypes.c_double, ctypes.c_double, P], I),
+        "eagle3_harness_verify_count": ([P, I, I, I, P, ctypes.c_double, P], I),
+        "eagle3_harness_branch_cap": ([P, I, I, P, ctypes.c_double, P], I),
+        "eagle3_tree_confidence": ([I, I, I, I, P, P, P, P], I),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -141,8 +155,9 @@ def dims_of(shape) -> Dims:
 
 def weights_of(t: dict) -> Weights:
     """eagle3_weights from a dict of device tensors (keeps no references)."""
+    opt = [t[n].data_ptr() if t.get(n) is not None else None for n in ("norm_fc", "norm_post_attn", "norm_post_ffn")]
     return Weights(*(t[n].data_ptr() for n in ("fc", "emb", "qkv", "o", "gate_up", "down", "lm",
-                                                "norm_e", "norm_s", "norm_ffn", "norm_out")), LAYOUT_ROWMAJOR)
+                                                "norm_e", "norm_s", "norm_ffn", "norm_out")), LAYOUT_ROWMAJOR, *opt)
 
 
 # ---------------------------------------------------------------- queries
@@ -299,6 +314,70 @@ def eagle3_kv_commit(dims, n_layers, kv_arr, B, rows, accept_len, accepted, Dmax
     _check("eagle3_kv_commit", load().eagle3_kv_commit(
         ctypes.byref(dims), n_layers, kv_arr, B, rows, ptr(accept_len), ptr(accepted), Dmax, ptr(feats),
         ptr(feats_next), ptr(ctx_len_out), ptr(status), stream_ptr(stream)))
+
+
+# ---------------------------------------------------------------- EAGLE-4 Harness
+class HarnessTable:
+    """A warm-up cost table held in host arrays (kept alive here) plus its
+    eagle3_cost_table struct.  draft_ms / verify_ms: [n_batch][n_ctx][n_tok]."""
+
+    def __init__(self, batch, ctx, tok, draft_ms, verify_ms):
+        import numpy as np
+        self.batch = np.ascontiguousarray(batch, dtype=np.int32)
+        self.ctx = np.ascontiguousarray(ctx, dtype=np.int32)
+        self.tok = np.ascontiguousarray(tok, dtype=np.int32)
+        self.draft_ms = np.ascontiguousarray(draft_ms, dtype=np.float32)
+        self.verify_ms = np.ascontiguousarray(verify_ms, dtype=np.float32)
+        shp = (len(self.batch), len(self.ctx), len(self.tok))
+        assert self.draft_ms.shape == shp and self.verify_ms.shape == shp
+        self.struct = CostTable(*shp, *(a.ctypes.data for a in (self.batch, self.ctx, self.tok, self.draft_ms,
+                                                                 self.verify_ms)))
+
+    def as_dict(self):
+        """The same table in the oracle's form."""
+        return dict(batch=self.batch.tolist(), ctx=self.ctx.tolist(), tok=self.tok.tolist(),
+                    draft=self.draft_ms.astype(float).tolist(), verify=self.verify_ms.astype(float).tolist())
+
+
+def _host_f32(a):
+    import numpy as np
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def harness_cost(table: HarnessTable, kind, B, ctx, n):
+    out = ctypes.c_double(0)
+    _check("eagle3_harness_cost", load().eagle3_harness_cost(ctypes.byref(table.struct), kind, B, ctx, float(n),
+                                                             ctypes.byref(out)))
+    return out.value
+
+
+def harness_continue(table: HarnessTable, B, ctx, k, depth, frontier_logconf, tau0, alpha):
+    a = _host_f32(frontier_logconf)
+    go = ctypes.c_int(0)
+    _check("eagle3_harness_continue", load().eagle3_harness_continue(
+        ctypes.byref(table.struct), B, ctx, k, depth, a.ctypes.data, float(tau0), float(alpha), ctypes.byref(go)))
+    return bool(go.value)
+
+
+def harness_verify_count(table: HarnessTable, B, ctx, logconf_sorted, tau):
+    a = _host_f32(logconf_sorted)
+    m = ctypes.c_int(0)
+    _check("eagle3_harness_verify_count", load().eagle3_harness_verify_count(
+        ctypes.byref(table.struct), B, ctx, a.shape[1], a.ctypes.data, float(tau), ctypes.byref(m)))
+    return m.value
+
+
+def harness_branch_cap(table: HarnessTable, B, ctx, root_lp, tau):
+    a = _host_f32(root_lp)
+    k = ctypes.c_int(0)
+    _check("eagle3_harness_branch_cap", load().eagle3_harness_branch_cap(
+        ctypes.byref(table.struct), B, ctx, a.ctypes.data, float(tau), ctypes.byref(k)))
+    return k.value
+
+
+def eagle3_tree_confidence(B, k, D, m_max, tree_state, frontier_logconf, pool_logconf, stream=None):
+    _check("eagle3_tree_confidence", load().eagle3_tree_confidence(
+        B, k, D, m_max, ptr(tree_state), ptr(frontier_logconf), ptr(pool_logconf), stream_ptr(stream)))
 
 
 # ---------------------------------------------------------------- kernel timing

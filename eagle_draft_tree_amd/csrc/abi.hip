@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "draft.hpp"
+#include "harness.hpp"
 #include "eagle3.h"
 #include "kernels.hpp"
 #include "pack.hpp"
@@ -66,6 +67,8 @@ int check_weights(const eagle3_weights* w) {
   REQUIRE(w->norm_e && w->norm_s && w->norm_ffn && w->norm_out, EAGLE3_EINVAL, "a norm gain is NULL");
   REQUIRE(w->layout == EAGLE3_LAYOUT_ROWMAJOR || w->layout == EAGLE3_LAYOUT_PACKED, EAGLE3_EINVAL, "layout %d",
           w->layout);
+  REQUIRE((w->norm_post_attn == nullptr) == (w->norm_post_ffn == nullptr), EAGLE3_EINVAL,
+          "post-norm needs both norm_post_attn and norm_post_ffn");
   return EAGLE3_OK;
 }
 
@@ -358,6 +361,7 @@ int eagle3_ttt_forward(const eagle3_dims* dims, const eagle3_weights* w, const v
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
   REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "TTT needs bf16");
+  REQUIRE(!w->norm_fc && !w->norm_post_attn, EAGLE3_EUNSUPPORTED, "TTT forward: no FC-norm / post-norm variant");
   REQUIRE(feats && tokens && pred && ce && loss && ws, EAGLE3_EINVAL, "a required pointer is NULL");
   REQUIRE(B >= 1 && S >= 1 && R >= 1, EAGLE3_EINVAL, "B/S/R");
   REQUIRE(S % 64 == 0, EAGLE3_EUNSUPPORTED, "S=%d must be a multiple of 64", S);
@@ -480,6 +484,72 @@ int eagle3_kv_commit(const eagle3_dims* dims, int n_layers, const eagle3_kv* kv,
   return hip_status(e3::kv_commit(*dims, n_layers, kv, B, rows, accept_len, accepted, Dmax, feats, feats_next,
                                   ctx_len_out, status, (hipStream_t)stream),
                     "eagle3_kv_commit");
+}
+
+}  // extern "C"
+
+namespace {
+int check_table(const eagle3_cost_table* t) {
+  REQUIRE(t, EAGLE3_EINVAL, "cost table is NULL");
+  REQUIRE(t->n_batch >= 1 && t->n_ctx >= 1 && t->n_tok >= 1, EAGLE3_EINVAL, "empty cost table");
+  REQUIRE(t->batch && t->ctx && t->tok && t->draft_ms && t->verify_ms, EAGLE3_EINVAL, "a cost-table array is NULL");
+  for (int i = 1; i < t->n_batch; ++i) REQUIRE(t->batch[i] > t->batch[i - 1], EAGLE3_EINVAL, "batch not ascending");
+  for (int i = 1; i < t->n_ctx; ++i) REQUIRE(t->ctx[i] > t->ctx[i - 1], EAGLE3_EINVAL, "ctx not ascending");
+  for (int i = 1; i < t->n_tok; ++i) REQUIRE(t->tok[i] > t->tok[i - 1], EAGLE3_EINVAL, "tok not ascending");
+  return EAGLE3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int eagle3_harness_cost(const eagle3_cost_table* t, int kind, int B, int ctx, float n, double* ms) {
+  int rc = check_table(t);
+  if (rc) return rc;
+  REQUIRE(kind == EAGLE3_COST_DRAFT || kind == EAGLE3_COST_VERIFY, EAGLE3_EINVAL, "kind %d", kind);
+  REQUIRE(ms, EAGLE3_EINVAL, "ms is NULL");
+  *ms = e3::harness_cost(*t, kind, B, ctx, (double)n);
+  return ok();
+}
+
+int eagle3_harness_continue(const eagle3_cost_table* t, int B, int ctx, int k, int depth,
+                            const float* frontier_logconf, double tau0, double alpha, int* go) {
+  int rc = check_table(t);
+  if (rc) return rc;
+  REQUIRE(B >= 1 && k >= 1 && depth >= 0, EAGLE3_EINVAL, "B/k/depth");
+  REQUIRE(frontier_logconf && go, EAGLE3_EINVAL, "frontier_logconf/go is NULL");
+  *go = e3::harness_continue(*t, B, ctx, k, depth, frontier_logconf, tau0, alpha, nullptr);
+  return ok();
+}
+
+int eagle3_harness_verify_count(const eagle3_cost_table* t, int B, int ctx, int m_max, const float* logconf_sorted,
+                                double tau, int* m) {
+  int rc = check_table(t);
+  if (rc) return rc;
+  REQUIRE(B >= 1 && m_max >= 0, EAGLE3_EINVAL, "B/m_max");
+  REQUIRE((logconf_sorted || m_max == 0) && m, EAGLE3_EINVAL, "logconf_sorted/m is NULL");
+  *m = e3::harness_verify_count(*t, B, ctx, m_max, logconf_sorted, tau);
+  return ok();
+}
+
+int eagle3_harness_branch_cap(const eagle3_cost_table* t, int B, int ctx, const float* root_lp, double tau, int* k) {
+  int rc = check_table(t);
+  if (rc) return rc;
+  REQUIRE(B >= 1, EAGLE3_EINVAL, "B=%d", B);
+  REQUIRE(root_lp && k, EAGLE3_EINVAL, "root_lp/k is NULL");
+  *k = e3::harness_branch_cap(*t, B, ctx, root_lp, tau);
+  return ok();
+}
+
+int eagle3_tree_confidence(int B, int k, int D, int m_max, const void* tree_state, float* frontier_logconf,
+                           float* pool_logconf, eagle3_stream_t stream) {
+  REQUIRE(B >= 1 && k >= 1 && D >= 1 && m_max >= 0, EAGLE3_EINVAL, "B/k/D/m_max");
+  REQUIRE(k <= EAGLE3_MAX_TOPK && (D - 1) * k <= EAGLE3_MAX_TREE_SLOTS, EAGLE3_ECAPACITY, "k=%d D=%d", k, D);
+  REQUIRE(tree_state, EAGLE3_EINVAL, "tree_state is NULL");
+  REQUIRE(frontier_logconf || pool_logconf, EAGLE3_EINVAL, "no output");
+  e3::TimedScope ts(EAGLE3_KC_TREE, (hipStream_t)stream);
+  return hip_status(e3::launch_tree_confidence(B, k, D, pool_logconf ? m_max : 0, tree_state, frontier_logconf,
+                                               pool_logconf, (hipStream_t)stream),
+                    "eagle3_tree_confidence");
 }
 
 }  // extern "C"

@@ -377,8 +377,12 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
 // KVM: cache addressing, 0 = contiguous, 1 = paged with the wave's block
 // entries staged in lanes (at most 64), 2 = paged with a table load per key.
 // MERGE: a workgroup's four waves are four splits merged before the store.
-template <int HD, int KVM, bool MERGE>
-__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(AttnArgs a) {
+// QG: 16-query groups per wave (1 or 2).  Every K/V sub-chunk a wave loads
+// serves all of its QG groups, so many query rows (a verification forward's
+// m+1 rows times the GQA group) load each key QG times fewer.
+template <int HD, int KVM, bool MERGE, int QG>
+__global__ __launch_bounds__(ATT_THREADS)
+__attribute__((amdgpu_waves_per_eu(QG == 1 ? 3 : 2))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = HD / 32;             // k-steps of S
   constexpr int HT = HD / 16;             // head-dim tiles of O^T
   constexpr int VROW = HD + 16;           // padded V tile row (elements)
@@ -405,11 +409,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     wsplit = wid / a.hkv;
     g = wid - wsplit * a.hkv;
   }
-  const int qgrp = blockIdx.y;
   const int b = blockIdx.z;
   const int G = a.hq / a.hkv;
   const int nq_total = a.rows * G;
-  const int q0 = qgrp * 16;
+  const int q0 = blockIdx.y * QG * 16;          // the wave's first query vector
   if (q0 >= nq_total) return;                   // uniform over the workgroup
   if (!merge4 && wsplit >= a.nsplits) return;  // no workgroup barrier without MERGE
   const int ctx = a.ctx_len[b];
@@ -422,20 +425,24 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
   const int i0 = min(wsplit * per, n_act), i1 = min(i0 + per, n_act);
   bf16* vt = vtile[w];
 
-  // the lane's query vector: row rr = qi / G, head g*G + qi % G (none past nq)
-  const int qi = q0 + c16;
-  const int qrow = qi < nq_total ? qi / G : -1;
-  bf16x8 qf[KS];
-  {
+  // the lane's query vector of group u: qi = q0 + 16u + c16, row qi / G,
+  // head g*G + qi % G (none past nq_total: qrow = -1, zero q)
+  int qrow[QG];
+  bf16x8 qf[QG][KS];
+  uint64_t vis_tree[QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u) {
+    const int qi = q0 + 16 * u + c16;
+    qrow[u] = qi < nq_total ? qi / G : -1;
     const int h = g * G + (qi - (qi / G) * G);
-    const bf16* qp = (const bf16*)a.q + ((size_t)(b * a.rows + max(qrow, 0)) * a.hq + h) * HD + 8 * g16;
+    const bf16* qp = (const bf16*)a.q + ((size_t)(b * a.rows + max(qrow[u], 0)) * a.hq + h) * HD + 8 * g16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4 v = *(const u32x4*)(qp + ks * 32);
-      qf[ks] = as_bf16x8(qrow >= 0 ? v : u32x4{0u, 0u, 0u, 0u});
+      qf[u][ks] = as_bf16x8(qrow[u] >= 0 ? v : u32x4{0u, 0u, 0u, 0u});
     }
+    vis_tree[u] = (tree && qrow[u] >= 0) ? a.anc[b * a.rows + qrow[u]] : 0ull;
   }
-  const uint64_t vis_tree = (tree && qrow >= 0) ? a.anc[b * a.rows + qrow] : 0ull;
   // tree slots some row can see (others are never loaded): the rows' masks
   // are loaded across the lanes and OR-reduced
   uint64_t any_vis = ~0ull;
@@ -462,10 +469,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     blk_reg = __builtin_amdgcn_update_dpp(0, blk_reg, 0xE4, 0xF, 0xF, false);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[HT];
+  float m_run[QG], l_run[QG];
+  f32x4 o[QG][HT];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) o[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < QG; ++u) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) o[u][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Source row of key p (0..31) of active sub-chunk i, and whether it is a
   // real, possibly visible key.  Every lane calls it (the block shuffle
@@ -524,128 +536,147 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const uint32_t keep = 0u - ((okm >> (2 + v)) & 1u);
       *(u32x4*)(vt + pk * VROW + 8 * c) = vf[v] & keep;
     }
-    // S^T = K Q^T for the two 16-key tiles
-    f32x4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const uint32_t keep = 0u - ((okm >> kt) & 1u);
-      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kt][ks] & keep), qf[ks], sc[kt], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] &= keep;
     }
-    // mask and scale: key p0 + kt*16 + 4*g16 + t for the lane's query row
     const bool is_tree = i >= ncs;
     const int p0 = is_tree ? (i - ncs) * SUB : i * SUB;
-    const int lim = tree ? ctx : ctx + qrow + 1;
-    float x[8];
-    float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int u = 0; u < QG; ++u) {
+      // S^T = K Q^T for the two 16-key tiles
+      f32x4 sc[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pk = p0 + kt * 16 + 4 * g16 + t;
-        const bool vis = qrow >= 0 && (is_tree ? ((vis_tree >> pk) & 1ull) != 0 : pk < lim);
-        x[kt * 4 + t] = vis ? sc[kt][t] * a.scale : -INFINITY;
-        mloc = fmaxf(mloc, x[kt * 4 + t]);
+      for (int kt = 0; kt < 2; ++kt) {
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kt][ks]), qf[u][ks], sc[kt], 0, 0, 0);
       }
-    const float m_new = fmaxf(m_run, xor_max16_32(mloc));
-    const float al = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
-    float psum = 0.f;
+      // mask and scale: key p0 + kt*16 + 4*g16 + t for the lane's query row
+      const int lim = tree ? ctx : ctx + qrow[u] + 1;
+      float x[8];
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      x[t] = m_new == -INFINITY ? 0.f : expf(x[t] - m_new);
-      psum += x[t];
-    }
-    l_run = l_run * al + psum;
-    m_run = m_new;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) o[ht] *= al;
-    bf16x8 phi, plo;
-    split_bf16x8(x, phi, plo);
+        for (int t = 0; t < 4; ++t) {
+          const int pk = p0 + kt * 16 + 4 * g16 + t;
+          const bool vis = qrow[u] >= 0 && (is_tree ? ((vis_tree[u] >> pk) & 1ull) != 0 : pk < lim);
+          x[kt * 4 + t] = vis ? sc[kt][t] * a.scale : -INFINITY;
+          mloc = fmaxf(mloc, x[kt * 4 + t]);
+        }
+      const float m_new = fmaxf(m_run[u], xor_max16_32(mloc));
+      const float al = m_new == -INFINITY ? 1.f : expf(m_run[u] - m_new);
+      float psum = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      // V^T fragment: dims ht*16 + c16, keys {4*g16 + t} and {16 + 4*g16 + t}, t < 4
-      const bf16* src = vt + (4 * g16 + (c16 >> 2)) * VROW + ht * 16 + 4 * (c16 & 3);
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)src);
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(src + 16 * VROW));
-      const bf16x8 vfr = cat_bf16x8(va, vb);
-      o[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, phi, o[ht], 0, 0, 0);
-      o[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, plo, o[ht], 0, 0, 0);
+      for (int t = 0; t < 8; ++t) {
+        x[t] = m_new == -INFINITY ? 0.f : expf(x[t] - m_new);
+        psum += x[t];
+      }
+      l_run[u] = l_run[u] * al + psum;
+      m_run[u] = m_new;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) o[u][ht] *= al;
+      bf16x8 phi, plo;
+      split_bf16x8(x, phi, plo);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        // V^T fragment: dims ht*16 + c16, keys {4*g16 + t} and {16 + 4*g16 + t}, t < 4
+        const bf16* src = vt + (4 * g16 + (c16 >> 2)) * VROW + ht * 16 + 4 * (c16 & 3);
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)src);
+        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(src + 16 * VROW));
+        const bf16x8 vfr = cat_bf16x8(va, vb);
+        o[u][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, phi, o[u][ht], 0, 0, 0);
+        o[u][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, plo, o[u][ht], 0, 0, 0);
+      }
     }
   }
   // the wave's split: (m, l) per query and o (unnormalised, relative to m)
-  const float l = xor_sum16_32(l_run);
   if constexpr (!merge4) {
-    if (qrow < 0) return;
-    const int h = g * G + (qi - qrow * G);
-    const size_t oi = ((size_t)(b * a.rows + qrow) * a.hq + h) * a.nsplits + wsplit;
-    if (g16 == 0) {
-      a.part_ml[2 * oi] = m_run;
-      a.part_ml[2 * oi + 1] = l;
-    }
-    float* dst = a.part_o + oi * HD + 4 * g16;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) *(float4*)(dst + ht * 16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
+    for (int u = 0; u < QG; ++u) {
+      const float l = xor_sum16_32(l_run[u]);
+      if (qrow[u] < 0) continue;
+      const int qi = q0 + 16 * u + c16;
+      const int h = g * G + (qi - qrow[u] * G);
+      const size_t oi = ((size_t)(b * a.rows + qrow[u]) * a.hq + h) * a.nsplits + wsplit;
+      if (g16 == 0) {
+        a.part_ml[2 * oi] = m_run[u];
+        a.part_ml[2 * oi + 1] = l;
+      }
+      float* dst = a.part_o + oi * HD + 4 * g16;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        *(float4*)(dst + ht * 16) = make_float4(o[u][ht][0], o[u][ht][1], o[u][ht][2], o[u][ht][3]);
+    }
     return;
   }
-  // MERGE: into the wave's own V-tile space as [query][HD + 4] floats
+  // MERGE, one query group at a time: into the wave's own V-tile space as
+  // [query][HD + 4] floats, then the four splits in wave order
   constexpr int OROW = HD + 4;  // padded: the 16 queries' float4 stores hit distinct banks
   static_assert(16 * OROW * 4 <= SUB * VROW * 2, "merge rows fit the V tile");
   const int sgi = wsplit >> 2;
-  asm volatile("" ::: "memory");  // the last V-tile reads stay before the stores below
-  float* ow = (float*)vt;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-    *(float4*)(ow + c16 * OROW + ht * 16 + 4 * g16) = make_float4(o[ht][0], o[ht][1], o[ht][2], o[ht][3]);
-  if (g16 == 0) {
-    mred[w][c16] = m_run;
-    lred[w][c16] = l;
-  }
-  __syncthreads();
-  // merge the four splits in wave order: thread t takes query t/16 and dims
-  // DPT*(t%16) ..; the merged partial is the split group's
   constexpr int DPT = HD / 16;
   const int qc = threadIdx.x >> 4, j = threadIdx.x & 15;
-  float mw[4], M = -INFINITY;
+  float* ow = (float*)vt;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    mw[u] = mred[u][qc];
-    M = fmaxf(M, mw[u]);
-  }
-  float wt[4], L = 0.f;
+  for (int u = 0; u < QG; ++u) {
+    const float l = xor_sum16_32(l_run[u]);
+    __syncthreads();  // the V tiles (and the previous group's merge rows) are no longer read
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    wt[u] = mw[u] == -INFINITY ? 0.f : expf(mw[u] - M);
-    L += lred[u][qc] * wt[u];
-  }
-  float acc[DPT];
+    for (int ht = 0; ht < HT; ++ht)
+      *(float4*)(ow + c16 * OROW + ht * 16 + 4 * g16) = make_float4(o[u][ht][0], o[u][ht][1], o[u][ht][2],
+                                                                    o[u][ht][3]);
+    if (g16 == 0) {
+      mred[w][c16] = m_run[u];
+      lred[w][c16] = l;
+    }
+    __syncthreads();
+    // thread t takes query t/16 and dims DPT*(t%16) ..; the merged partial is the split group's
+    float mw[4], M = -INFINITY;
 #pragma unroll
-  for (int d = 0; d < DPT; ++d) acc[d] = 0.f;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      mw[s4] = mred[s4][qc];
+      M = fmaxf(M, mw[s4]);
+    }
+    float wt[4], L = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float* src = (const float*)vtile[u] + qc * OROW + DPT * j;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      wt[s4] = mw[s4] == -INFINITY ? 0.f : expf(mw[s4] - M);
+      L += lred[s4][qc] * wt[s4];
+    }
+    float acc[DPT];
 #pragma unroll
-    for (int d = 0; d < DPT; d += 4) {
-      const float4 v = *(const float4*)(src + d);
-      acc[d] = fmaf(v.x, wt[u], acc[d]);
-      acc[d + 1] = fmaf(v.y, wt[u], acc[d + 1]);
-      acc[d + 2] = fmaf(v.z, wt[u], acc[d + 2]);
-      acc[d + 3] = fmaf(v.w, wt[u], acc[d + 3]);
+    for (int d = 0; d < DPT; ++d) acc[d] = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float* src = (const float*)vtile[s4] + qc * OROW + DPT * j;
+#pragma unroll
+      for (int d = 0; d < DPT; d += 4) {
+        const float4 v = *(const float4*)(src + d);
+        acc[d] = fmaf(v.x, wt[s4], acc[d]);
+        acc[d + 1] = fmaf(v.y, wt[s4], acc[d + 1]);
+        acc[d + 2] = fmaf(v.z, wt[s4], acc[d + 2]);
+        acc[d + 3] = fmaf(v.w, wt[s4], acc[d + 3]);
+      }
+    }
+    const int qim = q0 + 16 * u + qc;
+    if (qim < nq_total) {
+      const int qrm = qim / G;
+      const int h = g * G + (qim - qrm * G);
+      const size_t oi = ((size_t)(b * a.rows + qrm) * a.hq + h) * nsg + sgi;
+      if (j == 0) {
+        a.part_ml[2 * oi] = M;
+        a.part_ml[2 * oi + 1] = L;
+      }
+      float* dst = a.part_o + oi * HD + DPT * j;
+#pragma unroll
+      for (int d = 0; d < DPT; d += 4) *(float4*)(dst + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
     }
   }
-  const int qim = q0 + qc;
-  if (qim >= nq_total) return;
-  const int qrm = qim / G;
-  const int h = g * G + (qim - qrm * G);
-  const size_t oi = ((size_t)(b * a.rows + qrm) * a.hq + h) * nsg + sgi;
-  if (j == 0) {
-    a.part_ml[2 * oi] = M;
-    a.part_ml[2 * oi + 1] = L;
-  }
-  float* dst = a.part_o + oi * HD + DPT * j;
-#pragma unroll
-  for (int d = 0; d < DPT; d += 4) *(float4*)(dst + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
 }
 
 // out[row][h*hd + i] = merged attention output, rounded to T.  One
@@ -771,9 +802,15 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     // nsplits is sized so that the launch holds about 8192 waves of
     // capacity-sized work.
     a.n_qgroups = (nq + 15) / 16;
+    // query groups per wave: two when many rows share the keys (the 70B
+    // verification forward's 61 rows x 8 GQA heads, about 9 % faster), one
+    // otherwise (measured: the 8B forward's 16 groups run faster with one,
+    // and four per wave, at one wave per SIMD, is slower everywhere)
+    const int QG = a.n_qgroups > 16 ? 2 : 1;
+    const int nwq = (a.n_qgroups + QG - 1) / QG;
     a.n_cache_sub = (L.cap_rows + SUB - 1) / SUB;
     const int n_sub = a.n_cache_sub + (L.mode == EAGLE3_TREE ? 2 : 0);
-    const long units = (long)n_sub * L.hkv * a.n_qgroups * L.B;
+    const long units = (long)n_sub * L.hkv * nwq * L.B;
     int spw = (int)((units + 8191) / 8192);
     const int spw_min = (n_sub + 511) / 512;
     spw = spw < spw_min ? spw_min : spw;
@@ -789,12 +826,17 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     const bool merge4 = a.nsplits >= 32;
     const int nsg = (a.nsplits + 3) / 4;
     const int nparts = merge4 ? nsg : a.nsplits;
-    dim3 grid(merge4 ? nsg * L.hkv : (a.nsplits * L.hkv + 3) / 4, a.n_qgroups, L.B);
-#define E3_MFMA_K(HD, M)                                                               \
-  do {                                                                                 \
-    if (kvm == 0) attn_mfma_kernel<HD, 0, M><<<grid, ATT_THREADS, 0, st>>>(a);         \
-    else if (kvm == 1) attn_mfma_kernel<HD, 1, M><<<grid, ATT_THREADS, 0, st>>>(a);    \
-    else attn_mfma_kernel<HD, 2, M><<<grid, ATT_THREADS, 0, st>>>(a);                  \
+    dim3 grid(merge4 ? nsg * L.hkv : (a.nsplits * L.hkv + 3) / 4, nwq, L.B);
+#define E3_MFMA_Q(HD, KV, M)                                                      \
+  do {                                                                            \
+    if (QG == 1) attn_mfma_kernel<HD, KV, M, 1><<<grid, ATT_THREADS, 0, st>>>(a); \
+    else attn_mfma_kernel<HD, KV, M, 2><<<grid, ATT_THREADS, 0, st>>>(a);         \
+  } while (0)
+#define E3_MFMA_K(HD, M)                   \
+  do {                                     \
+    if (kvm == 0) E3_MFMA_Q(HD, 0, M);     \
+    else if (kvm == 1) E3_MFMA_Q(HD, 1, M); \
+    else E3_MFMA_Q(HD, 2, M);              \
   } while (0)
 #define E3_MFMA(HD)              \
   do {                           \
@@ -810,6 +852,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     }
 #undef E3_MFMA
 #undef E3_MFMA_K
+#undef E3_MFMA_Q
     return hipGetLastError();
   }
   // fp32 caches (head_dim 64, validated by the caller): vector-ALU kernel

@@ -55,7 +55,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds)
+      : "v"(src), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))  // wave-uniform by contract
       : "memory");
 }
 template <int N>

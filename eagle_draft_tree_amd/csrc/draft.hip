@@ -78,14 +78,15 @@ __global__ __launch_bounds__(RT) void prologue_kernel(
 }
 
 // h2 = h1 + sum of down partials (splits > 0), or h2 already complete;
-// h2 rows -> h_tree (COMMIT: last row of each request -> slot 0; TREE: row
-// rr -> 1 + slot_base + rr); y = rms(h2)*gain for the rows whose top-k is
-// taken (all rows, or the last row of each request), packed.
+// post-norm (post_gain not NULL): h2 = rms(h2) * post_gain; h2 rows ->
+// h_tree (COMMIT: last row of each request -> slot 0; TREE: row rr -> 1 +
+// slot_base + rr); y = rms(h2)*gain for the rows whose top-k is taken (all
+// rows, or the last row of each request), packed.
 template <typename T>
 __global__ __launch_bounds__(RT) void final_norm_kernel(
     const float* __restrict__ h1, const float* __restrict__ part, int splits, int R, const float* __restrict__ h2buf,
     int d, const float* __restrict__ gain, float eps, int mode, int rows, int slot_base, int topk_last,
-    float* __restrict__ h_tree, T* __restrict__ y) {
+    float* __restrict__ h_tree, T* __restrict__ y, const float* __restrict__ post_gain = nullptr) {
   __shared__ float red[RT / 64];
   const int r = blockIdx.x;
   const int b = r / rows, rr = r - b * rows;
@@ -101,6 +102,18 @@ __global__ __launch_bounds__(RT) void final_norm_kernel(
     v[j] = i < d ? (splits > 0 ? h1[(size_t)r * d + i] : h2buf[(size_t)r * d + i]) : 0.f;
   }
   if (splits > 0) add_partials(v, part, splits, (size_t)R * d, (size_t)r * d, d);
+  if (post_gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
+    ss = block_sum(ss, red);
+    const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+#pragma unroll
+    for (int j = 0; j < EPT_MAX; ++j) {
+      const int i = threadIdx.x + RT * j;
+      v[j] = i < d ? v[j] * inv * post_gain[i] : 0.f;
+    }
+  }
   if (hslot >= 0) {
     float* dst = h_tree + ((size_t)b * (EAGLE3_MAX_TREE_SLOTS + 1) + hslot) * d;
 #pragma unroll
@@ -120,6 +133,29 @@ __global__ __launch_bounds__(RT) void final_norm_kernel(
   for (int j = 0; j < EPT_MAX; ++j) {
     const int i = threadIdx.x + RT * j;
     if (i < d) Elem<T>::st(y, (size_t)yr * d + i, v[j] * inv * gain[i]);
+  }
+}
+
+// FC norm: g = rms(sum of fusion partials) * gain, rounded once; one
+// workgroup per row (partials [splits][n][d])
+template <typename T>
+__global__ __launch_bounds__(RT) void fuse_norm_kernel(const float* __restrict__ part, int splits, int n, int d,
+                                                       const float* __restrict__ gain, float eps, T* __restrict__ g) {
+  __shared__ float red[RT / 64];
+  const int r = blockIdx.x;
+  float v[EPT_MAX];
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) v[j] = 0.f;
+  add_partials(v, part, splits, (size_t)n * d, (size_t)r * d, d);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = block_sum(ss, red);
+  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+#pragma unroll
+  for (int j = 0; j < EPT_MAX; ++j) {
+    const int i = threadIdx.x + RT * j;
+    if (i < d) Elem<T>::st(g, (size_t)r * d + i, v[j] * inv * gain[i]);
   }
 }
 
@@ -303,7 +339,11 @@ size_t draft_ws_bytes(const eagle3_dims& dm, int B, int max_rows, int max_ctx) {
   return a > f ? a : f;
 }
 
-size_t fuse_ws_bytes(const eagle3_dims& dm, int n) { return max_partials(dm, n) * 4 + 512; }
+// split-K partials, or (FC norm without a split) the float32 projection [n][d]
+size_t fuse_ws_bytes(const eagle3_dims& dm, int n) {
+  const size_t p = max_partials(dm, n), f = (size_t)n * dm.d;
+  return (p > f ? p : f) * 4 + 512;
+}
 
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -318,6 +358,10 @@ static hipError_t fuse_impl(const eagle3_dims& dm, const eagle3_weights& w, cons
     EpiPartial epi{(float*)ws, dm.d, map};
     hipError_t e = rows_gemm<T>((const T*)feats, K, n, (const T*)w.fc, K, dm.d, map, epi, p, pk, st);
     if (e != hipSuccess) return e;
+    if (w.norm_fc) {
+      fuse_norm_kernel<T><<<n, RT, 0, st>>>((const float*)ws, p.splits, n, dm.d, w.norm_fc, dm.rms_eps, (T*)g);
+      return hipGetLastError();
+    }
     int blocks = (int)(((size_t)n * dm.d + 255) / 256);
     if (blocks > 1024) blocks = 1024;
     fuse_finish_kernel<T><<<blocks, 256, 0, st>>>((const float*)ws, p.splits, n, dm.d, (T*)g);
@@ -326,9 +370,19 @@ static hipError_t fuse_impl(const eagle3_dims& dm, const eagle3_weights& w, cons
   for (int r0 = 0; r0 < n; r0 += 64) {
     const int R = n - r0 < 64 ? n - r0 : 64;
     const RowsPlan pc = plan_rows(R, dm.d, K, sizeof(T) == 2, false);
-    EpiStore<T> epi{(T*)g + (size_t)r0 * dm.d, dm.d, map};
-    hipError_t e = rows_gemm<T>((const T*)feats + (size_t)r0 * K, K, R, (const T*)w.fc, K, dm.d, map, epi, pc, pk, st);
+    hipError_t e;
+    if (w.norm_fc) {  // float32 projection into the workspace, normalised below
+      EpiStore<float> epi{(float*)ws + (size_t)r0 * dm.d, dm.d, map};
+      e = rows_gemm<T>((const T*)feats + (size_t)r0 * K, K, R, (const T*)w.fc, K, dm.d, map, epi, pc, pk, st);
+    } else {
+      EpiStore<T> epi{(T*)g + (size_t)r0 * dm.d, dm.d, map};
+      e = rows_gemm<T>((const T*)feats + (size_t)r0 * K, K, R, (const T*)w.fc, K, dm.d, map, epi, pc, pk, st);
+    }
     if (e != hipSuccess) return e;
+  }
+  if (w.norm_fc) {
+    fuse_norm_kernel<T><<<n, RT, 0, st>>>((const float*)ws, 1, n, dm.d, w.norm_fc, dm.rms_eps, (T*)g);
+    return hipGetLastError();
   }
   return hipSuccess;
 }
@@ -450,7 +504,9 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   }
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
-    ffn_norm_kernel<T><<<R, RT, 0, st>>>(ws.S, ws.part, o_splits, R, d, w.norm_ffn, dm.rms_eps, ws.h1, (T*)ws.u);
+    const bool post = w.norm_post_attn != nullptr;
+    ffn_norm_kernel<T><<<R, RT, 0, st>>>(ws.S, ws.part, o_splits, R, d, post ? w.norm_post_attn : w.norm_ffn,
+                                         dm.rms_eps, ws.h1, (T*)ws.u, post);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // ---- gate/up + SwiGLU
@@ -489,7 +545,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
   {
     TimedScope ts(EAGLE3_KC_ROWOPS, st);
     final_norm_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, down_splits, R, ws.h2, d, w.norm_out, dm.rms_eps, c.mode,
-                                           c.rows, c.slot_base, topk_last, c.h_tree, (T*)ws.y);
+                                           c.rows, c.slot_base, topk_last, c.h_tree, (T*)ws.y, w.norm_post_ffn);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // ---- LM head + top-k

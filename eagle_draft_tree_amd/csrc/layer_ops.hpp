@@ -22,27 +22,37 @@ constexpr int EPT_MAX = 8;    // elements per thread: d <= 8192
 // row kernels: every thread owns elements i = threadIdx.x + RT*j, j < EPT_MAX,
 // and issues all of its loads before using any of them.
 
-// v[j] += sum over splits of part[s][row][i] (fixed split order)
+// v[j] += sum over splits of part[s][row][i] (fixed split order).  Four
+// splits' loads are issued before any of them is added, so a row's 8 or 16
+// splits take two to four memory round trips instead of one each.
 __device__ __forceinline__ void add_partials(float (&v)[EPT_MAX], const float* __restrict__ part, int splits,
                                              size_t split_stride, size_t row_off, int d) {
-  for (int s = 0; s < splits; ++s) {
-    float p[EPT_MAX];
+  constexpr int SG = 4;
+  for (int s0 = 0; s0 < splits; s0 += SG) {
+    float p[SG][EPT_MAX];
 #pragma unroll
-    for (int j = 0; j < EPT_MAX; ++j) {
-      const int i = threadIdx.x + RT * j;
-      p[j] = i < d ? part[(size_t)s * split_stride + row_off + i] : 0.f;
-    }
+    for (int u = 0; u < SG; ++u)
 #pragma unroll
-    for (int j = 0; j < EPT_MAX; ++j) v[j] += p[j];
+      for (int j = 0; j < EPT_MAX; ++j) {
+        const int i = threadIdx.x + RT * j;
+        p[u][j] = (s0 + u < splits && i < d) ? part[(size_t)(s0 + u) * split_stride + row_off + i] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < SG; ++u)
+      if (s0 + u < splits)
+#pragma unroll
+        for (int j = 0; j < EPT_MAX; ++j) v[j] += p[u][j];
   }
 }
 
 // h1 = res + sum of o partials (splits > 0), or h1 already complete;
-// u = rms(h1) * gain (dtype)
+// pre-norm (post == 0): u = rms(h1) * gain (dtype); post-norm (post != 0):
+// h1 = rms(h1) * gain is stored and u = h1 (dtype), the FFN's input.
 template <typename T>
 __global__ __launch_bounds__(RT) void ffn_norm_kernel(const float* __restrict__ res, const float* __restrict__ part,
                                                       int splits, int R, int d, const float* __restrict__ gain,
-                                                      float eps, float* __restrict__ h1, T* __restrict__ u) {
+                                                      float eps, float* __restrict__ h1, T* __restrict__ u,
+                                                      int post = 0) {
   __shared__ float red[RT / 64];
   const int r = blockIdx.x;
   float v[EPT_MAX];
@@ -61,8 +71,13 @@ __global__ __launch_bounds__(RT) void ffn_norm_kernel(const float* __restrict__ 
   for (int j = 0; j < EPT_MAX; ++j) {
     const int i = threadIdx.x + RT * j;
     if (i < d) {
-      if (splits > 0) h1[(size_t)r * d + i] = v[j];
-      Elem<T>::st(u, (size_t)r * d + i, v[j] * inv * gain[i]);
+      const float nv = v[j] * inv * gain[i];
+      if (post) {
+        h1[(size_t)r * d + i] = nv;
+      } else if (splits > 0) {
+        h1[(size_t)r * d + i] = v[j];
+      }
+      Elem<T>::st(u, (size_t)r * d + i, nv);
     }
   }
 }

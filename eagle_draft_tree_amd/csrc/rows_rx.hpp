@@ -81,18 +81,57 @@ __global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restr
           acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g].v, wf[s][j].v, acc[g][j], 0, 0, 0);
     }
   };
-  if (nch > 0) issue_x(0);
-  for (int c = 0; c < nch; ++c) {
-    U4 wf[KU][WT];
-    load_w(c, wf);
-    // the X copies of chunk c were issued before these weight loads
-    bg_wait_copies<KU * WT>();
-    bg_barrier();  // chunk c is in LDS for every wave; chunk c-1 is no longer read
-    compute(c, wf);
-    // next chunk's X, into the buffer every wave left before the barrier
-    // above; issued after this chunk's weight waits so that the compiler's
-    // vmcnt counts for its own loads stay exact
-    if (c + 1 < nch) issue_x(c + 1);
+  if constexpr (WAVES >= 8) {
+    // Long k ranges (the unsplit LM head): weights one chunk ahead, chunk
+    // c+1's weight loads in flight while chunk c is computed (two register
+    // buffers, so the loop runs in pairs; measured about 5 % faster on the
+    // 8B batch-64 LM head).  Issue order per chunk: w(c+1), compute(c),
+    // x(c+1); at the top of chunk c the only loads issued after w(c) and
+    // x(c) are those of w(c+1), so vmcnt(KU*WT) means chunk c's weights and
+    // X have landed.  The short split-K ranges keep the single buffer: its
+    // doubled registers halve their occupancy, which costs more than the
+    // overlap gains there (measured).
+    U4 wa[KU][WT], wb[KU][WT];
+    if (nch > 0) {
+      issue_x(0);
+      load_w(0, wa);
+    }
+    for (int c = 0; c < nch; c += 2) {
+      if (c + 1 < nch) {
+        load_w(c + 1, wb);
+        bg_wait_copies<KU * WT>();
+      } else {
+        bg_wait_copies<0>();
+      }
+      bg_barrier();  // chunk c is in LDS for every wave; chunk c-1 is no longer read
+      compute(c, wa);
+      if (c + 1 >= nch) break;
+      // next chunk's X, into the buffer every wave left before the barrier above
+      issue_x(c + 1);
+      if (c + 2 < nch) {
+        load_w(c + 2, wa);
+        bg_wait_copies<KU * WT>();
+      } else {
+        bg_wait_copies<0>();
+      }
+      bg_barrier();
+      compute(c + 1, wb);
+      if (c + 2 < nch) issue_x(c + 2);
+    }
+  } else {
+    if (nch > 0) issue_x(0);
+    for (int c = 0; c < nch; ++c) {
+      U4 wf[KU][WT];
+      load_w(c, wf);
+      // the X copies of chunk c were issued before these weight loads
+      bg_wait_copies<KU * WT>();
+      bg_barrier();  // chunk c is in LDS for every wave; chunk c-1 is no longer read
+      compute(c, wf);
+      // next chunk's X, into the buffer every wave left before the barrier
+      // above; issued after this chunk's weight waits so that the compiler's
+      // vmcnt counts for its own loads stay exact
+      if (c + 1 < nch) issue_x(c + 1);
+    }
   }
   bg_wait_copies<0>();
   __syncthreads();  // every wave is done with the X buffers

@@ -23,7 +23,9 @@
 //            feature layer; x for the next layer (its norm_attn), or the LM
 //            head input (norm_out) after the model's last layer
 // and after the last layer the LM head writes float32 logits.  The residual
-// stream is float32 in `hidden`; GEMM inputs are rounded to the dtype.
+// stream is float32 in `hidden`; GEMM inputs are rounded to the dtype.  More
+// than 64 rows (a batch of chains) run every GEMM and its finish on chunks
+// of 64 rows, each chunk with the split-K plan of its size.
 #include <string.h>
 
 #include "common.hpp"
@@ -121,19 +123,25 @@ __global__ __launch_bounds__(RT) void target_layer_end_kernel(const float* __res
 // ---------------------------------------------------------------------------
 // workspace
 namespace {
-// GEMMs of a target layer: qkv, o, down may split K (<= 64 rows); gate/up
-// and the LM head do not.
+// GEMMs of a target layer: qkv, o and down may split K; gate/up and the LM
+// head do not.  All of them run on row chunks of at most 64 rows (the rows
+// GEMM's limit), so the partials cover the larger of the two chunk sizes a
+// call can have.
 size_t target_partials(const eagle3_dims& dm, int R) {
   const bool bf = dm.dtype == EAGLE3_BF16;
   const int d = dm.d, qd = dm.n_q_heads * dm.head_dim;
   const int nqkv = (dm.n_q_heads + 2 * dm.n_kv_heads) * dm.head_dim;
   const int n[3] = {nqkv, d, d}, k[3] = {d, qd, dm.ffn};
+  const int rc[2] = {R < 64 ? R : 64, R % 64};
   size_t m = 0;
-  for (int i = 0; i < 3; ++i)
-    for (int pk = 0; pk < 2; ++pk) {
-      const size_t f = rows_partial_floats(plan_rows(R, n[i], k[i], bf, true, pk), R, n[i]);
-      if (f > m) m = f;
-    }
+  for (int c = 0; c < 2; ++c) {
+    if (rc[c] == 0) continue;
+    for (int i = 0; i < 3; ++i)
+      for (int pk = 0; pk < 2; ++pk) {
+        const size_t f = rows_partial_floats(plan_rows(rc[c], n[i], k[i], bf, true, pk), rc[c], n[i]);
+        if (f > m) m = f;
+      }
+  }
   return m;
 }
 
@@ -220,31 +228,31 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
     // ---- QKV + RoPE + k/v -> tree slots
     KVDest dst{kv.k, kv.v, kv.tk, kv.tv, kv.ctx_len, kv.block_table, kv.cap, kv.max_blocks, kv.block_size,
                c.rows, EAGLE3_TREE, 0, hkv, hd, 0};
-    {
-      const RowsPlan p = plan_rows(R, nqkv, d, bf, true, pk);
+    // every GEMM below runs on row chunks of at most 64 rows (the last one
+    // ragged), each with its own split-K plan and finish
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      const RowsPlan p = plan_rows(Rc, nqkv, d, bf, true, pk);
+      KVDest dc = dst;
+      dc.row0 = r0;
       if (p.splits > 1) {
         EpiPartial epi{ws.part, nqkv, pair_head};
-        if ((e = rows_gemm<T>((const T*)ws.x, d, R, (const T*)Lw.qkv, d, nqkv, pair_head, epi, p, pk, st)) !=
-            hipSuccess)
+        if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * d, d, Rc, (const T*)Lw.qkv, d, nqkv, pair_head, epi, p,
+                              pk, st)) != hipSuccess)
           return e;
-        qkv_finish_kernel<T><<<dim3(R, hq + 2 * hkv), 64, 0, st>>>(ws.part, p.splits, R, nqkv, c.pos, dst, (T*)ws.q,
-                                                                   hq, dm.rope_theta);
+        qkv_finish_kernel<T><<<dim3(Rc, hq + 2 * hkv), 64, 0, st>>>(ws.part, p.splits, Rc, nqkv, c.pos + r0, dc,
+                                                                    (T*)ws.q + (size_t)r0 * qd, hq, dm.rope_theta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       } else {
-        for (int r0 = 0; r0 < R; r0 += 64) {
-          const int Rc = R - r0 < 64 ? R - r0 : 64;
-          EpiQKV<T> epi;
-          epi.q_out = (T*)ws.q + (size_t)r0 * qd;
-          epi.pos = c.pos + r0;
-          epi.dst = dst;
-          epi.dst.row0 = r0;
-          epi.hq = hq;
-          epi.theta = dm.rope_theta;
-          const RowsPlan pc = plan_rows(Rc, nqkv, d, bf, false);
-          if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * d, d, Rc, (const T*)Lw.qkv, d, nqkv, pair_head, epi, pc,
-                                pk, st)) != hipSuccess)
-            return e;
-        }
+        EpiQKV<T> epi;
+        epi.q_out = (T*)ws.q + (size_t)r0 * qd;
+        epi.pos = c.pos + r0;
+        epi.dst = dc;
+        epi.hq = hq;
+        epi.theta = dm.rope_theta;
+        if ((e = rows_gemm<T>((const T*)ws.x + (size_t)r0 * d, d, Rc, (const T*)Lw.qkv, d, nqkv, pair_head, epi, p,
+                              pk, st)) != hipSuccess)
+          return e;
       }
     }
     // ---- attention over the committed rows and the ancestor slots
@@ -272,28 +280,27 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
     al.part_ml = ws.part_ml;
     al.out = ws.a;
     if ((e = launch_attention(al, st)) != hipSuccess) return e;
-    // ---- O projection (+ residual)
-    int o_splits = 0;
-    {
-      const RowsPlan p = plan_rows(R, d, qd, bf, true, pk);
+    // ---- O projection (+ residual) and the FFN norm
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      const RowsPlan p = plan_rows(Rc, d, qd, bf, true, pk);
+      int o_splits = 0;
       if (p.splits > 1) {
         EpiPartial epi{ws.part, d, plain};
-        if ((e = rows_gemm<T>((const T*)ws.a, qd, R, (const T*)Lw.o, qd, d, plain, epi, p, pk, st)) != hipSuccess)
+        if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)Lw.o, qd, d, plain, epi, p, pk,
+                              st)) != hipSuccess)
           return e;
         o_splits = p.splits;
       } else {
-        for (int r0 = 0; r0 < R; r0 += 64) {
-          const int Rc = R - r0 < 64 ? R - r0 : 64;
-          EpiResidual epi{ws.h1 + (size_t)r0 * d, c.hidden + (size_t)r0 * d, d};
-          const RowsPlan pc = plan_rows(Rc, d, qd, bf, false);
-          if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)Lw.o, qd, d, plain, epi, pc, pk,
-                                st)) != hipSuccess)
-            return e;
-        }
+        EpiResidual epi{ws.h1 + (size_t)r0 * d, c.hidden + (size_t)r0 * d, d};
+        if ((e = rows_gemm<T>((const T*)ws.a + (size_t)r0 * qd, qd, Rc, (const T*)Lw.o, qd, d, plain, epi, p, pk,
+                              st)) != hipSuccess)
+          return e;
       }
+      ffn_norm_kernel<T><<<Rc, RT, 0, st>>>(c.hidden + (size_t)r0 * d, ws.part, o_splits, Rc, d, Lw.norm_ffn,
+                                            dm.rms_eps, ws.h1 + (size_t)r0 * d, (T*)ws.u + (size_t)r0 * d);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    ffn_norm_kernel<T><<<R, RT, 0, st>>>(c.hidden, ws.part, o_splits, R, d, Lw.norm_ffn, dm.rms_eps, ws.h1, (T*)ws.u);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // ---- gate/up + SwiGLU
     for (int r0 = 0; r0 < R; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
@@ -304,34 +311,33 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
                             st, EAGLE3_KC_TGT_GATEUP)) != hipSuccess)
         return e;
     }
-    // ---- down (+ residual)
-    int down_splits = 0;
-    {
-      const RowsPlan p = plan_rows(R, d, F, bf, true, pk);
-      if (p.splits > 1) {
-        EpiPartial epi{ws.part, d, plain};
-        if ((e = rows_gemm<T>((const T*)ws.z, F, R, (const T*)Lw.down, F, d, plain, epi, p, pk, st)) != hipSuccess)
-          return e;
-        down_splits = p.splits;
-      } else {
-        for (int r0 = 0; r0 < R; r0 += 64) {
-          const int Rc = R - r0 < 64 ? R - r0 : 64;
-          EpiResidual epi{ws.h2 + (size_t)r0 * d, ws.h1 + (size_t)r0 * d, d};
-          const RowsPlan pc = plan_rows(Rc, d, F, bf, false);
-          if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)Lw.down, F, d, plain, epi, pc, pk,
-                                st)) != hipSuccess)
-            return e;
-        }
-      }
-    }
-    // ---- layer end: state, features, next norm
+    // ---- down (+ residual) and the layer end: state, features, next norm
     int feat_mask = 0;
     if (c.feats)
       for (int f = 0; f < 3; ++f)
         if (tg.feat_layers[f] == l + 1) feat_mask |= 1 << f;
-    target_layer_end_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, down_splits, R, ws.h2, d, feat_mask, (T*)c.feats,
-                                                 next_gain(l), dm.rms_eps, c.hidden, (T*)ws.x);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int Rc = R - r0 < 64 ? R - r0 : 64;
+      const RowsPlan p = plan_rows(Rc, d, F, bf, true, pk);
+      int down_splits = 0;
+      if (p.splits > 1) {
+        EpiPartial epi{ws.part, d, plain};
+        if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)Lw.down, F, d, plain, epi, p, pk,
+                              st)) != hipSuccess)
+          return e;
+        down_splits = p.splits;
+      } else {
+        EpiResidual epi{ws.h2 + (size_t)r0 * d, ws.h1 + (size_t)r0 * d, d};
+        if ((e = rows_gemm<T>((const T*)ws.z + (size_t)r0 * F, F, Rc, (const T*)Lw.down, F, d, plain, epi, p, pk,
+                              st)) != hipSuccess)
+          return e;
+      }
+      T* fo = c.feats ? (T*)c.feats + (size_t)r0 * 3 * d : nullptr;
+      target_layer_end_kernel<T><<<Rc, RT, 0, st>>>(ws.h1 + (size_t)r0 * d, ws.part, down_splits, Rc,
+                                                    ws.h2 + (size_t)r0 * d, d, feat_mask, fo, next_gain(l),
+                                                    dm.rms_eps, c.hidden + (size_t)r0 * d, (T*)ws.x + (size_t)r0 * d);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
 
   // ---- LM head: float32 logits of every row

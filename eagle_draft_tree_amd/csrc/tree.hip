@@ -9,6 +9,7 @@
 #include <limits.h>
 
 #include "common.hpp"
+#include "harness.hpp"
 #include "kernels.hpp"
 
 namespace e3 {
@@ -355,6 +356,56 @@ hipError_t launch_tree_expand(int phase, int B, int k, int D, int m, const int32
                                                  next_parent_slot, next_pos, next_anc);
   else
     tree_final_kernel<<<B, FIN_THREADS, 0, st>>>(k, D, m, state, v_tok, v_parent, v_depth, v_pos, v_anc);
+  return hipGetLastError();
+}
+
+// Confidences the harness rules read (EAGLE-4 blog, EAGLE-Harness): the
+// frontier's log-confidences in frontier-rank order, and the pool's in
+// rerank order -- descending; equal scores are equal values, so their order
+// does not matter -- with -inf past the pool.  One workgroup per request;
+// a bitonic sort of order-preserving keys in LDS.
+__device__ __forceinline__ uint32_t desc_key(float s) {
+  if (s == 0.f) s = 0.f;  // -0 and +0 compare equal
+  uint32_t u = __float_as_uint(s);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending in s
+  return ~u;                                        // ascending in -s
+}
+__device__ __forceinline__ float key_score(uint32_t key) {
+  const uint32_t u = ~key;
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+__global__ __launch_bounds__(FIN_THREADS) void tree_confidence_kernel(int k, int D, int m_max, void* state,
+                                                                      float* __restrict__ frontier,
+                                                                      float* __restrict__ pool_sorted) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  Pool P = pool_of(state, b, k, D);
+  __shared__ uint32_t sk[FIN_SORT_MAX];
+  const int n = P.hdr->npool;
+  if (frontier && tid < k) frontier[(size_t)b * k + tid] = P.hdr->fscore[tid];
+  int N = 64;
+  while (N < n) N <<= 1;
+  for (int i = tid; i < N; i += FIN_THREADS) sk[i] = i < n ? desc_key(P.score[i]) : 0xffffffffu;
+  __syncthreads();
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < (N >> 1); t += FIN_THREADS) {
+        const int i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1)), j = i | stride;
+        const uint32_t x = sk[i], y = sk[j];
+        if ((x > y) == ((i & size) == 0)) {
+          sk[i] = y;
+          sk[j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < m_max; i += FIN_THREADS) pool_sorted[(size_t)b * m_max + i] = i < n ? key_score(sk[i]) : -INFINITY;
+}
+
+hipError_t launch_tree_confidence(int B, int k, int D, int m_max, const void* state, float* frontier,
+                                  float* pool_sorted, hipStream_t st) {
+  tree_confidence_kernel<<<B, FIN_THREADS, 0, st>>>(k, D, m_max, (void*)state, frontier, pool_sorted);
   return hipGetLastError();
 }
 

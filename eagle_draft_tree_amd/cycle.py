@@ -202,3 +202,88 @@ def run_cycle(dr: Drafter, buf: CycleBuffers, kv: KVCache, feats, tokens, commit
     if verify and target_logits is not None:
         B.eagle3_verify(Bn, m, dr.shape.vocab, D, buf.v_tok, buf.v_parent, target_logits, mode, temperature,
                         u_try, u_res, buf.accept_len, buf.accepted, buf.bonus, buf.status, buf.vws)
+
+
+@dataclass
+class HarnessParams:
+    """Thresholds of the EAGLE-4 Harness rules (eagle3_harness_*)."""
+    tau_depth: float = 0.5     # depth rule: tau0 of tau0 * (1 + alpha * depth)
+    alpha: float = 0.25
+    tau_verify: float = 0.5    # expected accepted tokens per extra verify millisecond
+    tau_branch: float = 0.5    # ... per extra drafting millisecond of 8 branches over 4
+
+
+class HarnessCycle:
+    """A draft cycle under the EAGLE-4 Harness: the COMMIT round's top-8
+    decides the branch cap k (8 or 4); before every further round the depth
+    rule decides whether to draft another layer (at most D_max rounds); the
+    verify-count rule picks m <= m_max from the pool.  Each decision reads a
+    few scores back to the host (eagle3_tree_confidence) and runs the
+    library's host-side rules on the warm-up table.
+
+    Buffers are sized for k = 8, D_max and m_max; a call with k = 4 or a
+    smaller m uses their leading elements (the library reads and writes
+    them as packed [B][rows][k] / [B][m+1] arrays)."""
+
+    def __init__(self, drafter: Drafter, batch, commit_rows, D_max, m_max, cap_rows, table, params: HarnessParams,
+                 device="cuda"):
+        self.dr, self.table, self.p = drafter, table, params
+        self.Bn, self.n, self.D, self.m_max = batch, commit_rows, D_max, m_max
+        self.buf = CycleBuffers(drafter, CycleSpec(batch, commit_rows, 8, D_max, m_max, cap_rows), device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.root_ids4 = torch.empty(batch, 1, 4, **i32)
+        self.root_lp4 = torch.empty(batch, 1, 4, dtype=torch.float32, device=device)
+        self.front = torch.empty(batch * 8, dtype=torch.float32, device=device)
+        self.pool = torch.empty(batch * m_max, dtype=torch.float32, device=device)
+        self.decisions = None
+
+    def tree(self, m):
+        b = self.buf
+        M1 = m + 1
+        flat = lambda t: t.view(-1)[: self.Bn * M1].view(self.Bn, M1)
+        return dict(tok=flat(b.v_tok), parent=flat(b.v_parent), depth=flat(b.v_depth), pos=flat(b.v_pos),
+                    anc=flat(b.v_anc))
+
+    def run(self, kv: KVCache, feats, tokens, commit_pos, ctx_after, root_tok, root_pos, ctx_for_cost):
+        """Enqueue and decide one cycle; returns dict(k=, rounds=, m=) and
+        leaves the verify tree in tree(m)."""
+        dr, buf, Bn, n, D = self.dr, self.buf, self.Bn, self.n, self.D
+        B.eagle3_fuse(dr.dims, dr.weights, feats, Bn * n, buf.g, buf.ws)
+        kv_commit = kv.struct()
+        kv_tree = kv.struct(ctx_after)
+        draft_step(dr, buf, kv_commit, B.COMMIT, Bn, n, buf.g, None, tokens, commit_pos, None, 0, 8, B.TOPK_LAST,
+                   buf.root_ids, buf.root_lp, buf.commit_logits, buf.commit_cand)
+        lp8 = buf.root_lp.view(Bn, 8).cpu().numpy()
+        k = B.harness_branch_cap(self.table, Bn, ctx_for_cost, lp8, self.p.tau_branch)
+        ids, lp = buf.root_ids, buf.root_lp
+        if k == 4:
+            self.root_ids4.copy_(buf.root_ids[:, :, :4])
+            self.root_lp4.copy_(buf.root_lp[:, :, :4])
+            ids, lp = self.root_ids4, self.root_lp4
+        B.eagle3_tree_expand(B.INIT, Bn, k, D, self.m_max, root_tok, root_pos, buf.tree_state, ids, lp,
+                             buf.next_tok[0] if D > 1 else buf.v_tok, buf.next_par[0] if D > 1 else buf.v_tok,
+                             buf.next_pos[0] if D > 1 else buf.v_tok, buf.next_anc[0] if D > 1 else buf.v_anc)
+        rounds = 1
+        for j in range(2, D + 1):
+            B.eagle3_tree_confidence(Bn, k, D, 0, buf.tree_state, self.front, None)
+            front = self.front[: Bn * k].view(Bn, k).cpu().numpy()
+            if not B.harness_continue(self.table, Bn, ctx_for_cost, k, j - 1, front, self.p.tau_depth, self.p.alpha):
+                break
+            r = j - 2
+            draft_step(dr, buf, kv_tree, B.TREE, Bn, k, None, buf.next_par[r], buf.next_tok[r], buf.next_pos[r],
+                       buf.next_anc[r], r * k, k, B.TOPK_ALL, buf.round_ids[r], buf.round_lp[r],
+                       buf.round_logits[r] if buf.round_logits is not None else None, None)
+            nr = r + 1 if j < D else r
+            B.eagle3_tree_expand(B.STEP, Bn, k, D, self.m_max, None, None, buf.tree_state, buf.round_ids[r],
+                                 buf.round_lp[r], buf.next_tok[nr], buf.next_par[nr], buf.next_pos[nr],
+                                 buf.next_anc[nr])
+            rounds += 1
+        pool_n = k + (rounds - 1) * k * k
+        m_cap = min(self.m_max, pool_n)
+        B.eagle3_tree_confidence(Bn, k, D, m_cap, buf.tree_state, None, self.pool)
+        pool = self.pool[: Bn * m_cap].view(Bn, m_cap).cpu().numpy()
+        m = max(B.harness_verify_count(self.table, Bn, ctx_for_cost, pool, self.p.tau_verify), 1)
+        B.eagle3_tree_expand(B.FINAL, Bn, k, D, m, None, None, buf.tree_state, None, None, None, None, None, None,
+                             buf.v_tok, buf.v_parent, buf.v_depth, buf.v_pos, buf.v_anc)
+        self.decisions = dict(k=k, rounds=rounds, m=m)
+        return self.decisions

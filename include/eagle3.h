@@ -109,11 +109,19 @@ typedef struct eagle3_dims {
  *  gate_up [2*ffn, d]        rows 0..ffn-1 gate, ffn..2ffn-1 up
  *  down    [d, ffn]
  *  lm      [vocab, d]        frozen target LM head
- *  norm_*  [d] float32       RMSNorm gains (embedding, state, FFN, output) */
+ *  norm_*  [d] float32       RMSNorm gains (embedding, state, FFN, output)
+ * The EAGLE-3.1 variants that EAGLE-4 keeps (EAGLE-4 blog, the paragraph on
+ * what EAGLE-4 keeps of EAGLE-3.1), each off when its gains are NULL:
+ *  norm_fc         FC norm: g = rms(fc . [f_low|f_mid|f_high]) * norm_fc
+ *  norm_post_attn, norm_post_ffn  post-norm (both or neither): h1 =
+ *                  rms(s + o.a) * norm_post_attn; the FFN reads h1 itself
+ *                  (norm_ffn unused); h2 = rms(h1 + down.(...)) *
+ *                  norm_post_ffn, which children receive as their state. */
 typedef struct eagle3_weights {
   const void *fc, *emb, *qkv, *o, *gate_up, *down, *lm;
   const float *norm_e, *norm_s, *norm_ffn, *norm_out;
   int32_t layout; /* EAGLE3_LAYOUT_ROWMAJOR or EAGLE3_LAYOUT_PACKED */
+  const float *norm_fc, *norm_post_attn, *norm_post_ffn;
 } eagle3_weights;
 
 /* Draft KV cache of a batch of requests (device, dtype of dims).
@@ -346,13 +354,75 @@ int eagle3_verify_noalloc(int B, int m, int V, int Dmax, const int32_t *v_tok, c
  * 128 or 64, d and ffn multiples of 64, d <= 8192, S a multiple of 64
  * (EAGLE3_EUNSUPPORTED otherwise); token ids must lie in [0, vocab).
  * Precision: bf16 operands, fp32 accumulation; the attention probabilities
- * enter P.V as a bf16 hi + lo pair; log-sum-exp merged in fp64.
+ * enter P.V as a bf16 hi + lo pair; log-sum-exp merged in fp64.  The
+ * EAGLE-3.1 norm variants (norm_fc, post-norm) are not supported here
+ * (EAGLE3_EUNSUPPORTED).
  * ws: eagle3_ttt_workspace_size bytes, no initialisation needed.  All
  * outputs are written with fixed reduction orders (bit-reproducible). */
 int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const void *feats,
                        const int32_t *tokens, int B, int S, int R, const int32_t *forced_tokens,
                        int32_t *pred, float *ce, float *loss, void *ws, size_t ws_bytes,
                        eagle3_stream_t stream);
+
+/* ---- EAGLE-4 Harness: cost-aware tree control ----------------------------
+ * (EAGLE-4 blog, the EAGLE-Harness paragraph: a warm-up measures draft and
+ * verify times over batch sizes, context lengths and token counts into a
+ * lookup table; every round asks, in three places, whether the expected
+ * extra accepted tokens per extra unit of time exceed a threshold: one more
+ * draft layer, how many tokens to verify, and the branch cap per node, 8 at
+ * light load and 4 at heavy load.  The section on converging trends: the
+ * confidence is the product of draft probabilities, compensated by a
+ * threshold that rises with depth.)
+ *
+ * The rules are host code; their inputs are a few scores per request
+ * (eagle3_tree_confidence copies them out of the tree state, or the top-k
+ * log-probs of the root) and the warm-up table.  All arithmetic in double,
+ * sums in index order; confidence c = exp(log-confidence).  Every pointer
+ * of these calls is HOST memory except where stated. */
+#define EAGLE3_COST_DRAFT 0  /* one drafter round: tok rows per request (eagle3_draft_step) */
+#define EAGLE3_COST_VERIFY 1 /* one verification step: tok verify rows per request */
+
+/* Warm-up table: batch[n_batch], ctx[n_ctx], tok[n_tok] ascending measured
+ * values; draft_ms / verify_ms [n_batch][n_ctx][n_tok] milliseconds. */
+typedef struct eagle3_cost_table {
+  int32_t n_batch, n_ctx, n_tok;
+  const int32_t *batch, *ctx, *tok;
+  const float *draft_ms, *verify_ms;
+} eagle3_cost_table;
+
+/* Time of `kind` at (B, ctx, n tokens per request): B and ctx take the
+ * smallest measured value >= them (the largest if none is); n is
+ * interpolated linearly between measured token counts, clamped to the
+ * measured range. */
+int eagle3_harness_cost(const eagle3_cost_table *t, int kind, int B, int ctx, float n, double *ms);
+
+/* One more draft layer?  frontier_logconf [B][k]: the log-confidences of
+ * each request's frontier (eagle3_tree_confidence).  go = 1 iff
+ *   sum_b sum_j c_bj / T_draft(B, ctx, k) > tau0 * (1 + alpha * depth)
+ * (or the round's time is not positive); depth = the frontier's depth. */
+int eagle3_harness_continue(const eagle3_cost_table *t, int B, int ctx, int k, int depth,
+                            const float *frontier_logconf, double tau0, double alpha, int *go);
+
+/* How many drafted tokens to verify: logconf_sorted [B][m_max], each
+ * request's pool log-confidences in rerank order (descending).  Rank i is
+ * kept while sum_b c_b,i / (T_verify(B, ctx, i+2) - T_verify(B, ctx, i+1))
+ * > tau (a rank whose extra time is not positive is kept); m = the number
+ * of leading ranks kept, 0..m_max. */
+int eagle3_harness_verify_count(const eagle3_cost_table *t, int B, int ctx, int m_max, const float *logconf_sorted,
+                                double tau, int *m);
+
+/* Branch cap: root_lp [B][8], the root's top-8 log-probs (draft step with
+ * k = 8).  k = 8 iff sum_b sum_{i=4..7} exp(root_lp[b][i]) /
+ * (T_draft(B, ctx, 8) - T_draft(B, ctx, 4)) > tau (or the extra time is
+ * not positive), else 4. */
+int eagle3_harness_branch_cap(const eagle3_cost_table *t, int B, int ctx, const float *root_lp, double tau, int *k);
+
+/* The harness's inputs from the tree state (DEVICE pointers, enqueued on
+ * `stream`): frontier_logconf [B][k], the current frontier's scores in
+ * frontier-rank order; pool_logconf [B][m_max], the pool's scores in
+ * rerank order (descending), -inf past the pool.  Either may be NULL. */
+int eagle3_tree_confidence(int B, int k, int D, int m_max, const void *tree_state, float *frontier_logconf,
+                           float *pool_logconf, eagle3_stream_t stream);
 
 /* ---- the target's verification forward ---------------------------------
  * ("EAGLE-3 精读" §2 and §5: drafting ends in strict verification by the

@@ -200,7 +200,7 @@ def oracle_on_gpu_rows(w, W, ci, b, gc, isolate=True):
     K = np.zeros((N, s.n_kv_heads, s.head_dim))
     V = np.zeros((N, s.n_kv_heads, s.head_dim))
     K[:cap], V[:cap] = Kc, Vc
-    g = O.fuse(s, ci.feats.f32()[b * n:(b + 1) * n], W["fc"])
+    g = O.fuse(s, ci.feats.f32()[b * n:(b + 1) * n], W["fc"], W.get("norm_fc"))
     g_in = gc.buf.g.float().cpu().numpy()[b * n:(b + 1) * n].astype(np.float64) if isolate else g
     L0 = int(ci.ctx_len[b])
     vis = np.zeros((n, N), bool)

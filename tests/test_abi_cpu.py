@@ -272,3 +272,64 @@ def test_target_forward_argument_checks(blib):
                                         ctypes.byref(blib.TargetLayer()), None) == blib.EWORKSPACE
     f32 = blib.dims_of(TINY_SHAPE)
     assert lib.eagle3_target_layer_packed_size(ctypes.byref(f32), ctypes.byref(sz)) == blib.EUNSUPPORTED
+
+
+def test_harness_rules_native_equal_oracle(blib):
+    """The library's EAGLE-4 Harness rules (host code) take the oracle's
+    decisions on random cost tables and confidences."""
+    import numpy as np
+
+    from oracle import eagle3_oracle as O
+    rng = np.random.default_rng(17)
+    agree = {"cost": 0, "continue": 0, "verify": 0, "branch": 0}
+    for trial in range(60):
+        nb, nc, nt = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(2, 7))
+        batch = np.sort(rng.choice(np.arange(1, 129), nb, replace=False))
+        ctx = np.sort(rng.choice(np.arange(64, 8193), nc, replace=False))
+        tok = np.sort(rng.choice(np.arange(1, 65), nt, replace=False))
+        base = rng.uniform(0.05, 2.0, size=(nb, nc, 1))
+        draft = (base + np.cumsum(rng.uniform(0.0, 0.3, size=(nb, nc, nt)), axis=2)).astype(np.float32)
+        verify = (2 * base + np.cumsum(rng.uniform(0.0, 0.5, size=(nb, nc, nt)), axis=2)).astype(np.float32)
+        if trial % 5 == 0:   # a flat stretch: zero extra time
+            verify[..., -1] = verify[..., -2]
+        t = blib.HarnessTable(batch, ctx, tok, draft, verify)
+        td = t.as_dict()
+        B = int(rng.integers(1, 9))
+        c = int(rng.integers(1, 9000))
+        for kind in (0, 1):
+            n = float(rng.uniform(0, 70))
+            assert blib.harness_cost(t, kind, B, c, n) == pytest.approx(O.harness_cost(td, kind, B, c, np.float32(n)),
+                                                                          rel=1e-12, abs=1e-12)
+            agree["cost"] += 1
+        k = int(rng.integers(1, 9))
+        front = np.log(rng.uniform(1e-4, 1.0, size=(B, k))).astype(np.float32)
+        tau0, alpha, depth = float(rng.uniform(0, 3)), float(rng.uniform(0, 1)), int(rng.integers(1, 6))
+        want, _ = O.harness_continue(td, B, c, k, depth, front, tau0, alpha)
+        assert blib.harness_continue(t, B, c, k, depth, front, tau0, alpha) == want
+        agree["continue"] += 1
+        m_max = int(rng.integers(1, 40))
+        lc = -np.sort(-np.log(rng.uniform(1e-4, 1.0, size=(B, m_max))), axis=1).astype(np.float32)
+        tau = float(rng.uniform(0, 5))
+        assert blib.harness_verify_count(t, B, c, lc, tau) == O.harness_verify_count(td, B, c, lc, tau)
+        agree["verify"] += 1
+        lp = np.sort(np.log(rng.dirichlet(np.ones(8) * 0.5, size=B)), axis=1)[:, ::-1].astype(np.float32)
+        tau = float(rng.uniform(0, 2))
+        assert blib.harness_branch_cap(t, B, c, lp, tau) == O.harness_branch_cap(td, B, c, lp, tau)
+        agree["branch"] += 1
+    assert all(v >= 60 for v in agree.values())
+
+
+def test_harness_argument_checks(blib):
+    import numpy as np
+    lib = blib.load()
+    t = blib.HarnessTable([1, 8], [512], [1, 4], np.ones((2, 1, 2)), np.ones((2, 1, 2)))
+    ms = ctypes.c_double(0)
+    assert lib.eagle3_harness_cost(ctypes.byref(t.struct), 2, 1, 1, ctypes.c_float(1.0), ctypes.byref(ms)) == blib.EINVAL
+    bad = blib.HarnessTable([8, 1], [512], [1, 4], np.ones((2, 1, 2)), np.ones((2, 1, 2)))   # not ascending
+    assert lib.eagle3_harness_cost(ctypes.byref(bad.struct), 0, 1, 1, ctypes.c_float(1.0), ctypes.byref(ms)) == blib.EINVAL
+    assert lib.eagle3_harness_cost(None, 0, 1, 1, ctypes.c_float(1.0), ctypes.byref(ms)) == blib.EINVAL
+    go = ctypes.c_int(0)
+    assert lib.eagle3_harness_continue(ctypes.byref(t.struct), 0, 1, 4, 1, _P, ctypes.c_double(1.0),
+                                       ctypes.c_double(0.0), ctypes.byref(go)) == blib.EINVAL
+    assert lib.eagle3_tree_confidence(1, 17, 2, 4, _P, _P, None, None) == blib.ECAPACITY
+    assert lib.eagle3_tree_confidence(1, 4, 2, 4, None, _P, None, None) == blib.EINVAL

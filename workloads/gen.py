@@ -205,6 +205,19 @@ def target_kv_cuda(shape: DrafterShape, n_layers: int, rows_per_layer_shape, see
     return k, v
 
 
+def gen_norm_variant_gains(shape: DrafterShape, fc_norm: bool, post_norm: bool, seed: int = 0) -> dict:
+    """Gains of the EAGLE-3.1 norm variants, 1 + 0.5 N(0,1) each (a distinct
+    vector per norm): norm_fc for the FC norm, norm_post_attn and
+    norm_post_ffn for the post-norm."""
+    g = _rng(seed, 48)
+    out = {}
+    for name, on in (("norm_fc", fc_norm), ("norm_post_attn", post_norm), ("norm_post_ffn", post_norm)):
+        v = (1.0 + 0.5 * g.standard_normal(shape.d)).astype(np.float32)
+        if on:
+            out[name] = v
+    return out
+
+
 def gen_lowrank_head(shape: DrafterShape, rank: int, energy: float = 0.9, seed: int = 0,
                      std: float = 0.02) -> dict:
     """A synthetic LM head with a low-rank part, and that part's factors.
