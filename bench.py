@@ -662,6 +662,173 @@ def target_bench(w, Wt, steps, warmup):
     return res, ti
 
 
+def harness_bench(w, Wt, cycles, warmup, params=None):
+    """The 8B tree under the EAGLE-4 Harness.  Warm-up (the rules' cost
+    table): one TREE draft round of the drafter at 1..16 rows per request,
+    and one verification step of the 8B target (32 layers, forward +
+    greedy verify) at 2..64 rows, each timed with HIP events.  Then harness
+    cycles (HarnessCycle: branch cap from the root's top-8, the depth rule
+    before each round, the verify count from the pool), timed on the host
+    clock around each cycle (the decisions read scores back, so a cycle is
+    synchronous), next to plain cycles (k 10, 6 rounds, 60 nodes) on the
+    same drafter.  Returns the measurement dict and the table."""
+    import numpy as np
+    import torch
+
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.cycle import (CycleBuffers, CycleSpec, Drafter, HarnessCycle, HarnessParams, KVCache,
+                                            run_cycle)
+    from eagle_draft_tree_amd.target import TargetCache, TargetWeights, VerifyForward
+    from workloads import gen
+
+    s = w.shape
+    params = params or HarnessParams(tau_depth=1.0, alpha=0.25, tau_verify=4.0, tau_branch=2.0)
+    Wh = dict(Wt)
+    Wh["norm_out"] = np.full(s.d, 5.0, np.float32)
+    dr = Drafter(s, Wh, pack=True)
+    ci = gen.gen_cycle_inputs(w, seed=1)
+    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ctx = int(ci.ctx_len[0]) + 1
+    # ---- warm-up: drafter rounds
+    buf = CycleBuffers(dr, CycleSpec(1, 64, 16, 2, 16, ci.cap))
+    tk = torch.zeros(1, Bd.MAX_TREE_SLOTS, s.n_kv_heads, s.head_dim, dtype=dr.torch_dtype, device="cuda")
+    kv = KVCache(ci.kv_k.torch("cuda"), ci.kv_v.torch("cuda"), tk, torch.zeros_like(tk), i32(ci.ctx_len), cap=ci.cap)
+    kvs = kv.struct(i32(ci.ctx_len + 1))
+    toks = [1, 2, 4, 8, 16, 32, 64]   # rows per request, one grid for both tables
+    # the rows' parent state (the root slot): N(0,1), so the timed rounds see
+    # ordinary logits (an all-zero state would tie every logit)
+    buf.h_tree.normal_(0.0, 1.0, generator=torch.Generator(device="cuda").manual_seed(11))
+    draft_ms = []
+    for n in toks:
+        par = torch.zeros(1, n, dtype=torch.int32, device="cuda")
+        tok = i32(np.arange(n)[None] + 100)
+        pos = i32(np.full((1, n), ctx))
+        anc = torch.as_tensor((np.uint64(1) << np.arange(n, dtype=np.uint64)).view(np.int64)[None]).cuda()
+        ids = torch.empty(1, n, min(n, 16), dtype=torch.int32, device="cuda")
+        lps = torch.empty(1, n, min(n, 16), dtype=torch.float32, device="cuda")
+        call = lambda: Bd.eagle3_draft_step(dr.dims, dr.weights, kvs, Bd.TREE, 1, n, None, par, tok, pos, anc, 0,
+                                            min(n, 16), Bd.TOPK_ALL, buf.h_tree, ids, lps, None, buf.ws)
+        for _ in range(3):
+            call()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(20):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        draft_ms.append(a.elapsed_time(b) / 20)
+    # ---- warm-up: target verification steps
+    tm = w.target
+    L = tm.n_layers
+    layers = gen.target_weights_cuda(s, L, seed=0)
+    tw = TargetWeights(s, layers, Wt["emb"], Wt["lm"], np.ones(s.d, np.float32), tm.feat_layers, pack=True)
+    del layers
+    cap = ctx + 64
+    k_, v_ = gen.target_kv_cuda(s, L, (1, cap), seed=0)
+    cache = TargetCache(s, L, 1, cap, torch.bfloat16, k=k_, v=v_)
+    cache.ctx_len.fill_(ctx - 1)
+    verify_ms = []
+    for n in toks:
+        vf = VerifyForward(tw, cache, n)
+        par = np.arange(-1, n - 1, dtype=np.int32)[None]
+        tok, pos = i32(np.arange(n)[None] + 7), i32(ctx - 1 + np.arange(n)[None])
+        anc = torch.as_tensor(gen.ancestor_bits(par[0]).view(np.int64)[None]).cuda()
+        vpar = i32(par)
+        al, acc = torch.zeros(1, dtype=torch.int32, device="cuda"), torch.zeros(1, n, dtype=torch.int32, device="cuda")
+        bo, stt = torch.zeros(1, dtype=torch.int32, device="cuda"), torch.zeros(1, dtype=torch.int32, device="cuda")
+        vws = torch.zeros(Bd.verify_workspace_size(1, n - 1, s.vocab), dtype=torch.uint8, device="cuda")
+
+        def vstep():
+            vf.run(tok, pos, anc)
+            Bd.eagle3_verify(1, n - 1, s.vocab, n, tok, vpar, vf.logits, Bd.GREEDY, 1.0, None, None, al, acc, bo, stt,
+                             vws)
+        for _ in range(2):
+            vstep()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(5):
+            vstep()
+        b.record()
+        torch.cuda.synchronize()
+        verify_ms.append(a.elapsed_time(b) / 5)
+        del vf
+    del tw, cache
+    torch.cuda.empty_cache()
+    table = Bd.HarnessTable([1], [ctx], toks, [[draft_ms]], [[verify_ms]])
+    # ---- harness cycles and plain cycles on the same drafter and inputs
+    hc = HarnessCycle(dr, 1, 1, w.depth, w.keep, ci.cap, table, params)
+    x = dict(kv=kv, feats=ci.feats.torch("cuda"), tokens=i32(ci.tokens), commit_pos=i32(ci.ctx_len[:, None]),
+             ctx_after=i32(ci.ctx_len + 1), root_tok=i32(ci.tokens[:, -1]), root_pos=i32(ci.ctx_len))
+    for _ in range(warmup):
+        hc.run(x["kv"], x["feats"], x["tokens"], x["commit_pos"], x["ctx_after"], x["root_tok"], x["root_pos"], ctx)
+    torch.cuda.synchronize()
+    t_h, decs = [], []
+    for _ in range(cycles):
+        t0 = time.perf_counter()
+        decs.append(dict(hc.run(x["kv"], x["feats"], x["tokens"], x["commit_pos"], x["ctx_after"], x["root_tok"],
+                                x["root_pos"], ctx)))
+        torch.cuda.synchronize()
+        t_h.append((time.perf_counter() - t0) * 1e3)
+    d0 = decs[-1]
+    pool = hc.pool[: min(w.keep, d0["k"] + (d0["rounds"] - 1) * d0["k"] ** 2)].cpu().numpy()
+    exp_tokens = float(np.exp(pool[: d0["m"]].astype(np.float64)).sum())
+    pbuf = CycleBuffers(dr, CycleSpec(1, 1, w.topk, w.depth, w.keep, ci.cap))
+    for _ in range(warmup):
+        run_cycle(dr, pbuf, kv, x["feats"], x["tokens"], x["commit_pos"], x["ctx_after"], x["root_tok"],
+                  x["root_pos"], verify=False)
+    torch.cuda.synchronize()
+    t_p = []
+    for _ in range(cycles):
+        t0 = time.perf_counter()
+        run_cycle(dr, pbuf, kv, x["feats"], x["tokens"], x["commit_pos"], x["ctx_after"], x["root_tok"],
+                  x["root_pos"], verify=False)
+        torch.cuda.synchronize()
+        t_p.append((time.perf_counter() - t0) * 1e3)
+    vt = lambda m: Bd.harness_cost(table, Bd.COST_VERIFY, 1, ctx, m + 1)
+    med = lambda a: float(np.median(a))
+    res = {
+        "workload": w.name,
+        "params": dict(tau_depth=params.tau_depth, alpha=params.alpha, tau_verify=params.tau_verify,
+                       tau_branch=params.tau_branch),
+        "warmup_table": {"rows_per_request": toks, "draft_round_ms": [round(v, 4) for v in draft_ms],
+                         "verification_step_ms": [round(v, 4) for v in verify_ms]},
+        "decisions": d0,
+        "decisions_constant": all(dd == d0 for dd in decs),
+        "harness_cycle_ms_median": round(med(t_h), 4),
+        "plain_cycle_ms_median": round(med(t_p), 4),
+        "verify_ms_at_m_from_table": round(vt(d0["m"]), 4),
+        "plain_verify_ms_from_table": round(vt(w.keep), 4),
+        "expected_accepted_tokens_verified": round(exp_tokens, 3),
+        "note": "host-clock time per cycle including the decisions' read-backs (harness) / eager launches (plain), "
+                "drafting only; verification times are the warm-up table's at the verified row counts",
+    }
+    return res, table
+
+
+def cpu_baseline_harness(w, Wt, table, params, ci=None):
+    """The oracle's harness_cycle (the same rules and table, fp64 NumPy
+    decoder) for request 0, timed on the host cores."""
+    import numpy as np
+
+    from oracle import eagle3_oracle as O
+    from workloads import gen
+    threads, desc = _host_info()
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    W["norm_out"] = np.full(w.shape.d, 5.0)
+    ci = ci or gen.gen_cycle_inputs(w, seed=1)
+    t0 = time.time()
+    _, info = O.harness_cycle(w.shape, W, ci.feats.f32()[:1], ci.tokens[0], ci.kv_k.f32()[0].astype(np.float64),
+                              ci.kv_v.f32()[0].astype(np.float64), int(ci.ctx_len[0]), table.as_dict(), w.keep,
+                              w.depth, params["tau_depth"], params["alpha"], params["tau_verify"],
+                              params["tau_branch"])
+    dt = time.time() - t0
+    return {"value": 1.0 / dt, "unit": "harness cycles/s", "cores": threads, "kind": "oracle",
+            "decisions": info,
+            "sample": f"one harness cycle of request 0 (fuse + commit + {info['rounds'] - 1} tree rounds + rules + "
+                      f"rerank), fp64 NumPy, {dt:.1f} s; {desc}"}
+
+
 def cpu_baseline_target(w, Wt, ti):
     """The oracle's verification forward on a bounded sample: request 0's
     m+1 verify rows through one target layer (host-drawn weights of the
@@ -703,7 +870,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e", "c2v", "c3v", "c4v"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e", "c2v", "c3v", "c4v", "c2n", "c2h"],
+                    default=None,
                     help="run one workload only (profiling); the main line is then that workload's")
     ap.add_argument("--main-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
@@ -729,9 +897,28 @@ def main():
     from eagle_draft_tree_amd import binding as Bd
     from eagle_draft_tree_amd.cycle import Drafter
     from workloads import gen
-    from workloads.configs import (C2_8B_TREE, C2E_8B_TREE_LOWRANK, C2V_8B_TARGET_TREE, C3_8B_CHAIN,
-                                   C3V_8B_TARGET_CHAIN, C4_70B_TREE, C4E_70B_TREE_LOWRANK, C4V_70B_TARGET_TREE,
-                                   C5_8B_TTT)
+    from workloads.configs import (C2_8B_TREE, C2E_8B_TREE_LOWRANK, C2H_8B_TREE_HARNESS, C2N_8B_TREE_NORMS,
+                                   C2V_8B_TARGET_TREE, C3_8B_CHAIN, C3V_8B_TARGET_CHAIN, C4_70B_TREE,
+                                   C4E_70B_TREE_LOWRANK, C4V_70B_TARGET_TREE, C5_8B_TTT)
+
+    if args.only == "c2h":
+        w = C2H_8B_TREE_HARNESS
+        Wt = gen.gen_weights(w.shape, seed=0)
+        r, table = harness_bench(w, Wt, max(3, min(args.steps, 30)), min(args.warmup, 3))
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline_harness(w, Wt, table, r["params"])
+        print(json.dumps(r), flush=True)
+        return
+    if args.only == "c2n":
+        w = C2N_8B_TREE_NORMS
+        Wt = gen.gen_weights(w.shape, seed=0)
+        Wt.update(gen.gen_norm_variant_gains(w.shape, True, True, seed=1))
+        dr = Drafter(w.shape, Wt, pack=True)
+        r, ci, vin = cycle_bench(w, dr, args.steps, args.warmup, graph=not args.no_graph)
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline(w, Wt, ci, vin)
+        print(json.dumps(r), flush=True)
+        return
 
     if args.only in ("c2v", "c3v", "c4v"):
         w = {"c2v": C2V_8B_TARGET_TREE, "c3v": C3V_8B_TARGET_CHAIN, "c4v": C4V_70B_TARGET_TREE}[args.only]
@@ -846,11 +1033,30 @@ def main():
             rv, tiv = target_bench(wv, Wt, max(args.steps // 5, 2), min(args.warmup, 3))
             wl[wv.name] = rv
             cpu_jobs.append((wv.name, wv, Wt, tiv, None, None, None))
+        del Wt70
+        # the EAGLE-3.1 norm variants on the 8B tree
+        wn = C2N_8B_TREE_NORMS
+        WtN = dict(Wt8)
+        WtN.update(gen.gen_norm_variant_gains(wn.shape, True, True, seed=1))
+        drn = Drafter(wn.shape, WtN, pack=True)
+        rn, cin, vinn = cycle_bench(wn, drn, args.steps, args.warmup, graph=not args.no_graph)
+        wl[wn.name] = rn
+        cpu_jobs.append((wn.name, wn, WtN, cin, vinn, None, None))
+        del drn
+        torch.cuda.empty_cache()
+        # the EAGLE-4 Harness on the 8B tree (warm-up table, then harness cycles)
+        wh = C2H_8B_TREE_HARNESS
+        rh, table_h = harness_bench(wh, Wt8, max(args.steps // 5, 3), min(args.warmup, 3))
+        wl[wh.name] = rh
+        cpu_jobs.append((wh.name, wh, Wt8, table_h, rh["params"], "harness", None))
+        torch.cuda.empty_cache()
         out["workloads"] = wl
     if not args.no_cpu_baseline:
         for name, wk, Wt, inp, vi, reqs, hd in cpu_jobs:
             print(f"cpu baseline: {wk.name}", file=sys.stderr, flush=True)
-            if wk.target is not None:
+            if reqs == "harness":
+                cb = cpu_baseline_harness(wk, Wt, inp, vi)
+            elif wk.target is not None:
                 cb = cpu_baseline_target(wk, Wt, inp)
             elif wk.ttt_seq:
                 cb = cpu_baseline_ttt(wk, Wt, inp)

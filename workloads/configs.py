@@ -141,6 +141,17 @@ C3V_8B_TARGET_CHAIN = replace(C3_8B_CHAIN, name="llama3.1-8b-target32-b64-chain4
 C4V_70B_TARGET_TREE = replace(C4_70B_TREE, name="llama3.3-70b-target80-b1-tree61rows-ctx4096", target=L70B_TARGET)
 
 
+# The 8B tree with the EAGLE-3.1 norm variants EAGLE-4 keeps (FC norm and
+# post-norm; gains 1 + 0.5 N(0,1)).
+C2N_8B_TREE_NORMS = replace(C2_8B_TREE, name="llama3.1-8b-drafter-b1-tree6x10-keep60-fcnorm-postnorm")
+
+# The 8B tree under the EAGLE-4 Harness (branch cap 8/4, up to 6 rounds, up
+# to 60 verified nodes) with a warm-up table measured on the 8B drafter and
+# the 8B target.  The drafter's final-norm gain is 5 (logit spread about 6.4
+# instead of 1.3), so that draft confidences span the range the rules act on.
+C2H_8B_TREE_HARNESS = replace(C2_8B_TREE, name="llama3.1-8b-drafter-b1-harness-d6-m60-target32", target=L8B_TARGET)
+
+
 def tiny_shape(d=16, hq=2, hkv=1, hd=8, ffn=32, vocab=8, dtype=F32, theta=10000.0, name=None):
     """Very small drafters for exhaustive oracle checks."""
     return DrafterShape(name or f"micro-d{d}-v{vocab}-{dtype}", d=d, n_q_heads=hq,
