@@ -218,6 +218,14 @@ def gen_norm_variant_gains(shape: DrafterShape, fc_norm: bool, post_norm: bool, 
     return out
 
 
+def gen_drafter_gains(shape: DrafterShape, seed: int = 0) -> dict:
+    """Non-unit RMSNorm gains of the drafter, 1 + 0.5 N(0,1) each (a distinct
+    vector per norm): norm_e, norm_s, norm_ffn, norm_out."""
+    g = _rng(seed, 47)
+    return {name: (1.0 + 0.5 * g.standard_normal(shape.d)).astype(np.float32)
+            for name in ("norm_e", "norm_s", "norm_ffn", "norm_out")}
+
+
 def gen_lowrank_head(shape: DrafterShape, rank: int, energy: float = 0.9, seed: int = 0,
                      std: float = 0.02) -> dict:
     """A synthetic LM head with a low-rank part, and that part's factors.
