@@ -33,6 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10,
           lr_scores=14)
 KC_TTT = dict(rowops=1, ttt_gemm=11, ttt_attn=12, ttt_ce=13)
+KC_TTT_TRAIN = dict(KC_TTT, ttt_bwd_gemm=18, ttt_bwd_attn=19, ttt_wgrad=20, ttt_bwd_rows=21)
 
 
 # sources that build each workload's dominant kernel (a traffic record is
@@ -41,7 +42,8 @@ KERNEL_SOURCES = {
     "rows_gemm": ("gemm_rows.hpp", "layer_ops.hpp", "draft.hip", "common.hpp"),
     "rows_rx": ("rows_rx.hpp", "rows_dma.hpp", "layer_ops.hpp", "draft.hip", "common.hpp"),
     "lr_scores": ("lowrank.hip", "draft.hip", "common.hpp"),
-    "ttt_ce": ("bigemm.hpp", "ttt.hip", "common.hpp"),
+    "ttt_ce": ("bigemm.hpp", "ttt.hip", "ttt_common.hpp", "common.hpp"),
+    "ttt_dy": ("bigemm.hpp", "ttt.hip", "ttt_common.hpp", "common.hpp"),
     "target_gate_up": ("gemm_rows.hpp", "rows_dma.hpp", "layer_ops.hpp", "target.hip", "common.hpp"),
 }
 
@@ -535,6 +537,126 @@ def ttt_bench(w, dr, steps, warmup):
     }, ti
 
 
+def ttt_flops(w):
+    """Algorithmic flops of one TTT forward: (projection GEMMs, LM head, attention)."""
+    s = w.shape
+    B, S, R = w.batch, w.ttt_seq, w.ttt_steps
+    M = B * S
+    d, F, V, hq, hkv, hd = s.d, s.ffn, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim
+    qd, kvd = hq * hd, hkv * hd
+    f_fc = 2.0 * M * d * 3 * d
+    f_layer = R * (2.0 * M * 2 * d * (qd + 2 * kvd) + 2.0 * M * qd * d + 2.0 * M * d * 2 * F + 2.0 * M * F * d)
+    f_lm = R * 2.0 * M * d * V
+    keys = B * S * (S + 1) / 2.0
+    f_attn = sum(4.0 * (keys + M * (j - 1)) * hq * hd for j in range(1, R + 1))
+    return f_fc, f_layer, f_lm, f_attn
+
+
+def ttt_train_bench(w, dr, steps, warmup):
+    """Time one TTT training step: the forward keeping every step's
+    activations plus the backward to every trained parameter's gradient
+    (eagle3_ttt_train), B x S tokens, R rollout steps."""
+    import torch
+
+    from eagle_draft_tree_amd import binding as Bd
+    from eagle_draft_tree_amd.train import TTTTrain
+    from workloads import gen
+
+    s = w.shape
+    B, S, R = w.batch, w.ttt_seq, w.ttt_steps
+    ti = gen.gen_ttt_inputs(s, B, S, R, seed=1)
+    feats = ti.feats.torch("cuda")
+    tokens = torch.as_tensor(ti.tokens).cuda()
+    tr = TTTTrain(dr, B, S, R)
+
+    def run():
+        tr.run(feats, tokens)
+
+    for _ in range(max(warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    for c in KC_TTT_TRAIN.values():
+        Bd.timing_enable(c, 256 * (steps + 1))
+    # principal kernels: the dy GEMM (dlogits . W_lm) and the weight-gradient GEMMs
+    Bd.timing_mode(KC_TTT_TRAIN["ttt_bwd_gemm"], 1)
+    Bd.timing_mode(KC_TTT_TRAIN["ttt_wgrad"], 1)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    per_class = {}
+    for name, c in KC_TTT_TRAIN.items():
+        per_class[name] = Bd.timing_read(c)
+        Bd.timing_enable(c, 0)
+        Bd.timing_mode(c, 0)
+    M = B * S
+    f_fc, f_layer, f_lm, f_attn = ttt_flops(w)
+    f_fwd = f_fc + f_layer + f_lm + f_attn
+    # backward: dy (LM head, no weight gradient), the layer GEMMs' data and
+    # weight gradients (2 x forward), dW_fc, attention (dP, dQ, dK, dV: 2 x forward)
+    f_bwd = f_lm + 2 * f_layer + f_fc + 2 * f_attn
+    dy_launches = per_class["ttt_bwd_gemm"][1]
+    dy_ms = per_class["ttt_bwd_gemm"][0] / steps
+    dy_tf = f_lm / (dy_ms * 1e-3) / 1e12 if dy_ms > 0 else None
+    wg_ms = per_class["ttt_wgrad"][0] / steps
+    f_wgrad = f_layer + f_fc
+    return {
+        "workload": w.name + "-train",
+        "steps": steps,
+        "ms_per_step": round(ms, 3),
+        "tokens_per_s": round(M / (ms * 1e-3), 1),
+        "rows_per_s": round(M * R / (ms * 1e-3), 1),
+        "loss": round(float(tr.loss.item()), 4),
+        "TFLOPs": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 1),
+        "mfma_frac": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(dy_tf, 1) if dy_tf else None,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dy_tf / MFMA_BF16_PEAK_TFLOPS, 4) if dy_tf else None,
+                     "traffic": load_traffic(w.name + "-train", "ttt_dy"),
+                     "kernel": "dy GEMM (dlogits . W_lm, the LM head's backward)",
+                     "flops_per_launch": f_lm / R,
+                     "avg_launch_us": round(per_class["ttt_bwd_gemm"][0] / dy_launches * 1e3, 1)
+                     if dy_launches else None},
+        "wgrad_TFLOPs": round(f_wgrad / (wg_ms * 1e-3) / 1e12, 1) if wg_ms > 0 else None,
+        "flops_per_step": {"forward": f_fwd, "backward": f_bwd},
+        "workspace_GB": round(tr.ws.numel() / 1e9, 2),
+        "kernel_ms_per_step": {kk: round(v[0] / steps, 3) for kk, v in per_class.items()},
+        "timing_note": "kernel_ms_per_step: ttt_bwd_gemm and ttt_wgrad are their principal kernels' own "
+                       "durations (dy GEMM; the five weight-gradient GEMMs), the other classes event pairs "
+                       "around their launch scopes",
+    }, ti
+
+
+def cpu_baseline_ttt_train(w, Wt, ti, S_sample=128):
+    """The gradient oracle (fp64 autograd over the TTT forward) on a bounded
+    slice: the first S_sample tokens of sequence 0, all R steps, forward and
+    backward, timed on the host cores and scaled to rows per second and to
+    one whole training step (extrapolated)."""
+    import torch
+
+    from oracle import ttt_grad as G
+    W = {k: (v.f32() if hasattr(v, "f32") else v) for k, v in Wt.items()}
+    threads, desc = _host_info()
+    R, B, S = w.ttt_steps, w.batch, w.ttt_seq
+    feats = ti.feats.f32()[:1, :S_sample]
+    toks = ti.tokens[:1, :S_sample]
+    t0 = time.time()
+    G.ttt_loss_and_grads(w.shape, W, feats, toks, R)
+    dt = time.time() - t0
+    rows = S_sample * R
+    rate = rows / dt
+    return {"value": rate, "unit": "TTT rollout rows/s (forward + backward)", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "extrapolated_ms_per_step": round(B * S * R / rate * 1e3, 1),
+            "sample": f"sequence 0, tokens 0..{S_sample - 1} x {R} steps = {rows} rollout rows, loss and the "
+                      f"gradients of every trained parameter, fp64 PyTorch autograd, {dt:.1f} s (includes the "
+                      f"weights' fp64 copies); the per-step time scales this to {B} x {S} x {R} rows "
+                      f"(extrapolated; attention grows with S, so this understates the oracle's cost); {desc}"}
+
+
 def target_bench(w, Wt, steps, warmup):
     """Time the target's verification step of workload w: the forward of
     all target layers over the B x (m+1) verify rows (root + kept nodes)
@@ -870,7 +992,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "c2e", "c4e", "c2v", "c3v", "c4v", "c2n", "c2h"],
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "ttt", "tttb", "c2e", "c4e", "c2v", "c3v", "c4v", "c2n",
+                                       "c2h"],
                     default=None,
                     help="run one workload only (profiling); the main line is then that workload's")
     ap.add_argument("--main-only", action="store_true", help="skip the secondary workloads")
@@ -953,6 +1076,12 @@ def main():
             r["cpu_baseline"] = cpu_baseline_ttt(C5_8B_TTT, Wt8, ti)
         print(json.dumps(r), flush=True)
         return
+    if args.only == "tttb":
+        r, ti = ttt_train_bench(C5_8B_TTT, dr8, max(1, min(args.steps, 5)), 1)
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline_ttt_train(C5_8B_TTT, Wt8, ti)
+        print(json.dumps(r), flush=True)
+        return
     if args.only == "c2":
         args.main_only = True
     if args.only in ("c3", "c4"):
@@ -1003,6 +1132,10 @@ def main():
         r5, ti = ttt_bench(C5_8B_TTT, dr8, 5, 1)
         wl[C5_8B_TTT.name] = r5
         cpu_jobs.append((C5_8B_TTT.name, C5_8B_TTT, Wt8, ti, None, None, None))
+        r5t, ti5t = ttt_train_bench(C5_8B_TTT, dr8, 3, 1)
+        wl[r5t["workload"]] = r5t
+        cpu_jobs.append((r5t["workload"], C5_8B_TTT, Wt8, ti5t, None, "train", None))
+        torch.cuda.empty_cache()
         del dr8
         torch.cuda.empty_cache()
         # the 8B tree through the efficient LM head (same drafter, structured LM head)
@@ -1056,6 +1189,8 @@ def main():
             print(f"cpu baseline: {wk.name}", file=sys.stderr, flush=True)
             if reqs == "harness":
                 cb = cpu_baseline_harness(wk, Wt, inp, vi)
+            elif reqs == "train":
+                cb = cpu_baseline_ttt_train(wk, Wt, inp)
             elif wk.target is not None:
                 cb = cpu_baseline_target(wk, Wt, inp)
             elif wk.ttt_seq:

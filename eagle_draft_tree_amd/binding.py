@@ -41,6 +41,13 @@ class Weights(ctypes.Structure):
                [(n, vp) for n in ("norm_fc", "norm_post_attn", "norm_post_ffn")]
 
 
+GRAD_NAMES = ("fc", "qkv", "o", "gate_up", "down", "norm_e", "norm_s", "norm_ffn", "norm_out")
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, vp) for n in GRAD_NAMES]
+
+
 class KV(ctypes.Structure):
     _fields_ = [("k", vp), ("v", vp), ("cap", ctypes.c_int32), ("block_table", vp),
                 ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
@@ -103,6 +110,8 @@ def load(path: str = LIB_PATH):
         "eagle3_verify_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
         "eagle3_verify_noalloc": ([I, I, I, I, P, P, P, I, ctypes.c_float, P, P, P, P, P, P, P], I),
         "eagle3_ttt_forward": ([P, P, P, P, I, I, I, P, P, P, P, P, SZ, P], I),
+        "eagle3_ttt_train_workspace_size": ([P, I, I, I, ctypes.POINTER(SZ)], I),
+        "eagle3_ttt_train": ([P, P, P, P, I, I, I, P, P, P, P, P, P, SZ, P], I),
         "eagle3_topk": ([P, I, I, I, P, P, P, P, SZ, P], I),
         "eagle3_timing_enable": ([I, I], I),
         "eagle3_packed_weights_size": ([P, ctypes.POINTER(SZ)], I),
@@ -265,6 +274,26 @@ def eagle3_ttt_forward(dims, weights, feats, tokens, B, S, R, forced_tokens, pre
         ptr(pred), ptr(ce), ptr(loss), ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
 
 
+def ttt_train_workspace_size(dims: Dims, B: int, S: int, R: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("eagle3_ttt_train_workspace_size",
+           load().eagle3_ttt_train_workspace_size(ctypes.byref(dims), B, S, R, ctypes.byref(out)))
+    return out.value
+
+
+def grads_struct(grads: dict) -> Grads:
+    """eagle3_grads from a dict of fp32 device tensors keyed by GRAD_NAMES."""
+    return Grads(*(grads[n].data_ptr() for n in GRAD_NAMES))
+
+
+def eagle3_ttt_train(dims, weights, feats, tokens, B, S, R, forced_tokens, pred, ce, loss, grads, ws, stream=None):
+    g = grads_struct(grads)
+    _check("eagle3_ttt_train", load().eagle3_ttt_train(
+        ctypes.byref(dims), ctypes.byref(weights), ptr(feats), ptr(tokens), B, S, R, ptr(forced_tokens),
+        ptr(pred), ptr(ce), ptr(loss), ctypes.byref(g), ptr(ws), ws.numel() * ws.element_size(),
+        stream_ptr(stream)))
+
+
 def eagle3_topk(logits, rows, V, k, ids, lp, lse, ws, stream=None):
     _check("eagle3_topk", load().eagle3_topk(ptr(logits), rows, V, k, ptr(ids), ptr(lp), ptr(lse), ptr(ws),
                                              ws.numel() * ws.element_size(), stream_ptr(stream)))
@@ -382,7 +411,8 @@ def eagle3_tree_confidence(B, k, D, m_max, tree_state, frontier_logconf, pool_lo
 
 # ---------------------------------------------------------------- kernel timing
 KC = dict(fuse=0, rowops=1, qkv=2, attn=3, o=4, gate_up=5, down=6, lm_head=7, topk=8, tree=9, verify=10,
-          ttt_gemm=11, ttt_attn=12, ttt_ce=13, lr_scores=14, target=15, tgt_gate_up=16, tgt_lm_head=17)
+          ttt_gemm=11, ttt_attn=12, ttt_ce=13, lr_scores=14, target=15, tgt_gate_up=16, tgt_lm_head=17,
+          ttt_bwd_gemm=18, ttt_bwd_attn=19, ttt_wgrad=20, ttt_bwd_rows=21)
 
 
 def timing_enable(kc: int, max_launches: int):

@@ -26,7 +26,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 # The tiled GEMM's epilogues walk a fully unrolled 8 x 8 accumulator grid; a
 # higher full-unroll budget keeps the accumulators in registers (no
 # dynamically indexed copy in scratch).
-EXTRA = {"ttt.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+EXTRA = {"ttt.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+         "ttt_bwd.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 
 
 def _compile(src):

@@ -142,6 +142,15 @@ int eagle3_ttt_workspace_size(const eagle3_dims* dims, int B, int S, int R, size
   return ok();
 }
 
+int eagle3_ttt_train_workspace_size(const eagle3_dims* dims, int B, int S, int R, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  REQUIRE(bytes, EAGLE3_EINVAL, "bytes is NULL");
+  REQUIRE(B >= 1 && S >= 1 && R >= 1, EAGLE3_EINVAL, "B/S/R");
+  *bytes = e3::ttt_train_ws_bytes(*dims, B, S, R);
+  return ok();
+}
+
 int eagle3_fuse(const eagle3_dims* dims, const eagle3_weights* w, const void* feats, int n, void* g,
                 void* ws, size_t ws_bytes, eagle3_stream_t stream) {
   int rc = check_dims(dims);
@@ -373,6 +382,34 @@ int eagle3_ttt_forward(const eagle3_dims* dims, const eagle3_weights* w, const v
                        (hipStream_t)stream);
   if (rc == 1) return fail(EAGLE3_EUNSUPPORTED, "TTT forward: shape not supported");
   if (rc < 0) return fail(EAGLE3_EHIP, "eagle3_ttt_forward: HIP launch failed");
+  return ok();
+}
+
+int eagle3_ttt_train(const eagle3_dims* dims, const eagle3_weights* w, const void* feats, const int32_t* tokens,
+                     int B, int S, int R, const int32_t* forced_tokens, int32_t* pred, float* ce, float* loss,
+                     const eagle3_grads* grads, void* ws, size_t ws_bytes, eagle3_stream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  REQUIRE(dims->dtype == EAGLE3_BF16, EAGLE3_EUNSUPPORTED, "TTT needs bf16");
+  REQUIRE(!w->norm_fc && !w->norm_post_attn, EAGLE3_EUNSUPPORTED, "TTT train: no FC-norm / post-norm variant");
+  REQUIRE(feats && tokens && pred && ce && loss && ws && grads, EAGLE3_EINVAL, "a required pointer is NULL");
+  REQUIRE(grads->fc && grads->qkv && grads->o && grads->gate_up && grads->down && grads->norm_e && grads->norm_s &&
+              grads->norm_ffn && grads->norm_out,
+          EAGLE3_EINVAL, "a gradient pointer is NULL");
+  REQUIRE(B >= 1 && S >= 1 && R >= 1, EAGLE3_EINVAL, "B/S/R");
+  REQUIRE(S % 64 == 0, EAGLE3_EUNSUPPORTED, "S=%d must be a multiple of 64", S);
+  REQUIRE(dims->d % 64 == 0 && dims->ffn % 64 == 0 && dims->d <= 8192, EAGLE3_EUNSUPPORTED,
+          "TTT needs d and ffn multiples of 64 and d <= 8192");
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, EAGLE3_EUNSUPPORTED, "TTT train: Hq/Hkv=%d not in {1,2,4,8}", G);
+  REQUIRE(dims->vocab % 16 == 0, EAGLE3_EUNSUPPORTED, "TTT train: vocab %d not a multiple of 16", dims->vocab);
+  const size_t need = e3::ttt_train_ws_bytes(*dims, B, S, R);
+  REQUIRE(ws_bytes >= need, EAGLE3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rc = e3::ttt_train(*dims, *w, feats, tokens, B, S, R, forced_tokens, pred, ce, loss, *grads, ws,
+                     (hipStream_t)stream);
+  if (rc == 1) return fail(EAGLE3_EUNSUPPORTED, "TTT train: shape not supported");
+  if (rc < 0) return fail(EAGLE3_EHIP, "eagle3_ttt_train: HIP launch failed");
   return ok();
 }
 

@@ -22,6 +22,7 @@
 
 #include "common.hpp"
 #include "gemm_rows.hpp"
+#include "timing.hpp"
 
 namespace e3 {
 
@@ -202,6 +203,22 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   EpiHook<Epi>::run(epi, acc, pre, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
 }
 
+// Launch C = A . W^T on `st`.  apack: A in fragment order (frag_off) instead
+// of row-major with stride lda; packed: W in packed fragment order (else
+// row-major through `map`).  kc >= 0: timed as that class's principal kernel.
+template <class Epi>
+inline hipError_t bg_launch(const bf16* A, int lda, bool apack, int M, const void* W, bool packed, int N, int K,
+                            RowMap map, Epi epi, hipStream_t st, int kc = -1) {
+  const int grid = bg_grid(M, N);
+  const bf16* Wb = (const bf16*)W;
+  const dim3 g(grid), b(BG_THREADS);
+  if (packed && apack) launch_timed(kc, big_gemm_kernel<true, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else if (packed) launch_timed(kc, big_gemm_kernel<true, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else if (apack) launch_timed(kc, big_gemm_kernel<false, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  else launch_timed(kc, big_gemm_kernel<false, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
+  return hipGetLastError();
+}
+
 // Lane l receives lane l^8 of its 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float xor8(float v) { return dpp_f<0x128>(v); }
 
@@ -232,8 +249,10 @@ struct BEpiStoreF {
   }
 };
 
-// out = out + C (fp32, plain map): the residual update of the state stream.
-struct BEpiResid {
+// out = in + C (fp32, plain map): the residual update of the state stream
+// (in == out updates it in place).
+struct BEpiAdd {
+  const float* in;
   float* out;
   int ld;
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
@@ -250,8 +269,30 @@ struct BEpiResid {
         for (int e = 0; e < 4; ++e)
           if (row0 + e < M) {
             const size_t o = (size_t)(row0 + e) * ld + col16 * 16 + m;
-            out[o] = out[o] + acc[i][j][e];
+            out[o] = in[o] + acc[i][j][e];
           }
+      }
+    }
+  }
+};
+
+// C (plain map) -> bf16, row-major with stride ldo.
+struct BEpiStoreBF {
+  bf16* out;
+  int ldo;
+  __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
+                                             int nt16) const {
+    const int m = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < BG_NJ; ++j) {
+        const int col16 = colbase16 + j;
+        if (col16 >= nt16) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row0 + e < M) out[(size_t)(row0 + e) * ldo + col16 * 16 + m] = f2bf(acc[i][j][e]);
       }
     }
   }
@@ -259,10 +300,12 @@ struct BEpiResid {
 
 // SwiGLU on MAP_PAIR_FFN tiles: slot m < 8 is gate column 8t+m, slot m+8
 // the matching up column.  z = silu(gate) * up, rounded to bf16, written in
-// fragment order for the down projection's A operand.
+// fragment order for the down projection's A operand; with gu set, the fp32
+// (gate, up) pair is kept as well ([M][ffn], for the backward).
 struct BEpiSwiGLU {
   bf16* z;  // fragment order [M][ffn] (frag_off)
   int ffn;
+  float2* gu = nullptr;
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
     const int m = lane & 15;
@@ -281,6 +324,7 @@ struct BEpiSwiGLU {
             if (row0 + e < M) {
               const float g = acc[i][j][e];
               z[frag_off(row0 + e, col16 * 8 + m, ffn >> 5)] = f2bf(g / (1.f + expf(-g)) * up[e]);
+              if (gu) gu[(size_t)(row0 + e) * ffn + col16 * 8 + m] = make_float2(g, up[e]);
             }
         }
       }

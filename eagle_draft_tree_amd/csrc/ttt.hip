@@ -19,6 +19,7 @@
 #include "bigemm.hpp"
 #include "timing.hpp"
 #include "ttt.hpp"
+#include "ttt_common.hpp"
 
 namespace e3 {
 
@@ -89,48 +90,6 @@ __global__ void rope_table_kernel(float2* tab, int npos, int hd, float theta) {
   const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
   const double ang = (double)p * inv;
   tab[e] = make_float2((float)cos(ang), (float)sin(ang));
-}
-
-__device__ __forceinline__ void unpack8(uint4 u, float* f) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    f[2 * c] = __uint_as_float(w[c] << 16);
-    f[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ uint4 pack8(const float* f) {
-  uint32_t w[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = (uint32_t)f2bf(f[2 * c]) | ((uint32_t)f2bf(f[2 * c + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Row kernels over 16-row blocks (one MFMA m-tile): 256 threads, the 16
-// threads of a DPP row own one matrix row for the sums of squares, then every
-// thread writes whole 16-byte slots of the block's fragments (consecutive
-// threads -> consecutive slots, 1 KB per fragment).
-constexpr int TR = 256;
-
-// sum of squares of row r0 + (tid/16) over n elements of src (fp32 or bf16),
-// reduced over the 16 threads of the DPP row
-template <typename TS>
-__device__ __forceinline__ float row_ss(const TS* src, size_t ld, int r, int n) {
-  const int c = threadIdx.x & 15;
-  const TS* p = src + (size_t)r * ld;
-  float ss = 0.f;
-  for (int k = c * 8; k < n; k += 128) {
-    float v[8];
-    if (sizeof(TS) == 4) {
-      const float4 a = *(const float4*)((const float*)p + k), b = *(const float4*)((const float*)p + k + 4);
-      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
-    } else {
-      unpack8(*(const uint4*)((const bf16*)p + k), v);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
-  }
-  return row16_sum(ss);
 }
 
 // x = [rms(emb[t]) * norm_e ; rms(s) * norm_s] (bf16, fragment order, K = 2d)
@@ -275,6 +234,8 @@ struct TEpiCE {
   float* lab;
   const int32_t* tokens;  // [M], targets are tokens[row + step] inside the sequence
   int S, step, nblk;
+  float* logits = nullptr;  // optional fp32 logits [M][ldl] (kept for the backward)
+  int ldl = 0;
   struct Pre {
     int tg[8][4];
   };
@@ -315,6 +276,7 @@ struct TEpiCE {
             const float xv = acc[i][j][e];
             mx = fmaxf(mx, xv);
             if (n == target) lab[row] = xv;
+            if (logits && row < M) logits[(size_t)row * ldl + n] = xv;
           }
         }
         mx = row16_max(mx);
@@ -365,7 +327,8 @@ struct TEpiCE {
 __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict__ part, int nblk,
                                                        const float* __restrict__ lab, const int32_t* __restrict__ forced,
                                                        int S, int R, int step, int32_t* __restrict__ pred,
-                                                       float* __restrict__ ce, int32_t* __restrict__ tok_next) {
+                                                       float* __restrict__ ce, int32_t* __restrict__ tok_next,
+                                                       float* __restrict__ lse_out) {
   __shared__ float wv[4];
   __shared__ int wi[4];
   __shared__ double ws[4];
@@ -414,6 +377,31 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
     pred[o] = gi;
     ce[o] = i + step <= S - 1 ? (float)(lse - (double)lab[row]) : 0.f;
     if (tok_next) tok_next[row] = forced ? forced[((size_t)b * (R - 1) + (step - 1)) * S + i] : gi;
+    if (lse_out) lse_out[row] = (float)lse;
+  }
+}
+
+// Gradient of the mean CE at one step's logits, bf16 row-major [M][ldl]:
+// (softmax - onehot(target)) / count on rows with a target (i + step <=
+// S-1), zero on the others and in the padding columns V..ldl-1.
+__global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ logits, int V, int ldl,
+                                                      const float* __restrict__ lse, const int32_t* __restrict__ tokens,
+                                                      int S, int step, float inv_count, bf16* __restrict__ out) {
+  const int row = blockIdx.x;
+  const bool valid = row % S + step <= S - 1;
+  const int target = valid ? tokens[row + step] : -1;
+  const float l = lse[row];
+  const float* src = logits + (size_t)row * ldl;
+  bf16* dst = out + (size_t)row * ldl;
+  for (int k = threadIdx.x * 4; k < ldl; k += 256 * 4) {
+    float g[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid && k < V) {  // V % 16 == 0: a group of four is inside or outside
+      const float4 x = *(const float4*)(src + k);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[c] = (__expf(xv[c] - l) - (k + c == target ? 1.f : 0.f)) * inv_count;
+    }
+    *(uint2*)(dst + k) = make_uint2(f2bf2(g[0], g[1]), f2bf2(g[2], g[3]));
   }
 }
 
@@ -621,15 +609,12 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 // c ^ (r % chunks-per-row), so the 16 rows of a fragment read distinct
 // banks.  The per-wave arithmetic (MFMA operands, the online softmax, the P
 // hi/lo split, the chain keys) is that of ttt_attn_kernel, in the same order.
-constexpr int TA_WAVES = 8;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* tta_lds_s16x4;
 
 template <int HD, int G>
 __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K1, const bf16* __restrict__ V1,
     const bf16* __restrict__ KC, const bf16* __restrict__ VC, int nchain, size_t chain_stride,
-    bf16* __restrict__ out, int S, int hq, int hkv, float scale) {
+    bf16* __restrict__ out, int S, int hq, int hkv, float scale, float* __restrict__ lse) {
   constexpr int NC = HD / 32, NT = HD / 16, CPR = HD / 8;  // 16-byte chunks per row
   constexpr int RG = TA_WAVES / G, QB = 32 * RG, KB = 64;
   constexpr int BLK = KB * CPR;                    // 16-byte chunks per K (or V) block
@@ -824,6 +809,7 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
     const float inv = 1.f / L;
     const int row = b * S + i0 + 16 * nt + ml;
     const int nkc = (hq * HD) >> 5;
+    if (lse && q4 == 0) lse[(size_t)row * hq + h] = mrun[nt] + logf(L);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const f32x4 r = o[t][nt] * inv;
@@ -833,37 +819,34 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
   }
 }
 
-// apack: A in fragment order (every A operand the TTT kernels produce); the
-// fusion GEMM reads the caller's row-major features.
-template <class Epi>
-hipError_t bg_launch(const bf16* A, int lda, bool apack, int M, const void* W, bool packed, int N, int K, RowMap map,
-                     Epi epi, hipStream_t st, int kc = -1) {
-  const int grid = bg_grid(M, N);
-  const bf16* Wb = (const bf16*)W;
-  const dim3 g(grid), b(BG_THREADS);
-  if (packed && apack) launch_timed(kc, big_gemm_kernel<true, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
-  else if (packed) launch_timed(kc, big_gemm_kernel<true, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
-  else if (apack) launch_timed(kc, big_gemm_kernel<false, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
-  else launch_timed(kc, big_gemm_kernel<false, false, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 size_t ttt_ws_bytes(const eagle3_dims& dm, int B, int S, int R) { return layout_of(dm, B, S, R, nullptr).bytes; }
 
 int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feats, const int32_t* tokens, int B, int S,
-                int R, const int32_t* forced, int32_t* pred, float* ce, float* loss, void* wsp, hipStream_t st) {
+                int R, const int32_t* forced, int32_t* pred, float* ce, float* loss, void* wsp, hipStream_t st,
+                TttSave* sv) {
   const int d = dm.d, hq = dm.n_q_heads, hkv = dm.n_kv_heads, hd = dm.head_dim, F = dm.ffn, V = dm.vocab;
   const int qd = hq * hd, kvd = hkv * hd;
   if (dm.dtype != EAGLE3_BF16 || (hd != 64 && hd != 128) || S % 64 != 0) return 1;
   if (d % 64 || F % 64 || qd % 64 || d > 8192 || hq % hkv) return 1;
   const int M = B * S;
+  const size_t Md = (size_t)M * d;
   const TLayout L = layout_of(dm, B, S, R, wsp);
   const bool pk = w.layout == EAGLE3_LAYOUT_PACKED;
   const float eps = dm.rms_eps;
   const int nblk = ce_blocks(V);
   const RowMap plain{MAP_PLAIN, hd, F}, pair_head{MAP_PAIR_HEAD, hd, F}, pair_ffn{MAP_PAIR_FFN, hd, F};
+  const int gq = hq / hkv;
+  const bool lds_attn = 8 % gq == 0;  // step-1 values stay row-major for the LDS kernel
+  if (sv && !lds_attn) return 1;      // the backward reads row-major step-1 values
+  if (sv) {
+    sv->k1 = L.k1;
+    sv->v1 = L.v1t;
+    sv->kc = L.kc;
+    sv->vc = L.vc;
+    sv->rope = L.rope;
+  }
   hipError_t e;
 #define E3_CHECK(x) \
   if ((e = (x)) != hipSuccess) return -1;
@@ -876,32 +859,43 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
   }
   {
     TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-    E3_CHECK(bg_launch((const bf16*)feats, 3 * d, false, M, w.fc, pk, d, 3 * d, plain, BEpiStoreF{L.hs, d, true}, st));
+    E3_CHECK(bg_launch((const bf16*)feats, 3 * d, false, M, w.fc, pk, d, 3 * d, plain,
+                       BEpiStoreF{sv ? sv->s : L.hs, d, true}, st));
   }
   for (int j = 1; j <= R; ++j) {
+    // state buffers: in place without sv; kept per step with it
+    float* s_in = sv ? sv->s + (size_t)(j - 1) * Md : L.hs;
+    float* h1 = sv ? sv->h1 + (size_t)(j - 1) * Md : L.hs;
+    float* s_out = sv ? sv->s + (size_t)j * Md : L.hs;
+    bf16* x = sv ? sv->x + (size_t)(j - 1) * 2 * Md : L.x;
+    bf16* q = sv ? sv->q + (size_t)(j - 1) * M * qd : L.q;
+    bf16* a = sv ? sv->a + (size_t)(j - 1) * M * qd : L.a;
+    bf16* u = sv ? sv->u + (size_t)(j - 1) * Md : L.x;
+    bf16* z = sv ? sv->z + (size_t)(j - 1) * M * F : L.z;
+    const int32_t* tok_in = j == 1 ? tokens : (sv ? sv->tok + (size_t)(j - 1) * M : L.tok);
+    int32_t* tok_out = j == R ? nullptr : (sv ? sv->tok + (size_t)j * M : L.tok);
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_prologue_kernel<<<M / 16, TR, 0, st>>>((const bf16*)w.emb, j == 1 ? tokens : L.tok, L.hs, d, w.norm_e,
-                                                 w.norm_s, eps, L.x);
+      ttt_prologue_kernel<<<M / 16, TR, 0, st>>>((const bf16*)w.emb, tok_in, s_in, d, w.norm_e, w.norm_s, eps, x);
       E3_CHECK(hipGetLastError());
     }
     bf16* kdst = j == 1 ? L.k1 : L.kc + (size_t)(j - 2) * M * kvd;
     bf16* vdst = j == 1 ? L.v1t : L.vc + (size_t)(j - 2) * M * kvd;
-    const int gq = hq / hkv;
-    const bool lds_attn = 8 % gq == 0;  // step-1 values stay row-major for the LDS kernel
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      TEpiQKV epi{L.q, kdst, vdst, j == 1 && !lds_attn, L.rope, hq, hkv, hd, S, j - 1};
-      E3_CHECK(bg_launch(L.x, 2 * d, true, M, w.qkv, pk, qd + 2 * kvd, 2 * d, pair_head, epi, st));
+      TEpiQKV epi{q, kdst, vdst, j == 1 && !lds_attn, L.rope, hq, hkv, hd, S, j - 1};
+      E3_CHECK(bg_launch(x, 2 * d, true, M, w.qkv, pk, qd + 2 * kvd, 2 * d, pair_head, epi, st));
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_ATTN, st);
       const float scale = (float)(1.0 / sqrt((double)hd));
+      float* lse = sv ? sv->lse + (size_t)(j - 1) * M * hq : nullptr;
       if (lds_attn) {
         const int qbr = 32 * (TA_WAVES / gq);
         const dim3 grid((S + qbr - 1) / qbr, hkv, B);
 #define E3_TTA(HDV, GV) \
-  ttt_attn_lds_kernel<HDV, GV><<<grid, TA_WAVES * 64, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S, hq, hkv, scale)
+  ttt_attn_lds_kernel<HDV, GV><<<grid, TA_WAVES * 64, 0, st>>>(q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, a, S, \
+                                                               hq, hkv, scale, lse)
         if (hd == 128) {
           if (gq == 1) E3_TTA(128, 1);
           else if (gq == 2) E3_TTA(128, 2);
@@ -916,46 +910,64 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
 #undef E3_TTA
         E3_CHECK(hipGetLastError());
       } else {
-      const int wpb = gq % 4 == 0 ? 4 : (gq % 2 == 0 ? 2 : 1);
-      const dim3 grid(S / 32, hq / wpb, B);
-      const int threads = 64 * wpb;
-      if (hd == 128)
-        ttt_attn_kernel<128><<<grid, threads, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S,
-                                                       hq, hkv, scale);
-      else
-        ttt_attn_kernel<64><<<grid, threads, 0, st>>>(L.q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, L.a, S,
-                                                      hq, hkv, scale);
-      E3_CHECK(hipGetLastError());
+        const int wpb = gq % 4 == 0 ? 4 : (gq % 2 == 0 ? 2 : 1);
+        const dim3 grid(S / 32, hq / wpb, B);
+        const int threads = 64 * wpb;
+        if (hd == 128)
+          ttt_attn_kernel<128><<<grid, threads, 0, st>>>(q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, a, S,
+                                                         hq, hkv, scale);
+        else
+          ttt_attn_kernel<64><<<grid, threads, 0, st>>>(q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, a, S,
+                                                        hq, hkv, scale);
+        E3_CHECK(hipGetLastError());
       }
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      E3_CHECK(bg_launch(L.a, qd, true, M, w.o, pk, d, qd, plain, BEpiResid{L.hs, d}, st));
+      E3_CHECK(bg_launch(a, qd, true, M, w.o, pk, d, qd, plain, BEpiAdd{s_in, h1, d}, st));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(L.hs, d, w.norm_ffn, eps, L.x);
+      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(h1, d, w.norm_ffn, eps, u);
       E3_CHECK(hipGetLastError());
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_GEMM, st);
-      E3_CHECK(bg_launch(L.x, d, true, M, w.gate_up, pk, 2 * F, d, pair_ffn, BEpiSwiGLU{L.z, F}, st));
-      E3_CHECK(bg_launch(L.z, F, true, M, w.down, pk, d, F, plain, BEpiResid{L.hs, d}, st));
+      BEpiSwiGLU swi{z, F, sv ? sv->gu + (size_t)(j - 1) * M * F : nullptr};
+      E3_CHECK(bg_launch(u, d, true, M, w.gate_up, pk, 2 * F, d, pair_ffn, swi, st));
+      E3_CHECK(bg_launch(z, F, true, M, w.down, pk, d, F, plain, BEpiAdd{h1, s_out, d}, st));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(L.hs, d, w.norm_out, eps, L.x);
+      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(s_out, d, w.norm_out, eps, L.x);
       E3_CHECK(hipGetLastError());
     }
     {
       TimedScope ts(EAGLE3_KC_TTT_CE, st);
-      E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, TEpiCE{L.part, L.lab, tokens, S, j, nblk}, st,
-                         EAGLE3_KC_TTT_CE));
+      TEpiCE epi{L.part, L.lab, tokens, S, j, nblk};
+      if (sv) {
+        epi.logits = sv->logits;
+        epi.ldl = sv->vp;
+      }
+      E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, epi, st, EAGLE3_KC_TTT_CE));
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ce_merge_kernel<<<M, 256, 0, st>>>(L.part, nblk, L.lab, forced, S, R, j, pred, ce, j < R ? L.tok : nullptr);
+      ce_merge_kernel<<<M, 256, 0, st>>>(L.part, nblk, L.lab, forced, S, R, j, pred, ce, tok_out,
+                                         sv ? sv->lse_ce : nullptr);
       E3_CHECK(hipGetLastError());
+    }
+    if (sv) {
+      // dy = dlogits . W_lm: the LM head's backward, done while the logits are at hand
+      {
+        TimedScope ts(EAGLE3_KC_ROWOPS, st);
+        dlogits_kernel<<<M, 256, 0, st>>>(sv->logits, V, sv->vp, sv->lse_ce, tokens, S, j,
+                                          (float)(1.0 / sv->count), sv->dlogits);
+        E3_CHECK(hipGetLastError());
+      }
+      TimedScope ts(EAGLE3_KC_TTT_BWD_GEMM, st);
+      E3_CHECK(bg_launch(sv->dlogits, sv->vp, false, M, sv->lm_t, true, d, sv->vp, plain,
+                         BEpiStoreF{sv->dy + (size_t)(j - 1) * Md, d, false}, st, EAGLE3_KC_TTT_BWD_GEMM));
     }
   }
   {

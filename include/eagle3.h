@@ -364,6 +364,43 @@ int eagle3_ttt_forward(const eagle3_dims *dims, const eagle3_weights *w, const v
                        int32_t *pred, float *ce, float *loss, void *ws, size_t ws_bytes,
                        eagle3_stream_t stream);
 
+/* Gradients of the training-time-test loss, fp32 device arrays in the
+ * logical row-major layout of eagle3_weights (independent of w->layout):
+ * fc [d][3d], qkv [(Hq+2Hkv)hd][2d], o [d][Hq hd], gate_up [2F][d] (gate
+ * rows then up rows), down [d][F]; the RMSNorm gains [d]. */
+typedef struct {
+  float *fc, *qkv, *o, *gate_up, *down;
+  float *norm_e, *norm_s, *norm_ffn, *norm_out;
+} eagle3_grads;
+
+/* Workspace bytes needed by eagle3_ttt_train (it keeps every step's
+ * activations: about 3.8 GB per step plus 13 GB of one step's logits at the
+ * 8B drafter's shape with B*S = 16384; 45 GB for 5 steps). */
+int eagle3_ttt_train_workspace_size(const eagle3_dims *dims, int B, int S, int R, size_t *bytes);
+
+/* Training-time-test forward and backward ("EAGLE-3 精读" §1: the target
+ * and its LM head are frozen and the light decoder is trained; §2: the
+ * rollout's CE at every step under the training-time-test mask).  The
+ * forward and its outputs are those of eagle3_ttt_forward; `grads` receives
+ * the gradients of loss[0] (the mean CE over the valid rows) with respect to
+ * the drafter's trained parameters: the fusion FC, the layer's qkv, o,
+ * gate_up and down, and its gains norm_e, norm_s, norm_ffn, norm_out
+ * (every array overwritten).  The embedding and the LM head get none, nor
+ * do the fed tokens (an argmax or forced choice); gradients reach earlier
+ * steps through the fed state h2 and through the keys and values later
+ * queries attend to.  bf16 roundings of the forward pass gradients straight
+ * through.  Precision: bf16 GEMM operands (every gradient tensor that feeds a
+ * GEMM is rounded to bf16), fp32 accumulation; the weight gradients sum all
+ * R*B*S rows in one fp32 accumulation, deterministic (fixed orders, no
+ * atomics).  Requirements: those of eagle3_ttt_forward plus Hq/Hkv in
+ * {1, 2, 4, 8} and vocab a multiple of 16 (EAGLE3_EUNSUPPORTED otherwise).
+ * Optimizer steps, clipping and data are the caller's.  ws:
+ * eagle3_ttt_train_workspace_size bytes, no initialisation needed. */
+int eagle3_ttt_train(const eagle3_dims *dims, const eagle3_weights *w, const void *feats,
+                     const int32_t *tokens, int B, int S, int R, const int32_t *forced_tokens,
+                     int32_t *pred, float *ce, float *loss, const eagle3_grads *grads, void *ws,
+                     size_t ws_bytes, eagle3_stream_t stream);
+
 /* ---- EAGLE-4 Harness: cost-aware tree control ----------------------------
  * (EAGLE-4 blog, the EAGLE-Harness paragraph: a warm-up measures draft and
  * verify times over batch sizes, context lengths and token counts into a
@@ -558,7 +595,11 @@ int eagle3_topk(const float *logits, int rows, int V, int k, int32_t *ids, float
 #define EAGLE3_KC_TARGET 15     /* eagle3_target_forward, whole call          */
 #define EAGLE3_KC_TGT_GATEUP 16 /* its gate/up GEMMs (principal kernel)       */
 #define EAGLE3_KC_TGT_LMHEAD 17 /* its LM-head GEMM (principal kernel)        */
-#define EAGLE3_KC_COUNT 18
+#define EAGLE3_KC_TTT_BWD_GEMM 18 /* TTT backward: data-gradient GEMMs (dy, dz, du, da, dx) */
+#define EAGLE3_KC_TTT_BWD_ATTN 19 /* TTT backward: attention                              */
+#define EAGLE3_KC_TTT_WGRAD 20    /* TTT backward: weight-gradient GEMMs                  */
+#define EAGLE3_KC_TTT_BWD_ROWS 21 /* TTT backward: norm backward, transposes, reductions  */
+#define EAGLE3_KC_COUNT 22
 
 /* max_launches > 0 enables class `kc` with room for that many launches
  * (counters reset); 0 disables it and frees its events. */
@@ -571,7 +612,9 @@ int eagle3_timing_read(int kc, double *total_ms, int *launches);
  * a profiler reads): the LM-head GEMM for EAGLE3_KC_LMHEAD, the scores
  * kernel for EAGLE3_KC_LR_SCORES, the CE GEMM for EAGLE3_KC_TTT_CE, the
  * target's gate/up and LM-head GEMMs for EAGLE3_KC_TGT_GATEUP and
- * EAGLE3_KC_TGT_LMHEAD; other classes then record nothing. */
+ * EAGLE3_KC_TGT_LMHEAD, the TTT backward's dy GEMM (dlogits . W_lm) for
+ * EAGLE3_KC_TTT_BWD_GEMM and its weight-gradient GEMMs for
+ * EAGLE3_KC_TTT_WGRAD; other classes then record nothing. */
 int eagle3_timing_mode(int kc, int mode);
 
 #ifdef __cplusplus

@@ -85,16 +85,47 @@ def _t(a):
     return torch.as_tensor(np.asarray(a, dtype=np.float64))
 
 
-def _sequence(cfg, P, feats, tokens, R, forced):
+class _GradToBf16(torch.autograd.Function):
+    """Identity whose backward rounds the gradient to bfloat16."""
+
+    @staticmethod
+    def forward(ctx, x):
+        return x.view_as(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return _bf16(g)
+
+
+def _gq(on):
+    """Gradient rounding at a GEMM's operand (the bf16-gradient variant)."""
+    return _GradToBf16.apply if on else (lambda x: x)
+
+
+def _mm_f32(a, b):
+    """a @ b with float32 operands and accumulation (the f32 variant)."""
+    return (a.to(torch.float32) @ b.to(torch.float32)).to(torch.float64)
+
+
+def _es_f32(eq, *ops):
+    return torch.einsum(eq, *(o.to(torch.float32) for o in ops)).to(torch.float64)
+
+
+def _sequence(cfg, P, feats, tokens, R, forced, grad_bf16=False, gemm_f32=False):
     """Sum of the valid CE of one sequence plus its float32 predictions.
 
     feats [S, 3, d] (fp64 tensor), tokens [S] ints; forced [R-1, S] or None.
-    P: parameters (fp64 tensors; the trained ones require grad)."""
+    P: parameters (fp64 tensors; the trained ones require grad).  grad_bf16:
+    round to bf16 the gradients that reach a GEMM as an operand; gemm_f32:
+    products and their gradients in float32 (see ttt_loss_and_grads)."""
+    gq = _gq(grad_bf16)
+    mm = _mm_f32 if gemm_f32 else (lambda a, b: a @ b)
+    es = _es_f32 if gemm_f32 else torch.einsum
     S = len(tokens)
     d, Hq, Hkv, hd, F, eps = cfg.d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.rms_eps
     grp = Hq // Hkv
     scale = 1.0 / np.sqrt(hd)
-    g = _rnd(cfg, feats.reshape(S, 3 * d) @ P["fc"].T)
+    g = _rnd(cfg, gq(mm(feats.reshape(S, 3 * d), P["fc"].T)))
     s = g
     t = torch.as_tensor(np.asarray(tokens, dtype=np.int64))
     causal = torch.tril(torch.ones(S, S, dtype=torch.bool))
@@ -108,7 +139,7 @@ def _sequence(cfg, P, feats, tokens, R, forced):
         pos = torch.arange(S) + (j - 1)
         x = torch.cat([_rms(P["emb"][t], P["norm_e"], eps), _rms(s, P["norm_s"], eps)], dim=1)
         x = _rnd(cfg, x)
-        qkv = x @ P["qkv"].T
+        qkv = gq(mm(x, P["qkv"].T))
         q = qkv[:, : Hq * hd].reshape(S, Hq, hd)
         k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(S, Hkv, hd)
         v = qkv[:, (Hq + Hkv) * hd:].reshape(S, Hkv, hd)
@@ -123,25 +154,25 @@ def _sequence(cfg, P, feats, tokens, R, forced):
         # query (j, i), head h of group h // grp: step-1 keys i' <= i, then the
         # chain keys (j', i) of its own position, 2 <= j' <= j
         qg = q.reshape(S, Hkv, grp, hd)
-        sc1 = torch.einsum("igcd,kgd->gcik", qg, k1) * scale            # [Hkv, grp, S, S]
+        sc1 = es("igcd,kgd->gcik", qg, k1) * scale            # [Hkv, grp, S, S]
         sc1 = sc1.masked_fill(~causal, float("-inf"))
         scs = [sc1]
         for kc in chain_k:
-            scs.append((torch.einsum("igcd,igd->gci", qg, kc) * scale)[..., None])
+            scs.append((es("igcd,igd->gci", qg, kc) * scale)[..., None])
         p = torch.softmax(torch.cat(scs, dim=-1), dim=-1)
-        a = torch.einsum("gcik,kgd->igcd", p[..., :S], v1)
+        a = es("gcik,kgd->igcd", p[..., :S], v1)
         for c, vc in enumerate(chain_v):
-            a = a + torch.einsum("gci,igd->igcd", p[..., S + c], vc)
-        a = _rnd(cfg, a.reshape(S, Hq * hd))
-        h1 = s + a @ P["o"].T
+            a = a + es("gci,igd->igcd", p[..., S + c], vc)
+        a = gq(_rnd(cfg, a.reshape(S, Hq * hd)))
+        h1 = s + gq(mm(a, P["o"].T))
         u = _rnd(cfg, _rms(h1, P["norm_ffn"], eps))
-        gu = u @ P["gate_up"].T
+        gu = gq(mm(u, P["gate_up"].T))
         gate, up = gu[:, :F], gu[:, F:]
         z = _rnd(cfg, gate * torch.sigmoid(gate) * up)
-        h2 = h1 + z @ P["down"].T
+        h2 = h1 + gq(mm(z, P["down"].T))
         y = _rnd(cfg, _rms(h2, P["norm_out"], eps))
-        logits = y @ P["lm"].T
-        l32 = _st(logits, logits.detach().to(torch.float32).to(torch.float64))   # R43: CE on float32 logits
+        logits = mm(y, P["lm"].T)
+        l32 = gq(_st(logits, logits.detach().to(torch.float32).to(torch.float64)))   # R43: CE on float32 logits
         logits_all.append(l32.detach().numpy())
         pred[j - 1] = np.argmax(l32.detach().to(torch.float32).numpy(), axis=1)
         n_valid = max(S - j, 0)            # rows i <= S-1-j have the label x_{i+j}
@@ -158,8 +189,17 @@ def _sequence(cfg, P, feats, tokens, R, forced):
     return ce_sum, ce, pred, logits_all
 
 
-def ttt_loss_and_grads(cfg, W, feats, tokens, R, forced=None, want_grads=True):
+def ttt_loss_and_grads(cfg, W, feats, tokens, R, forced=None, want_grads=True, grad_bf16=False, gemm_f32=False):
     """Loss (R45) and its gradients w.r.t. the trained parameters (R42).
+
+    grad_bf16 (a precision variant, not the reference): the gradients that
+    reach a GEMM as an operand in a bf16 backward -- at the logits, at the
+    outputs of the g, qkv, o, gate_up and down projections and at the
+    attention output -- are rounded to bfloat16, as a backward with bf16 GEMM
+    operands must; gemm_f32 (another precision variant) takes every product
+    of the forward and the backward in float32.  Together they show how far
+    a bf16-operand, fp32-accumulation training step may lie from the exact
+    gradient (the forward's own bf16 roundings then differ now and then).
 
     W: drafter weights (arrays; row-major [out, in] matrices, gains [d]);
     feats [B, S, 3, d]; tokens [B, S]; forced [B, R-1, S] or None.
@@ -181,7 +221,7 @@ def ttt_loss_and_grads(cfg, W, feats, tokens, R, forced=None, want_grads=True):
     logits = []
     for b in range(Bn):
         s, ce[b], pred[b], lg = _sequence(cfg, P, _t(feats[b]), tokens[b], R,
-                                          None if forced is None else forced[b])
+                                          None if forced is None else forced[b], grad_bf16, gemm_f32)
         total = total + s
         logits.append(lg)
     loss = total / count if count else total

@@ -333,3 +333,34 @@ def test_harness_argument_checks(blib):
                                        ctypes.c_double(0.0), ctypes.byref(go)) == blib.EINVAL
     assert lib.eagle3_tree_confidence(1, 17, 2, 4, _P, _P, None, None) == blib.ECAPACITY
     assert lib.eagle3_tree_confidence(1, 4, 2, 4, None, _P, None, None) == blib.EINVAL
+
+
+def test_ttt_train_argument_checks(blib):
+    """eagle3_ttt_train validates before launching: workspace size, gradient
+    pointers, the head-group and vocabulary restrictions, the dtype."""
+    from workloads.configs import L8B_SHAPE, TINY_SHAPE, tiny_shape
+    lib = blib.load()
+    d = blib.dims_of(L8B_SHAPE)
+    w = _fake_weights(blib)
+    g = blib.Grads(*([0x1000] * len(blib.GRAD_NAMES)))
+    need = blib.ttt_train_workspace_size(d, 8, 2048, 5)
+    # the 8B shape at 8 x 2048 x 5 keeps ~45 GB of activations
+    assert 30e9 < need < 60e9
+    assert need > blib.ttt_workspace_size(d, 8, 2048, 5)
+
+    def call(dims, grads, ws_bytes, S=128, R=2):
+        return lib.eagle3_ttt_train(ctypes.byref(dims), ctypes.byref(w), _P, _P, 1, S, R, None, _P, _P, _P,
+                                    ctypes.byref(grads), _P, ws_bytes, None)
+    small = blib.ttt_train_workspace_size(d, 1, 128, 2)
+    assert call(d, g, small - 1) == blib.EWORKSPACE
+    nog = blib.Grads(*([0x1000] * (len(blib.GRAD_NAMES) - 1) + [0]))
+    assert call(d, nog, small) == blib.EINVAL
+    assert b"gradient" in lib.eagle3_last_error()
+    assert call(d, g, small, S=96) == blib.EUNSUPPORTED                      # S % 64
+    g3 = blib.dims_of(tiny_shape(d=384, hq=6, hkv=2, hd=64, ffn=512, vocab=2064, dtype="bf16"))
+    assert call(g3, g, 1 << 40) == blib.EUNSUPPORTED                          # Hq/Hkv = 3
+    assert b"Hq/Hkv" in lib.eagle3_last_error()
+    v8 = blib.dims_of(tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=512, vocab=1048, dtype="bf16"))
+    assert call(v8, g, 1 << 40) == blib.EUNSUPPORTED                          # vocab % 16
+    f32 = blib.dims_of(TINY_SHAPE)
+    assert call(f32, g, 1 << 40) == blib.EUNSUPPORTED                         # bf16 only

@@ -144,3 +144,16 @@ def test_no_valid_label_gives_zero_gradient():
     assert out["loss"] == 0.0
     for name in G.TRAINED:
         assert not np.any(out["grads"][name])
+
+
+def test_precision_variants_stay_near_the_exact_gradient():
+    """The bf16-gradient and fp32-product variants (tolerance calibration
+    only) move the bf16 drafter's gradients by rounding-sized amounts."""
+    cfg, W, feats, toks, forced = _setup(BF16)
+    ex = G.ttt_loss_and_grads(cfg, W, feats, toks, 4, forced=forced)
+    for kw in (dict(grad_bf16=True), dict(gemm_f32=True), dict(grad_bf16=True, gemm_f32=True)):
+        va = G.ttt_loss_and_grads(cfg, W, feats, toks, 4, forced=forced, **kw)
+        assert abs(va["loss"] - ex["loss"]) < 1e-3
+        for name in G.TRAINED:
+            rel = np.linalg.norm(va["grads"][name] - ex["grads"][name]) / np.linalg.norm(ex["grads"][name])
+            assert 0 < rel < 2e-2, (kw, name, rel)
