@@ -113,8 +113,21 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   const int ntm = (M + BG_BM - 1) / BG_BM;
   const int nb = gridDim.x;
   int bid = blockIdx.x;
+#ifndef E3_BG_MAP
+#define E3_BG_MAP 0
+#endif
+#if E3_BG_MAP != 3
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+#endif
+#if E3_BG_MAP == 1
+  const int GROUP = 16;
+#elif E3_BG_MAP == 2
+  const int GROUP = 4;
+#elif E3_BG_MAP == 5
+  const int GROUP = 32;
+#else
   const int GROUP = 8;
+#endif
   const int per_group = GROUP * ntn;
   const int first_m = (bid / per_group) * GROUP;
   const int gsz = min(GROUP, ntm - first_m);

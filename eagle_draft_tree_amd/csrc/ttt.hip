@@ -809,7 +809,7 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
     const float inv = 1.f / L;
     const int row = b * S + i0 + 16 * nt + ml;
     const int nkc = (hq * HD) >> 5;
-    if (lse && q4 == 0) lse[(size_t)row * hq + h] = mrun[nt] + logf(L);
+    if (lse && q4 == 0) lse[(size_t)h * gridDim.z * S + row] = mrun[nt] + logf(L);  // [hq][M]
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const f32x4 r = o[t][nt] * inv;

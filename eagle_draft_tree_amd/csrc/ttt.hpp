@@ -14,7 +14,7 @@ struct TttSave {
   float* h1;         // [R][M][d]    residual after attention
   bf16* x;           // [R][M][2d]   decoder input, fragment order
   bf16* q;           // [R][M][hq][hd] queries after RoPE
-  float* lse;        // [R][M][hq]   attention log-sum-exp per query row and head
+  float* lse;        // [R][hq][M]   attention log-sum-exp per query head and row
   bf16* a;           // [R][M][hq*hd] attention output, fragment order
   bf16* u;           // [R][M][d]    FFN input, fragment order
   float2* gu;        // [R][M][ffn]  (gate, up) before SwiGLU

@@ -264,7 +264,7 @@ struct BEpiSwiGLUBwd {
 // over the rollout mask: query (j, i) sees the step-1 keys i' <= i and the
 // chain keys (j', i), 2 <= j' <= j.
 
-// Per (row, kv head g), one wave: D for the g's query heads; then the chain
+// Per (row, kv head g), one wave: D ([hq][M]) for the g's query heads; then the chain
 // keys of this row: dQ's chain part (unscaled, dq_chain [M][hq][hd]) and
 // the chain keys' dK (scaled) and dV, summed over the group's heads in head
 // order and added to the fp32 accumulators [R-1][M][hkv][hd].
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const bf16* __restrict__
 #pragma unroll
     for (int u = 0; u < EPL; ++u) s = fmaf(go[hl][u], ov[u], s);
     D[hl] = wave_sum(s);
-    L[hl] = lse[(size_t)row * hq + h];
-    if (lane == 0) Dout[(size_t)row * hq + h] = D[hl];
+    L[hl] = lse[(size_t)h * M + row];
+    if (lane == 0) Dout[(size_t)h * M + row] = D[hl];
   }
   if (nchain == 0) return;
   float dqc[G][EPL];
@@ -403,8 +403,9 @@ __global__ __launch_bounds__(TA_WAVES * 64) void attn_dq_kernel(
       qf[nt][c].u = *(const uint4*)(Q + o * HD + 32 * c + 8 * q4);
       df[nt][c].u = *(const uint4*)(dO + o * HD + 32 * c + 8 * q4);
     }
-    Ln[nt] = lse[o];
-    Dn[nt] = Dd[o];
+    const size_t ho = (size_t)h * gridDim.z * S + b * S + i;  // [hq][M]
+    Ln[nt] = lse[ho];
+    Dn[nt] = Dd[ho];
   }
   f32x4 dq[NT][2];
 #pragma unroll
@@ -512,12 +513,14 @@ __global__ __launch_bounds__(TA_WAVES * 64) void attn_dq_kernel(
 // dK and dV of the step-1 keys from one step's queries: workgroup = (block
 // of 128 keys, kv head g, sequence b), four waves of 32 keys; the keys' K and
 // V operands stay in registers.  For every query head of the group and every
-// block of 32 queries at or after the workgroup's first key, Q and dO rows
-// are staged in LDS (double-buffered, the next block prefetched through
-// registers) and each wave computes S = Q K^T and dP = dO V^T (queries x
-// keys), P and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
-// read transposed from LDS.  The results are added to the fp32 accumulators
-// [M][hkv][hd] (each element owned by one lane: deterministic).
+// block of 32 queries at or after the workgroup's first key, the Q and dO
+// rows and the rows' L and D ([hq][M], contiguous per head) are copied into
+// LDS by direct global -> LDS copies (two stages: the next block's copies
+// are in flight while this one is computed); each wave computes S = Q K^T
+// and dP = dO V^T (queries x keys), P and dS, then dV^T += dO^T P and dK^T +=
+// Q^T dS with dO^T and Q^T read transposed from LDS.  The results are added
+// to the fp32 accumulators [M][hkv][hd] (each element owned by one lane:
+// deterministic).
 constexpr int DKV_KEYS = 128;
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ dO,
@@ -526,13 +529,17 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
                                                        float* __restrict__ dK, float* __restrict__ dV, int S, int hq,
                                                        int hkv, float scale) {
   constexpr int NC = HD / 32, NT = HD / 16, CPR = HD / 8;
-  constexpr int CH = 32 * CPR;           // 16-byte chunks of a 32-row block
-  constexpr int LPT = 2 * CH / 256;      // chunk loads per thread per stage (Q and dO)
-  __shared__ uint4 qs[2][CH], gs[2][CH];
-  __shared__ float ls[2][32], dsum[2][32];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int CH = 32 * CPR;            // 16-byte chunks of a 32-row block
+  constexpr int CPW = 2 * CH / 64 / 4;    // 64-lane copies per wave per stage (Q and dO)
+  static_assert(CPW * 64 * 4 == 2 * CH, "copies split evenly over the waves");
+  // one stage: Q rows, dO rows, then L[32] and D[32]
+  constexpr int STAGE = 2 * CH + 16;      // in 16-byte units
+  __shared__ uint4 sm[2][STAGE];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ml = lane & 15, q4 = lane >> 4;
   const int g = blockIdx.y, b = blockIdx.z;
+  const int M = gridDim.z * S;
   const int kblk = blockIdx.x * DKV_KEYS;
   const int k0 = kblk + 32 * w;  // the wave's first key
   const bool kact = k0 < S;      // S % 64 == 0: a wave's 32 keys are all inside or all outside
@@ -556,42 +563,36 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
 
   const int qb0 = kblk / 32, nqb = S / 32;
   const int per_head = nqb - qb0, n_it = G * per_head;
-  uint4 pre[LPT];
-  float pre_l = 0.f;
-  auto load = [&](int it) {
+  const uint32_t lds0 = lds_addr(&sm[0][0]);
+  auto issue = [&](int it) {
     const int hl = it / per_head, qb = qb0 + it - hl * per_head;
     const int h = g * G + hl;
+    const uint32_t st_base = lds0 + (uint32_t)((it & 1) * STAGE * 16);
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = threadIdx.x + 256 * u;  // < 2 CH
-      const int which = e / CH, ce = e - which * CH, r = ce / CPR, slot = ce - r * CPR;
+    for (int u = 0; u < CPW; ++u) {
+      const int dd = w * CPW + u;              // copy index within the stage
+      const int which = dd / (CH / 64), part = dd - which * (CH / 64);
+      const int e = part * 64 + lane;          // chunk index within the block
+      const int r = e / CPR, slot = e - r * CPR;
       const size_t o = ((size_t)(b * S + qb * 32 + r) * hq + h) * HD + 8 * (slot ^ (r % CPR));
-      pre[u] = *(const uint4*)((which ? dO : Q) + o);
+      dma16((which ? dO : Q) + o, st_base + (uint32_t)((which * CH + part * 64) * 16));
     }
-    if (threadIdx.x < 64) {
-      const int r = threadIdx.x & 31;
-      const size_t o = (size_t)(b * S + qb * 32 + r) * hq + h;
-      pre_l = threadIdx.x < 32 ? lse[o] : Dd[o];
+    if (w == 0 && lane < 16) {                 // L then D: 32 floats each
+      const float* src = (lane < 8 ? lse : Dd) + (size_t)h * M + b * S + qb * 32 + 4 * (lane & 7);
+      dma16(src, st_base + (uint32_t)(2 * CH * 16));
     }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int which = e / CH, ce = e - which * CH;
-      (which ? gs[buf] : qs[buf])[ce] = pre[u];
-    }
-    if (threadIdx.x < 64) (threadIdx.x < 32 ? ls[buf] : dsum[buf])[threadIdx.x & 31] = pre_l;
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0);
+  bg_wait_copies<0>();
+  bg_barrier();
   for (int it = 0; it < n_it; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < n_it) load(it + 1);
+    if (it + 1 < n_it) issue(it + 1);
     const int hl = it / per_head, qb = qb0 + it - hl * per_head;
     const int q0 = qb * 32;
+    const uint4* qs = &sm[it & 1][0];
+    const uint4* gs = qs + CH;
+    const float* ls = (const float*)(qs + 2 * CH);  // L[32], then D[32]
     (void)hl;
     if (kact && k0 <= q0 + 31) {
       f32x4 st[2][2], dp[2][2];
@@ -604,8 +605,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
         U4 qa[2], ga[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-          qa[a].u = lds_chunk<CPR>(qs[cur], 16 * a + ml, 4 * c + q4);
-          ga[a].u = lds_chunk<CPR>(gs[cur], 16 * a + ml, 4 * c + q4);
+          qa[a].u = lds_chunk<CPR>(qs, 16 * a + ml, 4 * c + q4);
+          ga[a].u = lds_chunk<CPR>(gs, 16 * a + ml, 4 * c + q4);
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qr = 16 * a + 4 * q4 + e;
-          const float L = ls[cur][qr], D = dsum[cur][qr];
+          const float L = ls[qr], D = ls[32 + qr];
 #pragma unroll
           for (int bb = 0; bb < 2; ++bb) {
             const bool masked = diag && k0 + 16 * bb + ml > q0 + qr;
@@ -637,8 +638,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
         pb[bb] = pack_b_from_acc(st[0][bb], st[1][bb]);
         sb[bb] = pack_b_from_acc(dp[0][bb], dp[1][bb]);
       }
-      const bf16* q16 = (const bf16*)qs[cur];
-      const bf16* g16 = (const bf16*)gs[cur];
+      const bf16* q16 = (const bf16*)qs;
+      const bf16* g16 = (const bf16*)gs;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const U4 gt = lds_tr_frag<CPR>(g16, 0, t, ml, q4);
@@ -650,8 +651,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16* __restrict__ 
         }
       }
     }
-    if (it + 1 < n_it) store(cur ^ 1);
-    __syncthreads();
+    bg_wait_copies<0>();
+    bg_barrier();
   }
   // lane holds dK^T[dim 16t + 4 q4 + e][key k0 + 16 bb + ml]
   if (!kact) return;
@@ -722,7 +723,7 @@ struct TrainLayout {
   bf16 *dh2f, *dh1f, *dguf, *dqkvf, *dgf;                 // fragment order [M][*]
   float *du, *dx;                                         // [M][d], [M][2d]
   bf16* da;                                               // [M][hq*hd] row-major
-  float *Dd, *dqc;                                        // [M][hq], [M][hq][hd]
+  float *Dd, *dqc;                                        // [hq][M], [M][hq][hd]
   float *dk1, *dv1, *dkc, *dvc;                           // [M][kvd], [R-1][M][kvd]
   bf16 *dqkvT, *xT, *dh1T, *aT, *dguT, *uT, *dh2T, *zT;  // [N][R*M] fragment order
   bf16 *dgT, *featsT;                                     // [d][M], [3d][M]
