@@ -234,7 +234,10 @@ struct TEpiCE {
   float* lab;
   const int32_t* tokens;  // [M], targets are tokens[row + step] inside the sequence
   int S, step, nblk;
-  float* logits = nullptr;  // optional fp32 logits [M][ldl] (kept for the backward)
+  // optional, for the backward: bf16 exp(logit - m) [M][ldl] with m the row's
+  // maximum over this wave's 64 columns, and those maxima [M][ldl / 64]
+  bf16* ex = nullptr;
+  float* exm = nullptr;
   int ldl = 0;
   struct Pre {
     int tg[8][4];
@@ -276,7 +279,6 @@ struct TEpiCE {
             const float xv = acc[i][j][e];
             mx = fmaxf(mx, xv);
             if (n == target) lab[row] = xv;
-            if (logits && row < M) logits[(size_t)row * ldl + n] = xv;
           }
         }
         mx = row16_max(mx);
@@ -288,7 +290,12 @@ struct TEpiCE {
             if (colbase16 + j < nt16 && acc[i][j][e] == mx) id = (colbase16 + j) * 16 + m;
 #pragma unroll
           for (int j = 0; j < BG_NJ; ++j)
-            if (colbase16 + j < nt16) s += __expf(acc[i][j][e] - mx);
+            if (colbase16 + j < nt16) {
+              const float ev = __expf(acc[i][j][e] - mx);
+              s += ev;
+              if (ex && row < M) ex[(size_t)row * ldl + (colbase16 + j) * 16 + m] = f2bf(ev);
+            }
+          if (exm && m == 0 && row < M) exm[(size_t)row * (ldl >> 6) + (colbase16 >> 2)] = mx;
         }
         id = row16_min(id);
         s = row16_sum(s);
@@ -381,27 +388,40 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float4* __restrict_
   }
 }
 
-// Gradient of the mean CE at one step's logits, bf16 row-major [M][ldl]:
-// (softmax - onehot(target)) / count on rows with a target (i + step <=
-// S-1), zero on the others and in the padding columns V..ldl-1.
-__global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ logits, int V, int ldl,
-                                                      const float* __restrict__ lse, const int32_t* __restrict__ tokens,
-                                                      int S, int step, float inv_count, bf16* __restrict__ out) {
+// Gradient of the mean CE at one step's logits, bf16 row-major [M][ldl],
+// written in place over the CE epilogue's e = exp(logit - m) (m the row's
+// maximum over each 64 columns, exm): (softmax - onehot(target)) / count on
+// rows with a target (i + step <= S-1), zero on the others and in the
+// padding columns V..ldl-1.  softmax = e exp(m - lse); the target column
+// takes exp(target logit - lse) - 1 from the fp32 target logit, so that the
+// cancellation near p = 1 keeps float precision.
+__global__ __launch_bounds__(256) void dlogits_kernel(bf16* __restrict__ e, const float* __restrict__ exm, int V,
+                                                      int ldl, const float* __restrict__ lse,
+                                                      const float* __restrict__ lab, const int32_t* __restrict__ tokens,
+                                                      int S, int step, float inv_count) {
   const int row = blockIdx.x;
   const bool valid = row % S + step <= S - 1;
   const int target = valid ? tokens[row + step] : -1;
   const float l = lse[row];
-  const float* src = logits + (size_t)row * ldl;
-  bf16* dst = out + (size_t)row * ldl;
+  const float pt = valid ? __expf(lab[row] - l) - 1.f : 0.f;
+  const float* mrow = exm + (size_t)row * (ldl >> 6);
+  bf16* p = e + (size_t)row * ldl;
   for (int k = threadIdx.x * 4; k < ldl; k += 256 * 4) {
     float g[4] = {0.f, 0.f, 0.f, 0.f};
-    if (valid && k < V) {  // V % 16 == 0: a group of four is inside or outside
-      const float4 x = *(const float4*)(src + k);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
+    if (valid && k < V) {  // V % 16 == 0: a group of four is inside or outside, within one 64-column group
+      const float sc = __expf(mrow[k >> 6] - l) * inv_count;
+      const uint2 u = *(const uint2*)(p + k);
+      const uint32_t w[2] = {u.x, u.y};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) g[c] = (__expf(xv[c] - l) - (k + c == target ? 1.f : 0.f)) * inv_count;
+      for (int c = 0; c < 2; ++c) {
+        g[2 * c] = __uint_as_float(w[c] << 16) * sc;
+        g[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u) * sc;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (k + c == target) g[c] = pt * inv_count;
     }
-    *(uint2*)(dst + k) = make_uint2(f2bf2(g[0], g[1]), f2bf2(g[2], g[3]));
+    *(uint2*)(p + k) = make_uint2(f2bf2(g[0], g[1]), f2bf2(g[2], g[3]));
   }
 }
 
@@ -946,7 +966,8 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
       TimedScope ts(EAGLE3_KC_TTT_CE, st);
       TEpiCE epi{L.part, L.lab, tokens, S, j, nblk};
       if (sv) {
-        epi.logits = sv->logits;
+        epi.ex = sv->dlogits;
+        epi.exm = sv->exm;
         epi.ldl = sv->vp;
       }
       E3_CHECK(bg_launch(L.x, d, true, M, w.lm, pk, V, d, plain, epi, st, EAGLE3_KC_TTT_CE));
@@ -961,8 +982,8 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
       // dy = dlogits . W_lm: the LM head's backward, done while the logits are at hand
       {
         TimedScope ts(EAGLE3_KC_ROWOPS, st);
-        dlogits_kernel<<<M, 256, 0, st>>>(sv->logits, V, sv->vp, sv->lse_ce, tokens, S, j,
-                                          (float)(1.0 / sv->count), sv->dlogits);
+        dlogits_kernel<<<M, 256, 0, st>>>(sv->dlogits, sv->exm, V, sv->vp, sv->lse_ce, L.lab, tokens, S, j,
+                                          (float)(1.0 / sv->count));
         E3_CHECK(hipGetLastError());
       }
       TimedScope ts(EAGLE3_KC_TTT_BWD_GEMM, st);

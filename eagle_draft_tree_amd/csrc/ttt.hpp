@@ -21,8 +21,8 @@ struct TttSave {
   bf16* z;           // [R][M][ffn]  SwiGLU output, fragment order
   float* dy;         // [R][M][d]    gradient at the LM head input rms(h2)*norm_out
   int32_t* tok;      // [R][M]       tokens fed at step j >= 2 (index 0 unused)
-  float* logits;     // [M][vp]      one step's fp32 logits (scratch)
-  bf16* dlogits;     // [M][vp]      one step's gradient at the logits (scratch)
+  bf16* dlogits;     // [M][vp]      one step's exp(logit - m), then its gradient at the logits (scratch)
+  float* exm;        // [M][vp/64]   the m of each 64 columns (scratch)
   float* lse_ce;     // [M]          one step's logits log-sum-exp (scratch)
   const bf16* lm_t;  // [d][vp]      LM head transposed, packed fragment order
   int vp;            // vocab rounded up to 64 (the backward's K padding)

@@ -752,8 +752,8 @@ TrainLayout train_layout(const eagle3_dims& dm, int B, int S, int R, void* base)
   s.z = c.take<bf16>(R * M * F);
   s.dy = c.take<float>(R * M * d);
   s.tok = c.take<int32_t>(R * M);
-  s.logits = c.take<float>(M * vp);
   s.dlogits = c.take<bf16>(M * vp);
+  s.exm = c.take<float>(M * (vp / 64));
   s.lse_ce = c.take<float>(M);
   bf16* lm_t = c.take<bf16>(d * vp);
   s.lm_t = lm_t;

@@ -374,8 +374,8 @@ typedef struct {
 } eagle3_grads;
 
 /* Workspace bytes needed by eagle3_ttt_train (it keeps every step's
- * activations: about 3.8 GB per step plus 13 GB of one step's logits at the
- * 8B drafter's shape with B*S = 16384; 45 GB for 5 steps). */
+ * activations: about 3.8 GB per step plus 4.3 GB for one step's logit
+ * gradient at the 8B drafter's shape with B*S = 16384; 43.3 GB for 5 steps). */
 int eagle3_ttt_train_workspace_size(const eagle3_dims *dims, int B, int S, int R, size_t *bytes);
 
 /* Training-time-test forward and backward ("EAGLE-3 精读" §1: the target

@@ -57,16 +57,17 @@ def run_gpu_train(shape, Wt, ti, B, S, R, forced, pack):
                                                          for n, g in tr.grads.items()}
 
 
-def compare_grads(gpu, ref, label, rel_bounds=None):
+def compare_grads(gpu, ref, label, rel_bounds=None, abs_bounds=None):
     """Every gradient within REL (or rel_bounds[name] when given) in relative
-    Frobenius norm, and elementwise within the matching scaled bound."""
+    Frobenius norm, and elementwise within ABS_FRAC * max|ref| + 4 REL |ref|
+    (or abs_bounds[name] when given)."""
     for n in G.TRAINED:
         a, r = gpu[n], ref[n]
         assert a.shape == r.shape, (n, a.shape, r.shape)
         assert np.all(np.isfinite(a)), f"{label} {n}: non-finite"
         rb = max(REL, rel_bounds[n]) if rel_bounds else REL
         rel = np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-30)
-        bound = ABS_FRAC * (rb / REL) * np.abs(r).max() + 4 * rb * np.abs(r)
+        bound = abs_bounds[n] if abs_bounds else ABS_FRAC * np.abs(r).max() + 4 * REL * np.abs(r)
         worst = float(np.max(np.abs(a - r) - bound))
         say(f"  {label} {n}: rel {rel:.2e} (bound {rb:.2e}) worst-excess {worst:.2e}")
         assert rel <= rb, f"{label} {n}: relative error {rel}"

@@ -4,7 +4,8 @@
   128256) on a slice the oracle can afford (one sequence of 64 tokens, five
   forced steps): every gradient against the fp64 autograd oracle, within
   twice the distance of the oracle's fp32-product, bf16-gradient variant from
-  it (at least the tolerance of test_gpu_ttt_grad).
+  it, in relative Frobenius norm (at least the tolerance of
+  test_gpu_ttt_grad) and in the largest entry.
 * At the benchmark's full size (8 x 2048 tokens, five self-fed steps, packed
   weights: the launch configuration bench.py times), properties that hold at
   any size:
@@ -78,8 +79,9 @@ def test_c5_train_full_model_shape_vs_oracle(lib):
     # 1e-3; the variant shows how far: the GPU may lie twice as far.
     bounds = {n: 2 * np.linalg.norm(var["grads"][n] - ref["grads"][n]) / np.linalg.norm(ref["grads"][n])
               for n in G.TRAINED}
+    abs_bounds = {n: 2 * np.abs(var["grads"][n] - ref["grads"][n]).max() for n in G.TRAINED}
     np.testing.assert_allclose(gloss, ref["loss"], rtol=1e-2, atol=2e-2)
-    compare_grads({n: g.astype(np.float64) for n, g in gg.items()}, ref["grads"], "8B-shape", bounds)
+    compare_grads({n: g.astype(np.float64) for n, g in gg.items()}, ref["grads"], "8B-shape", bounds, abs_bounds)
 
 
 @pytest.mark.timeout(900)
