@@ -205,6 +205,49 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   if (npre >= 3) bg_wait_copies<8>();
   else bg_wait_copies<0>();
   bg_barrier();
+#ifndef E3_BG_PINGPONG
+#define E3_BG_PINGPONG 1
+#endif
+#if E3_BG_PINGPONG
+  // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) one phase
+  // apart: while one group multiplies from registers at raised priority,
+  // the other reads its next operands from LDS and issues copies.  Every
+  // wave passes the same number of barriers (the lagging group's extra one
+  // first, the leading group's last).
+#if E3_BG_PINGPONG == 2
+  const int grp = wave & 1;
+#else
+  const int grp = wave >> 2;
+#endif
+  if (grp == 1) bg_barrier();
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + BG_NSTAGE - 1 < nk) issue_stage(ks + BG_NSTAGE - 1);
+    U4 b[BG_NJ], a[8];
+    {
+      const uint4* sa = smem + (size_t)(ks % BG_NSTAGE) * BG_STAGE_U4 + lane;
+      const uint4* sb = sa + BG_FRAGS * 64;
+#pragma unroll
+      for (int j = 0; j < BG_NJ; ++j) b[j].u = sb[(wn * BG_NJ + j) << 6];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i].u = sa[(wm * 8 + i) << 6];
+    }
+    if (ks + BG_NSTAGE - 1 < nk) bg_wait_copies<8>();
+    else bg_wait_copies<0>();
+    bg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < BG_NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i].v, b[j].v, acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    bg_barrier();
+  }
+  if (grp == 0) bg_barrier();
+  (void)compute_stage;
+#else
   for (int ks = 0; ks < nk; ++ks) {
     if (ks + BG_NSTAGE - 1 < nk) issue_stage(ks + BG_NSTAGE - 1);
     compute_stage(ks);
@@ -212,6 +255,7 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
     else bg_wait_copies<0>();
     bg_barrier();
   }
+#endif
   // lane l holds C[rowbase + 16 i + 4(l/16) + e][n of column tile colbase16 + j, slot l%16]
   EpiHook<Epi>::run(epi, acc, pre, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
 }
