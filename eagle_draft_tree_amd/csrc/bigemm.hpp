@@ -10,12 +10,13 @@
 // 32 fragment is 64 lanes x 16 bytes; lane l holds row l%16, k-slice
 // 8(l/16)) by direct global -> LDS copies (no VGPR staging), so an MFMA
 // operand is one linear, conflict-free 16-byte LDS read per lane.  Four
-// stages of LDS (128 KB) keep three k steps of copies in flight while one
-// is computed; inside a step the next A fragment is read while the current
-// one feeds its MFMAs.
+// stages of LDS (128 KB) keep three k steps of copies in flight.  The k loop
+// is a ping-pong of two wave groups one phase apart (see k_loop), and the
+// launch is persistent: one block per compute unit walks its tiles, copying
+// the next tile's first stages while the current tile's epilogue runs.
 //
-// Block order: 8 row tiles share a column tile (grouped order), and block
-// ids are remapped so that consecutive logical tiles run on the same XCD
+// Tile order: 8 row tiles share a column tile (grouped order), and tiles
+// are dealt so that consecutive logical tiles run on the same XCD
 // (hardware dispatch places block b on XCD b % 8) and share its L2.
 #pragma once
 #include <type_traits>
@@ -25,6 +26,10 @@
 #include "timing.hpp"
 
 namespace e3 {
+
+#ifndef E3_BG_PERSIST
+#define E3_BG_PERSIST 1
+#endif
 
 constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32;
 constexpr int BG_THREADS = 512;                   // 8 waves: 2 (rows) x 4 (columns)
@@ -111,36 +116,35 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   const int nt16 = N / 16;
   const int ntn = (nt16 + 15) / 16;
   const int ntm = (M + BG_BM - 1) / BG_BM;
-  const int nb = gridDim.x;
-  int bid = blockIdx.x;
+  // Tiles: ntm x ntn of 256 x 256.  Virtual block vb (the launch's block id,
+  // or with a persistent launch every gridDim.x-th one from it) -> tile.
+  const int ntiles = ntm * ntn;
+  const int nchunks = K / 32;
+  auto tile_of = [&](int vb, int& bm, int& bn) {
+    int bid = vb;
 #ifndef E3_BG_MAP
 #define E3_BG_MAP 0
 #endif
 #if E3_BG_MAP != 3
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
 #endif
 #if E3_BG_MAP == 1
-  const int GROUP = 16;
+    const int GROUP = 16;
 #elif E3_BG_MAP == 2
-  const int GROUP = 4;
+    const int GROUP = 4;
 #elif E3_BG_MAP == 5
-  const int GROUP = 32;
+    const int GROUP = 32;
 #else
-  const int GROUP = 8;
+    const int GROUP = 8;
 #endif
-  const int per_group = GROUP * ntn;
-  const int first_m = (bid / per_group) * GROUP;
-  const int gsz = min(GROUP, ntm - first_m);
-  const int bm = first_m + (bid % per_group) % gsz;
-  const int bn = (bid % per_group) / gsz;
-  const int nchunks = K / 32;
+    const int per_group = GROUP * ntn;
+    const int first_m = (bid / per_group) * GROUP;
+    const int gsz = min(GROUP, ntm - first_m);
+    bm = first_m + (bid % per_group) % gsz;
+    bn = (bid % per_group) / gsz;
+  };
 
   f32x4 acc[8][BG_NJ];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < BG_NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const typename EpiHook<Epi>::T pre = EpiHook<Epi>::pre(epi, bm * BG_BM + wm * 128, lane, M);
 
   // Copy sources.  Per stage (32 k) wave w copies A fragments (m-tiles 2w,
   // 2w+1) and B fragments (n-tiles 2w, 2w+1); lane l of a fragment is row
@@ -148,22 +152,27 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
   // read the last valid ones (their results are dropped by the epilogue).
   const bf16* asrc[2];
   const bf16* bsrc[2];
+  auto set_sources = [&](int bm, int bn) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int mt = wave * 2 + h;
-    if (APACK) {
-      const int mtc = min(bm * (BG_BM / 16) + mt, (M - 1) >> 4);
-      asrc[h] = A + ((size_t)mtc * nchunks * 64 + lane) * 8;
-    } else {
-      const int row = min(bm * BG_BM + mt * 16 + (lane & 15), M - 1);
-      asrc[h] = A + (size_t)row * lda + 8 * (lane >> 4);
+    for (int h = 0; h < 2; ++h) {
+      const int mt = wave * 2 + h;
+      if (APACK) {
+        const int mtc = min(bm * (BG_BM / 16) + mt, (M - 1) >> 4);
+        asrc[h] = A + ((size_t)mtc * nchunks * 64 + lane) * 8;
+      } else {
+        const int row = min(bm * BG_BM + mt * 16 + (lane & 15), M - 1);
+        asrc[h] = A + (size_t)row * lda + 8 * (lane >> 4);
+      }
+      const int ntile = min(bn * 16 + wave * 2 + h, nt16 - 1);
+      if (PACKED)
+        bsrc[h] = W + ((size_t)ntile * nchunks * 64 + lane) * 8;
+      else
+        bsrc[h] = W + (size_t)map(ntile, lane & 15) * K + 8 * (lane >> 4);
     }
-    const int ntile = min(bn * 16 + wave * 2 + h, nt16 - 1);
-    if (PACKED)
-      bsrc[h] = W + ((size_t)ntile * nchunks * 64 + lane) * 8;
-    else
-      bsrc[h] = W + (size_t)map(ntile, lane & 15) * K + 8 * (lane >> 4);
-  }
+  };
+  int vb = blockIdx.x, bm, bn;
+  tile_of(vb, bm, bn);
+  set_sources(bm, bn);
   const uint32_t lds0 = lds_addr(smem);
   auto issue_stage = [&](int ks) {
     const uint32_t sa = lds0 + (uint32_t)((ks % BG_NSTAGE) * BG_STAGE_U4 * 16);
@@ -178,95 +187,102 @@ __global__ __launch_bounds__(BG_THREADS) void big_gemm_kernel(const bf16* __rest
         dma16(bsrc[h] + ks * BG_BK, sb + f);
     }
   };
-  // One stage: 8 steps (m-tile i) of BG_NJ MFMAs; the next A fragment is
-  // read while the current one feeds its MFMAs.
-  auto compute_stage = [&](int ks) {
-    const uint4* sa = smem + (size_t)(ks % BG_NSTAGE) * BG_STAGE_U4 + lane;
-    const uint4* sb = sa + BG_FRAGS * 64;
-    U4 b[BG_NJ], a[2];
-#pragma unroll
-    for (int j = 0; j < BG_NJ; ++j) b[j].u = sb[(wn * BG_NJ + j) << 6];
-    a[0].u = sa[(wm * 8) << 6];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i + 1 < 8) a[(i + 1) & 1].u = sa[(wm * 8 + i + 1) << 6];
-#pragma unroll
-      for (int j = 0; j < BG_NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1].v, b[j].v, acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Pipeline: stages s+1..s+3 are being copied while stage s is computed.
-  // Each wave has 4 copies per stage in flight; before the barrier that
-  // ends step s it waits until stage s+1's copies have landed.
+  // The k loop.  Two wave groups, waves 0-3 and 4-7 (the hardware places
+  // waves w and w+4 on one SIMD), run one phase apart: while one group
+  // multiplies its k-step from registers at raised priority, the other reads
+  // its next k-step's operands from LDS into registers and issues its
+  // copies, so each SIMD always has a wave feeding the matrix pipe.  Every
+  // wave passes the same number of barriers (the lagging group's extra one
+  // first, the leading group's last).  Four LDS stages: stages s+1..s+3 are
+  // being copied while stage s is read; before the barrier that ends its
+  // read phase a wave waits until its copies of stage s+1 have landed.
   const int nk = K / BG_BK;
   const int npre = nk < BG_NSTAGE - 1 ? nk : BG_NSTAGE - 1;
+  const int grp = wave >> 2;
+  auto k_loop = [&]() {
+    if (grp == 1) bg_barrier();
+    for (int ks = 0; ks < nk; ++ks) {
+      U4 b[BG_NJ], a[8];
+      {
+        const uint4* sa = smem + (size_t)(ks % BG_NSTAGE) * BG_STAGE_U4 + lane;
+        const uint4* sb = sa + BG_FRAGS * 64;
+#pragma unroll
+        for (int j = 0; j < BG_NJ; ++j) b[j].u = sb[(wn * BG_NJ + j) << 6];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i].u = sa[(wm * 8 + i) << 6];
+      }
+      if (ks + BG_NSTAGE - 1 < nk) {
+        issue_stage(ks + BG_NSTAGE - 1);
+        bg_wait_copies<8>();  // stages ks+2, ks+3 may still be in flight
+      } else {
+        bg_wait_copies<0>();
+      }
+      bg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < BG_NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i].v, b[j].v, acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      bg_barrier();
+    }
+    if (grp == 0) bg_barrier();
+  };
+
+  typename EpiHook<Epi>::T pre = EpiHook<Epi>::pre(epi, bm * BG_BM + wm * 128, lane, M);
   for (int ks = 0; ks < npre; ++ks) issue_stage(ks);
   if (npre >= 3) bg_wait_copies<8>();
   else bg_wait_copies<0>();
   bg_barrier();
-#ifndef E3_BG_PINGPONG
-#define E3_BG_PINGPONG 1
-#endif
-#if E3_BG_PINGPONG
-  // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) one phase
-  // apart: while one group multiplies from registers at raised priority,
-  // the other reads its next operands from LDS and issues copies.  Every
-  // wave passes the same number of barriers (the lagging group's extra one
-  // first, the leading group's last).
-#if E3_BG_PINGPONG == 2
-  const int grp = wave & 1;
-#else
-  const int grp = wave >> 2;
-#endif
-  if (grp == 1) bg_barrier();
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + BG_NSTAGE - 1 < nk) issue_stage(ks + BG_NSTAGE - 1);
-    U4 b[BG_NJ], a[8];
-    {
-      const uint4* sa = smem + (size_t)(ks % BG_NSTAGE) * BG_STAGE_U4 + lane;
-      const uint4* sb = sa + BG_FRAGS * 64;
-#pragma unroll
-      for (int j = 0; j < BG_NJ; ++j) b[j].u = sb[(wn * BG_NJ + j) << 6];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[i].u = sa[(wm * 8 + i) << 6];
-    }
-    if (ks + BG_NSTAGE - 1 < nk) bg_wait_copies<8>();
-    else bg_wait_copies<0>();
-    bg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
+  // One tile per block, or (persistent launch) every gridDim.x-th tile: the
+  // next tile's first stages are copied while this tile's epilogue runs.
+  for (;;) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < BG_NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i].v, b[j].v, acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < BG_NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    k_loop();
+    const int bm_c = bm, bn_c = bn;
+    vb += E3_BG_PERSIST ? (int)gridDim.x : ntiles;
+    const bool more = vb < ntiles;
+    if (more) {
+      tile_of(vb, bm, bn);
+      set_sources(bm, bn);
+      for (int ks = 0; ks < npre; ++ks) issue_stage(ks);
+    }
+    // lane l holds C[rowbase + 16 i + 4(l/16) + e][n of column tile colbase16 + j, slot l%16]
+    EpiHook<Epi>::run(epi, acc, pre, bm_c * BG_BM + wm * 128, bn_c * 16 + wn * BG_NJ, lane, M, nt16);
+    if (!more) break;
+    pre = EpiHook<Epi>::pre(epi, bm * BG_BM + wm * 128, lane, M);
+    bg_wait_copies<0>();
     bg_barrier();
   }
-  if (grp == 0) bg_barrier();
-  (void)compute_stage;
-#else
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + BG_NSTAGE - 1 < nk) issue_stage(ks + BG_NSTAGE - 1);
-    compute_stage(ks);
-    if (ks + BG_NSTAGE - 1 < nk) bg_wait_copies<8>();  // stages ks+2, ks+3 may still be in flight
-    else bg_wait_copies<0>();
-    bg_barrier();
-  }
-#endif
-  // lane l holds C[rowbase + 16 i + 4(l/16) + e][n of column tile colbase16 + j, slot l%16]
-  EpiHook<Epi>::run(epi, acc, pre, bm * BG_BM + wm * 128, bn * 16 + wn * BG_NJ, lane, M, nt16);
 }
 
 // Launch C = A . W^T on `st`.  apack: A in fragment order (frag_off) instead
 // of row-major with stride lda; packed: W in packed fragment order (else
 // row-major through `map`).  kc >= 0: timed as that class's principal kernel.
+// Compute units of the current device (queried once per process).
+inline int bg_cus() {
+  static int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return v;
+  }();
+  return n;
+}
+
 template <class Epi>
 inline hipError_t bg_launch(const bf16* A, int lda, bool apack, int M, const void* W, bool packed, int N, int K,
                             RowMap map, Epi epi, hipStream_t st, int kc = -1) {
-  const int grid = bg_grid(M, N);
+  int grid = bg_grid(M, N);
+  // persistent: one block per compute unit (a multiple of the 8 XCDs keeps
+  // each block on the XCD its tiles are mapped to)
+  if (E3_BG_PERSIST && grid > bg_cus() && bg_cus() % 8 == 0) grid = bg_cus();
   const bf16* Wb = (const bf16*)W;
   const dim3 g(grid), b(BG_THREADS);
   if (packed && apack) launch_timed(kc, big_gemm_kernel<true, true, Epi>, g, b, 0, st, A, lda, M, Wb, N, K, map, epi);
