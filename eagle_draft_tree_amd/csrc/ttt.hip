@@ -446,8 +446,8 @@ __global__ __launch_bounds__(1024) void ttt_loss_kernel(const float* __restrict_
 // `wpb` query heads that share one kv head, sequence b); wave w takes query
 // head blockIdx.y * wpb + w.  Scores are computed
 // transposed, S^T = K Q^T, so that the probabilities come out of the MFMA in
-// the B-operand layout of O^T = V^T P^T; P is split into bf16 hi + lo parts
-// (two MFMAs) so that P.V keeps about 16 bits of the probabilities.  Causal
+// the B-operand layout of O^T = V^T P^T; P enters as bf16 (the output is
+// rounded to bf16 next, which dominates the error of P's rounding).  Causal
 // blocks of 64 step-1 keys use online softmax; afterwards each query folds
 // in its own chain keys (j', i) with plain FMAs.
 template <int HD>
@@ -534,24 +534,9 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       // B operand P^T: k-slots 8 q4 + e <- key 32kc + 4 q4 + e, slots 8 q4 + 4 + e <- key 32kc + 16 + 4 q4 + e
-      U4 phi[2], plo[2];
+      U4 pb[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            const float p0 = st[2 * kc + hh][nt][2 * e2], p1 = st[2 * kc + hh][nt][2 * e2 + 1];
-            const bf16 h0 = f2bf(p0), h1 = f2bf(p1);
-            const bf16 l0 = f2bf(p0 - bf2f(h0)), l1 = f2bf(p1 - bf2f(h1));
-            hw[2 * hh + e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lw[2 * hh + e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-          }
-        }
-        phi[nt].u = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        plo[nt].u = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
+      for (int nt = 0; nt < 2; ++nt) pb[nt] = pack_b_from_acc(st[2 * kc][nt], st[2 * kc + 1][nt]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const bf16* vp = vbase + (size_t)(16 * t + ml) * S + kb * 64 + 32 * kc + 4 * q4;
@@ -559,10 +544,8 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
         U4 vf;
         vf.u = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, phi[nt].v, o[t][nt], 0, 0, 0);
-          o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, plo[nt].v, o[t][nt], 0, 0, 0);
-        }
+        for (int nt = 0; nt < 2; ++nt)
+          o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pb[nt].v, o[t][nt], 0, 0, 0);
       }
     }
   }
@@ -628,7 +611,7 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 // ds_read_b64_tr_b16.  16-byte chunk c of key row r sits at slot
 // c ^ (r % chunks-per-row), so the 16 rows of a fragment read distinct
 // banks.  The per-wave arithmetic (MFMA operands, the online softmax, the P
-// hi/lo split, the chain keys) is that of ttt_attn_kernel, in the same order.
+// packing, the chain keys) is that of ttt_attn_kernel, in the same order.
 
 template <int HD, int G>
 __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
@@ -744,23 +727,9 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         // B operand P^T: k-slots 8 q4 + e <- key 32kc + 4 q4 + e, slots 8 q4 + 4 + e <- key 32kc + 16 + 4 q4 + e
-        U4 phi[2], plo[2];
+        U4 pb[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              const float p0 = st[2 * kc + hh][nt][2 * e2], p1 = st[2 * kc + hh][nt][2 * e2 + 1];
-              const uint32_t hh2 = f2bf2(p0, p1);
-              hw[2 * hh + e2] = hh2;
-              lw[2 * hh + e2] = f2bf2(p0 - __uint_as_float(hh2 << 16), p1 - __uint_as_float(hh2 & 0xffff0000u));
-            }
-          }
-          phi[nt].u = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          plo[nt].u = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
+        for (int nt = 0; nt < 2; ++nt) pb[nt] = pack_b_from_acc(st[2 * kc][nt], st[2 * kc + 1][nt]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           // V^T fragment: dim 16t + ml, keys 32kc + 4q4 + j and 32kc + 16 + 4q4 + j (j < 4): source lane
@@ -775,10 +744,8 @@ __global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
           __builtin_memcpy(&vf.u.x, &va, 8);
           __builtin_memcpy(&vf.u.z, &vb, 8);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, phi[nt].v, o[t][nt], 0, 0, 0);
-            o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, plo[nt].v, o[t][nt], 0, 0, 0);
-          }
+          for (int nt = 0; nt < 2; ++nt)
+            o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pb[nt].v, o[t][nt], 0, 0, 0);
         }
       }
     }

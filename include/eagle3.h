@@ -354,7 +354,7 @@ int eagle3_verify_noalloc(int B, int m, int V, int Dmax, const int32_t *v_tok, c
  * 128 or 64, d and ffn multiples of 64, d <= 8192, S a multiple of 64
  * (EAGLE3_EUNSUPPORTED otherwise); token ids must lie in [0, vocab).
  * Precision: bf16 operands, fp32 accumulation; the attention probabilities
- * enter P.V as a bf16 hi + lo pair; log-sum-exp merged in fp64.  The
+ * enter P.V in bf16; log-sum-exp merged in fp64.  The
  * EAGLE-3.1 norm variants (norm_fc, post-norm) are not supported here
  * (EAGLE3_EUNSUPPORTED).
  * ws: eagle3_ttt_workspace_size bytes, no initialisation needed.  All
