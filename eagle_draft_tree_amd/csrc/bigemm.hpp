@@ -323,7 +323,12 @@ struct BEpiStoreF {
 };
 
 // out = in + C (fp32, plain map): the residual update of the state stream
-// (in == out updates it in place).
+// (in == out updates it in place).  A tile that lies wholly inside the matrix
+// takes branch-free code that loads the residual values of row group i + 1
+// before it stores group i: out may be in itself, so the compiler keeps a
+// load behind the previous store, and guarded load, wait and store per
+// element cost a memory round trip each (128 per lane and tile).  Each element
+// is still read before it is written, so the in-place case holds.
 struct BEpiAdd {
   const float* in;
   float* out;
@@ -331,6 +336,35 @@ struct BEpiAdd {
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
     const int m = lane & 15;
+    if (rowbase + 128 <= M && colbase16 + BG_NJ <= nt16) {
+      const float* ip = in + (size_t)(rowbase + 4 * (lane >> 4)) * ld + colbase16 * 16 + m;
+      float* op = out + (size_t)(rowbase + 4 * (lane >> 4)) * ld + colbase16 * 16 + m;
+      float cur[BG_NJ][4], nxt[BG_NJ][4];
+#pragma unroll
+      for (int j = 0; j < BG_NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[j][e] = ip[(size_t)e * ld + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + 1 < 8) {
+#pragma unroll
+          for (int j = 0; j < BG_NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nxt[j][e] = ip[(size_t)(16 * (i + 1) + e) * ld + 16 * j];
+        }
+#pragma unroll
+        for (int j = 0; j < BG_NJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) op[(size_t)(16 * i + e) * ld + 16 * j] = cur[j][e] + acc[i][j][e];
+        if (i + 1 < 8) {
+#pragma unroll
+          for (int j = 0; j < BG_NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur[j][e] = nxt[j][e];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);

@@ -231,9 +231,58 @@ struct BEpiSwiGLUBwd {
   const float2* gu;  // [M][F]
   bf16* dgu;         // fragment order [M][2F]
   int F;
+  // d gate at g[0], d up at g[up]
+  __device__ __forceinline__ static void put(float dz, float2 p, bf16* g, size_t up) {
+    const float sg = 1.f / (1.f + expf(-p.x));
+    g[0] = f2bf(dz * p.y * sg * (1.f + p.x * (1.f - sg)));
+    g[up] = f2bf(dz * p.x * sg);
+  }
   __device__ __forceinline__ void operator()(const BGAcc& acc, int rowbase, int colbase16, int lane, int M,
                                              int nt16) const {
     const int m = lane & 15, nkc = (2 * F) >> 5;
+    const size_t up = (size_t)(F >> 5) * 512;  // F % 32 == 0: the up half starts a fragment column
+    if (rowbase + 128 <= M && colbase16 + BG_NJ <= nt16 && !(rowbase & 15) && !(colbase16 & 1)) {
+      // A tile wholly inside the matrix: branch-free, the (gate, up) pairs of
+      // the next half row group (two column tiles) load while this one is
+      // stored, so the loads are not each waited for behind a store.  Row
+      // group i is fragment band rowbase / 16 + i; column tile j is fragment
+      // column colbase16 / 2 + j / 2, 8-column half j % 2 at +256.
+      const float2* gp = gu + (size_t)(rowbase + 4 * (lane >> 4)) * F + colbase16 * 16 + m;
+      bf16* dp = dgu + ((size_t)(rowbase >> 4) * nkc + (colbase16 >> 1)) * 512 +
+                 (4 * (lane >> 4) + 16 * (m >> 3)) * 8 + (m & 7);
+      const size_t band = (size_t)nkc * 512;
+      float2 cur[2][4], nxt[2][4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[jj][e] = gp[(size_t)e * F + 16 * jj];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 1, j0 = 2 * (q & 1);
+        if (q + 1 < 16) {
+          const int i1 = (q + 1) >> 1, j1 = 2 * ((q + 1) & 1);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nxt[jj][e] = gp[(size_t)(16 * i1 + e) * F + 16 * (j1 + jj)];
+          __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this group's stores
+        }
+        bf16* di = dp + i * band;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = j0 + jj;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) put(acc[i][j][e], cur[jj][e], di + (j >> 1) * 512 + (j & 1) * 256 + e * 8, up);
+        }
+        if (q + 1 < 16) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur[jj][e] = nxt[jj][e];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row0 = rowbase + 16 * i + 4 * (lane >> 4);
@@ -246,11 +295,7 @@ struct BEpiSwiGLUBwd {
         for (int e = 0; e < 4; ++e) {
           const int row = row0 + e;
           if (row >= M) continue;
-          const float2 p = gu[(size_t)row * F + f];
-          const float sg = 1.f / (1.f + expf(-p.x));
-          const float dz = acc[i][j][e];
-          dgu[frag_off(row, f, nkc)] = f2bf(dz * p.y * sg * (1.f + p.x * (1.f - sg)));
-          dgu[frag_off(row, F + f, nkc)] = f2bf(dz * p.x * sg);
+          put(acc[i][j][e], gu[(size_t)row * F + f], dgu + frag_off(row, f, nkc), up);
         }
       }
     }
