@@ -92,6 +92,13 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} not built: run eagle_draft_tree_amd/build.py")
+    # torch ships its own HIP runtime under the same soname; when torch is
+    # used at all it must be loaded first, so that the library binds to that
+    # runtime rather than bringing in a second one (which then finds no device)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I, SZ = vp, ctypes.c_int, ctypes.c_size_t
     sigs = {

@@ -603,10 +603,11 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 
 // Step-1 causal attention with the K/V blocks shared through LDS: workgroup
 // = (sequence b, KV head g, block of QB query rows) with all G query heads of
-// the group, eight waves (head g*G + w%G, 32 rows of the block each).  Keys
-// come in blocks of 64; the block's K and V rows ([M][Hkv][hd] row-major)
-// are copied once into LDS by direct global -> LDS copies (two stages, the
-// next block in flight while this one is computed) and read by every wave:
+// the group, ta_waves(G, TA_FWD_WAVES) waves (head g*G + w%G, 32 rows of the
+// block each).  Keys come in blocks of 64; the block's K and V rows
+// ([M][Hkv][hd] row-major) are copied once into LDS by direct global -> LDS
+// copies (two stages, the next block in flight while this one is computed)
+// and read by every wave:
 // K fragments with ds_read_b128, V^T fragments with the transpose read
 // ds_read_b64_tr_b16.  16-byte chunk c of key row r sits at slot
 // c ^ (r % chunks-per-row), so the 16 rows of a fragment read distinct
@@ -614,15 +615,15 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 // packing, the chain keys) is that of ttt_attn_kernel, in the same order.
 
 template <int HD, int G>
-__global__ __launch_bounds__(TA_WAVES * 64) void ttt_attn_lds_kernel(
+__global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdgpu_waves_per_eu(2))) void ttt_attn_lds_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K1, const bf16* __restrict__ V1,
     const bf16* __restrict__ KC, const bf16* __restrict__ VC, int nchain, size_t chain_stride,
     bf16* __restrict__ out, int S, int hq, int hkv, float scale, float* __restrict__ lse) {
   constexpr int NC = HD / 32, NT = HD / 16, CPR = HD / 8;  // 16-byte chunks per row
-  constexpr int RG = TA_WAVES / G, QB = 32 * RG, KB = 64;
+  constexpr int W = ta_waves(G, TA_FWD_WAVES), RG = W / G, QB = 32 * RG, KB = 64;
   constexpr int BLK = KB * CPR;                    // 16-byte chunks per K (or V) block
-  constexpr int NDMA = 2 * BLK / 64 / TA_WAVES;    // copies per wave per stage
-  static_assert(NDMA * 64 * TA_WAVES == 2 * BLK, "copies split evenly over the waves");
+  constexpr int NDMA = 2 * BLK / 64 / W;           // copies per wave per stage
+  static_assert(W % G == 0 && NDMA * 64 * W == 2 * BLK, "whole row groups; copies split evenly over the waves");
   __shared__ uint4 sm[2][2][BLK];  // [stage][K, V][row * CPR + slot]
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -878,11 +879,11 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
       const float scale = (float)(1.0 / sqrt((double)hd));
       float* lse = sv ? sv->lse + (size_t)(j - 1) * M * hq : nullptr;
       if (lds_attn) {
-        const int qbr = 32 * (TA_WAVES / gq);
+        const int qbr = 32 * (ta_waves(gq, TA_FWD_WAVES) / gq);
         const dim3 grid((S + qbr - 1) / qbr, hkv, B);
-#define E3_TTA(HDV, GV) \
-  ttt_attn_lds_kernel<HDV, GV><<<grid, TA_WAVES * 64, 0, st>>>(q, L.k1, L.v1t, L.kc, L.vc, j - 1, (size_t)M * kvd, a, S, \
-                                                               hq, hkv, scale, lse)
+#define E3_TTA(HDV, GV)                                                                     \
+  ttt_attn_lds_kernel<HDV, GV><<<grid, ta_waves(GV, TA_FWD_WAVES) * 64, 0, st>>>(q, L.k1, L.v1t, L.kc, L.vc, j - 1, \
+                                                                  (size_t)M * kvd, a, S, hq, hkv, scale, lse)
         if (hd == 128) {
           if (gq == 1) E3_TTA(128, 1);
           else if (gq == 2) E3_TTA(128, 2);

@@ -391,23 +391,23 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const bf16* __restrict__
 }
 
 // dQ over the step-1 keys, the forward kernel's layout: workgroup = (block
-// of QB query rows, kv head g, sequence b), eight waves (head g*G + w%G, 32
-// rows each); K and V blocks of 64 keys staged in LDS by direct copies (two
+// of QB query rows, kv head g, sequence b), ta_waves(G, TA_DQ_WAVES) waves
+// (head g*G + w%G, 32 rows each); K and V blocks of 64 keys staged in LDS by direct copies (two
 // stages).  Per key block: S^T = K Q^T and dP^T = V dO^T (keys x queries),
 // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T with K^T read transposed from LDS.
 // Then the chain part (dq_chain), the scale, the inverse RoPE at position
 // i + pos_off, and bf16 stores into dqkv's q columns (fragment order).
 template <int HD, int G>
-__global__ __launch_bounds__(TA_WAVES * 64) void attn_dq_kernel(
+__global__ __launch_bounds__(ta_waves(G, TA_DQ_WAVES) * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ Dd, const bf16* __restrict__ K1, const bf16* __restrict__ V1,
     const float* __restrict__ dq_chain, const float2* __restrict__ rope, int pos_off, bf16* __restrict__ dqkv,
     int nkc_qkv, int S, int hq, int hkv, float scale) {
   constexpr int NC = HD / 32, NT = HD / 16, CPR = HD / 8;
-  constexpr int RG = TA_WAVES / G, QB = 32 * RG, KB = 64;
+  constexpr int W = ta_waves(G, TA_DQ_WAVES), RG = W / G, QB = 32 * RG, KB = 64;
   constexpr int BLK = KB * CPR;
-  constexpr int NDMA = 2 * BLK / 64 / TA_WAVES;
-  static_assert(NDMA * 64 * TA_WAVES == 2 * BLK, "copies split evenly over the waves");
+  constexpr int NDMA = 2 * BLK / 64 / W;
+  static_assert(W % G == 0 && NDMA * 64 * W == 2 * BLK, "whole row groups; copies split evenly over the waves");
   __shared__ uint4 sm[2][2][BLK];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -950,8 +950,8 @@ int ttt_train(const eagle3_dims& dm, const eagle3_weights& w, const void* feats,
     attn_prep_kernel<HDV, GV><<<(M * hkv + 3) / 4, 256, 0, st>>>(q, L.da, sv.a + js * M * qd, lse, sv.kc, sv.vc,      \
                                                                  nchain, cstride, M, hq, hkv, scale, L.Dd, L.dqc,     \
                                                                  L.dkc, L.dvc);                                       \
-    constexpr int QB = 32 * (TA_WAVES / GV);                                                                          \
-    attn_dq_kernel<HDV, GV><<<dim3((S + QB - 1) / QB, hkv, B), TA_WAVES * 64, 0, st>>>(                              \
+    constexpr int QB = 32 * (ta_waves(GV, TA_DQ_WAVES) / GV);                                                                      \
+    attn_dq_kernel<HDV, GV><<<dim3((S + QB - 1) / QB, hkv, B), ta_waves(GV, TA_DQ_WAVES) * 64, 0, st>>>(                          \
         q, L.da, lse, L.Dd, sv.k1, sv.v1, nchain ? L.dqc : nullptr, sv.rope, j - 1, L.dqkvf, nqkv / 32, S, hq, hkv,    \
         scale);                                                                                                       \
     attn_dkv_kernel<HDV, GV><<<dim3((S + DKV_KEYS - 1) / DKV_KEYS, hkv, B), 256, 0, st>>>(q, L.da, lse, L.Dd, sv.k1, sv.v1, L.dk1,    \

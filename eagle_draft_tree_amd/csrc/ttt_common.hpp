@@ -48,11 +48,18 @@ __device__ __forceinline__ float row_ss(const TS* src, size_t ld, int r, int n) 
   return row16_sum(ss);
 }
 
-// The rollout-mask attention kernels: eight waves per workgroup; LDS blocks
-// of K/V (or Q/dO) rows, row-major [rows][hd] bf16 with 16-byte chunk c of
-// row r at slot c ^ (r % chunks-per-row), so the 16 rows an MFMA fragment
-// reads sit in distinct banks.
-constexpr int TA_WAVES = 8;
+// The rollout-mask attention kernels: LDS blocks of K/V (or Q/dO) rows,
+// row-major [rows][hd] bf16 with 16-byte chunk c of row r at slot
+// c ^ (r % chunks-per-row), so the 16 rows an MFMA fragment reads sit in
+// distinct banks.  A query-block kernel takes ta_waves(G, W) waves per
+// workgroup (G query heads per kv head): W, or G when a group has more
+// heads.  The forward takes W = 4, one wave per SIMD, so that two workgroups
+// share a compute unit and the barrier after every key block does not hold
+// all of its waves in step (their MFMA and softmax phases then overlap); the
+// dQ kernel keeps W = 8, since with half the waves each wave's share of the
+// copies no longer fits its registers.
+constexpr int ta_waves(int G, int W) { return G > W ? G : W; }
+constexpr int TA_FWD_WAVES = 4, TA_DQ_WAVES = 8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* tta_lds_s16x4;
 
