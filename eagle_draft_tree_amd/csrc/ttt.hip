@@ -611,8 +611,9 @@ __global__ __launch_bounds__(256) void ttt_attn_kernel(const bf16* __restrict__ 
 // K fragments with ds_read_b128, V^T fragments with the transpose read
 // ds_read_b64_tr_b16.  16-byte chunk c of key row r sits at slot
 // c ^ (r % chunks-per-row), so the 16 rows of a fragment read distinct
-// banks.  The per-wave arithmetic (MFMA operands, the online softmax, the P
-// packing, the chain keys) is that of ttt_attn_kernel, in the same order.
+// banks.  The per-wave MFMA operands, P packing and chain keys are those of
+// ttt_attn_kernel; the online softmax runs in base 2 with a lazily moved
+// maximum (TA_RESCALE).
 
 template <int HD, int G>
 __global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdgpu_waves_per_eu(2))) void ttt_attn_lds_kernel(
@@ -665,6 +666,9 @@ __global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdg
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // softmax in base 2: p = 2^(s c2 - mrun) with c2 = scale log2(e), mrun the
+  // running maximum of s c2
+  const float c2 = scale * LOG2EF;
   float mrun[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
   issue(0);
@@ -703,24 +707,29 @@ __global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdg
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float sv = st[mt][nt][e] * scale;
-            if (diag && kb * KB + 16 * mt + 4 * q4 + e > qi) sv = -INFINITY;
-            st[mt][nt][e] = sv;
-            bm = fmaxf(bm, sv);
+            if (diag && kb * KB + 16 * mt + 4 * q4 + e > qi) st[mt][nt][e] = -INFINITY;
+            bm = fmaxf(bm, st[mt][nt][e]);
           }
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mnew = fmaxf(mrun[nt], bm);
-        const float alpha = __expf(mrun[nt] - mnew);
-        mrun[nt] = mnew;
-        lsum[nt] *= alpha;
+        // mrun (log2 units) moves only when the block's maximum exceeds it by
+        // more than TA_RESCALE, so most blocks skip the rescale of o
+        const float bmc = bm * c2;
+        const bool upd = bmc > mrun[nt] + TA_RESCALE;
+        if (__any(upd)) {
+          const float mnew = upd ? bmc : mrun[nt];
+          const float alpha = __builtin_amdgcn_exp2f(mrun[nt] - mnew);
+          mrun[nt] = mnew;
+          lsum[nt] *= alpha;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) o[t][nt] *= alpha;
+          for (int t = 0; t < NT; ++t) o[t][nt] *= alpha;
+        }
+        const float mneg = -mrun[nt];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pv = __expf(st[mt][nt][e] - mnew);
+            const float pv = __builtin_amdgcn_exp2f(fmaf(st[mt][nt][e], c2, mneg));
             st[mt][nt][e] = pv;
             lsum[nt] += pv;
           }
@@ -778,9 +787,9 @@ __global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdg
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
-      const float sv = dot * scale;
+      const float sv = dot * c2;
       const float mnew = fmaxf(mrun[nt], sv);
-      const float alpha = __expf(mrun[nt] - mnew), pv = __expf(sv - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[nt] - mnew), pv = __builtin_amdgcn_exp2f(sv - mnew);
       mrun[nt] = mnew;
       lsum[nt] = lsum[nt] * alpha + (q4 == 0 ? pv : 0.f);
 #pragma unroll
@@ -797,7 +806,7 @@ __global__ __launch_bounds__(ta_waves(G, TA_FWD_WAVES) * 64) __attribute__((amdg
     const float inv = 1.f / L;
     const int row = b * S + i0 + 16 * nt + ml;
     const int nkc = (hq * HD) >> 5;
-    if (lse && q4 == 0) lse[(size_t)h * gridDim.z * S + row] = mrun[nt] + logf(L);  // [hq][M]
+    if (lse && q4 == 0) lse[(size_t)h * gridDim.z * S + row] = mrun[nt] * LN2F + logf(L);  // [hq][M], natural log
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const f32x4 r = o[t][nt] * inv;

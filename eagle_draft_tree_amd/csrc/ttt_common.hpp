@@ -60,6 +60,13 @@ __device__ __forceinline__ float row_ss(const TS* src, size_t ld, int r, int n) 
 // copies no longer fits its registers.
 constexpr int ta_waves(int G, int W) { return G > W ? G : W; }
 constexpr int TA_FWD_WAVES = 4, TA_DQ_WAVES = 8;
+constexpr float LOG2EF = 1.44269504088896340736f, LN2F = 0.69314718055994530942f;
+// The forward's online softmax runs in base 2 with the scale folded into one
+// FMA per score; its running maximum (log2 units) moves only when a key
+// block's maximum exceeds it by more than TA_RESCALE, so most blocks skip
+// rescaling the output, and the unnormalised probabilities stay below 2^8
+// (the final division by their sum is unchanged).
+constexpr float TA_RESCALE = 8.f;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* tta_lds_s16x4;
 
