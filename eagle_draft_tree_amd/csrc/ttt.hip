@@ -150,6 +150,131 @@ __global__ __launch_bounds__(TR) void ttt_norm_kernel(const float* __restrict__ 
   }
 }
 
+// One-pass row kernels for d = 512 NJ (NJ <= 8): a workgroup of RB = 8 waves
+// takes 8 rows, wave w row 8 blockIdx.x + w, lane l columns 512 j + 8 l .. + 8
+// of each 512-column chunk j, so a row is read from memory once and kept in
+// registers (the two-pass kernels above read it twice).  Each output chunk
+// (16 fragments of the 16-row tile, the block's half of their slots) is
+// assembled in LDS and leaves as runs of eight 16-byte slots.
+constexpr int RB1 = 8;
+
+// Chunk j of a fragment-order bf16 matrix with nkc = K / 32 fragment
+// columns: the calling lane's slot (row of its wave, columns 512 j + 8 l ..)
+// goes through stage[j % 2]; one barrier per chunk (a buffer is written again
+// two chunks later, after every thread has passed the barrier in between).
+__device__ __forceinline__ void put_chunk(uint4 (*stage)[64 * RB1], bf16* __restrict__ out, int row0, int nkc, int j,
+                                          uint4 slot) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint4* buf = stage[j & 1];
+  buf[(l >> 2) * (4 * RB1) + (l & 3) * RB1 + w] = slot;
+  __syncthreads();
+  const int t = threadIdx.x, q = t / (4 * RB1), g = (t / RB1) & 3, ww = t % RB1;
+  if (16 * j + q < nkc)
+    ((uint4*)out)[((size_t)(row0 >> 4) * nkc + 16 * j + q) * 64 + (row0 & 15) + ww + 16 * g] = buf[t];
+}
+
+// y = rms(h) * gain, one pass (see above)
+template <int NJ>
+__global__ __launch_bounds__(64 * RB1) void ttt_norm1_kernel(const float* __restrict__ hs, int d,
+                                                             const float* __restrict__ gain, float eps,
+                                                             bf16* __restrict__ y) {
+  __shared__ uint4 stage[2][64 * RB1];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB1;
+  const float* p = hs + (size_t)(row0 + w) * d + 8 * l;
+  float v[NJ][8];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float4 a = *(const float4*)(p + 512 * j), b = *(const float4*)(p + 512 * j + 4);
+    v[j][0] = a.x, v[j][1] = a.y, v[j][2] = a.z, v[j][3] = a.w, v[j][4] = b.x, v[j][5] = b.y, v[j][6] = b.z,
+    v[j][7] = b.w;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(v[j][c], v[j][c], ss);
+  const float inv = (float)(1.0 / sqrt((double)wave_sum(ss) / d + (double)eps));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = v[j][c] * inv * gain[512 * j + 8 * l + c];
+    put_chunk(stage, y, row0, d >> 5, j, pack8(o));
+  }
+}
+
+// x = [rms(emb[t]) * norm_e ; rms(s) * norm_s], one pass (see above)
+template <int NJ>
+__global__ __launch_bounds__(64 * RB1) void ttt_prologue1_kernel(
+    const bf16* __restrict__ emb, const int32_t* __restrict__ tok, const float* __restrict__ hs, int d,
+    const float* __restrict__ ge, const float* __restrict__ gs, float eps, bf16* __restrict__ x) {
+  __shared__ uint4 stage[2][64 * RB1];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB1;
+  const int t = __builtin_amdgcn_readfirstlane(tok[row0 + w]);
+  const bf16* pe = emb + (size_t)t * d + 8 * l;
+  const float* ps = hs + (size_t)(row0 + w) * d + 8 * l;
+  uint4 e[NJ];
+  float v[NJ][8];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    e[j] = *(const uint4*)(pe + 512 * j);
+    const float4 a = *(const float4*)(ps + 512 * j), b = *(const float4*)(ps + 512 * j + 4);
+    v[j][0] = a.x, v[j][1] = a.y, v[j][2] = a.z, v[j][3] = a.w, v[j][4] = b.x, v[j][5] = b.y, v[j][6] = b.z,
+    v[j][7] = b.w;
+  }
+  float se = 0.f, ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float f[8];
+    unpack8(e[j], f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      se = fmaf(f[c], f[c], se);
+      ss = fmaf(v[j][c], v[j][c], ss);
+    }
+  }
+  const float ie = (float)(1.0 / sqrt((double)wave_sum(se) / d + (double)eps));
+  const float is = (float)(1.0 / sqrt((double)wave_sum(ss) / d + (double)eps));
+  const int nkc = (2 * d) >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float f[8], o[8];
+    unpack8(e[j], f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = f[c] * ie * ge[512 * j + 8 * l + c];
+    put_chunk(stage, x, row0, nkc, j, pack8(o));
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = v[j][c] * is * gs[512 * j + 8 * l + c];
+    put_chunk(stage, x, row0, nkc, NJ + j, pack8(o));
+  }
+}
+
+// Launch the one-pass kernel when d is 512, 1024, 2048 or 4096 (rows: a
+// multiple of 8), else the two-pass one.
+inline void ttt_norm(const float* hs, int M, int d, const float* gain, float eps, bf16* y, hipStream_t st) {
+  switch (d) {
+    case 512: ttt_norm1_kernel<1><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
+    case 1024: ttt_norm1_kernel<2><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
+    case 2048: ttt_norm1_kernel<4><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
+    case 4096: ttt_norm1_kernel<8><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
+    default: ttt_norm_kernel<<<M / 16, TR, 0, st>>>(hs, d, gain, eps, y);
+  }
+}
+inline void ttt_prologue(const bf16* emb, const int32_t* tok, const float* hs, int M, int d, const float* ge,
+                         const float* gs, float eps, bf16* x, hipStream_t st) {
+  switch (d) {
+    case 512: ttt_prologue1_kernel<1><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 1024: ttt_prologue1_kernel<2><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 2048: ttt_prologue1_kernel<4><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 4096: ttt_prologue1_kernel<8><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    default: ttt_prologue_kernel<<<M / 16, TR, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x);
+  }
+}
+
 // ------------------------------------------------------------------ GEMM epilogues
 // QKV on MAP_PAIR_HEAD tiles (slots m, m+8 = RoPE pair (p, p + hd/2) of one
 // head, p = 8t + m): RoPE at position (row % S) + pos_off on q and k, then
@@ -873,7 +998,7 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     int32_t* tok_out = j == R ? nullptr : (sv ? sv->tok + (size_t)j * M : L.tok);
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_prologue_kernel<<<M / 16, TR, 0, st>>>((const bf16*)w.emb, tok_in, s_in, d, w.norm_e, w.norm_s, eps, x);
+      ttt_prologue((const bf16*)w.emb, tok_in, s_in, M, d, w.norm_e, w.norm_s, eps, x, st);
       E3_CHECK(hipGetLastError());
     }
     bf16* kdst = j == 1 ? L.k1 : L.kc + (size_t)(j - 2) * M * kvd;
@@ -925,7 +1050,7 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(h1, d, w.norm_ffn, eps, u);
+      ttt_norm(h1, M, d, w.norm_ffn, eps, u, st);
       E3_CHECK(hipGetLastError());
     }
     {
@@ -936,7 +1061,7 @@ int ttt_forward(const eagle3_dims& dm, const eagle3_weights& w, const void* feat
     }
     {
       TimedScope ts(EAGLE3_KC_ROWOPS, st);
-      ttt_norm_kernel<<<M / 16, TR, 0, st>>>(s_out, d, w.norm_out, eps, L.x);
+      ttt_norm(s_out, M, d, w.norm_out, eps, L.x, st);
       E3_CHECK(hipGetLastError());
     }
     {
