@@ -38,7 +38,7 @@ def run_gpu_ttt(shape, Wt, ti, B, S, R, forced, pack):
     return pred.cpu().numpy(), ce.cpu().numpy(), float(loss.item())
 
 
-def compare(shape, W, ti, B, S, R, forced, gp, gce, gloss):
+def compare(shape, W, ti, B, S, R, forced, gp, gce, gloss, tie=TIE):
     tot, cnt, excused, compared = 0.0, 0, 0, 0
     for b in range(B):
         say("  oracle sequence", b)
@@ -59,7 +59,7 @@ def compare(shape, W, ti, B, S, R, forced, gp, gce, gloss):
                 if gp[b, j, i] != o["pred"][j, i]:
                     srt = np.sort(l32[i])[::-1]
                     gap = float(srt[0] - srt[1])
-                    ok = gap <= TIE and l32[i, gp[b, j, i]] >= srt[0] - TIE
+                    ok = gap <= tie and l32[i, gp[b, j, i]] >= srt[0] - tie
                     assert ok, f"pred b={b} step={j + 1} i={i}: gpu {gp[b, j, i]} oracle {o['pred'][j, i]} gap {gap}"
                     excused += 1
                     if not forced:
@@ -105,3 +105,24 @@ def test_ttt_is_deterministic_and_layout_independent(lib):
         np.testing.assert_array_equal(x[0], y[0])
         np.testing.assert_array_equal(x[1], y[1])
         assert x[2] == y[2]
+
+
+def test_ttt_large_scores_move_the_softmax_maximum(lib):
+    """q and k rows of W_qkv scaled by 16 (exact in bf16): attention scores
+    spread by about 50 instead of 0.2, so in later key blocks a row's running
+    maximum of the online softmax jumps by more than its lazy-rescale
+    threshold, on some lanes of a wave and not others, and the rescale of
+    the partial output runs there too (with small scores it runs only at a
+    row's first block).  Attention this close to one-hot passes rounding-level
+    score differences on to the logits: the CE differs from the oracle's by up
+    to about 1e-2 here (with the running maximum moved at every block as much
+    as with the lazy one), so predictions are excused up to that top-2 gap."""
+    shape = tiny_shape(d=256, hq=4, hkv=2, hd=64, ffn=768, vocab=4112, dtype=BF16, theta=10000.0)
+    Wt = gen.gen_weights(shape, seed=3)
+    f = Wt["qkv"].f32().copy()
+    f[: (shape.n_q_heads + shape.n_kv_heads) * shape.head_dim] *= 16.0
+    Wt["qkv"] = gen.Tensor(gen.f32_to_bf16_bits(f), BF16)
+    ti = gen.gen_ttt_inputs(shape, 2, 192, 3, seed=4)
+    say("ttt large scores")
+    gp, gce, gloss = run_gpu_ttt(shape, Wt, ti, 2, 192, 3, True, True)
+    compare(shape, host_weights(Wt), ti, 2, 192, 3, True, gp, gce, gloss, tie=1e-2)
