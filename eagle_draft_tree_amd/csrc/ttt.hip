@@ -150,36 +150,39 @@ __global__ __launch_bounds__(TR) void ttt_norm_kernel(const float* __restrict__ 
   }
 }
 
-// One-pass row kernels for d = 512 NJ (NJ <= 8): a workgroup of RB = 8 waves
-// takes 8 rows, wave w row 8 blockIdx.x + w, lane l columns 512 j + 8 l .. + 8
-// of each 512-column chunk j, so a row is read from memory once and kept in
-// registers (the two-pass kernels above read it twice).  Each output chunk
-// (16 fragments of the 16-row tile, the block's half of their slots) is
-// assembled in LDS and leaves as runs of eight 16-byte slots.
-constexpr int RB1 = 8;
+// One-pass row kernels for d = 512 NJ (NJ <= 8): a workgroup of RB waves
+// takes RB rows (RB = 8 for the norm; 4 for the prologue, whose two rows per
+// wave hold 164 VGPRs, so that three workgroups share a compute unit), wave
+// w row RB blockIdx.x + w, lane l columns 512 j + 8 l .. + 8 of each
+// 512-column chunk j: a row is read from memory once and kept in registers
+// (the two-pass kernels above read it twice).  Each output chunk (16
+// fragments of the 16-row tile, the block's RB rows of their slots) is
+// assembled in LDS and leaves as runs of RB 16-byte slots.
+constexpr int RB_NORM = 8, RB_PRO = 4;
 
 // Chunk j of a fragment-order bf16 matrix with nkc = K / 32 fragment
 // columns: the calling lane's slot (row of its wave, columns 512 j + 8 l ..)
 // goes through stage[j % 2]; one barrier per chunk (a buffer is written again
 // two chunks later, after every thread has passed the barrier in between).
-__device__ __forceinline__ void put_chunk(uint4 (*stage)[64 * RB1], bf16* __restrict__ out, int row0, int nkc, int j,
+template <int RB>
+__device__ __forceinline__ void put_chunk(uint4 (*stage)[64 * RB], bf16* __restrict__ out, int row0, int nkc, int j,
                                           uint4 slot) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint4* buf = stage[j & 1];
-  buf[(l >> 2) * (4 * RB1) + (l & 3) * RB1 + w] = slot;
+  buf[(l >> 2) * (4 * RB) + (l & 3) * RB + w] = slot;
   __syncthreads();
-  const int t = threadIdx.x, q = t / (4 * RB1), g = (t / RB1) & 3, ww = t % RB1;
+  const int t = threadIdx.x, q = t / (4 * RB), g = (t / RB) & 3, ww = t % RB;
   if (16 * j + q < nkc)
     ((uint4*)out)[((size_t)(row0 >> 4) * nkc + 16 * j + q) * 64 + (row0 & 15) + ww + 16 * g] = buf[t];
 }
 
 // y = rms(h) * gain, one pass (see above)
 template <int NJ>
-__global__ __launch_bounds__(64 * RB1) void ttt_norm1_kernel(const float* __restrict__ hs, int d,
+__global__ __launch_bounds__(64 * RB_NORM) void ttt_norm1_kernel(const float* __restrict__ hs, int d,
                                                              const float* __restrict__ gain, float eps,
                                                              bf16* __restrict__ y) {
-  __shared__ uint4 stage[2][64 * RB1];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB1;
+  __shared__ uint4 stage[2][64 * RB_NORM];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB_NORM;
   const float* p = hs + (size_t)(row0 + w) * d + 8 * l;
   float v[NJ][8];
 #pragma unroll
@@ -199,17 +202,17 @@ __global__ __launch_bounds__(64 * RB1) void ttt_norm1_kernel(const float* __rest
     float o[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = v[j][c] * inv * gain[512 * j + 8 * l + c];
-    put_chunk(stage, y, row0, d >> 5, j, pack8(o));
+    put_chunk<RB_NORM>(stage, y, row0, d >> 5, j, pack8(o));
   }
 }
 
 // x = [rms(emb[t]) * norm_e ; rms(s) * norm_s], one pass (see above)
 template <int NJ>
-__global__ __launch_bounds__(64 * RB1) void ttt_prologue1_kernel(
+__global__ __launch_bounds__(64 * RB_PRO) void ttt_prologue1_kernel(
     const bf16* __restrict__ emb, const int32_t* __restrict__ tok, const float* __restrict__ hs, int d,
     const float* __restrict__ ge, const float* __restrict__ gs, float eps, bf16* __restrict__ x) {
-  __shared__ uint4 stage[2][64 * RB1];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB1;
+  __shared__ uint4 stage[2][64 * RB_PRO];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB_PRO;
   const int t = __builtin_amdgcn_readfirstlane(tok[row0 + w]);
   const bf16* pe = emb + (size_t)t * d + 8 * l;
   const float* ps = hs + (size_t)(row0 + w) * d + 8 * l;
@@ -242,14 +245,14 @@ __global__ __launch_bounds__(64 * RB1) void ttt_prologue1_kernel(
     unpack8(e[j], f);
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = f[c] * ie * ge[512 * j + 8 * l + c];
-    put_chunk(stage, x, row0, nkc, j, pack8(o));
+    put_chunk<RB_PRO>(stage, x, row0, nkc, j, pack8(o));
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     float o[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = v[j][c] * is * gs[512 * j + 8 * l + c];
-    put_chunk(stage, x, row0, nkc, NJ + j, pack8(o));
+    put_chunk<RB_PRO>(stage, x, row0, nkc, NJ + j, pack8(o));
   }
 }
 
@@ -257,20 +260,20 @@ __global__ __launch_bounds__(64 * RB1) void ttt_prologue1_kernel(
 // multiple of 8), else the two-pass one.
 inline void ttt_norm(const float* hs, int M, int d, const float* gain, float eps, bf16* y, hipStream_t st) {
   switch (d) {
-    case 512: ttt_norm1_kernel<1><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
-    case 1024: ttt_norm1_kernel<2><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
-    case 2048: ttt_norm1_kernel<4><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
-    case 4096: ttt_norm1_kernel<8><<<M / RB1, 64 * RB1, 0, st>>>(hs, d, gain, eps, y); break;
+    case 512: ttt_norm1_kernel<1><<<M / RB_NORM, 64 * RB_NORM, 0, st>>>(hs, d, gain, eps, y); break;
+    case 1024: ttt_norm1_kernel<2><<<M / RB_NORM, 64 * RB_NORM, 0, st>>>(hs, d, gain, eps, y); break;
+    case 2048: ttt_norm1_kernel<4><<<M / RB_NORM, 64 * RB_NORM, 0, st>>>(hs, d, gain, eps, y); break;
+    case 4096: ttt_norm1_kernel<8><<<M / RB_NORM, 64 * RB_NORM, 0, st>>>(hs, d, gain, eps, y); break;
     default: ttt_norm_kernel<<<M / 16, TR, 0, st>>>(hs, d, gain, eps, y);
   }
 }
 inline void ttt_prologue(const bf16* emb, const int32_t* tok, const float* hs, int M, int d, const float* ge,
                          const float* gs, float eps, bf16* x, hipStream_t st) {
   switch (d) {
-    case 512: ttt_prologue1_kernel<1><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
-    case 1024: ttt_prologue1_kernel<2><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
-    case 2048: ttt_prologue1_kernel<4><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
-    case 4096: ttt_prologue1_kernel<8><<<M / RB1, 64 * RB1, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 512: ttt_prologue1_kernel<1><<<M / RB_PRO, 64 * RB_PRO, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 1024: ttt_prologue1_kernel<2><<<M / RB_PRO, 64 * RB_PRO, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 2048: ttt_prologue1_kernel<4><<<M / RB_PRO, 64 * RB_PRO, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
+    case 4096: ttt_prologue1_kernel<8><<<M / RB_PRO, 64 * RB_PRO, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x); break;
     default: ttt_prologue_kernel<<<M / 16, TR, 0, st>>>(emb, tok, hs, d, ge, gs, eps, x);
   }
 }
