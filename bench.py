@@ -465,6 +465,13 @@ def cycle_bench(w, dr, steps, warmup, n_plant=8, graph=True, lm_rows=None):
     return res, ci, vin
 
 
+def device_info():
+    """The GPU the numbers were taken on: name, architecture, compute units."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count}
+
+
 def ttt_bench(w, dr, steps, warmup):
     """Time the training-time-test forward (B x S tokens, R rollout steps)."""
     import numpy as np
@@ -1074,6 +1081,7 @@ def main():
         r, ti = ttt_bench(C5_8B_TTT, dr8, max(1, min(args.steps, 10)), 1)
         if not args.no_cpu_baseline:
             r["cpu_baseline"] = cpu_baseline_ttt(C5_8B_TTT, Wt8, ti)
+        r["device"] = device_info()
         print(json.dumps(r), flush=True)
         return
     if args.only == "tttb":
@@ -1121,6 +1129,7 @@ def main():
         "kernel_ms_per_cycle": r["kernel_ms_per_cycle"],
         "reporting": r["reporting"],
         "setup_s": round(setup_s, 1),
+        "device": device_info(),
     }
     # the GPU legs first, then every CPU baseline (host work only)
     cpu_jobs = [("main", w, Wt8, ci, vin, None, None)]
