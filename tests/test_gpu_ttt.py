@@ -79,6 +79,9 @@ CASES = [
     ("r1", dict(d=256, hq=2, hkv=2, hd=64, ffn=512, vocab=1040), 1, 64, 1, False, True),
     # query-head groups of 3 take the attention kernel without LDS staging
     ("hd64-gqa3-self", dict(d=384, hq=6, hkv=2, hd=64, ffn=512, vocab=2064), 1, 128, 2, False, True),
+    # widths 1024 and 2048: the one-pass prologue and RMSNorm with two and four 512-column chunks per row
+    ("d1024-forced", dict(d=1024, hq=8, hkv=2, hd=128, ffn=1024, vocab=1040), 1, 64, 2, True, True),
+    ("d2048-forced", dict(d=2048, hq=16, hkv=4, hd=128, ffn=1024, vocab=1024), 1, 64, 2, True, False),
 ]
 
 
