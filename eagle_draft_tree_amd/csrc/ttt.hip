@@ -160,22 +160,6 @@ __global__ __launch_bounds__(TR) void ttt_norm_kernel(const float* __restrict__ 
 // assembled in LDS and leaves as runs of RB 16-byte slots.
 constexpr int RB_NORM = 8, RB_PRO = 4;
 
-// Chunk j of a fragment-order bf16 matrix with nkc = K / 32 fragment
-// columns: the calling lane's slot (row of its wave, columns 512 j + 8 l ..)
-// goes through stage[j % 2]; one barrier per chunk (a buffer is written again
-// two chunks later, after every thread has passed the barrier in between).
-template <int RB>
-__device__ __forceinline__ void put_chunk(uint4 (*stage)[64 * RB], bf16* __restrict__ out, int row0, int nkc, int j,
-                                          uint4 slot) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  uint4* buf = stage[j & 1];
-  buf[(l >> 2) * (4 * RB) + (l & 3) * RB + w] = slot;
-  __syncthreads();
-  const int t = threadIdx.x, q = t / (4 * RB), g = (t / RB) & 3, ww = t % RB;
-  if (16 * j + q < nkc)
-    ((uint4*)out)[((size_t)(row0 >> 4) * nkc + 16 * j + q) * 64 + (row0 & 15) + ww + 16 * g] = buf[t];
-}
-
 // y = rms(h) * gain, one pass (see above)
 template <int NJ>
 __global__ __launch_bounds__(64 * RB_NORM) void ttt_norm1_kernel(const float* __restrict__ hs, int d,

@@ -191,6 +191,95 @@ __global__ __launch_bounds__(TR) void rms_bwd_kernel(const float* __restrict__ v
   }
 }
 
+// The same for d = 512 NJ (NJ <= 8) in one pass: a workgroup of RB_BWD waves
+// takes as many rows, wave w row RB_BWD blockIdx.x + w with lane l holding
+// columns 512 j + 8 l .. + 8 of v and gy in registers (read once; the
+// two-pass kernel above reads both twice); carry is read, updated and written
+// in the same pass, and the optional bf16 copy goes out through LDS in
+// fragment order.  v and gy take about 150 VGPRs, so four rows per workgroup
+// let three workgroups share a compute unit.
+constexpr int RB_BWD = 4;
+template <int NJ>
+__global__ __launch_bounds__(64 * RB_BWD) void rms_bwd1_kernel(
+    const float* __restrict__ v, const float* __restrict__ gy, int ldg, const float* __restrict__ gain, float eps,
+    int d, float* __restrict__ carry, int add, bf16* __restrict__ frag, float* __restrict__ inv_out,
+    const bf16* __restrict__ emb, const int32_t* __restrict__ tok, float* __restrict__ inv_e) {
+  __shared__ uint4 stage[2][64 * RB_BWD];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, row0 = blockIdx.x * RB_BWD, row = row0 + w;
+  const float* pv = v + (size_t)row * d + 8 * l;
+  const float* pg = gy + (size_t)row * ldg + 8 * l;
+  float vv[NJ][8], gg[NJ][8];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float4 a0 = *(const float4*)(pv + 512 * j), a1 = *(const float4*)(pv + 512 * j + 4);
+    const float4 b0 = *(const float4*)(pg + 512 * j), b1 = *(const float4*)(pg + 512 * j + 4);
+    vv[j][0] = a0.x, vv[j][1] = a0.y, vv[j][2] = a0.z, vv[j][3] = a0.w;
+    vv[j][4] = a1.x, vv[j][5] = a1.y, vv[j][6] = a1.z, vv[j][7] = a1.w;
+    gg[j][0] = b0.x, gg[j][1] = b0.y, gg[j][2] = b0.z, gg[j][3] = b0.w;
+    gg[j][4] = b1.x, gg[j][5] = b1.y, gg[j][6] = b1.z, gg[j][7] = b1.w;
+  }
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      ss = fmaf(vv[j][c], vv[j][c], ss);
+      dot = fmaf(gain[512 * j + 8 * l + c] * gg[j][c], vv[j][c], dot);
+    }
+  ss = wave_sum(ss);
+  dot = wave_sum(dot);
+  const float inv = (float)(1.0 / sqrt((double)ss / d + (double)eps));
+  const float coef = inv * inv * inv / (float)d * dot;
+  if (emb) {
+    const bf16* pe = emb + (size_t)__builtin_amdgcn_readfirstlane(tok[row]) * d + 8 * l;
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float f[8];
+      unpack8(*(const uint4*)(pe + 512 * j), f);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) se = fmaf(f[c], f[c], se);
+    }
+    se = wave_sum(se);
+    if (l == 0) inv_e[row] = (float)(1.0 / sqrt((double)se / d + (double)eps));
+  }
+  if (l == 0) inv_out[row] = inv;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float* pc = carry + (size_t)row * d + 512 * j + 8 * l;
+    float cc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (add) {
+      const float4 c0 = *(const float4*)pc, c1 = *(const float4*)(pc + 4);
+      cc[0] = c0.x, cc[1] = c0.y, cc[2] = c0.z, cc[3] = c0.w, cc[4] = c1.x, cc[5] = c1.y, cc[6] = c1.z, cc[7] = c1.w;
+    }
+    float out[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      out[c] = cc[c] + (inv * gain[512 * j + 8 * l + c] * gg[j][c] - coef * vv[j][c]);
+    *(float4*)pc = make_float4(out[0], out[1], out[2], out[3]);
+    *(float4*)(pc + 4) = make_float4(out[4], out[5], out[6], out[7]);
+    if (frag) put_chunk<RB_BWD>(stage, frag, row0, d >> 5, j, pack8(out));
+  }
+}
+
+// rms_bwd_kernel's operation: the one-pass kernel when d is 512, 1024, 2048
+// or 4096 (rows: a multiple of 16), else the two-pass one.
+inline void rms_bwd(const float* v, const float* gy, int ldg, const float* gain, float eps, int M, int d, float* carry,
+                    int add, bf16* frag, float* inv_out, const bf16* emb, const int32_t* tok, float* inv_e,
+                    hipStream_t st) {
+  const dim3 g1(M / RB_BWD), b1(64 * RB_BWD);
+  if (d == 512)
+    rms_bwd1_kernel<1><<<g1, b1, 0, st>>>(v, gy, ldg, gain, eps, d, carry, add, frag, inv_out, emb, tok, inv_e);
+  else if (d == 1024)
+    rms_bwd1_kernel<2><<<g1, b1, 0, st>>>(v, gy, ldg, gain, eps, d, carry, add, frag, inv_out, emb, tok, inv_e);
+  else if (d == 2048)
+    rms_bwd1_kernel<4><<<g1, b1, 0, st>>>(v, gy, ldg, gain, eps, d, carry, add, frag, inv_out, emb, tok, inv_e);
+  else if (d == 4096)
+    rms_bwd1_kernel<8><<<g1, b1, 0, st>>>(v, gy, ldg, gain, eps, d, carry, add, frag, inv_out, emb, tok, inv_e);
+  else
+    rms_bwd_kernel<<<M / 16, TR, 0, st>>>(v, gy, ldg, gain, eps, d, carry, add, frag, inv_out, emb, tok, inv_e);
+}
+
 // Gain gradient partials: part[c][k] (+)= sum over the rows r of chunk c of
 // gy[r][k] * v[r][k] * inv[r], rows in order; v is fp32 [M][d] or, with emb,
 // the bf16 embedding row of tok[r].
@@ -904,8 +993,8 @@ int ttt_train(const eagle3_dims& dm, const eagle3_weights& w, const void* feats,
     {
       // dh2 = carry + rms'(h2, norm_out) dy
       TimedScope ts(EAGLE3_KC_TTT_BWD_ROWS, st);
-      rms_bwd_kernel<<<M / 16, TR, 0, st>>>(h2, sv.dy + js * Md, d, w.norm_out, eps, d, L.carry, add, L.dh2f,
-                                           L.inv_a, nullptr, nullptr, nullptr);
+      rms_bwd(h2, sv.dy + js * Md, d, w.norm_out, eps, M, d, L.carry, add, L.dh2f, L.inv_a, nullptr, nullptr, nullptr,
+              st);
       gain_grad_kernel<<<gg_grid, 256, 0, st>>>(sv.dy + js * Md, d, h2, nullptr, nullptr, L.inv_a, d, gp_out, add);
       E3_CHECK(hipGetLastError());
       E3_CHECK(transpose(SrcFrag{L.dh2f, d / 32}, M, d, L.dh2T, MT / 32, col0, st));
@@ -928,8 +1017,7 @@ int ttt_train(const eagle3_dims& dm, const eagle3_weights& w, const void* feats,
     {
       // dh1 = dh2 + rms'(h1, norm_ffn) du
       TimedScope ts(EAGLE3_KC_TTT_BWD_ROWS, st);
-      rms_bwd_kernel<<<M / 16, TR, 0, st>>>(h1, L.du, d, w.norm_ffn, eps, d, L.carry, 1, L.dh1f, L.inv_a, nullptr,
-                                           nullptr, nullptr);
+      rms_bwd(h1, L.du, d, w.norm_ffn, eps, M, d, L.carry, 1, L.dh1f, L.inv_a, nullptr, nullptr, nullptr, st);
       gain_grad_kernel<<<gg_grid, 256, 0, st>>>(L.du, d, h1, nullptr, nullptr, L.inv_a, d, gp_ffn, add);
       E3_CHECK(hipGetLastError());
       E3_CHECK(transpose(SrcFrag{L.dh1f, d / 32}, M, d, L.dh1T, MT / 32, col0, st));
@@ -987,8 +1075,8 @@ int ttt_train(const eagle3_dims& dm, const eagle3_weights& w, const void* feats,
     {
       // carry = ds_j = dh1 + rms'(s_j, norm_s) dx_s; the embedding half only trains norm_e
       TimedScope ts(EAGLE3_KC_TTT_BWD_ROWS, st);
-      rms_bwd_kernel<<<M / 16, TR, 0, st>>>(s_in, L.dx + d, 2 * d, w.norm_s, eps, d, L.carry, 1,
-                                           j == 1 ? L.dgf : nullptr, L.inv_a, (const bf16*)w.emb, tok, L.inv_b);
+      rms_bwd(s_in, L.dx + d, 2 * d, w.norm_s, eps, M, d, L.carry, 1, j == 1 ? L.dgf : nullptr, L.inv_a,
+              (const bf16*)w.emb, tok, L.inv_b, st);
       gain_grad_kernel<<<gg_grid, 256, 0, st>>>(L.dx + d, 2 * d, s_in, nullptr, nullptr, L.inv_a, d, gp_s, add);
       gain_grad_kernel<<<gg_grid, 256, 0, st>>>(L.dx, 2 * d, nullptr, (const bf16*)w.emb, tok, L.inv_b, d, gp_e, add);
       E3_CHECK(hipGetLastError());
