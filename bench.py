@@ -748,15 +748,20 @@ def target_bench(w, Wt, steps, warmup):
     w_layer = ((hq + 2 * hkv) * hd * d + d * hq * hd + 2 * F * d + d * F) * es
     kv_read = int(np.sum(ti.ctx_len)) * hkv * hd * 2 * es
     fwd_bytes = L * (w_layer + kv_read + R * hkv * hd * 2 * es) + V * d * es + R * V * 4 + R * 3 * d * es
-    gu_bytes = 2 * F * d * es + R * d * es + R * F * es
-    lm_bytes = V * d * es + R * d * es + R * V * 4
     gu_ms, gu_cnt = per["tgt_gate_up"]
     lm_ms, lm_cnt = per["tgt_lm_head"]
     fw_ms, fw_cnt = per["target"]
     chunks = -(-R // 64)
+    # launches per layer (gate/up) and per forward (LM head): one over all row
+    # chunks when the library launches them together, else one per chunk; a
+    # launch streams the whole matrix and its own rows
+    gu_lpl = max(1, round(gu_cnt / (fw_cnt * L))) if gu_cnt and fw_cnt else 1
+    lm_lpf = max(1, round(lm_cnt / fw_cnt)) if lm_cnt and fw_cnt else 1
+    gu_launch_bytes = 2 * F * d * es + (R * d * es + R * F * es) / gu_lpl
+    lm_launch_bytes = V * d * es + (R * d * es + R * V * 4) / lm_lpf
     gu_us = gu_ms / gu_cnt * 1e3 if gu_cnt else None
-    gu_gbs = gu_bytes / chunks / (gu_us * 1e-6) / 1e9 if gu_us else None
-    lm_gbs = lm_bytes / (lm_ms / lm_cnt * 1e-3) / 1e9 if lm_cnt else None
+    gu_gbs = gu_launch_bytes / (gu_us * 1e-6) / 1e9 if gu_us else None
+    lm_gbs = lm_launch_bytes / (lm_ms / lm_cnt * 1e-3) / 1e9 if lm_cnt else None
     fw_ms_each = fw_ms / fw_cnt if fw_cnt else None
     res = {
         "workload": w.name,
@@ -771,10 +776,12 @@ def target_bench(w, Wt, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1) if gu_gbs else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4) if gu_gbs else None,
                      "traffic": load_traffic(w.name, "target_gate_up"),
-                     "kernel": "target gate/up GEMM with the SwiGLU epilogue (one launch per layer"
-                               + (f" and {chunks} row chunks)" if chunks > 1 else ")"),
+                     "kernel": "target gate/up GEMM with the SwiGLU epilogue ("
+                               + (f"{gu_lpl} launches per layer, one per 64-row chunk)" if gu_lpl > 1 else
+                                  f"one launch per layer over {chunks} row chunks)" if chunks > 1 else
+                                  "one launch per layer)"),
                      "scope": "dominant kernel only; the whole forward is forward_roofline",
-                     "bytes_per_launch": round(gu_bytes / chunks), "avg_launch_us": round(gu_us, 2) if gu_us else None},
+                     "bytes_per_launch": round(gu_launch_bytes), "avg_launch_us": round(gu_us, 2) if gu_us else None},
         "forward_roofline": {"bytes": fwd_bytes,
                              "achieved_GBs": round(fwd_bytes / (fw_ms_each * 1e-3) / 1e9, 1) if fw_ms_each else None,
                              "frac": round(fwd_bytes / (fw_ms_each * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)

@@ -590,7 +590,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       } else if (rx) {
         rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>
             <<<(nt16 + tpw - 1) / tpw, LM_RX_WAVES * 64, 0, st>>>((const bf16*)ws.lrz, r, Rl, (const bf16*)lr.a, r,
-                                                                   nt16, 1, es);
+                                                                   nt16, 1, es, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       } else if (small_k) {
         if constexpr (sizeof(T) == 2) {
@@ -623,7 +623,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       constexpr int KL = EAGLE3_KC_LMHEAD;
       if (rx)
         launch_timed(KL, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiTop1Part, LM_RX_WAVES>, dim3(nwg),
-                     dim3(LM_RX_WAVES * 64), 0, st, Xb, d, Rl, Wb, d, nt16, 1, epi);
+                     dim3(LM_RX_WAVES * 64), 0, st, Xb, d, Rl, Wb, d, nt16, 1, epi, 1);
       else if (tpw == 8)
         launch_timed(KL, skinny_gemm_kernel<128, EpiTop1Part>, dim3(nwg), dim3(256), 0, st, Xb, d, Rl, Wb, d, nt16, 1,
                      epi);
@@ -651,7 +651,7 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       if (rx) {
         launch_timed(EAGLE3_KC_LMHEAD, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiLogitsTiles, LM_RX_WAVES>,
                      dim3((nt16 + tpw - 1) / tpw), dim3(LM_RX_WAVES * 64), 0, st, (const bf16*)ws.y, d, Rl,
-                     (const bf16*)w.lm, d, nt16, 1, epi);
+                     (const bf16*)w.lm, d, nt16, 1, epi, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       } else if ((e = rows_gemm<T>((const T*)ws.y, d, Rl, (const T*)w.lm, d, V, plain, epi, pc, pk, st,
                                    EAGLE3_KC_LMHEAD)) != hipSuccess) {

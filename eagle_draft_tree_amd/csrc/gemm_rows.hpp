@@ -321,6 +321,7 @@ struct EpiStore {
   TO* out;
   int ldo;
   RowMap map;
+  __device__ void rebase(int r0) { out += (size_t)r0 * ldo; }
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int r = e >> 4, m = e & 15;  // 16 threads write one output row's 16 columns
@@ -391,8 +392,11 @@ struct EpiPartial {
   float* part;
   int N;
   RowMap map;
+  size_t sstride = 0;  // floats between splits; 0: R * N (the launch's own rows)
+  __device__ void rebase(int r0) { part += (size_t)r0 * N; }
+  __device__ size_t split_off(int split, int R) const { return (size_t)split * (sstride ? sstride : (size_t)R * N); }
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int split) const {
-    float* out = part + (size_t)split * R * N;
+    float* out = part + split_off(split, R);
     for (int e = threadIdx.x; e < 16 * R; e += blockDim.x) {
       const int r = e / 16, m = e - r * 16;
       out[(size_t)r * N + map(tile16, m)] = tile[m * RP + r];
@@ -406,7 +410,7 @@ struct EpiPartial {
   // Every map keeps rows 8h..8h+7 of a tile on consecutive columns.
   static constexpr bool kWhole = true;
   __device__ void whole(int wg, const float* tile, int RP, int R, int NB, int ntiles16, float*, int split) const {
-    float* out = part + (size_t)split * R * N;
+    float* out = part + split_off(split, R);
     for (int e = threadIdx.x; e < R * NB * 2; e += blockDim.x) {
       const int r = e / (NB * 2), q = e - r * (NB * 2), t = q >> 1, h = q & 1;
       const int t16 = wg * NB + t;
@@ -441,6 +445,7 @@ template <typename TO>
 struct EpiSwiGLU {
   TO* z;
   int ffn;
+  __device__ void rebase(int r0) { z += (size_t)r0 * ffn; }
   __device__ void operator()(int tile16, const float* tile, int RP, int R, int) const {
     for (int e = threadIdx.x; e < 8 * R; e += blockDim.x) {
       const int r = e >> 3, m = e & 7;

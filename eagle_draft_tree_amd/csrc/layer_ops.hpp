@@ -176,7 +176,7 @@ static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int
       const int nt16 = N / 16;
       const int grid = (nt16 + NB - 1) / NB * p.splits;
       rx_gemm_kernel<WT, RX_SPLIT_KU, Epi, WAVES><<<grid, WAVES * 64, 0, st>>>(
-          (const bf16*)X, ldx, R, (const bf16*)W, K, nt16, p.splits, epi);
+          (const bf16*)X, ldx, R, (const bf16*)W, K, nt16, p.splits, epi, 1);
       return hipGetLastError();
     }
   }
@@ -204,6 +204,62 @@ static hipError_t rows_gemm(const TW* X, int ldx, int R, const TW* W, int K, int
   }
   if (p.nt == 1) return rows_gemm_launch<TW, 1, 1, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
   return rows_gemm_launch<TW, 1, 4, 1, 4>(X, ldx, R, W, K, N, map, epi, p, false, st, kc);
+}
+
+// ---------------------------------------------------------------------------
+// More than 64 rows (a verification forward over a batch of chains): the row
+// chunks of 64 in one launch on the register-weight kernel (chunk_of_block),
+// so that the chunks of a weight tile read it together: split-K GEMMs
+// (EpiPartial with split stride R * N, splits = rx_splits_chunked(K)), the
+// unsplit gate/up GEMM (EpiSwiGLU) and, with the LM-head kernel's tiling,
+// the LM head (EpiStore).  Every chunk holds 17..64 rows.
+static inline bool rows_chunked_ok(int R, int K, bool packed) {
+  const int last = R % 64 == 0 ? 64 : R % 64;
+  return packed && R > 64 && last > 16 && K % (32 * RX_SPLIT_KU) == 0;
+}
+
+// Splits of a chunked split-K launch: the chunks already multiply the grid,
+// and at rx_splits(K) splits the partials of all R rows are as large as the
+// weights, so half as many (8B target at 4 x 64 rows: 13.5 against 13.9 ms
+// per verification step, a quarter 13.6); every split still holds whole KU
+// chunks.
+static inline int rx_splits_chunked(int K) {
+  const int s0 = rx_splits(K);
+  if (s0 <= 0) return 0;
+  const int ns = K / 32;
+  int s = s0 / 2;
+  while (s > 1 && (ns % s || (ns / s) % RX_SPLIT_KU)) s >>= 1;
+  return s;
+}
+
+template <class Epi>
+static hipError_t rows_gemm_chunked(const bf16* X, int ldx, int R, const bf16* W, int K, int N, const Epi& epi,
+                                    int splits, hipStream_t st, int kc = -1) {
+  static_assert(EpiRebase<Epi>::value, "a chunked launch needs an epilogue that can be rebased to its chunk");
+  const int nt16 = N / 16, nchunk = (R + 63) / 64;
+  if constexpr (std::is_same<Epi, EpiPartial>::value) {
+    if (splits < 1 || splits != rx_splits_chunked(K)) return hipErrorInvalidValue;
+    constexpr int WT = 2, WAVES = 4, NB = WT * WAVES;
+    const int grid = chunked_grid((nt16 + NB - 1) / NB * splits, nchunk);
+    // weights through the cache (not nontemporal as in the one-chunk
+    // launches), so that a unit's chunks share them in L2: 13.0 against
+    // 13.5 ms per verification step
+    launch_timed(kc, rx_gemm_kernel<WT, RX_SPLIT_KU, Epi, WAVES, false>, dim3(grid), dim3(WAVES * 64), 0, st, X, ldx,
+                 R, W, K, nt16, splits, epi, nchunk);
+  } else if constexpr (std::is_same<Epi, EpiStore<float>>::value) {
+    const int grid = chunked_grid((nt16 + LM_RX_TPW - 1) / LM_RX_TPW, nchunk);
+    launch_timed(kc, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, Epi, LM_RX_WAVES>, dim3(grid), dim3(LM_RX_WAVES * 64), 0, st,
+                 X, ldx, R, W, K, nt16, 1, epi, nchunk);
+  } else {
+    // unsplit (gate/up): the register-weight kernel with cached weights,
+    // 12.8 against 13.0 ms per verification step on the skinny kernel
+    constexpr int WT = 2, WAVES = 4, NB = WT * WAVES;
+    if ((K / 32) % RX_SPLIT_KU) return hipErrorInvalidValue;
+    const int grid = chunked_grid((nt16 + NB - 1) / NB, nchunk);
+    launch_timed(kc, rx_gemm_kernel<WT, RX_SPLIT_KU, Epi, WAVES, false>, dim3(grid), dim3(WAVES * 64), 0, st, X, ldx,
+                 R, W, K, nt16, 1, epi, nchunk);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

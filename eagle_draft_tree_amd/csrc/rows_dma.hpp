@@ -34,6 +34,39 @@ struct EpiWhole<E, std::void_t<decltype(E::kWhole)>> {
 };
 
 static inline bool sk_ok(int R, int K, bool packed) { return packed && R > 16 && R <= 64 && K % 32 == 0; }
+
+// Epilogues that can run on a row chunk of a larger call define
+// rebase(r0): from then on their row r is row r0 + r of the call.
+template <class E, class = void>
+struct EpiRebase {
+  static constexpr bool value = false;
+  static __device__ __forceinline__ void run(E&, int) {}
+};
+template <class E>
+struct EpiRebase<E, std::void_t<decltype(&E::rebase)>> {
+  static constexpr bool value = true;
+  static __device__ __forceinline__ void run(E& e, int r0) { e.rebase(r0); }
+};
+
+// More than 64 rows in one launch (a verification forward over a batch of
+// chains): workgroup -> (unit, row chunk of 64), unit = weight-tile group *
+// splits + split.  Workgroups are dealt round-robin over the eight XCDs, so
+// the nchunk workgroups of a unit take consecutive slots of one XCD: they
+// stream the same weights at about the same time, and the chunks after the
+// first find them in that XCD's L2 instead of reading HBM again.  The grid
+// is padded to whole rounds of 8 units; unit >= units marks a padding
+// workgroup.  nchunk = 1: the plain mapping.
+struct ChunkIdx {
+  int unit, chunk;
+};
+__device__ __forceinline__ ChunkIdx chunk_of_block(int nchunk) {
+  if (nchunk == 1) return {(int)blockIdx.x, 0};
+  const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+  return {(s / nchunk) * 8 + x, s % nchunk};
+}
+static inline int chunked_grid(int units, int nchunk) {
+  return nchunk == 1 ? units : (units + 7) / 8 * 8 * nchunk;
+}
 // weight rows per workgroup: 64 for split-K matrices up to 6144 rows (QKV and
 // O of the 8B drafter), else 128 unless that leaves fewer than 192
 // workgroups (measured on the 8B batch-64 shapes)

@@ -18,10 +18,10 @@
 
 namespace e3 {
 
-template <int WT, int KU, class Epi, int WAVES = 4>
+template <int WT, int KU, class Epi, int WAVES = 4, bool NTW = true>
 __global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restrict__ X, int ldx, int R,
                                                       const bf16* __restrict__ W, int K, int ntiles16,
-                                                      int splits, Epi epi) {
+                                                      int splits, Epi epi_in, int nchunk) {
   constexpr int NB = WAVES * WT;            // weight tiles per workgroup
   constexpr int XCH_U4 = KU * 4 * 64;       // one X chunk: KU steps x 4 row groups x 1 KB
   constexpr int RP = 65;                    // padded epilogue tile rows
@@ -31,7 +31,15 @@ __global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restr
   float* tile = (float*)smem;  // after the k loop: [NB*16][RP]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wgt = blockIdx.x / splits, split = blockIdx.x - wgt * splits;
+  const ChunkIdx ci = chunk_of_block(nchunk);
+  if (ci.unit >= (ntiles16 + NB - 1) / NB * splits) return;  // padding of a chunked grid (whole workgroup)
+  Epi epi = epi_in;
+  if (nchunk > 1) {
+    X += (size_t)ci.chunk * 64 * ldx;
+    R = min(64, R - ci.chunk * 64);
+    EpiRebase<Epi>::run(epi, ci.chunk * 64);
+  }
+  const int wgt = ci.unit / splits, split = ci.unit - wgt * splits;
   const int nsteps = K / 32;
   const int s0 = (int)((long)nsteps * split / splits), s1 = (int)((long)nsteps * (split + 1) / splits);
   const int nch = (s1 - s0) / KU;  // the host guarantees (s1 - s0) % KU == 0
@@ -65,7 +73,10 @@ __global__ __launch_bounds__(WAVES * 64) void rx_gemm_kernel(const bf16* __restr
 #pragma unroll
     for (int s = 0; s < KU; ++s)
 #pragma unroll
-      for (int j = 0; j < WT; ++j) wf[s][j].u = ld_stream(wsrc[j] + (size_t)(s0 + c * KU + s) * 512);
+      for (int j = 0; j < WT; ++j) {
+        const bf16* p = wsrc[j] + (size_t)(s0 + c * KU + s) * 512;
+        wf[s][j].u = NTW ? ld_stream(p) : *(const uint4*)p;
+      }
   };
   auto compute = [&](int c, const U4 (&wf)[KU][WT]) __attribute__((always_inline)) {
     const uint4* xb = smem + (size_t)(c & 1) * XCH_U4 + lane;

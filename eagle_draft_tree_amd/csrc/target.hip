@@ -24,8 +24,11 @@
 //            head input (norm_out) after the model's last layer
 // and after the last layer the LM head writes float32 logits.  The residual
 // stream is float32 in `hidden`; GEMM inputs are rounded to the dtype.  More
-// than 64 rows (a batch of chains) run every GEMM and its finish on chunks
-// of 64 rows, each chunk with the split-K plan of its size.
+// than 64 rows (a batch of chains) run every GEMM on row chunks of 64: with
+// bf16 packed weights and every chunk of 17..64 rows, all chunks of a GEMM
+// in one launch (the weights stream from HBM once; each finish kernel runs
+// once over all rows), otherwise one launch and finish per chunk, each with
+// the split-K plan of its size.
 #include <string.h>
 
 #include "common.hpp"
@@ -125,8 +128,9 @@ __global__ __launch_bounds__(RT) void target_layer_end_kernel(const float* __res
 namespace {
 // GEMMs of a target layer: qkv, o and down may split K; gate/up and the LM
 // head do not.  All of them run on row chunks of at most 64 rows (the rows
-// GEMM's limit), so the partials cover the larger of the two chunk sizes a
-// call can have.
+// GEMM's limit): one launch per chunk, whose partials cover the larger of
+// the two chunk sizes a call can have, or all chunks in one launch (more
+// than 64 rows), whose partials cover all R rows.
 size_t target_partials(const eagle3_dims& dm, int R) {
   const bool bf = dm.dtype == EAGLE3_BF16;
   const int d = dm.d, qd = dm.n_q_heads * dm.head_dim;
@@ -134,6 +138,10 @@ size_t target_partials(const eagle3_dims& dm, int R) {
   const int n[3] = {nqkv, d, d}, k[3] = {d, qd, dm.ffn};
   const int rc[2] = {R < 64 ? R : 64, R % 64};
   size_t m = 0;
+  // chunked launches (more than 64 rows): the partials of all R rows at once
+  if (R > 64)
+    for (int i = 0; i < 3; ++i)
+      if ((size_t)rx_splits_chunked(k[i]) * R * n[i] > m) m = (size_t)rx_splits_chunked(k[i]) * R * n[i];
   for (int c = 0; c < 2; ++c) {
     if (rc[c] == 0) continue;
     for (int i = 0; i < 3; ++i)
@@ -202,6 +210,8 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
   const RowMap plain{MAP_PLAIN, hd, F};
   const RowMap pair_head{MAP_PAIR_HEAD, hd, F};
   const bool last_layer = c.end == tg.n_layers;
+  // more than 64 rows in chunks of 17..64: every GEMM of a layer in one launch
+  const bool chunked = bf && rows_chunked_ok(R, d, pk) && rows_chunked_ok(R, qd, pk) && rows_chunked_ok(R, F, pk);
   const bool want_logits = last_layer && c.logits;
   hipError_t e;
   TimedScope total(EAGLE3_KC_TARGET, st);
@@ -229,8 +239,23 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
     KVDest dst{kv.k, kv.v, kv.tk, kv.tv, kv.ctx_len, kv.block_table, kv.cap, kv.max_blocks, kv.block_size,
                c.rows, EAGLE3_TREE, 0, hkv, hd, 0};
     // every GEMM below runs on row chunks of at most 64 rows (the last one
-    // ragged), each with its own split-K plan and finish
-    for (int r0 = 0; r0 < R; r0 += 64) {
+    // ragged): all chunks in one launch when each holds 17..64 rows and the
+    // GEMM has its chunked form (the weights then stream once per layer),
+    // else one launch per chunk, each with its own split-K plan and finish
+    const bool ck_qkv = chunked && rx_splits(d) > 0;
+    if (ck_qkv) {
+      if constexpr (sizeof(T) == 2) {
+        const int sp = rx_splits_chunked(d);
+        EpiPartial epi{ws.part, nqkv, pair_head, (size_t)R * nqkv};
+        if ((e = rows_gemm_chunked((const bf16*)ws.x, d, R, (const bf16*)Lw.qkv, d, nqkv, epi, sp, st)) !=
+            hipSuccess)
+          return e;
+        qkv_finish_kernel<T><<<dim3(R, hq + 2 * hkv), 64, 0, st>>>(ws.part, sp, R, nqkv, c.pos, dst, (T*)ws.q, hq,
+                                                                   dm.rope_theta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    }
+    for (int r0 = 0; r0 < R && !ck_qkv; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
       const RowsPlan p = plan_rows(Rc, nqkv, d, bf, true, pk);
       KVDest dc = dst;
@@ -281,7 +306,18 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
     al.out = ws.a;
     if ((e = launch_attention(al, st)) != hipSuccess) return e;
     // ---- O projection (+ residual) and the FFN norm
-    for (int r0 = 0; r0 < R; r0 += 64) {
+    const bool ck_o = chunked && rx_splits(qd) > 0;
+    if (ck_o) {
+      if constexpr (sizeof(T) == 2) {
+        const int sp = rx_splits_chunked(qd);
+        EpiPartial epi{ws.part, d, plain, (size_t)R * d};
+        if ((e = rows_gemm_chunked((const bf16*)ws.a, qd, R, (const bf16*)Lw.o, qd, d, epi, sp, st)) != hipSuccess)
+          return e;
+        ffn_norm_kernel<T><<<R, RT, 0, st>>>(c.hidden, ws.part, sp, R, d, Lw.norm_ffn, dm.rms_eps, ws.h1, (T*)ws.u);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    }
+    for (int r0 = 0; r0 < R && !ck_o; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
       const RowsPlan p = plan_rows(Rc, d, qd, bf, true, pk);
       int o_splits = 0;
@@ -302,7 +338,15 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // ---- gate/up + SwiGLU
-    for (int r0 = 0; r0 < R; r0 += 64) {
+    if (chunked) {
+      if constexpr (sizeof(T) == 2) {
+        EpiSwiGLU<T> epi{(T*)ws.z, F};
+        if ((e = rows_gemm_chunked((const bf16*)ws.u, d, R, (const bf16*)Lw.gate_up, d, 2 * F, epi, 1, st,
+                                   EAGLE3_KC_TGT_GATEUP)) != hipSuccess)
+          return e;
+      }
+    }
+    for (int r0 = 0; r0 < R && !chunked; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
       RowMap pf{MAP_PAIR_FFN, hd, F};
       EpiSwiGLU<T> epi{(T*)ws.z + (size_t)r0 * F, F};
@@ -316,7 +360,19 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
     if (c.feats)
       for (int f = 0; f < 3; ++f)
         if (tg.feat_layers[f] == l + 1) feat_mask |= 1 << f;
-    for (int r0 = 0; r0 < R; r0 += 64) {
+    const bool ck_down = chunked && rx_splits(F) > 0;
+    if (ck_down) {
+      if constexpr (sizeof(T) == 2) {
+        const int sp = rx_splits_chunked(F);
+        EpiPartial epi{ws.part, d, plain, (size_t)R * d};
+        if ((e = rows_gemm_chunked((const bf16*)ws.z, F, R, (const bf16*)Lw.down, F, d, epi, sp, st)) != hipSuccess)
+          return e;
+        target_layer_end_kernel<T><<<R, RT, 0, st>>>(ws.h1, ws.part, sp, R, ws.h2, d, feat_mask, (T*)c.feats,
+                                                     next_gain(l), dm.rms_eps, c.hidden, (T*)ws.x);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    }
+    for (int r0 = 0; r0 < R && !ck_down; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
       const RowsPlan p = plan_rows(Rc, d, F, bf, true, pk);
       int down_splits = 0;
@@ -343,14 +399,22 @@ static hipError_t target_impl(const TargetCall& c, hipStream_t st) {
   // ---- LM head: float32 logits of every row
   if (want_logits) {
     const int nt16 = V / 16;
-    for (int r0 = 0; r0 < R; r0 += 64) {
+    if (chunked) {
+      if constexpr (sizeof(T) == 2) {
+        EpiStore<float> epi{c.logits, V, plain};
+        if ((e = rows_gemm_chunked((const bf16*)ws.x, d, R, (const bf16*)tg.lm, d, V, epi, 1, st,
+                                   EAGLE3_KC_TGT_LMHEAD)) != hipSuccess)
+          return e;
+      }
+    }
+    for (int r0 = 0; r0 < R && !chunked; r0 += 64) {
       const int Rc = R - r0 < 64 ? R - r0 : 64;
       EpiStore<float> epi{c.logits + (size_t)r0 * V, V, plain};
       const T* X = (const T*)ws.x + (size_t)r0 * d;
       if (bf && lm_rx_ok(Rc, d, pk)) {
         launch_timed(EAGLE3_KC_TGT_LMHEAD, rx_gemm_kernel<LM_RX_WT, LM_RX_KU, EpiStore<float>, LM_RX_WAVES>,
                      dim3((nt16 + LM_RX_TPW - 1) / LM_RX_TPW), dim3(LM_RX_WAVES * 64), 0, st, (const bf16*)X, d, Rc,
-                     (const bf16*)tg.lm, d, nt16, 1, epi);
+                     (const bf16*)tg.lm, d, nt16, 1, epi, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       } else {
         const RowsPlan pc = plan_rows(Rc, V, d, bf, false);

@@ -211,13 +211,22 @@ def test_target_forward_small(lib, dtype, pack, paged, batch):
         np.testing.assert_allclose(feats[b], f_o, atol=tol[0], rtol=tol[1], err_msg=f"request {b}: features")
 
 
-def test_target_forward_chain_rows_over_64(lib):
-    """More than 64 verify rows in one call (batch 20 x 4-row chains, paged):
-    the row-chunked GEMM path."""
-    w = Workload("target-chains", SMALL_BF16, batch=20, depth=3, topk=1, keep=3, prefix=40, paged=True,
+MID_BF16 = tiny_shape(d=512, hq=8, hkv=2, hd=64, ffn=1024, vocab=4096, dtype=BF16, theta=500000.0, name="tgt-bf16-512")
+
+
+@pytest.mark.parametrize("shape,batch", [(SMALL_BF16, 20), (MID_BF16, 24), (MID_BF16, 32)],
+                         ids=["d256-80rows-per-chunk", "d512-96rows-chunked", "d512-128rows-chunked"])
+def test_target_forward_chain_rows_over_64(lib, shape, batch):
+    """More than 64 verify rows in one call (batch x 4-row chains, paged).
+    80 rows at width 256 end in a 16-row chunk, so every GEMM runs one launch
+    per 64-row chunk; 96 and 128 rows at width 512 (every chunk 17..64 rows,
+    split-K QKV, O and down) run all chunks of each GEMM and of the LM head
+    in one launch."""
+    w = Workload("target-chains", shape, batch=batch, depth=3, topk=1, keep=3, prefix=40, paged=True,
                  prefix_range=(1, 60))
+    say("target chains", shape.name, "batch", batch, "rows", batch * 4)
     case = Case(w, 2, (1, 1, 2))
-    layerwise = check_layerwise(case, [0, 7, 19], TOL_BF16)
+    layerwise = check_layerwise(case, [0, 7, batch - 1], TOL_BF16)
     check_one_call_equals_layerwise(case, layerwise)
 
 
