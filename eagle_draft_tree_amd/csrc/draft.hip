@@ -517,8 +517,8 @@ static hipError_t draft_impl(const DraftCall& c, hipStream_t st) {
       RowMap pf{MAP_PAIR_FFN, hd, F};
       EpiSwiGLU<T> epi{(T*)ws.z + (size_t)r0 * F, F};
       const RowsPlan pc = plan_rows(Rc, 2 * F, d, bf, false);
-      if ((e = rows_gemm<T>((const T*)ws.u + (size_t)r0 * d, d, Rc, (const T*)w.gate_up, d, 2 * F, pf, epi, pc, pk, st)) !=
-          hipSuccess)
+      if ((e = rows_gemm_gate_up<T>((const T*)ws.u + (size_t)r0 * d, d, Rc, (const T*)w.gate_up, d, 2 * F, pf, epi, pc,
+                                    pk, st)) != hipSuccess)
         return e;
     }
   }
