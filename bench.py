@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
     "lr_scores": ("lowrank.hip", "draft.hip", "common.hpp"),
     "ttt_ce": ("bigemm.hpp", "ttt.hip", "ttt_common.hpp", "common.hpp"),
     "ttt_dy": ("bigemm.hpp", "ttt.hip", "ttt_common.hpp", "common.hpp"),
-    "target_gate_up": ("gemm_rows.hpp", "rows_dma.hpp", "layer_ops.hpp", "target.hip", "common.hpp"),
+    "target_gate_up": ("gemm_rows.hpp", "rows_dma.hpp", "rows_rx.hpp", "layer_ops.hpp", "target.hip", "common.hpp"),
 }
 
 
