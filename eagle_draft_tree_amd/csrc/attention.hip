@@ -33,6 +33,7 @@ struct AttnArgs {
   const int32_t* block_table;
   const uint64_t* anc;  // [Rtot] (TREE) or NULL
   int cap, max_blocks, block_size;
+  int bs_log2;     // log2(block_size) when it is a power of two, else -1
   int B, rows, hq, hkv, mode, n_commit_splits, cpw, n_qgroups;
   int n_cache_sub, spw, nsplits;  // attn_mfma_kernel: cache sub-chunks, sub-chunks per wave, wave splits
   float scale;
@@ -491,11 +492,14 @@ __attribute__((amdgpu_waves_per_eu(QG == 1 ? 3 : 2))) void attn_mfma_kernel(Attn
       if (KVM == 0) {
         off = (((size_t)b * a.cap + pos) * a.hkv + g) * HD;
       } else {
-        const int bi = pos / a.block_size;
+        // power-of-two blocks (the usual 16): a shift and a mask instead of
+        // an integer division per key row
+        const int bi = a.bs_log2 >= 0 ? pos >> a.bs_log2 : pos / a.block_size;
+        const int po = pos - bi * a.block_size;
         int blk;
         if (KVM == 1) blk = __shfl(blk_reg, min(max(bi - blk0, 0), 63));
         else blk = ok ? a.block_table[(size_t)b * a.max_blocks + bi] : 0;
-        off = (((size_t)blk * a.block_size + pos % a.block_size) * a.hkv + g) * HD;
+        off = (((size_t)blk * a.block_size + po) * a.hkv + g) * HD;
       }
       return ok ? (const bf16*)cache + off : (const bf16*)cache;
     }
@@ -785,6 +789,10 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
   a.cap = L.cap;
   a.max_blocks = L.max_blocks;
   a.block_size = L.block_size;
+  a.bs_log2 = -1;
+  if (L.block_size > 0 && (L.block_size & (L.block_size - 1)) == 0)
+    for (a.bs_log2 = 0; (1 << a.bs_log2) < L.block_size; ++a.bs_log2) {
+    }
   a.B = L.B;
   a.rows = L.rows;
   a.hq = L.hq;
