@@ -829,9 +829,14 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     // paged: a wave's run spans at most 32*ceil(n_sub/nsplits)/block_size + 1 blocks
     const int run = (n_sub + a.nsplits - 1) / a.nsplits;
     const int kvm = !L.block_table ? 0 : ((SUB * run + L.block_size - 1) / L.block_size + 1 <= 64 ? 1 : 2);
-    // many splits (short runs, batch-1 shapes): a workgroup merges its four
-    // waves' splits, so four times fewer partials are written and merged
-    const bool merge4 = a.nsplits >= 32;
+    // many splits (short runs, batch-1 shapes), or at least 8 splits whose
+    // waves each hold a full group of 16 query vectors (the target's batch
+    // of 4-row chains: a partial is 8 KB per wave, 57 MB per call at 64 x 4
+    // rows): a workgroup merges its four waves' splits, so four times fewer
+    // partials are written and merged (8B target over 64 x 4 rows 12.25 ->
+    // 11.91 ms per step; the batch-64 drafter's 4 query vectors per wave
+    // write little and lost 0.6 % merging)
+    const bool merge4 = a.nsplits >= 32 || (a.nsplits >= 8 && nq >= 16);
     const int nsg = (a.nsplits + 3) / 4;
     const int nparts = merge4 ? nsg : a.nsplits;
     dim3 grid(merge4 ? nsg * L.hkv : (a.nsplits * L.hkv + 3) / 4, nwq, L.B);

@@ -94,6 +94,15 @@ __global__ __launch_bounds__(64) void qkv_finish_kernel(const float* __restrict_
   const int hd = dst.hd, half = hd >> 1;
   for (int i = threadIdx.x; i < half; i += 64) {
     const size_t n0 = (size_t)head * hd + i;
+    // the rotation first: its fp64 angle and cos/sin need no partial sum,
+    // so their latency overlaps the partials' loads
+    float c = 1.f, sn = 0.f;
+    if (head < hq + dst.hkv) {
+      const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
+      const double ang = (double)pos[r] * inv;
+      c = (float)cos(ang);
+      sn = (float)sin(ang);
+    }
     float p0[16], p1[16];
     float a = 0.f, b = 0.f;
     for (int s0 = 0; s0 < splits; s0 += 16) {
@@ -113,9 +122,6 @@ __global__ __launch_bounds__(64) void qkv_finish_kernel(const float* __restrict_
         }
     }
     if (head < hq + dst.hkv) {  // q or k: rotate
-      const double inv = pow((double)theta, -(2.0 * i) / (double)hd);
-      const double ang = (double)pos[r] * inv;
-      const float c = (float)cos(ang), sn = (float)sin(ang);
       const float a2 = a * c - b * sn, b2 = b * c + a * sn;
       a = a2;
       b = b2;
