@@ -820,7 +820,9 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
     const int n_sub = a.n_cache_sub + (L.mode == EAGLE3_TREE ? 2 : 0);
     const long units = (long)n_sub * L.hkv * nwq * L.B;
     int spw = (int)((units + 8191) / 8192);
-    const int spw_min = (n_sub + 511) / 512;
+    // at most 96 splits: the 70B tree's 130 sub-chunks (4096 keys) run two
+    // per wave (70B cycle +0.6 %), the 8B tree's 66 one per wave (two: -0.3 %)
+    const int spw_min = (n_sub + 95) / 96;
     spw = spw < spw_min ? spw_min : spw;
     a.spw = spw;
     a.nsplits = (n_sub + spw - 1) / spw;  // <= attn_num_chunks(cap_rows)
