@@ -13,6 +13,11 @@
 // the k-steps per workgroup as in the rows plan.  The epilogue interface is
 // the skinny kernel's: [16][RP] fp32 tiles (RP = 65), or the whole
 // workgroup tile (EpiWhole, with 1 KB of LDS scratch per wave).
+//
+// nchunk > 1: one launch covers R > 64 rows as row chunks of 64, a
+// workgroup per (unit, chunk) placed by chunk_of_block, the epilogue rebased
+// to its chunk's rows; NTW = false then loads the weights through the cache,
+// so that the chunks of a unit share them in L2.
 #pragma once
 #include "rows_dma.hpp"
 
